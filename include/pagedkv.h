@@ -1,0 +1,183 @@
+/*
+ * pagedkv.h — decode-time attention over a paged KV cache, for AMD Instinct
+ * MI355X (gfx950).  Plain C ABI: device pointers, sizes, and a HIP stream
+ * passed as void*.
+ *
+ * Pages cited:
+ *  [P1] «LLM推理显存优化：KV Cache管理3大策略实测，节省60%显存开销»
+ *  [P2] «生产级 LLM 推理的 KV 缓存优化» (The Ultimate Guide to KV Cache
+ *       Optimization for LLM Inference)
+ *  [P3] «大模型推理加速实战：KV Cache内存优化与PagedAttention分页管理方案»
+ *
+ * Cache layout (all entry points):
+ *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim], in kv_dtype.
+ *   INT8 scales        float32 [num_blocks][num_kv_heads][block_size], one per stored row.
+ *   FP8 scales         one float32 per tensor (per layer, one for K and one for V).
+ *   block_tables       int32 [batch][max_blocks_per_seq]: logical block j of sequence b
+ *                      lives in physical block block_tables[b][j] ([P1] §2 block table;
+ *                      [P3] PagedAttention section, worked tables A = 0,3,7 / B = 1,2,5).
+ *   context_lens       int32 [batch]: tokens of sequence b held in the cache.
+ *   slot               physical_block * block_size + offset_in_block.
+ *
+ * Conventions shared by every call:
+ *   - Pointers named as device pointers must point to device memory on the
+ *     current HIP device; the caller owns them.  The library never allocates,
+ *     frees or synchronises: every call only enqueues kernels on `stream`
+ *     (a hipStream_t; NULL = the null stream) and returns.
+ *   - Host-checkable problems (null pointers, unsupported sizes or dtype
+ *     pairs, too small a workspace) return a non-zero pkv_status before any
+ *     launch; pkv_last_error() then gives a text for the calling thread.
+ *   - Contents of device arrays are preconditions, not checked (that would
+ *     need a synchronisation).  For memory safety only, kernels skip — do not
+ *     read through — a block-table entry outside [0, num_blocks), an INT8/FP8
+ *     slot outside the pool, and clamp context_lens to
+ *     [0, min(max_context_len, max_blocks_per_seq * block_size)]; the results
+ *     for such inputs are unspecified but no access leaves the arrays.
+ *   - Unused cache slots (free blocks, the tail of a sequence's last block)
+ *     may hold any bytes, NaN included: they are never used in arithmetic.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shapes   */
+  PKV_ERR_UNSUPPORTED = 2, /* head_dim, block_size or dtype pair not built      */
+  PKV_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required         */
+  PKV_ERR_HIP = 4          /* a kernel launch failed; the text names the call    */
+} pkv_status;
+
+/* Storage types.  FP8 is OCP E4M3FN (bias 7, 3 mantissa bits, max 448,
+ * NaN = S.1111.111, no infinities): [P2] §4 and [P3] name an FP8 KV cache
+ * without fixing the variant; E4M3FN is the one gfx950 converts natively. */
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_I8 = 3,
+  PKV_FP8_E4M3FN = 4
+} pkv_dtype;
+
+/* Text of the last non-OK status returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/*
+ * kv_cache_bytes — closed-form size of a K+V cache:
+ * 2 * batch * seq_len * layers * kv_heads * head_dim * dtype_bytes
+ * ([P2] §2, estimating KV-cache memory; the same count as [P1] §1 and [P3]).
+ * Host only.  Returns 0 if the product overflows 64 bits.
+ */
+uint64_t kv_cache_bytes(uint64_t batch, uint64_t seq_len, uint64_t layers,
+                        uint64_t kv_heads, uint64_t head_dim, uint64_t dtype_bytes);
+
+/*
+ * kv_quantize — quantize rows of a float tensor for KV storage.
+ *
+ *   x         device, [n_rows][row_len] in x_dtype (PKV_F32 / PKV_F16 / PKV_BF16).
+ *   out       device, [n_rows][row_len] bytes in out_dtype.
+ *   out_dtype PKV_I8: per-row quantizer of [P1] §4 (quantize_tensor):
+ *               a = max|x_i| over the row; s = fl32(fl32(1/a) * 127) (the form
+ *               PyTorch evaluates for the page's 127 / absmax);
+ *               q_i = clamp(round_half_even(fl32(x_i * s)), -128, 127).
+ *               scale: device float32 [n_rows], written with s (1.0 and all-zero
+ *               codes for an all-zero row).  scale_given is ignored.
+ *             PKV_FP8_E4M3FN: one scale for the whole tensor.  If scale_given is
+ *               0, s = fl32(max|x| / 448) (1.0 if the tensor is all zero) is
+ *               computed on the device and written to scale[0]; otherwise
+ *               scale[0] is read.  Codes: RNE(clamp(fl32(x / s), -448, 448)).
+ *   Errors: PKV_ERR_INVALID_ARG (null pointer, n_rows < 0, row_len < 1),
+ *           PKV_ERR_UNSUPPORTED (dtype pair), PKV_ERR_HIP.
+ *   n_rows == 0 launches nothing (FP8 with scale_given == 0 still writes 1.0).
+ */
+pkv_status kv_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t row_len,
+                       int32_t out_dtype, void* out, float* scale, int32_t scale_given,
+                       void* stream);
+
+/*
+ * kv_cache_append — write the K/V rows of new tokens into their slots ([P3],
+ * PagedAttention section: blocks are filled on demand through the table).
+ *
+ *   k, v          device, [num_tokens][num_kv_heads][head_dim] in src_dtype
+ *                 (PKV_F32 / PKV_F16 / PKV_BF16), contiguous.
+ *   slot_mapping  device int64 [num_tokens]; token i goes to block slot/block_size,
+ *                 offset slot%block_size.  A negative slot writes nothing.
+ *   k_cache, v_cache  device, cache layout above, in cache_dtype:
+ *                 same as src_dtype: rows copied bit for bit;
+ *                 PKV_I8: each (token, head) row quantized as kv_quantize does,
+ *                   its scale written to k_scale/v_scale[block][head][offset];
+ *                 PKV_FP8_E4M3FN: encoded with the tensor scale read from
+ *                   k_scale[0] / v_scale[0] (saturating at +-448).
+ *   k_scale, v_scale  device float32 as above; NULL for plain float caches.
+ *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim not 64/128,
+ *           block_size not 16/256, dtype pair), PKV_ERR_HIP.
+ */
+pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int32_t num_tokens,
+                           const int64_t* slot_mapping, void* k_cache, void* v_cache,
+                           float* k_scale, float* v_scale, int32_t num_blocks,
+                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t cache_dtype, void* stream);
+
+/*
+ * paged_attention_workspace_size — bytes of device scratch paged_attention_decode
+ * needs for these sizes (partial softmax state of split contexts).  Host only.
+ */
+size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                      int32_t max_context_len);
+
+/*
+ * paged_attention_decode — one decode step: for every sequence b and query head
+ * h, attention of q[b][h] over the first context_lens[b] tokens of the cache,
+ * found through block_tables[b] ([P1] §2 and [P3]: the kernel locates each
+ * block through the table; the result equals standard attention over the
+ * stitched cache).  Query head h reads KV head h / (num_q_heads / num_kv_heads)
+ * ([P1] §3, grouped-query attention: MHA, GQA and MQA are the same rule):
+ *
+ *   out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t
+ *
+ *   out, q        device, [batch][num_q_heads][head_dim] in q_dtype
+ *                 (PKV_F32 / PKV_F16 / PKV_BF16), contiguous; out may not alias q.
+ *   k_cache, v_cache  device, cache layout above, kv_dtype = q_dtype, PKV_I8 or
+ *                 PKV_FP8_E4M3FN.  Dequantized values: INT8 code / scale
+ *                 (the inverse of [P1] §4's quantizer); FP8 decode(code) * scale.
+ *   k_scale, v_scale  device: INT8 [num_blocks][num_kv_heads][block_size];
+ *                 FP8 one float each; NULL otherwise.
+ *   block_tables  device int32 [batch][max_blocks_per_seq].
+ *   context_lens  device int32 [batch]; a sequence of length 0 gets zeros.
+ *   max_context_len  host int: an upper bound of context_lens (sizes the grid).
+ *   scale         softmax scale (1/sqrt(head_dim) for the usual attention).
+ *   workspace     device scratch of at least paged_attention_workspace_size(...)
+ *                 bytes (may be NULL when that size is 0); contents are
+ *                 overwritten.  Calls that share a workspace must be ordered.
+ *   Supported: head_dim 64 or 128; block_size 16 or 256; num_q_heads a multiple
+ *   of num_kv_heads.
+ *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int32_t batch,
+                                  int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, int32_t num_blocks,
+                                  int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t kv_dtype, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, float scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_partition_tokens — context tokens one workgroup of paged_attention_decode
+ * handles for these sizes (longer contexts are split and merged in a second
+ * pass).  Host only; informational.  Returns 0 for unsupported sizes.
+ */
+int32_t pkv_partition_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t block_size, int32_t max_context_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

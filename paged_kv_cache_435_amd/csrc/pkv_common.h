@@ -1,0 +1,92 @@
+// pkv_common.h — shared device helpers for the paged-KV kernels (gfx950).
+//
+// Storage formats: IEEE f32 / f16, bfloat16 (upper half of an f32), INT8 with a
+// per-row scale, and OCP FP8 E4M3FN (bias 7, 3 mantissa bits, max 448).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+// Wavefront width on CDNA.
+constexpr int kWave = 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+// Round to nearest even (the hardware conversion).
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  return __builtin_bit_cast(uint16_t, (_Float16)f);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return bitsf((uint32_t)h << 16); }
+// Round to nearest even; inputs here are finite.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = fbits(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// FP8 E4M3FN code -> f32, from the format definition (exact for every finite
+// code; the NaN code 0x7F/0xFF decodes to 480 here and is only ever met in slots
+// the kernels never use).
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t code) {
+  const uint32_t sign = (code & 0x80u) << 24;
+  const uint32_t e = (code >> 3) & 0xFu;
+  const uint32_t m = code & 0x7u;
+  const float sub = (float)m * 0.001953125f;               // m * 2^-9
+  const float nrm = bitsf(((e + 120u) << 23) | (m << 20));  // 2^(e-7) * (1 + m/8)
+  return bitsf(fbits(e == 0 ? sub : nrm) | sign);
+}
+
+// f32 (finite, |y| <= 448) -> nearest E4M3FN code, ties to even; sign from y.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  const uint32_t u = fbits(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(y);
+  uint32_t code;
+  if (a < 0.015625f) {                    // below 2^-6: the subnormal grid m * 2^-9
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // exact scaling, RNE; 8 -> 2^-6
+  } else {
+    const uint32_t ua = fbits(a);
+    int32_t e = (int32_t)(ua >> 23) - 127;            // -6 .. 8
+    uint32_t m3 = (ua >> 20) & 7u;
+    const uint32_t rem = ua & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+    if (m3 == 8u) { m3 = 0; ++e; }
+    code = ((uint32_t)(e + 7) << 3) | m3;
+  }
+  return sign | code;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Element size of a storage type.
+__host__ __device__ constexpr int dtype_bytes(int dt) {
+  return dt == PKV_F32 ? 4 : (dt == PKV_F16 || dt == PKV_BF16) ? 2 : 1;
+}
+
+}  // namespace pkv

@@ -1,0 +1,499 @@
+// pkv_decode.hip — decode attention over a paged KV cache, hand-written for gfx950.
+//
+// What is computed ([P1] «LLM推理显存优化：KV Cache管理3大策略实测，节省60%显存开销»
+// §2–§4; [P3] «大模型推理加速实战：KV Cache内存优化与PagedAttention分页管理方案»,
+// PagedAttention section): for each sequence b and query head h, softmax attention
+// of q[b][h] over the cached rows of KV head h / G, each row found through the
+// sequence's block table.  The pages run this on NVIDIA parts with vLLM's kernel;
+// the design here is for CDNA4:
+//
+//  * One 64-lane wave per (sequence, KV head, tile of up to 16 query heads of
+//    that KV head's group, context partition).  The KV rows are read from HBM
+//    once per KV head and shared by the whole query group.
+//  * Tokens go 16 at a time.  QK^T is one MFMA chain per 16 tokens:
+//    S^T[16 tok][16 heads] = K[16 tok][d] * Q^T[d][16 heads]
+//    (v_mfma_f32_16x16x32_{f16,bf16}, or 16x16x4 for f32).  K is loaded from HBM
+//    straight into the A-operand layout (16 B per lane, 64 contiguous bytes per
+//    row per instruction); Q sits in registers for the whole partition.
+//  * Online softmax in the exp2 domain on the MFMA output registers.  A lane
+//    holds 4 tokens of one head, so a head's max needs two cross-lane steps.
+//  * PV as O^T[d][heads] += V^T[d][16 tok] * P^T[16 tok][heads]
+//    (v_mfma_f32_16x16x16).  P^T is exactly the QK output layout, so P never
+//    leaves its registers.  V is staged through LDS (coalesced 16 B/lane
+//    writes) and read back transposed.
+//  * Long contexts are split into partitions of P tokens; each wave writes its
+//    (max, sum, unnormalised output) and a second kernel merges them with the
+//    log-sum-exp rule.  A sequence that fits one partition is finished in place.
+//  * Tokens past the context are selected out (never multiplied), and their V
+//    rows are zeroed in LDS, so stale or NaN bytes in unused slots never reach
+//    the sums.
+#include "pkv_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+enum { MT_F32 = 0, MT_F16 = 1, MT_BF16 = 2 };
+
+template <int QT>
+struct MfmaOf {
+  static constexpr int value = QT == PKV_F32 ? MT_F32 : (QT == PKV_F16 ? MT_F16 : MT_BF16);
+};
+
+// ---------------------------------------------------------------------------
+// Stored KV bytes -> MFMA input elements.
+//
+// Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
+// packed two elements per 32-bit word; for f32 it is one float per word.
+// FP8 -> f16 uses the bit layout: the code's 7 magnitude bits shifted into an
+// f16's exponent/mantissa give decode(code) * 2^-8 exactly (subnormals too);
+// the 2^8 is folded into the scales.  INT8 -> f16 uses 1024 + (q + 128) - 1152.
+// ---------------------------------------------------------------------------
+template <int KV, int MT>
+struct Cvt {
+  static constexpr int eb = dtype_bytes(KV);
+  static constexpr int in_elems = 16 / eb;                           // per 16 B chunk
+  static constexpr int out_words = MT == MT_F32 ? in_elems : in_elems / 2;
+
+  __device__ __forceinline__ static void run(const u32x4 raw, uint32_t* w) {
+    if constexpr ((KV == PKV_F16 && MT == MT_F16) || (KV == PKV_BF16 && MT == MT_BF16) ||
+                  (KV == PKV_F32 && MT == MT_F32)) {
+      w[0] = raw[0]; w[1] = raw[1]; w[2] = raw[2]; w[3] = raw[3];
+    } else if constexpr (KV == PKV_I8 && MT == MT_F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t t = raw[i] ^ 0x80808080u;
+        const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
+        const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
+        const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+        w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
+        w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
+      }
+    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // bytes b0 b1 -> [0, b0, 0, b1]; b2 b3 -> [0, b2, 0, b3]
+        const uint32_t lo = __builtin_amdgcn_perm(0u, raw[i], 0x010C000Cu);
+        const uint32_t hi = __builtin_amdgcn_perm(0u, raw[i], 0x030C020Cu);
+        w[2 * i] = (lo & 0x80008000u) | ((lo & 0x7F007F00u) >> 1);
+        w[2 * i + 1] = (hi & 0x80008000u) | ((hi & 0x7F007F00u) >> 1);
+      }
+    } else {
+      // Generic: through f32 (exact for every pair built here).
+      float f[in_elems];
+#pragma unroll
+      for (int e = 0; e < in_elems; ++e) {
+        const uint32_t word = raw[(e * eb) / 4];
+        const int sh = ((e * eb) % 4) * 8;
+        if constexpr (KV == PKV_I8) {
+          f[e] = (float)(int8_t)((word >> sh) & 0xFFu);
+        } else if constexpr (KV == PKV_FP8_E4M3FN) {
+          f[e] = e4m3fn_to_f32((word >> sh) & 0xFFu);
+        } else if constexpr (KV == PKV_F16) {
+          f[e] = f16_to_f32((uint16_t)((word >> sh) & 0xFFFFu));
+        } else if constexpr (KV == PKV_BF16) {
+          f[e] = bf16_to_f32((uint16_t)((word >> sh) & 0xFFFFu));
+        } else {
+          f[e] = bitsf(word);
+        }
+      }
+#pragma unroll
+      for (int o = 0; o < out_words; ++o) {
+        if constexpr (MT == MT_F32) {
+          w[o] = fbits(f[o]);
+        } else if constexpr (MT == MT_F16) {
+          w[o] = (uint32_t)f32_to_f16(f[2 * o]) | ((uint32_t)f32_to_f16(f[2 * o + 1]) << 16);
+        } else {  // bf16: every value converted here is exact in bf16, so truncate
+          w[o] = (fbits(f[2 * o]) >> 16) | (fbits(f[2 * o + 1]) & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+};
+
+// Extra factor the conversion above leaves in the value (2^-8 for FP8 via f16).
+template <int KV, int MT>
+__host__ __device__ constexpr float cvt_gain() {
+  return (KV == PKV_FP8_E4M3FN && MT == MT_F16) ? 256.0f : 1.0f;
+}
+
+// One query element (stored as QT) as an MFMA element (16-bit pattern or f32 bits).
+template <int QT>
+__device__ __forceinline__ uint32_t q_elem(const void* q, int64_t idx) {
+  if constexpr (QT == PKV_F32) {
+    return fbits(static_cast<const float*>(q)[idx]);
+  } else {
+    return static_cast<const uint16_t*>(q)[idx];
+  }
+}
+
+template <int QT>
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, float a, float b, float c,
+                                           float d) {
+  if constexpr (QT == PKV_F32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = f32x4{a, b, c, d};
+  } else if constexpr (QT == PKV_F16) {
+    u32x2 w = {(uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16),
+               (uint32_t)f32_to_f16(c) | ((uint32_t)f32_to_f16(d) << 16)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = w;
+  } else {
+    u32x2 w = {(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+               (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = w;
+  }
+}
+
+template <int MT>
+__device__ __forceinline__ uint32_t pack_p(float a, float b) {
+  if constexpr (MT == MT_F16) {
+    return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+  } else {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Partition kernel.
+// ---------------------------------------------------------------------------
+template <int KV, int QT, int D, int BS>
+__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+  constexpr int MT = MfmaOf<QT>::value;
+  constexpr int eb = dtype_bytes(KV);
+  constexpr int R = D * eb;            // bytes per stored row
+  constexpr int NL = R / 64;           // 16-byte loads per lane per 16-row tile
+  using C = Cvt<KV, MT>;
+  constexpr int WPC = C::out_words;    // MFMA words per chunk
+  constexpr int KW = NL * WPC;         // MFMA words per lane for a K tile (= D/8 or D/4)
+  constexpr int mtb = MT == MT_F32 ? 4 : 2;
+  constexpr int LDS_ROW = D * mtb + 16;  // bytes, padded against bank conflicts
+  constexpr int NC = D / 16;           // 16-wide d chunks of the output
+
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * LDS_ROW];
+
+  const int part = blockIdx.x;
+  const int g = blockIdx.y / a.head_tiles;
+  const int ht = blockIdx.y % a.head_tiles;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x;
+  const int r16 = lane & 15;   // MFMA row/column index of this lane
+  const int c16 = lane >> 4;   // MFMA k-group of this lane
+
+  int ctx = a.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (part >= (nparts > 0 ? nparts : 1)) return;
+
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int h_first = g * G + ht * 16;              // first query head of this tile
+  int nh = G - ht * 16;
+  nh = nh > 16 ? 16 : nh;
+  const bool head_ok = r16 < nh;
+  const int64_t hq = (int64_t)b * a.num_q_heads + h_first + r16;   // this lane's head row
+
+  if (ctx == 0) {  // nothing to attend to: defined as zeros
+    if (head_ok) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc)
+        store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, 0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+
+  const int t_begin = part * a.part_tokens;
+  const int t_end = (t_begin + a.part_tokens < ctx) ? t_begin + a.part_tokens : ctx;
+  const int ntiles = (t_end - t_begin + 15) >> 4;
+
+  // Block-table entries of this partition, one per lane (part_tokens/BS <= 64).
+  const int first_blk = t_begin / BS;
+  const int nblk = (t_end - t_begin + BS - 1) / BS;
+  int my_blk = -1;
+  if (lane < nblk) my_blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + first_blk + lane];
+  if (my_blk >= a.num_blocks) my_blk = -1;
+
+  // Query operand: lane holds head r16 at the d positions its K chunks carry.
+  uint32_t qop[KW];
+#pragma unroll
+  for (int i = 0; i < KW; ++i) qop[i] = 0u;
+  if (head_ok) {
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+#pragma unroll
+      for (int o = 0; o < WPC; ++o) {
+        if constexpr (MT == MT_F32) {
+          const int d = (64 * j + 16 * c16) / eb + o;
+          qop[j * WPC + o] = q_elem<QT>(a.q, hq * D + d);
+        } else {
+          const int d = (64 * j + 16 * c16) / eb + 2 * o;
+          qop[j * WPC + o] = q_elem<QT>(a.q, hq * D + d) | (q_elem<QT>(a.q, hq * D + d + 1) << 16);
+        }
+      }
+    }
+  }
+
+  // Constant factors: logits are taken in the exp2 domain.
+  float kfac = a.scale * 1.4426950408889634f;
+  float vfac = 1.0f;
+  if constexpr (KV == PKV_FP8_E4M3FN) {
+    kfac *= a.k_scale[0] * cvt_gain<KV, MT>();
+    vfac = a.v_scale[0] * cvt_gain<KV, MT>();
+  }
+
+  const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_cache);
+
+  f32x4 acc[NC];
+#pragma unroll
+  for (int nc = 0; nc < NC; ++nc) acc[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.f;
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int t0 = t_begin + tile * 16;
+    const int rel_blk = (tile * 16) / BS;
+    int phys = __builtin_amdgcn_readlane(my_blk, rel_blk);
+    int n_valid = t_end - t0;
+    n_valid = n_valid > 16 ? 16 : n_valid;
+    if (phys < 0) { phys = 0; n_valid = 0; }   // outside the pool: skip the tile
+    const int off = t0 % BS;
+    const int64_t row0 = ((int64_t)phys * a.num_kv_heads + g) * BS + off;   // first row
+
+    // ---- loads ----
+    const uint8_t* ktile = kbase + row0 * R;
+    const uint8_t* vtile = vbase + row0 * R;
+    u32x4 kraw[NL], vraw[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      kraw[j] = *reinterpret_cast<const u32x4*>(ktile + r16 * R + 64 * j + 16 * c16);
+#pragma unroll
+    for (int j = 0; j < NL; ++j)
+      vraw[j] = *reinterpret_cast<const u32x4*>(vtile + (lane + 64 * j) * 16);
+    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (KV == PKV_I8) {
+      ksc = *reinterpret_cast<const f32x4*>(a.k_scale + row0 + 4 * c16);
+      vsc = *reinterpret_cast<const f32x4*>(a.v_scale + row0 + 4 * c16);
+    }
+
+    // ---- V tile -> LDS (as MFMA elements), tail rows zeroed ----
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int chunk = lane + 64 * j;
+      const int row = (chunk * 16) / R;
+      const int col = ((chunk * 16) % R) / eb;   // element column
+      uint32_t w[WPC];
+      C::run(vraw[j], w);
+      if (row >= n_valid) {
+#pragma unroll
+        for (int o = 0; o < WPC; ++o) w[o] = 0u;
+      }
+      uint8_t* dst = lds_v + row * LDS_ROW + col * mtb;
+#pragma unroll
+      for (int o = 0; o < WPC; o += 4)
+        *reinterpret_cast<u32x4*>(dst + o * 4) = u32x4{w[o], w[o + 1], w[o + 2], w[o + 3]};
+    }
+
+    // ---- S^T = K Q^T ----
+    uint32_t kop[KW];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) C::run(kraw[j], kop + j * WPC);
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (MT == MT_F16) {
+#pragma unroll
+      for (int c = 0; c < KW / 4; ++c) {
+        const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+        const u32x4 qb = {qop[4 * c], qop[4 * c + 1], qop[4 * c + 2], qop[4 * c + 3]};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka),
+                                                   __builtin_bit_cast(f16x8, qb), s, 0, 0, 0);
+      }
+    } else if constexpr (MT == MT_BF16) {
+#pragma unroll
+      for (int c = 0; c < KW / 4; ++c) {
+        const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+        const u32x4 qb = {qop[4 * c], qop[4 * c + 1], qop[4 * c + 2], qop[4 * c + 3]};
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                    __builtin_bit_cast(bf16x8, qb), s, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < KW; ++c)
+        s = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[c]), s, 0, 0, 0);
+    }
+
+    // ---- online softmax (lane: tokens 4*c16 + i of head r16) ----
+    float z[4];
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool ok = 4 * c16 + i < n_valid;
+      float f = kfac;
+      if constexpr (KV == PKV_I8) f = kfac / ksc[i];
+      z[i] = ok ? s[i] * f : -__builtin_inff();
+      mx = fmaxf(mx, z[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const bool live = m_new != -__builtin_inff();
+    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = (live && z[i] != -__builtin_inff()) ? exp2f(z[i] - m_new) : 0.f;
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
+    if constexpr (KV == PKV_I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] / vsc[i] : 0.f;
+    }
+
+    __syncthreads();   // V tile visible in LDS
+
+    // ---- O^T += V^T P^T ----
+    if constexpr (MT == MT_F32) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = *reinterpret_cast<const float*>(lds_v + (4 * c16 + i) * LDS_ROW +
+                                                          (nc * 16 + r16) * 4);
+          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[i], acc[nc], 0, 0, 0);
+        }
+      }
+    } else {
+      const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        const uint8_t* src = lds_v + (4 * c16) * LDS_ROW + (nc * 16 + r16) * 2;
+        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(src);
+        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(src + LDS_ROW);
+        const uint32_t v2 = *reinterpret_cast<const uint16_t*>(src + 2 * LDS_ROW);
+        const uint32_t v3 = *reinterpret_cast<const uint16_t*>(src + 3 * LDS_ROW);
+        const u32x2 va = {v0 | (v1 << 16), v2 | (v3 << 16)};
+        if constexpr (MT == MT_F16) {
+          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
+                                                          __builtin_bit_cast(f16x4, pb), acc[nc],
+                                                          0, 0, 0);
+        } else {
+          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, va),
+                                                              __builtin_bit_cast(i16x4, pb),
+                                                              acc[nc], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();   // reads done before the next tile overwrites LDS
+  }
+
+  // ---- epilogue ----
+  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
+  l_tot += __shfl_xor(l_tot, 32, kWave);
+  if (!head_ok) return;
+  if (nparts == 1) {
+    const float inv = vfac / l_tot;
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+      store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, acc[nc][0] * inv, acc[nc][1] * inv,
+                     acc[nc][2] * inv, acc[nc][3] * inv);
+  } else {
+    const int64_t slot = hq * a.max_parts + part;
+    if (c16 == 0) {
+      a.ws_ml[2 * slot] = m_run;
+      a.ws_ml[2 * slot + 1] = l_tot;
+    }
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+      *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[nc] * vfac;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of partitions: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// One wave per (query head, sequence).
+// ---------------------------------------------------------------------------
+template <int QT, int D>
+__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  int ctx = a.context_lens[b];
+  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
+  if (nparts <= 1) return;
+  const int64_t hq = (int64_t)b * a.num_q_heads + h;
+  const float* ml = a.ws_ml + 2 * hq * a.max_parts;
+  const float* accp = a.ws_acc + hq * a.max_parts * D;
+
+  float M = -__builtin_inff();
+  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
+  M = wave_max(M);
+
+  constexpr int PER = D / kWave;   // 1 or 2 output elements per lane
+  float o[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) o[e] = 0.f;
+  float L = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float w = exp2f(ml[2 * p] - M);
+    L += w * ml[2 * p + 1];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] += w * accp[(int64_t)p * D + lane * PER + e];
+  }
+  const float inv = 1.0f / L;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const float v = o[e] * inv;
+    const int64_t idx = hq * D + lane * PER + e;
+    if constexpr (QT == PKV_F32) static_cast<float*>(a.out)[idx] = v;
+    else if constexpr (QT == PKV_F16) static_cast<uint16_t*>(a.out)[idx] = f32_to_f16(v);
+    else static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch over the compiled instances.
+// ---------------------------------------------------------------------------
+template <int KV, int QT, int D, int BS>
+static hipError_t launch4(const DecodeArgs& a, int grid_parts, hipStream_t st) {
+  dim3 grid(grid_parts, a.num_kv_heads * a.head_tiles, a.batch);
+  hipLaunchKernelGGL((decode_partition_kernel<KV, QT, D, BS>), grid, dim3(64), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.max_parts > 1) {
+    hipLaunchKernelGGL((decode_reduce_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
+                       st, a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int KV, int QT, int D>
+static hipError_t launch3(const DecodeArgs& a, int bs, int gp, hipStream_t st) {
+  return bs == 16 ? launch4<KV, QT, D, 16>(a, gp, st) : launch4<KV, QT, D, 256>(a, gp, st);
+}
+
+template <int KV, int QT>
+static hipError_t launch2(const DecodeArgs& a, int d, int bs, int gp, hipStream_t st) {
+  return d == 64 ? launch3<KV, QT, 64>(a, bs, gp, st) : launch3<KV, QT, 128>(a, bs, gp, st);
+}
+
+template <int QT>
+static hipError_t launch1(const DecodeArgs& a, int kv, int d, int bs, int gp, hipStream_t st) {
+  switch (kv) {
+    case PKV_I8: return launch2<PKV_I8, QT>(a, d, bs, gp, st);
+    case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT>(a, d, bs, gp, st);
+    default: return launch2<QT, QT>(a, d, bs, gp, st);
+  }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                         int block_size, int grid_parts, hipStream_t st) {
+  switch (q_dtype) {
+    case PKV_F32: return launch1<PKV_F32>(a, kv_dtype, head_dim, block_size, grid_parts, st);
+    case PKV_F16: return launch1<PKV_F16>(a, kv_dtype, head_dim, block_size, grid_parts, st);
+    default: return launch1<PKV_BF16>(a, kv_dtype, head_dim, block_size, grid_parts, st);
+  }
+}
+
+}  // namespace pkv

@@ -1,0 +1,250 @@
+// pkv_quant.hip — KV quantization and cache append, hand-written for gfx950.
+//
+// INT8 ([P1] «LLM推理显存优化：KV Cache管理3大策略实测，节省60%显存开销» §4,
+// quantize_tensor): per row a = max|x|, s = fl32(fl32(1/a) * 127) — the form
+// PyTorch evaluates for the page's scalar-over-tensor 127 / absmax — then
+// q = clamp(rint(fl32(x * s)), -128, 127).  Division is IEEE (no fast-math),
+// rint is round-half-even, so codes and scales are bit-exact.
+//
+// FP8 E4M3FN, one scale per tensor ([P2] «生产级 LLM 推理的 KV 缓存优化» §4
+// --kv-cache-dtype fp8; [P3] KV-quantization section): s = fl32(max|x| / 448),
+// codes = RNE(clamp(fl32(x / s), -448, 448)).
+//
+// Append ([P3] PagedAttention section: each new token's row goes to the slot
+// its block table names): one wave per (token, KV head); the row is copied or
+// quantized on the fly.
+#include "pkv_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+template <int XT>
+__device__ __forceinline__ float load_f32(const void* x, int64_t i) {
+  if constexpr (XT == PKV_F32) return static_cast<const float*>(x)[i];
+  else if constexpr (XT == PKV_F16) return f16_to_f32(static_cast<const uint16_t*>(x)[i]);
+  else return bf16_to_f32(static_cast<const uint16_t*>(x)[i]);
+}
+
+// Row scale of the INT8 quantizer; 0 marks an all-zero row.
+__device__ __forceinline__ float int8_row_scale(float absmax) {
+  if (absmax == 0.0f) return 0.0f;
+  const float r = 1.0f / absmax;   // IEEE correctly rounded
+  return r * 127.0f;
+}
+
+__device__ __forceinline__ int8_t int8_code(float x, float s) {
+  const float y = x * s;
+  float q = __builtin_rintf(y);
+  q = q < -128.0f ? -128.0f : (q > 127.0f ? 127.0f : q);
+  return (int8_t)(int)q;
+}
+
+__device__ __forceinline__ uint8_t fp8_code(float x, float s) {
+  float y = x / s;                 // IEEE correctly rounded
+  y = y < -448.0f ? -448.0f : (y > 448.0f ? 448.0f : y);
+  return (uint8_t)f32_to_e4m3fn(y);
+}
+
+// ---------------------------------------------------------------------------
+// INT8 rows: one wave per row, four rows per workgroup.
+// ---------------------------------------------------------------------------
+template <int XT>
+__global__ __launch_bounds__(256) void quantize_int8_kernel(const void* __restrict__ x,
+                                                            int8_t* __restrict__ out,
+                                                            float* __restrict__ scale,
+                                                            int64_t n_rows, int row_len) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int64_t base = row * row_len;
+  float a = 0.0f;
+  for (int i = lane; i < row_len; i += kWave) a = fmaxf(a, __builtin_fabsf(load_f32<XT>(x, base + i)));
+  a = wave_max(a);
+  const float s = int8_row_scale(a);
+  for (int i = lane; i < row_len; i += kWave)
+    out[base + i] = s == 0.0f ? (int8_t)0 : int8_code(load_f32<XT>(x, base + i), s);
+  if (lane == 0) scale[row] = s == 0.0f ? 1.0f : s;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 per tensor: absmax (atomic max on the bit pattern of non-negative
+// floats, accumulated in scale[0]), finalize, encode.
+// ---------------------------------------------------------------------------
+__global__ void fp8_scale_init_kernel(float* scale) {
+  if (threadIdx.x == 0) reinterpret_cast<uint32_t*>(scale)[0] = 0u;
+}
+
+template <int XT>
+__global__ __launch_bounds__(256) void fp8_absmax_kernel(const void* __restrict__ x, int64_t n,
+                                                         float* scale) {
+  float a = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    a = fmaxf(a, __builtin_fabsf(load_f32<XT>(x, i)));
+  a = wave_max(a);
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned int*>(scale), fbits(a));
+}
+
+__global__ void fp8_scale_finalize_kernel(float* scale) {
+  if (threadIdx.x == 0) {
+    const float a = bitsf(reinterpret_cast<uint32_t*>(scale)[0]);
+    scale[0] = a == 0.0f ? 1.0f : a / 448.0f;
+  }
+}
+
+template <int XT>
+__global__ __launch_bounds__(256) void fp8_encode_kernel(const void* __restrict__ x, int64_t n,
+                                                         const float* __restrict__ scale,
+                                                         uint8_t* __restrict__ out) {
+  const float s = scale[0];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = fp8_code(load_f32<XT>(x, i), s);
+}
+
+template <int XT>
+static hipError_t quantize_t(const void* x, int64_t n_rows, int row_len, int out_dtype, void* out,
+                             float* scale, int scale_given, hipStream_t st) {
+  if (out_dtype == PKV_I8) {
+    if (n_rows == 0) return hipSuccess;
+    const int64_t blocks = (n_rows + 3) / 4;
+    hipLaunchKernelGGL((quantize_int8_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                       static_cast<int8_t*>(out), scale, n_rows, row_len);
+    return hipGetLastError();
+  }
+  const int64_t n = n_rows * (int64_t)row_len;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  if (!scale_given) {
+    hipLaunchKernelGGL(fp8_scale_init_kernel, dim3(1), dim3(64), 0, st, scale);
+    if (n > 0)
+      hipLaunchKernelGGL((fp8_absmax_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x, n,
+                         scale);
+    hipLaunchKernelGGL(fp8_scale_finalize_kernel, dim3(1), dim3(64), 0, st, scale);
+  }
+  if (n > 0)
+    hipLaunchKernelGGL((fp8_encode_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x, n,
+                       (const float*)scale, static_cast<uint8_t*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
+                           void* out, float* scale, int scale_given, hipStream_t st) {
+  switch (x_dtype) {
+    case PKV_F32: return quantize_t<PKV_F32>(x, n_rows, row_len, out_dtype, out, scale, scale_given, st);
+    case PKV_F16: return quantize_t<PKV_F16>(x, n_rows, row_len, out_dtype, out, scale, scale_given, st);
+    default: return quantize_t<PKV_BF16>(x, n_rows, row_len, out_dtype, out, scale, scale_given, st);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Append: grid (num_kv_heads, num_tokens), one wave each.
+// ---------------------------------------------------------------------------
+template <int ST, int CT, int D>
+__global__ __launch_bounds__(64) void append_kernel(const void* __restrict__ k,
+                                                    const void* __restrict__ v,
+                                                    const int64_t* __restrict__ slots,
+                                                    void* __restrict__ k_cache,
+                                                    void* __restrict__ v_cache,
+                                                    float* __restrict__ k_scale,
+                                                    float* __restrict__ v_scale, int num_blocks,
+                                                    int block_size, int num_kv_heads) {
+  constexpr int PER = D / kWave;   // elements per lane
+  const int g = blockIdx.x;
+  const int t = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+  const int64_t blk = slot / block_size;
+  const int64_t off = slot % block_size;
+  const int64_t dst_row = (blk * num_kv_heads + g) * block_size + off;
+  const int64_t src_row = (int64_t)t * num_kv_heads + g;
+
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which == 0 ? k : v;
+    void* cache = which == 0 ? k_cache : v_cache;
+    float* sc = which == 0 ? k_scale : v_scale;
+    if constexpr (CT == ST) {
+      constexpr int eb = dtype_bytes(ST);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int64_t i = lane * PER + e;
+        if constexpr (eb == 4)
+          static_cast<uint32_t*>(cache)[dst_row * D + i] =
+              static_cast<const uint32_t*>(src)[src_row * D + i];
+        else
+          static_cast<uint16_t*>(cache)[dst_row * D + i] =
+              static_cast<const uint16_t*>(src)[src_row * D + i];
+      }
+    } else {
+      float xv[PER];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) xv[e] = load_f32<ST>(src, src_row * D + lane * PER + e);
+      if constexpr (CT == PKV_I8) {
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) a = fmaxf(a, __builtin_fabsf(xv[e]));
+        a = wave_max(a);
+        const float s = int8_row_scale(a);
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          static_cast<int8_t*>(cache)[dst_row * D + lane * PER + e] =
+              s == 0.0f ? (int8_t)0 : int8_code(xv[e], s);
+        if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
+      } else {  // FP8 with the tensor's scale
+        const float s = sc[0];
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          static_cast<uint8_t*>(cache)[dst_row * D + lane * PER + e] = fp8_code(xv[e], s);
+      }
+    }
+  }
+}
+
+template <int ST, int CT>
+static hipError_t append_t(const void* k, const void* v, int num_tokens, const int64_t* slots,
+                           void* kc, void* vc, float* ks, float* vs, int nb, int bs, int hkv,
+                           int d, hipStream_t st) {
+  if (num_tokens == 0) return hipSuccess;
+  dim3 grid(hkv, num_tokens);
+  if (d == 64)
+    hipLaunchKernelGGL((append_kernel<ST, CT, 64>), grid, dim3(64), 0, st, k, v, slots, kc, vc, ks,
+                       vs, nb, bs, hkv);
+  else
+    hipLaunchKernelGGL((append_kernel<ST, CT, 128>), grid, dim3(64), 0, st, k, v, slots, kc, vc,
+                       ks, vs, nb, bs, hkv);
+  return hipGetLastError();
+}
+
+template <int ST>
+static hipError_t append_s(int ct, const void* k, const void* v, int n, const int64_t* slots,
+                           void* kc, void* vc, float* ks, float* vs, int nb, int bs, int hkv,
+                           int d, hipStream_t st) {
+  switch (ct) {
+    case PKV_I8: return append_t<ST, PKV_I8>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
+    case PKV_FP8_E4M3FN:
+      return append_t<ST, PKV_FP8_E4M3FN>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
+    default: return append_t<ST, ST>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
+  }
+}
+
+hipError_t launch_append(const void* k, const void* v, int src_dtype, int num_tokens,
+                         const int64_t* slots, void* k_cache, void* v_cache, float* k_scale,
+                         float* v_scale, int num_blocks, int block_size, int num_kv_heads,
+                         int head_dim, int cache_dtype, hipStream_t st) {
+  switch (src_dtype) {
+    case PKV_F32:
+      return append_s<PKV_F32>(cache_dtype, k, v, num_tokens, slots, k_cache, v_cache, k_scale,
+                               v_scale, num_blocks, block_size, num_kv_heads, head_dim, st);
+    case PKV_F16:
+      return append_s<PKV_F16>(cache_dtype, k, v, num_tokens, slots, k_cache, v_cache, k_scale,
+                               v_scale, num_blocks, block_size, num_kv_heads, head_dim, st);
+    default:
+      return append_s<PKV_BF16>(cache_dtype, k, v, num_tokens, slots, k_cache, v_cache, k_scale,
+                                v_scale, num_blocks, block_size, num_kv_heads, head_dim, st);
+  }
+}
+
+}  // namespace pkv

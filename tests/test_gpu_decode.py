@@ -1,0 +1,144 @@
+"""paged_attention_decode vs the CPU oracle on the GPU, at sizes the oracle
+finishes in seconds: several 16-token tiles, several context partitions, ragged
+tails, every dtype pair, both block sizes, both head sizes, MHA/GQA/MQA."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_435_amd as pkv
+from paged_kv_cache_435_amd import workloads as W
+from paged_kv_cache_435_amd.device_cache import DeviceCase, to_host
+from tests.gpu_util import append_and_decode, compare, oracle_out, run_and_check, say
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 15, 16, 17, 255, 256, 257, 511, 513, 700, 1024, 2049]
+
+
+@pytest.mark.parametrize("q_dtype,kv", [
+    (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
+    (torch.float16, "i8"), (torch.bfloat16, "i8"), (torch.float32, "i8"),
+    (torch.float16, "fp8"), (torch.bfloat16, "fp8"), (torch.float32, "fp8"),
+])
+def test_dtype_pairs_ragged(q_dtype, kv):
+    w = W.custom(q_dtype, kv, RAGGED, 8, 2, 128, 16, appends=True, name=f"ragged-{kv}")
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_and_head_sizes(bs, d):
+    w = W.custom(torch.float16, "f16", [3, 300, 777, 1500], 4, 4, d, bs, extra_blocks=3,
+                 name=f"bs{bs}-d{d}")
+    run_and_check(w)
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (8, 1), (16, 2), (16, 1), (10, 2), (64, 8), (64, 1),
+                                    (40, 1)])
+def test_head_grouping(hq, hkv):
+    w = W.custom(torch.float16, "f16", [40, 600, 1100], hq, hkv, 128, 16, name=f"G{hq // hkv}")
+    run_and_check(w)
+
+
+def test_zero_length_sequence_gives_zeros():
+    w = W.custom(torch.float16, "f16", [100, 1, 700], 8, 2, 128, 16, name="zero-len")
+    case = DeviceCase(w)
+    case.context_lens[1] = 0
+    got = append_and_decode(case)
+    assert np.all(got[1] == 0)
+    ctx = w.context_lens.copy()
+    ctx[1] = 0
+    h = to_host(case)
+    ref = oracle.decode_attention(h["q"], h["k_cache"], h["v_cache"], w.block_tables, ctx,
+                                  w.scale, 16, "f16")
+    compare(got, ref, "f16", "zero-len")
+
+
+def test_single_token_is_its_value_row_exactly():
+    for q_dtype, fmt in [(torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32")]:
+        w = W.custom(q_dtype, fmt, [1, 1, 1], 8, 2, 128, 16, name="ctx1")
+        case = DeviceCase(w)
+        got = append_and_decode(case)
+        vrows = torch.stack([case.v_cache[w.block_tables[b, 0], :, 0, :] for b in range(3)])
+        want = vrows.repeat_interleave(4, dim=1)
+        assert torch.equal(case.out, want.to(case.out.dtype)), fmt
+
+
+def test_permuting_physical_blocks_is_bit_identical():
+    w = W.custom(torch.float16, "f16", [77, 1000, 3000], 16, 2, 128, 16, pool_factor=2.0,
+                 name="perm")
+    a = DeviceCase(w)
+    out_a = torch.from_numpy(append_and_decode(a))
+    NB = w.num_blocks
+    pi = torch.from_numpy(np.random.default_rng(12).permutation(NB)).cuda()
+    kb, vb = torch.empty_like(a.k_cache), torch.empty_like(a.v_cache)
+    kb[pi] = a.k_cache
+    vb[pi] = a.v_cache
+    bt = torch.where(a.block_tables >= 0, pi[a.block_tables.clamp(min=0).long()].int(),
+                     a.block_tables)
+    out_b = torch.empty_like(a.out)
+    pkv.paged_attention_decode(out_b, a.q, kb, vb, bt.contiguous(), a.context_lens, w.scale,
+                               w.max_context_len)
+    torch.cuda.synchronize()
+    assert torch.equal(a.out, out_b)
+    assert torch.equal(out_a, a.out.float().cpu().double())
+
+
+def test_repeat_runs_are_bit_identical():
+    w = W.custom(torch.bfloat16, "bf16", [5000, 33, 2500], 8, 1, 128, 16, name="repeat")
+    case = DeviceCase(w)
+    append_and_decode(case)
+    first = case.out.clone()
+    for _ in range(3):
+        pkv.paged_attention_decode(case.out, case.q, case.k_cache, case.v_cache,
+                                   case.block_tables, case.context_lens, w.scale,
+                                   w.max_context_len)
+        torch.cuda.synchronize()
+        assert torch.equal(first, case.out)
+
+
+def test_identity_table_equals_contiguous_attention():
+    B, Hq, Hkv, d, T = 3, 8, 2, 128, 640
+    w = W.custom(torch.float16, "f16", [T] * B, Hq, Hkv, d, 16, pool_factor=1.0, name="identity")
+    w.block_tables = np.arange(w.num_blocks, dtype=np.int32).reshape(B, -1)
+    case = DeviceCase(w)
+    got = append_and_decode(case)
+    nblk = T // 16
+    K = case.k_cache.float().cpu().numpy().reshape(B, nblk, Hkv, 16, d).transpose(0, 2, 1, 3, 4)
+    V = case.v_cache.float().cpu().numpy().reshape(B, nblk, Hkv, 16, d).transpose(0, 2, 1, 3, 4)
+    ref = oracle.attention.contiguous_attention(to_host(case)["q"], K.reshape(B, Hkv, T, d),
+                                                V.reshape(B, Hkv, T, d), w.scale)
+    compare(got, ref, "f16", "identity")
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_needles_localise_every_position(bs):
+    """A key parallel to the query with a large norm takes ~all the weight, so the
+    output is that token's V row: checks block boundaries, tails, partitions."""
+    ctx = 1500
+    positions = [0, 15, 16, 255, 256, 257, 511, 512, 1023, 1024, 1499]
+    w = W.custom(torch.float32, "f32", [ctx] * len(positions), 4, 1, 64, bs, name="needles")
+    case = DeviceCase(w)
+    q = case.q
+    for b, t in enumerate(positions):
+        blk = int(w.block_tables[b, t // bs])
+        qh = q[b, 0] / q[b, 0].norm()
+        case.k_cache[blk, 0, t % bs] = 60.0 * qh * 8.0   # scale 1/8 -> logit gap ~60
+        q[b, 1:] = q[b, 0]
+    got = append_and_decode(case)
+    for b, t in enumerate(positions):
+        blk = int(w.block_tables[b, t // bs])
+        vrow = case.v_cache[blk, 0, t % bs].double().cpu().numpy()
+        assert np.allclose(got[b, 0], vrow, atol=1e-5), (b, t)
+    compare(got, oracle_out(case), "f32", "needles")
+
+
+def test_workspace_too_small_raises():
+    w = W.custom(torch.float16, "f16", [3000], 8, 2, 128, 16, name="ws")
+    case = DeviceCase(w)
+    tiny = torch.empty(64, dtype=torch.uint8, device="cuda")
+    with pytest.raises(RuntimeError, match="workspace"):
+        pkv.paged_attention_decode(case.out, case.q, case.k_cache, case.v_cache,
+                                   case.block_tables, case.context_lens, w.scale,
+                                   w.max_context_len, workspace=tiny)
