@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of one decode step over a paged KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is the whole hot path for one batch: ``kv_cache_append`` writes the new
+token of every sequence into its slot (quantizing it for INT8/FP8 caches), then
+``paged_attention_decode`` attends each query head over its sequence's cache,
+found through the block table, for every layer of the workload.  Inputs are
+synthetic and seeded (``paged_kv_cache_435_amd.workloads``) and already resident
+in HBM when timing starts.
+
+The default workload is the Llama-2-70B-shaped GQA-8 layer: fp16 KV, 64 query
+heads over 8 KV heads, head_dim 128, 16-token blocks, batch 32 with context
+lengths drawn uniformly from [512, 32768], blocks shuffled over a pool 1.25x the
+demand.
+
+Printed (stdout, one JSON line): decode tokens/s (sequences x steps / time), the
+step time, the achieved KV-read bandwidth of the decode kernel (algorithmic K+V
+bytes per launch / average launch time from HIP events on the launch stream)
+against MI355X's 8 TB/s, and the CPU oracle timed on a bounded sample of the
+same workload on the host cores.  Progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode attention tokens/s + KV-read HBM GB/s (% of MI355X peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[1])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama70b_gqa8")
+    ap.add_argument("--block-size", type=int, default=None, help="llama70b_fp8 only: 16 or 256")
+    ap.add_argument("--cold-reps", type=int, default=30,
+                    help="extra decode launches timed after a 1 GiB cache-flushing write")
+    ap.add_argument("--read-ceiling", type=int, default=1,
+                    help="also time a plain 4 GiB streaming read kernel (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample (0 = skip)")
+    return ap.parse_args()
+
+
+def kernel_launch_times(pairs):
+    return [a.elapsed_time(b) * 1e-3 for a, b in pairs]   # seconds
+
+
+def cpu_baseline(w, cases, budget_s):
+    """The CPU oracle, as it stands, on whole sequences of the workload (every
+    query head), taken in a seeded order until about ``budget_s`` seconds of
+    oracle time have been spent.  Only the sampled sequences' blocks are copied
+    to the host, into a compact pool with its own table (bookkeeping only)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from paged_kv_cache_435_amd.device_cache import cache_to_host, q_to_host
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - informational only
+        cores = 1
+    order = np.random.default_rng(7).permutation(w.batch)
+    spent, seqs, layer_calls = 0.0, 0, 0
+    case = cases[0]
+    for b in order:
+        ctx = int(w.context_lens[b])
+        nblk = -(-ctx // w.block_size)
+        phys = torch.from_numpy(w.block_tables[b, :nblk].astype(np.int64)).to(case.k_cache.device)
+        kc = cache_to_host(case.k_cache[phys], w.kv_format)
+        vc = cache_to_host(case.v_cache[phys], w.kv_format)
+        ks = vs = None
+        if w.kv_format == "i8":
+            ks, vs = case.k_scale[phys].cpu().numpy(), case.v_scale[phys].cpu().numpy()
+        elif w.kv_format == "fp8":
+            ks, vs = np.float32(case.k_scale.item()), np.float32(case.v_scale.item())
+        q = q_to_host(case.q[b:b + 1])
+        bt = np.arange(nblk, dtype=np.int32)[None]
+        cl = np.array([ctx], dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.decode_attention(q, kc, vc, bt, cl, w.scale, w.block_size, w.kv_format, ks, vs)
+        spent += time.perf_counter() - t0
+        seqs += 1
+        layer_calls += 1
+        if spent >= budget_s:
+            break
+    # One sequence-layer of oracle work stands for 1/layers of a decoded token.
+    tokens = layer_calls / w.layers
+    return {"value": tokens / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{seqs} of {w.batch} sequences of {w.name} (layer 0, all "
+                       f"{w.num_q_heads} query heads, contexts summing to "
+                       f"{int(sum(int(w.context_lens[b]) for b in order[:seqs]))} tokens), "
+                       f"{spent:.1f} s of float64 oracle time"
+                       + ("; per-layer cost scaled by the layer count" if w.layers > 1 else ""))}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the decode path shards by sequence or KV head with no exchange, but no "
+              "multi-GPU run is provided.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_435_amd as pkv
+    from paged_kv_cache_435_amd import workloads as W
+    from paged_kv_cache_435_amd.device_cache import DeviceCase
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    pkv.load_library()   # raises if the HIP library was not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = W.make(args.workload, block_size=args.block_size)
+    log(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"d={w.head_dim} bs={w.block_size} kv={w.kv_format} layers={w.layers} "
+        f"sum(ctx)={int(w.context_lens.sum())} pool={w.num_blocks} blocks")
+    t0 = time.time()
+    cases = []
+    for layer in range(w.layers):
+        cases.append(DeviceCase(w, device=dev, layer=layer))
+        if layer == 0 or (layer + 1) % 10 == 0:
+            log(f"[bench] layer {layer + 1}/{w.layers} resident "
+                f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.0f} s)")
+    torch.cuda.synchronize()
+
+    mcl = w.max_context_len
+    ws_bytes = pkv.paged_attention_workspace_size(w.batch, w.num_q_heads, w.head_dim, mcl)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kv_dtype = cases[0].kv_dtype
+    part = pkv.partition_tokens(w.batch, w.num_q_heads, w.num_kv_heads, w.block_size, mcl)
+
+    def step(events=None):
+        for c in cases:
+            if w.appends:
+                pkv.kv_cache_append(c.new_k, c.new_v, c.slots, c.k_cache, c.v_cache,
+                                    c.k_scale, c.v_scale, kv_dtype=kv_dtype)
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            pkv.paged_attention_decode(c.out, c.q, c.k_cache, c.v_cache, c.block_tables,
+                                       c.context_lens, w.scale, mcl, k_scale=c.k_scale,
+                                       v_scale=c.v_scale, kv_dtype=kv_dtype, workspace=ws)
+            if events is not None:
+                e1.record()
+                events.append((e0, e1))
+
+    log(f"[bench] warmup {args.warmup} steps (partition {part} tokens, workspace {ws_bytes} B)")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = []
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    launch_s = kernel_launch_times(events)
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = w.batch * args.steps / elapsed
+
+    kv_bytes = w.kv_bytes_per_layer()          # algorithmic bytes of one decode launch
+    avg_launch = float(np.mean(launch_s))
+    achieved = kv_bytes / avg_launch / 1e9
+    log(f"[bench] {ms_per_step:.4f} ms/step, decode launch avg {avg_launch * 1e6:.1f} us "
+        f"(p10 {np.percentile(launch_s, 10) * 1e6:.1f}, p90 {np.percentile(launch_s, 90) * 1e6:.1f}), "
+        f"{achieved:.0f} GB/s of KV")
+
+    # Cold caches: a 1 GiB write before each decode launch evicts the L2s and the
+    # 256 MB Infinity Cache, so every KV byte comes from HBM.
+    cold = None
+    if args.cold_reps > 0:
+        flush = torch.empty(2**30, dtype=torch.uint8, device=dev)
+        cold_ev = []
+        for i in range(args.cold_reps):
+            flush.fill_(i & 0xFF)
+            c = cases[i % len(cases)]
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            pkv.paged_attention_decode(c.out, c.q, c.k_cache, c.v_cache, c.block_tables,
+                                       c.context_lens, w.scale, mcl, k_scale=c.k_scale,
+                                       v_scale=c.v_scale, kv_dtype=kv_dtype, workspace=ws)
+            e1.record()
+            cold_ev.append((e0, e1))
+        torch.cuda.synchronize()
+        cs = kernel_launch_times(cold_ev)
+        cold = {"avg_us": float(np.mean(cs)) * 1e6, "median_us": float(np.median(cs)) * 1e6,
+                "kv_gbps": kv_bytes / float(np.median(cs)) / 1e9, "reps": args.cold_reps}
+        del flush
+        log(f"[bench] cold: median {cold['median_us']:.1f} us, {cold['kv_gbps']:.0f} GB/s")
+
+    # What a plain streaming read reaches on this device (yardstick, not a target).
+    ceiling = None
+    if args.read_ceiling:
+        from paged_kv_cache_435_amd import probe
+        ceiling = probe.read_gbps(4 << 30, reps=10, device=dev)
+        log(f"[bench] plain 4 GiB read kernel: {ceiling:.0f} GB/s")
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        log(f"[bench] CPU oracle sample (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, cases, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.2f} tokens/s on {cpu['cores']} threads")
+
+    record = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "i8": "i8+f16",
+                  "fp8": "fp8+f16"}[w.kv_format],
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "block_size": w.block_size, "kv_format": w.kv_format, "layers": w.layers,
+                   "q_dtype": str(w.q_dtype).replace("torch.", ""),
+                   "sum_context_tokens": int(w.context_lens.sum()),
+                   "max_context_len": mcl, "pool_blocks": w.num_blocks,
+                   "partition_tokens": part, "appends_per_step": bool(w.appends)},
+        "kv_gbps": achieved,
+        "kv_pct_of_peak": achieved / HBM_PEAK_GBPS * 100.0,
+        "read_ceiling_gbps": ceiling,
+        "kv_pct_of_read_ceiling": None if not ceiling else achieved / ceiling * 100.0,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "paged_attention_decode",
+                     "bytes_per_launch": kv_bytes, "avg_launch_us": avg_launch * 1e6},
+        "cold_cache": cold,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(record), flush=True)
+
+
+if __name__ == "__main__":
+    main()

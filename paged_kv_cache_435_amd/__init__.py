@@ -33,7 +33,9 @@ _LIB = None
 
 
 def library_path():
-    return os.path.join(_HERE, "libpagedkv.so")
+    """The in-tree build, or the file named by PKV_LIBRARY (another build of the
+    same sources, e.g. with different compile-time tuning)."""
+    return os.environ.get("PKV_LIBRARY") or os.path.join(_HERE, "libpagedkv.so")
 
 
 def load_library():

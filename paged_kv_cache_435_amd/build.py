@@ -3,7 +3,8 @@
     python -m paged_kv_cache_435_amd.build
 
 Every HIP source under csrc/ is compiled to an object (in parallel), then linked
-into ``paged_kv_cache_435_amd/libpagedkv.so``.  No fast-math: the INT8/FP8
+into ``paged_kv_cache_435_amd/libpagedkv.so``.  The streaming yardstick kernels
+under csrc/probe/ (not part of the attention path) go into ``libpkvprobe.so``.  No fast-math: the INT8/FP8
 quantizers rely on IEEE division and round-half-even.  Packed-FP32 instruction
 selection is turned off for all device code.
 """
@@ -18,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
+PROBE_LIB = os.path.join(PKG, "libpkvprobe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
@@ -39,26 +41,35 @@ def _run(cmd):
     return out
 
 
-def build(verbose=False):
-    """Compile every csrc/*.hip and link libpagedkv.so.  Returns the library path."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose=False, out=None, defines=()):
+    """Compile every csrc/*.hip and link libpagedkv.so (or ``out``).  ``defines``
+    are extra -D flags (compile-time tuning knobs).  Returns the library path."""
+    lib = out or LIB
+    obj_dir = OBJ_DIR if out is None else out + ".objs"
+    os.makedirs(obj_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(OBJ_DIR, os.path.basename(s)[:-4] + ".o") for s in sources]
+    objs = [os.path.join(obj_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
+    extra = [f"-D{d}" for d in defines]
 
     def compile_one(pair):
         src, obj = pair
-        return _run([HIPCC, *CFLAGS, "-c", src, "-o", obj])
+        return _run([HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj])
 
     with ThreadPoolExecutor(max_workers=min(8, len(sources))) as ex:
         logs = list(ex.map(compile_one, zip(sources, objs)))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    if out is None:
+        probe_src = os.path.join(CSRC, "probe", "pkv_probe.hip")
+        tmp = PROBE_LIB + ".tmp"
+        logs.append(_run([HIPCC, *CFLAGS, "-shared", probe_src, "-o", tmp]))
+        os.replace(tmp, PROBE_LIB)
     if verbose:
         for log in logs:
             if log.strip():
                 print(log)
-    return LIB
+    return lib
 
 
 if __name__ == "__main__":

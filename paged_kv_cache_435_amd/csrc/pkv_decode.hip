@@ -153,9 +153,33 @@ __device__ __forceinline__ uint32_t pack_p(float a, float b) {
 
 // ---------------------------------------------------------------------------
 // Partition kernel.
+//
+// The tile loop is software-pipelined two deep: while tile i is converted and
+// multiplied, the K/V loads of tile i+1 are already in flight (two register
+// sets, the loop unrolled by two so no register copy waits on a load).  The
+// workgroup is one wave, so no workgroup barrier is needed: the V tile goes
+// through a per-tile LDS buffer (two buffers, alternating) and the wave's own
+// LDS operations complete in order.
 // ---------------------------------------------------------------------------
+#ifndef PKV_NT_LOADS
+#define PKV_NT_LOADS 1
+#endif
+
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+#if PKV_NT_LOADS
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+  return *reinterpret_cast<const u32x4*>(p);
+#endif
+}
+
+#ifndef PKV_WAVES_PER_EU
+#define PKV_WAVES_PER_EU 3
+#endif
+
 template <int KV, int QT, int D, int BS>
-__global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
   constexpr int eb = dtype_bytes(KV);
   constexpr int R = D * eb;            // bytes per stored row
@@ -165,9 +189,10 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   constexpr int KW = NL * WPC;         // MFMA words per lane for a K tile (= D/8 or D/4)
   constexpr int mtb = MT == MT_F32 ? 4 : 2;
   constexpr int LDS_ROW = D * mtb + 16;  // bytes, padded against bank conflicts
+  constexpr int LDS_TILE = 16 * LDS_ROW;
   constexpr int NC = D / 16;           // 16-wide d chunks of the output
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[16 * LDS_ROW];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * LDS_TILE];
 
   const int part = blockIdx.x;
   const int g = blockIdx.y / a.head_tiles;
@@ -246,33 +271,52 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  for (int tile = 0; tile < ntiles; ++tile) {
+  // Physical block of a tile (-1: outside the pool, the tile is skipped).
+  auto tile_phys = [&](int tile) -> int {
+    return __builtin_amdgcn_readlane(my_blk, (tile * 16) / BS);
+  };
+  // First cache row of a tile in the [NB][Hkv][BS] row space.
+  auto tile_row0 = [&](int tile) -> int64_t {
+    int phys = tile_phys(tile);
+    phys = phys < 0 ? 0 : phys;
+    return ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS);
+  };
+
+  // Per-lane byte offsets inside a tile (32-bit, so the loads take a scalar
+  // tile base plus one vector offset).
+  const uint32_t koff = (uint32_t)(r16 * R + 16 * c16);
+  const uint32_t voff = (uint32_t)(lane * 16);
+
+  // Issue the loads of one tile into a register set.
+  auto issue = [&](int tile, u32x4* kr, u32x4* vr, f32x4& ks, f32x4& vs) {
+    const int64_t row0 = tile_row0(tile);
+    const uint64_t tile_bytes = (uint64_t)row0 * R;   // uniform: keep it scalar
+    const uint64_t tb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tile_bytes >> 32)) << 32) |
+                        (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)tile_bytes);
+    const uint8_t* ktile = kbase + tb;
+    const uint8_t* vtile = vbase + tb;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile + koff + 64 * j);
+#pragma unroll
+    for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + voff + 1024 * j);
+    if constexpr (KV == PKV_I8) {
+      ks = *reinterpret_cast<const f32x4*>(a.k_scale + row0 + 4 * c16);
+      vs = *reinterpret_cast<const f32x4*>(a.v_scale + row0 + 4 * c16);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the compute they overlap
+  };
+
+  // Softmax update and both contractions for one loaded tile.
+  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, const f32x4& ksc,
+                     const f32x4& vsc, uint8_t* lbuf) {
     const int t0 = t_begin + tile * 16;
-    const int rel_blk = (tile * 16) / BS;
-    int phys = __builtin_amdgcn_readlane(my_blk, rel_blk);
     int n_valid = t_end - t0;
     n_valid = n_valid > 16 ? 16 : n_valid;
-    if (phys < 0) { phys = 0; n_valid = 0; }   // outside the pool: skip the tile
-    const int off = t0 % BS;
-    const int64_t row0 = ((int64_t)phys * a.num_kv_heads + g) * BS + off;   // first row
+    if (tile_phys(tile) < 0) n_valid = 0;
 
-    // ---- loads ----
-    const uint8_t* ktile = kbase + row0 * R;
-    const uint8_t* vtile = vbase + row0 * R;
-    u32x4 kraw[NL], vraw[NL];
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      kraw[j] = *reinterpret_cast<const u32x4*>(ktile + r16 * R + 64 * j + 16 * c16);
-#pragma unroll
-    for (int j = 0; j < NL; ++j)
-      vraw[j] = *reinterpret_cast<const u32x4*>(vtile + (lane + 64 * j) * 16);
-    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (KV == PKV_I8) {
-      ksc = *reinterpret_cast<const f32x4*>(a.k_scale + row0 + 4 * c16);
-      vsc = *reinterpret_cast<const f32x4*>(a.v_scale + row0 + 4 * c16);
-    }
-
-    // ---- V tile -> LDS (as MFMA elements), tail rows zeroed ----
+    // V tile -> LDS (as MFMA elements); rows past the context are zeroed (only
+    // a sequence's last tile has such rows: the test is uniform).
+    const bool full = n_valid == 16;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int chunk = lane + 64 * j;
@@ -280,17 +324,17 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       const int col = ((chunk * 16) % R) / eb;   // element column
       uint32_t w[WPC];
       C::run(vraw[j], w);
-      if (row >= n_valid) {
+      if (!full && row >= n_valid) {
 #pragma unroll
         for (int o = 0; o < WPC; ++o) w[o] = 0u;
       }
-      uint8_t* dst = lds_v + row * LDS_ROW + col * mtb;
+      uint8_t* dst = lbuf + row * LDS_ROW + col * mtb;
 #pragma unroll
       for (int o = 0; o < WPC; o += 4)
         *reinterpret_cast<u32x4*>(dst + o * 4) = u32x4{w[o], w[o + 1], w[o + 2], w[o + 3]};
     }
 
-    // ---- S^T = K Q^T ----
+    // S^T = K Q^T
     uint32_t kop[KW];
 #pragma unroll
     for (int j = 0; j < NL; ++j) C::run(kraw[j], kop + j * WPC);
@@ -317,7 +361,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         s = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[c]), s, 0, 0, 0);
     }
 
-    // ---- online softmax (lane: tokens 4*c16 + i of head r16) ----
+    // Online softmax (lane: tokens 4*c16 + i of head r16).
     float z[4];
     float mx = -__builtin_inff();
 #pragma unroll
@@ -332,32 +376,36 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
     const bool live = m_new != -__builtin_inff();
-    const float alpha = live ? exp2f(m_run - m_new) : 1.0f;
+    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may
+    // flush to zero, which only drops weights under 1e-38 of the largest.
+    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     float p[4];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = (live && z[i] != -__builtin_inff()) ? exp2f(z[i] - m_new) : 0.f;
+      p[i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
       psum += p[i];
     }
     l_run = l_run * alpha + psum;
     m_run = m_new;
+    // Rescale only when some head's running max moved (alpha == 1 elsewhere
+    // leaves the values unchanged, so the result is the same either way).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
+      for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
+    }
     if constexpr (KV == PKV_I8) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] / vsc[i] : 0.f;
     }
 
-    __syncthreads();   // V tile visible in LDS
-
-    // ---- O^T += V^T P^T ----
+    // O^T += V^T P^T (V read back from LDS, transposed).
     if constexpr (MT == MT_F32) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float v = *reinterpret_cast<const float*>(lds_v + (4 * c16 + i) * LDS_ROW +
+          const float v = *reinterpret_cast<const float*>(lbuf + (4 * c16 + i) * LDS_ROW +
                                                           (nc * 16 + r16) * 4);
           acc[nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[i], acc[nc], 0, 0, 0);
         }
@@ -366,7 +414,7 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
       const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
-        const uint8_t* src = lds_v + (4 * c16) * LDS_ROW + (nc * 16 + r16) * 2;
+        const uint8_t* src = lbuf + (4 * c16) * LDS_ROW + (nc * 16 + r16) * 2;
         const uint32_t v0 = *reinterpret_cast<const uint16_t*>(src);
         const uint32_t v1 = *reinterpret_cast<const uint16_t*>(src + LDS_ROW);
         const uint32_t v2 = *reinterpret_cast<const uint16_t*>(src + 2 * LDS_ROW);
@@ -383,7 +431,26 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
         }
       }
     }
-    __syncthreads();   // reads done before the next tile overwrites LDS
+  };
+
+  // Steady state without branches around the loads (a load issued on one path
+  // only would make the wait counts conservative), then a one- or two-tile tail.
+  u32x4 ka[NL], va[NL], kb[NL], vb[NL];
+  f32x4 ksa = {1.f, 1.f, 1.f, 1.f}, vsa = ksa, ksb = ksa, vsb = ksa;
+  issue(0, ka, va, ksa, vsa);
+  int tile = 0;
+  for (; tile + 2 < ntiles; tile += 2) {
+    issue(tile + 1, kb, vb, ksb, vsb);
+    compute(tile, ka, va, ksa, vsa, lds_v);
+    issue(tile + 2, ka, va, ksa, vsa);
+    compute(tile + 1, kb, vb, ksb, vsb, lds_v + LDS_TILE);
+  }
+  if (tile + 1 < ntiles) {
+    issue(tile + 1, kb, vb, ksb, vsb);
+    compute(tile, ka, va, ksa, vsa, lds_v);
+    compute(tile + 1, kb, vb, ksb, vsb, lds_v + LDS_TILE);
+  } else {
+    compute(tile, ka, va, ksa, vsa, lds_v);
   }
 
   // ---- epilogue ----
@@ -410,10 +477,16 @@ __global__ __launch_bounds__(64) void decode_partition_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of partitions: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// One wave per (query head, sequence).
+// One wave per (query head, sequence).  D/4 lanes cover one partial's output
+// row with 16-byte loads, so one load instruction takes 64/(D/4) partials at
+// once; the loop is unrolled so several such loads are in flight.  The lane
+// groups' sums are added at the end in a fixed order (results do not depend on
+// timing).
 // ---------------------------------------------------------------------------
 template <int QT, int D>
 __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+  constexpr int LPP = D / 4;          // lanes per partial row
+  constexpr int PPI = kWave / LPP;    // partials per load instruction
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
@@ -428,27 +501,30 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
   float M = -__builtin_inff();
   for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
   M = wave_max(M);
-
-  constexpr int PER = D / kWave;   // 1 or 2 output elements per lane
-  float o[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) o[e] = 0.f;
   float L = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float w = exp2f(ml[2 * p] - M);
-    L += w * ml[2 * p + 1];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] += w * accp[(int64_t)p * D + lane * PER + e];
+  for (int p = lane; p < nparts; p += kWave) L += exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+  L = wave_sum(L);
+
+  const int grp = lane / LPP;        // which partial of an instruction
+  const int dq = lane % LPP;         // which 4 output elements
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int p0 = 0; p0 < nparts; p0 += PPI) {
+    const int p = p0 + grp;
+    if (p < nparts) {
+      const float w = exp2f(ml[2 * p] - M);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(accp + (int64_t)p * D + 4 * dq);
+      o += w * v;
+    }
   }
+#pragma unroll
+  for (int off = LPP; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] += __shfl_xor(o[i], off, kWave);
+  }
+  if (grp != 0) return;
   const float inv = 1.0f / L;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const float v = o[e] * inv;
-    const int64_t idx = hq * D + lane * PER + e;
-    if constexpr (QT == PKV_F32) static_cast<float*>(a.out)[idx] = v;
-    else if constexpr (QT == PKV_F16) static_cast<uint16_t*>(a.out)[idx] = f32_to_f16(v);
-    else static_cast<uint16_t*>(a.out)[idx] = f32_to_bf16(v);
-  }
+  store_out4<QT>(a.out, hq * D + 4 * dq, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
 // ---------------------------------------------------------------------------

@@ -9,8 +9,10 @@ whose append has not happened yet shows up in the output.  The slot of each
 sequence's newest token is poisoned too when the workload appends it, so a
 missing append is visible.
 
-``to_host`` copies the stored bytes back for the CPU reference: the reference
-always sees exactly the bytes the kernels read.
+With ``keep_sources=True`` the seeded source pools (before quantization and
+poisoning) are also kept as host tensors, so a checker can build its own stored
+cache from the same draws instead of reading the library's output.
+``to_host`` copies the stored bytes back (used to time a CPU reference on them).
 """
 import numpy as np
 import torch
@@ -34,7 +36,7 @@ def poison_mask(w):
 class DeviceCase:
     """Device tensors of one layer of a workload."""
 
-    def __init__(self, w, device="cuda", layer=0, mask=None):
+    def __init__(self, w, device="cuda", layer=0, mask=None, keep_sources=False):
         self.w = w
         self.layer = layer
         self.device = device
@@ -47,8 +49,11 @@ class DeviceCase:
         self.out = torch.empty_like(self.q)
         self.k_scale = self.v_scale = None
         caches, scales = [], []
+        self.sources = {}
         for which in ("k", "v"):
             src = W.pool_source(w, which, device, layer)
+            if keep_sources:
+                self.sources[which] = src.cpu()
             if w.kv_format in ("f32", "f16", "bf16"):
                 src.permute(0, 2, 1, 3)[mask_t] = float("nan")
                 caches.append(src)

@@ -1,5 +1,18 @@
-"""Shared pieces of the GPU tests: run the library on a workload, run the CPU
-oracle on the same stored bytes, compare element by element."""
+"""Shared pieces of the GPU tests.
+
+The library side: a ``DeviceCase`` (seeded sources drawn on the device, stored
+through the library's ``kv_quantize`` for INT8/FP8, unused slots poisoned), then
+``kv_cache_append`` and ``paged_attention_decode`` through the C ABI.
+
+The oracle side (``OracleSide``) never reads anything the library wrote: it
+takes host copies of the same seeded draws (sources, query, appended rows),
+stores them with the oracle's own quantizers, writes the appended rows with the
+oracle's own append, and attends over that.  Large cases keep only the sampled
+sequences' blocks, in a compact pool with a remapped block table (bookkeeping
+only; the oracle's arithmetic is unchanged).  The library's stored bytes at
+every live slot of those sequences are then compared bit for bit with the
+oracle's, and the attention outputs element by element.
+"""
 import sys
 
 import numpy as np
@@ -7,7 +20,7 @@ import torch
 
 import oracle
 import paged_kv_cache_435_amd as pkv
-from paged_kv_cache_435_amd.device_cache import DeviceCase, to_host
+from paged_kv_cache_435_amd.device_cache import DeviceCase
 
 # Parity bar (|gpu - ref| <= atol + rtol * |ref|).  fp16/bf16 KV: 2e-2 abs /
 # 1e-2 rel; INT8/FP8 KV: 5e-2 abs and rel against the oracle on the same stored
@@ -17,10 +30,125 @@ from paged_kv_cache_435_amd.device_cache import DeviceCase, to_host
 TOL = {"f32": (1e-5, 1e-5), "f16": (2e-2, 1e-2), "bf16": (2e-2, 1e-2),
        "i8": (5e-2, 5e-2), "fp8": (5e-2, 5e-2)}
 
+_FMT_OF = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16"}
+
 
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def storage(t):
+    """CPU tensor -> numpy array in the form the oracle reads (bf16 as uint16 bits)."""
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen32(t):
+    """f32/f16/bf16 CPU tensor -> float32 numpy, through the oracle's exact widening."""
+    return oracle.widen.widen_plain(storage(t), _FMT_OF[t.dtype]).astype(np.float32)
+
+
+def compact_blocks(w, seqs, context_lens=None):
+    """Physical blocks live for ``seqs`` (in table order) and a block table over
+    a compact pool that holds just those blocks."""
+    ctx = w.context_lens if context_lens is None else np.asarray(context_lens)
+    blocks = []
+    tables = np.full((len(seqs), max(w.block_tables.shape[1], 1)), -1, dtype=np.int32)
+    for i, b in enumerate(seqs):
+        for j in range(-(-int(ctx[b]) // w.block_size)):
+            tables[i, j] = len(blocks)
+            blocks.append(int(w.block_tables[b, j]))
+    return np.array(blocks, dtype=np.int64), tables
+
+
+class OracleSide:
+    """The oracle's stored cache and query for ``seqs`` of a workload, built from
+    host copies of the seeded draws in ``case`` (made with keep_sources=True)."""
+
+    def __init__(self, w, case, seqs=None, context_lens=None):
+        seqs = list(range(w.batch)) if seqs is None else sorted(int(b) for b in seqs)
+        ctx_all = w.context_lens if context_lens is None else np.asarray(context_lens)
+        self.seqs = seqs
+        self.blocks, self.tables = compact_blocks(w, seqs, ctx_all)
+        self.context_lens = ctx_all[seqs].astype(np.int32)
+        self.fmt = w.kv_format
+        self.block_size = w.block_size
+        self.scale = w.scale
+        self.q = widen32(case.q.cpu()[seqs]).astype(np.float64)
+        idx = torch.from_numpy(self.blocks)
+        self.k_scale = self.v_scale = None
+        stored, scales = [], []
+        for which in ("k", "v"):
+            full = case.sources[which]
+            sub = full[idx]
+            if self.fmt in ("f32", "f16", "bf16"):
+                stored.append(storage(sub))
+                scales.append(None)
+            elif self.fmt == "i8":
+                codes, s = oracle.quantize_int8_rows(widen32(sub))
+                stored.append(codes)
+                scales.append(s)
+            else:
+                # One scale over the whole tensor: max|x| (exact in the source
+                # format) handed to the oracle, which divides by 448.
+                amax = (np.abs(widen32(full)).max() if full.dtype == torch.bfloat16
+                        else np.abs(full.numpy()).max())
+                s = oracle.fp8_tensor_scale(np.array([amax], dtype=np.float32))
+                codes, s = oracle.quantize_fp8(widen32(sub), scale=s)
+                stored.append(codes)
+                scales.append(s)
+        k, v = stored
+        ks, vs = scales
+        if w.appends:
+            pos = self.context_lens.astype(np.int64) - 1
+            slots = np.array([oracle.paging.slot_of(self.tables[i], int(pos[i]), self.block_size)
+                              for i in range(len(seqs))], dtype=np.int64)
+            nk, nv = case.new_k.cpu()[seqs], case.new_v.cpu()[seqs]
+            k, v, ks, vs = oracle.append.append_expected(
+                k, v, storage(nk), storage(nv), slots, self.block_size, self.fmt, ks, vs,
+                src_format=_FMT_OF[nk.dtype])
+        self.k_cache, self.v_cache, self.k_scale, self.v_scale = k, v, ks, vs
+
+    def live_mask(self):
+        """bool [compact blocks][bs]: slots holding a live token."""
+        m = np.zeros((len(self.blocks), self.block_size), dtype=bool)
+        for i, c in enumerate(self.context_lens):
+            for j in range(-(-int(c) // self.block_size)):
+                n = min(self.block_size, int(c) - j * self.block_size)
+                m[self.tables[i, j], :n] = True
+        return m
+
+    def attention(self):
+        return oracle.decode_attention(self.q, self.k_cache, self.v_cache, self.tables,
+                                       self.context_lens, self.scale, self.block_size, self.fmt,
+                                       self.k_scale, self.v_scale)
+
+
+def check_stored(case, side, what=""):
+    """The library's stored bytes (and INT8/FP8 scales) at every live slot of the
+    sampled sequences equal the oracle's, bit for bit."""
+    if len(side.blocks) == 0:
+        return
+    idx = torch.from_numpy(side.blocks).to(case.k_cache.device)
+    live = side.live_mask()
+    for name, dev, ref in (("K", case.k_cache, side.k_cache), ("V", case.v_cache, side.v_cache)):
+        got = storage(dev[idx].cpu())
+        g = got.transpose(0, 2, 1, 3)[live].view(np.uint8)
+        r = ref.transpose(0, 2, 1, 3)[live].view(np.uint8)
+        bad = int((g != r).sum())
+        assert bad == 0, f"{what}: stored {name} differs from the oracle's in {bad} bytes"
+    if side.fmt == "i8":
+        for name, dev, ref in (("K", case.k_scale, side.k_scale), ("V", case.v_scale, side.v_scale)):
+            g = dev[idx].cpu().numpy().transpose(0, 2, 1)[live].view(np.uint32)
+            r = ref.transpose(0, 2, 1)[live].view(np.uint32)
+            assert np.array_equal(g, r), f"{what}: INT8 {name} scales differ"
+    elif side.fmt == "fp8":
+        for name, dev, ref in (("K", case.k_scale, side.k_scale), ("V", case.v_scale, side.v_scale)):
+            assert np.float32(dev.item()).view(np.uint32) == np.float32(ref).view(np.uint32), \
+                f"{what}: FP8 {name} tensor scale differs"
 
 
 def append_and_decode(case, max_context_len=None):
@@ -38,31 +166,27 @@ def append_and_decode(case, max_context_len=None):
     return case.out.float().cpu().numpy().astype(np.float64)
 
 
-def oracle_out(case, pairs=None):
-    h = to_host(case)
-    return oracle.decode_attention(h["q"], h["k_cache"], h["v_cache"], h["block_tables"],
-                                   h["context_lens"], h["scale"], h["block_size"], h["kv_format"],
-                                   h["k_scale"], h["v_scale"], pairs=pairs)
-
-
-def compare(got, ref, fmt, what="", pairs=None):
+def compare(got, ref, fmt, what=""):
     atol, rtol = TOL[fmt]
-    if pairs is not None:
-        idx = tuple(np.array(pairs).T)
-        got, ref = got[idx], ref[idx]
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
-    say(f"  {what}: max|err| = {err.max():.3e}, max|ref| = {np.abs(ref).max():.3e}, "
+    say(f"  {what}: max|err| = {err.max() if err.size else 0:.3e}, "
+        f"max|ref| = {np.abs(ref).max() if ref.size else 0:.3e}, "
         f"{err.size} elements, {int(bad.sum())} outside tolerance")
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside (atol={atol}, rtol={rtol})"
-    return float(err.max())
+    return float(err.max()) if err.size else 0.0
 
 
-def run_and_check(w, pairs=None, layer=0):
+def run_and_check(w, seqs=None, layer=0):
+    """Library append + decode on ``w`` vs the oracle on ``seqs`` (all by default)."""
     say(f"[case] {w.name} fmt={w.kv_format} q={w.q_dtype} B={w.batch} Hq={w.num_q_heads} "
-        f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.block_size} ctx_max={w.max_context_len}")
-    case = DeviceCase(w, layer=layer)
+        f"Hkv={w.num_kv_heads} d={w.head_dim} bs={w.block_size} ctx_max={w.max_context_len} "
+        f"layer={layer} seqs={'all' if seqs is None else sorted(seqs)}")
+    case = DeviceCase(w, layer=layer, keep_sources=True)
     got = append_and_decode(case)
-    ref = oracle_out(case, pairs)
-    return compare(got, ref, w.kv_format, w.name, pairs), case, got
+    side = OracleSide(w, case, seqs)
+    check_stored(case, side, w.name)
+    ref = side.attention()
+    err = compare(got[side.seqs], ref, w.kv_format, w.name)
+    return err, case, got
