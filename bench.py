@@ -142,10 +142,10 @@ def main():
     torch.cuda.synchronize()
 
     mcl = w.max_context_len
-    ws_bytes = pkv.paged_attention_workspace_size(w.batch, w.num_q_heads, w.head_dim, mcl)
+    ws_bytes = pkv.paged_attention_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads,
+                                                  w.head_dim, mcl)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kv_dtype = cases[0].kv_dtype
-    part = pkv.partition_tokens(w.batch, w.num_q_heads, w.num_kv_heads, w.block_size, mcl)
 
     def step(events=None):
         for c in cases:
@@ -162,7 +162,7 @@ def main():
                 e1.record()
                 events.append((e0, e1))
 
-    log(f"[bench] warmup {args.warmup} steps (partition {part} tokens, workspace {ws_bytes} B)")
+    log(f"[bench] warmup {args.warmup} steps (workspace {ws_bytes} B)")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -242,7 +242,7 @@ def main():
                    "q_dtype": str(w.q_dtype).replace("torch.", ""),
                    "sum_context_tokens": int(w.context_lens.sum()),
                    "max_context_len": mcl, "pool_blocks": w.num_blocks,
-                   "partition_tokens": part, "appends_per_step": bool(w.appends)},
+                   "appends_per_step": bool(w.appends)},
         "kv_gbps": achieved,
         "kv_pct_of_peak": achieved / HBM_PEAK_GBPS * 100.0,
         "read_ceiling_gbps": ceiling,

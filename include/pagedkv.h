@@ -126,10 +126,13 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
 
 /*
  * paged_attention_workspace_size — bytes of device scratch paged_attention_decode
- * needs for these sizes (partial softmax state of split contexts).  Host only.
+ * needs for these sizes (partial softmax state of contexts split over several
+ * waves; sized for up to 256 compute units x 12 resident waves).  Host only, no
+ * device needed.  0 when no context can be split (max_context_len <= 256) or
+ * the sizes are invalid.
  */
-size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                      int32_t max_context_len);
+size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len);
 
 /*
  * paged_attention_decode — one decode step: for every sequence b and query head
@@ -142,7 +145,8 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *   out[b][h] = sum_t softmax_t(scale * <q[b][h], K_t>) * V_t
  *
  *   out, q        device, [batch][num_q_heads][head_dim] in q_dtype
- *                 (PKV_F32 / PKV_F16 / PKV_BF16), contiguous; out may not alias q.
+ *                 (PKV_F32 / PKV_F16 / PKV_BF16), contiguous, 16-byte aligned;
+ *                 out may not alias q.
  *   k_cache, v_cache  device, cache layout above, kv_dtype = q_dtype, PKV_I8 or
  *                 PKV_FP8_E4M3FN.  Dequantized values: INT8 code / scale
  *                 (the inverse of [P1] §4's quantizer); FP8 decode(code) * scale.
@@ -153,8 +157,9 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *   max_context_len  host int: an upper bound of context_lens (sizes the grid).
  *   scale         softmax scale (1/sqrt(head_dim) for the usual attention).
  *   workspace     device scratch of at least paged_attention_workspace_size(...)
- *                 bytes (may be NULL when that size is 0); contents are
- *                 overwritten.  Calls that share a workspace must be ordered.
+ *                 bytes, 256-byte aligned (may be NULL when that
+ *                 size is 0); contents are overwritten.  Calls that share a
+ *                 workspace must be ordered.
  *   Supported: head_dim 64 or 128; block_size 16 or 256; num_q_heads a multiple
  *   of num_kv_heads.
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
@@ -167,14 +172,6 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
                                   int32_t max_context_len, float scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
-
-/*
- * pkv_partition_tokens — context tokens one workgroup of paged_attention_decode
- * handles for these sizes (longer contexts are split and merged in a second
- * pass).  Host only; informational.  Returns 0 for unsupported sizes.
- */
-int32_t pkv_partition_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t block_size, int32_t max_context_len);
 
 #ifdef __cplusplus
 }

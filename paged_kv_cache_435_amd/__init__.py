@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "kv_quantize", "kv_cache_append", "paged_attention_decode",
-    "paged_attention_workspace_size", "kv_cache_bytes", "partition_tokens",
+    "paged_attention_workspace_size", "kv_cache_bytes",
     "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8",
     "PKV_FP8_E4M3FN", "EXPORTED_SYMBOLS",
 ]
@@ -25,7 +25,7 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "pkv_last_error", "kv_cache_bytes", "kv_quantize", "kv_cache_append",
-    "paged_attention_workspace_size", "paged_attention_decode", "pkv_partition_tokens",
+    "paged_attention_workspace_size", "paged_attention_decode",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,12 +58,10 @@ def load_library():
     lib.kv_cache_append.restype = I32
     lib.kv_cache_append.argtypes = [P, P, I32, I32, P, P, P, P, P, I32, I32, I32, I32, I32, P]
     lib.paged_attention_workspace_size.restype = SZ
-    lib.paged_attention_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.paged_attention_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.paged_attention_decode.restype = I32
     lib.paged_attention_decode.argtypes = [P, P, I32, I32, I32, P, P, P, P, I32, I32, I32, I32,
                                            I32, P, I32, P, I32, F, P, SZ, P]
-    lib.pkv_partition_tokens.restype = I32
-    lib.pkv_partition_tokens.argtypes = [I32, I32, I32, I32, I32]
     _LIB = lib
     return lib
 
@@ -115,14 +113,10 @@ def kv_cache_bytes(batch, seq_len, layers, kv_heads, head_dim, dtype_bytes):
     return int(load_library().kv_cache_bytes(batch, seq_len, layers, kv_heads, head_dim, dtype_bytes))
 
 
-def paged_attention_workspace_size(batch, num_q_heads, head_dim, max_context_len):
-    return int(load_library().paged_attention_workspace_size(batch, num_q_heads, head_dim,
-                                                             max_context_len))
-
-
-def partition_tokens(batch, num_q_heads, num_kv_heads, block_size, max_context_len):
-    return int(load_library().pkv_partition_tokens(batch, num_q_heads, num_kv_heads, block_size,
-                                                   max_context_len))
+def paged_attention_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, max_context_len):
+    """Bytes of workspace paged_attention_decode needs on the current device."""
+    return int(load_library().paged_attention_workspace_size(batch, num_q_heads, num_kv_heads,
+                                                             head_dim, max_context_len))
 
 
 def kv_quantize(x, out, scale, scale_given=False, out_dtype=None, stream=None):
@@ -187,7 +181,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise ValueError("out must match q, and the cache's head_dim must match q's")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables must be [B][MB] and context_lens [B]")
-    need = lib.paged_attention_workspace_size(B, Hq, d, int(max_context_len))
+    need = lib.paged_attention_workspace_size(B, Hq, Hkv, d, int(max_context_len))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()

@@ -1,8 +1,10 @@
-// pkv_api.hip — the C ABI: argument checks, partition choice, workspace sizing,
-// dispatch, and the per-thread error text.  Declarations and the meaning of every
+// pkv_api.hip — the C ABI: argument checks, workspace sizing for the decode
+// work plan, dispatch, and the per-thread error text.  Declarations and the meaning of every
 // argument are in include/pagedkv.h.
 #include <stdlib.h>
 
+#include <map>
+#include <mutex>
 #include <string>
 
 #include "pkv_common.h"
@@ -31,34 +33,37 @@ bool aligned(const void* p, size_t n) { return (reinterpret_cast<uintptr_t>(p) %
 
 bool is_float_dtype(int32_t d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
 
-// Smallest partition the decode path uses; the workspace is sized for it.
-constexpr int kMinPartition = 256;
-
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tokens per decode workgroup.  512 keeps the per-partition state (<2% of the
-// KV bytes it summarises) small while giving thousands of workgroups at the
-// long-context shapes; short contexts with few (sequence, head) pairs drop to
-// 256 to fill the 256 compute units.  PKV_PARTITION overrides it (tuning).
-int choose_partition(int32_t batch, int32_t num_kv_heads, int32_t head_tiles, int32_t block_size,
-                     int32_t max_context_len) {
-  const char* env = getenv("PKV_PARTITION");
-  if (env) {
-    const int v = atoi(env);
-    if (v >= kMinPartition && v <= 1024 && v % block_size == 0 && v / block_size <= 64) return v;
-  }
-  int p = 512;
-  const int64_t units = (int64_t)batch * num_kv_heads * head_tiles * ceil_div(max_context_len, p);
-  if (units < 2048) p = 256;
-  if (p % block_size != 0) p = block_size;
-  return p;
+// Compute units of the current device (cached per device; host query only).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  cache[dev] = cus;
+  return cus;
 }
 
-size_t workspace_bytes_for(int64_t batch, int64_t num_q_heads, int64_t head_dim, int64_t max_parts) {
-  if (max_parts <= 1) return 0;
-  const int64_t rows = batch * num_q_heads * max_parts;
-  const int64_t ml = ((rows * 2 * 4) + 255) / 256 * 256;
-  return (size_t)(ml + rows * head_dim * 4);
+// Workspace rows hold one (max, sum) pair and one head_dim-long output per
+// (item, head of its 16-head tile).
+int64_t row_bytes(int64_t head_dim) { return 16 * (2 + head_dim) * 4; }
+
+// Items the plan can make for these sizes when it plans for the largest slot
+// count (kMaxSlots; a device with fewer resident waves makes fewer items).
+// 0 when every unit fits one item (contexts of at most kItemTilesMin tiles):
+// no workspace is needed then.
+int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads,
+                        int64_t max_context_len) {
+  if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
+  const int64_t units = num_kv_heads * ceil_div(num_q_heads / num_kv_heads, 16);
+  return pkv::max_items_bound(batch, units, max_context_len, pkv::kMaxSlots);
 }
 
 }  // namespace
@@ -76,19 +81,13 @@ uint64_t kv_cache_bytes(uint64_t batch, uint64_t seq_len, uint64_t layers, uint6
   return r;
 }
 
-int32_t pkv_partition_tokens(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                             int32_t block_size, int32_t max_context_len) {
-  if (batch < 0 || num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads ||
-      (block_size != 16 && block_size != 256) || max_context_len < 0)
+size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, int32_t max_context_len) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      head_dim <= 0 || max_context_len <= 0)
     return 0;
-  const int32_t tiles = (num_q_heads / num_kv_heads + 15) / 16;
-  return choose_partition(batch, num_kv_heads, tiles, block_size, max_context_len);
-}
-
-size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                      int32_t max_context_len) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  return workspace_bytes_for(batch, num_q_heads, head_dim, ceil_div(max_context_len, kMinPartition));
+  return (size_t)(workspace_items(batch, num_q_heads, num_kv_heads, max_context_len) *
+                  row_bytes(head_dim));
 }
 
 pkv_status kv_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t row_len,
@@ -174,19 +173,18 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
     return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer");
   if ((kv_dtype == PKV_I8 || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: quantized cache needs k_scale and v_scale");
-  if (!aligned(out, 16) || !aligned(q, 4) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
       (kv_dtype == PKV_I8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: misaligned pointer (caches/out need 16 B, INT8 scales 16 B)");
+                "paged_attention_decode: misaligned pointer (q, out, caches and INT8 scales need 16 B)");
 
   const int32_t G = num_q_heads / num_kv_heads;
   const int32_t head_tiles = (G + 15) / 16;
-  if ((int64_t)num_kv_heads * head_tiles > 65535)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: too many KV heads");
-  const int part = choose_partition(batch, num_kv_heads, head_tiles, block_size, max_context_len);
-  const int64_t max_parts = max_context_len > 0 ? ceil_div(max_context_len, part) : 1;
-  const size_t need = workspace_bytes_for(batch, num_q_heads, head_dim, max_parts);
+  const int64_t items = workspace_items(batch, num_q_heads, num_kv_heads, max_context_len);
+  if (items > 0x7FFFFFF0)
+    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: batch x heads x context too large");
+  const size_t need = (size_t)(items * row_bytes(head_dim));
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "paged_attention_decode: workspace needs " +
                                        std::to_string(need) + " bytes, got " +
@@ -210,16 +208,15 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.ctx_cap = max_context_len;
-  a.part_tokens = part;
-  a.max_parts = (int32_t)max_parts;
+  a.max_items = (int32_t)items;
   a.scale = scale;
+  const int cus = device_cus();
+  if (cus <= 0) return fail(PKV_ERR_HIP, "paged_attention_decode: cannot query the device");
   if (need > 0) {
-    const int64_t rows = (int64_t)batch * num_q_heads * max_parts;
-    const int64_t ml = ((rows * 2 * 4) + 255) / 256 * 256;
     a.ws_ml = static_cast<float*>(workspace);
-    a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ml);
+    a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + items * 16 * 2 * 4);
   }
-  return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, (int)max_parts,
+  return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, cus,
                                        static_cast<hipStream_t>(stream)),
                     "paged_attention_decode");
 }

@@ -7,23 +7,27 @@
 // sequence's block table.  The pages run this on NVIDIA parts with vLLM's kernel;
 // the design here is for CDNA4:
 //
-//  * One 64-lane wave per (sequence, KV head, tile of up to 16 query heads of
-//    that KV head's group, context partition).  The KV rows are read from HBM
-//    once per KV head and shared by the whole query group.
+//  * One 64-lane wave per work item: a run of 16-token tiles of one (sequence,
+//    KV head, tile of up to 16 query heads of that KV head's group) unit.  The
+//    KV rows are read from HBM once per KV head and shared by the whole query
+//    group.  Every wave plans the cut itself from the device-resident context
+//    lengths, so that one round of near-equal items fills the waves the GPU
+//    runs at once (ragged batches otherwise leave a tail of stragglers).
+//    Items are dealt to the 8 XCDs in contiguous ranges.
 //  * Tokens go 16 at a time.  QK^T is one MFMA chain per 16 tokens:
 //    S^T[16 tok][16 heads] = K[16 tok][d] * Q^T[d][16 heads]
 //    (v_mfma_f32_16x16x32_{f16,bf16}, or 16x16x4 for f32).  K is loaded from HBM
 //    straight into the A-operand layout (16 B per lane, 64 contiguous bytes per
-//    row per instruction); Q sits in registers for the whole partition.
+//    row per instruction); Q sits in registers for the whole item.
 //  * Online softmax in the exp2 domain on the MFMA output registers.  A lane
 //    holds 4 tokens of one head, so a head's max needs two cross-lane steps.
 //  * PV as O^T[d][heads] += V^T[d][16 tok] * P^T[16 tok][heads]
 //    (v_mfma_f32_16x16x16).  P^T is exactly the QK output layout, so P never
 //    leaves its registers.  V is staged through LDS (coalesced 16 B/lane
 //    writes) and read back transposed.
-//  * Long contexts are split into partitions of P tokens; each wave writes its
-//    (max, sum, unnormalised output) and a second kernel merges them with the
-//    log-sum-exp rule.  A sequence that fits one partition is finished in place.
+//  * A unit cut into several items gets (max, sum, unnormalised output) per
+//    item, merged by a second kernel with the log-sum-exp rule.  A unit that is
+//    one item is finished in place.
 //  * Tokens past the context are selected out (never multiplied), and their V
 //    rows are zeroed in LDS, so stale or NaN bytes in unused slots never reach
 //    the sums.
@@ -152,6 +156,135 @@ __device__ __forceinline__ uint32_t pack_p(float a, float b) {
 }
 
 // ---------------------------------------------------------------------------
+// Work plan (computed identically by every wave of both kernels).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int64_t t = __shfl_up(v, o, kWave);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), lane);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Context length of sequence b, clamped to what the table can address.
+__device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int b) {
+  int c = a.context_lens[b];
+  return c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
+}
+
+struct Plan {
+  int64_t items;   // total work items
+  int tpi;         // tiles per item (a unit of n tiles makes ceil(n / tpi) items)
+};
+
+// Tiles per item: about (total tiles) / (slots - units), so that one round of
+// items fills the slots even after each unit's count is rounded up; several
+// equal rounds when an item would pass kItemTilesMax.
+__device__ Plan make_plan(const DecodeArgs& a, int lane) {
+  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
+  int64_t tiles = 0, live = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+    const int b = b0 + lane;
+    const int n = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+    tiles += n;
+    live += n > 0;
+  }
+  tiles = wave_sum_i64(tiles) * units_per_seq;
+  live = wave_sum_i64(live) * units_per_seq;
+  int64_t slots = a.slots - live;
+  if (slots < a.slots / 2) slots = a.slots / 2;
+  if (slots < 1) slots = 1;
+  int64_t k = (tiles + slots * kItemTilesMax - 1) / (slots * kItemTilesMax);
+  if (k < 1) k = 1;
+  int64_t tpi = (tiles + k * slots - 1) / (k * slots);
+  tpi = tpi < kItemTilesMin ? kItemTilesMin : (tpi > kItemTilesMax ? kItemTilesMax : tpi);
+  int64_t items = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+    const int b = b0 + lane;
+    const int n = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+    items += (n + tpi - 1) / tpi;
+  }
+  Plan p;
+  p.items = wave_sum_i64(items) * units_per_seq;
+  p.tpi = (int)tpi;
+  return p;
+}
+
+// Items of a sequence are numbered g-major, then by chunk, then by head tile:
+// item = first + (g * m + c) * head_tiles + ht, with m = ceil(n / tpi) chunks of
+// the sequence's n tiles per unit; chunk c covers tiles [c*n/m, (c+1)*n/m).
+struct SeqItems {
+  int64_t first;   // number of the sequence's first item
+  int ctx;         // clamped context length
+  int n;           // tiles
+  int m;           // chunks per unit
+};
+
+// The sequence holding item q (found = false if q is past the last item).
+__device__ bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int lane,
+                            int& b_out, SeqItems& s) {
+  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
+    const int b = b0 + lane;
+    const int ctx = b < a.batch ? seq_ctx(a, b) : 0;
+    const int n = (ctx + kTileTokens - 1) / kTileTokens;
+    const int m = (n + p.tpi - 1) / p.tpi;
+    const int64_t cnt = (int64_t)m * units_per_seq;
+    const int64_t incl = wave_incl_scan_i64(cnt, lane) + base;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(q >= incl - cnt && q < incl);
+    if (hit) {
+      const int L = __builtin_ctzll(hit);
+      b_out = b0 + L;
+      s.first = readlane_i64(incl - cnt, L);
+      s.ctx = __builtin_amdgcn_readlane(ctx, L);
+      s.n = __builtin_amdgcn_readlane(n, L);
+      s.m = __builtin_amdgcn_readlane(m, L);
+      return true;
+    }
+    base = readlane_i64(incl, kWave - 1);
+  }
+  return false;
+}
+
+// The item range of sequence b.
+__device__ SeqItems items_of_seq(const DecodeArgs& a, const Plan& p, int b, int lane) {
+  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
+  int64_t base = 0;
+  SeqItems s{};
+  for (int b0 = 0; b0 <= b; b0 += kWave) {
+    const int bb = b0 + lane;
+    const int ctx = bb < a.batch ? seq_ctx(a, bb) : 0;
+    const int n = (ctx + kTileTokens - 1) / kTileTokens;
+    const int m = (n + p.tpi - 1) / p.tpi;
+    const int64_t cnt = (int64_t)m * units_per_seq;
+    const int64_t incl = wave_incl_scan_i64(cnt, lane) + base;
+    if (b < b0 + kWave) {
+      const int L = b - b0;
+      s.first = readlane_i64(incl - cnt, L);
+      s.ctx = __builtin_amdgcn_readlane(ctx, L);
+      s.n = __builtin_amdgcn_readlane(n, L);
+      s.m = __builtin_amdgcn_readlane(m, L);
+    }
+    base = readlane_i64(incl, kWave - 1);
+  }
+  return s;
+}
+
+// ---------------------------------------------------------------------------
 // Partition kernel.
 //
 // The tile loop is software-pipelined two deep: while tile i is converted and
@@ -194,18 +327,31 @@ void decode_partition_kernel(DecodeArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * LDS_TILE];
 
-  const int part = blockIdx.x;
-  const int g = blockIdx.y / a.head_tiles;
-  const int ht = blockIdx.y % a.head_tiles;
-  const int b = blockIdx.z;
   const int lane = threadIdx.x;
   const int r16 = lane & 15;   // MFMA row/column index of this lane
   const int c16 = lane >> 4;   // MFMA k-group of this lane
 
-  int ctx = a.context_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (part >= (nparts > 0 ? nparts : 1)) return;
+  // ---- which item: contiguous item ranges per XCD (workgroups go round-robin
+  // over the 8 XCDs, so blockIdx % 8 is the XCD) ----
+  const Plan plan = make_plan(a, lane);
+  const int64_t per_xcd = (plan.items + 7) / 8;
+  const int64_t slot_in_xcd = blockIdx.x / 8;
+  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + slot_in_xcd;
+  if (slot_in_xcd >= per_xcd || item >= plan.items) return;
+  int b;
+  SeqItems sq;
+  if (!seq_of_item(a, plan, item, lane, b, sq)) return;
+  const int64_t local = item - sq.first;
+  const int64_t per_g = (int64_t)sq.m * a.head_tiles;
+  const int g = (int)(local / per_g);
+  const int chunk = (int)((local % per_g) / a.head_tiles);
+  const int ht = (int)(local % a.head_tiles);
+  const int ctx = sq.ctx;
+  const int t_begin = (int)((int64_t)chunk * sq.n / sq.m) * kTileTokens;
+  int t_end = (int)((int64_t)(chunk + 1) * sq.n / sq.m) * kTileTokens;
+  t_end = t_end < ctx ? t_end : ctx;
+  const int ntiles = (t_end - t_begin + 15) >> 4;
+  const bool whole_unit = sq.m == 1;
 
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h_first = g * G + ht * 16;              // first query head of this tile
@@ -214,42 +360,37 @@ void decode_partition_kernel(DecodeArgs a) {
   const bool head_ok = r16 < nh;
   const int64_t hq = (int64_t)b * a.num_q_heads + h_first + r16;   // this lane's head row
 
-  if (ctx == 0) {  // nothing to attend to: defined as zeros
-    if (head_ok) {
+  // Block-table entries of the item, one per lane per register.
+  constexpr int NREG = (kItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
+  const int first_blk = t_begin / BS;
+  const int nblk = (t_end - 1) / BS - first_blk + 1;
+  int blk[NREG];
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc)
-        store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, 0.f, 0.f, 0.f, 0.f);
-    }
-    return;
+  for (int r = 0; r < NREG; ++r) {
+    const int idx = r * 64 + lane;
+    int v = -1;
+    if (idx < nblk) v = a.block_tables[(int64_t)b * a.max_blocks_per_seq + first_blk + idx];
+    blk[r] = (v >= a.num_blocks) ? -1 : v;
   }
 
-  const int t_begin = part * a.part_tokens;
-  const int t_end = (t_begin + a.part_tokens < ctx) ? t_begin + a.part_tokens : ctx;
-  const int ntiles = (t_end - t_begin + 15) >> 4;
-
-  // Block-table entries of this partition, one per lane (part_tokens/BS <= 64).
-  const int first_blk = t_begin / BS;
-  const int nblk = (t_end - t_begin + BS - 1) / BS;
-  int my_blk = -1;
-  if (lane < nblk) my_blk = a.block_tables[(int64_t)b * a.max_blocks_per_seq + first_blk + lane];
-  if (my_blk >= a.num_blocks) my_blk = -1;
-
-  // Query operand: lane holds head r16 at the d positions its K chunks carry.
+  // Query operand: lane holds head r16 at the d positions its K chunks carry
+  // (the same bytes of q in memory order: 16-byte loads).
   uint32_t qop[KW];
 #pragma unroll
   for (int i = 0; i < KW; ++i) qop[i] = 0u;
   if (head_ok) {
+    constexpr int qsize = QT == PKV_F32 ? 4 : 2;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
+      const int d0 = (64 * j + 16 * c16) / eb;
+      const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq * D + d0) * qsize;
 #pragma unroll
-      for (int o = 0; o < WPC; ++o) {
-        if constexpr (MT == MT_F32) {
-          const int d = (64 * j + 16 * c16) / eb + o;
-          qop[j * WPC + o] = q_elem<QT>(a.q, hq * D + d);
-        } else {
-          const int d = (64 * j + 16 * c16) / eb + 2 * o;
-          qop[j * WPC + o] = q_elem<QT>(a.q, hq * D + d) | (q_elem<QT>(a.q, hq * D + d + 1) << 16);
-        }
+      for (int o = 0; o < WPC; o += 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 4 * o);
+        qop[j * WPC + o] = w[0];
+        qop[j * WPC + o + 1] = w[1];
+        qop[j * WPC + o + 2] = w[2];
+        qop[j * WPC + o + 3] = w[3];
       }
     }
   }
@@ -273,7 +414,16 @@ void decode_partition_kernel(DecodeArgs a) {
 
   // Physical block of a tile (-1: outside the pool, the tile is skipped).
   auto tile_phys = [&](int tile) -> int {
-    return __builtin_amdgcn_readlane(my_blk, (tile * 16) / BS);
+    const int rel = (t_begin + tile * 16) / BS - first_blk;   // uniform
+    // Every register read at a constant index (scalar selects), so the array
+    // stays in registers.
+    int v = __builtin_amdgcn_readlane(blk[0], rel & 63);
+#pragma unroll
+    for (int r = 1; r < NREG; ++r) {
+      const int w = __builtin_amdgcn_readlane(blk[r], rel & 63);
+      v = (rel >> 6) == r ? w : v;
+    }
+    return v;
   };
   // First cache row of a tile in the [NB][Hkv][BS] row space.
   auto tile_row0 = [&](int tile) -> int64_t {
@@ -457,14 +607,14 @@ void decode_partition_kernel(DecodeArgs a) {
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
   if (!head_ok) return;
-  if (nparts == 1) {
+  if (whole_unit) {
     const float inv = vfac / l_tot;
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc)
       store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, acc[nc][0] * inv, acc[nc][1] * inv,
                      acc[nc][2] * inv, acc[nc][3] * inv);
-  } else {
-    const int64_t slot = hq * a.max_parts + part;
+  } else if (item < a.max_items) {
+    const int64_t slot = item * 16 + r16;   // partial row of this item and head
     if (c16 == 0) {
       a.ws_ml[2 * slot] = m_run;
       a.ws_ml[2 * slot + 1] = l_tot;
@@ -476,44 +626,58 @@ void decode_partition_kernel(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of partitions: out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// One wave per (query head, sequence).  D/4 lanes cover one partial's output
-// row with 16-byte loads, so one load instruction takes 64/(D/4) partials at
-// once; the loop is unrolled so several such loads are in flight.  The lane
-// groups' sums are added at the end in a fixed order (results do not depend on
-// timing).
+// Merge of a unit's items: out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
+// One wave per (query head, sequence), planning like the item kernel to find
+// the unit's items.  D/4 lanes cover one partial row with 16-byte loads, so
+// one load instruction takes 64/(D/4) items at once; the lane groups are added
+// in a fixed order at the end (results do not depend on timing).  A sequence
+// with no context gets zeros here; a unit that was one item was finished by
+// the item kernel.
 // ---------------------------------------------------------------------------
 template <int QT, int D>
-__global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   constexpr int LPP = D / 4;          // lanes per partial row
   constexpr int PPI = kWave / LPP;    // partials per load instruction
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  int ctx = a.context_lens[b];
-  ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-  const int nparts = (ctx + a.part_tokens - 1) / a.part_tokens;
-  if (nparts <= 1) return;
+  const Plan plan = make_plan(a, lane);
+  const SeqItems sq = items_of_seq(a, plan, b, lane);
   const int64_t hq = (int64_t)b * a.num_q_heads + h;
-  const float* ml = a.ws_ml + 2 * hq * a.max_parts;
-  const float* accp = a.ws_acc + hq * a.max_parts * D;
+  const int grp = lane / LPP;         // which partial of an instruction
+  const int dq = lane % LPP;          // which 4 output elements
+  if (sq.m == 0) {
+    if (grp == 0) store_out4<QT>(a.out, hq * D + 4 * dq, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (sq.m == 1) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int g = h / G;
+  const int ht = (h % G) / 16;
+  const int r = (h % G) % 16;
+  // Partial row of chunk c: item (first + (g*m + c)*head_tiles + ht), head r.
+  const int64_t row0 = (sq.first + (int64_t)g * sq.m * a.head_tiles + ht) * 16 + r;
+  const int64_t row_step = (int64_t)a.head_tiles * 16;
+  if (sq.first + ((int64_t)g * sq.m + sq.m - 1) * a.head_tiles + ht >= a.max_items) return;
 
   float M = -__builtin_inff();
-  for (int p = lane; p < nparts; p += kWave) M = fmaxf(M, ml[2 * p]);
+  for (int c = lane; c < sq.m; c += kWave) M = fmaxf(M, a.ws_ml[2 * (row0 + c * row_step)]);
   M = wave_max(M);
   float L = 0.f;
-  for (int p = lane; p < nparts; p += kWave) L += exp2f(ml[2 * p] - M) * ml[2 * p + 1];
+  for (int c = lane; c < sq.m; c += kWave) {
+    const int64_t row = row0 + c * row_step;
+    L += __builtin_amdgcn_exp2f(a.ws_ml[2 * row] - M) * a.ws_ml[2 * row + 1];
+  }
   L = wave_sum(L);
 
-  const int grp = lane / LPP;        // which partial of an instruction
-  const int dq = lane % LPP;         // which 4 output elements
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int p0 = 0; p0 < nparts; p0 += PPI) {
-    const int p = p0 + grp;
-    if (p < nparts) {
-      const float w = exp2f(ml[2 * p] - M);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(accp + (int64_t)p * D + 4 * dq);
+  for (int c0 = 0; c0 < sq.m; c0 += PPI) {
+    const int c = c0 + grp;
+    if (c < sq.m) {
+      const int64_t row = row0 + c * row_step;
+      const float w = __builtin_amdgcn_exp2f(a.ws_ml[2 * row] - M);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_acc + row * D + 4 * dq);
       o += w * v;
     }
   }
@@ -531,44 +695,53 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(DecodeArgs a) {
 // Host-side dispatch over the compiled instances.
 // ---------------------------------------------------------------------------
 template <int KV, int QT, int D, int BS>
-static hipError_t launch4(const DecodeArgs& a, int grid_parts, hipStream_t st) {
-  dim3 grid(grid_parts, a.num_kv_heads * a.head_tiles, a.batch);
-  hipLaunchKernelGGL((decode_partition_kernel<KV, QT, D, BS>), grid, dim3(64), 0, st, a);
-  hipError_t e = hipGetLastError();
+static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
+  auto* kern = decode_partition_kernel<KV, QT, D, BS>;
+  int per_cu = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+      &per_cu, reinterpret_cast<const void*>(kern), 64, 0);
   if (e != hipSuccess) return e;
-  if (a.max_parts > 1) {
-    hipLaunchKernelGGL((decode_reduce_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
-                       st, a);
-    e = hipGetLastError();
-  }
-  return e;
+  per_cu = per_cu < 1 ? 1 : (per_cu > kWavesPerCuCap ? kWavesPerCuCap : per_cu);
+  a.slots = num_cus * per_cu;
+  if (a.slots > kMaxSlots) a.slots = kMaxSlots;
+  const int64_t units = (int64_t)a.num_kv_heads * a.head_tiles;
+  // The workspace was sized for kMaxSlots; fewer slots never need more items.
+  const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
+  const int64_t grid = (need + 7) / 8 * 8;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0, st,
+                     a);
+  return hipGetLastError();
 }
 
 template <int KV, int QT, int D>
-static hipError_t launch3(const DecodeArgs& a, int bs, int gp, hipStream_t st) {
-  return bs == 16 ? launch4<KV, QT, D, 16>(a, gp, st) : launch4<KV, QT, D, 256>(a, gp, st);
+static hipError_t launch3(DecodeArgs& a, int bs, int cus, hipStream_t st) {
+  return bs == 16 ? launch4<KV, QT, D, 16>(a, cus, st) : launch4<KV, QT, D, 256>(a, cus, st);
 }
 
 template <int KV, int QT>
-static hipError_t launch2(const DecodeArgs& a, int d, int bs, int gp, hipStream_t st) {
-  return d == 64 ? launch3<KV, QT, 64>(a, bs, gp, st) : launch3<KV, QT, 128>(a, bs, gp, st);
+static hipError_t launch2(DecodeArgs& a, int d, int bs, int cus, hipStream_t st) {
+  return d == 64 ? launch3<KV, QT, 64>(a, bs, cus, st) : launch3<KV, QT, 128>(a, bs, cus, st);
 }
 
 template <int QT>
-static hipError_t launch1(const DecodeArgs& a, int kv, int d, int bs, int gp, hipStream_t st) {
+static hipError_t launch1(DecodeArgs& a, int kv, int d, int bs, int cus, hipStream_t st) {
   switch (kv) {
-    case PKV_I8: return launch2<PKV_I8, QT>(a, d, bs, gp, st);
-    case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT>(a, d, bs, gp, st);
-    default: return launch2<QT, QT>(a, d, bs, gp, st);
+    case PKV_I8: return launch2<PKV_I8, QT>(a, d, bs, cus, st);
+    case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT>(a, d, bs, cus, st);
+    default: return launch2<QT, QT>(a, d, bs, cus, st);
   }
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
-                         int block_size, int grid_parts, hipStream_t st) {
+hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
+                         int num_cus, hipStream_t st) {
   switch (q_dtype) {
-    case PKV_F32: return launch1<PKV_F32>(a, kv_dtype, head_dim, block_size, grid_parts, st);
-    case PKV_F16: return launch1<PKV_F16>(a, kv_dtype, head_dim, block_size, grid_parts, st);
-    default: return launch1<PKV_BF16>(a, kv_dtype, head_dim, block_size, grid_parts, st);
+    case PKV_F32: return launch1<PKV_F32>(a, kv_dtype, head_dim, block_size, num_cus, st);
+    case PKV_F16: return launch1<PKV_F16>(a, kv_dtype, head_dim, block_size, num_cus, st);
+    default: return launch1<PKV_BF16>(a, kv_dtype, head_dim, block_size, num_cus, st);
   }
 }
 

@@ -1,10 +1,23 @@
-// pkv_internal.h — argument blocks and launchers shared by the library's sources.
+// pkv_internal.h — argument blocks, the decode work plan, and launchers shared
+// by the library's sources.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace pkv {
+
+// Decode work is cut into items: an item is a run of 16-token tiles of one
+// (sequence, KV head, tile of <= 16 query heads) unit, processed by one wave.
+// The kernels plan the cut themselves from context_lens (device-resident), so
+// that the item count matches the number of waves the GPU runs at once: one
+// round of near-equal items, no tail of stragglers.
+constexpr int kTileTokens = 16;
+constexpr int kItemTilesMin = 16;    // 256 tokens: keeps merge work small for short batches
+constexpr int kItemTilesMax = 256;   // 4096 tokens: 4 block-table registers per lane at bs 16
+constexpr int kWavesPerCuCap = 12;   // at most 3 waves per SIMD are planned for
+constexpr int kMaxCus = 256;         // MI355X; plans never use more slots than this many CUs give
+constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
 
 // Everything the decode kernels read, passed by value.
 struct DecodeArgs {
@@ -16,8 +29,8 @@ struct DecodeArgs {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_ml;    // [batch][num_q_heads][max_parts][2]: running max (log2 domain), sum
-  float* ws_acc;   // [batch][num_q_heads][max_parts][head_dim]: unnormalised output
+  float* ws_ml;    // [max_items][16][2]: running max (log2 domain), sum
+  float* ws_acc;   // [max_items][16][head_dim]: unnormalised output
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -25,13 +38,26 @@ struct DecodeArgs {
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
-  int32_t part_tokens;         // tokens per partition (multiple of block_size, <= 64 blocks)
-  int32_t max_parts;           // ceil(max_context_len / part_tokens): workspace stride
+  int32_t slots;               // items planned per round (waves resident at once)
+  int32_t max_items;           // capacity of the workspace, in items
   float scale;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
-                         int block_size, int grid_parts, hipStream_t st);
+// Host-side bound on the items a plan can make (grid size and workspace rows).
+// A plan over N tiles with S slots and U units makes at most
+// ceil(N / kItemTilesMax) + S + U items (each round holds fewer than S + N/rounds
+// tiles' worth, and rounding each unit's count up adds fewer than U).
+inline int64_t max_items_bound(int64_t batch, int64_t units_per_seq, int64_t max_context_len,
+                               int64_t slots) {
+  const int64_t units = batch * units_per_seq;
+  const int64_t tiles = units * ((max_context_len + kTileTokens - 1) / kTileTokens);
+  return (tiles + kItemTilesMax - 1) / kItemTilesMax + slots + units;
+}
+
+hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
+                         int num_cus, hipStream_t st);
+
+int decode_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int block_size);
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
                            void* out, float* scale, int scale_given, hipStream_t st);

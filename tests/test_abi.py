@@ -41,15 +41,18 @@ def test_kv_cache_bytes_closed_form(lib):
     assert pkv.kv_cache_bytes(1 << 40, 1 << 30, 1, 1, 1, 1) == 0   # overflow reported as 0
 
 
-def test_partition_and_workspace_sizing(lib):
-    for bs in (16, 256):
-        p = pkv.partition_tokens(32, 64, 8, bs, 32768)
-        assert p % bs == 0 and 256 <= p <= 1024 and p // bs <= 64
-    assert pkv.partition_tokens(1, 4, 3, 16, 100) == 0            # 4 % 3 != 0
-    assert pkv.paged_attention_workspace_size(4, 8, 128, 256) == 0  # fits one partition
-    ws = pkv.paged_attention_workspace_size(32, 64, 128, 32768)
-    rows = 32 * 64 * (32768 // 256)
-    assert ws >= rows * (128 + 2) * 4
+def test_workspace_sizing(lib):
+    # Contexts of at most 256 tokens are never split: no workspace.
+    assert pkv.paged_attention_workspace_size(4, 8, 2, 128, 256) == 0
+    assert pkv.paged_attention_workspace_size(4, 6, 4, 128, 4096) == 0      # 6 % 4 != 0
+    # Longer ones: rows of 16 heads x (2 + head_dim) floats, one per planned item;
+    # at least one item per (sequence, KV head) unit plus a full round of slots.
+    for (B, Hq, Hkv, d, ctx) in [(32, 64, 8, 128, 32768), (8, 32, 32, 128, 4096),
+                                 (2, 64, 1, 64, 100000)]:
+        ws = pkv.paged_attention_workspace_size(B, Hq, Hkv, d, ctx)
+        units = B * Hkv * -(-(Hq // Hkv) // 16)
+        row = 16 * (2 + d) * 4
+        assert ws % row == 0 and ws // row >= units + 256 * 12
 
 
 def _decode(lib, **kw):
