@@ -43,10 +43,15 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama70b_gqa8")
     ap.add_argument("--block-size", type=int, default=None, help="llama70b_fp8 only: 16 or 256")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="llama70b_fp8 only: fewer layers than its 80, for quick tuning runs")
     ap.add_argument("--cold-reps", type=int, default=30,
                     help="extra decode launches timed after a 1 GiB cache-flushing write")
     ap.add_argument("--read-ceiling", type=int, default=1,
                     help="also time a plain 4 GiB streaming read kernel (0 = skip)")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="run the plain copy kernel once over this many MiB first (a launch of "
+                         "known traffic, for calibrating hardware byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample (0 = skip)")
     return ap.parse_args()
@@ -128,7 +133,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    w = W.make(args.workload, block_size=args.block_size)
+    w = W.make(args.workload, block_size=args.block_size, layers=args.layers)
     log(f"[bench] workload {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"d={w.head_dim} bs={w.block_size} kv={w.kv_format} layers={w.layers} "
         f"sum(ctx)={int(w.context_lens.sum())} pool={w.num_blocks} blocks")
@@ -140,6 +145,16 @@ def main():
             log(f"[bench] layer {layer + 1}/{w.layers} resident "
                 f"({torch.cuda.memory_allocated() / 2**30:.1f} GiB, {time.time() - t0:.0f} s)")
     torch.cuda.synchronize()
+
+    if args.copy_probe > 0:
+        from paged_kv_cache_435_amd import probe
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        probe.copy(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] copy probe: {args.copy_probe} MiB read + {args.copy_probe} MiB written")
 
     mcl = w.max_context_len
     ws_bytes = pkv.paged_attention_workspace_size(w.batch, w.num_q_heads, w.num_kv_heads,

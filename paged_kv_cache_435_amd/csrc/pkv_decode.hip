@@ -31,8 +31,32 @@
 //  * Tokens past the context are selected out (never multiplied), and their V
 //    rows are zeroed in LDS, so stale or NaN bytes in unused slots never reach
 //    the sums.
+#include <stdlib.h>
+
 #include "pkv_common.h"
 #include "pkv_internal.h"
+
+// Compile-time tuning knobs (defaults are the shipped configuration):
+//   PKV_NT_LOADS            KV loads carry the non-temporal hint
+//   PKV_WAVES_PER_EU        occupancy target, 16-bit and f32 KV
+//   PKV_STAGES_1B           pipeline depth (tiles in flight), 1-byte KV
+//   PKV_WAVES_1B            occupancy target, 1-byte KV
+//   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
+#ifndef PKV_NT_LOADS
+#define PKV_NT_LOADS 1
+#endif
+#ifndef PKV_WAVES_PER_EU
+#define PKV_WAVES_PER_EU 3
+#endif
+#ifndef PKV_STAGES_1B
+#define PKV_STAGES_1B 2
+#endif
+#ifndef PKV_WAVES_1B
+#define PKV_WAVES_1B 3
+#endif
+#ifndef PKV_SLOTS_PER_CU_DEFAULT
+#define PKV_SLOTS_PER_CU_DEFAULT 12
+#endif
 
 namespace pkv {
 
@@ -173,6 +197,14 @@ __device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
   return v;
 }
 
+// A wave-uniform value held in VGPRs, moved to SGPRs.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), lane);
@@ -190,36 +222,64 @@ struct Plan {
   int tpi;         // tiles per item (a unit of n tiles makes ceil(n / tpi) items)
 };
 
+// Tiles of sequence 64*c + lane (0 past the batch).  The first 256 sequences'
+// counts come from registers filled once; later ones are read again.
+struct SeqTiles {
+  int cached[4];
+  __device__ __forceinline__ void fill(const DecodeArgs& a, int lane) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 64 * i + lane;
+      cached[i] = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+    }
+  }
+  __device__ __forceinline__ int get(const DecodeArgs& a, int c, int lane) const {
+    if (c < 4) {   // uniform selects: the array stays in registers
+      int v = cached[0];
+      v = c == 1 ? cached[1] : v;
+      v = c == 2 ? cached[2] : v;
+      v = c == 3 ? cached[3] : v;
+      return v;
+    }
+    const int b = 64 * c + lane;
+    return b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+  }
+};
+
+__device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqTiles& st, int tpi,
+                                               int lane) {
+  int64_t items = 0;
+  for (int c = 0; 64 * c < a.batch; ++c) items += (st.get(a, c, lane) + tpi - 1) / tpi;
+  return uni64(wave_sum_i64(items) * ((int64_t)a.num_kv_heads * a.head_tiles));
+}
+
 // Tiles per item: about (total tiles) / (slots - units), so that one round of
-// items fills the slots even after each unit's count is rounded up; several
-// equal rounds when an item would pass kItemTilesMax.
+// items fits the slots even after each unit's count is rounded up; several
+// rounds when an item would pass kItemTilesMax.  (Filling the slots exactly,
+// with more and smaller items, measured slower.)
 __device__ Plan make_plan(const DecodeArgs& a, int lane) {
-  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
+  SeqTiles st;
+  st.fill(a, lane);
+  const int64_t slots = a.slots > 0 ? a.slots : 1;
   int64_t tiles = 0, live = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
-    const int b = b0 + lane;
-    const int n = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+  for (int c = 0; 64 * c < a.batch; ++c) {
+    const int n = st.get(a, c, lane);
     tiles += n;
     live += n > 0;
   }
-  tiles = wave_sum_i64(tiles) * units_per_seq;
-  live = wave_sum_i64(live) * units_per_seq;
-  int64_t slots = a.slots - live;
-  if (slots < a.slots / 2) slots = a.slots / 2;
-  if (slots < 1) slots = 1;
-  int64_t k = (tiles + slots * kItemTilesMax - 1) / (slots * kItemTilesMax);
+  const int64_t ups = (int64_t)a.num_kv_heads * a.head_tiles;
+  tiles = uni64(wave_sum_i64(tiles) * ups);
+  live = uni64(wave_sum_i64(live) * ups);
+  int64_t se = slots - live;
+  if (se < slots / 2) se = slots / 2;
+  if (se < 1) se = 1;
+  int64_t k = (tiles + se * kItemTilesMax - 1) / (se * kItemTilesMax);
   if (k < 1) k = 1;
-  int64_t tpi = (tiles + k * slots - 1) / (k * slots);
-  tpi = tpi < kItemTilesMin ? kItemTilesMin : (tpi > kItemTilesMax ? kItemTilesMax : tpi);
-  int64_t items = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
-    const int b = b0 + lane;
-    const int n = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
-    items += (n + tpi - 1) / tpi;
-  }
+  int64_t t = (tiles + k * se - 1) / (k * se);
+  t = t < kItemTilesMin ? kItemTilesMin : (t > kItemTilesMax ? kItemTilesMax : t);
   Plan p;
-  p.items = wave_sum_i64(items) * units_per_seq;
-  p.tpi = (int)tpi;
+  p.tpi = (int)t;
+  p.items = count_items(a, st, p.tpi, lane);
   return p;
 }
 
@@ -294,9 +354,6 @@ __device__ SeqItems items_of_seq(const DecodeArgs& a, const Plan& p, int b, int 
 // through a per-tile LDS buffer (two buffers, alternating) and the wave's own
 // LDS operations complete in order.
 // ---------------------------------------------------------------------------
-#ifndef PKV_NT_LOADS
-#define PKV_NT_LOADS 1
-#endif
 
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 #if PKV_NT_LOADS
@@ -306,12 +363,17 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 #endif
 }
 
-#ifndef PKV_WAVES_PER_EU
-#define PKV_WAVES_PER_EU 3
-#endif
+
+// Occupancy target per KV type: 16-bit and f32 tiles keep two in flight at 3
+// waves per SIMD; 1-byte tiles keep four in flight at 2 waves per SIMD.
+template <int KV>
+struct Tuning {
+  static constexpr int stages = dtype_bytes(KV) == 1 ? PKV_STAGES_1B : 2;
+  static constexpr int waves_per_eu = dtype_bytes(KV) == 1 ? PKV_WAVES_1B : PKV_WAVES_PER_EU;
+};
 
 template <int KV, int QT, int D, int BS>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(PKV_WAVES_PER_EU)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
   constexpr int eb = dtype_bytes(KV);
@@ -341,15 +403,16 @@ void decode_partition_kernel(DecodeArgs a) {
   int b;
   SeqItems sq;
   if (!seq_of_item(a, plan, item, lane, b, sq)) return;
-  const int64_t local = item - sq.first;
-  const int64_t per_g = (int64_t)sq.m * a.head_tiles;
-  const int g = (int)(local / per_g);
-  const int chunk = (int)((local % per_g) / a.head_tiles);
-  const int ht = (int)(local % a.head_tiles);
-  const int ctx = sq.ctx;
-  const int t_begin = (int)((int64_t)chunk * sq.n / sq.m) * kTileTokens;
+  b = uni(b);
+  const int local = uni((int)(item - sq.first));   // < m * units per sequence
+  const int per_g = sq.m * a.head_tiles;
+  const int g = uni(local / per_g);
+  const int chunk = uni((local % per_g) / a.head_tiles);
+  const int ht = uni(local % a.head_tiles);
+  const int ctx = uni(sq.ctx);
+  const int t_begin = uni((int)((int64_t)chunk * sq.n / sq.m) * kTileTokens);
   int t_end = (int)((int64_t)(chunk + 1) * sq.n / sq.m) * kTileTokens;
-  t_end = t_end < ctx ? t_end : ctx;
+  t_end = uni(t_end < ctx ? t_end : ctx);
   const int ntiles = (t_end - t_begin + 15) >> 4;
   const bool whole_unit = sq.m == 1;
 
@@ -438,7 +501,11 @@ void decode_partition_kernel(DecodeArgs a) {
   const uint32_t voff = (uint32_t)(lane * 16);
 
   // Issue the loads of one tile into a register set.
-  auto issue = [&](int tile, u32x4* kr, u32x4* vr, f32x4& ks, f32x4& vs) {
+  // INT8 row scales: lane 16*c + i holds the scale of token 4*c + i (i < 4) of
+  // the tile (one register per tile and cache); the lanes that need tokens
+  // 4*c16 .. 4*c16+3 fetch them from their row's first four lanes.
+  const int scale_tok = 4 * c16 + (r16 & 3);
+  auto issue = [&](int tile, u32x4* kr, u32x4* vr, float& ks, float& vs) {
     const int64_t row0 = tile_row0(tile);
     const uint64_t tile_bytes = (uint64_t)row0 * R;   // uniform: keep it scalar
     const uint64_t tb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tile_bytes >> 32)) << 32) |
@@ -450,15 +517,23 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + voff + 1024 * j);
     if constexpr (KV == PKV_I8) {
-      ks = *reinterpret_cast<const f32x4*>(a.k_scale + row0 + 4 * c16);
-      vs = *reinterpret_cast<const f32x4*>(a.v_scale + row0 + 4 * c16);
+      ks = a.k_scale[row0 + scale_tok];
+      vs = a.v_scale[row0 + scale_tok];
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the compute they overlap
   };
 
   // Softmax update and both contractions for one loaded tile.
-  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, const f32x4& ksc,
-                     const f32x4& vsc, uint8_t* lbuf) {
+  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1,
+                     uint8_t* lbuf) {
+    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = ksc;
+    if constexpr (KV == PKV_I8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ksc[i] = __shfl(ks1, 16 * c16 + i, kWave);
+        vsc[i] = __shfl(vs1, 16 * c16 + i, kWave);
+      }
+    }
     const int t0 = t_begin + tile * 16;
     int n_valid = t_end - t0;
     n_valid = n_valid > 16 ? 16 : n_valid;
@@ -518,7 +593,7 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       const bool ok = 4 * c16 + i < n_valid;
       float f = kfac;
-      if constexpr (KV == PKV_I8) f = kfac / ksc[i];
+      if constexpr (KV == PKV_I8) f = kfac * __builtin_amdgcn_rcpf(ksc[i]);   // 1/s to ~1 ulp
       z[i] = ok ? s[i] * f : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
@@ -546,7 +621,7 @@ void decode_partition_kernel(DecodeArgs a) {
     }
     if constexpr (KV == PKV_I8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] / vsc[i] : 0.f;
+      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * __builtin_amdgcn_rcpf(vsc[i]) : 0.f;
     }
 
     // O^T += V^T P^T (V read back from LDS, transposed).
@@ -583,24 +658,42 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   };
 
-  // Steady state without branches around the loads (a load issued on one path
-  // only would make the wait counts conservative), then a one- or two-tile tail.
-  u32x4 ka[NL], va[NL], kb[NL], vb[NL];
-  f32x4 ksa = {1.f, 1.f, 1.f, 1.f}, vsa = ksa, ksb = ksa, vsb = ksa;
-  issue(0, ka, va, ksa, vsa);
+  // S-deep pipeline: tile t lives in register set t % S; while tile t is
+  // multiplied, tiles t+1 .. t+S-1 are in flight.  1-byte KV tiles carry half
+  // the bytes of 16-bit ones, so they keep twice as many in flight.  The
+  // steady state has no branch around the loads (a load issued on one path
+  // only would make the wait counts conservative); a short tail follows.
+  constexpr int S = Tuning<KV>::stages;
+  u32x4 kr[S][NL], vr[S][NL];
+  float ks[S], vs[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) ks[i] = vs[i] = 1.f;
   int tile = 0;
-  for (; tile + 2 < ntiles; tile += 2) {
-    issue(tile + 1, kb, vb, ksb, vsb);
-    compute(tile, ka, va, ksa, vsa, lds_v);
-    issue(tile + 2, ka, va, ksa, vsa);
-    compute(tile + 1, kb, vb, ksb, vsb, lds_v + LDS_TILE);
-  }
-  if (tile + 1 < ntiles) {
-    issue(tile + 1, kb, vb, ksb, vsb);
-    compute(tile, ka, va, ksa, vsa, lds_v);
-    compute(tile + 1, kb, vb, ksb, vsb, lds_v + LDS_TILE);
+  if (ntiles > 2 * S - 2) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i]);
+    for (; tile + 2 * S - 2 < ntiles; tile += S) {
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        const int nx = (i + S - 1) % S;
+        issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
+        compute(tile + i, kr[i], vr[i], ks[i], vs[i], lds_v + (i & 1) * LDS_TILE);
+      }
+    }
   } else {
-    compute(tile, ka, va, ksa, vsa, lds_v);
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      if (i < ntiles) issue(i, kr[i], vr[i], ks[i], vs[i]);
+  }
+  for (; tile < ntiles; tile += S) {
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+      if (tile + i < ntiles) {
+        const int nx = (i + S - 1) % S;
+        if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
+        compute(tile + i, kr[i], vr[i], ks[i], vs[i], lds_v + (i & 1) * LDS_TILE);
+      }
+    }
   }
 
   // ---- epilogue ----
@@ -694,6 +787,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // Host-side dispatch over the compiled instances.
 // ---------------------------------------------------------------------------
+// Items planned per compute unit and round.  Fewer concurrent waves than the
+// kernel's occupancy allows read HBM more efficiently (fewer streams fighting
+// over DRAM rows), as long as enough bytes stay in flight.  PKV_SLOTS_PER_CU
+// overrides the default (tuning).
+static int slots_per_cu() {
+  static const int v = [] {
+    const char* e = getenv("PKV_SLOTS_PER_CU");
+    const int x = e ? atoi(e) : 0;
+    return x > 0 ? x : PKV_SLOTS_PER_CU_DEFAULT;
+  }();
+  return v;
+}
+
 template <int KV, int QT, int D, int BS>
 static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
   auto* kern = decode_partition_kernel<KV, QT, D, BS>;
@@ -702,6 +808,8 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
       &per_cu, reinterpret_cast<const void*>(kern), 64, 0);
   if (e != hipSuccess) return e;
   per_cu = per_cu < 1 ? 1 : (per_cu > kWavesPerCuCap ? kWavesPerCuCap : per_cu);
+  const int target = slots_per_cu();
+  if (target > 0 && target < per_cu) per_cu = target;
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.num_kv_heads * a.head_tiles;

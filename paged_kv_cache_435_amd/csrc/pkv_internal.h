@@ -44,9 +44,10 @@ struct DecodeArgs {
 };
 
 // Host-side bound on the items a plan can make (grid size and workspace rows).
-// A plan over N tiles with S slots and U units makes at most
-// ceil(N / kItemTilesMax) + S + U items (each round holds fewer than S + N/rounds
-// tiles' worth, and rounding each unit's count up adds fewer than U).
+// With N tiles in U units and S slots, the plan uses S' = max(S - U, S/2) and
+// t >= N / (k S') tiles per item over k rounds, so it makes at most
+// sum ceil(n_u / t) <= k S' + U items, with k S' < N / kItemTilesMax + S'.
+// Hence at most N / kItemTilesMax + S + U.
 inline int64_t max_items_bound(int64_t batch, int64_t units_per_seq, int64_t max_context_len,
                                int64_t slots) {
   const int64_t units = batch * units_per_seq;

@@ -144,3 +144,19 @@ def test_workspace_too_small_raises():
         pkv.paged_attention_decode(case.out, case.q, case.k_cache, case.v_cache,
                                    case.block_tables, case.context_lens, w.scale,
                                    w.max_context_len, workspace=tiny)
+
+
+@pytest.mark.parametrize("name,ctx,hq,hkv,d,bs", [
+    # One sequence cut into hundreds of items per (KV head) unit, merged back.
+    ("one-long", [100_000], 8, 1, 128, 16),
+    ("one-long-gqa", [40_000], 64, 8, 128, 256),
+    # 70 and 300 sequences: the planner's scans span two and five chunks of 64
+    # (past the 256 sequences it keeps in registers), with empty contexts mixed in.
+    ("b70", [0 if i % 9 == 4 else 1 + (i * 37) % 900 for i in range(70)], 8, 2, 128, 16),
+    ("b300", [0 if i % 50 == 7 else 1 + (i * 53) % 400 for i in range(300)], 4, 1, 64, 16),
+    # Groups wider than one 16-head tile (3 head tiles per KV head).
+    ("g40", [3000, 17, 1100], 40, 1, 128, 16),
+])
+def test_planner_shapes(name, ctx, hq, hkv, d, bs):
+    w = W.custom(torch.float16, "f16", ctx, hq, hkv, d, bs, name=name)
+    run_and_check(w)
