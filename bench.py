@@ -65,7 +65,8 @@ def cpu_baseline(w, cases, budget_s):
     """The CPU oracle, as it stands, on whole sequences of the workload (every
     query head), taken in a seeded order until about ``budget_s`` seconds of
     oracle time have been spent.  Only the sampled sequences' blocks are copied
-    to the host, into a compact pool with its own table (bookkeeping only)."""
+    to the host, into a compact pool with its own table, and put in logical row
+    order (bookkeeping only, not timed)."""
     import numpy as np
     import torch
 
@@ -84,8 +85,8 @@ def cpu_baseline(w, cases, budget_s):
         ctx = int(w.context_lens[b])
         nblk = -(-ctx // w.block_size)
         phys = torch.from_numpy(w.block_tables[b, :nblk].astype(np.int64)).to(case.k_cache.device)
-        kc = cache_to_host(case.k_cache[phys], w.kv_format)
-        vc = cache_to_host(case.v_cache[phys], w.kv_format)
+        kc = oracle.layout.k_from_stored(cache_to_host(case.k_cache[phys], w.kv_format))
+        vc = oracle.layout.v_from_stored(cache_to_host(case.v_cache[phys], w.kv_format))
         ks = vs = None
         if w.kv_format == "i8":
             ks, vs = case.k_scale[phys].cpu().numpy(), case.v_scale[phys].cpu().numpy()

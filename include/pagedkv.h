@@ -10,7 +10,17 @@
  *  [P3] «大模型推理加速实战：KV Cache内存优化与PagedAttention分页管理方案»
  *
  * Cache layout (all entry points):
- *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim], in kv_dtype.
+ *   k_cache, v_cache   [num_blocks][num_kv_heads][block_size][head_dim] elements in
+ *                      kv_dtype, each group of 16 consecutive rows (tokens) of a
+ *                      (block, head) tile stored in the order the decode kernel's
+ *                      matrix instructions consume (eb = element bytes, rows of
+ *                      head_dim elements, t = token within the group):
+ *                        K: the row of token t is cut into 16-byte chunks; chunk c
+ *                           is stored at byte (c * 16 + t) * 16 of the group;
+ *                        V: element (t, d) is stored at byte
+ *                           ((n / G) * 64 + (t / 4) * 16 + d % 16) * 16
+ *                             + ((n % G) * 4 + t % 4) * eb,  n = d / 16, G = 4 / eb.
+ *                      kv_cache_append writes this order; no caller needs to.
  *   INT8 scales        float32 [num_blocks][num_kv_heads][block_size], one per stored row.
  *   FP8 scales         one float32 per tensor (per layer, one for K and one for V).
  *   block_tables       int32 [batch][max_blocks_per_seq]: logical block j of sequence b

@@ -30,9 +30,10 @@ Modules
   attention  paged decode attention = standard attention over the gathered cache
   quant      INT8 per-row and FP8 per-tensor quantizers      [P1] §4, [P3]
   append     expected cache after writing new tokens' rows   [P3]
+  layout     stored order of the pools <-> logical [NB][Hkv][bs][d] order
 """
 
-from . import kvsize, widen, paging, attention, quant, append  # noqa: F401
+from . import kvsize, widen, paging, attention, quant, append, layout  # noqa: F401
 from .attention import decode_attention, attend, validate_tables  # noqa: F401
 from .quant import (quantize_int8_rows, fp8_tensor_scale, encode_e4m3fn,  # noqa: F401
                     quantize_fp8)

@@ -89,4 +89,28 @@ __host__ __device__ constexpr int dtype_bytes(int dt) {
   return dt == PKV_F32 ? 4 : (dt == PKV_F16 || dt == PKV_BF16) ? 2 : 1;
 }
 
+// ---------------------------------------------------------------------------
+// Storage order inside a group of 16 consecutive token rows of one (block,
+// KV head) tile (the pool keeps the [NB][Hkv][bs][d] shape; only the order of
+// the 16 * d elements of each 16-row group changes).  eb = element bytes.
+//
+// K: the row of token t is cut into 16-byte chunks; chunk c of token t sits at
+//    byte (c * 16 + t) * 16.  A wave reading 16 bytes per lane at lane * 16
+//    (+1 KB per instruction) gets chunk (j * 4 + lane / 16) of token lane % 16:
+//    the A operand of a 16x16xK MFMA with tokens as rows.
+// V: element (t, d) with nc = d / 16, r = d % 16, c = t / 4, i = t % 4 and
+//    G = 4 / eb column blocks per 16 bytes sits at byte
+//    ((nc / G) * 64 + c * 16 + r) * 16 + ((nc % G) * 4 + i) * eb.
+//    Lane 16 c + r of instruction j then holds, for d = 16 nc + r with
+//    nc in [j G, j G + G), the values of tokens 4c .. 4c + 3: the A operand of
+//    O^T += V^T P^T.
+// ---------------------------------------------------------------------------
+__host__ __device__ constexpr int k_group_offset(int t, int d, int eb) {
+  return (((d * eb) >> 4) * 16 + t) * 16 + ((d * eb) & 15);
+}
+__host__ __device__ constexpr int v_group_offset(int t, int d, int eb) {
+  return (((d >> 4) / (4 / eb)) * 64 + (t >> 2) * 16 + (d & 15)) * 16 +
+         (((d >> 4) % (4 / eb)) * 4 + (t & 3)) * eb;
+}
+
 }  // namespace pkv

@@ -14,23 +14,25 @@
 //    lengths, so that one round of near-equal items fills the waves the GPU
 //    runs at once (ragged batches otherwise leave a tail of stragglers).
 //    Items are dealt to the 8 XCDs in contiguous ranges.
+//  * The cache stores each 16-token group of a (block, KV head) tile in MFMA
+//    operand order (pkv_common.h: k_group_offset, v_group_offset), so K and V
+//    are both read with 16 B per lane and 1 KB contiguous per instruction
+//    straight into operand registers: no LDS, no transposes.
 //  * Tokens go 16 at a time.  QK^T is one MFMA chain per 16 tokens:
 //    S^T[16 tok][16 heads] = K[16 tok][d] * Q^T[d][16 heads]
-//    (v_mfma_f32_16x16x32_{f16,bf16}, or 16x16x4 for f32).  K is loaded from HBM
-//    straight into the A-operand layout (16 B per lane, 64 contiguous bytes per
-//    row per instruction); Q sits in registers for the whole item.
+//    (v_mfma_f32_16x16x32_{f16,bf16}, or 16x16x4 for f32); Q sits in registers
+//    for the whole item.
 //  * Online softmax in the exp2 domain on the MFMA output registers.  A lane
 //    holds 4 tokens of one head, so a head's max needs two cross-lane steps.
 //  * PV as O^T[d][heads] += V^T[d][16 tok] * P^T[16 tok][heads]
-//    (v_mfma_f32_16x16x16).  P^T is exactly the QK output layout, so P never
-//    leaves its registers.  V is staged through LDS (coalesced 16 B/lane
-//    writes) and read back transposed.
+//    (v_mfma_f32_16x16x16, or 16x16x4 for f32).  P^T is exactly the QK output
+//    layout, so P never leaves its registers.
 //  * A unit cut into several items gets (max, sum, unnormalised output) per
 //    item, merged by a second kernel with the log-sum-exp rule.  A unit that is
 //    one item is finished in place.
-//  * Tokens past the context are selected out (never multiplied), and their V
-//    rows are zeroed in LDS, so stale or NaN bytes in unused slots never reach
-//    the sums.
+//  * Tokens past the context are selected out of the softmax (never
+//    multiplied), and their V values are masked to zero, so stale or NaN bytes
+//    in unused slots never reach the sums.
 #include <stdlib.h>
 
 #include "pkv_common.h"
@@ -81,51 +83,47 @@ struct Cvt {
   static constexpr int eb = dtype_bytes(KV);
   static constexpr int in_elems = 16 / eb;                           // per 16 B chunk
   static constexpr int out_words = MT == MT_F32 ? in_elems : in_elems / 2;
+  static constexpr int word_out = out_words / 4;                     // outputs per input word
 
-  __device__ __forceinline__ static void run(const u32x4 raw, uint32_t* w) {
+  // One 32-bit word of stored bytes -> word_out MFMA words.
+  __device__ __forceinline__ static void word(const uint32_t raw, uint32_t* w) {
     if constexpr ((KV == PKV_F16 && MT == MT_F16) || (KV == PKV_BF16 && MT == MT_BF16) ||
                   (KV == PKV_F32 && MT == MT_F32)) {
-      w[0] = raw[0]; w[1] = raw[1]; w[2] = raw[2]; w[3] = raw[3];
+      w[0] = raw;
     } else if constexpr (KV == PKV_I8 && MT == MT_F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t t = raw[i] ^ 0x80808080u;
-        const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
-        const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
-        const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-        w[2 * i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
-        w[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
-      }
+      const uint32_t t = raw ^ 0x80808080u;
+      const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
+      const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
+      const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+      w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
+      w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
     } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // bytes b0 b1 -> [0, b0, 0, b1]; b2 b3 -> [0, b2, 0, b3]
-        const uint32_t lo = __builtin_amdgcn_perm(0u, raw[i], 0x010C000Cu);
-        const uint32_t hi = __builtin_amdgcn_perm(0u, raw[i], 0x030C020Cu);
-        w[2 * i] = (lo & 0x80008000u) | ((lo & 0x7F007F00u) >> 1);
-        w[2 * i + 1] = (hi & 0x80008000u) | ((hi & 0x7F007F00u) >> 1);
-      }
+      // bytes b0 b1 -> [0, b0, 0, b1]; b2 b3 -> [0, b2, 0, b3]
+      const uint32_t lo = __builtin_amdgcn_perm(0u, raw, 0x010C000Cu);
+      const uint32_t hi = __builtin_amdgcn_perm(0u, raw, 0x030C020Cu);
+      w[0] = (lo & 0x80008000u) | ((lo & 0x7F007F00u) >> 1);
+      w[1] = (hi & 0x80008000u) | ((hi & 0x7F007F00u) >> 1);
     } else {
       // Generic: through f32 (exact for every pair built here).
-      float f[in_elems];
+      constexpr int per = 4 / eb;   // elements in the word
+      float f[per];
 #pragma unroll
-      for (int e = 0; e < in_elems; ++e) {
-        const uint32_t word = raw[(e * eb) / 4];
-        const int sh = ((e * eb) % 4) * 8;
+      for (int e = 0; e < per; ++e) {
+        const int sh = e * eb * 8;
         if constexpr (KV == PKV_I8) {
-          f[e] = (float)(int8_t)((word >> sh) & 0xFFu);
+          f[e] = (float)(int8_t)((raw >> sh) & 0xFFu);
         } else if constexpr (KV == PKV_FP8_E4M3FN) {
-          f[e] = e4m3fn_to_f32((word >> sh) & 0xFFu);
+          f[e] = e4m3fn_to_f32((raw >> sh) & 0xFFu);
         } else if constexpr (KV == PKV_F16) {
-          f[e] = f16_to_f32((uint16_t)((word >> sh) & 0xFFFFu));
+          f[e] = f16_to_f32((uint16_t)((raw >> sh) & 0xFFFFu));
         } else if constexpr (KV == PKV_BF16) {
-          f[e] = bf16_to_f32((uint16_t)((word >> sh) & 0xFFFFu));
+          f[e] = bf16_to_f32((uint16_t)((raw >> sh) & 0xFFFFu));
         } else {
-          f[e] = bitsf(word);
+          f[e] = bitsf(raw);
         }
       }
 #pragma unroll
-      for (int o = 0; o < out_words; ++o) {
+      for (int o = 0; o < word_out; ++o) {
         if constexpr (MT == MT_F32) {
           w[o] = fbits(f[o]);
         } else if constexpr (MT == MT_F16) {
@@ -135,6 +133,12 @@ struct Cvt {
         }
       }
     }
+  }
+
+  // One 16-byte chunk -> out_words MFMA words.
+  __device__ __forceinline__ static void run(const u32x4 raw, uint32_t* w) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) word(raw[i], w + i * word_out);
   }
 };
 
@@ -347,14 +351,11 @@ __device__ SeqItems items_of_seq(const DecodeArgs& a, const Plan& p, int b, int 
 // ---------------------------------------------------------------------------
 // Partition kernel.
 //
-// The tile loop is software-pipelined two deep: while tile i is converted and
-// multiplied, the K/V loads of tile i+1 are already in flight (two register
-// sets, the loop unrolled by two so no register copy waits on a load).  The
-// workgroup is one wave, so no workgroup barrier is needed: the V tile goes
-// through a per-tile LDS buffer (two buffers, alternating) and the wave's own
-// LDS operations complete in order.
+// The tile loop is software-pipelined: while tile i is converted and
+// multiplied, the K/V loads of the next tiles are already in flight (register
+// sets used in rotation, the loop unrolled so no register copy waits on a
+// load).  The workgroup is one wave and needs no LDS.
 // ---------------------------------------------------------------------------
-
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 #if PKV_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -382,12 +383,8 @@ void decode_partition_kernel(DecodeArgs a) {
   using C = Cvt<KV, MT>;
   constexpr int WPC = C::out_words;    // MFMA words per chunk
   constexpr int KW = NL * WPC;         // MFMA words per lane for a K tile (= D/8 or D/4)
-  constexpr int mtb = MT == MT_F32 ? 4 : 2;
-  constexpr int LDS_ROW = D * mtb + 16;  // bytes, padded against bank conflicts
-  constexpr int LDS_TILE = 16 * LDS_ROW;
   constexpr int NC = D / 16;           // 16-wide d chunks of the output
-
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * LDS_TILE];
+  constexpr int VG = 4 / eb;           // 16-wide d chunks per 16 bytes of a V lane
 
   const int lane = threadIdx.x;
   const int r16 = lane & 15;   // MFMA row/column index of this lane
@@ -495,10 +492,10 @@ void decode_partition_kernel(DecodeArgs a) {
     return ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS);
   };
 
-  // Per-lane byte offsets inside a tile (32-bit, so the loads take a scalar
-  // tile base plus one vector offset).
-  const uint32_t koff = (uint32_t)(r16 * R + 16 * c16);
-  const uint32_t voff = (uint32_t)(lane * 16);
+  // Per-lane byte offset inside a 16-token group (32-bit, so the loads take a
+  // scalar group base plus one vector offset).  Both caches are stored in the
+  // MFMA operand order, so every load is 1 KB contiguous per instruction.
+  const uint32_t loff = (uint32_t)(lane * 16);
 
   // Issue the loads of one tile into a register set.
   // INT8 row scales: lane 16*c + i holds the scale of token 4*c + i (i < 4) of
@@ -513,9 +510,9 @@ void decode_partition_kernel(DecodeArgs a) {
     const uint8_t* ktile = kbase + tb;
     const uint8_t* vtile = vbase + tb;
 #pragma unroll
-    for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile + koff + 64 * j);
+    for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile + loff + 1024 * j);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + voff + 1024 * j);
+    for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + loff + 1024 * j);
     if constexpr (KV == PKV_I8) {
       ks = a.k_scale[row0 + scale_tok];
       vs = a.v_scale[row0 + scale_tok];
@@ -524,8 +521,7 @@ void decode_partition_kernel(DecodeArgs a) {
   };
 
   // Softmax update and both contractions for one loaded tile.
-  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1,
-                     uint8_t* lbuf) {
+  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1) {
     f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = ksc;
     if constexpr (KV == PKV_I8) {
 #pragma unroll
@@ -539,25 +535,12 @@ void decode_partition_kernel(DecodeArgs a) {
     n_valid = n_valid > 16 ? 16 : n_valid;
     if (tile_phys(tile) < 0) n_valid = 0;
 
-    // V tile -> LDS (as MFMA elements); rows past the context are zeroed (only
-    // a sequence's last tile has such rows: the test is uniform).
-    const bool full = n_valid == 16;
+    // Tokens 4*c16 + i of this lane past the context get zero V (masks on the
+    // converted operands; all ones for a full tile).
+    const int vcnt = n_valid - 4 * c16;
+    uint32_t vmask[4];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const int chunk = lane + 64 * j;
-      const int row = (chunk * 16) / R;
-      const int col = ((chunk * 16) % R) / eb;   // element column
-      uint32_t w[WPC];
-      C::run(vraw[j], w);
-      if (!full && row >= n_valid) {
-#pragma unroll
-        for (int o = 0; o < WPC; ++o) w[o] = 0u;
-      }
-      uint8_t* dst = lbuf + row * LDS_ROW + col * mtb;
-#pragma unroll
-      for (int o = 0; o < WPC; o += 4)
-        *reinterpret_cast<u32x4*>(dst + o * 4) = u32x4{w[o], w[o + 1], w[o + 2], w[o + 3]};
-    }
+    for (int i = 0; i < 4; ++i) vmask[i] = i < vcnt ? 0xFFFFFFFFu : 0u;
 
     // S^T = K Q^T
     uint32_t kop[KW];
@@ -624,27 +607,40 @@ void decode_partition_kernel(DecodeArgs a) {
       for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * __builtin_amdgcn_rcpf(vsc[i]) : 0.f;
     }
 
-    // O^T += V^T P^T (V read back from LDS, transposed).
+    // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
+    // of tokens 4*c16 .. 4*c16+3 (storage order), i.e. the A operand.
     if constexpr (MT == MT_F32) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
+        uint32_t w[4];
+        if constexpr (eb == 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = *reinterpret_cast<const float*>(lbuf + (4 * c16 + i) * LDS_ROW +
-                                                          (nc * 16 + r16) * 4);
-          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(v, p[i], acc[nc], 0, 0, 0);
+          for (int i = 0; i < 4; ++i) w[i] = vraw[nc][i];
+        } else if constexpr (eb == 1) {
+          C::word(vraw[nc / VG][nc % VG], w);
+        } else {
+          C::word(vraw[nc / VG][2 * (nc % VG)], w);
+          C::word(vraw[nc / VG][2 * (nc % VG) + 1], w + 2);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[i] & vmask[i]), p[i], acc[nc],
+                                                         0, 0, 0);
       }
     } else {
       const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
+      const uint32_t m01 = (vmask[0] & 0xFFFFu) | (vmask[1] & 0xFFFF0000u);
+      const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
-        const uint8_t* src = lbuf + (4 * c16) * LDS_ROW + (nc * 16 + r16) * 2;
-        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(src);
-        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(src + LDS_ROW);
-        const uint32_t v2 = *reinterpret_cast<const uint16_t*>(src + 2 * LDS_ROW);
-        const uint32_t v3 = *reinterpret_cast<const uint16_t*>(src + 3 * LDS_ROW);
-        const u32x2 va = {v0 | (v1 << 16), v2 | (v3 << 16)};
+        uint32_t w[2];
+        if constexpr (eb == 1) {
+          C::word(vraw[nc / VG][nc % VG], w);
+        } else {
+          w[0] = vraw[nc / VG][2 * (nc % VG)];
+          w[1] = vraw[nc / VG][2 * (nc % VG) + 1];
+        }
+        const u32x2 va = {w[0] & m01, w[1] & m23};
         if constexpr (MT == MT_F16) {
           acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
                                                           __builtin_bit_cast(f16x4, pb), acc[nc],
@@ -677,7 +673,7 @@ void decode_partition_kernel(DecodeArgs a) {
       for (int i = 0; i < S; ++i) {
         const int nx = (i + S - 1) % S;
         issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        compute(tile + i, kr[i], vr[i], ks[i], vs[i], lds_v + (i & 1) * LDS_TILE);
+        compute(tile + i, kr[i], vr[i], ks[i], vs[i]);
       }
     }
   } else {
@@ -691,7 +687,7 @@ void decode_partition_kernel(DecodeArgs a) {
       if (tile + i < ntiles) {
         const int nx = (i + S - 1) % S;
         if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        compute(tile + i, kr[i], vr[i], ks[i], vs[i], lds_v + (i & 1) * LDS_TILE);
+        compute(tile + i, kr[i], vr[i], ks[i], vs[i]);
       }
     }
   }

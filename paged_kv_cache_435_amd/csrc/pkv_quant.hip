@@ -41,6 +41,7 @@ __device__ __forceinline__ int8_t int8_code(float x, float s) {
 
 __device__ __forceinline__ uint8_t fp8_code(float x, float s) {
   float y = x / s;                 // IEEE correctly rounded
+  if (y != y) return (uint8_t)(0x7Fu | ((fbits(y) >> 24) & 0x80u));   // NaN stays NaN
   y = y < -448.0f ? -448.0f : (y > 448.0f ? 448.0f : y);
   return (uint8_t)f32_to_e4m3fn(y);
 }
@@ -139,44 +140,56 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_l
 }
 
 // ---------------------------------------------------------------------------
-// Append: grid (num_kv_heads, num_tokens), one wave each.
+// Append: one wave per (token, KV head) row, four rows per workgroup.  Each
+// lane takes D/64 consecutive elements of the row and stores them at their
+// place in the row's 16-token group (k_group_offset / v_group_offset).
 // ---------------------------------------------------------------------------
 template <int ST, int CT, int D>
-__global__ __launch_bounds__(64) void append_kernel(const void* __restrict__ k,
-                                                    const void* __restrict__ v,
-                                                    const int64_t* __restrict__ slots,
-                                                    void* __restrict__ k_cache,
-                                                    void* __restrict__ v_cache,
-                                                    float* __restrict__ k_scale,
-                                                    float* __restrict__ v_scale, int num_blocks,
-                                                    int block_size, int num_kv_heads) {
+__global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k,
+                                                     const void* __restrict__ v,
+                                                     const int64_t* __restrict__ slots,
+                                                     void* __restrict__ k_cache,
+                                                     void* __restrict__ v_cache,
+                                                     float* __restrict__ k_scale,
+                                                     float* __restrict__ v_scale, int64_t rows,
+                                                     int num_blocks, int block_size,
+                                                     int num_kv_heads) {
   constexpr int PER = D / kWave;   // elements per lane
-  const int g = blockIdx.x;
-  const int t = blockIdx.y;
-  const int lane = threadIdx.x;
+  constexpr int eb = dtype_bytes(CT);
+  constexpr int R = D * eb;        // bytes per stored row
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const int64_t t = row / num_kv_heads;
+  const int g = (int)(row % num_kv_heads);
   const int64_t slot = slots[t];
   if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
   const int64_t blk = slot / block_size;
-  const int64_t off = slot % block_size;
-  const int64_t dst_row = (blk * num_kv_heads + g) * block_size + off;
-  const int64_t src_row = (int64_t)t * num_kv_heads + g;
+  const int off = (int)(slot % block_size);
+  const int t16 = off & 15;
+  const int64_t dst_row = (blk * num_kv_heads + g) * block_size + off;   // scale index
+  const int64_t group_byte = (dst_row - t16) * R;                      // first byte of the group
+  const int64_t src_row = t * num_kv_heads + g;
 
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const void* src = which == 0 ? k : v;
-    void* cache = which == 0 ? k_cache : v_cache;
+    uint8_t* cache = static_cast<uint8_t*>(which == 0 ? k_cache : v_cache) + group_byte;
     float* sc = which == 0 ? k_scale : v_scale;
+    int pos[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int d = lane * PER + e;
+      pos[e] = which == 0 ? k_group_offset(t16, d, eb) : v_group_offset(t16, d, eb);
+    }
     if constexpr (CT == ST) {
-      constexpr int eb = dtype_bytes(ST);
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const int64_t i = lane * PER + e;
+        const int64_t i = src_row * D + lane * PER + e;
         if constexpr (eb == 4)
-          static_cast<uint32_t*>(cache)[dst_row * D + i] =
-              static_cast<const uint32_t*>(src)[src_row * D + i];
+          *reinterpret_cast<uint32_t*>(cache + pos[e]) = static_cast<const uint32_t*>(src)[i];
         else
-          static_cast<uint16_t*>(cache)[dst_row * D + i] =
-              static_cast<const uint16_t*>(src)[src_row * D + i];
+          *reinterpret_cast<uint16_t*>(cache + pos[e]) = static_cast<const uint16_t*>(src)[i];
       }
     } else {
       float xv[PER];
@@ -190,14 +203,12 @@ __global__ __launch_bounds__(64) void append_kernel(const void* __restrict__ k,
         const float s = int8_row_scale(a);
 #pragma unroll
         for (int e = 0; e < PER; ++e)
-          static_cast<int8_t*>(cache)[dst_row * D + lane * PER + e] =
-              s == 0.0f ? (int8_t)0 : int8_code(xv[e], s);
+          cache[pos[e]] = (uint8_t)(s == 0.0f ? (int8_t)0 : int8_code(xv[e], s));
         if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
       } else {  // FP8 with the tensor's scale
         const float s = sc[0];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-          static_cast<uint8_t*>(cache)[dst_row * D + lane * PER + e] = fp8_code(xv[e], s);
+        for (int e = 0; e < PER; ++e) cache[pos[e]] = fp8_code(xv[e], s);
       }
     }
   }
@@ -208,13 +219,15 @@ static hipError_t append_t(const void* k, const void* v, int num_tokens, const i
                            void* kc, void* vc, float* ks, float* vs, int nb, int bs, int hkv,
                            int d, hipStream_t st) {
   if (num_tokens == 0) return hipSuccess;
-  dim3 grid(hkv, num_tokens);
+  const int64_t rows = (int64_t)num_tokens * hkv;
+  const int64_t blocks = (rows + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   if (d == 64)
-    hipLaunchKernelGGL((append_kernel<ST, CT, 64>), grid, dim3(64), 0, st, k, v, slots, kc, vc, ks,
-                       vs, nb, bs, hkv);
+    hipLaunchKernelGGL((append_kernel<ST, CT, 64>), dim3((unsigned)blocks), dim3(256), 0, st, k, v,
+                       slots, kc, vc, ks, vs, rows, nb, bs, hkv);
   else
-    hipLaunchKernelGGL((append_kernel<ST, CT, 128>), grid, dim3(64), 0, st, k, v, slots, kc, vc,
-                       ks, vs, nb, bs, hkv);
+    hipLaunchKernelGGL((append_kernel<ST, CT, 128>), dim3((unsigned)blocks), dim3(256), 0, st, k,
+                       v, slots, kc, vc, ks, vs, rows, nb, bs, hkv);
   return hipGetLastError();
 }
 

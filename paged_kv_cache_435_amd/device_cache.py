@@ -1,23 +1,25 @@
 """Device-resident caches for a workload: pools filled, quantized, poisoned.
 
 Setup for tests and the benchmark.  It draws the seeded inputs of
-``workloads``, stores them in the cache format through the library's own
-``kv_quantize`` (INT8 per row / FP8 per tensor) and fills every slot no live
-token occupies with poison — NaN for float caches, a NaN scale for INT8, the
-NaN code 0x7F for FP8 — so any read of a free block, a block tail or a slot
-whose append has not happened yet shows up in the output.  The slot of each
-sequence's newest token is poisoned too when the workload appends it, so a
-missing append is visible.
+``workloads`` and writes every slot of the pools through the library's own
+``kv_cache_append`` (the way a prefill fills a cache), which stores the rows
+in the library's storage order and quantizes them for INT8 (per row) and FP8
+(with the tensor scale ``kv_quantize`` computes over the whole source pool).
+Every slot no live token occupies is written from a NaN source row — NaN for
+float caches, the NaN code 0x7F for FP8, and a NaN row scale for INT8 — so any
+read of a free block, a block tail or a slot whose append has not happened yet
+shows up in the output.  The slot of each sequence's newest token is poisoned
+too when the workload appends it, so a missing append is visible.
 
 With ``keep_sources=True`` the seeded source pools (before quantization and
-poisoning) are also kept as host tensors, so a checker can build its own stored
-cache from the same draws instead of reading the library's output.
-``to_host`` copies the stored bytes back (used to time a CPU reference on them).
+poisoning, logical ``[NB][Hkv][bs][d]`` order) are also kept as host tensors,
+so a checker can build its own stored cache from the same draws instead of
+reading the library's output.
 """
 import numpy as np
 import torch
 
-from . import kv_quantize
+from . import kv_cache_append, kv_quantize
 from . import workloads as W
 
 _CACHE_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
@@ -47,34 +49,37 @@ class DeviceCase:
         self.context_lens = torch.from_numpy(w.context_lens).to(device)
         self.q = W.query(w, device, layer)
         self.out = torch.empty_like(self.q)
+        shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
+        cdt = _CACHE_DTYPE[w.kv_format]
+        self.k_cache = torch.empty(shape, dtype=cdt, device=device)
+        self.v_cache = torch.empty(shape, dtype=cdt, device=device)
         self.k_scale = self.v_scale = None
-        caches, scales = [], []
+        if w.kv_format == "i8":
+            self.k_scale = torch.empty(shape[:-1], dtype=torch.float32, device=device)
+            self.v_scale = torch.empty(shape[:-1], dtype=torch.float32, device=device)
+        elif w.kv_format == "fp8":
+            self.k_scale = torch.empty(1, dtype=torch.float32, device=device)
+            self.v_scale = torch.empty(1, dtype=torch.float32, device=device)
+
         self.sources = {}
-        for which in ("k", "v"):
+        rows = {}
+        for which, cache, sc in (("k", self.k_cache, self.k_scale), ("v", self.v_cache, self.v_scale)):
             src = W.pool_source(w, which, device, layer)
             if keep_sources:
                 self.sources[which] = src.cpu()
-            if w.kv_format in ("f32", "f16", "bf16"):
-                src.permute(0, 2, 1, 3)[mask_t] = float("nan")
-                caches.append(src)
-                scales.append(None)
-            elif w.kv_format == "i8":
-                codes = torch.empty(src.shape, dtype=torch.int8, device=device)
-                sc = torch.empty(src.shape[:-1], dtype=torch.float32, device=device)
-                kv_quantize(src, codes, sc)
-                sc.permute(0, 2, 1)[mask_t] = float("nan")
-                caches.append(codes)
-                scales.append(sc)
-            else:
-                codes = torch.empty(src.shape, dtype=torch.uint8, device=device)
-                sc = torch.empty(1, dtype=torch.float32, device=device)
-                kv_quantize(src, codes, sc, out_dtype="fp8")
-                codes.permute(0, 2, 1, 3)[mask_t] = 0x7F
-                caches.append(codes)
-                scales.append(sc)
+            if w.kv_format == "fp8":   # tensor scale over the clean source (codes rewritten below)
+                kv_quantize(src, cache, sc, out_dtype="fp8")
+            src.permute(0, 2, 1, 3)[mask_t] = float("nan")
+            # [NB][Hkv][bs][d] -> token rows [NB*bs][Hkv][d] for the append
+            rows[which] = src.permute(0, 2, 1, 3).reshape(-1, w.num_kv_heads, w.head_dim).contiguous()
             del src
-        self.k_cache, self.v_cache = caches
-        self.k_scale, self.v_scale = scales
+        slots = torch.arange(w.num_blocks * w.block_size, dtype=torch.int64, device=device)
+        kv_cache_append(rows["k"], rows["v"], slots, self.k_cache, self.v_cache, self.k_scale,
+                        self.v_scale, kv_dtype=self.kv_dtype)
+        del rows
+        if w.kv_format == "i8":   # a NaN row quantizes as an all-zero row: poison its scale
+            self.k_scale.permute(0, 2, 1)[mask_t] = float("nan")
+            self.v_scale.permute(0, 2, 1)[mask_t] = float("nan")
         if w.appends:
             self.new_k, self.new_v = W.new_rows(w, device, layer)
             self.slots = torch.from_numpy(w.append_slots()).to(device)
@@ -91,24 +96,7 @@ def q_to_host(q):
 
 
 def cache_to_host(t, fmt):
+    """Stored bytes of a pool (library storage order) as numpy."""
     if fmt == "bf16":
         return t.view(torch.int16).cpu().numpy().view(np.uint16)
     return t.cpu().numpy()
-
-
-def to_host(case):
-    """Stored bytes of one layer, as the CPU reference takes them."""
-    w = case.w
-    h = dict(q=q_to_host(case.q), k_cache=cache_to_host(case.k_cache, w.kv_format),
-             v_cache=cache_to_host(case.v_cache, w.kv_format),
-             block_tables=w.block_tables, context_lens=w.context_lens,
-             scale=w.scale, block_size=w.block_size, kv_format=w.kv_format)
-    if w.kv_format == "i8":
-        h["k_scale"] = case.k_scale.cpu().numpy()
-        h["v_scale"] = case.v_scale.cpu().numpy()
-    elif w.kv_format == "fp8":
-        h["k_scale"] = np.float32(case.k_scale.item())
-        h["v_scale"] = np.float32(case.v_scale.item())
-    else:
-        h["k_scale"] = h["v_scale"] = None
-    return h

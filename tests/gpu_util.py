@@ -1,17 +1,19 @@
 """Shared pieces of the GPU tests.
 
-The library side: a ``DeviceCase`` (seeded sources drawn on the device, stored
-through the library's ``kv_quantize`` for INT8/FP8, unused slots poisoned), then
-``kv_cache_append`` and ``paged_attention_decode`` through the C ABI.
+The library side: a ``DeviceCase`` (seeded sources drawn on the device, written
+into the pools by the library's ``kv_cache_append``, unused slots poisoned),
+then ``kv_cache_append`` of the new tokens and ``paged_attention_decode``
+through the C ABI.
 
 The oracle side (``OracleSide``) never reads anything the library wrote: it
 takes host copies of the same seeded draws (sources, query, appended rows),
 stores them with the oracle's own quantizers, writes the appended rows with the
 oracle's own append, and attends over that.  Large cases keep only the sampled
 sequences' blocks, in a compact pool with a remapped block table (bookkeeping
-only; the oracle's arithmetic is unchanged).  The library's stored bytes at
-every live slot of those sequences are then compared bit for bit with the
-oracle's, and the attention outputs element by element.
+only; the oracle's arithmetic is unchanged).  The library's stored bytes, put
+back into logical row order by the oracle's reading of the storage format, are
+compared bit for bit with the oracle's at every live slot of those sequences,
+and the attention outputs element by element.
 """
 import sys
 
@@ -134,8 +136,9 @@ def check_stored(case, side, what=""):
         return
     idx = torch.from_numpy(side.blocks).to(case.k_cache.device)
     live = side.live_mask()
-    for name, dev, ref in (("K", case.k_cache, side.k_cache), ("V", case.v_cache, side.v_cache)):
-        got = storage(dev[idx].cpu())
+    for name, dev, ref, order in (("K", case.k_cache, side.k_cache, oracle.layout.k_from_stored),
+                                  ("V", case.v_cache, side.v_cache, oracle.layout.v_from_stored)):
+        got = order(storage(dev[idx].cpu()))     # library storage order -> logical rows
         g = got.transpose(0, 2, 1, 3)[live].view(np.uint8)
         r = ref.transpose(0, 2, 1, 3)[live].view(np.uint8)
         bad = int((g != r).sum())

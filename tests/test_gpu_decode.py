@@ -56,11 +56,11 @@ def test_zero_length_sequence_gives_zeros():
 def test_single_token_is_its_value_row_exactly():
     for q_dtype, fmt in [(torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32")]:
         w = W.custom(q_dtype, fmt, [1, 1, 1], 8, 2, 128, 16, name="ctx1")
-        case = DeviceCase(w)
+        case = DeviceCase(w, keep_sources=True)
         got = append_and_decode(case)
-        vrows = torch.stack([case.v_cache[w.block_tables[b, 0], :, 0, :] for b in range(3)])
+        vrows = torch.stack([case.sources["v"][w.block_tables[b, 0], :, 0, :] for b in range(3)])
         want = vrows.repeat_interleave(4, dim=1)
-        assert torch.equal(case.out, want.to(case.out.dtype)), fmt
+        assert torch.equal(case.out.cpu(), want.to(case.out.dtype)), fmt
 
 
 def test_permuting_physical_blocks_is_bit_identical():
@@ -121,13 +121,20 @@ def test_needles_localise_every_position(bs):
     w = W.custom(torch.float32, "f32", [ctx] * len(positions), 4, 1, 64, bs, name="needles")
     case = DeviceCase(w, keep_sources=True)
     q = case.q
+    slots, krows, vrows = [], [], []
     for b, t in enumerate(positions):
         blk = int(w.block_tables[b, t // bs])
         qh = q[b, 0] / q[b, 0].norm()
         row = 60.0 * qh * 8.0            # scale 1/8 -> logit gap ~60
-        case.k_cache[blk, 0, t % bs] = row
         case.sources["k"][blk, 0, t % bs] = row.cpu()
+        slots.append(blk * bs + t % bs)
+        krows.append(row.view(1, 64))
+        vrows.append(case.sources["v"][blk, 0, t % bs].view(1, 64).cuda())
         q[b, 1:] = q[b, 0]
+    # The needle rows go in through the library's own append.
+    pkv.kv_cache_append(torch.stack(krows), torch.stack(vrows),
+                        torch.tensor(slots, dtype=torch.int64, device="cuda"),
+                        case.k_cache, case.v_cache)
     got = append_and_decode(case)
     for b, t in enumerate(positions):
         blk = int(w.block_tables[b, t // bs])

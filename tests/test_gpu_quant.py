@@ -126,11 +126,14 @@ def test_append_whole_pool_bit_exact(src_dtype, fmt, bs, d):
     torch.cuda.synchronize()
     np_scale = (lambda t: None if t is None else (t.numpy() if t.numel() > 1
                                                   else np.float32(t.item())))
+    # The pools hold bytes in the library's storage order: the oracle reads
+    # them in logical row order, before and after.
+    K, V = oracle.layout.k_from_stored, oracle.layout.v_from_stored
     ek, ev, eks, evs = oracle.append.append_expected(
-        _np_storage(kc), _np_storage(vc), _np_storage(kn), _np_storage(vn), slots.numpy(), bs,
-        fmt, np_scale(ks), np_scale(vs))
-    assert np.array_equal(_np_storage(kcd.cpu()).view(np.uint8), ek.view(np.uint8))
-    assert np.array_equal(_np_storage(vcd.cpu()).view(np.uint8), ev.view(np.uint8))
+        K(_np_storage(kc)), V(_np_storage(vc)), _np_storage(kn), _np_storage(vn), slots.numpy(),
+        bs, fmt, np_scale(ks), np_scale(vs))
+    assert np.array_equal(K(_np_storage(kcd.cpu())).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(V(_np_storage(vcd.cpu())).view(np.uint8), ev.view(np.uint8))
     if fmt == "i8":
         assert np.array_equal(ksd.cpu().numpy().view(np.uint32), eks.view(np.uint32))
         assert np.array_equal(vsd.cpu().numpy().view(np.uint32), evs.view(np.uint32))
