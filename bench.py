@@ -30,6 +30,13 @@ import time
 
 METRIC = "decode attention tokens/s + KV-read HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+COUNTERS = os.path.join(ROOT, "profiles", "decode_counters_llama70b_gqa8.json")
+DECODE_SOURCES = ("paged_kv_cache_435_amd/csrc/pkv_decode.hip",
+                  "paged_kv_cache_435_amd/csrc/pkv_common.h",
+                  "paged_kv_cache_435_amd/csrc/pkv_internal.h")
+DECODE_KERNELS = ("decode_partition_kernel", "decode_merge_kernel")
+COPY_KERNEL = "pkv_probe_copy_kernel"
 
 
 def log(*a):
@@ -57,6 +64,59 @@ def parse():
     return ap.parse_args()
 
 
+def decode_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_counters(fetch_csv, write_csv, copy_mib, command):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the decode kernels and of the
+    plain copy kernel, averaged over dispatches, from two rocprofv3 --pmc runs
+    (counter_collection.csv), written to the counters file with the hash of the
+    decode sources they were taken on."""
+    import csv
+
+    def per_kernel(path):
+        acc = {}
+        for row in csv.DictReader(open(path)):
+            name = row["Kernel_Name"]
+            for k in DECODE_KERNELS + (COPY_KERNEL,):
+                if k in name:
+                    acc.setdefault(k, []).append(float(row["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}
+
+    fetch, write = per_kernel(fetch_csv), per_kernel(write_csv)
+    out = {"about": "rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch, averaged), "
+                    "decode kernels on the llama70b_gqa8 workload and the plain copy kernel "
+                    "of known size for calibration",
+           "command": command, "decode_sources_sha256": decode_sources_sha256(),
+           "copy_bytes": copy_mib << 20,
+           "fetch_kib": fetch, "write_kib": write}
+    with open(COUNTERS, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+    print(json.dumps(out, indent=1, sort_keys=True))
+
+
+def decode_traffic(workload):
+    """HBM bytes one decode call moves (partition + merge kernels), from the
+    committed counters scaled by what the same counters read for the copy
+    kernel; None if they were taken on other decode sources or workload."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if workload != "llama70b_gqa8" or c.get("decode_sources_sha256") != decode_sources_sha256():
+        return None
+    f_scale = c["copy_bytes"] / (c["fetch_kib"][COPY_KERNEL] * 1024)
+    w_scale = c["copy_bytes"] / (c["write_kib"][COPY_KERNEL] * 1024)
+    return sum(c["fetch_kib"][k] * 1024 * f_scale + c["write_kib"][k] * 1024 * w_scale
+               for k in DECODE_KERNELS)
+
+
 def kernel_launch_times(pairs):
     return [a.elapsed_time(b) * 1e-3 for a, b in pairs]   # seconds
 
@@ -79,40 +139,52 @@ def cpu_baseline(w, cases, budget_s):
     except Exception:  # pragma: no cover - informational only
         cores = 1
     order = np.random.default_rng(7).permutation(w.batch)
-    spent, seqs, layer_calls = 0.0, 0, 0
+    spent, layer_calls, passes, tokens_ctx = 0.0, 0, 0, 0
     case = cases[0]
-    for b in order:
-        ctx = int(w.context_lens[b])
-        nblk = -(-ctx // w.block_size)
-        phys = torch.from_numpy(w.block_tables[b, :nblk].astype(np.int64)).to(case.k_cache.device)
-        kc = oracle.layout.k_from_stored(cache_to_host(case.k_cache[phys], w.kv_format))
-        vc = oracle.layout.v_from_stored(cache_to_host(case.v_cache[phys], w.kv_format))
-        ks = vs = None
-        if w.kv_format == "i8":
-            ks, vs = case.k_scale[phys].cpu().numpy(), case.v_scale[phys].cpu().numpy()
-        elif w.kv_format == "fp8":
-            ks, vs = np.float32(case.k_scale.item()), np.float32(case.v_scale.item())
-        q = q_to_host(case.q[b:b + 1])
-        bt = np.arange(nblk, dtype=np.int32)[None]
-        cl = np.array([ctx], dtype=np.int32)
-        t0 = time.perf_counter()
-        oracle.decode_attention(q, kc, vc, bt, cl, w.scale, w.block_size, w.kv_format, ks, vs)
-        spent += time.perf_counter() - t0
-        seqs += 1
-        layer_calls += 1
-        if spent >= budget_s:
-            break
+    host = {}
+    done = False
+    while not done:
+        passes += 1
+        for b in order:
+            if int(b) not in host:
+                ctx = int(w.context_lens[b])
+                nblk = -(-ctx // w.block_size)
+                phys = torch.from_numpy(w.block_tables[b, :nblk].astype(np.int64)).to(
+                    case.k_cache.device)
+                kc = oracle.layout.k_from_stored(cache_to_host(case.k_cache[phys], w.kv_format))
+                vc = oracle.layout.v_from_stored(cache_to_host(case.v_cache[phys], w.kv_format))
+                ks = vs = None
+                if w.kv_format == "i8":
+                    ks, vs = case.k_scale[phys].cpu().numpy(), case.v_scale[phys].cpu().numpy()
+                elif w.kv_format == "fp8":
+                    ks, vs = np.float32(case.k_scale.item()), np.float32(case.v_scale.item())
+                host[int(b)] = (q_to_host(case.q[b:b + 1]), kc, vc, ks, vs,
+                                np.arange(nblk, dtype=np.int32)[None],
+                                np.array([ctx], dtype=np.int32))
+            q, kc, vc, ks, vs, bt, cl = host[int(b)]
+            t0 = time.perf_counter()
+            oracle.decode_attention(q, kc, vc, bt, cl, w.scale, w.block_size, w.kv_format, ks, vs)
+            spent += time.perf_counter() - t0
+            layer_calls += 1
+            tokens_ctx += int(cl[0])
+            if spent >= budget_s:
+                done = True
+                break
     # One sequence-layer of oracle work stands for 1/layers of a decoded token.
     tokens = layer_calls / w.layers
     return {"value": tokens / spent, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{seqs} of {w.batch} sequences of {w.name} (layer 0, all "
-                       f"{w.num_q_heads} query heads, contexts summing to "
-                       f"{int(sum(int(w.context_lens[b]) for b in order[:seqs]))} tokens), "
-                       f"{spent:.1f} s of float64 oracle time"
+            "sample": (f"{layer_calls} sequence decodes of {w.name} (layer 0, all "
+                       f"{w.num_q_heads} query heads each; {passes} pass(es) over the "
+                       f"{w.batch} sequences in a seeded order, {tokens_ctx} context tokens "
+                       f"in all), {spent:.1f} s of float64 oracle time"
                        + ("; per-layer cost scaled by the layer count" if w.layers > 1 else ""))}
 
 
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        # bench.py --summarize-counters FETCH_CSV WRITE_CSV COPY_MIB "COMMAND"
+        summarize_counters(sys.argv[2], sys.argv[3], int(sys.argv[4]), sys.argv[5])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -264,7 +336,8 @@ def main():
         "read_ceiling_gbps": ceiling,
         "kv_pct_of_read_ceiling": None if not ceiling else achieved / ceiling * 100.0,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": decode_traffic(w.name),
                      "kernel": "paged_attention_decode",
                      "bytes_per_launch": kv_bytes, "avg_launch_us": avg_launch * 1e6},
         "cold_cache": cold,

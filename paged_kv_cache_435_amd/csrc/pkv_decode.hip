@@ -41,14 +41,19 @@
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_NT_LOADS            KV loads carry the non-temporal hint
 //   PKV_WAVES_PER_EU        occupancy target, 16-bit and f32 KV
+//   PKV_STAGES_2B           pipeline depth (tiles in flight), 16-bit and f32 KV
 //   PKV_STAGES_1B           pipeline depth (tiles in flight), 1-byte KV
 //   PKV_WAVES_1B            occupancy target, 1-byte KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
+//   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
 #ifndef PKV_WAVES_PER_EU
 #define PKV_WAVES_PER_EU 3
+#endif
+#ifndef PKV_STAGES_2B
+#define PKV_STAGES_2B 2
 #endif
 #ifndef PKV_STAGES_1B
 #define PKV_STAGES_1B 2
@@ -57,7 +62,10 @@
 #define PKV_WAVES_1B 3
 #endif
 #ifndef PKV_SLOTS_PER_CU_DEFAULT
-#define PKV_SLOTS_PER_CU_DEFAULT 12
+#define PKV_SLOTS_PER_CU_DEFAULT 8
+#endif
+#ifndef PKV_SLOTS_PER_CU_I8
+#define PKV_SLOTS_PER_CU_I8 12
 #endif
 
 namespace pkv {
@@ -367,10 +375,13 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 
 // Occupancy target per KV type: 16-bit and f32 tiles keep two in flight at 3
 // waves per SIMD; 1-byte tiles keep four in flight at 2 waves per SIMD.
+// Items planned per CU and round: 8 for 16-bit, f32 and FP8 KV; INT8, whose
+// tiles carry more vector work (per-token scales), keeps 12 waves per CU busy.
 template <int KV>
 struct Tuning {
-  static constexpr int stages = dtype_bytes(KV) == 1 ? PKV_STAGES_1B : 2;
+  static constexpr int stages = dtype_bytes(KV) == 1 ? PKV_STAGES_1B : PKV_STAGES_2B;
   static constexpr int waves_per_eu = dtype_bytes(KV) == 1 ? PKV_WAVES_1B : PKV_WAVES_PER_EU;
+  static constexpr int slots_per_cu = KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8 : PKV_SLOTS_PER_CU_DEFAULT;
 };
 
 template <int KV, int QT, int D, int BS>
@@ -786,12 +797,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // Items planned per compute unit and round.  Fewer concurrent waves than the
 // kernel's occupancy allows read HBM more efficiently (fewer streams fighting
 // over DRAM rows), as long as enough bytes stay in flight.  PKV_SLOTS_PER_CU
-// overrides the default (tuning).
-static int slots_per_cu() {
+// overrides the per-type default (tuning); 0 when unset.
+static int slots_per_cu_override() {
   static const int v = [] {
     const char* e = getenv("PKV_SLOTS_PER_CU");
     const int x = e ? atoi(e) : 0;
-    return x > 0 ? x : PKV_SLOTS_PER_CU_DEFAULT;
+    return x > 0 ? x : 0;
   }();
   return v;
 }
@@ -804,8 +815,9 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
       &per_cu, reinterpret_cast<const void*>(kern), 64, 0);
   if (e != hipSuccess) return e;
   per_cu = per_cu < 1 ? 1 : (per_cu > kWavesPerCuCap ? kWavesPerCuCap : per_cu);
-  const int target = slots_per_cu();
-  if (target > 0 && target < per_cu) per_cu = target;
+  const int target = slots_per_cu_override() > 0 ? slots_per_cu_override()
+                                                 : Tuning<KV>::slots_per_cu;
+  if (target < per_cu) per_cu = target;
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.num_kv_heads * a.head_tiles;

@@ -10,14 +10,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-namespace {
-
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBlocks = 256 * 8;   // 8 workgroups per compute unit
 
-__global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict__ x, int64_t n,
+}  // namespace
+
+__global__ __launch_bounds__(kThreads) void pkv_probe_read_kernel(const u32x4* __restrict__ x, int64_t n,
                                                         uint32_t* __restrict__ sink) {
   const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -38,13 +40,11 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const u32x4* __restrict_
   sink[tid] = acc;
 }
 
-__global__ __launch_bounds__(kThreads) void copy_kernel(u32x4* __restrict__ dst,
+__global__ __launch_bounds__(kThreads) void pkv_probe_copy_kernel(u32x4* __restrict__ dst,
                                                         const u32x4* __restrict__ src, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
-
-}  // namespace
 
 extern "C" {
 
@@ -52,7 +52,7 @@ int32_t pkv_probe_grid(void) { return kBlocks * kThreads; }
 
 int32_t pkv_probe_read(const void* x, uint64_t bytes, uint32_t* sink, void* stream) {
   if (!x || !sink || bytes % 16) return 1;
-  hipLaunchKernelGGL(read_kernel, dim3(kBlocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL(pkv_probe_read_kernel, dim3(kBlocks), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const u32x4*>(x),
                      (int64_t)(bytes / 16), sink);
   return hipGetLastError() == hipSuccess ? 0 : 4;
@@ -60,7 +60,7 @@ int32_t pkv_probe_read(const void* x, uint64_t bytes, uint32_t* sink, void* stre
 
 int32_t pkv_probe_copy(void* dst, const void* src, uint64_t bytes, void* stream) {
   if (!dst || !src || bytes % 16) return 1;
-  hipLaunchKernelGGL(copy_kernel, dim3(kBlocks), dim3(kThreads), 0,
+  hipLaunchKernelGGL(pkv_probe_copy_kernel, dim3(kBlocks), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<u32x4*>(dst),
                      static_cast<const u32x4*>(src), (int64_t)(bytes / 16));
   return hipGetLastError() == hipSuccess ? 0 : 4;
