@@ -82,9 +82,8 @@ struct MfmaOf {
 //
 // Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
 // packed two elements per 32-bit word; for f32 it is one float per word.
-// FP8 -> f16 uses the bit layout: the code's 7 magnitude bits shifted into an
-// f16's exponent/mantissa give decode(code) * 2^-8 exactly (subnormals too);
-// the 2^8 is folded into the scales.  INT8 -> f16 uses 1024 + (q + 128) - 1152.
+// FP8 -> f16/bf16/f32 uses gfx950's E4M3 conversions (exact).  INT8 -> f16
+// uses 1024 + (q + 128) - 1152.
 // ---------------------------------------------------------------------------
 template <int KV, int MT>
 struct Cvt {
@@ -106,11 +105,19 @@ struct Cvt {
       w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
       w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
     } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F16) {
-      // bytes b0 b1 -> [0, b0, 0, b1]; b2 b3 -> [0, b2, 0, b3]
-      const uint32_t lo = __builtin_amdgcn_perm(0u, raw, 0x010C000Cu);
-      const uint32_t hi = __builtin_amdgcn_perm(0u, raw, 0x030C020Cu);
-      w[0] = (lo & 0x80008000u) | ((lo & 0x7F007F00u) >> 1);
-      w[1] = (hi & 0x80008000u) | ((hi & 0x7F007F00u) >> 1);
+      // gfx950 converts OCP E4M3 pairs to f16 (exact; scale 1).
+      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
+      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, true));
+    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_BF16) {
+      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, false));
+      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, true));
+    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F32) {
+      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw, 1.0f, false);
+      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw, 1.0f, true);
+      w[0] = fbits(lo[0]);
+      w[1] = fbits(lo[1]);
+      w[2] = fbits(hi[0]);
+      w[3] = fbits(hi[1]);
     } else {
       // Generic: through f32 (exact for every pair built here).
       constexpr int per = 4 / eb;   // elements in the word
@@ -150,10 +157,11 @@ struct Cvt {
   }
 };
 
-// Extra factor the conversion above leaves in the value (2^-8 for FP8 via f16).
+// Extra factor the conversion above leaves in the value (none: every
+// conversion is exact).
 template <int KV, int MT>
 __host__ __device__ constexpr float cvt_gain() {
-  return (KV == PKV_FP8_E4M3FN && MT == MT_F16) ? 256.0f : 1.0f;
+  return 1.0f;
 }
 
 // One query element (stored as QT) as an MFMA element (16-bit pattern or f32 bits).
@@ -533,12 +541,16 @@ void decode_partition_kernel(DecodeArgs a) {
 
   // Softmax update and both contractions for one loaded tile.
   auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1) {
-    f32x4 ksc = {1.f, 1.f, 1.f, 1.f}, vsc = ksc;
+    // INT8: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane takes
+    // its four tokens' values from its row's first four lanes.
+    f32x4 krcp = {1.f, 1.f, 1.f, 1.f}, vrcp = krcp;
     if constexpr (KV == PKV_I8) {
+      const float kr1 = __builtin_amdgcn_rcpf(ks1);
+      const float vr1 = __builtin_amdgcn_rcpf(vs1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ksc[i] = __shfl(ks1, 16 * c16 + i, kWave);
-        vsc[i] = __shfl(vs1, 16 * c16 + i, kWave);
+        krcp[i] = __shfl(kr1, 16 * c16 + i, kWave);
+        vrcp[i] = __shfl(vr1, 16 * c16 + i, kWave);
       }
     }
     const int t0 = t_begin + tile * 16;
@@ -587,7 +599,7 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       const bool ok = 4 * c16 + i < n_valid;
       float f = kfac;
-      if constexpr (KV == PKV_I8) f = kfac * __builtin_amdgcn_rcpf(ksc[i]);   // 1/s to ~1 ulp
+      if constexpr (KV == PKV_I8) f = kfac * krcp[i];
       z[i] = ok ? s[i] * f : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
@@ -615,7 +627,7 @@ void decode_partition_kernel(DecodeArgs a) {
     }
     if constexpr (KV == PKV_I8) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * __builtin_amdgcn_rcpf(vsc[i]) : 0.f;
+      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * vrcp[i] : 0.f;
     }
 
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
@@ -642,6 +654,7 @@ void decode_partition_kernel(DecodeArgs a) {
       const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
       const uint32_t m01 = (vmask[0] & 0xFFFFu) | (vmask[1] & 0xFFFF0000u);
       const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
+      const bool full = n_valid == 16;   // uniform: only a sequence's last tile is partial
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
         uint32_t w[2];
@@ -651,7 +664,8 @@ void decode_partition_kernel(DecodeArgs a) {
           w[0] = vraw[nc / VG][2 * (nc % VG)];
           w[1] = vraw[nc / VG][2 * (nc % VG) + 1];
         }
-        const u32x2 va = {w[0] & m01, w[1] & m23};
+        u32x2 va = {w[0], w[1]};
+        if (!full) va = u32x2{w[0] & m01, w[1] & m23};
         if constexpr (MT == MT_F16) {
           acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
                                                           __builtin_bit_cast(f16x4, pb), acc[nc],
