@@ -51,9 +51,11 @@ int device_cus() {
   return cus;
 }
 
-// Workspace rows hold one (max, sum) pair and one head_dim-long output per
-// (item, head of its 16-head tile).
+// Workspace: per sequence (first item, items per unit), 16 B, padded to 256 B;
+// then rows of one (max, sum) pair and one head_dim-long output per (item, head
+// of its 16-head tile).
 int64_t row_bytes(int64_t head_dim) { return 16 * (2 + head_dim) * 4; }
+int64_t seq_bytes(int64_t batch) { return (batch * 16 + 255) / 256 * 256; }
 
 // Items the plan can make for these sizes when it plans for the largest slot
 // count (kMaxSlots; a device with fewer resident waves makes fewer items).
@@ -86,8 +88,8 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
   if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
       head_dim <= 0 || max_context_len <= 0)
     return 0;
-  return (size_t)(workspace_items(batch, num_q_heads, num_kv_heads, max_context_len) *
-                  row_bytes(head_dim));
+  const int64_t items = workspace_items(batch, num_q_heads, num_kv_heads, max_context_len);
+  return items > 0 ? (size_t)(seq_bytes(batch) + items * row_bytes(head_dim)) : 0;
 }
 
 pkv_status kv_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t row_len,
@@ -184,7 +186,7 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   const int64_t items = workspace_items(batch, num_q_heads, num_kv_heads, max_context_len);
   if (items > 0x7FFFFFF0)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: batch x heads x context too large");
-  const size_t need = (size_t)(items * row_bytes(head_dim));
+  const size_t need = items > 0 ? (size_t)(seq_bytes(batch) + items * row_bytes(head_dim)) : 0;
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "paged_attention_decode: workspace needs " +
                                        std::to_string(need) + " bytes, got " +
@@ -213,8 +215,10 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   const int cus = device_cus();
   if (cus <= 0) return fail(PKV_ERR_HIP, "paged_attention_decode: cannot query the device");
   if (need > 0) {
-    a.ws_ml = static_cast<float*>(workspace);
-    a.ws_acc = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + items * 16 * 2 * 4);
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.ws_seq = reinterpret_cast<int64_t*>(w);
+    a.ws_ml = reinterpret_cast<float*>(w + seq_bytes(batch));
+    a.ws_acc = reinterpret_cast<float*>(w + seq_bytes(batch) + items * 16 * 2 * 4);
   }
   return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, cus,
                                        static_cast<hipStream_t>(stream)),

@@ -340,30 +340,6 @@ __device__ bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int l
   return false;
 }
 
-// The item range of sequence b.
-__device__ SeqItems items_of_seq(const DecodeArgs& a, const Plan& p, int b, int lane) {
-  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
-  int64_t base = 0;
-  SeqItems s{};
-  for (int b0 = 0; b0 <= b; b0 += kWave) {
-    const int bb = b0 + lane;
-    const int ctx = bb < a.batch ? seq_ctx(a, bb) : 0;
-    const int n = (ctx + kTileTokens - 1) / kTileTokens;
-    const int m = (n + p.tpi - 1) / p.tpi;
-    const int64_t cnt = (int64_t)m * units_per_seq;
-    const int64_t incl = wave_incl_scan_i64(cnt, lane) + base;
-    if (b < b0 + kWave) {
-      const int L = b - b0;
-      s.first = readlane_i64(incl - cnt, L);
-      s.ctx = __builtin_amdgcn_readlane(ctx, L);
-      s.n = __builtin_amdgcn_readlane(n, L);
-      s.m = __builtin_amdgcn_readlane(m, L);
-    }
-    base = readlane_i64(incl, kWave - 1);
-  }
-  return s;
-}
-
 // ---------------------------------------------------------------------------
 // Partition kernel.
 //
@@ -431,6 +407,12 @@ void decode_partition_kernel(DecodeArgs a) {
   t_end = uni(t_end < ctx ? t_end : ctx);
   const int ntiles = (t_end - t_begin + 15) >> 4;
   const bool whole_unit = sq.m == 1;
+  // The first item of each sequence records where its items start and how
+  // many each unit has, for the merge kernel.
+  if (a.ws_seq && local == 0 && lane == 0) {
+    a.ws_seq[2 * b] = sq.first;
+    a.ws_seq[2 * b + 1] = sq.m;
+  }
 
   const int G = a.num_q_heads / a.num_kv_heads;
   const int h_first = g * G + ht * 16;              // first query head of this tile
@@ -741,12 +723,12 @@ void decode_partition_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of a unit's items: out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
-// One wave per (query head, sequence), planning like the item kernel to find
-// the unit's items.  D/4 lanes cover one partial row with 16-byte loads, so
-// one load instruction takes 64/(D/4) items at once; the lane groups are added
-// in a fixed order at the end (results do not depend on timing).  A sequence
-// with no context gets zeros here; a unit that was one item was finished by
-// the item kernel.
+// One wave per (query head, sequence); the item kernel recorded each
+// sequence's first item and items per unit.  D/4 lanes cover one partial row
+// with 16-byte loads, so one load instruction takes 64/(D/4) items at once; the
+// lane groups are added in a fixed order at the end (results do not depend on
+// timing).  A sequence with no context gets zeros here; a unit that was one
+// item was finished by the item kernel.
 // ---------------------------------------------------------------------------
 template <int QT, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
@@ -755,16 +737,18 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  const Plan plan = make_plan(a, lane);
-  const SeqItems sq = items_of_seq(a, plan, b, lane);
   const int64_t hq = (int64_t)b * a.num_q_heads + h;
   const int grp = lane / LPP;         // which partial of an instruction
   const int dq = lane % LPP;          // which 4 output elements
-  if (sq.m == 0) {
+  if (seq_ctx(a, b) == 0) {
     if (grp == 0) store_out4<QT>(a.out, hq * D + 4 * dq, 0.f, 0.f, 0.f, 0.f);
     return;
   }
-  if (sq.m == 1) return;
+  if (!a.ws_seq) return;              // no workspace: every unit was one item
+  SeqItems sq{};
+  sq.first = a.ws_seq[2 * b];
+  sq.m = (int)a.ws_seq[2 * b + 1];
+  if (sq.m <= 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int g = h / G;
   const int ht = (h % G) / 16;

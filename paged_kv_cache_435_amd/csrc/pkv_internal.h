@@ -29,8 +29,9 @@ struct DecodeArgs {
   const float* v_scale;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_ml;    // [max_items][16][2]: running max (log2 domain), sum
-  float* ws_acc;   // [max_items][16][head_dim]: unnormalised output
+  int64_t* ws_seq;  // [batch][2]: first item and items per unit of each sequence
+  float* ws_ml;     // [max_items][16][2]: running max (log2 domain), sum
+  float* ws_acc;    // [max_items][16][head_dim]: unnormalised output
   int32_t batch;
   int32_t num_q_heads;
   int32_t num_kv_heads;

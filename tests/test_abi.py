@@ -52,7 +52,8 @@ def test_workspace_sizing(lib):
         ws = pkv.paged_attention_workspace_size(B, Hq, Hkv, d, ctx)
         units = B * Hkv * -(-(Hq // Hkv) // 16)
         row = 16 * (2 + d) * 4
-        assert ws % row == 0 and ws // row >= units + 256 * 12
+        per_seq = -(-B * 16 // 256) * 256          # (first item, items per unit) per sequence
+        assert (ws - per_seq) % row == 0 and (ws - per_seq) // row >= units + 256 * 12
 
 
 def _decode(lib, **kw):
