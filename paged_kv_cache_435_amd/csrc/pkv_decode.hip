@@ -42,7 +42,8 @@
 //   PKV_NT_LOADS            KV loads carry the non-temporal hint
 //   PKV_WAVES_PER_EU        occupancy target, 16-bit and f32 KV
 //   PKV_STAGES_2B           pipeline depth (tiles in flight), 16-bit and f32 KV
-//   PKV_STAGES_1B           pipeline depth (tiles in flight), 1-byte KV
+//   PKV_STAGES_I8           pipeline depth (tiles in flight), INT8 KV
+//   PKV_STAGES_FP8          pipeline depth (tiles in flight), FP8 KV
 //   PKV_WAVES_1B            occupancy target, 1-byte KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
@@ -55,8 +56,11 @@
 #ifndef PKV_STAGES_2B
 #define PKV_STAGES_2B 2
 #endif
-#ifndef PKV_STAGES_1B
-#define PKV_STAGES_1B 2
+#ifndef PKV_STAGES_I8
+#define PKV_STAGES_I8 2
+#endif
+#ifndef PKV_STAGES_FP8
+#define PKV_STAGES_FP8 2
 #endif
 #ifndef PKV_WAVES_1B
 #define PKV_WAVES_1B 3
@@ -363,7 +367,8 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 // tiles carry more vector work (per-token scales), keeps 12 waves per CU busy.
 template <int KV>
 struct Tuning {
-  static constexpr int stages = dtype_bytes(KV) == 1 ? PKV_STAGES_1B : PKV_STAGES_2B;
+  static constexpr int stages =
+      KV == PKV_I8 ? PKV_STAGES_I8 : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
   static constexpr int waves_per_eu = dtype_bytes(KV) == 1 ? PKV_WAVES_1B : PKV_WAVES_PER_EU;
   static constexpr int slots_per_cu = KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8 : PKV_SLOTS_PER_CU_DEFAULT;
 };
@@ -515,8 +520,10 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + loff + 1024 * j);
     if constexpr (KV == PKV_I8) {
-      ks = a.k_scale[row0 + scale_tok];
-      vs = a.v_scale[row0 + scale_tok];
+      const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)row0 >> 32))
+                           << 32) | (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)row0);
+      ks = (a.k_scale + sb)[scale_tok];
+      vs = (a.v_scale + sb)[scale_tok];
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the compute they overlap
   };

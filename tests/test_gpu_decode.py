@@ -167,3 +167,16 @@ def test_workspace_too_small_raises():
 def test_planner_shapes(name, ctx, hq, hkv, d, bs):
     w = W.custom(torch.float16, "f16", ctx, hq, hkv, d, bs, name=name)
     run_and_check(w)
+
+
+@pytest.mark.parametrize("q_dtype,kv", [
+    (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
+    (torch.float16, "i8"), (torch.bfloat16, "fp8"), (torch.float32, "i8"), (torch.float32, "fp8"),
+])
+@pytest.mark.parametrize("bs", [16, 256])
+def test_head_dim_64_every_format(q_dtype, kv, bs):
+    """d = 64: one 1 KB piece per 16-token group for 1-byte KV, two for 16-bit,
+    four for f32 (each a different operand order), with appends and ragged tails."""
+    w = W.custom(q_dtype, kv, [1, 17, 300, 1025, 2600], 8, 2, 64, bs, appends=True,
+                 name=f"d64-{kv}-bs{bs}")
+    run_and_check(w)
