@@ -40,11 +40,10 @@
 
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_NT_LOADS            KV loads carry the non-temporal hint
-//   PKV_WAVES_PER_EU        occupancy target, 16-bit and f32 KV
+//   PKV_WAVES_PER_EU        occupancy target, KV other than INT8
 //   PKV_STAGES_2B           pipeline depth (tiles in flight), 16-bit and f32 KV
 //   PKV_STAGES_I8           pipeline depth (tiles in flight), INT8 KV
 //   PKV_STAGES_FP8          pipeline depth (tiles in flight), FP8 KV
-//   PKV_WAVES_1B            occupancy target, 1-byte KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
 #ifndef PKV_NT_LOADS
@@ -54,22 +53,19 @@
 #define PKV_WAVES_PER_EU 3
 #endif
 #ifndef PKV_STAGES_2B
-#define PKV_STAGES_2B 2
+#define PKV_STAGES_2B 1
 #endif
 #ifndef PKV_STAGES_I8
-#define PKV_STAGES_I8 2
+#define PKV_STAGES_I8 1
 #endif
 #ifndef PKV_STAGES_FP8
 #define PKV_STAGES_FP8 2
-#endif
-#ifndef PKV_WAVES_1B
-#define PKV_WAVES_1B 3
 #endif
 #ifndef PKV_SLOTS_PER_CU_DEFAULT
 #define PKV_SLOTS_PER_CU_DEFAULT 8
 #endif
 #ifndef PKV_SLOTS_PER_CU_I8
-#define PKV_SLOTS_PER_CU_I8 12
+#define PKV_SLOTS_PER_CU_I8 16
 #endif
 
 namespace pkv {
@@ -361,15 +357,17 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 }
 
 
-// Occupancy target per KV type: 16-bit and f32 tiles keep two in flight at 3
-// waves per SIMD; 1-byte tiles keep four in flight at 2 waves per SIMD.
-// Items planned per CU and round: 8 for 16-bit, f32 and FP8 KV; INT8, whose
-// tiles carry more vector work (per-token scales), keeps 12 waves per CU busy.
+// Per KV type: pipeline depth (tiles in flight per wave), occupancy target and
+// items planned per CU and round.  Measured on MI355X, HBM streams best with
+// roughly 14-16 MB outstanding over the chip: 16-bit and f32 KV (8 KB tiles)
+// run without prefetch at 8 waves per CU; FP8 (4 KB tiles) keeps two tiles in
+// flight at 8 waves per CU; INT8, whose tiles carry more vector work (row
+// scales), runs without prefetch at 16 waves per CU.
 template <int KV>
 struct Tuning {
   static constexpr int stages =
       KV == PKV_I8 ? PKV_STAGES_I8 : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
-  static constexpr int waves_per_eu = dtype_bytes(KV) == 1 ? PKV_WAVES_1B : PKV_WAVES_PER_EU;
+  static constexpr int waves_per_eu = KV == PKV_I8 ? 4 : PKV_WAVES_PER_EU;
   static constexpr int slots_per_cu = KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8 : PKV_SLOTS_PER_CU_DEFAULT;
 };
 

@@ -15,7 +15,7 @@ namespace pkv {
 constexpr int kTileTokens = 16;
 constexpr int kItemTilesMin = 16;    // 256 tokens: keeps merge work small for short batches
 constexpr int kItemTilesMax = 256;   // 4096 tokens: 4 block-table registers per lane at bs 16
-constexpr int kWavesPerCuCap = 12;   // at most 3 waves per SIMD are planned for
+constexpr int kWavesPerCuCap = 16;   // at most 4 waves per SIMD are planned for
 constexpr int kMaxCus = 256;         // MI355X; plans never use more slots than this many CUs give
 constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
 
