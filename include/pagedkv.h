@@ -183,6 +183,89 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   int32_t max_context_len, float scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * kv_copy_blocks — copy whole physical blocks inside the pools (copy-on-write
+ * of a shared block before an append, or compaction): for each pair i,
+ * block pairs[2i + 1] of both caches (and, for INT8, of both scale arrays)
+ * becomes a byte-for-byte copy of block pairs[2i].
+ *
+ *   k_cache, v_cache, k_scale, v_scale  device, as for kv_cache_append (scales
+ *                 are read only for PKV_I8; FP8's one tensor scale needs no copy).
+ *   pairs         device int32 [n_pairs][2] (src, dst).  Pairs with an index
+ *                 outside [0, num_blocks) or src == dst are skipped.  The copies
+ *                 of one call run concurrently: no dst may be another pair's src.
+ *   Errors: PKV_ERR_INVALID_ARG (NULL pointers, misalignment, bad sizes),
+ *           PKV_ERR_UNSUPPORTED (unknown dtype), PKV_ERR_HIP.
+ */
+pkv_status kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                          int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t kv_dtype, const int32_t* pairs,
+                          int32_t n_pairs, void* stream);
+
+/*
+ * Block manager — host-side allocation of physical blocks to sequences
+ * ([P1] §2: fixed-size blocks, a block table per sequence, reference counts
+ * so blocks can be shared; [P3] PagedAttention section: blocks are taken on
+ * demand and returned as soon as a sequence ends; [P2] §4 and [P3]: prefix
+ * caching).  It only hands out block numbers; device memory is untouched.
+ *
+ * Rules:
+ *   - A block referenced by more than one sequence is never written.  Appending
+ *     into a shared, partly filled last block first gives the sequence a fresh
+ *     block and reports (src, dst) so the caller can run kv_copy_blocks before
+ *     writing the new rows (copy-on-write).
+ *   - With prefix caching, each full block is keyed by a hash chained over all
+ *     token ids from the sequence start through the block's end; a new
+ *     sequence whose leading full blocks match cached keys shares those blocks
+ *     (their slots come back as -1: their rows are already stored, and
+ *     kv_cache_append skips negative slots).  Unreferenced cached blocks stay
+ *     reusable until a fresh block is needed and no free block is left; then
+ *     the least recently released is taken.
+ *   - Failed calls change nothing.  Every call is host only and thread-safe.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* Text of the last failed block-manager call on this thread. */
+const char* pkv_bm_last_error(void);
+
+/* New manager over blocks 0 .. num_blocks-1 of block_size tokens; NULL on bad
+ * sizes.  Blocks are handed out lowest number first while never used. */
+pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
+                                 int32_t enable_prefix_caching);
+void pkv_bm_destroy(pkv_block_manager* bm);
+
+/* Blocks a fresh allocation can still take (free plus unreferenced cached). */
+int32_t pkv_bm_num_free(pkv_block_manager* bm);
+/* References held on a block (-1 for a bad index). */
+int32_t pkv_bm_ref_count(pkv_block_manager* bm, int32_t block);
+
+/* Starts sequence seq_id with its n prompt tokens (host int32 ids; ids only
+ * matter for prefix caching).  Writes the pool slot of every token to host
+ * slots[n] (-1 for tokens in shared cached blocks).  PKV_ERR_INVALID_ARG if the
+ * id is in use or the blocks run out. */
+pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
+                               int32_t n, int64_t* slots);
+
+/* Appends n tokens to seq_id, writing their slots to host slots[n].  If the
+ * last block was shared and partly filled it is replaced by a fresh block:
+ * (src, dst) is written to host copies[0..1] and *n_copies = 1 (else 0); the
+ * caller copies that block on the device before writing the new rows. */
+pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int32_t n,
+                         int64_t* slots, int32_t* copies, int32_t max_copies, int32_t* n_copies);
+
+/* child starts as a copy of parent sharing all its blocks (parallel samples,
+ * beam search). */
+pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child);
+
+/* Ends seq_id: every block loses one reference; blocks left unreferenced are
+ * free again at once (cached ones become reusable). */
+pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+
+/* Host int32 tables[n_seqs][max_blocks] (-1 padded) and context_lens[n_seqs]
+ * of the given sequences, ready for paged_attention_decode. */
+pkv_status pkv_bm_block_tables(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
+                               int32_t max_blocks, int32_t* tables, int32_t* context_lens);
+
 #ifdef __cplusplus
 }
 #endif

@@ -15,8 +15,8 @@ import os
 import torch
 
 __all__ = [
-    "kv_quantize", "kv_cache_append", "paged_attention_decode",
-    "paged_attention_workspace_size", "kv_cache_bytes",
+    "kv_quantize", "kv_cache_append", "paged_attention_decode", "kv_copy_blocks",
+    "BlockManager", "paged_attention_workspace_size", "kv_cache_bytes",
     "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8",
     "PKV_FP8_E4M3FN", "EXPORTED_SYMBOLS",
 ]
@@ -25,7 +25,10 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (
     "pkv_last_error", "kv_cache_bytes", "kv_quantize", "kv_cache_append",
-    "paged_attention_workspace_size", "paged_attention_decode",
+    "paged_attention_workspace_size", "paged_attention_decode", "kv_copy_blocks",
+    "pkv_bm_last_error", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
+    "pkv_bm_ref_count", "pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
+    "pkv_bm_block_tables",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -62,6 +65,28 @@ def load_library():
     lib.paged_attention_decode.restype = I32
     lib.paged_attention_decode.argtypes = [P, P, I32, I32, I32, P, P, P, P, I32, I32, I32, I32,
                                            I32, P, I32, P, I32, F, P, SZ, P]
+    lib.kv_copy_blocks.restype = I32
+    lib.kv_copy_blocks.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, P]
+    lib.pkv_bm_last_error.restype = ctypes.c_char_p
+    lib.pkv_bm_last_error.argtypes = []
+    lib.pkv_bm_create.restype = P
+    lib.pkv_bm_create.argtypes = [I32, I32, I32]
+    lib.pkv_bm_destroy.restype = None
+    lib.pkv_bm_destroy.argtypes = [P]
+    lib.pkv_bm_num_free.restype = I32
+    lib.pkv_bm_num_free.argtypes = [P]
+    lib.pkv_bm_ref_count.restype = I32
+    lib.pkv_bm_ref_count.argtypes = [P, I32]
+    lib.pkv_bm_add_sequence.restype = I32
+    lib.pkv_bm_add_sequence.argtypes = [P, I64, P, I32, P]
+    lib.pkv_bm_append.restype = I32
+    lib.pkv_bm_append.argtypes = [P, I64, P, I32, P, P, I32, P]
+    lib.pkv_bm_fork.restype = I32
+    lib.pkv_bm_fork.argtypes = [P, I64, I64]
+    lib.pkv_bm_free.restype = I32
+    lib.pkv_bm_free.argtypes = [P, I64]
+    lib.pkv_bm_block_tables.restype = I32
+    lib.pkv_bm_block_tables.argtypes = [P, P, I32, I32, P, P]
     _LIB = lib
     return lib
 
@@ -192,3 +217,98 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         float(scale), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, lib)
     return out
+
+
+def kv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, kv_dtype=None,
+                   stream=None):
+    """Copy whole blocks: for each row (src, dst) of the device int32 ``pairs``
+    ``[n][2]``, block dst of both caches (and INT8 scales) becomes block src."""
+    lib = load_library()
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache"), (pairs, "pairs"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise TypeError("pairs must be int32 [n][2]")
+    NB, Hkv, bs, d = k_cache.shape
+    st = lib.kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), NB, bs,
+                            Hkv, d, _kv_code(k_cache, kv_dtype, "k_cache"), _ptr(pairs),
+                            pairs.numel() // 2, _stream(stream))
+    _check(st, lib)
+
+
+class BlockManager:
+    """Host-side block allocation with reference-counted sharing, copy-on-write
+    and optional prefix caching (the C block manager of libpagedkv)."""
+
+    def __init__(self, num_blocks, block_size, prefix_caching=False):
+        import numpy as np
+        self._np = np
+        self._lib = load_library()
+        self._h = self._lib.pkv_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)))
+        if not self._h:
+            raise RuntimeError(self._lib.pkv_bm_last_error().decode())
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+
+    def close(self):
+        if self._h:
+            self._lib.pkv_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _ok(self, status):
+        if status != 0:
+            raise RuntimeError(f"block manager status {status}: "
+                               f"{self._lib.pkv_bm_last_error().decode()}")
+
+    def _tokens(self, tokens):
+        t = self._np.ascontiguousarray(tokens, dtype=self._np.int32).reshape(-1)
+        return t, t.ctypes.data_as(ctypes.c_void_p)
+
+    @property
+    def num_free(self):
+        return int(self._lib.pkv_bm_num_free(self._h))
+
+    def ref_count(self, block):
+        return int(self._lib.pkv_bm_ref_count(self._h, int(block)))
+
+    def add_sequence(self, seq_id, tokens):
+        """Slots (int64 numpy, -1 for tokens in shared cached blocks)."""
+        t, tp = self._tokens(tokens)
+        slots = self._np.empty(len(t), dtype=self._np.int64)
+        self._ok(self._lib.pkv_bm_add_sequence(self._h, int(seq_id), tp, len(t),
+                                               slots.ctypes.data_as(ctypes.c_void_p)))
+        return slots
+
+    def append(self, seq_id, tokens):
+        """(slots, copies): copies is a list of (src, dst) blocks to copy first."""
+        t, tp = self._tokens(tokens)
+        slots = self._np.empty(len(t), dtype=self._np.int64)
+        copies = self._np.empty(2, dtype=self._np.int32)
+        n = ctypes.c_int32(0)
+        self._ok(self._lib.pkv_bm_append(self._h, int(seq_id), tp, len(t),
+                                         slots.ctypes.data_as(ctypes.c_void_p),
+                                         copies.ctypes.data_as(ctypes.c_void_p), 1,
+                                         ctypes.byref(n)))
+        return slots, [tuple(int(x) for x in copies)] if n.value else []
+
+    def fork(self, parent, child):
+        self._ok(self._lib.pkv_bm_fork(self._h, int(parent), int(child)))
+
+    def free(self, seq_id):
+        self._ok(self._lib.pkv_bm_free(self._h, int(seq_id)))
+
+    def block_tables(self, seq_ids, max_blocks):
+        """(tables int32 [n][max_blocks], context_lens int32 [n]) as numpy."""
+        ids = self._np.ascontiguousarray(seq_ids, dtype=self._np.int64)
+        tables = self._np.empty((len(ids), max_blocks), dtype=self._np.int32)
+        ctx = self._np.empty(len(ids), dtype=self._np.int32)
+        self._ok(self._lib.pkv_bm_block_tables(self._h, ids.ctypes.data_as(ctypes.c_void_p),
+                                               len(ids), int(max_blocks),
+                                               tables.ctypes.data_as(ctypes.c_void_p),
+                                               ctx.ctypes.data_as(ctypes.c_void_p)))
+        return tables, ctx

@@ -141,6 +141,32 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
                     "kv_cache_append");
 }
 
+pkv_status kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                          int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t kv_dtype, const int32_t* pairs,
+                          int32_t n_pairs, void* stream) {
+  if (kv_dtype < PKV_F32 || kv_dtype > PKV_FP8_E4M3FN)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_copy_blocks: unknown kv_dtype");
+  if (num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 || n_pairs < 0)
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: bad sizes");
+  if (n_pairs == 0) return ok();
+  if (n_pairs > 0x3FFFFFFF) return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: too many pairs");
+  if (!k_cache || !v_cache || !pairs) return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: NULL pointer");
+  if (kv_dtype == PKV_I8 && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: an INT8 cache needs k_scale and v_scale");
+  const int64_t block_rows = (int64_t)num_kv_heads * block_size;
+  const int64_t block_bytes = block_rows * head_dim * pkv::dtype_bytes(kv_dtype);
+  if (block_bytes % 16 || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 4))
+    return fail(PKV_ERR_INVALID_ARG,
+                "kv_copy_blocks: caches need 16-byte alignment and 16-byte-multiple blocks");
+  return hip_status(pkv::launch_copy_blocks(k_cache, v_cache,
+                                            kv_dtype == PKV_I8 ? k_scale : nullptr,
+                                            kv_dtype == PKV_I8 ? v_scale : nullptr, pairs,
+                                            n_pairs, block_bytes, block_rows, num_blocks,
+                                            static_cast<hipStream_t>(stream)),
+                    "kv_copy_blocks");
+}
+
 pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int32_t batch,
                                   int32_t num_q_heads, const void* k_cache, const void* v_cache,
                                   const float* k_scale, const float* v_scale, int32_t num_blocks,

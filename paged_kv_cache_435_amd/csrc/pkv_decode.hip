@@ -35,6 +35,8 @@
 //    in unused slots never reach the sums.
 #include <stdlib.h>
 
+#include <atomic>
+
 #include "pkv_common.h"
 #include "pkv_internal.h"
 
@@ -813,10 +815,17 @@ static int slots_per_cu_override() {
 template <int KV, int QT, int D, int BS>
 static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
   auto* kern = decode_partition_kernel<KV, QT, D, BS>;
-  int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-      &per_cu, reinterpret_cast<const void*>(kern), 64, 0);
-  if (e != hipSuccess) return e;
+  // Resident waves per CU of this instance: a property of the compiled code,
+  // queried once (every device the library runs on is gfx950).
+  static std::atomic<int> occupancy{0};
+  int per_cu = occupancy.load(std::memory_order_relaxed);
+  hipError_t e = hipSuccess;
+  if (per_cu == 0) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                      64, 0);
+    if (e != hipSuccess) return e;
+    occupancy.store(per_cu, std::memory_order_relaxed);
+  }
   per_cu = per_cu < 1 ? 1 : (per_cu > kWavesPerCuCap ? kWavesPerCuCap : per_cu);
   const int target = slots_per_cu_override() > 0 ? slots_per_cu_override()
                                                  : Tuning<KV>::slots_per_cu;

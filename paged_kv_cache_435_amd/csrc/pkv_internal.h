@@ -64,6 +64,10 @@ int decode_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int block_size)
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
                            void* out, float* scale, int scale_given, hipStream_t st);
 
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                              const int32_t* pairs, int32_t n_pairs, int64_t block_bytes,
+                              int64_t block_rows, int32_t num_blocks, hipStream_t st);
+
 hipError_t launch_append(const void* k, const void* v, int src_dtype, int num_tokens,
                          const int64_t* slots, void* k_cache, void* v_cache, float* k_scale,
                          float* v_scale, int num_blocks, int block_size, int num_kv_heads,
