@@ -7,8 +7,8 @@ carries a pool slot ``slot[i] = physical * bs + offset``; a negative slot means
 converted to the cache's storage:
 
 * same float format: copied;
-* INT8: quantized per row ([P1] §4), its scale written at the same position of
-  the scale array;
+* INT8 / INT4: quantized per row ([P1] §4; INT4 with 7 for 127, packed two
+  per byte), its scale written at the same position of the scale array;
 * FP8: encoded with the tensor's existing scale (saturating at +-448).
 
 Everything else in the pool is left as it was, byte for byte.
@@ -29,7 +29,7 @@ def append_expected(k_cache, v_cache, k_new, v_new, slot_mapping, block_size,
     arrays are ``[NB][Hkv][bs]``; for ``fp8`` they are scalars (read, returned
     unchanged).
     """
-    if kv_format in ("i8", "fp8"):
+    if kv_format in ("i8", "fp8", "i4"):
         fmt = src_format or {np.dtype(np.float16): "f16", np.dtype(np.uint16): "bf16",
                              np.dtype(np.float32): "f32"}[np.asarray(k_new).dtype]
         k_new = widen.widen_plain(k_new, fmt).astype(np.float32)
@@ -50,6 +50,10 @@ def append_expected(k_cache, v_cache, k_new, v_new, slot_mapping, block_size,
                 if kv_format == "i8":
                     q, s = quant.quantize_int8_rows(row[None, :])
                     cache[blk, g, off] = q[0]
+                    scales[blk, g, off] = s[0]
+                elif kv_format == "i4":
+                    q, s = quant.quantize_int4_rows(row[None, :])
+                    cache[blk, g, off] = quant.pack_int4(q)[0]
                     scales[blk, g, off] = s[0]
                 elif kv_format == "fp8":
                     codes, _ = quant.quantize_fp8(row, scale=given)

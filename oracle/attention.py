@@ -80,8 +80,10 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     q            [B][Hq][d], any real dtype (widened exactly to fp64 by the caller
                  or here; pass bf16 already widened).
     k_cache      [NB][Hkv][bs][d] stored K: float32 / float16 / uint16 (bf16 bits)
-                 / int8 / uint8 (fp8 codes), per ``kv_format``; v_cache alike.
-    k_scale      i8: float32 [NB][Hkv][bs] (127/absmax per row); fp8: one float.
+                 / int8 / uint8 (fp8 codes), per ``kv_format``; for ``i4``
+                 [NB][Hkv][bs][d/2] packed bytes; v_cache alike.
+    k_scale      i8 / i4: float32 [NB][Hkv][bs] (127 or 7 over absmax per row);
+                 fp8: one float.
     block_tables int [B][MB];  context_lens int [B].
     pairs        optional iterable of (b, h) to compute (the rest stay NaN), for
                  sampled checks of large cases.
@@ -89,7 +91,7 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
     q = np.asarray(q, dtype=np.float64)
     B, Hq, d = q.shape
     NB, Hkv, bs, dk = k_cache.shape
-    if bs != block_size or dk != d:
+    if bs != block_size or dk * (2 if kv_format == "i4" else 1) != d:
         raise ValueError("cache shape does not match block_size / head_dim")
     if Hq % Hkv != 0:
         raise ValueError("query heads must be a multiple of KV heads")
@@ -120,11 +122,11 @@ def decode_attention(q, k_cache, v_cache, block_tables, context_lens, scale,
             Kraw = paging.gather(k_cache, bt[b], ctx, block_size, g)
             Vraw = paging.gather(v_cache, bt[b], ctx, block_size, g)
             # Step 3: dequantize.
-            if kv_format == "i8":
+            if kv_format in ("i8", "i4"):
                 ks = paging.gather_scales(np.asarray(k_scale), bt[b], ctx, block_size, g)
                 vs = paging.gather_scales(np.asarray(v_scale), bt[b], ctx, block_size, g)
-                K = widen.widen_kv(Kraw, "i8", ks)
-                V = widen.widen_kv(Vraw, "i8", vs)
+                K = widen.widen_kv(Kraw, kv_format, ks)
+                V = widen.widen_kv(Vraw, kv_format, vs)
             elif kv_format == "fp8":
                 K = widen.widen_kv(Kraw, "fp8", k_scale)
                 V = widen.widen_kv(Vraw, "fp8", v_scale)

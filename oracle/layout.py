@@ -68,3 +68,56 @@ def v_to_stored(logical):
     x = g.reshape(NB, Hkv, bs // 16, 4, 4, d // (16 * G), G, 16)     # [c][i][nq][nm][r]
     x = x.transpose(0, 1, 2, 5, 3, 7, 6, 4)                           # [nq][c][r][nm][i]
     return np.ascontiguousarray(x).reshape(NB, Hkv, bs, d)
+
+
+# ---------------------------------------------------------------------------
+# INT4 pools hold packed bytes ``[NB][Hkv][bs][d/2]`` (logical order: element
+# 2k of a row in the low nibble of byte k, 2k+1 in the high nibble).
+#
+# * K: the packed row is cut into 16-byte chunks exactly as above (the
+#   functions above apply to the packed uint8 array unchanged).
+# * V: nibbles move, not just bytes.  With ``n = d // 16``, ``r = d % 16``,
+#   ``c = t // 4``, ``i = t % 4``, element ``(t, d)`` sits in byte
+#   ``((n // 8) * 64 + c * 16 + r) * 16 + ((n % 8) // 2) * 4 + i`` of the group,
+#   low nibble for even ``n``, high for odd: each stored byte holds token
+#   ``t``'s elements ``d`` and ``d + 16``.  ``d`` must be a multiple of 128.
+# ---------------------------------------------------------------------------
+def _nibbles(packed):
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.uint8)
+    out[..., 0::2], out[..., 1::2] = b & 0xF, b >> 4
+    return out
+
+
+def _pack(nibbles):
+    n = np.asarray(nibbles, dtype=np.uint8)
+    return (n[..., 0::2] | (n[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _v4_shape(packed):
+    a = np.asarray(packed)
+    if a.dtype != np.uint8:
+        raise TypeError("int4 pools are packed uint8")
+    NB, Hkv, bs, half = a.shape
+    d = 2 * half
+    if bs % 16 or d % 128:
+        raise ValueError("int4 V needs block_size % 16 == 0 and head_dim % 128 == 0")
+    return NB, Hkv, bs, d
+
+
+def v4_from_stored(stored):
+    """Stored INT4 V pool -> logical packed ``[NB][Hkv][bs][d/2]``."""
+    NB, Hkv, bs, d = _v4_shape(stored)
+    # nibble index in a group = (((nq*4 + c)*16 + r)*16 + nw*4 + i)*2 + np,
+    # with n = 8*nq + 2*nw + np
+    x = _nibbles(stored).reshape(NB, Hkv, bs // 16, d // 128, 4, 16, 4, 4, 2)  # nq c r nw i np
+    x = x.transpose(0, 1, 2, 4, 7, 3, 6, 8, 5)                                # c i nq nw np r
+    return _pack(np.ascontiguousarray(x).reshape(NB, Hkv, bs, d))
+
+
+def v4_to_stored(logical):
+    """Logical packed INT4 V pool -> stored order (inverse of ``v4_from_stored``)."""
+    NB, Hkv, bs, d = _v4_shape(logical)
+    x = _nibbles(logical).reshape(NB, Hkv, bs // 16, 4, 4, d // 128, 4, 2, 16)  # c i nq nw np r
+    x = x.transpose(0, 1, 2, 5, 3, 8, 6, 4, 7)                                 # nq c r nw i np
+    return _pack(np.ascontiguousarray(x).reshape(NB, Hkv, bs, d))

@@ -1,5 +1,7 @@
 """KV quantizers (TEST INFRASTRUCTURE ONLY; see the package header).
 
+(INT4, per row, and its nibble packing: see ``quantize_int4_rows``.)
+
 INT8, per row — [P1] §4 (INT8 quantization, quantize_tensor): the scale is 127
 divided by the row's largest magnitude (``dim=-1``, one scale per row), the row
 is multiplied by it, rounded and clamped to [-128, 127].  Readings taken:
@@ -47,6 +49,43 @@ def quantize_int8_rows(x):
     q = np.clip(np.rint(y), -128, 127)
     q = np.where(zero[..., None], 0, q)
     return q.astype(np.int8), scale
+
+
+def quantize_int4_rows(x):
+    """Per-row INT4 quantization: [P1] §4's rule with the 4-bit range — the
+    pages report an INT4 cache ([P1] §4, quantization-effect table) but give
+    its quantizer only for INT8; the reading taken keeps every step and puts
+    7 = 2**3 - 1 where the INT8 code has 127: ``s = fl32(fl32(1/a) * 7)``,
+    ``q = clamp(rint(fl32(x * s)), -8, 7)``, a zero row gives codes 0 and scale
+    1.0.  Returns ``(codes int8 in [-8, 7], scale float32)``."""
+    x32 = np.asarray(x).astype(np.float32)
+    absmax = np.max(np.abs(x32), axis=-1)
+    zero = absmax == 0
+    safe = np.where(zero, np.float32(1.0), absmax).astype(np.float32)
+    recip = (np.float32(1.0) / safe).astype(np.float32)
+    scale = (recip * np.float32(7.0)).astype(np.float32)
+    scale = np.where(zero, np.float32(1.0), scale).astype(np.float32)
+    y = (x32 * scale[..., None]).astype(np.float32)
+    q = np.clip(np.rint(y), -8, 7)
+    q = np.where(zero[..., None], 0, q)
+    return q.astype(np.int8), scale
+
+
+def pack_int4(codes):
+    """INT4 codes ``[..., d]`` (int8 in [-8, 7]) -> bytes ``[..., d/2]``: element
+    2k in the low nibble of byte k, element 2k+1 in the high nibble, two's
+    complement."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_int4(packed):
+    """Inverse of ``pack_int4``: bytes ``[..., d/2]`` -> int8 codes ``[..., d]``."""
+    b = np.asarray(packed).astype(np.int64)
+    lo, hi = b & 0xF, b >> 4
+    out = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.int64)
+    out[..., 0::2], out[..., 1::2] = lo, hi
+    return np.where(out >= 8, out - 16, out).astype(np.int8)
 
 
 def fp8_tensor_scale(x):

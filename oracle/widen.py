@@ -18,7 +18,7 @@ Each decoder is written from the format's definition, not from a library cast:
 
 import numpy as np
 
-FORMATS = ("f32", "f16", "bf16", "i8", "fp8")
+FORMATS = ("f32", "f16", "bf16", "i8", "fp8", "i4")
 
 
 def bf16_bits_to_f64(bits):
@@ -79,4 +79,16 @@ def widen_kv(x, fmt, scale=None):
         return x.astype(np.float64) / s[..., None]
     if fmt == "fp8":
         return e4m3fn_to_f64(x) * float(np.float32(scale))
+    if fmt == "i4":
+        # Two's-complement nibbles, two per byte (element 2k low, 2k+1 high),
+        # value code / scale like INT8.
+        b = np.asarray(x)
+        if b.dtype != np.uint8:
+            raise TypeError("int4 cache rows are packed uint8")
+        lo, hi = b.astype(np.int64) & 0xF, b.astype(np.int64) >> 4
+        codes = np.empty(b.shape[:-1] + (2 * b.shape[-1],), dtype=np.float64)
+        codes[..., 0::2] = np.where(lo >= 8, lo - 16, lo)
+        codes[..., 1::2] = np.where(hi >= 8, hi - 16, hi)
+        s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+        return codes / s[..., None]
     raise ValueError(f"unknown KV format {fmt}")

@@ -71,3 +71,22 @@ def test_fp8_append_uses_the_given_tensor_scale():
     want, _ = quant.quantize_fp8(kn[0, 0], scale=s)
     assert np.array_equal(k2[1, 0, 1], want)
     assert np.any((want & 0x7F) == 0x7E)
+
+
+def test_int4_append_quantizes_packs_and_writes_the_scale():
+    rng = np.random.default_rng(3)
+    NB, Hkv, bs, d = 3, 2, 16, 32
+    kc = rng.integers(0, 256, (NB, Hkv, bs, d // 2)).astype(np.uint8)
+    vc = rng.integers(0, 256, (NB, Hkv, bs, d // 2)).astype(np.uint8)
+    ks = rng.standard_normal((NB, Hkv, bs)).astype(np.float32)
+    vs = rng.standard_normal((NB, Hkv, bs)).astype(np.float32)
+    kn = rng.standard_normal((1, Hkv, d)).astype(np.float16)
+    vn = rng.standard_normal((1, Hkv, d)).astype(np.float16)
+    k2, v2, ks2, vs2 = append.append_expected(kc, vc, kn, vn, [bs + 9], bs, "i4", ks, vs)
+    q, s = quant.quantize_int4_rows(kn[0].astype(np.float32))
+    assert np.array_equal(k2[1, :, 9], quant.pack_int4(q)) and np.array_equal(ks2[1, :, 9], s)
+    q, s = quant.quantize_int4_rows(vn[0].astype(np.float32))
+    assert np.array_equal(v2[1, :, 9], quant.pack_int4(q)) and np.array_equal(vs2[1, :, 9], s)
+    mask = np.ones((NB, bs), dtype=bool)
+    mask[1, 9] = False
+    assert np.array_equal(k2.transpose(0, 2, 1, 3)[mask], kc.transpose(0, 2, 1, 3)[mask])

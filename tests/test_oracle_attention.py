@@ -295,3 +295,29 @@ def test_bf16_widening_is_exact():
     x = torch.randn(1000, dtype=torch.float32).to(torch.bfloat16)
     bits = x.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(widen.widen_kv(bits, "bf16"), x.to(torch.float64).numpy())
+
+
+def test_int4_cache_stays_within_quantization_error():
+    """INT4 (7 / absmax per row, packed nibbles) vs the float rows it came from:
+    lossy, and further from the float result than INT8 over the same rows."""
+    rng = np.random.default_rng(21)
+    ctx = [64, 100]
+    q, K, V, _, _, _ = random_case(rng, 2, 4, 2, 32, 16, ctx)
+    bs = 16
+    need = sum(-(-c // bs) for c in ctx)
+    kpool, tables = scatter_to_pool(K, ctx, bs, need + 2, np.random.default_rng(1), fill=0.0)
+    vpool, _ = scatter_to_pool(V, ctx, bs, need + 2, np.random.default_rng(1), fill=0.0)
+    k4, ks = quant.quantize_int4_rows(kpool.astype(np.float32))
+    v4, vs = quant.quantize_int4_rows(vpool.astype(np.float32))
+    k8, ks8 = quant.quantize_int8_rows(kpool.astype(np.float32))
+    v8, vs8 = quant.quantize_int8_rows(vpool.astype(np.float32))
+    f = attention.decode_attention(q, kpool, vpool, tables, ctx, 0.2, bs, "f32")
+    i4 = attention.decode_attention(q, quant.pack_int4(k4), quant.pack_int4(v4), tables, ctx,
+                                    0.2, bs, "i4", ks, vs)
+    i8 = attention.decode_attention(q, k8, v8, tables, ctx, 0.2, bs, "i8", ks8, vs8)
+    e4, e8 = np.max(np.abs(f - i4)), np.max(np.abs(f - i8))
+    assert 0 < e8 < e4 < 0.5
+    # the same codes fed as unpacked INT8 codes with the INT4 scales give the
+    # same attention: packing is lossless
+    same = attention.decode_attention(q, k4, v4, tables, ctx, 0.2, bs, "i8", ks, vs)
+    assert np.array_equal(same, i4)

@@ -61,3 +61,38 @@ def test_v_lane_groups_hold_four_tokens_of_one_column():
     piece = stored[8 * (16 * 1 + 5): 8 * (16 * 1 + 5) + 8]     # lane 21 of load 0: c=1, r=5
     assert list(piece[:4]) == [logical[0, 0, 4 + i, 5] for i in range(4)]
     assert list(piece[4:]) == [logical[0, 0, 4 + i, 21] for i in range(4)]
+
+
+# INT4 V: element (t, d) -> (byte, nibble) by hand, d = 128, bs = 16:
+# n = d // 16, r = d % 16, c = t // 4, i = t % 4:
+#   byte = (c*16 + r)*16 + ((n % 8)//2)*4 + i, high nibble for odd n.
+HAND4 = [
+    (0, 0, 0, 0),           # token 0, column 0: first byte, low nibble
+    (0, 16, 0, 1),          # column 16 (n = 1) shares the byte, high nibble
+    (6, 37, (1 * 16 + 5) * 16 + 1 * 4 + 2, 0),   # n=2 r=5 c=1 i=2
+    (13, 125, (3 * 16 + 13) * 16 + 3 * 4 + 1, 1),  # n=7 r=13 c=3 i=1
+]
+
+
+@pytest.mark.parametrize("t,dim,byte,hi", HAND4)
+def test_int4_v_hand_worked_positions(t, dim, byte, hi):
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, size=(1, 1, 16, 128)).astype(np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    stored = layout.v4_to_stored(packed).reshape(-1)
+    got = (stored[byte] >> 4) if hi else (stored[byte] & 0xF)
+    assert got == codes[0, 0, t, dim]
+
+
+@pytest.mark.parametrize("d,bs", [(128, 16), (128, 256), (256, 16)])
+def test_int4_v_round_trip_and_bytes_hold_one_token(d, bs):
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 256, size=(2, 3, bs, d // 2)).astype(np.uint8)
+    y = layout.v4_to_stored(x)
+    assert np.array_equal(layout.v4_from_stored(y), x)
+    # every stored byte holds two elements of a single token: stamp each token's
+    # nibbles with its own index and read back one value per byte
+    tok = np.broadcast_to((np.arange(bs) % 16).astype(np.uint8)[:, None], (bs, d // 2))
+    stamped = np.broadcast_to(tok | (tok << 4), x.shape).copy()
+    s = layout.v4_to_stored(stamped)
+    assert np.all((s & 0xF) == (s >> 4))

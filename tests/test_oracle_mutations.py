@@ -99,3 +99,34 @@ def test_fp8_wrong_bias_is_caught(monkeypatch):
     table = np.array([widen.e4m3fn_value(c) * 2.0 for c in range(256)])
     monkeypatch.setattr(widen, "E4M3FN_TABLE", table)
     _fails(TQ.test_e4m3fn_decoder_matches_torch_on_all_codes)
+
+
+def test_int4_wrong_range_is_caught(monkeypatch):
+    def bad(x):   # 15 levels per side instead of 7
+        x32 = np.asarray(x).astype(np.float32)
+        a = np.max(np.abs(x32), axis=-1)
+        s = ((np.float32(1) / a).astype(np.float32) * np.float32(15)).astype(np.float32)
+        return np.clip(np.rint(x32 * s[..., None]), -16, 15).astype(np.int8), s
+    monkeypatch.setattr(quant, "quantize_int4_rows", bad)
+    _fails(TQ.test_int4_hand_worked_row)
+
+
+def test_int4_swapped_nibbles_are_caught(monkeypatch):
+    def bad(codes):
+        c = np.asarray(codes).astype(np.int64) & 0xF
+        return (c[..., 1::2] | (c[..., 0::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(quant, "pack_int4", bad)
+    _fails(TQ.test_int4_packing_by_hand_and_round_trip)
+
+
+def test_int4_unsigned_widening_is_caught(monkeypatch):
+    orig = widen.widen_kv
+
+    def bad(x, fmt, scale=None):
+        if fmt == "i4":
+            b = np.asarray(x).astype(np.int64)
+            codes = np.stack([b & 0xF, b >> 4], axis=-1).reshape(b.shape[:-1] + (-1,))
+            return codes / np.asarray(scale, dtype=np.float64)[..., None]
+        return orig(x, fmt, scale)
+    monkeypatch.setattr(widen, "widen_kv", bad)
+    _fails(TQ.test_int4_widening_divides_by_the_row_scale)

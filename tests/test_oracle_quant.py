@@ -144,3 +144,75 @@ def test_fp8_tensor_quantizer():
     assert list(c2) == [0x7E, 0xFE, 0x7E, 0x7E]
     zc, zs = quant.quantize_fp8(np.zeros(8, dtype=np.float32))
     assert zs == np.float32(1.0) and np.all(zc == 0)
+
+
+# ---------------------------------------------------------------------------
+# INT4: [P1] §4 lists an INT4 cache only by its size and speed; the quantizer
+# read here is the page's INT8 rule with 7 for 127 and [-8, 7] for the clamp.
+# Pins: a hand-worked row, the nearest-code definition checked by brute force
+# over all 16 codes, the sign/absmax properties, the nibble order by hand.
+# ---------------------------------------------------------------------------
+def test_int4_hand_worked_row():
+    # a = 1, s = fl32(1/1) * 7 = 7: codes rint(3.5) = 4 (half to even),
+    # rint(-7) = -7, rint(1.75) = 2, 0; rint(-0.35) = -0.
+    q, s = quant.quantize_int4_rows(np.array([[0.5, -1.0, 0.25, 0.0, -0.05]], np.float32))
+    assert s[0] == np.float32(7.0)
+    assert q[0].tolist() == [4, -7, 2, 0, 0]
+    # a = 0.75: s = fl32(fl32(1/0.75) * 7); 0.1 * s = 0.9333.. -> 1, -0.375 * s = -3.5 -> -4
+    q, s = quant.quantize_int4_rows(np.array([[0.1, -0.375, 0.75]], np.float32))
+    assert s[0] == np.float32(np.float32(np.float32(1) / np.float32(0.75)) * np.float32(7))
+    assert q[0].tolist() == [1, -4, 7]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_int4_codes_are_the_nearest_of_all_sixteen(seed):
+    """Brute force: for every element, the code is the one of -8..7 closest to
+    fl32(x * s), ties to the even code."""
+    x = _rows(seed, n=600, d=64)
+    q, s = quant.quantize_int4_rows(x)
+    y = (x * s[:, None]).astype(np.float32).astype(np.float64)
+    codes = np.arange(-8, 8, dtype=np.float64)
+    dist = np.abs(y[..., None] - codes)
+    best = dist.min(axis=-1, keepdims=True)
+    ties = dist == best
+    # among tied codes pick the even one
+    pick = np.where(ties.sum(-1) > 1, np.argmax(ties & (codes % 2 == 0), axis=-1), np.argmin(dist, -1))
+    assert np.array_equal(q.astype(np.int64), (pick - 8).astype(np.int64))
+
+
+def test_int4_absmax_maps_to_seven_and_zero_rows():
+    x = _rows(5, n=500, d=128)
+    x[7] = 0.0
+    q, s = quant.quantize_int4_rows(x)
+    idx = np.argmax(np.abs(x), axis=-1)
+    picked = q[np.arange(len(q)), idx].astype(np.int64)
+    live = np.arange(len(q)) != 7
+    assert np.all(np.abs(picked[live]) == 7)
+    assert np.array_equal(np.sign(picked[live]), np.sign(x[np.arange(len(q)), idx][live]))
+    assert q.min() >= -7 and q.max() <= 7 and np.all(q[7] == 0) and s[7] == 1.0
+    # error bound: |x - q/s| <= 0.5/s (+ one rounding of x*s)
+    err = np.abs(x.astype(np.float64) - q / s[:, None].astype(np.float64))
+    assert np.all(err[live] <= (0.5 + 1e-5) / s[live, None])
+
+
+def test_int4_odd_symmetry_and_power_of_two_scaling():
+    x = _rows(6, n=300, d=64)
+    q, s = quant.quantize_int4_rows(x)
+    qn, sn = quant.quantize_int4_rows(-x)
+    assert np.array_equal(qn, -q) and np.array_equal(sn, s)
+    q4, s4 = quant.quantize_int4_rows(x * 4)
+    assert np.array_equal(q4, q) and np.array_equal(s4, s / 4)
+
+
+def test_int4_packing_by_hand_and_round_trip():
+    assert quant.pack_int4(np.array([1, -2, 7, -8], np.int8)).tolist() == [0xE1, 0x87]
+    assert quant.unpack_int4(np.array([0xE1, 0x87], np.uint8)).tolist() == [1, -2, 7, -8]
+    rng = np.random.default_rng(7)
+    c = rng.integers(-8, 8, size=(5, 3, 64)).astype(np.int8)
+    assert np.array_equal(quant.unpack_int4(quant.pack_int4(c)), c)
+
+
+def test_int4_widening_divides_by_the_row_scale():
+    packed = quant.pack_int4(np.array([[3, -8, 0, 7]], np.int8))
+    got = widen.widen_kv(packed, "i4", np.array([2.0], np.float32))
+    assert got.tolist() == [[1.5, -4.0, 0.0, 3.5]]
