@@ -151,10 +151,12 @@ def cpu_baseline(w, cases, budget_s):
                 nblk = -(-ctx // w.block_size)
                 phys = torch.from_numpy(w.block_tables[b, :nblk].astype(np.int64)).to(
                     case.k_cache.device)
+                v_order = (oracle.layout.v4_from_stored if w.kv_format == "i4"
+                           else oracle.layout.v_from_stored)
                 kc = oracle.layout.k_from_stored(cache_to_host(case.k_cache[phys], w.kv_format))
-                vc = oracle.layout.v_from_stored(cache_to_host(case.v_cache[phys], w.kv_format))
+                vc = v_order(cache_to_host(case.v_cache[phys], w.kv_format))
                 ks = vs = None
-                if w.kv_format == "i8":
+                if w.kv_format in ("i8", "i4"):
                     ks, vs = case.k_scale[phys].cpu().numpy(), case.v_scale[phys].cpu().numpy()
                 elif w.kv_format == "fp8":
                     ks, vs = np.float32(case.k_scale.item()), np.float32(case.v_scale.item())
@@ -392,7 +394,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"f32": "f32", "f16": "f16", "bf16": "bf16", "i8": "i8+f16",
-                  "fp8": "fp8+f16"}[w.kv_format],
+                  "fp8": "fp8+f16", "i4": "i4+f16"}[w.kv_format],
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
                    "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,

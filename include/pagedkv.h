@@ -21,7 +21,15 @@
  *                           ((n / G) * 64 + (t / 4) * 16 + d % 16) * 16
  *                             + ((n % G) * 4 + t % 4) * eb,  n = d / 16, G = 4 / eb.
  *                      kv_cache_append writes this order; no caller needs to.
- *   INT8 scales        float32 [num_blocks][num_kv_heads][block_size], one per stored row.
+ *   INT4 caches        [num_blocks][num_kv_heads][block_size][head_dim / 2] bytes, head_dim
+ *                      128; a row packs element 2k in the low nibble of byte k and 2k+1
+ *                      in the high nibble (two's complement).  K groups: the packed row
+ *                      is chunked as above (eb = 1 on the packed bytes).  V groups move
+ *                      nibbles: element (t, d), n = d / 16, sits in byte
+ *                        ((t / 4) * 16 + d % 16) * 16 + ((n % 8) / 2) * 4 + t % 4
+ *                      of the group, low nibble for even n, high for odd (a byte holds
+ *                      one token's elements d and d + 16).
+ *   INT8 / INT4 scales float32 [num_blocks][num_kv_heads][block_size], one per stored row.
  *   FP8 scales         one float32 per tensor (per layer, one for K and one for V).
  *   block_tables       int32 [batch][max_blocks_per_seq]: logical block j of sequence b
  *                      lives in physical block block_tables[b][j] ([P1] §2 block table;
@@ -72,7 +80,8 @@ typedef enum {
   PKV_F16 = 1,
   PKV_BF16 = 2,
   PKV_I8 = 3,
-  PKV_FP8_E4M3FN = 4
+  PKV_FP8_E4M3FN = 4,
+  PKV_I4 = 5               /* signed 4-bit codes, two per byte, per-row scale */
 } pkv_dtype;
 
 /* Text of the last non-OK status returned on this thread ("" if none). */
@@ -91,7 +100,8 @@ uint64_t kv_cache_bytes(uint64_t batch, uint64_t seq_len, uint64_t layers,
  * kv_quantize — quantize rows of a float tensor for KV storage.
  *
  *   x         device, [n_rows][row_len] in x_dtype (PKV_F32 / PKV_F16 / PKV_BF16).
- *   out       device, [n_rows][row_len] bytes in out_dtype.
+ *   out       device, [n_rows][row_len] bytes in out_dtype ([n_rows][row_len / 2]
+ *             for PKV_I4).
  *   out_dtype PKV_I8: per-row quantizer of [P1] §4 (quantize_tensor):
  *               a = max|x_i| over the row; s = fl32(fl32(1/a) * 127) (the form
  *               PyTorch evaluates for the page's 127 / absmax);
@@ -102,7 +112,13 @@ uint64_t kv_cache_bytes(uint64_t batch, uint64_t seq_len, uint64_t layers,
  *               0, s = fl32(max|x| / 448) (1.0 if the tensor is all zero) is
  *               computed on the device and written to scale[0]; otherwise
  *               scale[0] is read.  Codes: RNE(clamp(fl32(x / s), -448, 448)).
- *   Errors: PKV_ERR_INVALID_ARG (null pointer, n_rows < 0, row_len < 1),
+ *             PKV_I4: the INT8 rule with 7 for 127 and [-8, 7] for the clamp
+ *               (the INT4 cache of [P1] §4's quantization table, whose
+ *               quantizer the page leaves open): s = fl32(fl32(1/a) * 7),
+ *               q_i = clamp(round_half_even(fl32(x_i * s)), -8, 7); codes packed
+ *               in row order, element 2k in the low nibble of byte k.  Scales as
+ *               for PKV_I8.  row_len must be even.
+ *   Errors: PKV_ERR_INVALID_ARG (null pointer, n_rows < 0, row_len < 1 or odd for I4),
  *           PKV_ERR_UNSUPPORTED (dtype pair), PKV_ERR_HIP.
  *   n_rows == 0 launches nothing (FP8 with scale_given == 0 still writes 1.0).
  */
@@ -123,10 +139,12 @@ pkv_status kv_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t r
  *                 PKV_I8: each (token, head) row quantized as kv_quantize does,
  *                   its scale written to k_scale/v_scale[block][head][offset];
  *                 PKV_FP8_E4M3FN: encoded with the tensor scale read from
- *                   k_scale[0] / v_scale[0] (saturating at +-448).
+ *                   k_scale[0] / v_scale[0] (saturating at +-448);
+ *                 PKV_I4: quantized as kv_quantize does, scale as for PKV_I8
+ *                   (head_dim 128 only).
  *   k_scale, v_scale  device float32 as above; NULL for plain float caches.
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_dim not 64/128,
- *           block_size not 16/256, dtype pair), PKV_ERR_HIP.
+ *           block_size not 16/256, dtype pair, INT4 with head_dim 64), PKV_ERR_HIP.
  */
 pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int32_t num_tokens,
                            const int64_t* slot_mapping, void* k_cache, void* v_cache,
@@ -137,7 +155,7 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
 /*
  * paged_attention_workspace_size — bytes of device scratch paged_attention_decode
  * needs for these sizes (partial softmax state of contexts split over several
- * waves; sized for up to 256 compute units x 12 resident waves).  Host only, no
+ * waves; sized for up to 256 compute units x 16 resident waves).  Host only, no
  * device needed.  0 when no context can be split (max_context_len <= 256) or
  * the sizes are invalid.
  */
@@ -157,10 +175,11 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *   out, q        device, [batch][num_q_heads][head_dim] in q_dtype
  *                 (PKV_F32 / PKV_F16 / PKV_BF16), contiguous, 16-byte aligned;
  *                 out may not alias q.
- *   k_cache, v_cache  device, cache layout above, kv_dtype = q_dtype, PKV_I8 or
- *                 PKV_FP8_E4M3FN.  Dequantized values: INT8 code / scale
- *                 (the inverse of [P1] §4's quantizer); FP8 decode(code) * scale.
- *   k_scale, v_scale  device: INT8 [num_blocks][num_kv_heads][block_size];
+ *   k_cache, v_cache  device, cache layout above, kv_dtype = q_dtype, PKV_I8,
+ *                 PKV_FP8_E4M3FN or PKV_I4.  Dequantized values: INT8 / INT4
+ *                 code / scale (the inverse of [P1] §4's quantizer); FP8
+ *                 decode(code) * scale.
+ *   k_scale, v_scale  device: INT8 / INT4 [num_blocks][num_kv_heads][block_size];
  *                 FP8 one float each; NULL otherwise.
  *   block_tables  device int32 [batch][max_blocks_per_seq].
  *   context_lens  device int32 [batch]; a sequence of length 0 gets zeros.
@@ -171,7 +190,7 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *                 size is 0); contents are overwritten.  Calls that share a
  *                 workspace must be ordered.
  *   Supported: head_dim 64 or 128; block_size 16 or 256; num_q_heads a multiple
- *   of num_kv_heads.
+ *   of num_kv_heads.  INT4 caches: head_dim 128 and q_dtype F16 or BF16.
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  */
 pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int32_t batch,
@@ -186,11 +205,12 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
 /*
  * kv_copy_blocks — copy whole physical blocks inside the pools (copy-on-write
  * of a shared block before an append, or compaction): for each pair i,
- * block pairs[2i + 1] of both caches (and, for INT8, of both scale arrays)
+ * block pairs[2i + 1] of both caches (and, for INT8 / INT4, of both scale arrays)
  * becomes a byte-for-byte copy of block pairs[2i].
  *
  *   k_cache, v_cache, k_scale, v_scale  device, as for kv_cache_append (scales
- *                 are read only for PKV_I8; FP8's one tensor scale needs no copy).
+ *                 are read only for PKV_I8 / PKV_I4; FP8's one tensor scale needs
+ *                 no copy); head_dim counts elements (INT4 rows are head_dim / 2 bytes).
  *   pairs         device int32 [n_pairs][2] (src, dst).  Pairs with an index
  *                 outside [0, num_blocks) or src == dst are skipped.  The copies
  *                 of one call run concurrently: no dst may be another pair's src.

@@ -25,16 +25,16 @@ library routines on the special cases, invariants).  No function here is
 
 Modules
   kvsize     closed-form KV-cache sizes                     [P1] §1, [P2] §2, [P3]
-  widen      stored bytes (f32/f16/bf16/int8/fp8) -> float64 [P1] §4, [P2] §4, [P3]
+  widen      stored bytes (f32/f16/bf16/int8/fp8/int4) -> float64  [P1] §4, [P2] §4, [P3]
   paging     slot arithmetic and block-table gather          [P1] §2, [P3]
   attention  paged decode attention = standard attention over the gathered cache
-  quant      INT8 per-row and FP8 per-tensor quantizers      [P1] §4, [P3]
+  quant      INT8 / INT4 per-row and FP8 per-tensor quantizers, nibble packing  [P1] §4, [P3]
   append     expected cache after writing new tokens' rows   [P3]
   layout     stored order of the pools <-> logical [NB][Hkv][bs][d] order
 """
 
 from . import kvsize, widen, paging, attention, quant, append, layout  # noqa: F401
 from .attention import decode_attention, attend, validate_tables  # noqa: F401
-from .quant import (quantize_int8_rows, fp8_tensor_scale, encode_e4m3fn,  # noqa: F401
-                    quantize_fp8)
+from .quant import (quantize_int8_rows, quantize_int4_rows, pack_int4, unpack_int4,  # noqa: F401
+                    fp8_tensor_scale, encode_e4m3fn, quantize_fp8)
 from .widen import widen_kv  # noqa: F401

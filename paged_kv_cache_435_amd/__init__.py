@@ -21,7 +21,7 @@ __all__ = [
     "PKV_FP8_E4M3FN", "EXPORTED_SYMBOLS",
 ]
 
-PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN = 0, 1, 2, 3, 4
+PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN, PKV_I4 = 0, 1, 2, 3, 4, 5
 
 EXPORTED_SYMBOLS = (
     "pkv_last_error", "kv_cache_bytes", "kv_quantize", "kv_cache_append",
@@ -105,9 +105,9 @@ def _dtype_code(t, what):
 def _kv_code(t, kv_dtype, what):
     if kv_dtype is not None:
         return {"f32": PKV_F32, "f16": PKV_F16, "bf16": PKV_BF16, "i8": PKV_I8,
-                "fp8": PKV_FP8_E4M3FN}[kv_dtype]
+                "fp8": PKV_FP8_E4M3FN, "i4": PKV_I4}[kv_dtype]
     if t.dtype == torch.uint8:
-        raise TypeError(f"{what}: uint8 storage needs kv_dtype='fp8' or 'i8'")
+        raise TypeError(f"{what}: uint8 storage needs kv_dtype='fp8', 'i8' or 'i4'")
     return _dtype_code(t, what)
 
 
@@ -146,16 +146,17 @@ def paged_attention_workspace_size(batch, num_q_heads, num_kv_heads, head_dim, m
 
 def kv_quantize(x, out, scale, scale_given=False, out_dtype=None, stream=None):
     """Quantize the rows of ``x`` (last axis) into ``out`` (int8, or uint8 /
-    float8_e4m3fn FP8 codes).  ``scale``: float32 ``x.shape[:-1]`` for INT8,
-    one element for FP8 (read if ``scale_given``, else written)."""
+    float8_e4m3fn FP8 codes, or uint8 packed INT4 codes with ``out_dtype="i4"``,
+    half as many bytes per row).  ``scale``: float32 ``x.shape[:-1]`` for INT8
+    and INT4, one element for FP8 (read if ``scale_given``, else written)."""
     lib = load_library()
     for t, n in ((x, "x"), (out, "out"), (scale, "scale")):
         _dev(t, n)
     if out_dtype is None:
         out_dtype = "i8" if out.dtype == torch.int8 else "fp8"
     oc = _kv_code(out, out_dtype, "out")
-    if out.numel() != x.numel():
-        raise ValueError("out must have as many elements as x")
+    if out.numel() * (2 if oc == PKV_I4 else 1) != x.numel():
+        raise ValueError("out must hold x's elements (INT4: two per byte)")
     if scale.dtype != torch.float32:
         raise TypeError("scale must be float32")
     row_len = x.shape[-1]
@@ -175,13 +176,15 @@ def kv_cache_append(k, v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=
         _dev(t, n)
     if slot_mapping.dtype != torch.int64:
         raise TypeError("slot_mapping must be int64")
-    NB, Hkv, bs, d = k_cache.shape
+    NB, Hkv, bs, dc = k_cache.shape
+    kc = _kv_code(k_cache, kv_dtype, "k_cache")
+    d = 2 * dc if kc == PKV_I4 else dc
     T = k.shape[0]
     if tuple(k.shape) != (T, Hkv, d) or tuple(v.shape) != (T, Hkv, d) or slot_mapping.numel() != T:
         raise ValueError("k, v must be [T][Hkv][d] and slot_mapping [T]")
     st = lib.kv_cache_append(_ptr(k), _ptr(v), _dtype_code(k, "k"), T, _ptr(slot_mapping),
                              _ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), NB, bs,
-                             Hkv, d, _kv_code(k_cache, kv_dtype, "k_cache"), _stream(stream))
+                             Hkv, d, kc, _stream(stream))
     _check(st, lib)
 
 
@@ -202,6 +205,9 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         raise TypeError("block_tables and context_lens must be int32")
     B, Hq, d = q.shape
     NB, Hkv, bs, dk = k_cache.shape
+    kc = _kv_code(k_cache, kv_dtype, "k_cache")
+    if kc == PKV_I4:
+        dk *= 2
     if tuple(out.shape) != (B, Hq, d) or out.dtype != q.dtype or dk != d:
         raise ValueError("out must match q, and the cache's head_dim must match q's")
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
@@ -212,7 +218,7 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.paged_attention_decode(
         _ptr(out), _ptr(q), _dtype_code(q, "q"), B, Hq, _ptr(k_cache), _ptr(v_cache),
-        _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, _kv_code(k_cache, kv_dtype, "k_cache"),
+        _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, kc,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
         float(scale), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, lib)
@@ -230,8 +236,11 @@ def kv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, kv_dtype
     if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
         raise TypeError("pairs must be int32 [n][2]")
     NB, Hkv, bs, d = k_cache.shape
+    kc = _kv_code(k_cache, kv_dtype, "k_cache")
+    if kc == PKV_I4:
+        d *= 2
     st = lib.kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), NB, bs,
-                            Hkv, d, _kv_code(k_cache, kv_dtype, "k_cache"), _ptr(pairs),
+                            Hkv, d, kc, _ptr(pairs),
                             pairs.numel() // 2, _stream(stream))
     _check(st, lib)
 

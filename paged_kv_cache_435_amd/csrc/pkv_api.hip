@@ -97,10 +97,12 @@ pkv_status kv_quantize(const void* x, int32_t x_dtype, int64_t n_rows, int32_t r
                        void* stream) {
   if (!is_float_dtype(x_dtype))
     return fail(PKV_ERR_UNSUPPORTED, "kv_quantize: x_dtype must be F32, F16 or BF16");
-  if (out_dtype != PKV_I8 && out_dtype != PKV_FP8_E4M3FN)
-    return fail(PKV_ERR_UNSUPPORTED, "kv_quantize: out_dtype must be I8 or FP8_E4M3FN");
+  if (out_dtype != PKV_I8 && out_dtype != PKV_FP8_E4M3FN && out_dtype != PKV_I4)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_quantize: out_dtype must be I8, FP8_E4M3FN or I4");
   if (n_rows < 0 || row_len < 1)
     return fail(PKV_ERR_INVALID_ARG, "kv_quantize: n_rows must be >= 0 and row_len >= 1");
+  if (out_dtype == PKV_I4 && row_len % 2)
+    return fail(PKV_ERR_INVALID_ARG, "kv_quantize: INT4 rows need an even row_len");
   if (!scale) return fail(PKV_ERR_INVALID_ARG, "kv_quantize: scale is NULL");
   if (n_rows > 0 && (!x || !out)) return fail(PKV_ERR_INVALID_ARG, "kv_quantize: x or out is NULL");
   if (!aligned(x, pkv::dtype_bytes(x_dtype)) || !aligned(scale, 4))
@@ -117,11 +119,14 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
                            void* stream) {
   if (!is_float_dtype(src_dtype))
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: src_dtype must be F32, F16 or BF16");
-  if (cache_dtype != src_dtype && cache_dtype != PKV_I8 && cache_dtype != PKV_FP8_E4M3FN)
+  if (cache_dtype != src_dtype && cache_dtype != PKV_I8 && cache_dtype != PKV_FP8_E4M3FN &&
+      cache_dtype != PKV_I4)
     return fail(PKV_ERR_UNSUPPORTED,
-                "kv_cache_append: cache_dtype must equal src_dtype, or be I8 or FP8_E4M3FN");
+                "kv_cache_append: cache_dtype must equal src_dtype, or be I8, FP8_E4M3FN or I4");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: head_dim must be 64 or 128");
+  if (cache_dtype == PKV_I4 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: INT4 caches need head_dim 128");
   if (block_size != 16 && block_size != 256)
     return fail(PKV_ERR_UNSUPPORTED, "kv_cache_append: block_size must be 16 or 256");
   if (num_tokens < 0 || num_blocks < 1 || num_kv_heads < 1 || num_kv_heads > 65535)
@@ -129,7 +134,7 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
   if (num_tokens == 0) return ok();
   if (!k || !v || !slot_mapping || !k_cache || !v_cache)
     return fail(PKV_ERR_INVALID_ARG, "kv_cache_append: NULL pointer");
-  if ((cache_dtype == PKV_I8 || cache_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
+  if ((pkv::row_scaled(cache_dtype) || cache_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID_ARG, "kv_cache_append: quantized cache needs k_scale and v_scale");
   const int eb = pkv::dtype_bytes(src_dtype);
   if (!aligned(k, eb) || !aligned(v, eb) || !aligned(k_cache, 4) || !aligned(v_cache, 4) ||
@@ -145,23 +150,23 @@ pkv_status kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v
                           int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
                           int32_t head_dim, int32_t kv_dtype, const int32_t* pairs,
                           int32_t n_pairs, void* stream) {
-  if (kv_dtype < PKV_F32 || kv_dtype > PKV_FP8_E4M3FN)
+  if (kv_dtype < PKV_F32 || kv_dtype > PKV_I4)
     return fail(PKV_ERR_UNSUPPORTED, "kv_copy_blocks: unknown kv_dtype");
   if (num_blocks < 1 || block_size < 1 || num_kv_heads < 1 || head_dim < 1 || n_pairs < 0)
     return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: bad sizes");
   if (n_pairs == 0) return ok();
   if (n_pairs > 0x3FFFFFFF) return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: too many pairs");
   if (!k_cache || !v_cache || !pairs) return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: NULL pointer");
-  if (kv_dtype == PKV_I8 && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: an INT8 cache needs k_scale and v_scale");
+  if (pkv::row_scaled(kv_dtype) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, "kv_copy_blocks: an INT8 / INT4 cache needs k_scale and v_scale");
   const int64_t block_rows = (int64_t)num_kv_heads * block_size;
-  const int64_t block_bytes = block_rows * head_dim * pkv::dtype_bytes(kv_dtype);
+  const int64_t block_bytes = block_rows * pkv::row_bytes_of(kv_dtype, head_dim);
   if (block_bytes % 16 || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(pairs, 4))
     return fail(PKV_ERR_INVALID_ARG,
                 "kv_copy_blocks: caches need 16-byte alignment and 16-byte-multiple blocks");
   return hip_status(pkv::launch_copy_blocks(k_cache, v_cache,
-                                            kv_dtype == PKV_I8 ? k_scale : nullptr,
-                                            kv_dtype == PKV_I8 ? v_scale : nullptr, pairs,
+                                            pkv::row_scaled(kv_dtype) ? k_scale : nullptr,
+                                            pkv::row_scaled(kv_dtype) ? v_scale : nullptr, pairs,
                                             n_pairs, block_bytes, block_rows, num_blocks,
                                             static_cast<hipStream_t>(stream)),
                     "kv_copy_blocks");
@@ -177,11 +182,15 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   size_t workspace_bytes, void* stream) {
   if (!is_float_dtype(q_dtype))
     return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: q_dtype must be F32, F16 or BF16");
-  if (kv_dtype != q_dtype && kv_dtype != PKV_I8 && kv_dtype != PKV_FP8_E4M3FN)
+  if (kv_dtype != q_dtype && kv_dtype != PKV_I8 && kv_dtype != PKV_FP8_E4M3FN &&
+      kv_dtype != PKV_I4)
     return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_decode: kv_dtype must equal q_dtype, or be I8 or FP8_E4M3FN");
+                "paged_attention_decode: kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: head_dim must be 64 or 128");
+  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
+    return fail(PKV_ERR_UNSUPPORTED,
+                "paged_attention_decode: INT4 caches need head_dim 128 and F16 or BF16 queries");
   if (block_size != 16 && block_size != 256)
     return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: block_size must be 16 or 256");
   if (batch < 0 || batch > 65535 || num_q_heads < 1 || num_kv_heads < 1 ||
@@ -199,13 +208,13 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   if (batch == 0) return ok();
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer");
-  if ((kv_dtype == PKV_I8 || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
+  if ((pkv::row_scaled(kv_dtype) || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
     return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: quantized cache needs k_scale and v_scale");
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
       !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      (kv_dtype == PKV_I8 && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
+      (pkv::row_scaled(kv_dtype) && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
     return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: misaligned pointer (q, out, caches and INT8 scales need 16 B)");
+                "paged_attention_decode: misaligned pointer (q, out, caches and row scales need 16 B)");
 
   const int32_t G = num_q_heads / num_kv_heads;
   const int32_t head_tiles = (G + 15) / 16;

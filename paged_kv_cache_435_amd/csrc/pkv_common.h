@@ -1,7 +1,8 @@
 // pkv_common.h — shared device helpers for the paged-KV kernels (gfx950).
 //
-// Storage formats: IEEE f32 / f16, bfloat16 (upper half of an f32), INT8 with a
-// per-row scale, and OCP FP8 E4M3FN (bias 7, 3 mantissa bits, max 448).
+// Storage formats: IEEE f32 / f16, bfloat16 (upper half of an f32), INT8 and
+// INT4 (two's-complement nibbles, two per byte) with a per-row scale, and OCP
+// FP8 E4M3FN (bias 7, 3 mantissa bits, max 448).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -85,10 +86,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Element size of a storage type.
+// Element size of a storage type (INT4: two elements per byte; use
+// dtype_bits or row_bytes for it).
 __host__ __device__ constexpr int dtype_bytes(int dt) {
   return dt == PKV_F32 ? 4 : (dt == PKV_F16 || dt == PKV_BF16) ? 2 : 1;
 }
+__host__ __device__ constexpr int dtype_bits(int dt) { return dt == PKV_I4 ? 4 : 8 * dtype_bytes(dt); }
+// Bytes of one stored row of d elements.
+__host__ __device__ constexpr int64_t row_bytes_of(int dt, int64_t d) { return d * dtype_bits(dt) / 8; }
+// Storage types with one float32 scale per stored row.
+__host__ __device__ constexpr bool row_scaled(int dt) { return dt == PKV_I8 || dt == PKV_I4; }
 
 // ---------------------------------------------------------------------------
 // Storage order inside a group of 16 consecutive token rows of one (block,
@@ -106,12 +113,26 @@ __host__ __device__ constexpr int dtype_bytes(int dt) {
 //    nc in [j G, j G + G), the values of tokens 4c .. 4c + 3: the A operand of
 //    O^T += V^T P^T.
 // ---------------------------------------------------------------------------
+//
+// INT4 (rows of d / 2 packed bytes, element 2k in the low nibble of byte k):
+// K groups chunk the packed rows as above (k_group_offset(t, d / 2, 1), the
+// nibble of element d being d & 1).  V groups move nibbles: element (t, d),
+// n = d / 16, sits at nibble v4_group_nibble(t, d) of the group, i.e. byte
+// ((n / 8) * 64 + (t / 4) * 16 + d % 16) * 16 + ((n % 8) / 2) * 4 + t % 4,
+// low nibble for even n.  Lane 16 c + r of a 16-byte load then holds, in word
+// w, tokens 4c .. 4c + 3 of columns 16 (2w) + r (low nibbles) and
+// 16 (2w + 1) + r (high nibbles); a byte holds one token's d and d + 16.
+// ---------------------------------------------------------------------------
 __host__ __device__ constexpr int k_group_offset(int t, int d, int eb) {
   return (((d * eb) >> 4) * 16 + t) * 16 + ((d * eb) & 15);
 }
 __host__ __device__ constexpr int v_group_offset(int t, int d, int eb) {
   return (((d >> 4) / (4 / eb)) * 64 + (t >> 2) * 16 + (d & 15)) * 16 +
          (((d >> 4) % (4 / eb)) * 4 + (t & 3)) * eb;
+}
+__host__ __device__ constexpr int v4_group_nibble(int t, int d) {
+  return ((((d >> 4) >> 3) * 64 + (t >> 2) * 16 + (d & 15)) * 16 + (((d >> 4) & 7) >> 1) * 4 +
+          (t & 3)) * 2 + ((d >> 4) & 1);
 }
 
 }  // namespace pkv

@@ -46,8 +46,11 @@
 //   PKV_STAGES_2B           pipeline depth (tiles in flight), 16-bit and f32 KV
 //   PKV_STAGES_I8           pipeline depth (tiles in flight), INT8 KV
 //   PKV_STAGES_FP8          pipeline depth (tiles in flight), FP8 KV
+//   PKV_STAGES_I4           pipeline depth (tiles in flight), INT4 KV
+//   PKV_WAVES_PER_EU_I4     occupancy target, INT4 KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
+//   PKV_SLOTS_PER_CU_I4       the same for INT4 KV
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
@@ -69,6 +72,15 @@
 #ifndef PKV_SLOTS_PER_CU_I8
 #define PKV_SLOTS_PER_CU_I8 16
 #endif
+#ifndef PKV_STAGES_I4
+#define PKV_STAGES_I4 1
+#endif
+#ifndef PKV_WAVES_PER_EU_I4
+#define PKV_WAVES_PER_EU_I4 4
+#endif
+#ifndef PKV_SLOTS_PER_CU_I4
+#define PKV_SLOTS_PER_CU_I4 16
+#endif
 
 namespace pkv {
 
@@ -85,12 +97,14 @@ struct MfmaOf {
 // Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
 // packed two elements per 32-bit word; for f32 it is one float per word.
 // FP8 -> f16/bf16/f32 uses gfx950's E4M3 conversions (exact).  INT8 -> f16
-// uses 1024 + (q + 128) - 1152.
+// uses 1024 + (q + 128) - 1152.  INT4 (8 nibbles per word) -> f16 uses
+// 1024 + (q + 8) - 1032 on nibble pairs 16 bits apart, so word w of the
+// output holds nibbles (w, w + 4) of the input word (an order the query
+// operand is loaded in to match); -> bf16 goes through f32 (2^23 + u - (2^23 + 8)).
 // ---------------------------------------------------------------------------
 template <int KV, int MT>
 struct Cvt {
-  static constexpr int eb = dtype_bytes(KV);
-  static constexpr int in_elems = 16 / eb;                           // per 16 B chunk
+  static constexpr int in_elems = 128 / dtype_bits(KV);             // per 16 B chunk
   static constexpr int out_words = MT == MT_F32 ? in_elems : in_elems / 2;
   static constexpr int word_out = out_words / 4;                     // outputs per input word
 
@@ -106,6 +120,25 @@ struct Cvt {
       const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
       w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
       w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
+    } else if constexpr (KV == PKV_I4 && MT == MT_F16) {
+      const uint32_t x = raw ^ 0x88888888u;   // two's complement -> offset binary per nibble
+      const uint32_t x8 = x >> 8;
+      const f16x2 bias_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+      const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const f16x2 bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+      auto h2 = [](uint32_t u) { return __builtin_bit_cast(f16x2, u); };
+      w[0] = __builtin_bit_cast(uint32_t, h2((x & 0x000F000Fu) | 0x64006400u) + bias_lo);
+      w[1] = __builtin_bit_cast(uint32_t, h2((x & 0x00F000F0u) | 0x64006400u) * sixteenth + bias_hi);
+      w[2] = __builtin_bit_cast(uint32_t, h2((x8 & 0x000F000Fu) | 0x64006400u) + bias_lo);
+      w[3] = __builtin_bit_cast(uint32_t, h2((x8 & 0x00F000F0u) | 0x64006400u) * sixteenth + bias_hi);
+    } else if constexpr (KV == PKV_I4 && MT == MT_BF16) {
+      const uint32_t x = raw ^ 0x88888888u;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float lo = bitsf(0x4B000000u | ((x >> (4 * k)) & 0xFu)) - 8388616.0f;
+        const float hi = bitsf(0x4B000000u | ((x >> (4 * k + 16)) & 0xFu)) - 8388616.0f;
+        w[k] = __builtin_amdgcn_perm(fbits(hi), fbits(lo), 0x07060302u);   // exact: truncation
+      }
     } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F16) {
       // gfx950 converts OCP E4M3 pairs to f16 (exact; scale 1).
       w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
@@ -122,6 +155,8 @@ struct Cvt {
       w[3] = fbits(hi[1]);
     } else {
       // Generic: through f32 (exact for every pair built here).
+      static_assert(KV != PKV_I4, "INT4 converts to f16 or bf16 only");
+      constexpr int eb = dtype_bytes(KV);
       constexpr int per = 4 / eb;   // elements in the word
       float f[per];
 #pragma unroll
@@ -368,17 +403,22 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 template <int KV>
 struct Tuning {
   static constexpr int stages =
-      KV == PKV_I8 ? PKV_STAGES_I8 : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
-  static constexpr int waves_per_eu = KV == PKV_I8 ? 4 : PKV_WAVES_PER_EU;
-  static constexpr int slots_per_cu = KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8 : PKV_SLOTS_PER_CU_DEFAULT;
+      KV == PKV_I8 ? PKV_STAGES_I8
+                   : KV == PKV_I4 ? PKV_STAGES_I4
+                                  : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
+  static constexpr int waves_per_eu =
+      KV == PKV_I8 ? 4 : (KV == PKV_I4 ? PKV_WAVES_PER_EU_I4 : PKV_WAVES_PER_EU);
+  static constexpr int slots_per_cu =
+      KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8
+                   : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4 : PKV_SLOTS_PER_CU_DEFAULT);
 };
 
 template <int KV, int QT, int D, int BS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
-  constexpr int eb = dtype_bytes(KV);
-  constexpr int R = D * eb;            // bytes per stored row
+  constexpr int eb = dtype_bytes(KV);  // (INT4: handled apart wherever it matters)
+  constexpr int R = (int)row_bytes_of(KV, D);   // bytes per stored row
   constexpr int NL = R / 64;           // 16-byte loads per lane per 16-row tile
   using C = Cvt<KV, MT>;
   constexpr int WPC = C::out_words;    // MFMA words per chunk
@@ -444,7 +484,22 @@ void decode_partition_kernel(DecodeArgs a) {
   uint32_t qop[KW];
 #pragma unroll
   for (int i = 0; i < KW; ++i) qop[i] = 0u;
-  if (head_ok) {
+  if constexpr (KV == PKV_I4) {
+   if (head_ok) {
+    // INT4: the lane's K chunk holds d = 32 c16 .. 32 c16 + 31; word i of it
+    // converts to elements 8 i + (0 4 1 5 2 6 3 7), so q pairs are taken in
+    // that order.
+    const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq * D + 32 * c16) * 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + 16 * i);
+      qop[4 * i + 0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);   // (8i, 8i+4)
+      qop[4 * i + 1] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);   // (8i+1, 8i+5)
+      qop[4 * i + 2] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);   // (8i+2, 8i+6)
+      qop[4 * i + 3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);   // (8i+3, 8i+7)
+    }
+   }
+  } else if (head_ok) {
     constexpr int qsize = QT == PKV_F32 ? 4 : 2;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
@@ -504,7 +559,7 @@ void decode_partition_kernel(DecodeArgs a) {
   const uint32_t loff = (uint32_t)(lane * 16);
 
   // Issue the loads of one tile into a register set.
-  // INT8 row scales: lane 16*c + i holds the scale of token 4*c + i (i < 4) of
+  // Row scales (INT8, INT4): lane 16*c + i holds the scale of token 4*c + i (i < 4) of
   // the tile (one register per tile and cache); the lanes that need tokens
   // 4*c16 .. 4*c16+3 fetch them from their row's first four lanes.
   const int scale_tok = 4 * c16 + (r16 & 3);
@@ -519,7 +574,7 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile + loff + 1024 * j);
 #pragma unroll
     for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + loff + 1024 * j);
-    if constexpr (KV == PKV_I8) {
+    if constexpr (row_scaled(KV)) {
       const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)row0 >> 32))
                            << 32) | (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)row0);
       ks = (a.k_scale + sb)[scale_tok];
@@ -533,7 +588,7 @@ void decode_partition_kernel(DecodeArgs a) {
     // INT8: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane takes
     // its four tokens' values from its row's first four lanes.
     f32x4 krcp = {1.f, 1.f, 1.f, 1.f}, vrcp = krcp;
-    if constexpr (KV == PKV_I8) {
+    if constexpr (row_scaled(KV)) {
       const float kr1 = __builtin_amdgcn_rcpf(ks1);
       const float vr1 = __builtin_amdgcn_rcpf(vs1);
 #pragma unroll
@@ -588,7 +643,7 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       const bool ok = 4 * c16 + i < n_valid;
       float f = kfac;
-      if constexpr (KV == PKV_I8) f = kfac * krcp[i];
+      if constexpr (row_scaled(KV)) f = kfac * krcp[i];
       z[i] = ok ? s[i] * f : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
@@ -614,14 +669,43 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
     }
-    if constexpr (KV == PKV_I8) {
+    if constexpr (row_scaled(KV)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * vrcp[i] : 0.f;
     }
 
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
     // of tokens 4*c16 .. 4*c16+3 (storage order), i.e. the A operand.
-    if constexpr (MT == MT_F32) {
+    if constexpr (KV == PKV_I4) {
+      // Word wd of the lane's 16 bytes converts to column blocks 2 wd (words
+      // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
+      // lane's four: P is packed in the same token order.
+      const u32x2 pb = {pack_p<MT>(p[0], p[2]), pack_p<MT>(p[1], p[3])};
+      const uint32_t m02 = (vmask[0] & 0xFFFFu) | (vmask[2] & 0xFFFF0000u);
+      const uint32_t m13 = (vmask[1] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
+      const bool full = n_valid == 16;
+#pragma unroll
+      for (int wd = 0; wd < NC / 2; ++wd) {
+        uint32_t w[4];
+        C::word(vraw[0][wd], w);
+        u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
+        if (!full) {
+          va = u32x2{w[0] & m02, w[2] & m13};
+          vb = u32x2{w[1] & m02, w[3] & m13};
+        }
+        if constexpr (MT == MT_F16) {
+          acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb), acc[2 * wd], 0, 0, 0);
+          acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+              __builtin_bit_cast(f16x4, vb), __builtin_bit_cast(f16x4, pb), acc[2 * wd + 1], 0, 0, 0);
+        } else {
+          acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(i16x4, va), __builtin_bit_cast(i16x4, pb), acc[2 * wd], 0, 0, 0);
+          acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+              __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb), acc[2 * wd + 1], 0, 0, 0);
+        }
+      }
+    } else if constexpr (MT == MT_F32) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
         uint32_t w[4];
@@ -860,6 +944,13 @@ static hipError_t launch1(DecodeArgs& a, int kv, int d, int bs, int cus, hipStre
   switch (kv) {
     case PKV_I8: return launch2<PKV_I8, QT>(a, d, bs, cus, st);
     case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT>(a, d, bs, cus, st);
+    case PKV_I4:
+      if constexpr (QT == PKV_F32) {
+        return hipErrorInvalidValue;   // rejected by the entry point
+      } else {
+        if (d != 128) return hipErrorInvalidValue;
+        return launch3<PKV_I4, QT, 128>(a, bs, cus, st);
+      }
     default: return launch2<QT, QT>(a, d, bs, cus, st);
   }
 }

@@ -6,6 +6,9 @@
 // q = clamp(rint(fl32(x * s)), -128, 127).  Division is IEEE (no fast-math),
 // rint is round-half-even, so codes and scales are bit-exact.
 //
+// INT4: the same rule with 7 for 127 and codes clamped to [-8, 7], packed two
+// per byte (see int4_row_scale).
+//
 // FP8 E4M3FN, one scale per tensor ([P2] «生产级 LLM 推理的 KV 缓存优化» §4
 // --kv-cache-dtype fp8; [P3] KV-quantization section): s = fl32(max|x| / 448),
 // codes = RNE(clamp(fl32(x / s), -448, 448)).
@@ -39,6 +42,22 @@ __device__ __forceinline__ int8_t int8_code(float x, float s) {
   return (int8_t)(int)q;
 }
 
+// INT4 ([P1] §4 lists an INT4 cache without its quantizer; the rule here is
+// the INT8 one with 7 for 127): s = fl32(fl32(1/a) * 7), codes in [-8, 7]
+// (|x * s| <= 7 up to rounding, so -8 is never produced).
+__device__ __forceinline__ float int4_row_scale(float absmax) {
+  if (absmax == 0.0f) return 0.0f;
+  const float r = 1.0f / absmax;
+  return r * 7.0f;
+}
+
+__device__ __forceinline__ uint32_t int4_nibble(float x, float s) {
+  if (s == 0.0f) return 0u;
+  float q = __builtin_rintf(x * s);
+  q = q < -8.0f ? -8.0f : (q > 7.0f ? 7.0f : q);
+  return (uint32_t)(int)q & 0xFu;
+}
+
 __device__ __forceinline__ uint8_t fp8_code(float x, float s) {
   float y = x / s;                 // IEEE correctly rounded
   if (y != y) return (uint8_t)(0x7Fu | ((fbits(y) >> 24) & 0x80u));   // NaN stays NaN
@@ -64,6 +83,30 @@ __global__ __launch_bounds__(256) void quantize_int8_kernel(const void* __restri
   const float s = int8_row_scale(a);
   for (int i = lane; i < row_len; i += kWave)
     out[base + i] = s == 0.0f ? (int8_t)0 : int8_code(load_f32<XT>(x, base + i), s);
+  if (lane == 0) scale[row] = s == 0.0f ? 1.0f : s;
+}
+
+// INT4 rows: one wave per row, four rows per workgroup; lane i packs elements
+// 2i and 2i + 1 into byte i (low nibble first).
+template <int XT>
+__global__ __launch_bounds__(256) void quantize_int4_kernel(const void* __restrict__ x,
+                                                            uint8_t* __restrict__ out,
+                                                            float* __restrict__ scale,
+                                                            int64_t n_rows, int row_len) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= n_rows) return;
+  const int64_t base = row * row_len;
+  float a = 0.0f;
+  for (int i = lane; i < row_len; i += kWave) a = fmaxf(a, __builtin_fabsf(load_f32<XT>(x, base + i)));
+  a = wave_max(a);
+  const float s = int4_row_scale(a);
+  const int half = row_len / 2;
+  for (int i = lane; i < half; i += kWave) {
+    const uint32_t lo = int4_nibble(load_f32<XT>(x, base + 2 * i), s);
+    const uint32_t hi = int4_nibble(load_f32<XT>(x, base + 2 * i + 1), s);
+    out[row * half + i] = (uint8_t)(lo | (hi << 4));
+  }
   if (lane == 0) scale[row] = s == 0.0f ? 1.0f : s;
 }
 
@@ -106,11 +149,16 @@ __global__ __launch_bounds__(256) void fp8_encode_kernel(const void* __restrict_
 template <int XT>
 static hipError_t quantize_t(const void* x, int64_t n_rows, int row_len, int out_dtype, void* out,
                              float* scale, int scale_given, hipStream_t st) {
-  if (out_dtype == PKV_I8) {
+  if (out_dtype == PKV_I8 || out_dtype == PKV_I4) {
     if (n_rows == 0) return hipSuccess;
     const int64_t blocks = (n_rows + 3) / 4;
-    hipLaunchKernelGGL((quantize_int8_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
-                       static_cast<int8_t*>(out), scale, n_rows, row_len);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (out_dtype == PKV_I8)
+      hipLaunchKernelGGL((quantize_int8_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                         static_cast<int8_t*>(out), scale, n_rows, row_len);
+    else
+      hipLaunchKernelGGL((quantize_int4_kernel<XT>), dim3((unsigned)blocks), dim3(256), 0, st, x,
+                         static_cast<uint8_t*>(out), scale, n_rows, row_len);
     return hipGetLastError();
   }
   const int64_t n = n_rows * (int64_t)row_len;
@@ -156,7 +204,7 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k,
                                                      int num_kv_heads) {
   constexpr int PER = D / kWave;   // elements per lane
   constexpr int eb = dtype_bytes(CT);
-  constexpr int R = D * eb;        // bytes per stored row
+  constexpr int R = (int)row_bytes_of(CT, D);   // bytes per stored row
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= rows) return;
@@ -171,6 +219,28 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k,
   const int64_t group_byte = (dst_row - t16) * R;                      // first byte of the group
   const int64_t src_row = t * num_kv_heads + g;
 
+  if constexpr (CT == PKV_I4) {
+    // Lane i holds two elements that share a stored byte: K elements 2i, 2i+1;
+    // V elements d and d + 16 with d = 32 (i / 16) + i % 16.
+    static_assert(D == 128, "INT4 rows are 128 elements");
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const void* src = which == 0 ? k : v;
+      uint8_t* cache = static_cast<uint8_t*>(which == 0 ? k_cache : v_cache) + group_byte;
+      float* sc = which == 0 ? k_scale : v_scale;
+      const int d0 = which == 0 ? 2 * lane : 32 * (lane >> 4) + (lane & 15);
+      const int d1 = which == 0 ? d0 + 1 : d0 + 16;
+      const float x0 = load_f32<ST>(src, src_row * D + d0);
+      const float x1 = load_f32<ST>(src, src_row * D + d1);
+      const float a = wave_max(fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1)));
+      const float s = int4_row_scale(a);
+      const uint32_t b = int4_nibble(x0, s) | (int4_nibble(x1, s) << 4);
+      const int pos = which == 0 ? k_group_offset(t16, lane, 1) : v4_group_nibble(t16, d0) >> 1;
+      cache[pos] = (uint8_t)b;
+      if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
+    }
+    return;
+  }
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
     const void* src = which == 0 ? k : v;
@@ -222,10 +292,13 @@ static hipError_t append_t(const void* k, const void* v, int num_tokens, const i
   const int64_t rows = (int64_t)num_tokens * hkv;
   const int64_t blocks = (rows + 3) / 4;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  if (d == 64)
+  if constexpr (CT == PKV_I4) {
+    if (d != 128) return hipErrorInvalidValue;
+  } else if (d == 64) {
     hipLaunchKernelGGL((append_kernel<ST, CT, 64>), dim3((unsigned)blocks), dim3(256), 0, st, k, v,
                        slots, kc, vc, ks, vs, rows, nb, bs, hkv);
-  else
+    return hipGetLastError();
+  }
     hipLaunchKernelGGL((append_kernel<ST, CT, 128>), dim3((unsigned)blocks), dim3(256), 0, st, k,
                        v, slots, kc, vc, ks, vs, rows, nb, bs, hkv);
   return hipGetLastError();
@@ -237,6 +310,7 @@ static hipError_t append_s(int ct, const void* k, const void* v, int n, const in
                            int d, hipStream_t st) {
   switch (ct) {
     case PKV_I8: return append_t<ST, PKV_I8>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
+    case PKV_I4: return append_t<ST, PKV_I4>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
     case PKV_FP8_E4M3FN:
       return append_t<ST, PKV_FP8_E4M3FN>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);
     default: return append_t<ST, ST>(k, v, n, slots, kc, vc, ks, vs, nb, bs, hkv, d, st);

@@ -3,10 +3,11 @@
 Setup for tests and the benchmark.  It draws the seeded inputs of
 ``workloads`` and writes every slot of the pools through the library's own
 ``kv_cache_append`` (the way a prefill fills a cache), which stores the rows
-in the library's storage order and quantizes them for INT8 (per row) and FP8
-(with the tensor scale ``kv_quantize`` computes over the whole source pool).
-Every slot no live token occupies is written from a NaN source row — NaN for
-float caches, the NaN code 0x7F for FP8, and a NaN row scale for INT8 — so any
+in the library's storage order and quantizes them for INT8 and INT4 (per row)
+and FP8 (with the tensor scale ``kv_quantize`` computes over the whole source
+pool).  Every slot no live token occupies is written from a NaN source row —
+NaN for float caches, the NaN code 0x7F for FP8, and a NaN row scale for INT8
+and INT4 — so any
 read of a free block, a block tail or a slot whose append has not happened yet
 shows up in the output.  The slot of each sequence's newest token is poisoned
 too when the workload appends it, so a missing append is visible.
@@ -23,7 +24,7 @@ from . import kv_cache_append, kv_quantize
 from . import workloads as W
 
 _CACHE_DTYPE = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-                "i8": torch.int8, "fp8": torch.uint8}
+                "i8": torch.int8, "fp8": torch.uint8, "i4": torch.uint8}
 
 
 def poison_mask(w):
@@ -51,10 +52,11 @@ class DeviceCase:
         self.out = torch.empty_like(self.q)
         shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
         cdt = _CACHE_DTYPE[w.kv_format]
-        self.k_cache = torch.empty(shape, dtype=cdt, device=device)
-        self.v_cache = torch.empty(shape, dtype=cdt, device=device)
+        row = w.head_dim // 2 if w.kv_format == "i4" else w.head_dim   # INT4: two per byte
+        self.k_cache = torch.empty(shape[:-1] + (row,), dtype=cdt, device=device)
+        self.v_cache = torch.empty(shape[:-1] + (row,), dtype=cdt, device=device)
         self.k_scale = self.v_scale = None
-        if w.kv_format == "i8":
+        if w.kv_format in ("i8", "i4"):
             self.k_scale = torch.empty(shape[:-1], dtype=torch.float32, device=device)
             self.v_scale = torch.empty(shape[:-1], dtype=torch.float32, device=device)
         elif w.kv_format == "fp8":
@@ -77,7 +79,7 @@ class DeviceCase:
         kv_cache_append(rows["k"], rows["v"], slots, self.k_cache, self.v_cache, self.k_scale,
                         self.v_scale, kv_dtype=self.kv_dtype)
         del rows
-        if w.kv_format == "i8":   # a NaN row quantizes as an all-zero row: poison its scale
+        if w.kv_format in ("i8", "i4"):   # a NaN row quantizes as an all-zero row: poison its scale
             self.k_scale.permute(0, 2, 1)[mask_t] = float("nan")
             self.v_scale.permute(0, 2, 1)[mask_t] = float("nan")
         if w.appends:
@@ -88,7 +90,7 @@ class DeviceCase:
 
     @property
     def kv_dtype(self):
-        return {"i8": "i8", "fp8": "fp8"}.get(self.w.kv_format)
+        return {"i8": "i8", "fp8": "fp8", "i4": "i4"}.get(self.w.kv_format)
 
 
 def q_to_host(q):

@@ -20,6 +20,9 @@ The five workloads (shapes of the Llama-2 family the pages discuss):
   llama70b_fp8  fp16 q, FP8 E4M3FN KV (per-tensor scale), GQA 64/8, d 128,
                 batch 64, log-normal contexts (median 4096, sigma 1) clipped to
                 [128, 32768], 80 layers, bs 16 or 256
+  llama13b_int4 the llama13b_int8 case with an INT4 cache (per-row scale,
+                packed nibbles)
+  llama70b_int4 the llama70b_gqa8 case with an INT4 cache
 
 Pools hold 1.25x the blocks the sequences need (16 for the tiny case).  Blocks
 are dealt from ``default_rng(1).permutation(pool)`` to sequence 0's logical
@@ -38,7 +41,7 @@ import torch
 class Workload:
     name: str
     q_dtype: torch.dtype
-    kv_format: str            # "f32" | "f16" | "bf16" | "i8" | "fp8"
+    kv_format: str            # "f32" | "f16" | "bf16" | "i8" | "fp8" | "i4"
     batch: int
     num_q_heads: int
     num_kv_heads: int
@@ -66,11 +69,11 @@ class Workload:
 
     def kv_bytes_per_layer(self):
         """Algorithmic KV bytes one decode step reads per layer: K and V rows of
-        every context token of every KV head, plus INT8 row scales."""
-        elem = {"f32": 4, "f16": 2, "bf16": 2, "i8": 1, "fp8": 1}[self.kv_format]
+        every context token of every KV head, plus INT8 / INT4 row scales."""
+        bits = {"f32": 32, "f16": 16, "bf16": 16, "i8": 8, "fp8": 8, "i4": 4}[self.kv_format]
         tokens = int(self.context_lens.astype(np.int64).sum())
-        b = 2 * tokens * self.num_kv_heads * self.head_dim * elem
-        if self.kv_format == "i8":
+        b = 2 * tokens * self.num_kv_heads * self.head_dim * bits // 8
+        if self.kv_format in ("i8", "i4"):
             b += 2 * tokens * self.num_kv_heads * 4
         return b
 
@@ -129,18 +132,20 @@ def make(name, block_size=None, layers=None):
         return Workload(name, torch.bfloat16, "bf16", 8, 32, 32, 128, bs, 1, ctx, nb,
                         deal_blocks(ctx, bs, nb), appends=True,
                         seeds=dict(context=None, permutation=1, q=2, k=3, v=4, new=6))
-    if name == "llama70b_gqa8":
+    if name in ("llama70b_gqa8", "llama70b_int4"):
         ctx = np.random.default_rng(0).integers(512, 32768, 32, endpoint=True).astype(np.int32)
         bs = 16
         nb = pool_for(ctx, bs)
-        return Workload(name, torch.float16, "f16", 32, 64, 8, 128, bs, 1, ctx, nb,
+        fmt = "f16" if name == "llama70b_gqa8" else "i4"
+        return Workload(name, torch.float16, fmt, 32, 64, 8, 128, bs, 1, ctx, nb,
                         deal_blocks(ctx, bs, nb), appends=True,
                         seeds=dict(context=0, permutation=1, q=2, k=3, v=4, new=6))
-    if name == "llama13b_int8":
+    if name in ("llama13b_int8", "llama13b_int4"):
         ctx = np.full(32, 2049, dtype=np.int32)
         bs = 16
         nb = pool_for(ctx, bs)
-        return Workload(name, torch.float16, "i8", 32, 40, 40, 128, bs, 1, ctx, nb,
+        fmt = "i8" if name == "llama13b_int8" else "i4"
+        return Workload(name, torch.float16, fmt, 32, 40, 40, 128, bs, 1, ctx, nb,
                         deal_blocks(ctx, bs, nb), appends=True, outliers=True,
                         seeds=dict(context=None, permutation=1, q=2, k=3, v=4, outliers=5, new=6))
     if name == "llama70b_fp8":
@@ -154,7 +159,8 @@ def make(name, block_size=None, layers=None):
     raise KeyError(name)
 
 
-NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70b_fp8")
+NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70b_fp8",
+         "llama13b_int4", "llama70b_int4")
 
 
 def custom(q_dtype, kv_format, context_lens, num_q_heads, num_kv_heads, head_dim, block_size,

@@ -1,7 +1,7 @@
 """Block copies and the block manager driving the device cache.
 
 kv_copy_blocks: whole pools compared byte for byte with a host copy of the
-same blocks (every KV format; INT8 scales move with their blocks).
+same blocks (every KV format; INT8 / INT4 row scales move with their blocks).
 
 End to end: the block manager places two prompts that share a prefix (prefix
 caching: the shared blocks are written once), forks one sequence, and appends
@@ -28,6 +28,8 @@ def _pool(shape, fmt, seed):
         return torch.randint(-128, 128, shape, generator=g, dtype=torch.int8)
     if fmt == "fp8":
         return torch.randint(0, 256, shape, generator=g, dtype=torch.uint8)
+    if fmt == "i4":   # packed: two elements per byte
+        return torch.randint(0, 256, shape[:-1] + (shape[-1] // 2,), generator=g, dtype=torch.uint8)
     dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[fmt]
     return torch.randn(shape, generator=g).to(dt)
 
@@ -36,14 +38,14 @@ def _bytes(t):
     return t.cpu().contiguous().view(torch.uint8).numpy()
 
 
-@pytest.mark.parametrize("fmt", ["f16", "bf16", "f32", "i8", "fp8"])
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "f32", "i8", "fp8", "i4"])
 @pytest.mark.parametrize("bs,d", [(16, 128), (256, 64)])
 def test_copy_blocks_bit_exact(fmt, bs, d):
     NB, Hkv = 12, 3
     shape = (NB, Hkv, bs, d)
     kc, vc = _pool(shape, fmt, 1), _pool(shape, fmt, 2)
     ks = vs = None
-    if fmt == "i8":
+    if fmt in ("i8", "i4"):
         ks, vs = torch.rand(NB, Hkv, bs), torch.rand(NB, Hkv, bs)
     elif fmt == "fp8":
         ks, vs = torch.tensor([0.5]), torch.tensor([0.25])
@@ -54,16 +56,16 @@ def test_copy_blocks_bit_exact(fmt, bs, d):
     for s, t in pairs:
         if 0 <= s < NB and 0 <= t < NB and s != t:
             want_k[t], want_v[t] = kc[s], vc[s]
-            if fmt == "i8":
+            if fmt in ("i8", "i4"):
                 want_ks[t], want_vs[t] = ks[s], vs[s]
     dev = lambda t: None if t is None else t.cuda()
     kd, vd, ksd, vsd = dev(kc), dev(vc), dev(ks), dev(vs)
     pkv.kv_copy_blocks(kd, vd, torch.from_numpy(pairs).cuda(), ksd, vsd,
-                       kv_dtype={"i8": "i8", "fp8": "fp8"}.get(fmt))
+                       kv_dtype={"i8": "i8", "fp8": "fp8", "i4": "i4"}.get(fmt))
     torch.cuda.synchronize()
     assert np.array_equal(_bytes(kd), _bytes(want_k))
     assert np.array_equal(_bytes(vd), _bytes(want_v))
-    if fmt == "i8":
+    if fmt in ("i8", "i4"):
         assert np.array_equal(_bytes(ksd), _bytes(want_ks))
         assert np.array_equal(_bytes(vsd), _bytes(want_vs))
     if fmt == "fp8":

@@ -1,4 +1,4 @@
-"""The five named workloads at full size, in the launch configuration the
+"""The named workloads at full size, in the launch configuration the
 benchmark times (append of one token per sequence, then decode), against the
 CPU oracle: every sequence for the small ones; for the large ones the shortest
 and the longest sequence plus seeded random ones, each with all its query
@@ -50,3 +50,12 @@ def test_llama70b_fp8_sampled_layers(bs):
     for layer in (0, w.layers - 1):
         run_and_check(w, seqs=_sample_seqs(w, 5, seed=layer), layer=layer)
         torch.cuda.empty_cache()
+
+
+def test_llama13b_int4_whole():
+    run_and_check(W.make("llama13b_int4"))
+
+
+def test_llama70b_int4_sampled():
+    w = W.make("llama70b_int4")
+    run_and_check(w, seqs=_sample_seqs(w, 6))

@@ -20,6 +20,7 @@ RAGGED = [1, 15, 16, 17, 255, 256, 257, 511, 513, 700, 1024, 2049]
     (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
     (torch.float16, "i8"), (torch.bfloat16, "i8"), (torch.float32, "i8"),
     (torch.float16, "fp8"), (torch.bfloat16, "fp8"), (torch.float32, "fp8"),
+    (torch.float16, "i4"), (torch.bfloat16, "i4"),
 ])
 def test_dtype_pairs_ragged(q_dtype, kv):
     w = W.custom(q_dtype, kv, RAGGED, 8, 2, 128, 16, appends=True, name=f"ragged-{kv}")
@@ -180,3 +181,28 @@ def test_head_dim_64_every_format(q_dtype, kv, bs):
     w = W.custom(q_dtype, kv, [1, 17, 300, 1025, 2600], 8, 2, 64, bs, appends=True,
                  name=f"d64-{kv}-bs{bs}")
     run_and_check(w)
+
+
+@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("name,ctx,hq,hkv,bs", [
+    ("i4-bs256-ragged", [1, 15, 255, 256, 257, 3000], 8, 2, 256),
+    ("i4-mqa", [40, 600, 1100], 16, 1, 16),
+    ("i4-g40", [3000, 17, 1100], 40, 1, 16),
+    ("i4-one-long", [60_000], 8, 1, 16),
+])
+def test_int4_shapes(q_dtype, name, ctx, hq, hkv, bs):
+    """INT4 KV (packed nibbles, per-row scales) over block sizes, MHA/GQA/MQA,
+    groups wider than a head tile and a context split into many items."""
+    w = W.custom(q_dtype, "i4", ctx, hq, hkv, 128, bs, appends=True, name=name)
+    run_and_check(w)
+
+
+def test_int4_f32_queries_are_rejected():
+    w = W.custom(torch.float16, "i4", [20], 4, 4, 128, 16, name="i4-f32q")
+    case = DeviceCase(w)
+    q = case.q.float()
+    with pytest.raises(RuntimeError, match="F16 or BF16"):
+        pkv.paged_attention_decode(torch.empty_like(q), q, case.k_cache, case.v_cache,
+                                   case.block_tables, case.context_lens, w.scale,
+                                   w.max_context_len, k_scale=case.k_scale, v_scale=case.v_scale,
+                                   kv_dtype="i4")

@@ -45,6 +45,32 @@ def test_int8_quantize_bit_exact(dtype, d):
 
 
 @pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("d", [128, 64, 100, 1000])
+def test_int4_quantize_bit_exact(dtype, d):
+    x = _source(20011, d, dtype, seed=d + 1, zero_rows=(0, 9))
+    xd = x.cuda()
+    codes = torch.empty(x.shape[0], d // 2, dtype=torch.uint8, device="cuda")
+    scale = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    pkv.kv_quantize(xd, codes, scale, out_dtype="i4")
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_int4_rows(_host_f32(x))
+    p_ref = oracle.pack_int4(q_ref)
+    c = codes.cpu().numpy()
+    s = scale.cpu().numpy()
+    say(f"  int4 {dtype} d={d}: byte mismatches {int((c != p_ref).sum())}, "
+        f"scale mismatches {int((s.view(np.uint32) != s_ref.view(np.uint32)).sum())}")
+    assert np.array_equal(c, p_ref)
+    assert np.array_equal(s.view(np.uint32), s_ref.view(np.uint32))
+
+
+def test_int4_quantize_rejects_odd_rows():
+    x = torch.zeros(4, 7, dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError):
+        pkv.kv_quantize(x, torch.empty(4, 3, dtype=torch.uint8, device="cuda"),
+                        torch.empty(4, device="cuda"), out_dtype="i4")
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16, torch.float32])
 def test_fp8_quantize_bit_exact(dtype):
     x = _source(30000, 128, dtype, seed=5)
     xd = x.cuda()
@@ -84,6 +110,8 @@ def test_fp8_every_code_and_tie():
 def _pool(w, fmt, seed):
     shape = (w.num_blocks, w.num_kv_heads, w.block_size, w.head_dim)
     g = torch.Generator().manual_seed(seed)
+    if fmt == "i4":
+        return torch.randint(0, 256, shape[:-1] + (w.head_dim // 2,), generator=g, dtype=torch.uint8)
     if fmt == "i8":
         return torch.randint(-128, 128, shape, generator=g, dtype=torch.int8)
     if fmt == "fp8":
@@ -102,13 +130,16 @@ def _np_storage(t):
     (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
     (torch.float16, "i8"), (torch.bfloat16, "i8"), (torch.float32, "i8"),
     (torch.float16, "fp8"), (torch.bfloat16, "fp8"),
+    (torch.float16, "i4"), (torch.bfloat16, "i4"), (torch.float32, "i4"),
 ])
-@pytest.mark.parametrize("bs,d", [(16, 128), (256, 64)])
+@pytest.mark.parametrize("bs,d", [(16, 128), (256, 64), (256, 128)])
 def test_append_whole_pool_bit_exact(src_dtype, fmt, bs, d):
+    if fmt == "i4" and d != 128:
+        pytest.skip("INT4 caches are built for head_dim 128 (d = 64 is rejected: see below)")
     w = W.custom(src_dtype, fmt, [30, 300, 17, 1], 8, 4, d, bs, extra_blocks=2, appends=True)
     kc, vc = _pool(w, fmt, 1), _pool(w, fmt, 2)
     ks = vs = None
-    if fmt == "i8":
+    if fmt in ("i8", "i4"):
         ks = torch.rand(w.num_blocks, w.num_kv_heads, bs)
         vs = torch.rand(w.num_blocks, w.num_kv_heads, bs)
     elif fmt == "fp8":
@@ -122,18 +153,34 @@ def test_append_whole_pool_bit_exact(src_dtype, fmt, bs, d):
     dev = lambda t: None if t is None else t.cuda()
     kcd, vcd, ksd, vsd = dev(kc), dev(vc), dev(ks), dev(vs)
     pkv.kv_cache_append(kn.cuda(), vn.cuda(), slots.cuda(), kcd, vcd, ksd, vsd,
-                        kv_dtype={"i8": "i8", "fp8": "fp8"}.get(fmt))
+                        kv_dtype={"i8": "i8", "fp8": "fp8", "i4": "i4"}.get(fmt))
     torch.cuda.synchronize()
     np_scale = (lambda t: None if t is None else (t.numpy() if t.numel() > 1
                                                   else np.float32(t.item())))
     # The pools hold bytes in the library's storage order: the oracle reads
     # them in logical row order, before and after.
-    K, V = oracle.layout.k_from_stored, oracle.layout.v_from_stored
+    K = oracle.layout.k_from_stored
+    V = oracle.layout.v4_from_stored if fmt == "i4" else oracle.layout.v_from_stored
     ek, ev, eks, evs = oracle.append.append_expected(
         K(_np_storage(kc)), V(_np_storage(vc)), _np_storage(kn), _np_storage(vn), slots.numpy(),
         bs, fmt, np_scale(ks), np_scale(vs))
     assert np.array_equal(K(_np_storage(kcd.cpu())).view(np.uint8), ek.view(np.uint8))
     assert np.array_equal(V(_np_storage(vcd.cpu())).view(np.uint8), ev.view(np.uint8))
-    if fmt == "i8":
+    if fmt in ("i8", "i4"):
         assert np.array_equal(ksd.cpu().numpy().view(np.uint32), eks.view(np.uint32))
         assert np.array_equal(vsd.cpu().numpy().view(np.uint32), evs.view(np.uint32))
+
+
+def test_int4_head_dim_64_is_rejected():
+    kc = torch.zeros(4, 2, 16, 32, dtype=torch.uint8, device="cuda")
+    k = torch.zeros(1, 2, 64, dtype=torch.float16, device="cuda")
+    sc = torch.zeros(4, 2, 16, device="cuda")
+    with pytest.raises(RuntimeError, match="head_dim 128"):
+        pkv.kv_cache_append(k, k, torch.zeros(1, dtype=torch.int64, device="cuda"), kc, kc.clone(),
+                            sc, sc.clone(), kv_dtype="i4")
+    q = torch.zeros(1, 2, 64, dtype=torch.float16, device="cuda")
+    with pytest.raises(RuntimeError, match="head_dim 128"):
+        pkv.paged_attention_decode(torch.empty_like(q), q, kc, kc.clone(),
+                                   torch.zeros(1, 1, dtype=torch.int32, device="cuda"),
+                                   torch.ones(1, dtype=torch.int32, device="cuda"), 0.125, 1,
+                                   k_scale=sc, v_scale=sc.clone(), kv_dtype="i4")

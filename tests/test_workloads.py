@@ -32,6 +32,17 @@ def test_published_shapes():
     f = W.make("llama70b_fp8")
     assert f.layers == 80 and f.context_lens.min() >= 128 and f.context_lens.max() <= 32768
     assert W.make("llama70b_fp8", block_size=256).num_blocks == 2087
+    i4 = W.make("llama70b_int4")
+    assert i4.kv_format == "i4" and np.array_equal(i4.context_lens, w.context_lens)
+    # packed nibbles plus one float32 scale per row
+    assert i4.kv_bytes_per_layer() == 2 * 560359 * 8 * (128 // 2 + 4)
+    assert W.make("llama13b_int4").kv_format == "i4"
+
+
+@pytest.mark.parametrize("name", W.NAMES)
+def test_every_workload_names_a_known_format(name):
+    from oracle import widen
+    assert W.make(name).kv_format in widen.FORMATS
 
 
 @pytest.mark.parametrize("name", ["llama7b_bf16", "llama13b_int8", "llama70b_fp8"])
