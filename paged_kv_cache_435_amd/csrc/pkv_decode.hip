@@ -121,16 +121,17 @@ struct Cvt {
       w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
       w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
     } else if constexpr (KV == PKV_I4 && MT == MT_F16) {
-      const uint32_t x = raw ^ 0x88888888u;   // two's complement -> offset binary per nibble
-      const uint32_t x8 = x >> 8;
+      // (raw & mask) ^ 0x6408: the f16 0x6400 | (u ^ 8) = 1024 + (q + 8) in one
+      // bit operation (u = the stored nibble, u ^ 8 its offset-binary form).
+      const uint32_t x8 = raw >> 8;
       const f16x2 bias_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
       const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
       const f16x2 bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
       auto h2 = [](uint32_t u) { return __builtin_bit_cast(f16x2, u); };
-      w[0] = __builtin_bit_cast(uint32_t, h2((x & 0x000F000Fu) | 0x64006400u) + bias_lo);
-      w[1] = __builtin_bit_cast(uint32_t, h2((x & 0x00F000F0u) | 0x64006400u) * sixteenth + bias_hi);
-      w[2] = __builtin_bit_cast(uint32_t, h2((x8 & 0x000F000Fu) | 0x64006400u) + bias_lo);
-      w[3] = __builtin_bit_cast(uint32_t, h2((x8 & 0x00F000F0u) | 0x64006400u) * sixteenth + bias_hi);
+      w[0] = __builtin_bit_cast(uint32_t, h2((raw & 0x000F000Fu) ^ 0x64086408u) + bias_lo);
+      w[1] = __builtin_bit_cast(uint32_t, h2((raw & 0x00F000F0u) ^ 0x64806480u) * sixteenth + bias_hi);
+      w[2] = __builtin_bit_cast(uint32_t, h2((x8 & 0x000F000Fu) ^ 0x64086408u) + bias_lo);
+      w[3] = __builtin_bit_cast(uint32_t, h2((x8 & 0x00F000F0u) ^ 0x64806480u) * sixteenth + bias_hi);
     } else if constexpr (KV == PKV_I4 && MT == MT_BF16) {
       const uint32_t x = raw ^ 0x88888888u;
 #pragma unroll
@@ -385,6 +386,12 @@ __device__ bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int l
 // sets used in rotation, the loop unrolled so no register copy waits on a
 // load).  The workgroup is one wave and needs no LDS.
 // ---------------------------------------------------------------------------
+// Lane L of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+template <int L>
+__device__ __forceinline__ float row_bcast(float v) {
+  return bitsf((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(v), 0x150 + L, 0xF, 0xF, false));
+}
+
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 #if PKV_NT_LOADS
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -585,17 +592,21 @@ void decode_partition_kernel(DecodeArgs a) {
 
   // Softmax update and both contractions for one loaded tile.
   auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1) {
-    // INT8: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane takes
-    // its four tokens' values from its row's first four lanes.
+    // INT8 / INT4: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane
+    // takes its four tokens' values from its row's first four lanes (DPP row
+    // broadcast of lane i of each 16-lane row).
     f32x4 krcp = {1.f, 1.f, 1.f, 1.f}, vrcp = krcp;
     if constexpr (row_scaled(KV)) {
       const float kr1 = __builtin_amdgcn_rcpf(ks1);
       const float vr1 = __builtin_amdgcn_rcpf(vs1);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        krcp[i] = __shfl(kr1, 16 * c16 + i, kWave);
-        vrcp[i] = __shfl(vr1, 16 * c16 + i, kWave);
-      }
+      krcp[0] = row_bcast<0>(kr1);
+      krcp[1] = row_bcast<1>(kr1);
+      krcp[2] = row_bcast<2>(kr1);
+      krcp[3] = row_bcast<3>(kr1);
+      vrcp[0] = row_bcast<0>(vr1);
+      vrcp[1] = row_bcast<1>(vr1);
+      vrcp[2] = row_bcast<2>(vr1);
+      vrcp[3] = row_bcast<3>(vr1);
     }
     const int t0 = t_begin + tile * 16;
     int n_valid = t_end - t0;
@@ -681,18 +692,12 @@ void decode_partition_kernel(DecodeArgs a) {
       // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
       // lane's four: P is packed in the same token order.
       const u32x2 pb = {pack_p<MT>(p[0], p[2]), pack_p<MT>(p[1], p[3])};
-      const uint32_t m02 = (vmask[0] & 0xFFFFu) | (vmask[2] & 0xFFFF0000u);
-      const uint32_t m13 = (vmask[1] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
-      const bool full = n_valid == 16;
+      // Codes are finite and P is exactly 0 past the context, so no mask.
 #pragma unroll
       for (int wd = 0; wd < NC / 2; ++wd) {
         uint32_t w[4];
         C::word(vraw[0][wd], w);
-        u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
-        if (!full) {
-          va = u32x2{w[0] & m02, w[2] & m13};
-          vb = u32x2{w[1] & m02, w[3] & m13};
-        }
+        const u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
         if constexpr (MT == MT_F16) {
           acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
               __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb), acc[2 * wd], 0, 0, 0);
@@ -727,7 +732,9 @@ void decode_partition_kernel(DecodeArgs a) {
       const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
       const uint32_t m01 = (vmask[0] & 0xFFFFu) | (vmask[1] & 0xFFFF0000u);
       const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
-      const bool full = n_valid == 16;   // uniform: only a sequence's last tile is partial
+      // uniform: only a sequence's last tile is partial.  INT8 codes are finite
+      // and P is exactly 0 past the context: no mask needed.
+      const bool full = n_valid == 16 || KV == PKV_I8;
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
         uint32_t w[2];
