@@ -36,6 +36,7 @@
 #include <stdlib.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "pkv_common.h"
 #include "pkv_internal.h"
@@ -73,7 +74,7 @@
 #define PKV_SLOTS_PER_CU_I8 16
 #endif
 #ifndef PKV_STAGES_I4
-#define PKV_STAGES_I4 1
+#define PKV_STAGES_I4 2
 #endif
 #ifndef PKV_WAVES_PER_EU_I4
 #define PKV_WAVES_PER_EU_I4 4
@@ -591,7 +592,11 @@ void decode_partition_kernel(DecodeArgs a) {
   };
 
   // Softmax update and both contractions for one loaded tile.
-  auto compute = [&](int tile, const u32x4* kraw, const u32x4* vraw, float ks1, float vs1) {
+  // `checked` (a std::bool_constant): the tile may be partial or outside the
+  // pool, so tokens are masked one by one; otherwise all 16 are live.
+  auto compute = [&](auto checked_c, int tile, const u32x4* kraw, const u32x4* vraw, float ks1,
+                     float vs1) {
+    constexpr bool checked = decltype(checked_c)::value;
     // INT8 / INT4: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane
     // takes its four tokens' values from its row's first four lanes (DPP row
     // broadcast of lane i of each 16-lane row).
@@ -608,10 +613,12 @@ void decode_partition_kernel(DecodeArgs a) {
       vrcp[2] = row_bcast<2>(vr1);
       vrcp[3] = row_bcast<3>(vr1);
     }
-    const int t0 = t_begin + tile * 16;
-    int n_valid = t_end - t0;
-    n_valid = n_valid > 16 ? 16 : n_valid;
-    if (tile_phys(tile) < 0) n_valid = 0;
+    int n_valid = 16;
+    if constexpr (checked) {
+      n_valid = t_end - (t_begin + tile * 16);
+      n_valid = n_valid > 16 ? 16 : n_valid;
+      if (tile_phys(tile) < 0) n_valid = 0;
+    }
 
     // Tokens 4*c16 + i of this lane past the context get zero V (masks on the
     // converted operands; all ones for a full tile).
@@ -652,16 +659,17 @@ void decode_partition_kernel(DecodeArgs a) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool ok = 4 * c16 + i < n_valid;
       float f = kfac;
       if constexpr (row_scaled(KV)) f = kfac * krcp[i];
-      z[i] = ok ? s[i] * f : -__builtin_inff();
+      z[i] = s[i] * f;
+      if constexpr (checked) z[i] = 4 * c16 + i < n_valid ? z[i] : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
-    const bool live = m_new != -__builtin_inff();
+    // A live tile has a finite max, so exp2(-inf) = 0 covers the first one.
+    const bool live = !checked || m_new != -__builtin_inff();
     // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may
     // flush to zero, which only drops weights under 1e-38 of the largest.
     const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -669,7 +677,10 @@ void decode_partition_kernel(DecodeArgs a) {
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
+      if constexpr (checked)
+        p[i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
+      else
+        p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
       psum += p[i];
     }
     l_run = l_run * alpha + psum;
@@ -681,8 +692,9 @@ void decode_partition_kernel(DecodeArgs a) {
       for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
     }
     if constexpr (row_scaled(KV)) {
+      // (the guard keeps a masked token's P at 0 even if its slot's scale is NaN)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = p[i] > 0.f ? p[i] * vrcp[i] : 0.f;
+      for (int i = 0; i < 4; ++i) p[i] = (!checked || p[i] > 0.f) ? p[i] * vrcp[i] : 0.f;
     }
 
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
@@ -734,7 +746,7 @@ void decode_partition_kernel(DecodeArgs a) {
       const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
       // uniform: only a sequence's last tile is partial.  INT8 codes are finite
       // and P is exactly 0 past the context: no mask needed.
-      const bool full = n_valid == 16 || KV == PKV_I8;
+      const bool full = !checked || n_valid == 16 || KV == PKV_I8;
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) {
         uint32_t w[2];
@@ -769,16 +781,21 @@ void decode_partition_kernel(DecodeArgs a) {
   float ks[S], vs[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) ks[i] = vs[i] = 1.f;
+  // The steady loop never reaches an item's last tile (the only one that can
+  // be partial), so its tiles take the unchecked path; a table entry outside
+  // the pool skips its tile (a uniform branch with nothing on the other side).
+  // The tail takes the checked path.
   int tile = 0;
-  if (ntiles > 2 * S - 2) {
+  if (ntiles > 2 * S - 1) {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i]);
-    for (; tile + 2 * S - 2 < ntiles; tile += S) {
+    for (; tile + 2 * S - 1 < ntiles; tile += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int nx = (i + S - 1) % S;
         issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        compute(tile + i, kr[i], vr[i], ks[i], vs[i]);
+        if (tile_phys(tile + i) >= 0)
+          compute(std::false_type{}, tile + i, kr[i], vr[i], ks[i], vs[i]);
       }
     }
   } else {
@@ -792,7 +809,7 @@ void decode_partition_kernel(DecodeArgs a) {
       if (tile + i < ntiles) {
         const int nx = (i + S - 1) % S;
         if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        compute(tile + i, kr[i], vr[i], ks[i], vs[i]);
+        compute(std::true_type{}, tile + i, kr[i], vr[i], ks[i], vs[i]);
       }
     }
   }
