@@ -98,10 +98,11 @@ struct MfmaOf {
 // Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
 // packed two elements per 32-bit word; for f32 it is one float per word.
 // FP8 -> f16/bf16/f32 uses gfx950's E4M3 conversions (exact).  INT8 -> f16
-// uses 1024 + (q + 128) - 1152.  INT4 (8 nibbles per word) -> f16 uses
-// 1024 + (q + 8) - 1032 on nibble pairs 16 bits apart, so word w of the
-// output holds nibbles (w, w + 4) of the input word (an order the query
-// operand is loaded in to match); -> bf16 goes through f32 (2^23 + u - (2^23 + 8)).
+// uses 1024 + (q + 128) - 1152.  INT4 (8 nibbles per word) takes nibble pairs
+// 16 bits apart, so word w of the output holds nibbles (w, w + 4) of the
+// input word (an order the query operand is loaded in to match): -> f16 as
+// offset subnormals (q + 8) 2^-24 / 2^-20, corrected after the products;
+// -> bf16 exactly, through f32 (2^23 + u - (2^23 + 8)).
 // ---------------------------------------------------------------------------
 template <int KV, int MT>
 struct Cvt {
@@ -122,17 +123,17 @@ struct Cvt {
       w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
       w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
     } else if constexpr (KV == PKV_I4 && MT == MT_F16) {
-      // (raw & mask) ^ 0x6408: the f16 0x6400 | (u ^ 8) = 1024 + (q + 8) in one
-      // bit operation (u = the stored nibble, u ^ 8 its offset-binary form).
+      // Offset codes as f16 subnormals, one bit operation per word:
+      // (raw & mask) ^ 8 puts u ^ 8 = q + 8 (u = the stored two's-complement
+      // nibble) in the low mantissa bits, i.e. (q + 8) 2^-24 for the low nibble
+      // of a byte pair and (q + 8) 2^-20 for the high one.  The kernel takes
+      // the offset and the powers of two back out (see OffsetCodes); the MFMA
+      // multiplies f16 subnormals exactly.
       const uint32_t x8 = raw >> 8;
-      const f16x2 bias_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-      const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-      const f16x2 bias_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
-      auto h2 = [](uint32_t u) { return __builtin_bit_cast(f16x2, u); };
-      w[0] = __builtin_bit_cast(uint32_t, h2((raw & 0x000F000Fu) ^ 0x64086408u) + bias_lo);
-      w[1] = __builtin_bit_cast(uint32_t, h2((raw & 0x00F000F0u) ^ 0x64806480u) * sixteenth + bias_hi);
-      w[2] = __builtin_bit_cast(uint32_t, h2((x8 & 0x000F000Fu) ^ 0x64086408u) + bias_lo);
-      w[3] = __builtin_bit_cast(uint32_t, h2((x8 & 0x00F000F0u) ^ 0x64806480u) * sixteenth + bias_hi);
+      w[0] = (raw & 0x000F000Fu) ^ 0x00080008u;
+      w[1] = (raw & 0x00F000F0u) ^ 0x00800080u;
+      w[2] = (x8 & 0x000F000Fu) ^ 0x00080008u;
+      w[3] = (x8 & 0x00F000F0u) ^ 0x00800080u;
     } else if constexpr (KV == PKV_I4 && MT == MT_BF16) {
       const uint32_t x = raw ^ 0x88888888u;
 #pragma unroll
@@ -524,9 +525,36 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
+  // INT4 with f16 queries (offset codes): K and V enter the MFMAs as
+  // (q + 8) 2^-24 (low nibbles) and (q + 8) 2^-20 (high nibbles).  Query words
+  // that meet high nibbles are taken at 1/16 (exact: a power of two), so
+  // S = 2^24 S_mfma - 8 sum(q); V block pairs come out as
+  // 2^-24 (sum p q + 8 sum p) and 2^-20 (...), with sum p (the P values the
+  // MFMA saw) from one more MFMA against ones.
+  constexpr bool offset_codes = KV == PKV_I4 && MT == MT_F16;
+  float qsum = 0.f;
+  if constexpr (offset_codes) {
+    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      f16x2 h = __builtin_bit_cast(f16x2, qop[i]);
+      if (i & 1) {
+        h = h * sixteenth;
+        qop[i] = __builtin_bit_cast(uint32_t, h);
+      }
+      const float t = (float)h[0] + (float)h[1];
+      qsum += (i & 1) ? 16.f * t : t;
+    }
+    qsum += __shfl_xor(qsum, 16, kWave);
+    qsum += __shfl_xor(qsum, 32, kWave);
+  }
+
   // Constant factors: logits are taken in the exp2 domain.
   float kfac = a.scale * 1.4426950408889634f;
   float vfac = 1.0f;
+  // offset codes: z = (s * 2^24 - 8 qsum) * kfac * (1 / row scale)
+  const float kf24 = kfac * 16777216.0f;
+  const float kbias = -8.0f * qsum * kfac;
   if constexpr (KV == PKV_FP8_E4M3FN) {
     kfac *= a.k_scale[0] * cvt_gain<KV, MT>();
     vfac = a.v_scale[0] * cvt_gain<KV, MT>();
@@ -538,6 +566,7 @@ void decode_partition_kernel(DecodeArgs a) {
   f32x4 acc[NC];
 #pragma unroll
   for (int nc = 0; nc < NC; ++nc) acc[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};   // offset codes: sum of P per head (every row)
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
@@ -555,8 +584,7 @@ void decode_partition_kernel(DecodeArgs a) {
     return v;
   };
   // First cache row of a tile in the [NB][Hkv][BS] row space.
-  auto tile_row0 = [&](int tile) -> int64_t {
-    int phys = tile_phys(tile);
+  auto tile_row0 = [&](int tile, int phys) -> int64_t {
     phys = phys < 0 ? 0 : phys;
     return ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS);
   };
@@ -571,8 +599,9 @@ void decode_partition_kernel(DecodeArgs a) {
   // the tile (one register per tile and cache); the lanes that need tokens
   // 4*c16 .. 4*c16+3 fetch them from their row's first four lanes.
   const int scale_tok = 4 * c16 + (r16 & 3);
-  auto issue = [&](int tile, u32x4* kr, u32x4* vr, float& ks, float& vs) {
-    const int64_t row0 = tile_row0(tile);
+  auto issue = [&](int tile, u32x4* kr, u32x4* vr, float& ks, float& vs, int& phys) {
+    phys = tile_phys(tile);
+    const int64_t row0 = tile_row0(tile, phys);
     const uint64_t tile_bytes = (uint64_t)row0 * R;   // uniform: keep it scalar
     const uint64_t tb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tile_bytes >> 32)) << 32) |
                         (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)tile_bytes);
@@ -595,7 +624,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // `checked` (a std::bool_constant): the tile may be partial or outside the
   // pool, so tokens are masked one by one; otherwise all 16 are live.
   auto compute = [&](auto checked_c, int tile, const u32x4* kraw, const u32x4* vraw, float ks1,
-                     float vs1) {
+                     float vs1, int phys) {
     constexpr bool checked = decltype(checked_c)::value;
     // INT8 / INT4: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane
     // takes its four tokens' values from its row's first four lanes (DPP row
@@ -617,7 +646,7 @@ void decode_partition_kernel(DecodeArgs a) {
     if constexpr (checked) {
       n_valid = t_end - (t_begin + tile * 16);
       n_valid = n_valid > 16 ? 16 : n_valid;
-      if (tile_phys(tile) < 0) n_valid = 0;
+      if (phys < 0) n_valid = 0;
     }
 
     // Tokens 4*c16 + i of this lane past the context get zero V (masks on the
@@ -659,9 +688,13 @@ void decode_partition_kernel(DecodeArgs a) {
     float mx = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float f = kfac;
-      if constexpr (row_scaled(KV)) f = kfac * krcp[i];
-      z[i] = s[i] * f;
+      if constexpr (offset_codes) {
+        z[i] = __builtin_fmaf(s[i], kf24, kbias) * krcp[i];
+      } else {
+        float f = kfac;
+        if constexpr (row_scaled(KV)) f = kfac * krcp[i];
+        z[i] = s[i] * f;
+      }
       if constexpr (checked) z[i] = 4 * c16 + i < n_valid ? z[i] : -__builtin_inff();
       mx = fmaxf(mx, z[i]);
     }
@@ -690,6 +723,7 @@ void decode_partition_kernel(DecodeArgs a) {
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
+      if constexpr (offset_codes) acc_p[0] *= alpha;   // only row 0 is read
     }
     if constexpr (row_scaled(KV)) {
       // (the guard keeps a masked token's P at 0 even if its slot's scale is NaN)
@@ -721,6 +755,11 @@ void decode_partition_kernel(DecodeArgs a) {
           acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
               __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb), acc[2 * wd + 1], 0, 0, 0);
         }
+      }
+      if constexpr (offset_codes) {
+        const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+        acc_p = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb), acc_p,
+                                                      0, 0, 0);
       }
     } else if constexpr (MT == MT_F32) {
 #pragma unroll
@@ -779,8 +818,12 @@ void decode_partition_kernel(DecodeArgs a) {
   constexpr int S = Tuning<KV>::stages;
   u32x4 kr[S][NL], vr[S][NL];
   float ks[S], vs[S];
+  int ph[S];   // physical block of the tile in each register set (-1: skipped)
 #pragma unroll
-  for (int i = 0; i < S; ++i) ks[i] = vs[i] = 1.f;
+  for (int i = 0; i < S; ++i) {
+    ks[i] = vs[i] = 1.f;
+    ph[i] = -1;
+  }
   // The steady loop never reaches an item's last tile (the only one that can
   // be partial), so its tiles take the unchecked path; a table entry outside
   // the pool skips its tile (a uniform branch with nothing on the other side).
@@ -788,28 +831,28 @@ void decode_partition_kernel(DecodeArgs a) {
   int tile = 0;
   if (ntiles > 2 * S - 1) {
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i]);
+    for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i], ph[i]);
     for (; tile + 2 * S - 1 < ntiles; tile += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int nx = (i + S - 1) % S;
-        issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        if (tile_phys(tile + i) >= 0)
-          compute(std::false_type{}, tile + i, kr[i], vr[i], ks[i], vs[i]);
+        issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx], ph[nx]);
+        if (ph[i] >= 0)
+          compute(std::false_type{}, tile + i, kr[i], vr[i], ks[i], vs[i], ph[i]);
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
-      if (i < ntiles) issue(i, kr[i], vr[i], ks[i], vs[i]);
+      if (i < ntiles) issue(i, kr[i], vr[i], ks[i], vs[i], ph[i]);
   }
   for (; tile < ntiles; tile += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
       if (tile + i < ntiles) {
         const int nx = (i + S - 1) % S;
-        if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx]);
-        compute(std::true_type{}, tile + i, kr[i], vr[i], ks[i], vs[i]);
+        if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx], ph[nx]);
+        compute(std::true_type{}, tile + i, kr[i], vr[i], ks[i], vs[i], ph[i]);
       }
     }
   }
@@ -818,6 +861,11 @@ void decode_partition_kernel(DecodeArgs a) {
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
   if (!head_ok) return;
+  if constexpr (offset_codes) {
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+      acc[nc] = acc[nc] * ((nc & 1) ? 1048576.0f : 16777216.0f) - 8.0f * acc_p[0];
+  }
   if (whole_unit) {
     const float inv = vfac / l_tot;
 #pragma unroll
