@@ -98,7 +98,8 @@ struct MfmaOf {
 // Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
 // packed two elements per 32-bit word; for f32 it is one float per word.
 // FP8 -> f16/bf16/f32 uses gfx950's E4M3 conversions (exact).  INT8 -> f16
-// uses 1024 + (q + 128) - 1152.  INT4 (8 nibbles per word) takes nibble pairs
+// gives offset subnormals (q + 128) 2^-24, corrected after the products.
+// INT4 (8 nibbles per word) takes nibble pairs
 // 16 bits apart, so word w of the output holds nibbles (w, w + 4) of the
 // input word (an order the query operand is loaded in to match): -> f16 as
 // offset subnormals (q + 8) 2^-24 / 2^-20, corrected after the products;
@@ -116,12 +117,11 @@ struct Cvt {
                   (KV == PKV_F32 && MT == MT_F32)) {
       w[0] = raw;
     } else if constexpr (KV == PKV_I8 && MT == MT_F16) {
+      // Offset codes as f16 subnormals (q + 128) 2^-24: the bytes of
+      // raw ^ 0x80 moved to the low byte of each half (see OffsetCodes).
       const uint32_t t = raw ^ 0x80808080u;
-      const uint32_t lo = __builtin_amdgcn_perm(0x64646464u, t, 0x04010400u);
-      const uint32_t hi = __builtin_amdgcn_perm(0x64646464u, t, 0x04030402u);
-      const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-      w[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, lo) - bias);
-      w[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2, hi) - bias);
+      w[0] = __builtin_amdgcn_perm(0u, t, 0x04010400u);
+      w[1] = __builtin_amdgcn_perm(0u, t, 0x04030402u);
     } else if constexpr (KV == PKV_I4 && MT == MT_F16) {
       // Offset codes as f16 subnormals, one bit operation per word:
       // (raw & mask) ^ 8 puts u ^ 8 = q + 8 (u = the stored two's-complement
@@ -525,25 +525,29 @@ void decode_partition_kernel(DecodeArgs a) {
     }
   }
 
-  // INT4 with f16 queries (offset codes): K and V enter the MFMAs as
-  // (q + 8) 2^-24 (low nibbles) and (q + 8) 2^-20 (high nibbles).  Query words
-  // that meet high nibbles are taken at 1/16 (exact: a power of two), so
-  // S = 2^24 S_mfma - 8 sum(q); V block pairs come out as
-  // 2^-24 (sum p q + 8 sum p) and 2^-20 (...), with sum p (the P values the
-  // MFMA saw) from one more MFMA against ones.
-  constexpr bool offset_codes = KV == PKV_I4 && MT == MT_F16;
+  // OffsetCodes — INT8 and INT4 with f16 queries: codes enter the MFMAs as
+  // f16 subnormals (q + o) 2^-24 (o = 128 for INT8, 8 for INT4; INT4 high
+  // nibbles as (q + 8) 2^-20), which costs one bit operation per word.  Query
+  // words that meet INT4 high nibbles are taken at 1/16 (a power of two), so
+  // S = 2^24 S_mfma - o sum(q); V comes out as 2^-24 (sum p q + o sum p) (2^-20
+  // for INT4's odd column blocks), with sum p (the P values the MFMA saw)
+  // from one more MFMA against ones.  The offsets are small next to the sums
+  // they are taken from (fp32 keeps about 1e-5 of the result).
+  constexpr bool offset_codes = (KV == PKV_I4 || KV == PKV_I8) && MT == MT_F16;
+  constexpr float code_offset = KV == PKV_I4 ? 8.0f : 128.0f;
   float qsum = 0.f;
   if constexpr (offset_codes) {
     const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
       f16x2 h = __builtin_bit_cast(f16x2, qop[i]);
-      if (i & 1) {
+      const bool hi = KV == PKV_I4 && (i & 1);
+      if (hi) {
         h = h * sixteenth;
         qop[i] = __builtin_bit_cast(uint32_t, h);
       }
       const float t = (float)h[0] + (float)h[1];
-      qsum += (i & 1) ? 16.f * t : t;
+      qsum += hi ? 16.f * t : t;
     }
     qsum += __shfl_xor(qsum, 16, kWave);
     qsum += __shfl_xor(qsum, 32, kWave);
@@ -552,9 +556,9 @@ void decode_partition_kernel(DecodeArgs a) {
   // Constant factors: logits are taken in the exp2 domain.
   float kfac = a.scale * 1.4426950408889634f;
   float vfac = 1.0f;
-  // offset codes: z = (s * 2^24 - 8 qsum) * kfac * (1 / row scale)
+  // offset codes: z = (s * 2^24 - o qsum) * kfac * (1 / row scale)
   const float kf24 = kfac * 16777216.0f;
-  const float kbias = -8.0f * qsum * kfac;
+  const float kbias = -code_offset * qsum * kfac;
   if constexpr (KV == PKV_FP8_E4M3FN) {
     kfac *= a.k_scale[0] * cvt_gain<KV, MT>();
     vfac = a.v_scale[0] * cvt_gain<KV, MT>();
@@ -807,6 +811,11 @@ void decode_partition_kernel(DecodeArgs a) {
                                                               acc[nc], 0, 0, 0);
         }
       }
+      if constexpr (offset_codes) {
+        const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+        acc_p = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb), acc_p,
+                                                      0, 0, 0);
+      }
     }
   };
 
@@ -864,7 +873,8 @@ void decode_partition_kernel(DecodeArgs a) {
   if constexpr (offset_codes) {
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc)
-      acc[nc] = acc[nc] * ((nc & 1) ? 1048576.0f : 16777216.0f) - 8.0f * acc_p[0];
+      acc[nc] = acc[nc] * ((KV == PKV_I4 && (nc & 1)) ? 1048576.0f : 16777216.0f) -
+                code_offset * acc_p[0];
   }
   if (whole_unit) {
     const float inv = vfac / l_tot;
