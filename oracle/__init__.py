@@ -31,10 +31,12 @@ Modules
   quant      INT8 / INT4 per-row and FP8 per-tensor quantizers, nibble packing  [P1] §4, [P3]
   append     expected cache after writing new tokens' rows   [P3]
   layout     stored order of the pools <-> logical [NB][Hkv][bs][d] order
+  multi      several new query tokens per sequence, causal   [P3]
 """
 
-from . import kvsize, widen, paging, attention, quant, append, layout  # noqa: F401
+from . import kvsize, widen, paging, attention, quant, append, layout, multi  # noqa: F401
 from .attention import decode_attention, attend, validate_tables  # noqa: F401
+from .multi import multi_query_attention  # noqa: F401
 from .quant import (quantize_int8_rows, quantize_int4_rows, pack_int4, unpack_int4,  # noqa: F401
                     fp8_tensor_scale, encode_e4m3fn, quantize_fp8)
 from .widen import widen_kv  # noqa: F401

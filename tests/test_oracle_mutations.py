@@ -130,3 +130,14 @@ def test_int4_unsigned_widening_is_caught(monkeypatch):
         return orig(x, fmt, scale)
     monkeypatch.setattr(widen, "widen_kv", bad)
     _fails(TQ.test_int4_widening_divides_by_the_row_scale)
+
+
+def test_causal_off_by_one_is_caught(monkeypatch):
+    from oracle import multi
+    from tests import test_oracle_multi as TM
+    orig = multi.attend
+
+    def bad(q_vec, K, V, scale, return_weights=False):   # sees one row fewer than its position
+        return orig(q_vec, K[:-1] if len(K) > 1 else K, V[:-1] if len(V) > 1 else V, scale)
+    monkeypatch.setattr(multi, "attend", bad)
+    _fails(TM.test_whole_prompt_is_causal_sdpa, 4, 4)
