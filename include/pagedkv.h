@@ -203,6 +203,51 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_multi_workspace_size — bytes of device scratch
+ * paged_attention_multi_query needs for these sizes (never 0 for valid sizes:
+ * the call keeps its row-tile plan there).  Host only.  0 for invalid sizes.
+ */
+size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tokens,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t max_context_len);
+
+/*
+ * paged_attention_multi_query — several new query tokens per sequence at once
+ * (a chunk of a long prompt, or draft tokens to verify), attending through the
+ * block tables ([P3], PagedAttention section: standard attention over the
+ * stitched cache) with a causal mask.  The pages show only one-token decode;
+ * the causal reading: the new tokens' K/V rows are appended first, so
+ * context_lens[b] counts them, and query token j of the L_b new tokens of
+ * sequence b sits at position p = context_lens[b] - L_b + j and attends to
+ * positions 0 .. p.  Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *
+ *   out, q        device, [num_query_tokens][num_q_heads][head_dim] in q_dtype,
+ *                 sequences packed in order, 16-byte aligned; out may not alias q.
+ *   query_start   device int32 [batch + 1]: sequence b's rows are
+ *                 query_start[b] .. query_start[b + 1]; query_start[0] = 0,
+ *                 nondecreasing, query_start[batch] = num_query_tokens
+ *                 (preconditions; rows past num_query_tokens are never touched).
+ *   k_cache ... max_context_len, scale  as for paged_attention_decode; a row with
+ *                 p < 0 (more new tokens than cached ones) gets zeros.
+ *   workspace     device scratch of paged_attention_multi_workspace_size(...) bytes,
+ *                 256-byte aligned; contents overwritten; calls that share it
+ *                 must be ordered.
+ *   Supported: as paged_attention_decode.  L_b = 1 for every b gives exactly
+ *   the decode result.
+ *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype, int32_t batch,
+                                       int32_t num_query_tokens, const int32_t* query_start,
+                                       int32_t num_q_heads, const void* k_cache,
+                                       const void* v_cache, const float* k_scale,
+                                       const float* v_scale, int32_t num_blocks,
+                                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t kv_dtype, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t max_context_len, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * kv_copy_blocks — copy whole physical blocks inside the pools (copy-on-write
  * of a shared block before an append, or compaction): for each pair i,
  * block pairs[2i + 1] of both caches (and, for INT8 / INT4, of both scale arrays)

@@ -15,10 +15,10 @@ import os
 import torch
 
 __all__ = [
-    "kv_quantize", "kv_cache_append", "paged_attention_decode", "kv_copy_blocks",
-    "BlockManager", "paged_attention_workspace_size", "kv_cache_bytes",
-    "library_path", "load_library", "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8",
-    "PKV_FP8_E4M3FN", "EXPORTED_SYMBOLS",
+    "kv_quantize", "kv_cache_append", "paged_attention_decode", "paged_attention_multi_query",
+    "kv_copy_blocks", "BlockManager", "paged_attention_workspace_size",
+    "paged_attention_multi_workspace_size", "kv_cache_bytes", "library_path", "load_library",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8", "PKV_FP8_E4M3FN", "PKV_I4", "EXPORTED_SYMBOLS",
 ]
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN, PKV_I4 = 0, 1, 2, 3, 4, 5
@@ -26,6 +26,7 @@ PKV_F32, PKV_F16, PKV_BF16, PKV_I8, PKV_FP8_E4M3FN, PKV_I4 = 0, 1, 2, 3, 4, 5
 EXPORTED_SYMBOLS = (
     "pkv_last_error", "kv_cache_bytes", "kv_quantize", "kv_cache_append",
     "paged_attention_workspace_size", "paged_attention_decode", "kv_copy_blocks",
+    "paged_attention_multi_workspace_size", "paged_attention_multi_query",
     "pkv_bm_last_error", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
     "pkv_bm_ref_count", "pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
     "pkv_bm_block_tables",
@@ -65,6 +66,12 @@ def load_library():
     lib.paged_attention_decode.restype = I32
     lib.paged_attention_decode.argtypes = [P, P, I32, I32, I32, P, P, P, P, I32, I32, I32, I32,
                                            I32, P, I32, P, I32, F, P, SZ, P]
+    lib.paged_attention_multi_workspace_size.restype = SZ
+    lib.paged_attention_multi_workspace_size.argtypes = [I32] * 6
+    lib.paged_attention_multi_query.restype = I32
+    lib.paged_attention_multi_query.argtypes = [P, P, I32, I32, I32, P, I32, P, P, P, P, I32, I32,
+                                                I32, I32, I32, P, I32, P, I32, ctypes.c_float, P,
+                                                SZ, P]
     lib.kv_copy_blocks.restype = I32
     lib.kv_copy_blocks.argtypes = [P, P, P, P, I32, I32, I32, I32, I32, P, I32, P]
     lib.pkv_bm_last_error.restype = ctypes.c_char_p
@@ -221,6 +228,53 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, kc,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
         float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, lib)
+    return out
+
+
+def paged_attention_multi_workspace_size(batch, num_query_tokens, num_q_heads, num_kv_heads,
+                                         head_dim, max_context_len):
+    """Bytes of workspace paged_attention_multi_query needs."""
+    return int(load_library().paged_attention_multi_workspace_size(
+        batch, num_query_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len))
+
+
+def paged_attention_multi_query(out, q, query_start, k_cache, v_cache, block_tables,
+                                context_lens, scale, max_context_len, k_scale=None, v_scale=None,
+                                kv_dtype=None, workspace=None, stream=None):
+    """Several new query tokens per sequence, causal: ``q``/``out`` are
+    ``[T][Hq][d]`` with sequence ``b``'s rows at ``query_start[b] ..
+    query_start[b+1]`` (device int32 ``[B+1]``); query token ``j`` of the ``L_b``
+    new tokens sits at position ``context_lens[b] - L_b + j`` and attends to
+    positions ``0 .. p``.  A workspace is allocated with torch if none is given."""
+    lib = load_library()
+    for t, n in ((out, "out"), (q, "q"), (query_start, "query_start"), (k_cache, "k_cache"),
+                 (v_cache, "v_cache"), (block_tables, "block_tables"),
+                 (context_lens, "context_lens"), (k_scale, "k_scale"), (v_scale, "v_scale"),
+                 (workspace, "workspace")):
+        _dev(t, n)
+    if (block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32
+            or query_start.dtype != torch.int32):
+        raise TypeError("block_tables, context_lens and query_start must be int32")
+    T, Hq, d = q.shape
+    NB, Hkv, bs, dk = k_cache.shape
+    kc = _kv_code(k_cache, kv_dtype, "k_cache")
+    if kc == PKV_I4:
+        dk *= 2
+    if tuple(out.shape) != (T, Hq, d) or out.dtype != q.dtype or dk != d:
+        raise ValueError("out must match q, and the cache's head_dim must match q's")
+    B = context_lens.numel()
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.numel() != B + 1:
+        raise ValueError("block_tables must be [B][MB], context_lens [B], query_start [B+1]")
+    need = lib.paged_attention_multi_workspace_size(B, T, Hq, Hkv, d, int(max_context_len))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.paged_attention_multi_query(
+        _ptr(out), _ptr(q), _dtype_code(q, "q"), B, T, _ptr(query_start), Hq, _ptr(k_cache),
+        _ptr(v_cache), _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, kc, _ptr(block_tables),
+        block_tables.shape[1], _ptr(context_lens), int(max_context_len), float(scale),
+        _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, lib)
     return out
 

@@ -68,6 +68,20 @@ int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads
   return pkv::max_items_bound(batch, units, max_context_len, pkv::kMaxSlots);
 }
 
+// Several query tokens per sequence: virtual sequences (16-row tiles of
+// (query token, head) rows) can number at most ceil(T G / 16) + batch.
+int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group) {
+  return (num_query_tokens * group + 15) / 16 + batch;
+}
+int64_t multi_items(int64_t vseqs, int64_t num_kv_heads, int64_t max_context_len) {
+  if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
+  return pkv::max_items_bound(vseqs, num_kv_heads, max_context_len, pkv::kMaxSlots);
+}
+int64_t vseq_bytes(int64_t vseqs) { return (3 * vseqs * 4 + 255) / 256 * 256; }
+int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim) {
+  return vseq_bytes(vseqs) + (items > 0 ? seq_bytes(vseqs) + items * row_bytes(head_dim) : 0);
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,6 +272,110 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, cus,
                                        static_cast<hipStream_t>(stream)),
                     "paged_attention_decode");
+}
+
+size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tokens,
+                                            int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, int32_t max_context_len) {
+  if (batch <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads || head_dim <= 0 || max_context_len < 0)
+    return 0;
+  const int64_t v = multi_vseqs(batch, num_query_tokens, num_q_heads / num_kv_heads);
+  return (size_t)multi_workspace(v, multi_items(v, num_kv_heads, max_context_len), head_dim);
+}
+
+pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype, int32_t batch,
+                                       int32_t num_query_tokens, const int32_t* query_start,
+                                       int32_t num_q_heads, const void* k_cache,
+                                       const void* v_cache, const float* k_scale,
+                                       const float* v_scale, int32_t num_blocks,
+                                       int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t kv_dtype, const int32_t* block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                       int32_t max_context_len, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  const char* fn = "paged_attention_multi_query";
+  if (!is_float_dtype(q_dtype)) return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": q_dtype must be F32, F16 or BF16");
+  if (kv_dtype != q_dtype && kv_dtype != PKV_I8 && kv_dtype != PKV_FP8_E4M3FN && kv_dtype != PKV_I4)
+    return fail(PKV_ERR_UNSUPPORTED,
+                std::string(fn) + ": kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
+  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
+    return fail(PKV_ERR_UNSUPPORTED,
+                std::string(fn) + ": INT4 caches need head_dim 128 and F16 or BF16 queries");
+  if (block_size != 16 && block_size != 256)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": block_size must be 16 or 256");
+  if (batch < 0 || num_query_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || num_kv_heads > 65535)
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": need batch, num_query_tokens >= 0 and num_q_heads a multiple of "
+                "num_kv_heads");
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": bad pool or table sizes");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!(scale == scale) || __builtin_isinf(scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": scale must be finite");
+  if (batch == 0 || num_query_tokens == 0) return ok();
+  if (!out || !q || !query_start || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL pointer");
+  if ((pkv::row_scaled(kv_dtype) || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": quantized cache needs k_scale and v_scale");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(query_start, 4) ||
+      (pkv::row_scaled(kv_dtype) && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": misaligned pointer (q, out, caches and row scales need 16 B)");
+  const int32_t G = num_q_heads / num_kv_heads;
+  const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G);
+  const int64_t items = multi_items(vseqs, num_kv_heads, max_context_len);
+  if (vseqs > 0x7FFFFFF0 || items > 0x7FFFFFF0)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": query rows x heads x context too large");
+  const size_t need = (size_t)multi_workspace(vseqs, items, head_dim);
+  if (!workspace || workspace_bytes < need)
+    return fail(PKV_ERR_WORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) +
+                                       " bytes, got " + std::to_string(workspace_bytes));
+  if (!aligned(workspace, 256))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+  const int cus = device_cus();
+  if (cus <= 0) return fail(PKV_ERR_HIP, std::string(fn) + ": cannot query the device");
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  int32_t* vctx = reinterpret_cast<int32_t*>(w);
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = vctx;
+  a.batch = (int32_t)vseqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_tiles = 1;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.ctx_cap = max_context_len;
+  a.max_items = (int32_t)items;
+  a.scale = scale;
+  a.vseq_b = vctx + vseqs;
+  a.vseq_rt = vctx + 2 * vseqs;
+  a.query_start = query_start;
+  a.real_ctx = context_lens;
+  a.q_rows = num_query_tokens;
+  if (items > 0) {
+    uint8_t* rest = w + vseq_bytes(vseqs);
+    a.ws_seq = reinterpret_cast<int64_t*>(rest);
+    a.ws_ml = reinterpret_cast<float*>(rest + seq_bytes(vseqs));
+    a.ws_acc = reinterpret_cast<float*>(rest + seq_bytes(vseqs) + items * 16 * 2 * 4);
+  }
+  return hip_status(pkv::launch_multi(a, batch, vctx, q_dtype, kv_dtype, head_dim, block_size, cus,
+                                      static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 }  // extern "C"

@@ -422,7 +422,12 @@ struct Tuning {
                    : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4 : PKV_SLOTS_PER_CU_DEFAULT);
 };
 
-template <int KV, int QT, int D, int BS>
+// MULTI: several query tokens per sequence (causal).  The planner then works
+// on virtual sequences, one per 16-row tile of a sequence's (query token,
+// head of the group) rows, whose context ends at the tile's last causal limit;
+// a.context_lens holds those lengths and a.vseq_b / a.vseq_rt say which
+// sequence and row tile each is (written by multi_prep_kernel).
+template <int KV, int QT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
@@ -469,11 +474,34 @@ void decode_partition_kernel(DecodeArgs a) {
   }
 
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int h_first = g * G + ht * 16;              // first query head of this tile
-  int nh = G - ht * 16;
-  nh = nh > 16 ? 16 : nh;
-  const bool head_ok = r16 < nh;
-  const int64_t hq = (int64_t)b * a.num_q_heads + h_first + r16;   // this lane's head row
+  bool head_ok;
+  int64_t hq;                 // this lane's row of q and out
+  int prow = 0x7FFFFFFF;      // last cache position this lane's row may see
+  int p_min = 0x7FFFFFFF;     // the smallest such position over the tile's rows
+  int bq = b;                 // the real sequence (block table row)
+  if constexpr (MULTI) {
+    bq = uni(a.vseq_b[b]);
+    const int rt = uni(a.vseq_rt[b]);
+    const int q0 = uni(a.query_start[bq]);
+    const int L = uni(a.query_start[bq + 1]) - q0;
+    int cr = a.real_ctx[bq];
+    cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
+    const int rho = 16 * rt + r16;                   // row = query token * G + head
+    const int j = rho / G;
+    head_ok = rho < L * G && q0 + j < a.q_rows;
+    hq = (int64_t)(q0 + j) * a.num_q_heads + g * G + rho % G;
+    prow = cr - L + j;
+    p_min = cr - L + (16 * rt) / G;
+  } else {
+    const int h_first = g * G + ht * 16;             // first query head of this tile
+    int nh = G - ht * 16;
+    nh = nh > 16 ? 16 : nh;
+    head_ok = r16 < nh;
+    hq = (int64_t)b * a.num_q_heads + h_first + r16;
+  }
+  // Leading tiles of the item that every row sees whole (uniform).
+  const int full_end = p_min < t_end ? p_min + 1 : t_end;   // (no overflow at INT_MAX)
+  const int nfull = full_end > t_begin ? (full_end - t_begin) >> 4 : 0;
 
   // Block-table entries of the item, one per lane per register.
   constexpr int NREG = (kItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
@@ -484,7 +512,7 @@ void decode_partition_kernel(DecodeArgs a) {
   for (int r = 0; r < NREG; ++r) {
     const int idx = r * 64 + lane;
     int v = -1;
-    if (idx < nblk) v = a.block_tables[(int64_t)b * a.max_blocks_per_seq + first_blk + idx];
+    if (idx < nblk) v = a.block_tables[(int64_t)bq * a.max_blocks_per_seq + first_blk + idx];
     blk[r] = (v >= a.num_blocks) ? -1 : v;
   }
 
@@ -699,7 +727,10 @@ void decode_partition_kernel(DecodeArgs a) {
         if constexpr (row_scaled(KV)) f = kfac * krcp[i];
         z[i] = s[i] * f;
       }
-      if constexpr (checked) z[i] = 4 * c16 + i < n_valid ? z[i] : -__builtin_inff();
+      if constexpr (checked) {
+        const bool ok = 4 * c16 + i < n_valid && t_begin + tile * 16 + 4 * c16 + i <= prow;
+        z[i] = ok ? z[i] : -__builtin_inff();
+      }
       mx = fmaxf(mx, z[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -833,15 +864,15 @@ void decode_partition_kernel(DecodeArgs a) {
     ks[i] = vs[i] = 1.f;
     ph[i] = -1;
   }
-  // The steady loop never reaches an item's last tile (the only one that can
-  // be partial), so its tiles take the unchecked path; a table entry outside
-  // the pool skips its tile (a uniform branch with nothing on the other side).
-  // The tail takes the checked path.
+  // The steady loop takes only tiles that every row sees whole and never an
+  // item's last tile (the only one that can be partial), so its tiles take the
+  // unchecked path; a table entry outside the pool skips its tile (a uniform
+  // branch with nothing on the other side).  The tail takes the checked path.
   int tile = 0;
   if (ntiles > 2 * S - 1) {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i], ph[i]);
-    for (; tile + 2 * S - 1 < ntiles; tile += S) {
+    for (; tile + 2 * S - 1 < ntiles && tile + S <= nfull; tile += S) {
 #pragma unroll
       for (int i = 0; i < S; ++i) {
         const int nx = (i + S - 1) % S;
@@ -877,7 +908,8 @@ void decode_partition_kernel(DecodeArgs a) {
                 code_offset * acc_p[0];
   }
   if (whole_unit) {
-    const float inv = vfac / l_tot;
+    // (l_tot = 0 only for a row that sees no token: its output is zeros)
+    const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc)
       store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, acc[nc][0] * inv, acc[nc][1] * inv,
@@ -896,46 +928,30 @@ void decode_partition_kernel(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of a unit's items: out = sum_c 2^(m_c - M) acc_c / sum_c 2^(m_c - M) l_c.
-// One wave per (query head, sequence); the item kernel recorded each
-// sequence's first item and items per unit.  D/4 lanes cover one partial row
-// with 16-byte loads, so one load instruction takes 64/(D/4) items at once; the
-// lane groups are added in a fixed order at the end (results do not depend on
-// timing).  A sequence with no context gets zeros here; a unit that was one
-// item was finished by the item kernel.
+// The item kernel recorded each (virtual) sequence's first item and items per
+// unit.  D/4 lanes cover one partial row with 16-byte loads, so one load
+// instruction takes 64/(D/4) items at once; the lane groups are added in a
+// fixed order at the end (results do not depend on timing).  A unit that was
+// one item was finished by the item kernel.
 // ---------------------------------------------------------------------------
+// One output row from its m partial rows row0 + c * row_step (a row that saw
+// no token in any item, M = -inf, gets zeros).
 template <int QT, int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int64_t row_step,
+                                          int m, int64_t hq, int lane) {
   constexpr int LPP = D / 4;          // lanes per partial row
   constexpr int PPI = kWave / LPP;    // partials per load instruction
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int lane = threadIdx.x;
-  const int64_t hq = (int64_t)b * a.num_q_heads + h;
   const int grp = lane / LPP;         // which partial of an instruction
   const int dq = lane % LPP;          // which 4 output elements
-  if (seq_ctx(a, b) == 0) {
+  float M = -__builtin_inff();
+  for (int c = lane; c < m; c += kWave) M = fmaxf(M, a.ws_ml[2 * (row0 + c * row_step)]);
+  M = wave_max(M);
+  if (M == -__builtin_inff()) {
     if (grp == 0) store_out4<QT>(a.out, hq * D + 4 * dq, 0.f, 0.f, 0.f, 0.f);
     return;
   }
-  if (!a.ws_seq) return;              // no workspace: every unit was one item
-  SeqItems sq{};
-  sq.first = a.ws_seq[2 * b];
-  sq.m = (int)a.ws_seq[2 * b + 1];
-  if (sq.m <= 1) return;
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int g = h / G;
-  const int ht = (h % G) / 16;
-  const int r = (h % G) % 16;
-  // Partial row of chunk c: item (first + (g*m + c)*head_tiles + ht), head r.
-  const int64_t row0 = (sq.first + (int64_t)g * sq.m * a.head_tiles + ht) * 16 + r;
-  const int64_t row_step = (int64_t)a.head_tiles * 16;
-  if (sq.first + ((int64_t)g * sq.m + sq.m - 1) * a.head_tiles + ht >= a.max_items) return;
-
-  float M = -__builtin_inff();
-  for (int c = lane; c < sq.m; c += kWave) M = fmaxf(M, a.ws_ml[2 * (row0 + c * row_step)]);
-  M = wave_max(M);
   float L = 0.f;
-  for (int c = lane; c < sq.m; c += kWave) {
+  for (int c = lane; c < m; c += kWave) {
     const int64_t row = row0 + c * row_step;
     L += __builtin_amdgcn_exp2f(a.ws_ml[2 * row] - M) * a.ws_ml[2 * row + 1];
   }
@@ -943,9 +959,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-  for (int c0 = 0; c0 < sq.m; c0 += PPI) {
+  for (int c0 = 0; c0 < m; c0 += PPI) {
     const int c = c0 + grp;
-    if (c < sq.m) {
+    if (c < m) {
       const int64_t row = row0 + c * row_step;
       const float w = __builtin_amdgcn_exp2f(a.ws_ml[2 * row] - M);
       const f32x4 v = *reinterpret_cast<const f32x4*>(a.ws_acc + row * D + 4 * dq);
@@ -960,6 +976,122 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   if (grp != 0) return;
   const float inv = 1.0f / L;
   store_out4<QT>(a.out, hq * D + 4 * dq, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+}
+
+// Decode: one wave per (query head, sequence).  A sequence with no context
+// gets zeros here.
+template <int QT, int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int64_t hq = (int64_t)b * a.num_q_heads + h;
+  if (seq_ctx(a, b) == 0) {
+    if (lane < D / 4) store_out4<QT>(a.out, hq * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (!a.ws_seq) return;              // no workspace: every unit was one item
+  const int64_t first = a.ws_seq[2 * b];
+  const int m = (int)a.ws_seq[2 * b + 1];
+  if (m <= 1) return;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int g = h / G;
+  const int ht = (h % G) / 16;
+  const int r = (h % G) % 16;
+  // Partial row of chunk c: item (first + (g*m + c)*head_tiles + ht), head r.
+  if (first + ((int64_t)g * m + m - 1) * a.head_tiles + ht >= a.max_items) return;
+  merge_row<QT, D>(a, (first + (int64_t)g * m * a.head_tiles + ht) * 16 + r,
+                   (int64_t)a.head_tiles * 16, m, hq, lane);
+}
+
+// Several query tokens per sequence: one wave per (virtual sequence, KV head),
+// i.e. per 16-row tile of (query token, head) rows; rows of a virtual sequence
+// with no context (rows before the cache) get zeros.
+template <int QT, int D>
+__global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
+  const int v = blockIdx.x;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int bq = a.vseq_b[v];
+  const int rt = a.vseq_rt[v];
+  const int q0 = a.query_start[bq];
+  const int L = a.query_start[bq + 1] - q0;
+  int rows = L * G - 16 * rt;
+  rows = rows > 16 ? 16 : rows;
+  // rows past the query tensor (inconsistent query_start) are never written
+  const int rows_q = (a.q_rows - q0) * G - 16 * rt;
+  rows = rows < rows_q ? rows : rows_q;
+  if (rows <= 0) return;              // a padding entry
+  auto out_row = [&](int r) -> int64_t {
+    const int rho = 16 * rt + r;
+    return (int64_t)(q0 + rho / G) * a.num_q_heads + g * G + rho % G;
+  };
+  if (seq_ctx(a, v) == 0) {
+    for (int r = 0; r < rows; ++r)
+      if (lane < D / 4) store_out4<QT>(a.out, out_row(r) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
+    return;
+  }
+  if (!a.ws_seq) return;
+  const int64_t first = a.ws_seq[2 * v];
+  const int m = (int)a.ws_seq[2 * v + 1];
+  if (m <= 1) return;
+  // head_tiles is 1: chunk c of KV head g is item first + g*m + c.
+  if (first + (int64_t)g * m + m - 1 >= a.max_items) return;
+  for (int r = 0; r < rows; ++r)
+    merge_row<QT, D>(a, (first + (int64_t)g * m) * 16 + r, 16, m, out_row(r), lane);
+}
+
+// Virtual sequences of a multi-token call (one workgroup): sequence b's
+// ceil(L_b G / 16) row tiles, in order, each with the context its last row may
+// see; entries past the last are padding with no context.
+__global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batch_real,
+                                                          int32_t* vctx) {
+  __shared__ int scan[1024];
+  __shared__ int carry;
+  const int t = threadIdx.x;
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < batch_real; b0 += 1024) {
+    const int b = b0 + t;
+    int L = 0, ctx = 0;
+    if (b < batch_real) {
+      L = a.query_start[b + 1] - a.query_start[b];
+      L = L < 0 ? 0 : L;
+      ctx = a.real_ctx[b];
+      ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+    }
+    const int n = (L * G + 15) / 16;
+    scan[t] = n;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+      const int x = t >= o ? scan[t - o] : 0;
+      __syncthreads();
+      scan[t] += x;
+      __syncthreads();
+    }
+    const int base = carry + scan[t] - n;
+    for (int rt = 0; rt < n; ++rt) {
+      const int v = base + rt;
+      if (v < a.batch) {
+        int last = 16 * rt + 15;
+        last = last < L * G - 1 ? last : L * G - 1;
+        int c = ctx - L + last / G + 1;
+        vctx[v] = c < 0 ? 0 : c;
+        a.vseq_b[v] = b;
+        a.vseq_rt[v] = rt;
+      }
+    }
+    __syncthreads();
+    if (t == 1023) carry += scan[1023];
+    __syncthreads();
+  }
+  for (int v = carry + t; v < a.batch; v += 1024) {
+    vctx[v] = 0;
+    a.vseq_b[v] = 0;
+    a.vseq_rt[v] = 0x07FFFFFF;   // no rows (16 * rt stays below 2^31)
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -978,9 +1110,15 @@ static int slots_per_cu_override() {
   return v;
 }
 
-template <int KV, int QT, int D, int BS>
-static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
-  auto* kern = decode_partition_kernel<KV, QT, D, BS>;
+// Extra arguments of a multi-query call.
+struct MultiLaunch {
+  int batch_real;
+  int32_t* vctx;
+};
+
+template <int KV, int QT, int D, int BS, bool MULTI>
+static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hipStream_t st) {
+  auto* kern = decode_partition_kernel<KV, QT, D, BS, MULTI>;
   // Resident waves per CU of this instance: a property of the compiled code,
   // queried once (every device the library runs on is gfx950).
   static std::atomic<int> occupancy{0};
@@ -1003,47 +1141,73 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, hipStream_t st) {
   const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
   const int64_t grid = (need + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if constexpr (MULTI) {
+    hipLaunchKernelGGL(multi_prep_kernel, dim3(1), dim3(1024), 0, st, a, ml.batch_real, ml.vctx);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0, st,
-                     a);
+  if constexpr (MULTI)
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, a.num_kv_heads), dim3(64), 0,
+                       st, a);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
+                       st, a);
   return hipGetLastError();
 }
 
-template <int KV, int QT, int D>
-static hipError_t launch3(DecodeArgs& a, int bs, int cus, hipStream_t st) {
-  return bs == 16 ? launch4<KV, QT, D, 16>(a, cus, st) : launch4<KV, QT, D, 256>(a, cus, st);
+template <int KV, int QT, int D, bool MULTI>
+static hipError_t launch3(DecodeArgs& a, int bs, int cus, const MultiLaunch& ml, hipStream_t st) {
+  return bs == 16 ? launch4<KV, QT, D, 16, MULTI>(a, cus, ml, st)
+                  : launch4<KV, QT, D, 256, MULTI>(a, cus, ml, st);
 }
 
-template <int KV, int QT>
-static hipError_t launch2(DecodeArgs& a, int d, int bs, int cus, hipStream_t st) {
-  return d == 64 ? launch3<KV, QT, 64>(a, bs, cus, st) : launch3<KV, QT, 128>(a, bs, cus, st);
+template <int KV, int QT, bool MULTI>
+static hipError_t launch2(DecodeArgs& a, int d, int bs, int cus, const MultiLaunch& ml,
+                          hipStream_t st) {
+  return d == 64 ? launch3<KV, QT, 64, MULTI>(a, bs, cus, ml, st)
+                 : launch3<KV, QT, 128, MULTI>(a, bs, cus, ml, st);
 }
 
-template <int QT>
-static hipError_t launch1(DecodeArgs& a, int kv, int d, int bs, int cus, hipStream_t st) {
+template <int QT, bool MULTI>
+static hipError_t launch1(DecodeArgs& a, int kv, int d, int bs, int cus, const MultiLaunch& ml,
+                          hipStream_t st) {
   switch (kv) {
-    case PKV_I8: return launch2<PKV_I8, QT>(a, d, bs, cus, st);
-    case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT>(a, d, bs, cus, st);
+    case PKV_I8: return launch2<PKV_I8, QT, MULTI>(a, d, bs, cus, ml, st);
+    case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT, MULTI>(a, d, bs, cus, ml, st);
     case PKV_I4:
       if constexpr (QT == PKV_F32) {
         return hipErrorInvalidValue;   // rejected by the entry point
       } else {
         if (d != 128) return hipErrorInvalidValue;
-        return launch3<PKV_I4, QT, 128>(a, bs, cus, st);
+        return launch3<PKV_I4, QT, 128, MULTI>(a, bs, cus, ml, st);
       }
-    default: return launch2<QT, QT>(a, d, bs, cus, st);
+    default: return launch2<QT, QT, MULTI>(a, d, bs, cus, ml, st);
+  }
+}
+
+template <bool MULTI>
+static hipError_t launch0(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
+                          int num_cus, const MultiLaunch& ml, hipStream_t st) {
+  switch (q_dtype) {
+    case PKV_F32: return launch1<PKV_F32, MULTI>(a, kv_dtype, head_dim, block_size, num_cus, ml, st);
+    case PKV_F16: return launch1<PKV_F16, MULTI>(a, kv_dtype, head_dim, block_size, num_cus, ml, st);
+    default: return launch1<PKV_BF16, MULTI>(a, kv_dtype, head_dim, block_size, num_cus, ml, st);
   }
 }
 
 hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
                          int num_cus, hipStream_t st) {
-  switch (q_dtype) {
-    case PKV_F32: return launch1<PKV_F32>(a, kv_dtype, head_dim, block_size, num_cus, st);
-    case PKV_F16: return launch1<PKV_F16>(a, kv_dtype, head_dim, block_size, num_cus, st);
-    default: return launch1<PKV_BF16>(a, kv_dtype, head_dim, block_size, num_cus, st);
-  }
+  return launch0<false>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus, MultiLaunch{0, nullptr},
+                        st);
+}
+
+hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
+                        int head_dim, int block_size, int num_cus, hipStream_t st) {
+  return launch0<true>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus,
+                       MultiLaunch{batch_real, vctx}, st);
 }
 
 }  // namespace pkv

@@ -42,6 +42,13 @@ struct DecodeArgs {
   int32_t slots;               // items planned per round (waves resident at once)
   int32_t max_items;           // capacity of the workspace, in items
   float scale;
+  // Several query tokens per sequence (multi-query calls only; batch is then
+  // the number of virtual sequences and context_lens their lengths).
+  int32_t* vseq_b;             // real sequence of each virtual sequence
+  int32_t* vseq_rt;            // its 16-row tile of (query token, head) rows
+  const int32_t* query_start;  // [real batch + 1]: first query row of each sequence
+  const int32_t* real_ctx;     // context_lens of the real sequences
+  int32_t q_rows;              // query rows (tokens) in q and out
 };
 
 // Host-side bound on the items a plan can make (grid size and workspace rows).
@@ -59,7 +66,10 @@ inline int64_t max_items_bound(int64_t batch, int64_t units_per_seq, int64_t max
 hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
                          int num_cus, hipStream_t st);
 
-int decode_waves_per_cu(int q_dtype, int kv_dtype, int head_dim, int block_size);
+// Multi-query: a.batch = virtual sequences (upper bound), a.context_lens =
+// vctx (written by the prep kernel first), batch_real real sequences.
+hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
+                        int head_dim, int block_size, int num_cus, hipStream_t st);
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
                            void* out, float* scale, int scale_given, hipStream_t st);
