@@ -248,7 +248,101 @@ def bench_blocks(args):
           flush=True)
 
 
+def bench_multi(args, name):
+    """Multi-token query row: one step appends the new tokens' K/V rows (every
+    sequence's L new tokens, written to their slots) and runs
+    paged_attention_multi_query over the batch.  Prints one JSON line with query
+    tokens/s and the attention kernel against its roofline: HBM (K+V bytes of
+    every context token of every KV head, once) for draft verification, MFMA
+    (fp16 dense, 2.5 PFLOP/s; 4 d flops per (row, visible token)) for a prompt
+    chunk."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_435_amd as pkv
+    from paged_kv_cache_435_amd import workloads as W
+    from paged_kv_cache_435_amd.device_cache import DeviceCase
+
+    dev = torch.device("cuda:0")
+    w, q_lens = W.make_multi(name)
+    T = int(q_lens.sum())
+    case = DeviceCase(w, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(41)
+    q = torch.randn(T, w.num_q_heads, w.head_dim, generator=g, device=dev).to(w.q_dtype)
+    out = torch.empty_like(q)
+    starts = torch.from_numpy(np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)).to(dev)
+    new_k = torch.randn(T, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(w.q_dtype)
+    new_v = torch.randn(T, w.num_kv_heads, w.head_dim, generator=g, device=dev).to(w.q_dtype)
+    slots = []
+    for b in range(w.batch):
+        for p in range(int(w.context_lens[b] - q_lens[b]), int(w.context_lens[b])):
+            slots.append(int(w.block_tables[b, p // w.block_size]) * w.block_size + p % w.block_size)
+    slots = torch.tensor(slots, dtype=torch.int64, device=dev)
+    mcl = w.max_context_len
+    ws = torch.empty(pkv.paged_attention_multi_workspace_size(w.batch, T, w.num_q_heads,
+                                                              w.num_kv_heads, w.head_dim, mcl),
+                     dtype=torch.uint8, device=dev)
+    log(f"[bench] multi {name}: B={w.batch} T={T} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"sum(ctx)={int(w.context_lens.sum())} workspace {ws.numel()} B")
+
+    def step(events=None):
+        pkv.kv_cache_append(new_k, new_v, slots, case.k_cache, case.v_cache)
+        if events is not None:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+        pkv.paged_attention_multi_query(out, q, starts, case.k_cache, case.v_cache,
+                                        case.block_tables, case.context_lens, w.scale, mcl,
+                                        workspace=ws)
+        if events is not None:
+            e1.record()
+            events.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_attn = float(np.mean(kernel_launch_times(events)))
+    kv_bytes = w.kv_bytes_per_layer()
+    visible = 0                                 # (row, visible token) pairs per KV head group
+    for b in range(w.batch):
+        L, c = int(q_lens[b]), int(w.context_lens[b])
+        visible += sum(c - L + j + 1 for j in range(L))
+    flops = 4 * w.head_dim * w.num_q_heads * visible
+    if name == "llama70b_verify4":
+        roof = {"bound": "hbm", "achieved": kv_bytes / t_attn / 1e9, "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "bytes_per_launch": kv_bytes}
+    else:
+        roof = {"bound": "mfma", "achieved": flops / t_attn / 1e12, "peak": 2500.0,
+                "unit": "TFLOP/s", "flops_per_launch": flops}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof.update({"kernel": "paged_attention_multi_query", "avg_launch_us": t_attn * 1e6,
+                 "traffic": None})
+    log(f"[bench] attention launch avg {t_attn * 1e6:.1f} us, "
+        f"{roof['achieved']:.1f} {roof['unit']} ({roof['frac'] * 100:.1f} % of peak)")
+    print(json.dumps({
+        "metric": "multi-token query attention: query tokens/s, 1 GPU", "value": T * args.steps / elapsed,
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": w.batch, "query_tokens": T,
+                   "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "block_size": w.block_size,
+                   "sum_context_tokens": int(w.context_lens.sum())},
+        "roofline": roof}), flush=True)
+
+
 def main():
+    if len(sys.argv) > 2 and sys.argv[1] == "--multi":
+        name = sys.argv[2]
+        del sys.argv[1:3]
+        bench_multi(parse(), name)
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--blocks":
         sys.argv.pop(1)
         bench_blocks(parse())

@@ -163,6 +163,33 @@ NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70
          "llama13b_int4", "llama70b_int4")
 
 
+# Several new query tokens per sequence (paged_attention_multi_query): each
+# returns the workload (contexts count the new tokens) and the new tokens per
+# sequence.
+#   llama70b_verify4    the llama70b_gqa8 batch with 4 draft tokens per sequence
+#                       to verify
+#   llama70b_prefill512 8 sequences of the 70B GQA-8 shape, cached prefixes
+#                       U[0, 4096] (seed 0) and a 512-token prompt chunk each
+MULTI_NAMES = ("llama70b_verify4", "llama70b_prefill512")
+
+
+def make_multi(name):
+    if name == "llama70b_verify4":
+        w = make("llama70b_gqa8")
+        w.name, w.appends = name, False
+        return w, np.full(w.batch, 4, dtype=np.int64)
+    if name == "llama70b_prefill512":
+        prefix = np.random.default_rng(0).integers(0, 4096, 8, endpoint=True)
+        ctx = (prefix + 512).astype(np.int32)
+        bs = 16
+        nb = pool_for(ctx, bs)
+        w = Workload(name, torch.float16, "f16", 8, 64, 8, 128, bs, 1, ctx, nb,
+                     deal_blocks(ctx, bs, nb), appends=False,
+                     seeds=dict(context=0, permutation=1, q=2, k=3, v=4, new=6))
+        return w, np.full(8, 512, dtype=np.int64)
+    raise KeyError(name)
+
+
 def custom(q_dtype, kv_format, context_lens, num_q_heads, num_kv_heads, head_dim, block_size,
            pool_factor=1.25, extra_blocks=0, perm_seed=1, appends=False, name="custom"):
     """A workload of any shape, dealt the same way (for edge-case tests)."""
