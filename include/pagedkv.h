@@ -331,6 +331,64 @@ pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
 pkv_status pkv_bm_block_tables(pkv_block_manager* bm, const int64_t* seq_ids, int32_t n_seqs,
                                int32_t max_blocks, int32_t* tables, int32_t* context_lens);
 
+/*
+ * Swap space ([P3], vLLM configuration: swap_space moves inactive KV cache to
+ * CPU memory, so more requests fit than HBM holds).
+ *
+ * pkv_bm_enable_swap gives the manager a host pool of num_host_blocks blocks
+ * (numbered 0 ..; the caller allocates the host pools, pinned, with the device
+ * pools' block layout).  Once per manager.
+ *
+ * pkv_bm_swap_out moves seq_id to the host pool: each of its n blocks gets a
+ * host block, its device references are dropped (blocks left unreferenced are
+ * free at once), and (device block, host block) pairs go to host
+ * pairs[0 .. 2n) with *n_pairs = n.  The sequence cannot be appended to,
+ * forked or listed in block tables until swapped in; pkv_bm_free still ends
+ * it.  The caller copies the pairs with kv_swap_blocks before any later kernel
+ * writes a device block handed out again (same stream, or an event).
+ *
+ * pkv_bm_swap_in brings it back into fresh device blocks: (host block, device
+ * block) pairs as above; the host blocks are free again at once, so enqueue
+ * these copies before any later swap-out's copies (one stream keeps the order).
+ * Blocks swapped in are private to the sequence (not prefix-cache entries).
+ *
+ * Both fail without changing anything (PKV_ERR_INVALID_ARG) when the other
+ * pool runs out, pairs is too small (max_pairs pairs), the sequence is
+ * unknown or already in the requested place.
+ */
+pkv_status pkv_bm_enable_swap(pkv_block_manager* bm, int32_t num_host_blocks);
+int32_t pkv_bm_num_free_host(pkv_block_manager* bm);
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs,
+                           int32_t max_pairs, int32_t* n_pairs);
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs,
+                          int32_t max_pairs, int32_t* n_pairs);
+
+/*
+ * kv_swap_blocks — copy whole blocks between two pools of the same layout,
+ * device <-> pinned host (swap out / swap in) or device <-> device: for each
+ * pair i, block pairs[2i + 1] of the destination pools becomes a byte-for-byte
+ * copy of block pairs[2i] of the source pools (K, V and, for PKV_I8 / PKV_I4,
+ * the row scales; FP8's tensor scale is shared by both pools).
+ *
+ *   src_*, dst_*  device memory or host memory from hipHostMalloc (pinned); the
+ *                 pools are [num_blocks][num_kv_heads][block_size][head_dim] in
+ *                 kv_dtype (INT4: head_dim / 2 bytes a row), scales
+ *                 [num_blocks][num_kv_heads][block_size] float32.
+ *   pairs         HOST int32 [n_pairs][2] (src block, dst block), each index
+ *                 inside its pool (checked before anything is enqueued).
+ *   stream        the copies are DMA transfers enqueued on it (typically a side
+ *                 stream, so they overlap decode kernels without taking compute
+ *                 units); runs of consecutive blocks go as one transfer.
+ *   Errors: PKV_ERR_INVALID_ARG (NULL pointers, bad sizes or pairs, pageable
+ *           host memory), PKV_ERR_UNSUPPORTED (unknown dtype), PKV_ERR_HIP.
+ */
+pkv_status kv_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                          const float* src_v_scale, int32_t src_num_blocks, void* dst_k,
+                          void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                          int32_t dst_num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t kv_dtype, const int32_t* pairs,
+                          int32_t n_pairs, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

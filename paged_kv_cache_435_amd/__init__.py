@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "kv_quantize", "kv_cache_append", "paged_attention_decode", "paged_attention_multi_query",
-    "kv_copy_blocks", "BlockManager", "paged_attention_workspace_size",
+    "kv_copy_blocks", "kv_swap_blocks", "BlockManager", "paged_attention_workspace_size",
     "paged_attention_multi_workspace_size", "kv_cache_bytes", "library_path", "load_library",
     "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8", "PKV_FP8_E4M3FN", "PKV_I4", "EXPORTED_SYMBOLS",
 ]
@@ -29,7 +29,8 @@ EXPORTED_SYMBOLS = (
     "paged_attention_multi_workspace_size", "paged_attention_multi_query",
     "pkv_bm_last_error", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
     "pkv_bm_ref_count", "pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
-    "pkv_bm_block_tables",
+    "pkv_bm_block_tables", "pkv_bm_enable_swap", "pkv_bm_num_free_host", "pkv_bm_swap_out",
+    "pkv_bm_swap_in", "kv_swap_blocks",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -94,6 +95,16 @@ def load_library():
     lib.pkv_bm_free.argtypes = [P, I64]
     lib.pkv_bm_block_tables.restype = I32
     lib.pkv_bm_block_tables.argtypes = [P, P, I32, I32, P, P]
+    lib.pkv_bm_enable_swap.restype = I32
+    lib.pkv_bm_enable_swap.argtypes = [P, I32]
+    lib.pkv_bm_num_free_host.restype = I32
+    lib.pkv_bm_num_free_host.argtypes = [P]
+    lib.pkv_bm_swap_out.restype = I32
+    lib.pkv_bm_swap_out.argtypes = [P, I64, P, I32, P]
+    lib.pkv_bm_swap_in.restype = I32
+    lib.pkv_bm_swap_in.argtypes = [P, I64, P, I32, P]
+    lib.kv_swap_blocks.restype = I32
+    lib.kv_swap_blocks.argtypes = [P, P, P, P, I32, P, P, P, P, I32, I32, I32, I32, I32, P, I32, P]
     _LIB = lib
     return lib
 
@@ -299,6 +310,42 @@ def kv_copy_blocks(k_cache, v_cache, pairs, k_scale=None, v_scale=None, kv_dtype
     _check(st, lib)
 
 
+def _pool(t, what):
+    """A swap pool: device tensor or pinned host tensor, contiguous."""
+    if t is None:
+        return
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError(f"{what} must be a device tensor or pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def kv_swap_blocks(src_k, src_v, dst_k, dst_v, pairs, src_k_scale=None, src_v_scale=None,
+                   dst_k_scale=None, dst_v_scale=None, kv_dtype=None, stream=None):
+    """Copy whole blocks between pools of the same layout (device <-> pinned host):
+    for each row (src, dst) of the host int32 ``pairs`` ``[n][2]`` (numpy or CPU
+    tensor), block dst of the destination pools becomes block src of the source
+    pools (row scales too for INT8 / INT4).  DMA transfers on ``stream``."""
+    import numpy as np
+    lib = load_library()
+    for t, n in ((src_k, "src_k"), (src_v, "src_v"), (dst_k, "dst_k"), (dst_v, "dst_v"),
+                 (src_k_scale, "src_k_scale"), (src_v_scale, "src_v_scale"),
+                 (dst_k_scale, "dst_k_scale"), (dst_v_scale, "dst_v_scale")):
+        _pool(t, n)
+    p = np.ascontiguousarray(pairs.numpy() if isinstance(pairs, torch.Tensor) else pairs,
+                             dtype=np.int32).reshape(-1, 2)
+    NBs, Hkv, bs, dc = src_k.shape
+    kc = _kv_code(src_k, kv_dtype, "src_k")
+    d = 2 * dc if kc == PKV_I4 else dc
+    if tuple(dst_k.shape[1:]) != (Hkv, bs, dc) or dst_k.dtype != src_k.dtype:
+        raise ValueError("source and destination pools must share the block layout")
+    st = lib.kv_swap_blocks(_ptr(src_k), _ptr(src_v), _ptr(src_k_scale), _ptr(src_v_scale), NBs,
+                            _ptr(dst_k), _ptr(dst_v), _ptr(dst_k_scale), _ptr(dst_v_scale),
+                            dst_k.shape[0], bs, Hkv, d, kc, p.ctypes.data_as(ctypes.c_void_p),
+                            len(p), _stream(stream))
+    _check(st, lib)
+
+
 class BlockManager:
     """Host-side block allocation with reference-counted sharing, copy-on-write
     and optional prefix caching (the C block manager of libpagedkv)."""
@@ -364,6 +411,29 @@ class BlockManager:
 
     def free(self, seq_id):
         self._ok(self._lib.pkv_bm_free(self._h, int(seq_id)))
+
+    def enable_swap(self, num_host_blocks):
+        """Give the manager a host pool of ``num_host_blocks`` blocks."""
+        self._ok(self._lib.pkv_bm_enable_swap(self._h, int(num_host_blocks)))
+
+    @property
+    def num_free_host(self):
+        return int(self._lib.pkv_bm_num_free_host(self._h))
+
+    def _swap(self, fn, seq_id, max_pairs):
+        pairs = self._np.empty((max(int(max_pairs), 1), 2), dtype=self._np.int32)
+        n = ctypes.c_int32(0)
+        self._ok(fn(self._h, int(seq_id), pairs.ctypes.data_as(ctypes.c_void_p), len(pairs),
+                    ctypes.byref(n)))
+        return pairs[:n.value].copy()
+
+    def swap_out(self, seq_id, max_pairs=1 << 16):
+        """(device block, host block) pairs to copy out; the sequence is swapped."""
+        return self._swap(self._lib.pkv_bm_swap_out, seq_id, max_pairs)
+
+    def swap_in(self, seq_id, max_pairs=1 << 16):
+        """(host block, device block) pairs to copy in; the sequence is live again."""
+        return self._swap(self._lib.pkv_bm_swap_in, seq_id, max_pairs)
 
     def block_tables(self, seq_ids, max_blocks):
         """(tables int32 [n][max_blocks], context_lens int32 [n]) as numpy."""

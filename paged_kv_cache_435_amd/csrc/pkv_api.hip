@@ -378,4 +378,66 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
                     fn);
 }
 
+pkv_status kv_swap_blocks(const void* src_k, const void* src_v, const float* src_k_scale,
+                          const float* src_v_scale, int32_t src_num_blocks, void* dst_k,
+                          void* dst_v, float* dst_k_scale, float* dst_v_scale,
+                          int32_t dst_num_blocks, int32_t block_size, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t kv_dtype, const int32_t* pairs,
+                          int32_t n_pairs, void* stream) {
+  const char* fn = "kv_swap_blocks";
+  if (kv_dtype < PKV_F32 || kv_dtype > PKV_I4)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": unknown kv_dtype");
+  if (src_num_blocks < 1 || dst_num_blocks < 1 || block_size < 1 || num_kv_heads < 1 ||
+      head_dim < 1 || n_pairs < 0 || (kv_dtype == PKV_I4 && head_dim % 2))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": bad sizes");
+  if (n_pairs == 0) return ok();
+  if (!src_k || !src_v || !dst_k || !dst_v || !pairs)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL pointer");
+  const bool scaled = pkv::row_scaled(kv_dtype);
+  if (scaled && (!src_k_scale || !src_v_scale || !dst_k_scale || !dst_v_scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": INT8 / INT4 pools need their row scales");
+  for (int32_t i = 0; i < n_pairs; ++i)
+    if (pairs[2 * i] < 0 || pairs[2 * i] >= src_num_blocks || pairs[2 * i + 1] < 0 ||
+        pairs[2 * i + 1] >= dst_num_blocks)
+      return fail(PKV_ERR_INVALID_ARG,
+                  std::string(fn) + ": pair " + std::to_string(i) + " is outside its pool");
+  // Every pool must be device memory or pinned host memory (a DMA engine
+  // cannot read pageable memory asynchronously).
+  const void* pools[8] = {src_k, src_v, dst_k, dst_v,
+                          src_k_scale, src_v_scale, dst_k_scale, dst_v_scale};
+  for (int i = 0; i < (scaled ? 8 : 4); ++i) {
+    hipPointerAttribute_t at;
+    if (hipPointerGetAttributes(&at, pools[i]) != hipSuccess ||
+        (at.type != hipMemoryTypeDevice && at.type != hipMemoryTypeHost)) {
+      (void)hipGetLastError();   // the query's error is not the caller's
+      return fail(PKV_ERR_INVALID_ARG,
+                  std::string(fn) + ": pools must be device memory or pinned host memory");
+    }
+  }
+  const int64_t block_rows = (int64_t)num_kv_heads * block_size;
+  const int64_t block_bytes = block_rows * pkv::row_bytes_of(kv_dtype, head_dim);
+  const int64_t scale_bytes = block_rows * 4;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  auto copy = [&](const void* s, void* d, int64_t per, int32_t sb, int32_t db, int32_t n) {
+    return hipMemcpyAsync(static_cast<uint8_t*>(d) + (int64_t)db * per,
+                          static_cast<const uint8_t*>(s) + (int64_t)sb * per, (size_t)(n * per),
+                          hipMemcpyDefault, st);
+  };
+  for (int32_t i = 0; i < n_pairs;) {
+    // a run of pairs whose source and destination blocks both step by one
+    int32_t n = 1;
+    while (i + n < n_pairs && pairs[2 * (i + n)] == pairs[2 * i] + n &&
+           pairs[2 * (i + n) + 1] == pairs[2 * i + 1] + n)
+      ++n;
+    const int32_t sb = pairs[2 * i], db = pairs[2 * i + 1];
+    hipError_t e = copy(src_k, dst_k, block_bytes, sb, db, n);
+    if (e == hipSuccess) e = copy(src_v, dst_v, block_bytes, sb, db, n);
+    if (e == hipSuccess && scaled) e = copy(src_k_scale, dst_k_scale, scale_bytes, sb, db, n);
+    if (e == hipSuccess && scaled) e = copy(src_v_scale, dst_v_scale, scale_bytes, sb, db, n);
+    if (e != hipSuccess) return hip_status(e, fn);
+    i += n;
+  }
+  return ok();
+}
+
 }  // extern "C"

@@ -16,6 +16,12 @@
 // every token from the start of the sequence through the block's end.  Cached
 // blocks nobody references stay reusable until a fresh block is needed and the
 // free list is empty; then the least recently released one is taken.
+//
+// Swap space ([P3], vLLM configuration: swap_space moves inactive KV cache to
+// CPU memory so more requests fit than HBM holds): with a host pool enabled, a
+// sequence can be swapped out (each of its blocks gets a host block, its device
+// references are dropped) and swapped back in (fresh device blocks).  The
+// manager returns the block pairs to copy; kv_swap_blocks moves the bytes.
 #include <stdint.h>
 #include <string.h>
 
@@ -47,7 +53,8 @@ uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int n) {
 }
 
 struct Sequence {
-  std::vector<int32_t> blocks;   // physical block of each logical block
+  std::vector<int32_t> blocks;   // physical block of each logical block (host block when swapped)
+  bool swapped = false;
   int64_t tokens = 0;            // tokens held
   uint64_t last_full_key = kNoHash;   // key of the last full block (chain)
   std::vector<int32_t> pending;  // token ids of the partly filled last block
@@ -67,6 +74,8 @@ struct pkv_block_manager {
   std::vector<bool> in_evictable;
   std::unordered_map<uint64_t, int32_t> cache;   // key -> block
   std::unordered_map<int64_t, Sequence> seqs;
+  int32_t num_host_blocks = 0;                 // swap space (0: none)
+  std::vector<int32_t> host_free;
   std::mutex mu;
 };
 
@@ -237,6 +246,7 @@ pkv_status pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, const int32_t* t
   auto it = bm->seqs.find(seq_id);
   if (it == bm->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_append: unknown sequence");
   Sequence& s = it->second;
+  if (s.swapped) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_append: sequence is swapped out");
   const int bs = bm->block_size;
   const bool cow = s.tokens % bs != 0 && bm->ref[s.blocks.back()] > 1;
   const int64_t room = s.tokens % bs == 0 ? 0 : bs - s.tokens % bs;
@@ -269,6 +279,7 @@ pkv_status pkv_bm_fork(pkv_block_manager* bm, int64_t parent, int64_t child) {
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_fork: unknown parent");
   if (bm->seqs.count(child)) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_fork: child id in use");
+  if (it->second.swapped) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_fork: parent is swapped out");
   Sequence c = it->second;   // same blocks, same tokens
   for (int32_t b : c.blocks) take_ref(bm, b);
   bm->seqs.emplace(child, std::move(c));
@@ -282,7 +293,11 @@ pkv_status pkv_bm_free(pkv_block_manager* bm, int64_t seq_id) {
   if (it == bm->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_free: unknown sequence");
   // Release from the last block back, so the oldest-released cached blocks are
   // the deepest ones of a prefix (evicted first).
-  for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) drop_ref(bm, *b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.blocks) bm->host_free.push_back(h);
+  } else {
+    for (auto b = it->second.blocks.rbegin(); b != it->second.blocks.rend(); ++b) drop_ref(bm, *b);
+  }
   bm->seqs.erase(it);
   return PKV_OK;
 }
@@ -296,6 +311,8 @@ pkv_status pkv_bm_block_tables(pkv_block_manager* bm, const int64_t* seq_ids, in
     auto it = bm->seqs.find(seq_ids[i]);
     if (it == bm->seqs.end())
       return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_block_tables: unknown sequence");
+    if (it->second.swapped)
+      return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_block_tables: sequence is swapped out");
     if ((int64_t)it->second.blocks.size() > max_blocks)
       return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_block_tables: max_blocks too small");
   }
@@ -306,6 +323,76 @@ pkv_status pkv_bm_block_tables(pkv_block_manager* bm, const int64_t* seq_ids, in
       row[j] = j < (int32_t)s.blocks.size() ? s.blocks[j] : -1;
     context_lens[i] = (int32_t)s.tokens;
   }
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_enable_swap(pkv_block_manager* bm, int32_t num_host_blocks) {
+  if (!bm || num_host_blocks < 1)
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_enable_swap: need a manager and >= 1 host block");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  if (bm->num_host_blocks > 0)
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_enable_swap: swap space already set");
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_free.reserve(num_host_blocks);
+  for (int32_t h = num_host_blocks - 1; h >= 0; --h) bm->host_free.push_back(h);   // 0 first
+  return PKV_OK;
+}
+
+int32_t pkv_bm_num_free_host(pkv_block_manager* bm) {
+  if (!bm) return -1;
+  std::lock_guard<std::mutex> lock(bm->mu);
+  return (int32_t)bm->host_free.size();
+}
+
+pkv_status pkv_bm_swap_out(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs,
+                           int32_t max_pairs, int32_t* n_pairs) {
+  if (!bm || !n_pairs) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_out: NULL argument");
+  *n_pairs = 0;
+  std::lock_guard<std::mutex> lock(bm->mu);
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_out: unknown sequence");
+  Sequence& s = it->second;
+  if (s.swapped) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_out: already swapped out");
+  const int32_t n = (int32_t)s.blocks.size();
+  if (n > 0 && (!pairs || max_pairs < n))
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_out: pairs holds fewer than the sequence's blocks");
+  if (n > (int32_t)bm->host_free.size())
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_out: out of host blocks");
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t h = bm->host_free.back();
+    bm->host_free.pop_back();
+    pairs[2 * j] = s.blocks[j];
+    pairs[2 * j + 1] = h;
+  }
+  for (int32_t j = n - 1; j >= 0; --j) drop_ref(bm, s.blocks[j]);
+  for (int32_t j = 0; j < n; ++j) s.blocks[j] = pairs[2 * j + 1];
+  s.swapped = true;
+  *n_pairs = n;
+  return PKV_OK;
+}
+
+pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs,
+                          int32_t max_pairs, int32_t* n_pairs) {
+  if (!bm || !n_pairs) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_in: NULL argument");
+  *n_pairs = 0;
+  std::lock_guard<std::mutex> lock(bm->mu);
+  auto it = bm->seqs.find(seq_id);
+  if (it == bm->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_in: unknown sequence");
+  Sequence& s = it->second;
+  if (!s.swapped) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_in: not swapped out");
+  const int32_t n = (int32_t)s.blocks.size();
+  if (n > 0 && (!pairs || max_pairs < n))
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_in: pairs holds fewer than the sequence's blocks");
+  if (n > free_count(bm)) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_swap_in: out of blocks");
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t d = take_fresh(bm);
+    pairs[2 * j] = s.blocks[j];
+    pairs[2 * j + 1] = d;
+    bm->host_free.push_back(s.blocks[j]);
+    s.blocks[j] = d;
+  }
+  s.swapped = false;
+  *n_pairs = n;
   return PKV_OK;
 }
 

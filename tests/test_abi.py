@@ -102,3 +102,47 @@ def test_empty_calls_are_ok_without_launch(lib):
     assert _decode(lib, batch=0) == 0
     assert lib.kv_cache_append(None, None, pkv.PKV_F16, 0, None, None, None, None, None, 4, 16, 2,
                                128, pkv.PKV_F16, None) == 0
+
+
+def test_int4_rejections(lib):
+    assert lib.kv_quantize(1, pkv.PKV_F16, 4, 127, pkv.PKV_I4, 1, 4, 0, None) == 1
+    assert "even" in lib.pkv_last_error().decode()
+    assert _decode(lib, kv_dtype=pkv.PKV_I4, k_scale=16, v_scale=16, q_dtype=pkv.PKV_F32) == 2
+    assert _decode(lib, kv_dtype=pkv.PKV_I4, k_scale=16, v_scale=16, head_dim=64) == 2
+    assert "INT4" in lib.pkv_last_error().decode()
+
+
+def test_multi_query_sizing_and_rejections(lib):
+    # 3 sequences, 40 query tokens, G = 8: at most ceil(40*8/16) + 3 = 23 row tiles,
+    # each with 3 int32 of plan (276 B, padded to 512); contexts <= 256 are never split.
+    assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 256) == 512
+    # longer: + 16 B per row tile (padded to 512) + rows of 16 x (2 + d) floats per item
+    big = pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 32768)
+    assert big > 1024 and (big - 512 - 512) % (16 * 130 * 4) == 0
+    args = dict(out=16, q=16, q_dtype=pkv.PKV_F16, batch=2, num_query_tokens=10, query_start=4,
+                num_q_heads=8, k_cache=16, v_cache=16, k_scale=None, v_scale=None, num_blocks=4,
+                block_size=16, num_kv_heads=2, head_dim=128, kv_dtype=pkv.PKV_F16,
+                block_tables=4, max_blocks_per_seq=4, context_lens=4, max_context_len=64,
+                scale=0.1, workspace=None, workspace_bytes=0, stream=None)
+    assert lib.paged_attention_multi_query(*args.values()) == 3
+    assert "workspace" in lib.pkv_last_error().decode()
+    args.update(query_start=None)
+    assert lib.paged_attention_multi_query(*args.values()) == 1
+    args.update(query_start=4, num_query_tokens=0)
+    assert lib.paged_attention_multi_query(*args.values()) == 0
+
+
+def test_swap_blocks_checks_pairs_on_the_host(lib):
+    import numpy as np
+    pairs = np.array([[0, 1], [3, 9]], dtype=np.int32)   # 9 is outside an 8-block pool
+    p = pairs.ctypes.data_as(ctypes.c_void_p)
+    assert lib.kv_swap_blocks(16, 16, None, None, 4, 16, 16, None, None, 8, 16, 2, 128,
+                              pkv.PKV_F16, p, 2, None) == 1
+    assert "outside" in lib.pkv_last_error().decode()
+    assert lib.kv_swap_blocks(16, 16, None, None, 4, 16, 16, None, None, 8, 16, 2, 128, 9, p, 2,
+                              None) == 2
+    assert lib.kv_swap_blocks(16, 16, None, None, 4, 16, 16, None, None, 8, 16, 2, 128,
+                              pkv.PKV_I8, p, 1, None) == 1
+    assert "row scales" in lib.pkv_last_error().decode()
+    assert lib.kv_swap_blocks(None, None, None, None, 4, None, None, None, None, 8, 16, 2, 128,
+                              pkv.PKV_F16, None, 0, None) == 0

@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _pool(shape, fmt, seed):
+    shape = tuple(shape)
     g = torch.Generator().manual_seed(seed)
     if fmt == "i8":
         return torch.randint(-128, 128, shape, generator=g, dtype=torch.int8)
@@ -141,3 +142,133 @@ def test_manager_prefix_fork_and_copy_on_write_end_to_end():
             ref[b, h] = oracle.attend(q[b, h].double().numpy(), K[:, h // G], V[:, h // G],
                                       d ** -0.5)
     compare(got, ref, "f16", "manager end to end")
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16", "f32", "i8", "fp8", "i4"])
+def test_swap_blocks_device_host_bit_exact(fmt):
+    """Device pool -> pinned host pool -> other device blocks, byte for byte,
+    with runs of consecutive blocks and single blocks mixed; row scales move
+    with their blocks."""
+    NB, NH, Hkv, bs, d = 16, 10, 2, 16, 128
+    kc, vc = _pool((NB, Hkv, bs, d), fmt, 3), _pool((NB, Hkv, bs, d), fmt, 4)
+    ks = vs = None
+    if fmt in ("i8", "i4"):
+        ks, vs = torch.rand(NB, Hkv, bs), torch.rand(NB, Hkv, bs)
+    kd, vd = kc.cuda(), vc.cuda()
+    ksd = None if ks is None else ks.cuda()
+    vsd = None if vs is None else vs.cuda()
+    hk = torch.zeros(NH, *kc.shape[1:], dtype=kc.dtype, pin_memory=True)
+    hv = torch.zeros_like(hk, pin_memory=True)
+    hks = hvs = None
+    if ks is not None:
+        hks = torch.zeros(NH, Hkv, bs, pin_memory=True)
+        hvs = torch.zeros(NH, Hkv, bs, pin_memory=True)
+    kvd = {"i8": "i8", "fp8": "fp8", "i4": "i4"}.get(fmt)
+    out_pairs = np.array([[2, 0], [3, 1], [4, 2], [9, 7], [15, 3], [0, 9]], dtype=np.int32)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        pkv.kv_swap_blocks(kd, vd, hk, hv, out_pairs, ksd, vsd, hks, hvs, kv_dtype=kvd)
+    side.synchronize()
+    for s, h in out_pairs:
+        assert np.array_equal(_bytes(hk[h]), _bytes(kc[s])) and np.array_equal(_bytes(hv[h]), _bytes(vc[s]))
+        if ks is not None:
+            assert torch.equal(hks[h], ks[s]) and torch.equal(hvs[h], vs[s])
+    # back into other device blocks
+    in_pairs = np.array([[0, 10], [1, 11], [2, 12], [7, 5], [3, 6], [9, 14]], dtype=np.int32)
+    with torch.cuda.stream(side):
+        pkv.kv_swap_blocks(hk, hv, kd, vd, in_pairs, hks, hvs, ksd, vsd, kv_dtype=kvd)
+    side.synchronize()
+    want_k, want_v = kc.clone(), vc.clone()
+    for (s, h), (h2, dst) in zip(out_pairs, in_pairs):
+        assert h == h2
+        want_k[dst], want_v[dst] = kc[s], vc[s]
+    assert np.array_equal(_bytes(kd), _bytes(want_k)) and np.array_equal(_bytes(vd), _bytes(want_v))
+    if ks is not None:
+        want_ks = ks.clone()
+        for (s, _), (_, dst) in zip(out_pairs, in_pairs):
+            want_ks[dst] = ks[s]
+        assert torch.equal(ksd.cpu(), want_ks)
+
+
+def test_swap_rejects_pageable_host_memory():
+    kd = torch.zeros(4, 2, 16, 128, dtype=torch.float16, device="cuda")
+    pageable = torch.zeros(4, 2, 16, 128, dtype=torch.float16)
+    with pytest.raises(ValueError, match="pinned"):
+        pkv.kv_swap_blocks(kd, kd.clone(), pageable, pageable.clone(), np.array([[0, 1]], np.int32))
+    # the library's own check, past the binding
+    import ctypes
+    lib = pkv.load_library()
+    pairs = np.array([[0, 1]], dtype=np.int32)
+    st = lib.kv_swap_blocks(kd.data_ptr(), kd.data_ptr(), None, None, 4, pageable.data_ptr(),
+                            pageable.data_ptr(), None, None, 4, 16, 2, 128, pkv.PKV_F16,
+                            pairs.ctypes.data_as(ctypes.c_void_p), 1, None)
+    assert st == 1 and "pinned" in lib.pkv_last_error().decode()
+
+
+def test_manager_swap_out_reuse_and_swap_in_end_to_end():
+    """Sequences written through the manager; one is swapped out on a side
+    stream, its freed blocks are reused by a new sequence (overwritten), then it
+    is swapped back into fresh blocks; decode over every live sequence equals
+    the oracle over each sequence's own rows."""
+    bs, NB, NH, Hq, Hkv, d = 16, 24, 12, 8, 2, 128
+    G = Hq // Hkv
+    vocab, max_pos = 50, 256
+    g = torch.Generator().manual_seed(12)
+    table_k = torch.randn(vocab, max_pos, Hkv, d, generator=g).half()
+    table_v = torch.randn(vocab, max_pos, Hkv, d, generator=g).half()
+    rng = np.random.default_rng(4)
+    kc = torch.full((NB, Hkv, bs, d), float("nan"), dtype=torch.float16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    hk = torch.full((NH, Hkv, bs, d), float("nan"), dtype=torch.float16, pin_memory=True)
+    hv = torch.full_like(hk, float("nan"), pin_memory=True)
+    bm = pkv.BlockManager(NB, bs, prefix_caching=False)
+    bm.enable_swap(NH)
+    seqs = {}
+    side = torch.cuda.Stream()
+
+    def write(tokens, start, slots):
+        pos = np.arange(start, start + len(tokens))
+        pkv.kv_cache_append(table_k[tokens, pos].cuda(), table_v[tokens, pos].cuda(),
+                            torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda(), kc, vc)
+
+    def add(sid, n):
+        toks = rng.integers(0, vocab, n).tolist()
+        write(toks, 0, bm.add_sequence(sid, toks))
+        seqs[sid] = toks
+
+    add(1, 70)
+    add(2, 100)
+    add(3, 40)
+    out = bm.swap_out(2)                               # 7 blocks to the host pool
+    with torch.cuda.stream(side):
+        pkv.kv_swap_blocks(kc, vc, hk, hv, out)
+    done = torch.cuda.Event()
+    done.record(side)
+    torch.cuda.current_stream().wait_event(done)      # before the freed blocks are rewritten
+    add(4, 110)                                        # takes sequence 2's old blocks
+    bm.free(4)
+    add(5, 30)
+    back = bm.swap_in(2)
+    torch.cuda.current_stream().synchronize()
+    with torch.cuda.stream(side):
+        pkv.kv_swap_blocks(hk, hv, kc, vc, back)
+    side.synchronize()
+    ids = [1, 2, 3, 5]
+    mb = max(-(-len(seqs[i]) // bs) for i in ids)
+    tables, ctx = bm.block_tables(ids, mb)
+    say(f"  tables {tables.tolist()} ctx {ctx.tolist()} free {bm.num_free} host {bm.num_free_host}")
+    q = torch.randn(len(ids), Hq, d, generator=g).half()
+    res = torch.empty(len(ids), Hq, d, dtype=torch.float16, device="cuda")
+    pkv.paged_attention_decode(res, q.cuda(), kc, vc, torch.from_numpy(tables).cuda(),
+                               torch.from_numpy(ctx).cuda(), d ** -0.5, int(ctx.max()))
+    torch.cuda.synchronize()
+    got = res.double().cpu().numpy()
+    ref = np.zeros_like(got)
+    for b, sid in enumerate(ids):
+        toks = seqs[sid]
+        pos = np.arange(len(toks))
+        K = table_k[toks, pos].double().numpy()
+        V = table_v[toks, pos].double().numpy()
+        for h in range(Hq):
+            ref[b, h] = oracle.attend(q[b, h].double().numpy(), K[:, h // G], V[:, h // G], d ** -0.5)
+    compare(got, ref, "f16", "swap end to end")
