@@ -30,6 +30,7 @@ import time
 
 METRIC = "decode attention tokens/s + KV-read HBM GB/s (% of MI355X peak), 1 GPU"
 HBM_PEAK_GBPS = 8000.0
+PCIE_PEAK_GBPS = 64.0        # host link, PCIe 5.0 x16, per direction
 ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters_llama70b_gqa8.json")
 DECODE_SOURCES = ("paged_kv_cache_435_amd/csrc/pkv_decode.hip",
@@ -183,10 +184,11 @@ def cpu_baseline(w, cases, budget_s):
 
 
 def bench_blocks(args):
-    """Block-manager row: kv_copy_blocks bandwidth (each pair reads and writes
-    one block of both pools) at the 70B GQA-8 fp16 shape, and the host
-    manager's operation rate for a decode loop (one append per sequence per
-    step, with a fork and a release every step).  Prints one JSON line."""
+    """Block-manager rows: kv_copy_blocks bandwidth (each pair reads and writes
+    one block of both pools) at the 70B GQA-8 fp16 shape, kv_swap_blocks
+    bandwidth to pinned host memory and back, and the host manager's operation
+    rate for a decode loop (one append per sequence per step, with a fork and a
+    release every step).  Prints one JSON line."""
     import numpy as np
     import torch
 
@@ -218,6 +220,40 @@ def bench_blocks(args):
     moved = 2 * 2 * n_pairs * block_bytes      # K and V, read + write
     gbps = moved / t / 1e9
 
+    # Swap: 4096 blocks (512 MiB of K+V at this shape) to pinned host memory and
+    # back, each direction as one kv_swap_blocks call on a side stream (DMA);
+    # runs of consecutive blocks are merged, so the pairs are shuffled singles.
+    n_swap = 4096
+    hk = torch.empty((n_swap, Hkv, bs, d), dtype=torch.float16, pin_memory=True)
+    hv = torch.empty_like(hk, pin_memory=True)
+    dev_blocks = np.random.default_rng(2).permutation(NB)[:n_swap]
+    host_blocks = np.random.default_rng(3).permutation(n_swap)
+    out_pairs = np.stack([dev_blocks, host_blocks], 1).astype(np.int32)
+    in_pairs = np.stack([host_blocks, dev_blocks], 1).astype(np.int32)
+    side = torch.cuda.Stream()
+    swap_bytes = 2 * n_swap * block_bytes
+
+    def timed_swap(pairs, to_host, reps):
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(side):
+                e0.record()
+                if to_host:
+                    pkv.kv_swap_blocks(kc, vc, hk, hv, pairs)
+                else:
+                    pkv.kv_swap_blocks(hk, hv, kc, vc, pairs)
+                e1.record()
+            ts.append((e0, e1))
+        side.synchronize()
+        return float(np.mean(kernel_launch_times(ts)))
+
+    timed_swap(out_pairs, True, 1)
+    t_out = timed_swap(out_pairs, True, 5)
+    t_in = timed_swap(in_pairs, False, 5)
+    log(f"[bench] swap {n_swap} blocks: out {swap_bytes / t_out / 1e9:.1f} GB/s, "
+        f"in {swap_bytes / t_in / 1e9:.1f} GB/s")
+
     bm = pkv.BlockManager(1 << 16, 16, prefix_caching=True)
     rng = np.random.default_rng(1)
     B = 256
@@ -238,10 +274,17 @@ def bench_blocks(args):
         ops += 2
     host_s = time.perf_counter() - t0
     print(json.dumps({
-        "metric": "kv_copy_blocks GB/s (read + write) and block-manager host ops/s",
+        "metric": "kv_copy_blocks GB/s (read + write), kv_swap_blocks GB/s each way, "
+                  "block-manager host ops/s",
         "copy_blocks": {"pairs": n_pairs, "block_bytes_per_cache": block_bytes,
                         "avg_launch_us": t * 1e6, "achieved": gbps, "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS},
+        "swap": {"blocks": n_swap, "bytes": swap_bytes, "pairs": "shuffled single blocks",
+                 "out_us": t_out * 1e6, "out_gbps": swap_bytes / t_out / 1e9,
+                 "in_us": t_in * 1e6, "in_gbps": swap_bytes / t_in / 1e9,
+                 "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                 "frac_out": swap_bytes / t_out / 1e9 / PCIE_PEAK_GBPS,
+                 "frac_in": swap_bytes / t_in / 1e9 / PCIE_PEAK_GBPS},
         "block_manager": {"ops": ops, "seconds": host_s, "ops_per_s": ops / host_s,
                           "sequences": B, "mix": "append 1 token per live sequence per step, "
                                                  "plus one release and one fork per step"}}),

@@ -376,9 +376,11 @@ pkv_status pkv_bm_swap_in(pkv_block_manager* bm, int64_t seq_id, int32_t* pairs,
  *                 [num_blocks][num_kv_heads][block_size] float32.
  *   pairs         HOST int32 [n_pairs][2] (src block, dst block), each index
  *                 inside its pool (checked before anything is enqueued).
- *   stream        the copies are DMA transfers enqueued on it (typically a side
- *                 stream, so they overlap decode kernels without taking compute
- *                 units); runs of consecutive blocks go as one transfer.
+ *   stream        the copies are enqueued on it (typically a side stream, so they
+ *                 overlap decode kernels).  Up to 32 runs of consecutive blocks
+ *                 go as DMA transfers (no compute units taken); more, shorter
+ *                 runs are moved by a copy kernel that reads and writes pinned
+ *                 host memory directly (per-transfer overhead would dominate).
  *   Errors: PKV_ERR_INVALID_ARG (NULL pointers, bad sizes or pairs, pageable
  *           host memory), PKV_ERR_UNSUPPORTED (unknown dtype), PKV_ERR_HIP.
  */

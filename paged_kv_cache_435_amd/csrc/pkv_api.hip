@@ -68,6 +68,10 @@ int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads
   return pkv::max_items_bound(batch, units, max_context_len, pkv::kMaxSlots);
 }
 
+// kv_swap_blocks: at most this many runs of consecutive blocks go as DMA
+// transfers; more take the copy kernel.
+constexpr int32_t kSwapDmaRuns = 32;
+
 // Several query tokens per sequence: virtual sequences (16-row tiles of
 // (query token, head) rows) can number at most ceil(T G / 16) + batch.
 int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group) {
@@ -418,6 +422,21 @@ pkv_status kv_swap_blocks(const void* src_k, const void* src_v, const float* src
   const int64_t block_bytes = block_rows * pkv::row_bytes_of(kv_dtype, head_dim);
   const int64_t scale_bytes = block_rows * 4;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // Runs of consecutive blocks go to the DMA engines as single transfers (no
+  // compute units taken); when the pairs make many short runs, one transfer
+  // each would cost more in per-transfer overhead than the bytes take, so a
+  // gather/scatter kernel moves them instead (reading and writing pinned host
+  // memory directly).
+  int32_t runs = 0;
+  for (int32_t i = 0; i < n_pairs; ++i)
+    runs += i == 0 || pairs[2 * i] != pairs[2 * i - 2] + 1 || pairs[2 * i + 1] != pairs[2 * i - 1] + 1;
+  if (runs > kSwapDmaRuns) {
+    pkv::SwapArrays arr{{src_k, src_v, src_k_scale, src_v_scale},
+                        {dst_k, dst_v, dst_k_scale, dst_v_scale}};
+    return hip_status(pkv::launch_swap_blocks(arr, scaled ? 4 : 2, pairs, n_pairs, block_bytes,
+                                              scale_bytes, st),
+                      fn);
+  }
   auto copy = [&](const void* s, void* d, int64_t per, int32_t sb, int32_t db, int32_t n) {
     return hipMemcpyAsync(static_cast<uint8_t*>(d) + (int64_t)db * per,
                           static_cast<const uint8_t*>(s) + (int64_t)sb * per, (size_t)(n * per),

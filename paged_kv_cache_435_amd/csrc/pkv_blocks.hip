@@ -33,6 +33,7 @@
 #include <vector>
 
 #include "pkv_common.h"
+#include "pkv_internal.h"
 
 namespace {
 
@@ -425,6 +426,46 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ 
   if (sc)
     for (int64_t i = threadIdx.x; i < block_rows; i += blockDim.x)
       sc[(int64_t)dst * block_rows + i] = sc[(int64_t)src * block_rows + i];
+}
+
+// Swap copies between two pools (device and pinned host memory, which the
+// kernel reads and writes directly over the host link).  One workgroup per
+// (pair, array); the pairs of a launch travel in the kernel arguments, so the
+// host's pair list needs no device copy.
+__global__ __launch_bounds__(256) void swap_blocks_kernel(SwapArrays arr, SwapChunk chunk,
+                                                          int64_t block_bytes,
+                                                          int64_t scale_bytes) {
+  const int pair = blockIdx.x;
+  const int which = blockIdx.y;            // 0 K, 1 V, 2 K scales, 3 V scales
+  if (pair >= chunk.n) return;
+  const int64_t per = which < 2 ? block_bytes : scale_bytes;
+  const uint8_t* s = static_cast<const uint8_t*>(arr.src[which]) + (int64_t)chunk.src[pair] * per;
+  uint8_t* d = static_cast<uint8_t*>(arr.dst[which]) + (int64_t)chunk.dst[pair] * per;
+  if (((per | (int64_t)(uintptr_t)s | (int64_t)(uintptr_t)d) & 15) == 0) {
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(s);
+    u32x4* d4 = reinterpret_cast<u32x4*>(d);
+    for (int64_t i = threadIdx.x; i < per / 16; i += blockDim.x) d4[i] = s4[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < per; i += blockDim.x) d[i] = s[i];
+  }
+}
+
+hipError_t launch_swap_blocks(const SwapArrays& arr, int arrays, const int32_t* pairs,
+                              int32_t n_pairs, int64_t block_bytes, int64_t scale_bytes,
+                              hipStream_t st) {
+  for (int32_t i0 = 0; i0 < n_pairs; i0 += kSwapChunk) {
+    SwapChunk c;
+    c.n = n_pairs - i0 < kSwapChunk ? n_pairs - i0 : kSwapChunk;
+    for (int j = 0; j < c.n; ++j) {
+      c.src[j] = pairs[2 * (i0 + j)];
+      c.dst[j] = pairs[2 * (i0 + j) + 1];
+    }
+    hipLaunchKernelGGL(swap_blocks_kernel, dim3(c.n, arrays), dim3(256), 0, st, arr, c,
+                       block_bytes, scale_bytes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v_scale,

@@ -78,6 +78,22 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, float* k_scale, floa
                               const int32_t* pairs, int32_t n_pairs, int64_t block_bytes,
                               int64_t block_rows, int32_t num_blocks, hipStream_t st);
 
+// Swap copies: pools K, V, K scales, V scales (source and destination), and
+// the pairs of one launch passed by value.
+struct SwapArrays {
+  const void* src[4];
+  void* dst[4];
+};
+constexpr int kSwapChunk = 256;
+struct SwapChunk {
+  int32_t n;
+  int32_t src[kSwapChunk];
+  int32_t dst[kSwapChunk];
+};
+hipError_t launch_swap_blocks(const SwapArrays& arr, int arrays, const int32_t* pairs,
+                              int32_t n_pairs, int64_t block_bytes, int64_t scale_bytes,
+                              hipStream_t st);
+
 hipError_t launch_append(const void* k, const void* v, int src_dtype, int num_tokens,
                          const int64_t* slots, void* k_cache, void* v_cache, float* k_scale,
                          float* v_scale, int num_blocks, int block_size, int num_kv_heads,

@@ -144,12 +144,14 @@ def test_manager_prefix_fork_and_copy_on_write_end_to_end():
     compare(got, ref, "f16", "manager end to end")
 
 
+@pytest.mark.parametrize("scattered", [False, True])
 @pytest.mark.parametrize("fmt", ["f16", "bf16", "f32", "i8", "fp8", "i4"])
-def test_swap_blocks_device_host_bit_exact(fmt):
+def test_swap_blocks_device_host_bit_exact(fmt, scattered):
     """Device pool -> pinned host pool -> other device blocks, byte for byte,
-    with runs of consecutive blocks and single blocks mixed; row scales move
-    with their blocks."""
-    NB, NH, Hkv, bs, d = 16, 10, 2, 16, 128
+    with runs of consecutive blocks and single blocks mixed (DMA transfers), or
+    300 shuffled single blocks (the copy kernel, two launches of pairs); row
+    scales move with their blocks."""
+    NB, NH, Hkv, bs, d = (640, 320, 2, 16, 128) if scattered else (16, 10, 2, 16, 128)
     kc, vc = _pool((NB, Hkv, bs, d), fmt, 3), _pool((NB, Hkv, bs, d), fmt, 4)
     ks = vs = None
     if fmt in ("i8", "i4"):
@@ -165,6 +167,9 @@ def test_swap_blocks_device_host_bit_exact(fmt):
         hvs = torch.zeros(NH, Hkv, bs, pin_memory=True)
     kvd = {"i8": "i8", "fp8": "fp8", "i4": "i4"}.get(fmt)
     out_pairs = np.array([[2, 0], [3, 1], [4, 2], [9, 7], [15, 3], [0, 9]], dtype=np.int32)
+    if scattered:
+        r = np.random.default_rng(5)
+        out_pairs = np.stack([r.permutation(NB)[:300], r.permutation(NH)[:300]], 1).astype(np.int32)
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         pkv.kv_swap_blocks(kd, vd, hk, hv, out_pairs, ksd, vsd, hks, hvs, kv_dtype=kvd)
@@ -175,6 +180,9 @@ def test_swap_blocks_device_host_bit_exact(fmt):
             assert torch.equal(hks[h], ks[s]) and torch.equal(hvs[h], vs[s])
     # back into other device blocks
     in_pairs = np.array([[0, 10], [1, 11], [2, 12], [7, 5], [3, 6], [9, 14]], dtype=np.int32)
+    if scattered:
+        dests = np.random.default_rng(6).permutation(NB)[:300]
+        in_pairs = np.stack([out_pairs[:, 1], dests], 1).astype(np.int32)
     with torch.cuda.stream(side):
         pkv.kv_swap_blocks(hk, hv, kd, vd, in_pairs, hks, hvs, ksd, vsd, kv_dtype=kvd)
     side.synchronize()
