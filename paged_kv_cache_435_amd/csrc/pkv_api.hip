@@ -72,10 +72,11 @@ int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads
 // transfers; more take the copy kernel.
 constexpr int32_t kSwapDmaRuns = 32;
 
-// Several query tokens per sequence: virtual sequences (16-row tiles of
-// (query token, head) rows) can number at most ceil(T G / 16) + batch.
+// Several query tokens per sequence: virtual sequences (32-row tiles of
+// (query token, head) rows) can number at most ceil(T G / 32) + batch.
 int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group) {
-  return (num_query_tokens * group + 15) / 16 + batch;
+  const int64_t rows = 16 * pkv::kMultiRowTiles;
+  return (num_query_tokens * group + rows - 1) / rows + batch;
 }
 int64_t multi_items(int64_t vseqs, int64_t num_kv_heads, int64_t max_context_len) {
   if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
@@ -83,7 +84,8 @@ int64_t multi_items(int64_t vseqs, int64_t num_kv_heads, int64_t max_context_len
 }
 int64_t vseq_bytes(int64_t vseqs) { return (3 * vseqs * 4 + 255) / 256 * 256; }
 int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim) {
-  return vseq_bytes(vseqs) + (items > 0 ? seq_bytes(vseqs) + items * row_bytes(head_dim) : 0);
+  return vseq_bytes(vseqs) +
+         (items > 0 ? seq_bytes(vseqs) + items * pkv::kMultiRowTiles * row_bytes(head_dim) : 0);
 }
 
 }  // namespace
@@ -375,7 +377,8 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
     uint8_t* rest = w + vseq_bytes(vseqs);
     a.ws_seq = reinterpret_cast<int64_t*>(rest);
     a.ws_ml = reinterpret_cast<float*>(rest + seq_bytes(vseqs));
-    a.ws_acc = reinterpret_cast<float*>(rest + seq_bytes(vseqs) + items * 16 * 2 * 4);
+    a.ws_acc = reinterpret_cast<float*>(rest + seq_bytes(vseqs) +
+                                        items * pkv::kMultiRowTiles * 16 * 2 * 4);
   }
   return hip_status(pkv::launch_multi(a, batch, vctx, q_dtype, kv_dtype, head_dim, block_size, cus,
                                       static_cast<hipStream_t>(stream)),

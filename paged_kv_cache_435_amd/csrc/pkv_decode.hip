@@ -428,7 +428,8 @@ struct Tuning {
 // a.context_lens holds those lengths and a.vseq_b / a.vseq_rt say which
 // sequence and row tile each is (written by multi_prep_kernel).
 template <int KV, int QT, int D, int BS, bool MULTI>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(Tuning<KV>::waves_per_eu)))
+__global__ __launch_bounds__(64)
+__attribute__((amdgpu_waves_per_eu(MULTI ? 2 : Tuning<KV>::waves_per_eu)))   // (32 rows: 2 waves/SIMD)
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
   constexpr int eb = dtype_bytes(KV);  // (INT4: handled apart wherever it matters)
@@ -439,6 +440,10 @@ void decode_partition_kernel(DecodeArgs a) {
   constexpr int KW = NL * WPC;         // MFMA words per lane for a K tile (= D/8 or D/4)
   constexpr int NC = D / 16;           // 16-wide d chunks of the output
   constexpr int VG = 4 / eb;           // 16-wide d chunks per 16 bytes of a V lane
+  // Query rows per wave, in tiles of 16 (the MFMA's N): 16 for decode, 32 for
+  // multi-token calls, whose query tokens x heads of a KV head run to dozens of
+  // rows (each loaded K/V tile then serves twice the rows).
+  constexpr int RT = MULTI ? kMultiRowTiles : 1;
 
   const int lane = threadIdx.x;
   const int r16 = lane & 15;   // MFMA row/column index of this lane
@@ -474,10 +479,10 @@ void decode_partition_kernel(DecodeArgs a) {
   }
 
   const int G = a.num_q_heads / a.num_kv_heads;
-  bool head_ok;
-  int64_t hq;                 // this lane's row of q and out
-  int prow = 0x7FFFFFFF;      // last cache position this lane's row may see
-  int p_min = 0x7FFFFFFF;     // the smallest such position over the tile's rows
+  bool head_ok[RT];
+  int64_t hq[RT];             // this lane's rows of q and out
+  int prow[RT];               // last cache position each of this lane's rows may see
+  int p_min = 0x7FFFFFFF;     // the smallest such position over the wave's rows
   int bq = b;                 // the real sequence (block table row)
   if constexpr (MULTI) {
     bq = uni(a.vseq_b[b]);
@@ -486,18 +491,22 @@ void decode_partition_kernel(DecodeArgs a) {
     const int L = uni(a.query_start[bq + 1]) - q0;
     int cr = a.real_ctx[bq];
     cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
-    const int rho = 16 * rt + r16;                   // row = query token * G + head
-    const int j = rho / G;
-    head_ok = rho < L * G && q0 + j < a.q_rows;
-    hq = (int64_t)(q0 + j) * a.num_q_heads + g * G + rho % G;
-    prow = cr - L + j;
-    p_min = cr - L + (16 * rt) / G;
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const int rho = 16 * RT * rt + 16 * k + r16;   // row = query token * G + head
+      const int j = rho / G;
+      head_ok[k] = rho < L * G && q0 + j < a.q_rows;
+      hq[k] = (int64_t)(q0 + j) * a.num_q_heads + g * G + rho % G;
+      prow[k] = cr - L + j;
+    }
+    p_min = cr - L + (16 * RT * rt) / G;
   } else {
     const int h_first = g * G + ht * 16;             // first query head of this tile
     int nh = G - ht * 16;
     nh = nh > 16 ? 16 : nh;
-    head_ok = r16 < nh;
-    hq = (int64_t)b * a.num_q_heads + h_first + r16;
+    head_ok[0] = r16 < nh;
+    hq[0] = (int64_t)b * a.num_q_heads + h_first + r16;
+    prow[0] = 0x7FFFFFFF;
   }
   // Leading tiles of the item that every row sees whole (uniform).
   const int full_end = p_min < t_end ? p_min + 1 : t_end;   // (no overflow at INT_MAX)
@@ -518,39 +527,44 @@ void decode_partition_kernel(DecodeArgs a) {
 
   // Query operand: lane holds head r16 at the d positions its K chunks carry
   // (the same bytes of q in memory order: 16-byte loads).
-  uint32_t qop[KW];
+  uint32_t qop[RT][KW];
 #pragma unroll
-  for (int i = 0; i < KW; ++i) qop[i] = 0u;
+  for (int k = 0; k < RT; ++k)
+#pragma unroll
+    for (int i = 0; i < KW; ++i) qop[k][i] = 0u;
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
   if constexpr (KV == PKV_I4) {
-   if (head_ok) {
+   if (head_ok[k]) {
     // INT4: the lane's K chunk holds d = 32 c16 .. 32 c16 + 31; word i of it
     // converts to elements 8 i + (0 4 1 5 2 6 3 7), so q pairs are taken in
     // that order.
-    const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq * D + 32 * c16) * 2;
+    const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + 32 * c16) * 2;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(src + 16 * i);
-      qop[4 * i + 0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);   // (8i, 8i+4)
-      qop[4 * i + 1] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);   // (8i+1, 8i+5)
-      qop[4 * i + 2] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);   // (8i+2, 8i+6)
-      qop[4 * i + 3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);   // (8i+3, 8i+7)
+      qop[k][4 * i + 0] = __builtin_amdgcn_perm(w[2], w[0], 0x05040100u);   // (8i, 8i+4)
+      qop[k][4 * i + 1] = __builtin_amdgcn_perm(w[2], w[0], 0x07060302u);   // (8i+1, 8i+5)
+      qop[k][4 * i + 2] = __builtin_amdgcn_perm(w[3], w[1], 0x05040100u);   // (8i+2, 8i+6)
+      qop[k][4 * i + 3] = __builtin_amdgcn_perm(w[3], w[1], 0x07060302u);   // (8i+3, 8i+7)
     }
    }
-  } else if (head_ok) {
+  } else if (head_ok[k]) {
     constexpr int qsize = QT == PKV_F32 ? 4 : 2;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       const int d0 = (64 * j + 16 * c16) / eb;
-      const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq * D + d0) * qsize;
+      const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + d0) * qsize;
 #pragma unroll
       for (int o = 0; o < WPC; o += 4) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(src + 4 * o);
-        qop[j * WPC + o] = w[0];
-        qop[j * WPC + o + 1] = w[1];
-        qop[j * WPC + o + 2] = w[2];
-        qop[j * WPC + o + 3] = w[3];
+        qop[k][j * WPC + o] = w[0];
+        qop[k][j * WPC + o + 1] = w[1];
+        qop[k][j * WPC + o + 2] = w[2];
+        qop[k][j * WPC + o + 3] = w[3];
       }
     }
+  }
   }
 
   // OffsetCodes — INT8 and INT4 with f16 queries: codes enter the MFMAs as
@@ -563,22 +577,26 @@ void decode_partition_kernel(DecodeArgs a) {
   // they are taken from (fp32 keeps about 1e-5 of the result).
   constexpr bool offset_codes = (KV == PKV_I4 || KV == PKV_I8) && MT == MT_F16;
   constexpr float code_offset = KV == PKV_I4 ? 8.0f : 128.0f;
-  float qsum = 0.f;
-  if constexpr (offset_codes) {
-    const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  float qsum[RT];
 #pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      f16x2 h = __builtin_bit_cast(f16x2, qop[i]);
-      const bool hi = KV == PKV_I4 && (i & 1);
-      if (hi) {
-        h = h * sixteenth;
-        qop[i] = __builtin_bit_cast(uint32_t, h);
+  for (int k = 0; k < RT; ++k) {
+    qsum[k] = 0.f;
+    if constexpr (offset_codes) {
+      const f16x2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+#pragma unroll
+      for (int i = 0; i < KW; ++i) {
+        f16x2 h = __builtin_bit_cast(f16x2, qop[k][i]);
+        const bool hi = KV == PKV_I4 && (i & 1);
+        if (hi) {
+          h = h * sixteenth;
+          qop[k][i] = __builtin_bit_cast(uint32_t, h);
+        }
+        const float t = (float)h[0] + (float)h[1];
+        qsum[k] += hi ? 16.f * t : t;
       }
-      const float t = (float)h[0] + (float)h[1];
-      qsum += hi ? 16.f * t : t;
+      qsum[k] += __shfl_xor(qsum[k], 16, kWave);
+      qsum[k] += __shfl_xor(qsum[k], 32, kWave);
     }
-    qsum += __shfl_xor(qsum, 16, kWave);
-    qsum += __shfl_xor(qsum, 32, kWave);
   }
 
   // Constant factors: logits are taken in the exp2 domain.
@@ -586,7 +604,9 @@ void decode_partition_kernel(DecodeArgs a) {
   float vfac = 1.0f;
   // offset codes: z = (s * 2^24 - o qsum) * kfac * (1 / row scale)
   const float kf24 = kfac * 16777216.0f;
-  const float kbias = -code_offset * qsum * kfac;
+  float kbias[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) kbias[k] = -code_offset * qsum[k] * kfac;
   if constexpr (KV == PKV_FP8_E4M3FN) {
     kfac *= a.k_scale[0] * cvt_gain<KV, MT>();
     vfac = a.v_scale[0] * cvt_gain<KV, MT>();
@@ -595,12 +615,17 @@ void decode_partition_kernel(DecodeArgs a) {
   const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_cache);
   const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_cache);
 
-  f32x4 acc[NC];
+  f32x4 acc[RT][NC];
+  f32x4 acc_p[RT];                      // offset codes: sum of P per head (every row)
+  float m_run[RT], l_run[RT];
 #pragma unroll
-  for (int nc = 0; nc < NC; ++nc) acc[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  f32x4 acc_p = {0.f, 0.f, 0.f, 0.f};   // offset codes: sum of P per head (every row)
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  for (int k = 0; k < RT; ++k) {
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) acc[k][nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_p[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[k] = -__builtin_inff();
+    l_run[k] = 0.f;
+  }
 
   // Physical block of a tile (-1: outside the pool, the tile is skipped).
   auto tile_phys = [&](int tile) -> int {
@@ -692,109 +717,135 @@ void decode_partition_kernel(DecodeArgs a) {
     uint32_t kop[KW];
 #pragma unroll
     for (int j = 0; j < NL; ++j) C::run(kraw[j], kop + j * WPC);
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (MT == MT_F16) {
+    f32x4 s[RT];
 #pragma unroll
-      for (int c = 0; c < KW / 4; ++c) {
-        const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
-        const u32x4 qb = {qop[4 * c], qop[4 * c + 1], qop[4 * c + 2], qop[4 * c + 3]};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka),
-                                                   __builtin_bit_cast(f16x8, qb), s, 0, 0, 0);
+    for (int k = 0; k < RT; ++k) {
+      s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (MT == MT_F16) {
+#pragma unroll
+        for (int c = 0; c < KW / 4; ++c) {
+          const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
+          s[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka),
+                                                        __builtin_bit_cast(f16x8, qb), s[k], 0, 0, 0);
+        }
+      } else if constexpr (MT == MT_BF16) {
+#pragma unroll
+        for (int c = 0; c < KW / 4; ++c) {
+          const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
+          s[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                         __builtin_bit_cast(bf16x8, qb), s[k], 0, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < KW; ++c)
+          s[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[k][c]), s[k], 0, 0, 0);
       }
-    } else if constexpr (MT == MT_BF16) {
-#pragma unroll
-      for (int c = 0; c < KW / 4; ++c) {
-        const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
-        const u32x4 qb = {qop[4 * c], qop[4 * c + 1], qop[4 * c + 2], qop[4 * c + 3]};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                    __builtin_bit_cast(bf16x8, qb), s, 0, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < KW; ++c)
-        s = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[c]), s, 0, 0, 0);
     }
 
-    // Online softmax (lane: tokens 4*c16 + i of head r16).
-    float z[4];
-    float mx = -__builtin_inff();
+    // Online softmax (lane: tokens 4*c16 + i of row r16 of each row tile).
+    float p[RT][4];
+    float alpha[RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (offset_codes) {
-        z[i] = __builtin_fmaf(s[i], kf24, kbias) * krcp[i];
-      } else {
-        float f = kfac;
-        if constexpr (row_scaled(KV)) f = kfac * krcp[i];
-        z[i] = s[i] * f;
-      }
-      if constexpr (checked) {
-        const bool ok = 4 * c16 + i < n_valid && t_begin + tile * 16 + 4 * c16 + i <= prow;
-        z[i] = ok ? z[i] : -__builtin_inff();
-      }
-      mx = fmaxf(mx, z[i]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    // A live tile has a finite max, so exp2(-inf) = 0 covers the first one.
-    const bool live = !checked || m_new != -__builtin_inff();
-    // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may
-    // flush to zero, which only drops weights under 1e-38 of the largest.
-    const float alpha = live ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
-    float p[4];
-    float psum = 0.f;
+    for (int k = 0; k < RT; ++k) {
+      float z[4];
+      float mx = -__builtin_inff();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (checked)
-        p[i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
-      else
-        p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
-      psum += p[i];
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (offset_codes) {
+          z[i] = __builtin_fmaf(s[k][i], kf24, kbias[k]) * krcp[i];
+        } else {
+          float f = kfac;
+          if constexpr (row_scaled(KV)) f = kfac * krcp[i];
+          z[i] = s[k][i] * f;
+        }
+        if constexpr (checked) {
+          const bool ok = 4 * c16 + i < n_valid && t_begin + tile * 16 + 4 * c16 + i <= prow[k];
+          z[i] = ok ? z[i] : -__builtin_inff();
+        }
+        mx = fmaxf(mx, z[i]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run[k], mx);
+      // A live tile has a finite max, so exp2(-inf) = 0 covers the first one.
+      const bool live = !checked || m_new != -__builtin_inff();
+      // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may
+      // flush to zero, which only drops weights under 1e-38 of the largest.
+      alpha[k] = live ? __builtin_amdgcn_exp2f(m_run[k] - m_new) : 1.0f;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (checked)
+          p[k][i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
+        else
+          p[k][i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+        psum += p[k][i];
+      }
+      l_run[k] = l_run[k] * alpha[k] + psum;
+      m_run[k] = m_new;
+      if constexpr (row_scaled(KV)) {
+        // (the guard keeps a masked token's P at 0 even if its slot's scale is NaN)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          p[k][i] = (!checked || p[k][i] > 0.f) ? p[k][i] * vrcp[i] : 0.f;
+      }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    // Rescale only when some head's running max moved (alpha == 1 elsewhere
+    // Rescale only when some row's running max moved (alpha == 1 elsewhere
     // leaves the values unchanged, so the result is the same either way).
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    bool moved = false;
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[nc] *= alpha;
-      if constexpr (offset_codes) acc_p[0] *= alpha;   // only row 0 is read
-    }
-    if constexpr (row_scaled(KV)) {
-      // (the guard keeps a masked token's P at 0 even if its slot's scale is NaN)
+    for (int k = 0; k < RT; ++k) moved = moved || alpha[k] != 1.0f;
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = (!checked || p[i] > 0.f) ? p[i] * vrcp[i] : 0.f;
+      for (int k = 0; k < RT; ++k) {
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) acc[k][nc] *= alpha[k];
+        if constexpr (offset_codes) acc_p[k][0] *= alpha[k];   // only row 0 is read
+      }
     }
 
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
     // of tokens 4*c16 .. 4*c16+3 (storage order), i.e. the A operand.
+    const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
     if constexpr (KV == PKV_I4) {
       // Word wd of the lane's 16 bytes converts to column blocks 2 wd (words
       // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
       // lane's four: P is packed in the same token order.
-      const u32x2 pb = {pack_p<MT>(p[0], p[2]), pack_p<MT>(p[1], p[3])};
+      u32x2 pb[RT];
+#pragma unroll
+      for (int k = 0; k < RT; ++k)
+        pb[k] = u32x2{pack_p<MT>(p[k][0], p[k][2]), pack_p<MT>(p[k][1], p[k][3])};
       // Codes are finite and P is exactly 0 past the context, so no mask.
 #pragma unroll
       for (int wd = 0; wd < NC / 2; ++wd) {
         uint32_t w[4];
         C::word(vraw[0][wd], w);
         const u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
-        if constexpr (MT == MT_F16) {
-          acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb), acc[2 * wd], 0, 0, 0);
-          acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-              __builtin_bit_cast(f16x4, vb), __builtin_bit_cast(f16x4, pb), acc[2 * wd + 1], 0, 0, 0);
-        } else {
-          acc[2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(i16x4, va), __builtin_bit_cast(i16x4, pb), acc[2 * wd], 0, 0, 0);
-          acc[2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb), acc[2 * wd + 1], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RT; ++k) {
+          if constexpr (MT == MT_F16) {
+            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd], 0, 0, 0);
+            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                __builtin_bit_cast(f16x4, vb), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd + 1], 0,
+                0, 0);
+          } else {
+            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(i16x4, va), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd], 0, 0,
+                0);
+            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd + 1], 0,
+                0, 0);
+          }
         }
       }
       if constexpr (offset_codes) {
-        const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-        acc_p = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb), acc_p,
-                                                      0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RT; ++k)
+          acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
+                                                           acc_p[k], 0, 0, 0);
       }
     } else if constexpr (MT == MT_F32) {
 #pragma unroll
@@ -810,12 +861,17 @@ void decode_partition_kernel(DecodeArgs a) {
           C::word(vraw[nc / VG][2 * (nc % VG) + 1], w + 2);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[i] & vmask[i]), p[i], acc[nc],
-                                                         0, 0, 0);
+        for (int k = 0; k < RT; ++k)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[i] & vmask[i]), p[k][i],
+                                                              acc[k][nc], 0, 0, 0);
       }
     } else {
-      const u32x2 pb = {pack_p<MT>(p[0], p[1]), pack_p<MT>(p[2], p[3])};
+      u32x2 pb[RT];
+#pragma unroll
+      for (int k = 0; k < RT; ++k)
+        pb[k] = u32x2{pack_p<MT>(p[k][0], p[k][1]), pack_p<MT>(p[k][2], p[k][3])};
       const uint32_t m01 = (vmask[0] & 0xFFFFu) | (vmask[1] & 0xFFFF0000u);
       const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
       // uniform: only a sequence's last tile is partial.  INT8 codes are finite
@@ -832,20 +888,24 @@ void decode_partition_kernel(DecodeArgs a) {
         }
         u32x2 va = {w[0], w[1]};
         if (!full) va = u32x2{w[0] & m01, w[1] & m23};
-        if constexpr (MT == MT_F16) {
-          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
-                                                          __builtin_bit_cast(f16x4, pb), acc[nc],
-                                                          0, 0, 0);
-        } else {
-          acc[nc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, va),
-                                                              __builtin_bit_cast(i16x4, pb),
-                                                              acc[nc], 0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RT; ++k) {
+          if constexpr (MT == MT_F16) {
+            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
+                                                               __builtin_bit_cast(f16x4, pb[k]),
+                                                               acc[k][nc], 0, 0, 0);
+          } else {
+            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, va),
+                                                                   __builtin_bit_cast(i16x4, pb[k]),
+                                                                   acc[k][nc], 0, 0, 0);
+          }
         }
       }
       if constexpr (offset_codes) {
-        const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-        acc_p = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb), acc_p,
-                                                      0, 0, 0);
+#pragma unroll
+        for (int k = 0; k < RT; ++k)
+          acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
+                                                           acc_p[k], 0, 0, 0);
       }
     }
   };
@@ -898,31 +958,34 @@ void decode_partition_kernel(DecodeArgs a) {
   }
 
   // ---- epilogue ----
-  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (!head_ok) return;
-  if constexpr (offset_codes) {
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc)
-      acc[nc] = acc[nc] * ((KV == PKV_I4 && (nc & 1)) ? 1048576.0f : 16777216.0f) -
-                code_offset * acc_p[0];
-  }
-  if (whole_unit) {
-    // (l_tot = 0 only for a row that sees no token: its output is zeros)
-    const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
+  for (int k = 0; k < RT; ++k) {
+    float l_tot = l_run[k] + __shfl_xor(l_run[k], 16, kWave);
+    l_tot += __shfl_xor(l_tot, 32, kWave);
+    if (!head_ok[k]) continue;
+    if constexpr (offset_codes) {
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc)
-      store_out4<QT>(a.out, hq * D + nc * 16 + c16 * 4, acc[nc][0] * inv, acc[nc][1] * inv,
-                     acc[nc][2] * inv, acc[nc][3] * inv);
-  } else if (item < a.max_items) {
-    const int64_t slot = item * 16 + r16;   // partial row of this item and head
-    if (c16 == 0) {
-      a.ws_ml[2 * slot] = m_run;
-      a.ws_ml[2 * slot + 1] = l_tot;
+      for (int nc = 0; nc < NC; ++nc)
+        acc[k][nc] = acc[k][nc] * ((KV == PKV_I4 && (nc & 1)) ? 1048576.0f : 16777216.0f) -
+                     code_offset * acc_p[k][0];
     }
+    if (whole_unit) {
+      // (l_tot = 0 only for a row that sees no token: its output is zeros)
+      const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
 #pragma unroll
-    for (int nc = 0; nc < NC; ++nc)
-      *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[nc] * vfac;
+      for (int nc = 0; nc < NC; ++nc)
+        store_out4<QT>(a.out, hq[k] * D + nc * 16 + c16 * 4, acc[k][nc][0] * inv,
+                       acc[k][nc][1] * inv, acc[k][nc][2] * inv, acc[k][nc][3] * inv);
+    } else if (item < a.max_items) {
+      const int64_t slot = item * (16 * RT) + 16 * k + r16;   // partial row of this item and row
+      if (c16 == 0) {
+        a.ws_ml[2 * slot] = m_run[k];
+        a.ws_ml[2 * slot + 1] = l_tot;
+      }
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc)
+        *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[k][nc] * vfac;
+    }
   }
 }
 
@@ -1004,32 +1067,34 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
                    (int64_t)a.head_tiles * 16, m, hq, lane);
 }
 
-// Several query tokens per sequence: one wave per (virtual sequence, KV head),
-// i.e. per 16-row tile of (query token, head) rows; rows of a virtual sequence
-// with no context (rows before the cache) get zeros.
+// Several query tokens per sequence: one wave per (virtual sequence, KV head,
+// row of the 16-row tile of (query token, head) rows); rows of a virtual
+// sequence with no context (rows before the cache) get zeros.
 template <int QT, int D>
 __global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
+  constexpr int ROWS = 16 * kMultiRowTiles;   // rows of a virtual sequence
   const int v = blockIdx.x;
   const int g = blockIdx.y;
+  const int r_only = blockIdx.z;      // this wave's row of the tile
   const int lane = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bq = a.vseq_b[v];
   const int rt = a.vseq_rt[v];
   const int q0 = a.query_start[bq];
   const int L = a.query_start[bq + 1] - q0;
-  int rows = L * G - 16 * rt;
-  rows = rows > 16 ? 16 : rows;
+  int rows = L * G - ROWS * rt;
+  rows = rows > ROWS ? ROWS : rows;
   // rows past the query tensor (inconsistent query_start) are never written
-  const int rows_q = (a.q_rows - q0) * G - 16 * rt;
+  const int rows_q = (a.q_rows - q0) * G - ROWS * rt;
   rows = rows < rows_q ? rows : rows_q;
   if (rows <= 0) return;              // a padding entry
   auto out_row = [&](int r) -> int64_t {
-    const int rho = 16 * rt + r;
+    const int rho = ROWS * rt + r;
     return (int64_t)(q0 + rho / G) * a.num_q_heads + g * G + rho % G;
   };
+  if (r_only >= rows) return;
   if (seq_ctx(a, v) == 0) {
-    for (int r = 0; r < rows; ++r)
-      if (lane < D / 4) store_out4<QT>(a.out, out_row(r) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
+    if (lane < D / 4) store_out4<QT>(a.out, out_row(r_only) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   if (!a.ws_seq) return;
@@ -1038,16 +1103,17 @@ __global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
   if (m <= 1) return;
   // head_tiles is 1: chunk c of KV head g is item first + g*m + c.
   if (first + (int64_t)g * m + m - 1 >= a.max_items) return;
-  for (int r = 0; r < rows; ++r)
-    merge_row<QT, D>(a, (first + (int64_t)g * m) * 16 + r, 16, m, out_row(r), lane);
+  merge_row<QT, D>(a, (first + (int64_t)g * m) * ROWS + r_only, ROWS, m, out_row(r_only), lane);
 }
 
 // Virtual sequences of a multi-token call (one workgroup): sequence b's
-// ceil(L_b G / 16) row tiles, in order, each with the context its last row may
-// see; entries past the last are padding with no context.
+// ceil(L_b G / 32) row tiles, in order, each with the context its last row may
+// see; entries past the last are padding with no context.  Sequences go 1024
+// at a time: a block scan gives each its first entry, then every thread fills
+// entries, finding its sequence by binary search over the scan.
 __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batch_real,
                                                           int32_t* vctx) {
-  __shared__ int scan[1024];
+  __shared__ int scan[1024];   // inclusive: entries of sequences b0 .. b0 + t
   __shared__ int carry;
   const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -1055,14 +1121,13 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   __syncthreads();
   for (int b0 = 0; b0 < batch_real; b0 += 1024) {
     const int b = b0 + t;
-    int L = 0, ctx = 0;
+    int L = 0;
     if (b < batch_real) {
       L = a.query_start[b + 1] - a.query_start[b];
       L = L < 0 ? 0 : L;
-      ctx = a.real_ctx[b];
-      ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
     }
-    const int n = (L * G + 15) / 16;
+    constexpr int ROWS = 16 * kMultiRowTiles;
+    const int n = (L * G + ROWS - 1) / ROWS;
     scan[t] = n;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
@@ -1071,26 +1136,36 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       scan[t] += x;
       __syncthreads();
     }
-    const int base = carry + scan[t] - n;
-    for (int rt = 0; rt < n; ++rt) {
-      const int v = base + rt;
-      if (v < a.batch) {
-        int last = 16 * rt + 15;
-        last = last < L * G - 1 ? last : L * G - 1;
-        int c = ctx - L + last / G + 1;
-        vctx[v] = c < 0 ? 0 : c;
-        a.vseq_b[v] = b;
-        a.vseq_rt[v] = rt;
+    const int base = carry;
+    const int total = scan[1023];
+    for (int e = t; e < total; e += 1024) {
+      const int v = base + e;
+      if (v >= a.batch) break;
+      int lo = 0, hi = 1023;                 // first sequence whose scan passes e
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] > e) hi = mid; else lo = mid + 1;
       }
+      const int bb = b0 + lo;
+      const int rt = e - (lo > 0 ? scan[lo - 1] : 0);
+      const int Lb = a.query_start[bb + 1] - a.query_start[bb];
+      int ctx = a.real_ctx[bb];
+      ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+      int last = 16 * kMultiRowTiles * rt + 16 * kMultiRowTiles - 1;
+      last = last < Lb * G - 1 ? last : Lb * G - 1;
+      const int c = ctx - Lb + last / G + 1;
+      vctx[v] = c < 0 ? 0 : c;
+      a.vseq_b[v] = bb;
+      a.vseq_rt[v] = rt;
     }
     __syncthreads();
-    if (t == 1023) carry += scan[1023];
+    if (t == 0) carry = base + total;
     __syncthreads();
   }
   for (int v = carry + t; v < a.batch; v += 1024) {
     vctx[v] = 0;
     a.vseq_b[v] = 0;
-    a.vseq_rt[v] = 0x07FFFFFF;   // no rows (16 * rt stays below 2^31)
+    a.vseq_rt[v] = 0x03FFFFFF;   // no rows (32 * rt stays below 2^31)
   }
 }
 
@@ -1150,8 +1225,8 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MULTI)
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, a.num_kv_heads), dim3(64), 0,
-                       st, a);
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>),
+                       dim3(a.batch, a.num_kv_heads, 16 * kMultiRowTiles), dim3(64), 0, st, a);
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
                        st, a);
