@@ -1067,16 +1067,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
                    (int64_t)a.head_tiles * 16, m, hq, lane);
 }
 
-// Several query tokens per sequence: one wave per (virtual sequence, KV head,
-// row of the 16-row tile of (query token, head) rows); rows of a virtual
-// sequence with no context (rows before the cache) get zeros.
+// Several query tokens per sequence: one workgroup of 8 waves per (virtual
+// sequence, KV head), i.e. per 32-row tile of (query token, head) rows, each
+// wave merging every 8th row; rows of a virtual sequence with no context (rows
+// before the cache) get zeros.  A unit that was one item (the common case for
+// prompt chunks) costs one read of its record.
+constexpr int kMergeWaves = 8;
 template <int QT, int D>
-__global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
   constexpr int ROWS = 16 * kMultiRowTiles;   // rows of a virtual sequence
   const int v = blockIdx.x;
   const int g = blockIdx.y;
-  const int r_only = blockIdx.z;      // this wave's row of the tile
-  const int lane = threadIdx.x;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bq = a.vseq_b[v];
   const int rt = a.vseq_rt[v];
@@ -1092,9 +1095,9 @@ __global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
     const int rho = ROWS * rt + r;
     return (int64_t)(q0 + rho / G) * a.num_q_heads + g * G + rho % G;
   };
-  if (r_only >= rows) return;
   if (seq_ctx(a, v) == 0) {
-    if (lane < D / 4) store_out4<QT>(a.out, out_row(r_only) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
+    for (int r = wave; r < rows; r += kMergeWaves)
+      if (lane < D / 4) store_out4<QT>(a.out, out_row(r) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
     return;
   }
   if (!a.ws_seq) return;
@@ -1103,7 +1106,8 @@ __global__ __launch_bounds__(64) void multi_merge_kernel(DecodeArgs a) {
   if (m <= 1) return;
   // head_tiles is 1: chunk c of KV head g is item first + g*m + c.
   if (first + (int64_t)g * m + m - 1 >= a.max_items) return;
-  merge_row<QT, D>(a, (first + (int64_t)g * m) * ROWS + r_only, ROWS, m, out_row(r_only), lane);
+  for (int r = wave; r < rows; r += kMergeWaves)
+    merge_row<QT, D>(a, (first + (int64_t)g * m) * ROWS + r, ROWS, m, out_row(r), lane);
 }
 
 // Virtual sequences of a multi-token call (one workgroup): sequence b's
@@ -1225,8 +1229,8 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MULTI)
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>),
-                       dim3(a.batch, a.num_kv_heads, 16 * kMultiRowTiles), dim3(64), 0, st, a);
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, a.num_kv_heads),
+                       dim3(64 * kMergeWaves), 0, st, a);
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
                        st, a);
