@@ -72,15 +72,23 @@ int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads
 // transfers; more take the copy kernel.
 constexpr int32_t kSwapDmaRuns = 32;
 
-// Several query tokens per sequence: virtual sequences (32-row tiles of
-// (query token, head) rows) can number at most ceil(T G / 32) + batch.
+// Several query tokens per sequence.  A wave takes a tile of 32 (query token,
+// head) rows; a virtual sequence (the planner's unit of work per KV head) is a
+// group of up to kMultiGroupMax such tiles, run as one workgroup so they read
+// each K/V tile together.  The group size follows the mean rows per sequence
+// (so a few draft tokens do not leave waves idle).
+int64_t multi_group(int64_t batch, int64_t num_query_tokens, int64_t group) {
+  const int64_t tr = 16 * pkv::kMultiRowTiles;
+  int64_t g = (num_query_tokens * group + batch * tr - 1) / (batch * tr);
+  return g < 1 ? 1 : (g > pkv::kMultiGroupMax ? pkv::kMultiGroupMax : g);
+}
 int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group) {
-  const int64_t rows = 16 * pkv::kMultiRowTiles;
+  const int64_t rows = 16 * pkv::kMultiRowTiles * multi_group(batch, num_query_tokens, group);
   return (num_query_tokens * group + rows - 1) / rows + batch;
 }
-int64_t multi_items(int64_t vseqs, int64_t num_kv_heads, int64_t max_context_len) {
+int64_t multi_items(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_len) {
   if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
-  return pkv::max_items_bound(vseqs, num_kv_heads, max_context_len, pkv::kMaxSlots);
+  return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
 }
 int64_t vseq_bytes(int64_t vseqs) { return (3 * vseqs * 4 + 255) / 256 * 256; }
 int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim) {
@@ -286,8 +294,10 @@ size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tok
   if (batch <= 0 || num_query_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads || head_dim <= 0 || max_context_len < 0)
     return 0;
-  const int64_t v = multi_vseqs(batch, num_query_tokens, num_q_heads / num_kv_heads);
-  return (size_t)multi_workspace(v, multi_items(v, num_kv_heads, max_context_len), head_dim);
+  const int64_t G = num_q_heads / num_kv_heads;
+  const int64_t v = multi_vseqs(batch, num_query_tokens, G);
+  const int64_t units = num_kv_heads * multi_group(batch, num_query_tokens, G);
+  return (size_t)multi_workspace(v, multi_items(v, units, max_context_len), head_dim);
 }
 
 pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype, int32_t batch,
@@ -336,7 +346,8 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
                 std::string(fn) + ": misaligned pointer (q, out, caches and row scales need 16 B)");
   const int32_t G = num_q_heads / num_kv_heads;
   const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G);
-  const int64_t items = multi_items(vseqs, num_kv_heads, max_context_len);
+  const int32_t wg = (int32_t)multi_group(batch, num_query_tokens, G);
+  const int64_t items = multi_items(vseqs, (int64_t)num_kv_heads * wg, max_context_len);
   if (vseqs > 0x7FFFFFF0 || items > 0x7FFFFFF0)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": query rows x heads x context too large");
   const size_t need = (size_t)multi_workspace(vseqs, items, head_dim);
@@ -362,7 +373,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.batch = (int32_t)vseqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
-  a.head_tiles = 1;
+  a.head_tiles = wg;   // row tiles (waves) per virtual sequence
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.ctx_cap = max_context_len;

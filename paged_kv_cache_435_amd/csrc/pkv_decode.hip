@@ -48,6 +48,7 @@
 //   PKV_STAGES_I8           pipeline depth (tiles in flight), INT8 KV
 //   PKV_STAGES_FP8          pipeline depth (tiles in flight), FP8 KV
 //   PKV_STAGES_I4           pipeline depth (tiles in flight), INT4 KV
+//   PKV_STAGES_MULTI        pipeline depth (tiles in flight), multi-token calls
 //   PKV_WAVES_PER_EU_I4     occupancy target, INT4 KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
@@ -75,6 +76,9 @@
 #endif
 #ifndef PKV_STAGES_I4
 #define PKV_STAGES_I4 2
+#endif
+#ifndef PKV_STAGES_MULTI
+#define PKV_STAGES_MULTI 1
 #endif
 #ifndef PKV_WAVES_PER_EU_I4
 #define PKV_WAVES_PER_EU_I4 4
@@ -428,7 +432,7 @@ struct Tuning {
 // a.context_lens holds those lengths and a.vseq_b / a.vseq_rt say which
 // sequence and row tile each is (written by multi_prep_kernel).
 template <int KV, int QT, int D, int BS, bool MULTI>
-__global__ __launch_bounds__(64)
+__global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64)
 __attribute__((amdgpu_waves_per_eu(MULTI ? 2 : Tuning<KV>::waves_per_eu)))   // (32 rows: 2 waves/SIMD)
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
@@ -445,16 +449,22 @@ void decode_partition_kernel(DecodeArgs a) {
   // rows (each loaded K/V tile then serves twice the rows).
   constexpr int RT = MULTI ? kMultiRowTiles : 1;
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
   const int r16 = lane & 15;   // MFMA row/column index of this lane
   const int c16 = lane >> 4;   // MFMA k-group of this lane
 
   // ---- which item: contiguous item ranges per XCD (workgroups go round-robin
-  // over the 8 XCDs, so blockIdx % 8 is the XCD) ----
+  // over the 8 XCDs, so blockIdx % 8 is the XCD).  A multi-token workgroup is
+  // head_tiles waves taking aligned consecutive items: the row tiles of one
+  // (virtual sequence, KV head, chunk), which read the same K/V tiles in step,
+  // so the copies after the first come from the CU's caches. ----
+  const int wpg = MULTI ? a.head_tiles : 1;           // waves per workgroup
   const Plan plan = make_plan(a, lane);
-  const int64_t per_xcd = (plan.items + 7) / 8;
+  const int64_t groups = (plan.items + wpg - 1) / wpg;
+  const int64_t per_xcd = (groups + 7) / 8;
   const int64_t slot_in_xcd = blockIdx.x / 8;
-  const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + slot_in_xcd;
+  const int64_t item =
+      ((int64_t)(blockIdx.x % 8) * per_xcd + slot_in_xcd) * wpg + (threadIdx.x >> 6);
   if (slot_in_xcd >= per_xcd || item >= plan.items) return;
   int b;
   SeqItems sq;
@@ -491,15 +501,17 @@ void decode_partition_kernel(DecodeArgs a) {
     const int L = uni(a.query_start[bq + 1]) - q0;
     int cr = a.real_ctx[bq];
     cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
+    const int row0 = (a.head_tiles * rt + ht) * 16 * RT;   // first row of this wave
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      const int rho = 16 * RT * rt + 16 * k + r16;   // row = query token * G + head
+      const int rho = row0 + 16 * k + r16;             // row = query token * G + head
       const int j = rho / G;
       head_ok[k] = rho < L * G && q0 + j < a.q_rows;
       hq[k] = (int64_t)(q0 + j) * a.num_q_heads + g * G + rho % G;
       prow[k] = cr - L + j;
     }
-    p_min = cr - L + (16 * RT * rt) / G;
+    p_min = cr - L + row0 / G;
+    if (__builtin_amdgcn_ballot_w64(head_ok[0]) == 0) return;   // a row tile past the rows
   } else {
     const int h_first = g * G + ht * 16;             // first query head of this tile
     int nh = G - ht * 16;
@@ -915,7 +927,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // the bytes of 16-bit ones, so they keep twice as many in flight.  The
   // steady state has no branch around the loads (a load issued on one path
   // only would make the wait counts conservative); a short tail follows.
-  constexpr int S = Tuning<KV>::stages;
+  constexpr int S = MULTI ? PKV_STAGES_MULTI : Tuning<KV>::stages;
   u32x4 kr[S][NL], vr[S][NL];
   float ks[S], vs[S];
   int ph[S];   // physical block of the tile in each register set (-1: skipped)
@@ -1075,7 +1087,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 constexpr int kMergeWaves = 8;
 template <int QT, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
-  constexpr int ROWS = 16 * kMultiRowTiles;   // rows of a virtual sequence
+  const int TR = 16 * kMultiRowTiles;         // rows of a wave's tile
+  const int ROWS = TR * a.head_tiles;         // rows of a virtual sequence
   const int v = blockIdx.x;
   const int g = blockIdx.y;
   const int wave = threadIdx.x / kWave;
@@ -1104,10 +1117,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int64_t first = a.ws_seq[2 * v];
   const int m = (int)a.ws_seq[2 * v + 1];
   if (m <= 1) return;
-  // head_tiles is 1: chunk c of KV head g is item first + g*m + c.
-  if (first + (int64_t)g * m + m - 1 >= a.max_items) return;
+  // chunk c of KV head g, row tile ht: item first + (g*m + c)*head_tiles + ht,
+  // rows item*TR ..
+  if (first + ((int64_t)g * m + m) * a.head_tiles - 1 >= a.max_items) return;
   for (int r = wave; r < rows; r += kMergeWaves)
-    merge_row<QT, D>(a, (first + (int64_t)g * m) * ROWS + r, ROWS, m, out_row(r), lane);
+    merge_row<QT, D>(a, (first + (int64_t)g * m * a.head_tiles + r / TR) * TR + r % TR,
+                     (int64_t)a.head_tiles * TR, m, out_row(r), lane);
 }
 
 // Virtual sequences of a multi-token call (one workgroup): sequence b's
@@ -1130,7 +1145,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       L = a.query_start[b + 1] - a.query_start[b];
       L = L < 0 ? 0 : L;
     }
-    constexpr int ROWS = 16 * kMultiRowTiles;
+    const int ROWS = 16 * kMultiRowTiles * a.head_tiles;   // rows of a virtual sequence
     const int n = (L * G + ROWS - 1) / ROWS;
     scan[t] = n;
     __syncthreads();
@@ -1155,7 +1170,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       const int Lb = a.query_start[bb + 1] - a.query_start[bb];
       int ctx = a.real_ctx[bb];
       ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-      int last = 16 * kMultiRowTiles * rt + 16 * kMultiRowTiles - 1;
+      const int ROWS = 16 * kMultiRowTiles * a.head_tiles;
+      int last = ROWS * rt + ROWS - 1;
       last = last < Lb * G - 1 ? last : Lb * G - 1;
       const int c = ctx - Lb + last / G + 1;
       vctx[v] = c < 0 ? 0 : c;
@@ -1169,7 +1185,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   for (int v = carry + t; v < a.batch; v += 1024) {
     vctx[v] = 0;
     a.vseq_b[v] = 0;
-    a.vseq_rt[v] = 0x03FFFFFF;   // no rows (32 * rt stays below 2^31)
+    a.vseq_rt[v] = 0x00FFFFFF;   // no rows (128 * rt stays below 2^31)
   }
 }
 
@@ -1213,19 +1229,21 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   const int target = slots_per_cu_override() > 0 ? slots_per_cu_override()
                                                  : Tuning<KV>::slots_per_cu;
   if (target < per_cu) per_cu = target;
+  if (MULTI && per_cu > a.head_tiles) per_cu = per_cu / a.head_tiles * a.head_tiles;   // whole workgroups
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.num_kv_heads * a.head_tiles;
   // The workspace was sized for kMaxSlots; fewer slots never need more items.
   const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
-  const int64_t grid = (need + 7) / 8 * 8;
+  const int wpg = MULTI ? a.head_tiles : 1;
+  const int64_t grid = ((need + wpg - 1) / wpg + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if constexpr (MULTI) {
     hipLaunchKernelGGL(multi_prep_kernel, dim3(1), dim3(1024), 0, st, a, ml.batch_real, ml.vctx);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * wpg), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MULTI)

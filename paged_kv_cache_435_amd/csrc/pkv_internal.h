@@ -18,8 +18,10 @@ constexpr int kItemTilesMax = 256;   // 4096 tokens: 4 block-table registers per
 constexpr int kWavesPerCuCap = 16;   // at most 4 waves per SIMD are planned for
 constexpr int kMaxCus = 256;         // MI355X; plans never use more slots than this many CUs give
 constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
-// Multi-token calls: 16-row tiles of (query token, head) rows per wave.
+// Multi-token calls: 16-row tiles of (query token, head) rows per wave, and
+// at most this many waves (32-row tiles) per workgroup.
 constexpr int kMultiRowTiles = 2;
+constexpr int kMultiGroupMax = 4;
 
 // Everything the decode kernels read, passed by value.
 struct DecodeArgs {
