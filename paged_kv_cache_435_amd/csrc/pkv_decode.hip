@@ -33,6 +33,13 @@
 //  * Tokens past the context are selected out of the softmax (never
 //    multiplied), and their V values are masked to zero, so stale or NaN bytes
 //    in unused slots never reach the sums.
+//  * Several query tokens per sequence (prompt chunks, draft verification) use
+//    the same kernel with MULTI set: a wave takes 32 rows of (query token, head
+//    of the group), each lane masking tokens past its row's causal position,
+//    and up to four such waves of one (sequence, KV head, chunk) form a
+//    workgroup.  multi_prep_kernel turns each sequence's rows into "virtual
+//    sequences" whose contexts end at their last row's position, so the planner
+//    and the merge above work unchanged.
 #include <stdlib.h>
 
 #include <atomic>
@@ -412,7 +419,9 @@ __device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
 // roughly 14-16 MB outstanding over the chip: 16-bit and f32 KV (8 KB tiles)
 // run without prefetch at 8 waves per CU; FP8 (4 KB tiles) keeps two tiles in
 // flight at 8 waves per CU; INT8, whose tiles carry more vector work (row
-// scales), runs without prefetch at 16 waves per CU.
+// scales), runs without prefetch at 16 waves per CU; INT4 (2 KB tiles, vector
+// bound) keeps two tiles in flight at 16 waves per CU.  Multi-token calls
+// (32 rows per wave, ~170 VGPRs) run at 2 waves per SIMD without prefetch.
 template <int KV>
 struct Tuning {
   static constexpr int stages =
