@@ -27,7 +27,7 @@ def _queries(w, q_lens, seed=41):
     return torch.randn(T, w.num_q_heads, w.head_dim, generator=g).to(w.q_dtype)
 
 
-def run_multi(w, q_lens, seqs_check=None, what=""):
+def run_multi(w, q_lens, seqs_check=None, what="", rows_of=None):
     q_lens = np.asarray(q_lens, dtype=np.int64)
     say(f"[multi] {what or w.name} fmt={w.kv_format} q={w.q_dtype} B={w.batch} "
         f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} bs={w.block_size} "
@@ -42,20 +42,32 @@ def run_multi(w, q_lens, seqs_check=None, what=""):
                                     kv_dtype=case.kv_dtype)
     torch.cuda.synchronize()
     got = out.float().cpu().numpy().astype(np.float64)
-    side = OracleSide(w, case)       # all sequences, compact pool
-    rows = None
+    side = OracleSide(w, case, seqs_check)   # the checked sequences (all by default), compact pool
     if seqs_check is not None:
-        rows = [(r, h) for b in seqs_check for r in range(starts[b], starts[b + 1])
-                for h in range(w.num_q_heads)]
+        pick = rows_of or (lambda b: range(starts[b], starts[b + 1]))
+        rows = [(r, h) for b in seqs_check for r in pick(b) for h in range(w.num_q_heads)]
+        keep = sorted(int(b) for b in seqs_check)
+        q_lens_o = q_lens[keep]
+        starts_o = np.concatenate([[0], np.cumsum(q_lens_o)])
+        q_o = np.concatenate([widen32(q[starts[b]:starts[b + 1]]) for b in keep]).astype(np.float64)
+        remap = {}
+        for i, b in enumerate(keep):
+            for j in range(int(q_lens[b])):
+                remap[int(starts[b]) + j] = int(starts_o[i]) + j
+        rows_o = [(remap[r], h) for r, h in rows]
+        ref_o = oracle.multi_query_attention(q_o, q_lens_o, side.k_cache, side.v_cache, side.tables,
+                                             side.context_lens, w.scale, w.block_size,
+                                             w.kv_format, side.k_scale, side.v_scale, rows=rows_o)
+        idx = sorted({r for r, _ in rows})
+        ref = np.full_like(got, np.nan)
+        for r in idx:
+            ref[r] = ref_o[remap[r]]
+        compare(got[idx], ref[idx], w.kv_format, what or w.name)
+        return got, case, q, starts
     ref = oracle.multi_query_attention(widen32(q).astype(np.float64), q_lens, side.k_cache,
                                        side.v_cache, side.tables, side.context_lens, w.scale,
-                                       w.block_size, w.kv_format, side.k_scale, side.v_scale,
-                                       rows=rows)
-    if rows is not None:
-        idx = np.array([r for r, _ in rows[::w.num_q_heads]])
-        compare(got[idx], ref[idx], w.kv_format, what or w.name)
-    else:
-        compare(got, ref, w.kv_format, what or w.name)
+                                       w.block_size, w.kv_format, side.k_scale, side.v_scale)
+    compare(got, ref, w.kv_format, what or w.name)
     return got, case, q, starts
 
 
@@ -114,3 +126,20 @@ def test_workspace_too_small_raises():
         pkv.paged_attention_multi_query(torch.empty_like(q), q, starts, case.k_cache, case.v_cache,
                                         case.block_tables, case.context_lens, w.scale,
                                         w.max_context_len, workspace=tiny)
+
+
+@pytest.mark.parametrize("name", W.MULTI_NAMES)
+def test_benchmark_workloads_sampled(name):
+    """The benchmark's multi-token workloads at full size, in the configuration
+    it times: the shortest and longest sequence plus one more, every query
+    token of a verification step, and the first, middle and last rows of each
+    512-token chunk, every query head."""
+    w, q_lens = W.make_multi(name)
+    ctx = w.context_lens
+    seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 3})
+    if name == "llama70b_prefill512":
+        starts = np.concatenate([[0], np.cumsum(q_lens)])
+        pick = lambda b: [int(starts[b]), int(starts[b]) + 255, int(starts[b + 1]) - 1]
+        run_multi(w, q_lens, seqs_check=seqs, rows_of=pick)
+    else:
+        run_multi(w, q_lens, seqs_check=seqs)
