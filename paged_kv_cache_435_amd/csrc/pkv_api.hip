@@ -82,15 +82,15 @@ int64_t multi_group(int64_t batch, int64_t num_query_tokens, int64_t group) {
   int64_t g = (num_query_tokens * group + batch * tr - 1) / (batch * tr);
   return g < 1 ? 1 : (g > pkv::kMultiGroupMax ? pkv::kMultiGroupMax : g);
 }
-int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group) {
+int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group, int64_t kv_heads) {
   const int64_t rows = 16 * pkv::kMultiRowTiles * multi_group(batch, num_query_tokens, group);
-  return (num_query_tokens * group + rows - 1) / rows + batch;
+  return kv_heads * ((num_query_tokens * group + rows - 1) / rows + batch);
 }
 int64_t multi_items(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_len) {
   if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
   return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
 }
-int64_t vseq_bytes(int64_t vseqs) { return (3 * vseqs * 4 + 255) / 256 * 256; }
+int64_t vseq_bytes(int64_t vseqs) { return (4 * vseqs * 4 + 255) / 256 * 256; }
 int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim) {
   return vseq_bytes(vseqs) +
          (items > 0 ? seq_bytes(vseqs) + items * pkv::kMultiRowTiles * row_bytes(head_dim) : 0);
@@ -270,6 +270,7 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_tiles = head_tiles;
+  a.plan_heads = num_kv_heads;
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.ctx_cap = max_context_len;
@@ -295,8 +296,8 @@ size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tok
       num_q_heads % num_kv_heads || head_dim <= 0 || max_context_len < 0)
     return 0;
   const int64_t G = num_q_heads / num_kv_heads;
-  const int64_t v = multi_vseqs(batch, num_query_tokens, G);
-  const int64_t units = num_kv_heads * multi_group(batch, num_query_tokens, G);
+  const int64_t v = multi_vseqs(batch, num_query_tokens, G, num_kv_heads);
+  const int64_t units = multi_group(batch, num_query_tokens, G);
   return (size_t)multi_workspace(v, multi_items(v, units, max_context_len), head_dim);
 }
 
@@ -345,9 +346,9 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
     return fail(PKV_ERR_INVALID_ARG,
                 std::string(fn) + ": misaligned pointer (q, out, caches and row scales need 16 B)");
   const int32_t G = num_q_heads / num_kv_heads;
-  const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G);
+  const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G, num_kv_heads);
   const int32_t wg = (int32_t)multi_group(batch, num_query_tokens, G);
-  const int64_t items = multi_items(vseqs, (int64_t)num_kv_heads * wg, max_context_len);
+  const int64_t items = multi_items(vseqs, wg, max_context_len);
   if (vseqs > 0x7FFFFFF0 || items > 0x7FFFFFF0)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": query rows x heads x context too large");
   const size_t need = (size_t)multi_workspace(vseqs, items, head_dim);
@@ -374,6 +375,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_tiles = wg;   // row tiles (waves) per virtual sequence
+  a.plan_heads = 1;    // a virtual sequence is one KV head
   a.num_blocks = num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.ctx_cap = max_context_len;
@@ -381,6 +383,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.scale = scale;
   a.vseq_b = vctx + vseqs;
   a.vseq_rt = vctx + 2 * vseqs;
+  a.vseq_g = vctx + 3 * vseqs;
   a.query_start = query_start;
   a.real_ctx = context_lens;
   a.q_rows = num_query_tokens;

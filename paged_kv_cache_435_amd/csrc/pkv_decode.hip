@@ -321,7 +321,7 @@ __device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqTil
                                                int lane) {
   int64_t items = 0;
   for (int c = 0; 64 * c < a.batch; ++c) items += (st.get(a, c, lane) + tpi - 1) / tpi;
-  return uni64(wave_sum_i64(items) * ((int64_t)a.num_kv_heads * a.head_tiles));
+  return uni64(wave_sum_i64(items) * ((int64_t)a.plan_heads * a.head_tiles));
 }
 
 // Tiles per item: about (total tiles) / (slots - units), so that one round of
@@ -338,7 +338,7 @@ __device__ Plan make_plan(const DecodeArgs& a, int lane) {
     tiles += n;
     live += n > 0;
   }
-  const int64_t ups = (int64_t)a.num_kv_heads * a.head_tiles;
+  const int64_t ups = (int64_t)a.plan_heads * a.head_tiles;
   tiles = uni64(wave_sum_i64(tiles) * ups);
   live = uni64(wave_sum_i64(live) * ups);
   int64_t se = slots - live;
@@ -367,7 +367,7 @@ struct SeqItems {
 // The sequence holding item q (found = false if q is past the last item).
 __device__ bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int lane,
                             int& b_out, SeqItems& s) {
-  const int64_t units_per_seq = (int64_t)a.num_kv_heads * a.head_tiles;
+  const int64_t units_per_seq = (int64_t)a.plan_heads * a.head_tiles;
   int64_t base = 0;
   for (int b0 = 0; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
@@ -481,7 +481,7 @@ void decode_partition_kernel(DecodeArgs a) {
   b = uni(b);
   const int local = uni((int)(item - sq.first));   // < m * units per sequence
   const int per_g = sq.m * a.head_tiles;
-  const int g = uni(local / per_g);
+  const int g = MULTI ? uni(a.vseq_g[b]) : uni(local / per_g);
   const int chunk = uni((local % per_g) / a.head_tiles);
   const int ht = uni(local % a.head_tiles);
   const int ctx = uni(sq.ctx);
@@ -1088,9 +1088,9 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
                    (int64_t)a.head_tiles * 16, m, hq, lane);
 }
 
-// Several query tokens per sequence: one workgroup of 8 waves per (virtual
-// sequence, KV head), i.e. per 32-row tile of (query token, head) rows, each
-// wave merging every 8th row; rows of a virtual sequence with no context (rows
+// Several query tokens per sequence: one workgroup of 8 waves per virtual
+// sequence (sequence, KV head, group of 32-row tiles of (query token, head)
+// rows), each wave merging every 8th row; rows of a virtual sequence with no context (rows
 // before the cache) get zeros.  A unit that was one item (the common case for
 // prompt chunks) costs one read of its record.
 constexpr int kMergeWaves = 8;
@@ -1099,7 +1099,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int TR = 16 * kMultiRowTiles;         // rows of a wave's tile
   const int ROWS = TR * a.head_tiles;         // rows of a virtual sequence
   const int v = blockIdx.x;
-  const int g = blockIdx.y;
+  const int g = a.vseq_g[v];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int G = a.num_q_heads / a.num_kv_heads;
@@ -1126,17 +1126,18 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int64_t first = a.ws_seq[2 * v];
   const int m = (int)a.ws_seq[2 * v + 1];
   if (m <= 1) return;
-  // chunk c of KV head g, row tile ht: item first + (g*m + c)*head_tiles + ht,
-  // rows item*TR ..
-  if (first + ((int64_t)g * m + m) * a.head_tiles - 1 >= a.max_items) return;
+  // (one KV head per virtual sequence) chunk c, row tile ht: item
+  // first + c*head_tiles + ht, rows item*TR ..
+  if (first + (int64_t)m * a.head_tiles - 1 >= a.max_items) return;
   for (int r = wave; r < rows; r += kMergeWaves)
-    merge_row<QT, D>(a, (first + (int64_t)g * m * a.head_tiles + r / TR) * TR + r % TR,
-                     (int64_t)a.head_tiles * TR, m, out_row(r), lane);
+    merge_row<QT, D>(a, (first + r / TR) * TR + r % TR, (int64_t)a.head_tiles * TR, m, out_row(r),
+                     lane);
 }
 
-// Virtual sequences of a multi-token call (one workgroup): sequence b's
-// ceil(L_b G / 32) row tiles, in order, each with the context its last row may
-// see; entries past the last are padding with no context.  Sequences go 1024
+// Virtual sequences of a multi-token call (one workgroup): for sequence b, each
+// KV head (head-major, so the workgroups running together on an XCD share one
+// head's K/V in its L2) times each group of row tiles, with the context the
+// group's last row may see; entries past the last are padding with no context.  Sequences go 1024
 // at a time: a block scan gives each its first entry, then every thread fills
 // entries, finding its sequence by binary search over the scan.
 __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batch_real,
@@ -1155,7 +1156,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       L = L < 0 ? 0 : L;
     }
     const int ROWS = 16 * kMultiRowTiles * a.head_tiles;   // rows of a virtual sequence
-    const int n = (L * G + ROWS - 1) / ROWS;
+    const int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
     scan[t] = n;
     __syncthreads();
     for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
@@ -1175,8 +1176,12 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
         if (scan[mid] > e) hi = mid; else lo = mid + 1;
       }
       const int bb = b0 + lo;
-      const int rt = e - (lo > 0 ? scan[lo - 1] : 0);
       const int Lb = a.query_start[bb + 1] - a.query_start[bb];
+      const int ng = ((Lb < 0 ? 0 : Lb) * G + 16 * kMultiRowTiles * a.head_tiles - 1) /
+                     (16 * kMultiRowTiles * a.head_tiles);   // row groups of the sequence
+      const int local = e - (lo > 0 ? scan[lo - 1] : 0);   // KV head major, then row group
+      const int gg = local / ng;
+      const int rt = local % ng;
       int ctx = a.real_ctx[bb];
       ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
       const int ROWS = 16 * kMultiRowTiles * a.head_tiles;
@@ -1186,6 +1191,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       vctx[v] = c < 0 ? 0 : c;
       a.vseq_b[v] = bb;
       a.vseq_rt[v] = rt;
+      a.vseq_g[v] = gg;
     }
     __syncthreads();
     if (t == 0) carry = base + total;
@@ -1195,6 +1201,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     vctx[v] = 0;
     a.vseq_b[v] = 0;
     a.vseq_rt[v] = 0x00FFFFFF;   // no rows (128 * rt stays below 2^31)
+    a.vseq_g[v] = 0;
   }
 }
 
@@ -1241,7 +1248,7 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   if (MULTI && per_cu > a.head_tiles) per_cu = per_cu / a.head_tiles * a.head_tiles;   // whole workgroups
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
-  const int64_t units = (int64_t)a.num_kv_heads * a.head_tiles;
+  const int64_t units = (int64_t)a.plan_heads * a.head_tiles;
   // The workspace was sized for kMaxSlots; fewer slots never need more items.
   const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
   const int wpg = MULTI ? a.head_tiles : 1;
@@ -1256,7 +1263,7 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (MULTI)
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, a.num_kv_heads),
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch),
                        dim3(64 * kMergeWaves), 0, st, a);
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,

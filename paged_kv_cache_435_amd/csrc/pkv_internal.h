@@ -40,6 +40,8 @@ struct DecodeArgs {
   int32_t num_q_heads;
   int32_t num_kv_heads;
   int32_t head_tiles;          // ceil(G / 16): query heads of a group are taken 16 at a time
+                               // (multi: row tiles per virtual sequence)
+  int32_t plan_heads;          // KV heads per planned sequence: num_kv_heads (multi: 1)
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
@@ -49,7 +51,8 @@ struct DecodeArgs {
   // Several query tokens per sequence (multi-query calls only; batch is then
   // the number of virtual sequences and context_lens their lengths).
   int32_t* vseq_b;             // real sequence of each virtual sequence
-  int32_t* vseq_rt;            // its 16-row tile of (query token, head) rows
+  int32_t* vseq_rt;            // its group of row tiles of (query token, head) rows
+  int32_t* vseq_g;             // its KV head
   const int32_t* query_start;  // [real batch + 1]: first query row of each sequence
   const int32_t* real_ctx;     // context_lens of the real sequences
   int32_t q_rows;              // query rows (tokens) in q and out
