@@ -357,6 +357,8 @@ __device__ Plan make_plan(const DecodeArgs& a, int lane) {
 // Items of a sequence are numbered g-major, then by chunk, then by head tile:
 // item = first + (g * m + c) * head_tiles + ht, with m = ceil(n / tpi) chunks of
 // the sequence's n tiles per unit; chunk c covers tiles [c*n/m, (c+1)*n/m).
+// (g runs over plan_heads KV heads: all of them for decode, one for a
+// multi-token virtual sequence, which carries its own.)
 struct SeqItems {
   int64_t first;   // number of the sequence's first item
   int ctx;         // clamped context length
@@ -436,10 +438,12 @@ struct Tuning {
 };
 
 // MULTI: several query tokens per sequence (causal).  The planner then works
-// on virtual sequences, one per 16-row tile of a sequence's (query token,
-// head of the group) rows, whose context ends at the tile's last causal limit;
-// a.context_lens holds those lengths and a.vseq_b / a.vseq_rt say which
-// sequence and row tile each is (written by multi_prep_kernel).
+// on virtual sequences, one per (sequence, KV head, group of head_tiles 32-row
+// tiles of (query token, head of the group) rows), whose context ends at the
+// group's last causal limit; a.context_lens holds those lengths and a.vseq_b /
+// a.vseq_g / a.vseq_rt say which sequence, KV head and row group each is
+// (written by multi_prep_kernel).  A wave takes one 32-row tile; the
+// head_tiles waves of a group form one workgroup.
 template <int KV, int QT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64)
 __attribute__((amdgpu_waves_per_eu(MULTI ? 2 : Tuning<KV>::waves_per_eu)))   // (32 rows: 2 waves/SIMD)
