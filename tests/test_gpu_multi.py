@@ -143,3 +143,10 @@ def test_benchmark_workloads_sampled(name):
         run_multi(w, q_lens, seqs_check=seqs, rows_of=pick)
     else:
         run_multi(w, q_lens, seqs_check=seqs)
+
+
+def test_sequences_without_new_tokens_are_skipped():
+    """Zero new tokens for some sequences (they contribute no rows), the others
+    ragged, on an INT8 cache."""
+    w = W.custom(torch.float16, "i8", [500, 90, 1200, 33, 700], 16, 4, 128, 16, name="L0")
+    run_multi(w, [0, 7, 0, 33, 1])
