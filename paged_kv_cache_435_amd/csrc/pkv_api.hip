@@ -346,6 +346,8 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
     return fail(PKV_ERR_INVALID_ARG,
                 std::string(fn) + ": misaligned pointer (q, out, caches and row scales need 16 B)");
   const int32_t G = num_q_heads / num_kv_heads;
+  if ((int64_t)num_query_tokens * G > 0x7FFFF000)   // rows are counted in 32 bits on the device
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": num_query_tokens x group too large");
   const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G, num_kv_heads);
   const int32_t wg = (int32_t)multi_group(batch, num_query_tokens, G);
   const int64_t items = multi_items(vseqs, wg, max_context_len);

@@ -56,6 +56,7 @@
 //   PKV_STAGES_FP8          pipeline depth (tiles in flight), FP8 KV
 //   PKV_STAGES_I4           pipeline depth (tiles in flight), INT4 KV
 //   PKV_STAGES_MULTI        pipeline depth (tiles in flight), multi-token calls
+//   PKV_MULTI_WAVES_PER_EU  occupancy target, multi-token calls
 //   PKV_WAVES_PER_EU_I4     occupancy target, INT4 KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
@@ -86,6 +87,9 @@
 #endif
 #ifndef PKV_STAGES_MULTI
 #define PKV_STAGES_MULTI 1
+#endif
+#ifndef PKV_MULTI_WAVES_PER_EU
+#define PKV_MULTI_WAVES_PER_EU 2
 #endif
 #ifndef PKV_WAVES_PER_EU_I4
 #define PKV_WAVES_PER_EU_I4 4
@@ -446,7 +450,7 @@ struct Tuning {
 // head_tiles waves of a group form one workgroup.
 template <int KV, int QT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64)
-__attribute__((amdgpu_waves_per_eu(MULTI ? 2 : Tuning<KV>::waves_per_eu)))   // (32 rows: 2 waves/SIMD)
+__attribute__((amdgpu_waves_per_eu(MULTI ? PKV_MULTI_WAVES_PER_EU : Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
   constexpr int eb = dtype_bytes(KV);  // (INT4: handled apart wherever it matters)
@@ -509,6 +513,7 @@ void decode_partition_kernel(DecodeArgs a) {
   int bq = b;                 // the real sequence (block table row)
   if constexpr (MULTI) {
     bq = uni(a.vseq_b[b]);
+    if (bq < 0) return;                                // padding (never planned: no context)
     const int rt = uni(a.vseq_rt[b]);
     const int q0 = uni(a.query_start[bq]);
     const int L = uni(a.query_start[bq + 1]) - q0;
@@ -1108,18 +1113,19 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int lane = threadIdx.x % kWave;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int bq = a.vseq_b[v];
-  const int rt = a.vseq_rt[v];
+  if (bq < 0) return;                 // a padding entry
+  const int64_t row0 = (int64_t)ROWS * a.vseq_rt[v];   // first row of this virtual sequence
   const int q0 = a.query_start[bq];
   const int L = a.query_start[bq + 1] - q0;
-  int rows = L * G - ROWS * rt;
+  int64_t rows = (int64_t)L * G - row0;
   rows = rows > ROWS ? ROWS : rows;
   // rows past the query tensor (inconsistent query_start) are never written
-  const int rows_q = (a.q_rows - q0) * G - ROWS * rt;
+  const int64_t rows_q = (int64_t)(a.q_rows - q0) * G - row0;
   rows = rows < rows_q ? rows : rows_q;
-  if (rows <= 0) return;              // a padding entry
+  if (rows <= 0) return;
   auto out_row = [&](int r) -> int64_t {
-    const int rho = ROWS * rt + r;
-    return (int64_t)(q0 + rho / G) * a.num_q_heads + g * G + rho % G;
+    const int64_t rho = row0 + r;
+    return (q0 + rho / G) * a.num_q_heads + g * G + rho % G;
   };
   if (seq_ctx(a, v) == 0) {
     for (int r = wave; r < rows; r += kMergeWaves)
@@ -1203,8 +1209,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   }
   for (int v = carry + t; v < a.batch; v += 1024) {
     vctx[v] = 0;
-    a.vseq_b[v] = 0;
-    a.vseq_rt[v] = 0x00FFFFFF;   // no rows (128 * rt stays below 2^31)
+    a.vseq_b[v] = -1;            // padding: no sequence, no rows
+    a.vseq_rt[v] = 0;
     a.vseq_g[v] = 0;
   }
 }

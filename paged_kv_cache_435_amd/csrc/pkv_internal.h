@@ -20,8 +20,14 @@ constexpr int kMaxCus = 256;         // MI355X; plans never use more slots than 
 constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
 // Multi-token calls: 16-row tiles of (query token, head) rows per wave, and
 // at most this many waves (32-row tiles) per workgroup.
-constexpr int kMultiRowTiles = 2;
-constexpr int kMultiGroupMax = 4;
+#ifndef PKV_MULTI_ROW_TILES
+#define PKV_MULTI_ROW_TILES 2
+#endif
+#ifndef PKV_MULTI_GROUP_MAX
+#define PKV_MULTI_GROUP_MAX 4
+#endif
+constexpr int kMultiRowTiles = PKV_MULTI_ROW_TILES;
+constexpr int kMultiGroupMax = PKV_MULTI_GROUP_MAX;
 
 // Everything the decode kernels read, passed by value.
 struct DecodeArgs {

@@ -131,6 +131,10 @@ def test_multi_query_sizing_and_rejections(lib):
     assert lib.paged_attention_multi_query(*args.values()) == 1
     args.update(query_start=4, num_query_tokens=0)
     assert lib.paged_attention_multi_query(*args.values()) == 0
+    # (query token, head) rows are counted in 32 bits on the device: refused above 2^31 - 4096
+    args.update(num_query_tokens=(0x7FFFF000 // 4) + 1, workspace=16, workspace_bytes=1 << 40)
+    assert lib.paged_attention_multi_query(*args.values()) == 2
+    assert "too large" in lib.pkv_last_error().decode()
 
 
 def test_swap_blocks_checks_pairs_on_the_host(lib):
