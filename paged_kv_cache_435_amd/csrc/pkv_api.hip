@@ -72,28 +72,65 @@ int64_t workspace_items(int64_t batch, int64_t num_q_heads, int64_t num_kv_heads
 // transfers; more take the copy kernel.
 constexpr int32_t kSwapDmaRuns = 32;
 
-// Several query tokens per sequence.  A wave takes a tile of 32 (query token,
-// head) rows; a virtual sequence (the planner's unit of work per KV head) is a
-// group of up to kMultiGroupMax such tiles, run as one workgroup so they read
-// each K/V tile together.  The group size follows the mean rows per sequence
-// (so a few draft tokens do not leave waves idle).
-int64_t multi_group(int64_t batch, int64_t num_query_tokens, int64_t group) {
+// Several query tokens per sequence.  The rows of a KV head, (query token,
+// head of its group), are cut into virtual sequences, the planner's unit of
+// work, each run as one workgroup whose waves read every K/V tile together.
+// Two shapes: prompt chunks (a mean of at least one workgroup's rows per
+// sequence, 16-bit caches read by queries of their type) take the
+// LDS-sharing kernel, kPrefillWaves waves of kPrefillRowTiles 16-row tiles;
+// everything else takes the multi-token decode kernel, whose waves hold
+// kMultiRowTiles tiles and whose group size follows the mean rows per
+// sequence (so a few draft tokens do not leave waves idle).
+struct MultiShape {
+  int64_t row_tiles;   // 16-row tiles per wave
+  int64_t waves;       // waves (row groups) per virtual sequence
+  bool prefill;
+};
+MultiShape multi_shape(int64_t batch, int64_t num_query_tokens, int64_t group, bool prefill_ok) {
+  const int64_t rows = num_query_tokens * group;
+  if (prefill_ok && rows >= batch * 16 * pkv::kPrefillRowTiles * pkv::kPrefillWaves)
+    return MultiShape{pkv::kPrefillRowTiles, pkv::kPrefillWaves, true};
   const int64_t tr = 16 * pkv::kMultiRowTiles;
-  int64_t g = (num_query_tokens * group + batch * tr - 1) / (batch * tr);
-  return g < 1 ? 1 : (g > pkv::kMultiGroupMax ? pkv::kMultiGroupMax : g);
+  int64_t g = (rows + batch * tr - 1) / (batch * tr);
+  g = g < 1 ? 1 : (g > pkv::kMultiGroupMax ? pkv::kMultiGroupMax : g);
+  return MultiShape{pkv::kMultiRowTiles, g, false};
 }
-int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group, int64_t kv_heads) {
-  const int64_t rows = 16 * pkv::kMultiRowTiles * multi_group(batch, num_query_tokens, group);
+bool prefill_types(int32_t q_dtype, int32_t kv_dtype, int32_t head_dim) {
+  return q_dtype == kv_dtype && (q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
+         (head_dim == 64 || head_dim == 128);
+}
+int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group, int64_t kv_heads,
+                    const MultiShape& sh) {
+  const int64_t rows = 16 * sh.row_tiles * sh.waves;
   return kv_heads * ((num_query_tokens * group + rows - 1) / rows + batch);
 }
 int64_t multi_items(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_len) {
   if (max_context_len <= (int64_t)pkv::kItemTilesMin * pkv::kTileTokens) return 0;
   return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
 }
-int64_t vseq_bytes(int64_t vseqs) { return (4 * vseqs * 4 + 255) / 256 * 256; }
-int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim) {
-  return vseq_bytes(vseqs) +
-         (items > 0 ? seq_bytes(vseqs) + items * pkv::kMultiRowTiles * row_bytes(head_dim) : 0);
+// Entries of the item -> virtual sequence map: the most items any plan makes
+// (every unit one item when no context needs cutting).
+int64_t map_entries(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_len) {
+  return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
+}
+// The plan of a call: [items, tiles per item] (2 int64), six int32 per virtual
+// sequence (context, sequence, row group, KV head, first item, items per row
+// tile) and the item map.
+int64_t vseq_bytes(int64_t vseqs, int64_t map_cap) {
+  return (16 + 6 * 4 * vseqs + 4 * map_cap + 255) / 256 * 256;
+}
+// Partial rows of an item: 16 x row tiles, each (max, sum) and head_dim floats.
+int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim, int64_t row_tiles,
+                        int64_t map_cap) {
+  return vseq_bytes(vseqs, map_cap) +
+         (items > 0 ? seq_bytes(vseqs) + items * row_tiles * row_bytes(head_dim) : 0);
+}
+int64_t multi_workspace_of(int64_t batch, int64_t num_query_tokens, int64_t group,
+                           int64_t kv_heads, int64_t head_dim, int64_t max_context_len,
+                           const MultiShape& sh) {
+  const int64_t v = multi_vseqs(batch, num_query_tokens, group, kv_heads, sh);
+  return multi_workspace(v, multi_items(v, sh.waves, max_context_len), head_dim, sh.row_tiles,
+                         map_entries(v, sh.waves, max_context_len));
 }
 
 }  // namespace
@@ -296,9 +333,12 @@ size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tok
       num_q_heads % num_kv_heads || head_dim <= 0 || max_context_len < 0)
     return 0;
   const int64_t G = num_q_heads / num_kv_heads;
-  const int64_t v = multi_vseqs(batch, num_query_tokens, G, num_kv_heads);
-  const int64_t units = multi_group(batch, num_query_tokens, G);
-  return (size_t)multi_workspace(v, multi_items(v, units, max_context_len), head_dim);
+  // (no dtypes here: enough for either shape the call may take)
+  const int64_t a = multi_workspace_of(batch, num_query_tokens, G, num_kv_heads, head_dim,
+                                       max_context_len, multi_shape(batch, num_query_tokens, G, false));
+  const int64_t b = multi_workspace_of(batch, num_query_tokens, G, num_kv_heads, head_dim,
+                                       max_context_len, multi_shape(batch, num_query_tokens, G, true));
+  return (size_t)(a > b ? a : b);
 }
 
 pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype, int32_t batch,
@@ -348,12 +388,15 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   const int32_t G = num_q_heads / num_kv_heads;
   if ((int64_t)num_query_tokens * G > 0x7FFFF000)   // rows are counted in 32 bits on the device
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": num_query_tokens x group too large");
-  const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G, num_kv_heads);
-  const int32_t wg = (int32_t)multi_group(batch, num_query_tokens, G);
+  const MultiShape sh =
+      multi_shape(batch, num_query_tokens, G, prefill_types(q_dtype, kv_dtype, head_dim));
+  const int64_t vseqs = multi_vseqs(batch, num_query_tokens, G, num_kv_heads, sh);
+  const int32_t wg = (int32_t)sh.waves;
   const int64_t items = multi_items(vseqs, wg, max_context_len);
   if (vseqs > 0x7FFFFFF0 || items > 0x7FFFFFF0)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": query rows x heads x context too large");
-  const size_t need = (size_t)multi_workspace(vseqs, items, head_dim);
+  const int64_t map_cap = map_entries(vseqs, wg, max_context_len);
+  const size_t need = (size_t)multi_workspace(vseqs, items, head_dim, sh.row_tiles, map_cap);
   if (!workspace || workspace_bytes < need)
     return fail(PKV_ERR_WORKSPACE, std::string(fn) + ": workspace needs " + std::to_string(need) +
                                        " bytes, got " + std::to_string(workspace_bytes));
@@ -363,7 +406,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   if (cus <= 0) return fail(PKV_ERR_HIP, std::string(fn) + ": cannot query the device");
 
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  int32_t* vctx = reinterpret_cast<int32_t*>(w);
+  int32_t* vctx = reinterpret_cast<int32_t*>(w + 16);
   pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;
@@ -386,18 +429,24 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.vseq_b = vctx + vseqs;
   a.vseq_rt = vctx + 2 * vseqs;
   a.vseq_g = vctx + 3 * vseqs;
+  a.vseq_first = vctx + 4 * vseqs;
+  a.vseq_m = vctx + 5 * vseqs;
+  a.item_vseq = vctx + 6 * vseqs;
+  a.map_cap = map_cap;
+  a.plan_info = reinterpret_cast<int64_t*>(w);
   a.query_start = query_start;
   a.real_ctx = context_lens;
   a.q_rows = num_query_tokens;
+  a.wave_rows = (int32_t)(16 * sh.row_tiles);
   if (items > 0) {
-    uint8_t* rest = w + vseq_bytes(vseqs);
+    uint8_t* rest = w + vseq_bytes(vseqs, map_cap);
     a.ws_seq = reinterpret_cast<int64_t*>(rest);
     a.ws_ml = reinterpret_cast<float*>(rest + seq_bytes(vseqs));
     a.ws_acc = reinterpret_cast<float*>(rest + seq_bytes(vseqs) +
-                                        items * pkv::kMultiRowTiles * 16 * 2 * 4);
+                                        items * sh.row_tiles * 16 * 2 * 4);
   }
   return hip_status(pkv::launch_multi(a, batch, vctx, q_dtype, kv_dtype, head_dim, block_size, cus,
-                                      static_cast<hipStream_t>(stream)),
+                                      sh.prefill, static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -47,6 +47,7 @@
 
 #include "pkv_common.h"
 #include "pkv_internal.h"
+#include "pkv_kernel.h"
 
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_NT_LOADS            KV loads carry the non-temporal hint
@@ -99,303 +100,6 @@
 #endif
 
 namespace pkv {
-
-enum { MT_F32 = 0, MT_F16 = 1, MT_BF16 = 2 };
-
-template <int QT>
-struct MfmaOf {
-  static constexpr int value = QT == PKV_F32 ? MT_F32 : (QT == PKV_F16 ? MT_F16 : MT_BF16);
-};
-
-// ---------------------------------------------------------------------------
-// Stored KV bytes -> MFMA input elements.
-//
-// Each call converts one 16-byte chunk.  For 16-bit MFMA types the result is
-// packed two elements per 32-bit word; for f32 it is one float per word.
-// FP8 -> f16/bf16/f32 uses gfx950's E4M3 conversions (exact).  INT8 -> f16
-// gives offset subnormals (q + 128) 2^-24, corrected after the products.
-// INT4 (8 nibbles per word) takes nibble pairs
-// 16 bits apart, so word w of the output holds nibbles (w, w + 4) of the
-// input word (an order the query operand is loaded in to match): -> f16 as
-// offset subnormals (q + 8) 2^-24 / 2^-20, corrected after the products;
-// -> bf16 exactly, through f32 (2^23 + u - (2^23 + 8)).
-// ---------------------------------------------------------------------------
-template <int KV, int MT>
-struct Cvt {
-  static constexpr int in_elems = 128 / dtype_bits(KV);             // per 16 B chunk
-  static constexpr int out_words = MT == MT_F32 ? in_elems : in_elems / 2;
-  static constexpr int word_out = out_words / 4;                     // outputs per input word
-
-  // One 32-bit word of stored bytes -> word_out MFMA words.
-  __device__ __forceinline__ static void word(const uint32_t raw, uint32_t* w) {
-    if constexpr ((KV == PKV_F16 && MT == MT_F16) || (KV == PKV_BF16 && MT == MT_BF16) ||
-                  (KV == PKV_F32 && MT == MT_F32)) {
-      w[0] = raw;
-    } else if constexpr (KV == PKV_I8 && MT == MT_F16) {
-      // Offset codes as f16 subnormals (q + 128) 2^-24: the bytes of
-      // raw ^ 0x80 moved to the low byte of each half (see OffsetCodes).
-      const uint32_t t = raw ^ 0x80808080u;
-      w[0] = __builtin_amdgcn_perm(0u, t, 0x04010400u);
-      w[1] = __builtin_amdgcn_perm(0u, t, 0x04030402u);
-    } else if constexpr (KV == PKV_I4 && MT == MT_F16) {
-      // Offset codes as f16 subnormals, one bit operation per word:
-      // (raw & mask) ^ 8 puts u ^ 8 = q + 8 (u = the stored two's-complement
-      // nibble) in the low mantissa bits, i.e. (q + 8) 2^-24 for the low nibble
-      // of a byte pair and (q + 8) 2^-20 for the high one.  The kernel takes
-      // the offset and the powers of two back out (see OffsetCodes); the MFMA
-      // multiplies f16 subnormals exactly.
-      const uint32_t x8 = raw >> 8;
-      w[0] = (raw & 0x000F000Fu) ^ 0x00080008u;
-      w[1] = (raw & 0x00F000F0u) ^ 0x00800080u;
-      w[2] = (x8 & 0x000F000Fu) ^ 0x00080008u;
-      w[3] = (x8 & 0x00F000F0u) ^ 0x00800080u;
-    } else if constexpr (KV == PKV_I4 && MT == MT_BF16) {
-      const uint32_t x = raw ^ 0x88888888u;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float lo = bitsf(0x4B000000u | ((x >> (4 * k)) & 0xFu)) - 8388616.0f;
-        const float hi = bitsf(0x4B000000u | ((x >> (4 * k + 16)) & 0xFu)) - 8388616.0f;
-        w[k] = __builtin_amdgcn_perm(fbits(hi), fbits(lo), 0x07060302u);   // exact: truncation
-      }
-    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F16) {
-      // gfx950 converts OCP E4M3 pairs to f16 (exact; scale 1).
-      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, false));
-      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw, 1.0f, true));
-    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_BF16) {
-      w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, false));
-      w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw, 1.0f, true));
-    } else if constexpr (KV == PKV_FP8_E4M3FN && MT == MT_F32) {
-      const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw, 1.0f, false);
-      const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(raw, 1.0f, true);
-      w[0] = fbits(lo[0]);
-      w[1] = fbits(lo[1]);
-      w[2] = fbits(hi[0]);
-      w[3] = fbits(hi[1]);
-    } else {
-      // Generic: through f32 (exact for every pair built here).
-      static_assert(KV != PKV_I4, "INT4 converts to f16 or bf16 only");
-      constexpr int eb = dtype_bytes(KV);
-      constexpr int per = 4 / eb;   // elements in the word
-      float f[per];
-#pragma unroll
-      for (int e = 0; e < per; ++e) {
-        const int sh = e * eb * 8;
-        if constexpr (KV == PKV_I8) {
-          f[e] = (float)(int8_t)((raw >> sh) & 0xFFu);
-        } else if constexpr (KV == PKV_FP8_E4M3FN) {
-          f[e] = e4m3fn_to_f32((raw >> sh) & 0xFFu);
-        } else if constexpr (KV == PKV_F16) {
-          f[e] = f16_to_f32((uint16_t)((raw >> sh) & 0xFFFFu));
-        } else if constexpr (KV == PKV_BF16) {
-          f[e] = bf16_to_f32((uint16_t)((raw >> sh) & 0xFFFFu));
-        } else {
-          f[e] = bitsf(raw);
-        }
-      }
-#pragma unroll
-      for (int o = 0; o < word_out; ++o) {
-        if constexpr (MT == MT_F32) {
-          w[o] = fbits(f[o]);
-        } else if constexpr (MT == MT_F16) {
-          w[o] = (uint32_t)f32_to_f16(f[2 * o]) | ((uint32_t)f32_to_f16(f[2 * o + 1]) << 16);
-        } else {  // bf16: every value converted here is exact in bf16, so truncate
-          w[o] = (fbits(f[2 * o]) >> 16) | (fbits(f[2 * o + 1]) & 0xFFFF0000u);
-        }
-      }
-    }
-  }
-
-  // One 16-byte chunk -> out_words MFMA words.
-  __device__ __forceinline__ static void run(const u32x4 raw, uint32_t* w) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) word(raw[i], w + i * word_out);
-  }
-};
-
-// Extra factor the conversion above leaves in the value (none: every
-// conversion is exact).
-template <int KV, int MT>
-__host__ __device__ constexpr float cvt_gain() {
-  return 1.0f;
-}
-
-// One query element (stored as QT) as an MFMA element (16-bit pattern or f32 bits).
-template <int QT>
-__device__ __forceinline__ uint32_t q_elem(const void* q, int64_t idx) {
-  if constexpr (QT == PKV_F32) {
-    return fbits(static_cast<const float*>(q)[idx]);
-  } else {
-    return static_cast<const uint16_t*>(q)[idx];
-  }
-}
-
-template <int QT>
-__device__ __forceinline__ void store_out4(void* out, int64_t idx, float a, float b, float c,
-                                           float d) {
-  if constexpr (QT == PKV_F32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = f32x4{a, b, c, d};
-  } else if constexpr (QT == PKV_F16) {
-    u32x2 w = {(uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16),
-               (uint32_t)f32_to_f16(c) | ((uint32_t)f32_to_f16(d) << 16)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = w;
-  } else {
-    u32x2 w = {(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
-               (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = w;
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ uint32_t pack_p(float a, float b) {
-  if constexpr (MT == MT_F16) {
-    return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
-  } else {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Work plan (computed identically by every wave of both kernels).
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ int64_t wave_sum_i64(int64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
-}
-
-__device__ __forceinline__ int64_t wave_incl_scan_i64(int64_t v, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int64_t t = __shfl_up(v, o, kWave);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// A wave-uniform value held in VGPRs, moved to SGPRs.
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-__device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), lane);
-  return (int64_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Context length of sequence b, clamped to what the table can address.
-__device__ __forceinline__ int seq_ctx(const DecodeArgs& a, int b) {
-  int c = a.context_lens[b];
-  return c < 0 ? 0 : (c > a.ctx_cap ? a.ctx_cap : c);
-}
-
-struct Plan {
-  int64_t items;   // total work items
-  int tpi;         // tiles per item (a unit of n tiles makes ceil(n / tpi) items)
-};
-
-// Tiles of sequence 64*c + lane (0 past the batch).  The first 256 sequences'
-// counts come from registers filled once; later ones are read again.
-struct SeqTiles {
-  int cached[4];
-  __device__ __forceinline__ void fill(const DecodeArgs& a, int lane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int b = 64 * i + lane;
-      cached[i] = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
-    }
-  }
-  __device__ __forceinline__ int get(const DecodeArgs& a, int c, int lane) const {
-    if (c < 4) {   // uniform selects: the array stays in registers
-      int v = cached[0];
-      v = c == 1 ? cached[1] : v;
-      v = c == 2 ? cached[2] : v;
-      v = c == 3 ? cached[3] : v;
-      return v;
-    }
-    const int b = 64 * c + lane;
-    return b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
-  }
-};
-
-__device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqTiles& st, int tpi,
-                                               int lane) {
-  int64_t items = 0;
-  for (int c = 0; 64 * c < a.batch; ++c) items += (st.get(a, c, lane) + tpi - 1) / tpi;
-  return uni64(wave_sum_i64(items) * ((int64_t)a.plan_heads * a.head_tiles));
-}
-
-// Tiles per item: about (total tiles) / (slots - units), so that one round of
-// items fits the slots even after each unit's count is rounded up; several
-// rounds when an item would pass kItemTilesMax.  (Filling the slots exactly,
-// with more and smaller items, measured slower.)
-__device__ Plan make_plan(const DecodeArgs& a, int lane) {
-  SeqTiles st;
-  st.fill(a, lane);
-  const int64_t slots = a.slots > 0 ? a.slots : 1;
-  int64_t tiles = 0, live = 0;
-  for (int c = 0; 64 * c < a.batch; ++c) {
-    const int n = st.get(a, c, lane);
-    tiles += n;
-    live += n > 0;
-  }
-  const int64_t ups = (int64_t)a.plan_heads * a.head_tiles;
-  tiles = uni64(wave_sum_i64(tiles) * ups);
-  live = uni64(wave_sum_i64(live) * ups);
-  int64_t se = slots - live;
-  if (se < slots / 2) se = slots / 2;
-  if (se < 1) se = 1;
-  int64_t k = (tiles + se * kItemTilesMax - 1) / (se * kItemTilesMax);
-  if (k < 1) k = 1;
-  int64_t t = (tiles + k * se - 1) / (k * se);
-  t = t < kItemTilesMin ? kItemTilesMin : (t > kItemTilesMax ? kItemTilesMax : t);
-  Plan p;
-  p.tpi = (int)t;
-  p.items = count_items(a, st, p.tpi, lane);
-  return p;
-}
-
-// Items of a sequence are numbered g-major, then by chunk, then by head tile:
-// item = first + (g * m + c) * head_tiles + ht, with m = ceil(n / tpi) chunks of
-// the sequence's n tiles per unit; chunk c covers tiles [c*n/m, (c+1)*n/m).
-// (g runs over plan_heads KV heads: all of them for decode, one for a
-// multi-token virtual sequence, which carries its own.)
-struct SeqItems {
-  int64_t first;   // number of the sequence's first item
-  int ctx;         // clamped context length
-  int n;           // tiles
-  int m;           // chunks per unit
-};
-
-// The sequence holding item q (found = false if q is past the last item).
-__device__ bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int lane,
-                            int& b_out, SeqItems& s) {
-  const int64_t units_per_seq = (int64_t)a.plan_heads * a.head_tiles;
-  int64_t base = 0;
-  for (int b0 = 0; b0 < a.batch; b0 += kWave) {
-    const int b = b0 + lane;
-    const int ctx = b < a.batch ? seq_ctx(a, b) : 0;
-    const int n = (ctx + kTileTokens - 1) / kTileTokens;
-    const int m = (n + p.tpi - 1) / p.tpi;
-    const int64_t cnt = (int64_t)m * units_per_seq;
-    const int64_t incl = wave_incl_scan_i64(cnt, lane) + base;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(q >= incl - cnt && q < incl);
-    if (hit) {
-      const int L = __builtin_ctzll(hit);
-      b_out = b0 + L;
-      s.first = readlane_i64(incl - cnt, L);
-      s.ctx = __builtin_amdgcn_readlane(ctx, L);
-      s.n = __builtin_amdgcn_readlane(n, L);
-      s.m = __builtin_amdgcn_readlane(m, L);
-      return true;
-    }
-    base = readlane_i64(incl, kWave - 1);
-  }
-  return false;
-}
 
 // ---------------------------------------------------------------------------
 // Partition kernel.
@@ -476,7 +180,13 @@ void decode_partition_kernel(DecodeArgs a) {
   // (virtual sequence, KV head, chunk), which read the same K/V tiles in step,
   // so the copies after the first come from the CU's caches. ----
   const int wpg = MULTI ? a.head_tiles : 1;           // waves per workgroup
-  const Plan plan = make_plan(a, lane);
+  Plan plan;
+  if constexpr (MULTI) {
+    plan.items = planned_items(a);                    // made by multi_prep_kernel
+    plan.tpi = 0;
+  } else {
+    plan = make_plan(a, lane);
+  }
   const int64_t groups = (plan.items + wpg - 1) / wpg;
   const int64_t per_xcd = (groups + 7) / 8;
   const int64_t slot_in_xcd = blockIdx.x / 8;
@@ -485,7 +195,11 @@ void decode_partition_kernel(DecodeArgs a) {
   if (slot_in_xcd >= per_xcd || item >= plan.items) return;
   int b;
   SeqItems sq;
-  if (!seq_of_item(a, plan, item, lane, b, sq)) return;
+  if constexpr (MULTI) {
+    planned_seq(a, item, b, sq);
+  } else {
+    if (!seq_of_item(a, plan, item, lane, b, sq)) return;
+  }
   b = uni(b);
   const int local = uni((int)(item - sq.first));   // < m * units per sequence
   const int per_g = sq.m * a.head_tiles;
@@ -499,8 +213,9 @@ void decode_partition_kernel(DecodeArgs a) {
   const int ntiles = (t_end - t_begin + 15) >> 4;
   const bool whole_unit = sq.m == 1;
   // The first item of each sequence records where its items start and how
-  // many each unit has, for the merge kernel.
-  if (a.ws_seq && local == 0 && lane == 0) {
+  // many each unit has, for the merge kernel (multi-token calls: done by the
+  // prep kernel).
+  if (!MULTI && a.ws_seq && local == 0 && lane == 0) {
     a.ws_seq[2 * b] = sq.first;
     a.ws_seq[2 * b + 1] = sq.m;
   }
@@ -1105,7 +820,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 constexpr int kMergeWaves = 8;
 template <int QT, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
-  const int TR = 16 * kMultiRowTiles;         // rows of a wave's tile
+  const int TR = a.wave_rows;                 // rows of a wave's tile
   const int ROWS = TR * a.head_tiles;         // rows of a virtual sequence
   const int v = blockIdx.x;
   const int g = a.vseq_g[v];
@@ -1165,7 +880,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       L = a.query_start[b + 1] - a.query_start[b];
       L = L < 0 ? 0 : L;
     }
-    const int ROWS = 16 * kMultiRowTiles * a.head_tiles;   // rows of a virtual sequence
+    const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
     const int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
     scan[t] = n;
     __syncthreads();
@@ -1187,14 +902,14 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
       const int bb = b0 + lo;
       const int Lb = a.query_start[bb + 1] - a.query_start[bb];
-      const int ng = ((Lb < 0 ? 0 : Lb) * G + 16 * kMultiRowTiles * a.head_tiles - 1) /
-                     (16 * kMultiRowTiles * a.head_tiles);   // row groups of the sequence
+      const int ng = ((Lb < 0 ? 0 : Lb) * G + a.wave_rows * a.head_tiles - 1) /
+                     (a.wave_rows * a.head_tiles);   // row groups of the sequence
       const int local = e - (lo > 0 ? scan[lo - 1] : 0);   // KV head major, then row group
       const int gg = local / ng;
       const int rt = local % ng;
       int ctx = a.real_ctx[bb];
       ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
-      const int ROWS = 16 * kMultiRowTiles * a.head_tiles;
+      const int ROWS = a.wave_rows * a.head_tiles;
       int last = ROWS * rt + ROWS - 1;
       last = last < Lb * G - 1 ? last : Lb * G - 1;
       const int c = ctx - Lb + last / G + 1;
@@ -1212,6 +927,67 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     a.vseq_b[v] = -1;            // padding: no sequence, no rows
     a.vseq_rt[v] = 0;
     a.vseq_g[v] = 0;
+  }
+
+  // ---- the plan, once for every kernel of the call: make_plan's rule over
+  // all virtual sequences (one KV head each, head_tiles units), then each
+  // one's items numbered in order and mapped back to it ----
+  __threadfence();
+  __syncthreads();
+  __shared__ int64_t red[2][1024 / kWave];
+  __shared__ int64_t carry_items;
+  const int units = a.head_tiles;
+  int64_t tiles = 0, live = 0;
+  for (int v = t; v < a.batch; v += 1024) {
+    const int n = (seq_ctx(a, v) + kTileTokens - 1) / kTileTokens;
+    tiles += n;
+    live += n > 0;
+  }
+  tiles = wave_sum_i64(tiles);
+  live = wave_sum_i64(live);
+  if ((t & (kWave - 1)) == 0) {
+    red[0][t / kWave] = tiles;
+    red[1][t / kWave] = live;
+  }
+  if (t == 0) carry_items = 0;
+  __syncthreads();
+  tiles = live = 0;
+  for (int w = 0; w < 1024 / kWave; ++w) {
+    tiles += red[0][w];
+    live += red[1][w];
+  }
+  const int tpi = plan_tpi(tiles * units, live * units, a.slots);
+  for (int v0 = 0; v0 < a.batch; v0 += 1024) {
+    const int v = v0 + t;
+    int m = 0;
+    if (v < a.batch) m = ((seq_ctx(a, v) + kTileTokens - 1) / kTileTokens + tpi - 1) / tpi;
+    const int cnt = m * units;
+    scan[t] = cnt;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+      const int x = t >= o ? scan[t - o] : 0;
+      __syncthreads();
+      scan[t] += x;
+      __syncthreads();
+    }
+    if (v < a.batch) {
+      const int64_t first = carry_items + scan[t] - cnt;
+      a.vseq_first[v] = (int32_t)first;
+      a.vseq_m[v] = m;
+      if (a.ws_seq) {
+        a.ws_seq[2 * v] = first;
+        a.ws_seq[2 * v + 1] = m;
+      }
+      for (int i = 0; i < cnt && first + i < a.map_cap; ++i) a.item_vseq[first + i] = v;
+    }
+    __syncthreads();
+    if (t == 0) carry_items += scan[1023];
+    __syncthreads();
+  }
+  if (t == 0) {
+    // (the host sizes the map for the most items any plan makes)
+    a.plan_info[0] = carry_items < a.map_cap ? carry_items : a.map_cap;
+    a.plan_info[1] = tpi;
   }
 }
 
@@ -1327,8 +1103,33 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
                         st);
 }
 
+template <int QT, int D>
+static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vctx, int block_size,
+                                      int num_cus, hipStream_t st) {
+  hipError_t e = launch_prefill(a, QT, D, block_size, num_cus, true, st);   // a.slots
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(multi_prep_kernel, dim3(1), dim3(1024), 0, st, a, batch_real, vctx);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_prefill(a, QT, D, block_size, num_cus, false, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch), dim3(64 * kMergeWaves), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
-                        int head_dim, int block_size, int num_cus, hipStream_t st) {
+                        int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st) {
+  if (prefill) {
+    if (kv_dtype != q_dtype || (q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
+        (head_dim != 64 && head_dim != 128))
+      return hipErrorInvalidValue;
+    if (q_dtype == PKV_F16)
+      return head_dim == 64 ? launch_prefill_call<PKV_F16, 64>(a, batch_real, vctx, block_size, num_cus, st)
+                            : launch_prefill_call<PKV_F16, 128>(a, batch_real, vctx, block_size, num_cus, st);
+    return head_dim == 64 ? launch_prefill_call<PKV_BF16, 64>(a, batch_real, vctx, block_size, num_cus, st)
+                          : launch_prefill_call<PKV_BF16, 128>(a, batch_real, vctx, block_size, num_cus, st);
+  }
+  if (a.wave_rows != 16 * kMultiRowTiles) return hipErrorInvalidValue;
   return launch0<true>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus,
                        MultiLaunch{batch_real, vctx}, st);
 }

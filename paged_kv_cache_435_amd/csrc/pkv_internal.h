@@ -28,6 +28,17 @@ constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
 #endif
 constexpr int kMultiRowTiles = PKV_MULTI_ROW_TILES;
 constexpr int kMultiGroupMax = PKV_MULTI_GROUP_MAX;
+// Prompt chunks (many rows per sequence, 16-bit caches): waves per workgroup
+// of the LDS-sharing kernel and 16-row tiles per wave.  It is used when the
+// mean rows per sequence fill at least one workgroup.
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4
+#endif
+#ifndef PKV_PREFILL_ROW_TILES
+#define PKV_PREFILL_ROW_TILES 2
+#endif
+constexpr int kPrefillWaves = PKV_PREFILL_WAVES;
+constexpr int kPrefillRowTiles = PKV_PREFILL_ROW_TILES;
 
 // Everything the decode kernels read, passed by value.
 struct DecodeArgs {
@@ -62,6 +73,13 @@ struct DecodeArgs {
   const int32_t* query_start;  // [real batch + 1]: first query row of each sequence
   const int32_t* real_ctx;     // context_lens of the real sequences
   int32_t q_rows;              // query rows (tokens) in q and out
+  int32_t wave_rows;           // (query token, head) rows per wave: 16 x row tiles
+  // The plan of a multi-query call, made by its prep kernel.
+  int64_t* plan_info;          // [items, tiles per item]
+  int32_t* vseq_first;         // first item of each virtual sequence
+  int32_t* vseq_m;             // items (chunks of its context) per row tile
+  int32_t* item_vseq;          // virtual sequence of each item
+  int64_t map_cap;             // entries of item_vseq
 };
 
 // Host-side bound on the items a plan can make (grid size and workspace rows).
@@ -81,8 +99,17 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
 
 // Multi-query: a.batch = virtual sequences (upper bound), a.context_lens =
 // vctx (written by the prep kernel first), batch_real real sequences.
+// prefill: the LDS-sharing kernel (a.head_tiles = kPrefillWaves, a.wave_rows =
+// 16 kPrefillRowTiles; 16-bit caches of the query's type), else the
+// multi-token decode kernel (a.wave_rows = 16 kMultiRowTiles).
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
-                        int head_dim, int block_size, int num_cus, hipStream_t st);
+                        int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st);
+
+// The prefill kernel alone (pkv_prefill.hip); launch_multi runs the plan
+// before it and the merge after it.  slots_only: set a.slots (the resident
+// waves the plan is made for) and launch nothing.
+hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int head_dim, int block_size, int num_cus,
+                          bool slots_only, hipStream_t st);
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
                            void* out, float* scale, int scale_given, hipStream_t st);

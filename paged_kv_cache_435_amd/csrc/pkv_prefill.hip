@@ -1,0 +1,462 @@
+// pkv_prefill.hip — causal attention of many new query tokens per sequence
+// over a paged KV cache (prompt chunks), hand-written for gfx950.
+//
+// What is computed is the multi-token form of the paged attention in
+// [P3] «大模型推理加速实战：KV Cache内存优化与PagedAttention分页管理方案»
+// (PagedAttention section: the cache is gathered through the block table and
+// standard attention runs over it), with the causal rule that query token j
+// of a sequence whose cache holds c tokens after the call sees positions
+// 0 .. c - L + j.  Query head h reads KV head h / G ([P1] §3).
+//
+// When a sequence brings hundreds of (query token, head) rows per KV head,
+// the work is a dense contraction: about 64 flop per K/V byte per 64 rows.
+// The design for CDNA4:
+//
+//  * A workgroup of W waves takes W consecutive items of the work plan: the
+//    row tiles of one (virtual sequence, chunk of its context), which read the
+//    same K/V tiles.  Each 32-token step of those tiles is loaded from the
+//    cache once per workgroup (16 bytes per thread and instruction, in the
+//    storage order, which is already the MFMA operand order) into LDS, and
+//    every wave reads it from there: no copy per wave through the caches.
+//    LDS is double-buffered, so the next step's global loads are in flight
+//    while the current one is multiplied; one barrier per step.
+//  * A wave holds RT tiles of 16 rows: Q in registers for the whole item,
+//    S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16} per 16 tokens, online
+//    softmax in the exp2 domain, and O^T += V^T P^T with the same 32-deep MFMA
+//    over the step's two 16-token groups (the K index of the PV product runs
+//    over the lane's four tokens of each group, in the order the QK output
+//    leaves P in the registers).
+//  * Steps that every row of the wave sees whole take an unmasked path; the
+//    rest mask tokens past the context or past a row's causal position, and
+//    zero the V values of slots past the context.
+//  * Items, virtual sequences, the plan (made once per call by the prep
+//    kernel) and the split-K merge are those of the multi-token decode kernel
+//    (pkv_decode.hip): a virtual sequence here is a group of W * RT * 16 rows.
+//
+// 16-bit caches read by queries of the same type (f16/f16, bf16/bf16).
+#include <atomic>
+
+#include "pkv_common.h"
+#include "pkv_internal.h"
+#include "pkv_kernel.h"
+
+// Compile-time tuning knobs (defaults are the shipped configuration):
+//   PKV_PREFILL_WAVES_PER_EU   occupancy target of the prefill kernel
+#ifndef PKV_PREFILL_WAVES_PER_EU
+#define PKV_PREFILL_WAVES_PER_EU 2
+#endif
+
+namespace pkv {
+
+template <int QT, int D, int BS>
+__global__ __launch_bounds__(64 * kPrefillWaves)
+__attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
+void prefill_kernel(DecodeArgs a) {
+  constexpr int MT = MfmaOf<QT>::value;
+  static_assert(MT == MT_F16 || MT == MT_BF16, "16-bit queries and caches");
+  constexpr int W = kPrefillWaves;
+  constexpr int RT = kPrefillRowTiles;
+  constexpr int R = 2 * D;                 // bytes per stored row
+  constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
+  constexpr int NL = R / 64;               // 16-byte reads per lane per group
+  constexpr int KW = 4 * NL;               // K operand words per lane per group (D / 8)
+  constexpr int NC = D / 16;               // 16-wide d chunks of the output
+  constexpr int STEP = 4 * GB;             // K and V of two groups
+  constexpr int NLD = STEP / (16 * 64 * W);   // 16-byte global loads per thread per step
+  static_assert(NLD >= 1 && STEP % (16 * 64 * W) == 0, "step must split evenly over the threads");
+  static_assert((2 * D) % 64 == 0, "a wave's loads stay inside one group");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STEP];   // [K g0][K g1][V g0][V g1]
+
+  const int tid = threadIdx.x;
+  const int wave = uni(tid >> 6);         // (uniform: keeps the load addresses scalar)
+  const int lane = tid & (kWave - 1);
+  const int r16 = lane & 15;
+  const int c16 = lane >> 4;
+
+  // ---- the workgroup's items: W consecutive items of one (virtual
+  // sequence, chunk), one per wave (contiguous ranges per XCD) ----
+  const int64_t items = planned_items(a);   // the plan made by multi_prep_kernel
+  const int64_t groups = (items + W - 1) / W;
+  const int64_t per_xcd = (groups + 7) / 8;
+  const int64_t slot_in_xcd = blockIdx.x / 8;
+  const int64_t item0 = ((int64_t)(blockIdx.x % 8) * per_xcd + slot_in_xcd) * W;
+  if (slot_in_xcd >= per_xcd || item0 >= items) return;        // whole workgroup
+  int b;
+  SeqItems sq;
+  planned_seq(a, item0, b, sq);
+  b = uni(b);
+  const int64_t item = item0 + wave;
+  const int local0 = uni((int)(item0 - sq.first));
+  const int chunk = local0 / W;                                 // (head_tiles == W)
+  const int ctx = uni(sq.ctx);
+  const int t_begin = uni((int)((int64_t)chunk * sq.n / sq.m) * kTileTokens);
+  int t_end = (int)((int64_t)(chunk + 1) * sq.n / sq.m) * kTileTokens;
+  t_end = uni(t_end < ctx ? t_end : ctx);
+  const int ntiles = (t_end - t_begin + 15) >> 4;
+  const int nsteps = (ntiles + 1) >> 1;
+  const bool whole_unit = sq.m == 1;
+  const int bq = uni(a.vseq_b[b]);
+  if (bq < 0) return;                      // padding (never planned: no context)
+  const int g = uni(a.vseq_g[b]);
+  const int rt = uni(a.vseq_rt[b]);
+
+  // ---- this wave's rows: row = query token * G + head of the group ----
+  const int G = a.num_q_heads / a.num_kv_heads;
+  const int q0 = uni(a.query_start[bq]);
+  const int L = uni(a.query_start[bq + 1]) - q0;
+  int cr = a.real_ctx[bq];
+  cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
+  const int row0 = (W * rt + wave) * 16 * RT;
+  bool head_ok[RT];
+  int64_t hq[RT];
+  int prow[RT];                            // last position each of this lane's rows sees
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    const int rho = row0 + 16 * k + r16;
+    const int j = rho / G;
+    head_ok[k] = rho < L * G && q0 + j < a.q_rows;
+    hq[k] = (int64_t)(q0 + j) * a.num_q_heads + g * G + rho % G;
+    prow[k] = cr - L + j;
+  }
+  // A wave whose rows all lie past the sequence's rows still loads its share
+  // of every step and meets every barrier; it skips the products.
+  const bool wave_live = __builtin_amdgcn_ballot_w64(head_ok[0]) != 0;
+  const int p_min = cr - L + row0 / G;     // smallest causal limit of the wave's rows
+  const int full_end = p_min < t_end ? p_min + 1 : t_end;
+  const int nfull = full_end > t_begin ? (full_end - t_begin) >> 4 : 0;   // whole tiles
+
+  // Block-table entries of the item, one per lane per register.
+  constexpr int NREG = (kItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
+  const int first_blk = t_begin / BS;
+  const int nblk = ntiles > 0 ? (t_end - 1) / BS - first_blk + 1 : 0;
+  int blk[NREG];
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) {
+    const int idx = r * 64 + lane;
+    int v = -1;
+    if (idx < nblk) v = a.block_tables[(int64_t)bq * a.max_blocks_per_seq + first_blk + idx];
+    blk[r] = (v >= a.num_blocks) ? -1 : v;
+  }
+  // Physical block of a tile (-1: outside the pool; its tokens are skipped).
+  auto tile_phys = [&](int tile) -> int {
+    const int rel = (t_begin + tile * 16) / BS - first_blk;
+    int v = __builtin_amdgcn_readlane(blk[0], rel & 63);
+#pragma unroll
+    for (int r = 1; r < NREG; ++r) {
+      const int w = __builtin_amdgcn_readlane(blk[r], rel & 63);
+      v = (rel >> 6) == r ? w : v;
+    }
+    return v;
+  };
+
+  // ---- query operands (lane: row r16 of each row tile, the d positions of
+  // its K chunks) ----
+  uint32_t qop[RT][KW];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+#pragma unroll
+    for (int i = 0; i < KW; ++i) qop[k][i] = 0u;
+    if (head_ok[k]) {
+      const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + 8 * c16) * 2;
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 64 * j);
+        qop[k][4 * j] = w[0];
+        qop[k][4 * j + 1] = w[1];
+        qop[k][4 * j + 2] = w[2];
+        qop[k][4 * j + 3] = w[3];
+      }
+    }
+  }
+  const float kfac = a.scale * 1.4426950408889634f;   // logits in the exp2 domain
+
+  // Per row: m_run, the reference the row's P values are taken against (exp2
+  // domain), acc = unnormalised O^T and lsum = the sum of those P, from one
+  // more MFMA against ones (so it adds exactly the rounded P of the PV
+  // product).  The reference moves only when a row's max passes it by more
+  // than 2^kLazy, so P <= 2^kLazy and most steps rescale nothing; the
+  // normalised result is the same whichever reference is used.
+  constexpr float kLazy = 8.0f;
+  f32x4 acc[RT][NC];
+  f32x4 lsum[RT];
+  float m_run[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) acc[k][nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    lsum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[k] = -__builtin_inff();
+  }
+
+  // ---- global -> registers -> LDS.  Thread tid's load j of a step is the
+  // 16-byte chunk c = j * 64 W + tid of the step's [K g0][K g1][V g0][V g1]
+  // bytes, stored at LDS byte 16 c; a wave's chunks lie in one group of one
+  // cache.  Tiles past the item or outside the pool load zeros. ----
+  const uint8_t* __restrict__ kbase = static_cast<const uint8_t*>(a.k_cache);
+  const uint8_t* __restrict__ vbase = static_cast<const uint8_t*>(a.v_cache);
+  // Physical blocks of a step's two tiles (uniform; -1: past the item or
+  // outside the pool).
+  auto step_phys = [&](int step, int& p0, int& p1) {
+    const int t0 = 2 * step;
+    p0 = t0 < ntiles ? tile_phys(t0) : -1;
+    p1 = t0 + 1 < ntiles ? tile_phys(t0 + 1) : -1;
+  };
+  u32x4 pre[NLD];
+  auto issue = [&](int step, int p0, int p1) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const int c0 = j * 64 * W + wave * 64;           // the wave's first chunk
+      const int part = c0 / (GB / 16);                 // 0 K g0, 1 K g1, 2 V g0, 3 V g1
+      const int tile = 2 * step + (part & 1);
+      const int phys = (part & 1) ? p1 : p0;
+      if (phys >= 0) {
+        const int64_t row = ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS);
+        const uint8_t* src = (part < 2 ? kbase : vbase) + (uint64_t)row * R;
+        pre[j] = *reinterpret_cast<const u32x4*>(src + (c0 % (GB / 16) + lane) * 16);
+      } else {
+        pre[j] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < NLD; ++j)
+      *reinterpret_cast<u32x4*>(&lds[buf][(j * 64 * W + tid) * 16]) = pre[j];
+  };
+
+  // Max of a value over the four 16-lane rows (lanes L, L ^ 16, L ^ 32, L ^ 48):
+  // gfx950's row swaps, no LDS round trip.
+  auto rows_max = [](float v) -> float {
+    const auto x16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+    v = fmaxf(bitsf(x16[0]), bitsf(x16[1]));
+    const auto x32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+    return fmaxf(bitsf(x32[0]), bitsf(x32[1]));
+  };
+  auto pack2 = [](float x, float y) -> uint32_t {   // round to nearest even
+    const f32x2 v = {x, y};
+    if constexpr (MT == MT_F16)
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  };
+  const uint32_t one2 = MT == MT_F16 ? 0x3C003C00u : 0x3F803F80u;   // (1, 1) as f16 / bf16
+  const u32x4 ones = {one2, one2, one2, one2};
+  auto mfma32 = [](const u32x4& x, const u32x4& y, const f32x4& c) -> f32x4 {
+    if constexpr (MT == MT_F16)
+      return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x),
+                                                    __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x),
+                                                     __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+  };
+
+  // ---- one step (two 16-token groups) from LDS buffer `buf` ----
+  auto compute = [&](auto checked_c, int step, int buf, int p0, int p1) {
+    constexpr bool checked = decltype(checked_c)::value;
+    const uint8_t* base = lds[buf];
+    int n_valid[2] = {16, 16};
+    if constexpr (checked) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        int n = t_end - (t_begin + (2 * step + gi) * 16);
+        n = n > 16 ? 16 : (n < 0 ? 0 : n);
+        n_valid[gi] = (gi ? p1 : p0) < 0 ? 0 : n;
+      }
+    }
+    // S^T = K Q^T for both groups.
+    f32x4 s[RT][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      u32x4 kr[NL];
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        kr[j] = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        s[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NL; ++c) {
+          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
+          s[k][gi] = mfma32(kr[c], qb, s[k][gi]);
+        }
+      }
+    }
+
+    // Online softmax over the step's 32 tokens (lane: tokens 4 c16 + i of each
+    // group, row r16 of each row tile).  kfac > 0, so the max of the raw
+    // scores gives the max logit.
+    const int tok0 = t_begin + 2 * step * 16 + 4 * c16;
+    bool ok[RT][8];
+    float mz[RT];
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      float x[8];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ok[k][4 * gi + i] = !checked || (4 * c16 + i < n_valid[gi] && tok0 + 16 * gi + i <= prow[k]);
+          x[4 * gi + i] = ok[k][4 * gi + i] ? s[k][gi][i] : -__builtin_inff();
+        }
+      const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+      mz[k] = rows_max(mx) * kfac;
+      need = need || mz[k] > m_run[k] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        const float m_new = fmaxf(m_run[k], mz[k]);
+        // (a row that has seen no token keeps -inf and zeros)
+        const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) acc[k][nc] *= alpha;
+        lsum[k] *= alpha;
+        m_run[k] = m_new;
+      }
+    }
+    u32x4 pb[RT];
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      float p[8];
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kfac, -m_run[k]));
+          p[4 * gi + i] = checked ? (ok[k][4 * gi + i] ? e : 0.f) : e;
+        }
+      pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
+      lsum[k] = mfma32(ones, pb[k], lsum[k]);
+    }
+
+    // O^T += V^T P^T, 32 tokens deep.  Lane 16 c16 + r16 of a V group holds,
+    // for d = 16 nc + r16, tokens 4 c16 .. 4 c16 + 3 (two words per chunk nc).
+    // Slots past the context may hold anything: their V words are zeroed.
+    uint32_t vm[2][2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int cnt = n_valid[gi] - 4 * c16;
+      vm[gi][0] = (cnt > 0 ? 0xFFFFu : 0u) | (cnt > 1 ? 0xFFFF0000u : 0u);
+      vm[gi][1] = (cnt > 2 ? 0xFFFFu : 0u) | (cnt > 3 ? 0xFFFF0000u : 0u);
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16 + 1024 * j);
+      const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + 3 * GB + lane * 16 + 1024 * j);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {       // d chunk nc = 2 j + h
+        u32x4 va = {v0[2 * h], v0[2 * h + 1], v1[2 * h], v1[2 * h + 1]};
+        if constexpr (checked)
+          va = u32x4{va[0] & vm[0][0], va[1] & vm[0][1], va[2] & vm[1][0], va[3] & vm[1][1]};
+#pragma unroll
+        for (int k = 0; k < RT; ++k) acc[k][2 * j + h] = mfma32(va, pb[k], acc[k][2 * j + h]);
+      }
+    }
+  };
+
+  // ---- the step loop: loads of step s + 1 in flight while step s is
+  // multiplied; one barrier per step ----
+  int ph0 = -1, ph1 = -1;                  // physical blocks of the current step's tiles
+  if (nsteps > 0) {
+    step_phys(0, ph0, ph1);
+    issue(0, ph0, ph1);
+    stash(0);
+  }
+  __syncthreads();
+  for (int step = 0; step < nsteps; ++step) {
+    const int buf = step & 1;
+    const bool more = step + 1 < nsteps;
+    int nx0 = -1, nx1 = -1;
+    if (more) {
+      step_phys(step + 1, nx0, nx1);
+      issue(step + 1, nx0, nx1);
+    }
+    if (wave_live) {
+      if (2 * step + 2 <= nfull && ph0 >= 0 && ph1 >= 0)
+        compute(std::false_type{}, step, buf, ph0, ph1);
+      else
+        compute(std::true_type{}, step, buf, ph0, ph1);
+    }
+    if (more) stash(buf ^ 1);
+    ph0 = nx0;
+    ph1 = nx1;
+    __syncthreads();
+  }
+  if (!wave_live) return;
+
+  // ---- epilogue (as in the multi-token decode kernel) ----
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    const float l_tot = lsum[k][0];        // (every entry holds the row's sum)
+    if (!head_ok[k]) continue;
+    if (whole_unit) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc)
+        store_out4<QT>(a.out, hq[k] * D + nc * 16 + c16 * 4, acc[k][nc][0] * inv,
+                       acc[k][nc][1] * inv, acc[k][nc][2] * inv, acc[k][nc][3] * inv);
+    } else if (item < a.max_items) {
+      const int64_t slot = item * (16 * RT) + 16 * k + r16;
+      if (c16 == 0) {
+        a.ws_ml[2 * slot] = m_run[k];
+        a.ws_ml[2 * slot + 1] = l_tot;
+      }
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc)
+        *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[k][nc];
+    }
+  }
+}
+
+// Slots (resident waves) the plan is made for: whole workgroups per CU.
+template <int QT, int D, int BS>
+static hipError_t prefill_slots3(DecodeArgs& a, int num_cus) {
+  static std::atomic<int> occupancy{0};    // resident workgroups per CU (compiled property)
+  int per_cu = occupancy.load(std::memory_order_relaxed);
+  if (per_cu == 0) {
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(prefill_kernel<QT, D, BS>), 64 * kPrefillWaves, 0);
+    if (e != hipSuccess) return e;
+    occupancy.store(per_cu, std::memory_order_relaxed);
+  }
+  int waves = (per_cu < 1 ? 1 : per_cu) * kPrefillWaves;
+  if (waves > kWavesPerCuCap) waves = kWavesPerCuCap / kPrefillWaves * kPrefillWaves;
+  a.slots = num_cus * waves;
+  if (a.slots > kMaxSlots) a.slots = kMaxSlots;
+  return hipSuccess;
+}
+
+template <int QT, int D, int BS>
+static hipError_t launch_prefill3(DecodeArgs& a, int num_cus, bool slots_only, hipStream_t st) {
+  if (slots_only) return prefill_slots3<QT, D, BS>(a, num_cus);
+  const int64_t need = max_items_bound(a.batch, a.head_tiles, a.ctx_cap, a.slots);
+  const int64_t grid = ((need + kPrefillWaves - 1) / kPrefillWaves + 7) / 8 * 8;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<QT, D, BS>), dim3((unsigned)grid), dim3(64 * kPrefillWaves),
+                     0, st, a);
+  return hipGetLastError();
+}
+
+template <int QT, int D>
+static hipError_t launch_prefill2(DecodeArgs& a, int bs, int num_cus, bool slots_only,
+                                  hipStream_t st) {
+  return bs == 16 ? launch_prefill3<QT, D, 16>(a, num_cus, slots_only, st)
+                  : launch_prefill3<QT, D, 256>(a, num_cus, slots_only, st);
+}
+
+hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int head_dim, int block_size, int num_cus,
+                          bool slots_only, hipStream_t st) {
+  if (a.head_tiles != kPrefillWaves || a.wave_rows != 16 * kPrefillRowTiles)
+    return hipErrorInvalidValue;
+  if (q_dtype == PKV_F16)
+    return head_dim == 64 ? launch_prefill2<PKV_F16, 64>(a, block_size, num_cus, slots_only, st)
+                          : launch_prefill2<PKV_F16, 128>(a, block_size, num_cus, slots_only, st);
+  if (q_dtype == PKV_BF16)
+    return head_dim == 64 ? launch_prefill2<PKV_BF16, 64>(a, block_size, num_cus, slots_only, st)
+                          : launch_prefill2<PKV_BF16, 128>(a, block_size, num_cus, slots_only, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace pkv

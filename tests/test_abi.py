@@ -114,12 +114,17 @@ def test_int4_rejections(lib):
 
 def test_multi_query_sizing_and_rejections(lib):
     # 3 sequences, 40 query tokens, G = 8: 4 row tiles of 32 per group (mean rows per
-    # sequence 107), so at most 8 KV heads x (ceil(320 / 128) + 3) = 48 virtual
-    # sequences, each with 4 int32 of plan (768 B); contexts <= 256 are never split.
-    assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 256) == 768
-    # longer: + 16 B per virtual sequence (768 B) + 32 rows of (2 + d) floats per item
+    # sequence 107, too few for the prompt-chunk kernel), so at most 8 KV heads x
+    # (ceil(320 / 128) + 3) = 48 virtual sequences.  The plan: 16 B, six int32 per
+    # virtual sequence, and an item map with room for the most items any plan makes:
+    # 48 x 4 units x 16 tiles / 256 + 4096 slots + 192 units = 4300 entries.
+    # Contexts <= 256 are never split: nothing else.
+    plan = lambda entries: -(-(16 + 6 * 4 * 48 + 4 * entries) // 256) * 256
+    assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 256) == plan(4300)
+    # 32K contexts: 192 units x 2048 tiles / 256 + 4096 + 192 = 5824 items, each
+    # with 32 partial rows of (2 + d) floats, and 16 B per virtual sequence.
     big = pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 32768)
-    assert big > 1536 and (big - 768 - 768) % (32 * 130 * 4) == 0
+    assert big == plan(5824) + 48 * 16 + 5824 * 32 * 130 * 4
     args = dict(out=16, q=16, q_dtype=pkv.PKV_F16, batch=2, num_query_tokens=10, query_start=4,
                 num_q_heads=8, k_cache=16, v_cache=16, k_scale=None, v_scale=None, num_blocks=4,
                 block_size=16, num_kv_heads=2, head_dim=128, kv_dtype=pkv.PKV_F16,

@@ -150,3 +150,31 @@ def test_sequences_without_new_tokens_are_skipped():
     ragged, on an INT8 cache."""
     w = W.custom(torch.float16, "i8", [500, 90, 1200, 33, 700], 16, 4, 128, 16, name="L0")
     run_multi(w, [0, 7, 0, 33, 1])
+
+
+# Prompt chunks: a mean of several hundred (query token, head) rows per
+# sequence, 16-bit caches read by queries of their type, so the calls take the
+# LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
+# new tokens, one with more new tokens than cached ones (rows before the
+# cache), a whole prompt (L = context), both block sizes, d 64 and 128, GQA,
+# MHA and MQA.
+@pytest.mark.parametrize("q_dtype,d,bs,hq,hkv,ctx,lens", [
+    (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90]),
+    (torch.bfloat16, 128, 256, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90]),
+    (torch.float16, 64, 256, 4, 4, [600, 1000], [600, 400]),
+    (torch.bfloat16, 64, 16, 16, 1, [300, 129], [64, 129]),
+])
+def test_prompt_chunks(q_dtype, d, bs, hq, hkv, ctx, lens):
+    kv = "f16" if q_dtype == torch.float16 else "bf16"
+    w = W.custom(q_dtype, kv, ctx, hq, hkv, d, bs, name=f"prompt-{kv}-d{d}-bs{bs}-{hq}x{hkv}")
+    got, _, _, starts = run_multi(w, lens)
+    if ctx[1] < lens[1] and len(lens) > 2:
+        assert np.all(got[starts[1]:starts[1] + lens[1] - ctx[1]] == 0)
+
+
+def test_prompt_chunk_on_a_long_context_is_split_and_merged():
+    """One 64-token chunk (512 rows at G = 8) on a 12,000-token context: few
+    virtual sequences, many tiles, so each one's context is cut into several
+    items and merged.  Every row of the chunk is checked."""
+    w = W.custom(torch.float16, "f16", [12000], 8, 1, 128, 16, name="prompt-split")
+    run_multi(w, [64])
