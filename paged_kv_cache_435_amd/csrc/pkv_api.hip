@@ -113,11 +113,13 @@ int64_t multi_items(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_l
 int64_t map_entries(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_len) {
   return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
 }
-// The plan of a call: [items, tiles per item] (2 int64), six int32 per virtual
-// sequence (context, sequence, row group, KV head, first item, items per row
-// tile) and the item map.
+// The plan of a call: 128 bytes of scalars (items, tiles per item, the first
+// workgroup group of each XCD and the groups), six int32 per virtual sequence
+// (context, sequence, row group, KV head, first item, items per row tile) and
+// the item map.
+constexpr int64_t kPlanHead = 128;
 int64_t vseq_bytes(int64_t vseqs, int64_t map_cap) {
-  return (16 + 6 * 4 * vseqs + 4 * map_cap + 255) / 256 * 256;
+  return (kPlanHead + 6 * 4 * vseqs + 4 * map_cap + 255) / 256 * 256;
 }
 // Partial rows of an item: 16 x row tiles, each (max, sum) and head_dim floats.
 int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim, int64_t row_tiles,
@@ -406,7 +408,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   if (cus <= 0) return fail(PKV_ERR_HIP, std::string(fn) + ": cannot query the device");
 
   uint8_t* w = static_cast<uint8_t*>(workspace);
-  int32_t* vctx = reinterpret_cast<int32_t*>(w + 16);
+  int32_t* vctx = reinterpret_cast<int32_t*>(w + kPlanHead);
   pkv::DecodeArgs a{};
   a.out = out;
   a.q = q;

@@ -935,7 +935,9 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   __threadfence();
   __syncthreads();
   __shared__ int64_t red[2][1024 / kWave];
-  __shared__ int64_t carry_items;
+  __shared__ int64_t carry_items, carry_tiles;
+  __shared__ int scan_t[1024];           // inclusive: tiles of virtual sequences v0 .. v0 + t
+  __shared__ int xcd_groups[8];
   const int units = a.head_tiles;
   int64_t tiles = 0, live = 0;
   for (int v = t; v < a.batch; v += 1024) {
@@ -949,7 +951,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     red[0][t / kWave] = tiles;
     red[1][t / kWave] = live;
   }
-  if (t == 0) carry_items = 0;
+  if (t == 0) carry_items = carry_tiles = 0;
+  if (t < 8) xcd_groups[t] = 0;
   __syncthreads();
   tiles = live = 0;
   for (int w = 0; w < 1024 / kWave; ++w) {
@@ -957,18 +960,38 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     live += red[1][w];
   }
   const int tpi = plan_tpi(tiles * units, live * units, a.slots);
+  const int64_t total_tiles = tiles;       // of one unit per virtual sequence
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
-    int m = 0;
-    if (v < a.batch) m = ((seq_ctx(a, v) + kTileTokens - 1) / kTileTokens + tpi - 1) / tpi;
+    int m = 0, n = 0;
+    if (v < a.batch) {
+      n = (seq_ctx(a, v) + kTileTokens - 1) / kTileTokens;
+      m = (n + tpi - 1) / tpi;
+    }
     const int cnt = m * units;
     scan[t] = cnt;
+    scan_t[t] = n;
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
+    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scans
       const int x = t >= o ? scan[t - o] : 0;
+      const int y = t >= o ? scan_t[t - o] : 0;
       __syncthreads();
       scan[t] += x;
+      scan_t[t] += y;
       __syncthreads();
+    }
+    // Groups (the units of one chunk: one workgroup of the prompt-chunk
+    // kernel) to XCDs: group = chunk c of v, weighted by its tiles; XCD x
+    // takes the groups whose middle tile falls in the x-th eighth of all
+    // tiles (monotone in the group number, so counts give the ranges).
+    if (v < a.batch && total_tiles > 0) {
+      const int64_t t0 = carry_tiles + scan_t[t] - n;
+      for (int c = 0; c < m; ++c) {
+        const int64_t cs = (int64_t)c * n / m, ce = (int64_t)(c + 1) * n / m;
+        int64_t x = (8 * (2 * (t0 + cs) + (ce - cs))) / (2 * total_tiles);
+        x = x > 7 ? 7 : x;
+        atomicAdd(&xcd_groups[x], 1);
+      }
     }
     if (v < a.batch) {
       const int64_t first = carry_items + scan[t] - cnt;
@@ -981,13 +1004,22 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       for (int i = 0; i < cnt && first + i < a.map_cap; ++i) a.item_vseq[first + i] = v;
     }
     __syncthreads();
-    if (t == 0) carry_items += scan[1023];
+    if (t == 0) {
+      carry_items += scan[1023];
+      carry_tiles += scan_t[1023];
+    }
     __syncthreads();
   }
   if (t == 0) {
     // (the host sizes the map for the most items any plan makes)
     a.plan_info[0] = carry_items < a.map_cap ? carry_items : a.map_cap;
     a.plan_info[1] = tpi;
+    int64_t f = 0;                         // first group of each XCD, and the end
+    for (int x = 0; x < 8; ++x) {
+      a.plan_info[2 + x] = f;
+      f += xcd_groups[x];
+    }
+    a.plan_info[10] = f;
   }
 }
 

@@ -18,8 +18,9 @@
 //    cache once per workgroup (16 bytes per thread and instruction, in the
 //    storage order, which is already the MFMA operand order) into LDS, and
 //    every wave reads it from there: no copy per wave through the caches.
-//    LDS is double-buffered, so the next step's global loads are in flight
-//    while the current one is multiplied; one barrier per step.
+//    LDS is double-buffered and filled by direct global-to-LDS loads, so the
+//    next step's loads are in flight while the current one is multiplied,
+//    with no registers held for them; one barrier per step.
 //  * A wave holds RT tiles of 16 rows: Q in registers for the whole item,
 //    S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16} per 16 tokens, online
 //    softmax in the exp2 domain, and O^T += V^T P^T with the same 32-deep MFMA
@@ -42,30 +43,46 @@
 
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_PREFILL_WAVES_PER_EU   occupancy target of the prefill kernel
+//   PKV_PREFILL_DEPTH          LDS buffers (steps in flight + the one multiplied)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
+#endif
+#ifndef PKV_PREFILL_DEPTH
+#define PKV_PREFILL_DEPTH 3
 #endif
 
 namespace pkv {
 
+// Sizes of one instance.
+template <int QT, int D>
+struct PrefillShape {
+  static constexpr int W = kPrefillWaves;
+  static constexpr int R = 2 * D;                 // bytes per stored row
+  static constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
+  static constexpr int STEP = 4 * GB;             // K and V of two groups
+  static constexpr int NB = PKV_PREFILL_DEPTH;    // LDS buffers: NB - 1 steps in flight
+};
+
+// One group of the plan: the W items (row tiles of one virtual sequence,
+// chunk of its context) starting at item0, one per wave.
 template <int QT, int D, int BS>
-__global__ __launch_bounds__(64 * kPrefillWaves)
-__attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
-void prefill_kernel(DecodeArgs a) {
+__device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0,
+                                              uint8_t (*lds)[PrefillShape<QT, D>::STEP]) {
   constexpr int MT = MfmaOf<QT>::value;
   static_assert(MT == MT_F16 || MT == MT_BF16, "16-bit queries and caches");
   constexpr int W = kPrefillWaves;
   constexpr int RT = kPrefillRowTiles;
-  constexpr int R = 2 * D;                 // bytes per stored row
-  constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
+  constexpr int R = PrefillShape<QT, D>::R;
+  constexpr int GB = PrefillShape<QT, D>::GB;
   constexpr int NL = R / 64;               // 16-byte reads per lane per group
   constexpr int KW = 4 * NL;               // K operand words per lane per group (D / 8)
   constexpr int NC = D / 16;               // 16-wide d chunks of the output
-  constexpr int STEP = 4 * GB;             // K and V of two groups
+  constexpr int STEP = PrefillShape<QT, D>::STEP;
   constexpr int NLD = STEP / (16 * 64 * W);   // 16-byte global loads per thread per step
   static_assert(NLD >= 1 && STEP % (16 * 64 * W) == 0, "step must split evenly over the threads");
   static_assert((2 * D) % 64 == 0, "a wave's loads stay inside one group");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][STEP];   // [K g0][K g1][V g0][V g1]
+  constexpr int NB = PrefillShape<QT, D>::NB;
+  static_assert(NB >= 2 && (NB - 2) * NLD <= 63, "vmcnt threshold");
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);         // (uniform: keeps the load addresses scalar)
@@ -73,14 +90,6 @@ void prefill_kernel(DecodeArgs a) {
   const int r16 = lane & 15;
   const int c16 = lane >> 4;
 
-  // ---- the workgroup's items: W consecutive items of one (virtual
-  // sequence, chunk), one per wave (contiguous ranges per XCD) ----
-  const int64_t items = planned_items(a);   // the plan made by multi_prep_kernel
-  const int64_t groups = (items + W - 1) / W;
-  const int64_t per_xcd = (groups + 7) / 8;
-  const int64_t slot_in_xcd = blockIdx.x / 8;
-  const int64_t item0 = ((int64_t)(blockIdx.x % 8) * per_xcd + slot_in_xcd) * W;
-  if (slot_in_xcd >= per_xcd || item0 >= items) return;        // whole workgroup
   int b;
   SeqItems sq;
   planned_seq(a, item0, b, sq);
@@ -201,27 +210,42 @@ void prefill_kernel(DecodeArgs a) {
     p0 = t0 < ntiles ? tile_phys(t0) : -1;
     p1 = t0 + 1 < ntiles ? tile_phys(t0 + 1) : -1;
   };
-  u32x4 pre[NLD];
-  auto issue = [&](int step, int p0, int p1) {
+  // The loads go straight to LDS (gfx950's 16-byte global_load_lds: lane l
+  // writes at the wave's LDS base + 16 l), so no registers hold the steps in
+  // flight.  Every step issues the same NLD loads per thread (a tile past the
+  // item or outside the pool loads the first group of block 0 instead, which
+  // the products mask like any token past the context), so a fixed vmcnt
+  // threshold waits for exactly the oldest step.
+  auto issue = [&](int step, int p0, int p1, int buf) {
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int c0 = j * 64 * W + wave * 64;           // the wave's first chunk
       const int part = c0 / (GB / 16);                 // 0 K g0, 1 K g1, 2 V g0, 3 V g1
       const int tile = 2 * step + (part & 1);
       const int phys = (part & 1) ? p1 : p0;
-      if (phys >= 0) {
-        const int64_t row = ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS);
-        const uint8_t* src = (part < 2 ? kbase : vbase) + (uint64_t)row * R;
-        pre[j] = *reinterpret_cast<const u32x4*>(src + (c0 % (GB / 16) + lane) * 16);
-      } else {
-        pre[j] = u32x4{0u, 0u, 0u, 0u};
-      }
+      const int64_t row =
+          phys >= 0 ? ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS) : 0;
+      const uint8_t* src = (part < 2 ? kbase : vbase) + (uint64_t)row * R + (c0 % (GB / 16) + lane) * 16;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(&lds[buf][c0 * 16]),
+                                       16, 0, 0);
     }
   };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NLD; ++j)
-      *reinterpret_cast<u32x4*>(&lds[buf][(j * 64 * W + tid) * 16]) = pre[j];
+  // End of a step: this wave's LDS reads are done (lgkmcnt 0, so the buffer
+  // can be refilled after the barrier) and its loads of the next step have
+  // landed: all its loads, or all but the newest NB - 2 steps' (vmcnt n).
+  // The barrier carries no memory fence, which would wait for every load in
+  // flight; the empty asm statements keep the compiler from moving LDS
+  // accesses across it.
+  auto step_barrier = [](bool steady) {
+    constexpr int n = (NB - 2) * NLD;
+    if (steady)
+      __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));   // vmcnt(n) lgkmcnt(0)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);                                 // vmcnt(0) lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
   };
 
   // Max of a value over the four 16-lane rows (lanes L, L ^ 16, L ^ 32, L ^ 48):
@@ -285,22 +309,24 @@ void prefill_kernel(DecodeArgs a) {
     // Online softmax over the step's 32 tokens (lane: tokens 4 c16 + i of each
     // group, row r16 of each row tile).  kfac > 0, so the max of the raw
     // scores gives the max logit.
+    // Masked scores become -inf (a select: stale slots may hold NaN), so
+    // their P is exp2(-inf) = 0.
     const int tok0 = t_begin + 2 * step * 16 + 4 * c16;
-    bool ok[RT][8];
     float mz[RT];
     bool need = false;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      float x[8];
+      if constexpr (checked) {
 #pragma unroll
-      for (int gi = 0; gi < 2; ++gi)
+        for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[k][4 * gi + i] = !checked || (4 * c16 + i < n_valid[gi] && tok0 + 16 * gi + i <= prow[k]);
-          x[4 * gi + i] = ok[k][4 * gi + i] ? s[k][gi][i] : -__builtin_inff();
-        }
-      const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                             fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = 4 * c16 + i < n_valid[gi] && tok0 + 16 * gi + i <= prow[k];
+            s[k][gi][i] = ok ? s[k][gi][i] : -__builtin_inff();
+          }
+      }
+      const float mx = fmaxf(fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
+                             fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3])));
       mz[k] = rows_max(mx) * kfac;
       need = need || mz[k] > m_run[k] + kLazy;
     }
@@ -319,14 +345,15 @@ void prefill_kernel(DecodeArgs a) {
     u32x4 pb[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
+      // (a row that has seen no token: every score is -inf, and the finite
+      // reference keeps exp2 at 0 rather than NaN)
+      const float mref = checked ? fmaxf(m_run[k], -3.402823466e38f) : m_run[k];
       float p[8];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kfac, -m_run[k]));
-          p[4 * gi + i] = checked ? (ok[k][4 * gi + i] ? e : 0.f) : e;
-        }
+        for (int i = 0; i < 4; ++i)
+          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kfac, -mref));
       pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
     }
@@ -358,31 +385,40 @@ void prefill_kernel(DecodeArgs a) {
 
   // ---- the step loop: loads of step s + 1 in flight while step s is
   // multiplied; one barrier per step ----
-  int ph0 = -1, ph1 = -1;                  // physical blocks of the current step's tiles
-  if (nsteps > 0) {
-    step_phys(0, ph0, ph1);
-    issue(0, ph0, ph1);
-    stash(0);
+  // Physical blocks of the tiles of the steps in LDS or in flight, by buffer.
+  int phq0[NB], phq1[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) phq0[i] = phq1[i] = -1;
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) {
+    if (i < nsteps) {
+      step_phys(i, phq0[i], phq1[i]);
+      issue(i, phq0[i], phq1[i], i);
+    }
   }
-  __syncthreads();
-  for (int step = 0; step < nsteps; ++step) {
-    const int buf = step & 1;
-    const bool more = step + 1 < nsteps;
-    int nx0 = -1, nx1 = -1;
-    if (more) {
-      step_phys(step + 1, nx0, nx1);
-      issue(step + 1, nx0, nx1);
+  step_barrier(false);
+  for (int step0 = 0; step0 < nsteps; step0 += NB) {
+    // (unrolled by NB so the buffer numbers are constants)
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int step = step0 + u;
+      if (step < nsteps) {
+        const int nx = step + NB - 1;              // the step loaded now, into the buffer
+        const int nb = (u + NB - 1) % NB;          // read during step - 1 (before the barrier)
+        const bool more = nx < nsteps;
+        if (more) {
+          step_phys(nx, phq0[nb], phq1[nb]);
+          issue(nx, phq0[nb], phq1[nb], nb);
+        }
+        if (wave_live) {
+          if (2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0)
+            compute(std::false_type{}, step, u, phq0[u], phq1[u]);
+          else
+            compute(std::true_type{}, step, u, phq0[u], phq1[u]);
+        }
+        step_barrier(more);                        // step + 1 has landed everywhere
+      }
     }
-    if (wave_live) {
-      if (2 * step + 2 <= nfull && ph0 >= 0 && ph1 >= 0)
-        compute(std::false_type{}, step, buf, ph0, ph1);
-      else
-        compute(std::true_type{}, step, buf, ph0, ph1);
-    }
-    if (more) stash(buf ^ 1);
-    ph0 = nx0;
-    ph1 = nx1;
-    __syncthreads();
   }
   if (!wave_live) return;
 
@@ -411,6 +447,25 @@ void prefill_kernel(DecodeArgs a) {
 }
 
 // Slots (resident waves) the plan is made for: whole workgroups per CU.
+// The groups of the plan go to the 8 XCDs in contiguous ranges of near-equal
+// tiles (workgroups go round-robin over the XCDs, so blockIdx % 8 is the XCD;
+// the ranges were cut by multi_prep_kernel): each XCD's L2 serves few
+// sequences' K/V, and no XCD is left with the longest contexts.  A workgroup
+// takes every S-th group of its XCD's range (S workgroups per XCD); the
+// hardware starts workgroups as others finish, which evens out the rest.
+template <int QT, int D, int BS>
+__global__ __launch_bounds__(64 * kPrefillWaves)
+__attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
+void prefill_kernel(DecodeArgs a) {
+  using Sh = PrefillShape<QT, D>;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[Sh::NB][Sh::STEP];   // [K g0][K g1][V g0][V g1]
+  const int x = blockIdx.x % 8;
+  const int64_t per_xcd = gridDim.x / 8;
+  const int64_t hi = a.plan_info[3 + x];
+  for (int64_t grp = a.plan_info[2 + x] + blockIdx.x / 8; grp < hi; grp += per_xcd)
+    prefill_group<QT, D, BS>(a, grp * kPrefillWaves, lds);
+}
+
 template <int QT, int D, int BS>
 static hipError_t prefill_slots3(DecodeArgs& a, int num_cus) {
   static std::atomic<int> occupancy{0};    // resident workgroups per CU (compiled property)

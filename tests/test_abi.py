@@ -115,11 +115,11 @@ def test_int4_rejections(lib):
 def test_multi_query_sizing_and_rejections(lib):
     # 3 sequences, 40 query tokens, G = 8: 4 row tiles of 32 per group (mean rows per
     # sequence 107, too few for the prompt-chunk kernel), so at most 8 KV heads x
-    # (ceil(320 / 128) + 3) = 48 virtual sequences.  The plan: 16 B, six int32 per
-    # virtual sequence, and an item map with room for the most items any plan makes:
-    # 48 x 4 units x 16 tiles / 256 + 4096 slots + 192 units = 4300 entries.
-    # Contexts <= 256 are never split: nothing else.
-    plan = lambda entries: -(-(16 + 6 * 4 * 48 + 4 * entries) // 256) * 256
+    # (ceil(320 / 128) + 3) = 48 virtual sequences.  The plan: 128 B of scalars, six
+    # int32 per virtual sequence, and an item map with room for the most items any
+    # plan makes: 48 x 4 units x 16 tiles / 256 + 4096 slots + 192 units = 4300
+    # entries.  Contexts <= 256 are never split: nothing else.
+    plan = lambda entries: -(-(128 + 6 * 4 * 48 + 4 * entries) // 256) * 256
     assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 256) == plan(4300)
     # 32K contexts: 192 units x 2048 tiles / 256 + 4096 + 192 = 5824 items, each
     # with 32 partial rows of (2 + d) floats, and 16 B per virtual sequence.
