@@ -440,6 +440,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.real_ctx = context_lens;
   a.q_rows = num_query_tokens;
   a.wave_rows = (int32_t)(16 * sh.row_tiles);
+  a.prefill = sh.prefill ? 1 : 0;
   if (items > 0) {
     uint8_t* rest = w + vseq_bytes(vseqs, map_cap);
     a.ws_seq = reinterpret_cast<int64_t*>(rest);

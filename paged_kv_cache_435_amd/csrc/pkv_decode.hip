@@ -859,6 +859,43 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
                      lane);
 }
 
+// Inclusive prefix sums of two ints per thread over a 1024-thread block:
+// shuffle scans within each wave, then the 16 wave totals (two barriers in
+// all); tot_x, tot_y get the block totals.  wtot: LDS, [16][2].
+__device__ __forceinline__ void block_scan2(int& x, int& y, int (*wtot)[2], int& tot_x, int& tot_y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int xs = __shfl_up(x, o, kWave);
+    const int ys = __shfl_up(y, o, kWave);
+    if (lane >= o) {
+      x += xs;
+      y += ys;
+    }
+  }
+  if (lane == kWave - 1) {
+    wtot[w][0] = x;
+    wtot[w][1] = y;
+  }
+  __syncthreads();
+  int ox = 0, oy = 0;
+  tot_x = tot_y = 0;
+#pragma unroll
+  for (int i = 0; i < 1024 / kWave; ++i) {
+    const int a = wtot[i][0], b = wtot[i][1];
+    if (i < w) {
+      ox += a;
+      oy += b;
+    }
+    tot_x += a;
+    tot_y += b;
+  }
+  x += ox;
+  y += oy;
+  __syncthreads();   // (wtot is reused by the next call)
+}
+
 // Virtual sequences of a multi-token call (one workgroup): for sequence b, each
 // KV head (head-major, so the workgroups running together on an XCD share one
 // head's K/V in its L2) times each group of row tiles, with the context the
@@ -868,30 +905,33 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
 __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batch_real,
                                                           int32_t* vctx) {
   __shared__ int scan[1024];   // inclusive: entries of sequences b0 .. b0 + t
+  __shared__ int seq_len[1024], seq_cx[1024];   // new tokens and context of sequence b0 + t
+  constexpr int kCtxCache = 4096;               // contexts of the first virtual sequences
+  __shared__ int vctx_s[kCtxCache];
   __shared__ int carry;
+  __shared__ int wtot[1024 / kWave][2];
   const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
   if (t == 0) carry = 0;
   __syncthreads();
   for (int b0 = 0; b0 < batch_real; b0 += 1024) {
     const int b = b0 + t;
-    int L = 0;
+    int L = 0, cx = 0;
     if (b < batch_real) {
       L = a.query_start[b + 1] - a.query_start[b];
       L = L < 0 ? 0 : L;
+      cx = a.real_ctx[b];
+      cx = cx < 0 ? 0 : (cx > a.ctx_cap ? a.ctx_cap : cx);
     }
+    seq_len[t] = L;
+    seq_cx[t] = cx;
     const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
-    const int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
-    scan[t] = n;
+    int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
+    int unused = 0, total = 0, unused_tot = 0;
+    block_scan2(n, unused, wtot, total, unused_tot);
+    scan[t] = n;                             // inclusive
     __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scan
-      const int x = t >= o ? scan[t - o] : 0;
-      __syncthreads();
-      scan[t] += x;
-      __syncthreads();
-    }
     const int base = carry;
-    const int total = scan[1023];
     for (int e = t; e < total; e += 1024) {
       const int v = base + e;
       if (v >= a.batch) break;
@@ -901,19 +941,20 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
         if (scan[mid] > e) hi = mid; else lo = mid + 1;
       }
       const int bb = b0 + lo;
-      const int Lb = a.query_start[bb + 1] - a.query_start[bb];
-      const int ng = ((Lb < 0 ? 0 : Lb) * G + a.wave_rows * a.head_tiles - 1) /
+      const int Lb = seq_len[lo];
+      const int ng = (Lb * G + a.wave_rows * a.head_tiles - 1) /
                      (a.wave_rows * a.head_tiles);   // row groups of the sequence
       const int local = e - (lo > 0 ? scan[lo - 1] : 0);   // KV head major, then row group
       const int gg = local / ng;
       const int rt = local % ng;
-      int ctx = a.real_ctx[bb];
-      ctx = ctx < 0 ? 0 : (ctx > a.ctx_cap ? a.ctx_cap : ctx);
+      const int ctx = seq_cx[lo];
       const int ROWS = a.wave_rows * a.head_tiles;
       int last = ROWS * rt + ROWS - 1;
       last = last < Lb * G - 1 ? last : Lb * G - 1;
-      const int c = ctx - Lb + last / G + 1;
-      vctx[v] = c < 0 ? 0 : c;
+      int c = ctx - Lb + last / G + 1;
+      c = c < 0 ? 0 : c;
+      vctx[v] = c;
+      if (v < kCtxCache) vctx_s[v] = c;
       a.vseq_b[v] = bb;
       a.vseq_rt[v] = rt;
       a.vseq_g[v] = gg;
@@ -924,6 +965,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   }
   for (int v = carry + t; v < a.batch; v += 1024) {
     vctx[v] = 0;
+    if (v < kCtxCache) vctx_s[v] = 0;
     a.vseq_b[v] = -1;            // padding: no sequence, no rows
     a.vseq_rt[v] = 0;
     a.vseq_g[v] = 0;
@@ -931,17 +973,20 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
 
   // ---- the plan, once for every kernel of the call: make_plan's rule over
   // all virtual sequences (one KV head each, head_tiles units), then each
-  // one's items numbered in order and mapped back to it ----
-  __threadfence();
+  // one's items numbered in order and mapped back to it.  (Only this
+  // workgroup reads what was written above: the barrier's workgroup-scope
+  // fence makes it visible.) ----
   __syncthreads();
   __shared__ int64_t red[2][1024 / kWave];
   __shared__ int64_t carry_items, carry_tiles;
-  __shared__ int scan_t[1024];           // inclusive: tiles of virtual sequences v0 .. v0 + t
   __shared__ int xcd_groups[8];
   const int units = a.head_tiles;
+  // (contexts of the first kCtxCache virtual sequences from LDS, the rest
+  // from the workspace)
+  auto vctx_of = [&](int v) { return v < kCtxCache ? vctx_s[v] : seq_ctx(a, v); };
   int64_t tiles = 0, live = 0;
   for (int v = t; v < a.batch; v += 1024) {
-    const int n = (seq_ctx(a, v) + kTileTokens - 1) / kTileTokens;
+    const int n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
     tiles += n;
     live += n > 0;
   }
@@ -959,33 +1004,28 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     tiles += red[0][w];
     live += red[1][w];
   }
-  const int tpi = plan_tpi(tiles * units, live * units, a.slots);
+  // The prompt-chunk kernel is bound by its products, not by HBM: once the
+  // units fill a round of slots, items take whole contexts up to the item
+  // limit (fewer partial rows to write and merge); otherwise make_plan's rule.
+  const int tpi = a.prefill && live * units >= a.slots ? kItemTilesMax
+                                                        : plan_tpi(tiles * units, live * units, a.slots);
   const int64_t total_tiles = tiles;       // of one unit per virtual sequence
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
     int m = 0, n = 0;
     if (v < a.batch) {
-      n = (seq_ctx(a, v) + kTileTokens - 1) / kTileTokens;
+      n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
       m = (n + tpi - 1) / tpi;
     }
     const int cnt = m * units;
-    scan[t] = cnt;
-    scan_t[t] = n;
-    __syncthreads();
-    for (int o = 1; o < 1024; o <<= 1) {   // inclusive scans
-      const int x = t >= o ? scan[t - o] : 0;
-      const int y = t >= o ? scan_t[t - o] : 0;
-      __syncthreads();
-      scan[t] += x;
-      scan_t[t] += y;
-      __syncthreads();
-    }
+    int inc_items = cnt, inc_tiles = n, tot_items = 0, tot_tiles = 0;
+    block_scan2(inc_items, inc_tiles, wtot, tot_items, tot_tiles);
     // Groups (the units of one chunk: one workgroup of the prompt-chunk
     // kernel) to XCDs: group = chunk c of v, weighted by its tiles; XCD x
     // takes the groups whose middle tile falls in the x-th eighth of all
     // tiles (monotone in the group number, so counts give the ranges).
     if (v < a.batch && total_tiles > 0) {
-      const int64_t t0 = carry_tiles + scan_t[t] - n;
+      const int64_t t0 = carry_tiles + inc_tiles - n;
       for (int c = 0; c < m; ++c) {
         const int64_t cs = (int64_t)c * n / m, ce = (int64_t)(c + 1) * n / m;
         int64_t x = (8 * (2 * (t0 + cs) + (ce - cs))) / (2 * total_tiles);
@@ -994,7 +1034,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
     }
     if (v < a.batch) {
-      const int64_t first = carry_items + scan[t] - cnt;
+      const int64_t first = carry_items + inc_items - cnt;
       a.vseq_first[v] = (int32_t)first;
       a.vseq_m[v] = m;
       if (a.ws_seq) {
@@ -1005,8 +1045,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     }
     __syncthreads();
     if (t == 0) {
-      carry_items += scan[1023];
-      carry_tiles += scan_t[1023];
+      carry_items += tot_items;
+      carry_tiles += tot_tiles;
     }
     __syncthreads();
   }

@@ -80,6 +80,7 @@ struct DecodeArgs {
   int32_t* vseq_m;             // items (chunks of its context) per row tile
   int32_t* item_vseq;          // virtual sequence of each item
   int64_t map_cap;             // entries of item_vseq
+  int32_t prefill;             // the call takes the prompt-chunk kernel
 };
 
 // Host-side bound on the items a plan can make (grid size and workspace rows).

@@ -160,21 +160,15 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 
   // ---- query operands (lane: row r16 of each row tile, the d positions of
   // its K chunks) ----
-  uint32_t qop[RT][KW];
+  u32x4 qop[RT][NL];                       // (quads: the MFMA's B operands as they are)
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
 #pragma unroll
-    for (int i = 0; i < KW; ++i) qop[k][i] = 0u;
+    for (int j = 0; j < NL; ++j) qop[k][j] = u32x4{0u, 0u, 0u, 0u};
     if (head_ok[k]) {
       const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + 8 * c16) * 2;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(src + 64 * j);
-        qop[k][4 * j] = w[0];
-        qop[k][4 * j + 1] = w[1];
-        qop[k][4 * j + 2] = w[2];
-        qop[k][4 * j + 3] = w[3];
-      }
+      for (int j = 0; j < NL; ++j) qop[k][j] = *reinterpret_cast<const u32x4*>(src + 64 * j);
     }
   }
   const float kfac = a.scale * 1.4426950408889634f;   // logits in the exp2 domain
@@ -250,11 +244,15 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 
   // Max of a value over the four 16-lane rows (lanes L, L ^ 16, L ^ 32, L ^ 48):
   // gfx950's row swaps, no LDS round trip.
-  auto rows_max = [](float v) -> float {
+  // (IEEE maximum: no operand canonicalisation, which fmaxf costs on MFMA
+  // results; scores here are finite or -inf, never NaN)
+  auto fmax2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+  auto fmax4 = [&](float x, float y, float z, float w) { return fmax2(fmax2(x, y), fmax2(z, w)); };
+  auto rows_max = [&](float v) -> float {
     const auto x16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
-    v = fmaxf(bitsf(x16[0]), bitsf(x16[1]));
+    v = fmax2(bitsf(x16[0]), bitsf(x16[1]));
     const auto x32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
-    return fmaxf(bitsf(x32[0]), bitsf(x32[1]));
+    return fmax2(bitsf(x32[0]), bitsf(x32[1]));
   };
   auto pack2 = [](float x, float y) -> uint32_t {   // round to nearest even
     const f32x2 v = {x, y};
@@ -274,12 +272,14 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
                                                      __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
   };
 
-  // ---- one step (two 16-token groups) from LDS buffer `buf` ----
-  auto compute = [&](auto checked_c, int step, int buf, int p0, int p1) {
-    constexpr bool checked = decltype(checked_c)::value;
+  // ---- one step (two 16-token groups) from LDS buffer `buf`.  `checked`
+  // (uniform): the step may hold tokens past the context, past a row's causal
+  // position or outside the pool, which are masked; only the masking is
+  // conditional, so the accumulators never cross a branch. ----
+  auto compute = [&](bool checked, int step, int buf, int p0, int p1) {
     const uint8_t* base = lds[buf];
     int n_valid[2] = {16, 16};
-    if constexpr (checked) {
+    if (checked) {
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         int n = t_end - (t_begin + (2 * step + gi) * 16);
@@ -299,24 +299,37 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
       for (int k = 0; k < RT; ++k) {
         s[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NL; ++c) {
-          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
-          s[k][gi] = mfma32(kr[c], qb, s[k][gi]);
-        }
+        for (int c = 0; c < NL; ++c) s[k][gi] = mfma32(kr[c], qop[k][c], s[k][gi]);
       }
+    }
+    // V operands, read now so their latency hides behind the softmax.  Lane
+    // 16 c16 + r16 of a V group holds, for d = 16 nc + r16, tokens
+    // 4 c16 .. 4 c16 + 3 (8 bytes per chunk nc); the operand of chunk nc is
+    // group 0's 8 bytes then group 1's, each read straight into its registers
+    // (the first halves of all chunks, then the second halves: the empty asm
+    // statement keeps the two halves of one 16-byte slot from being read as
+    // one and copied apart).
+    u32x4 va[NC];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        const int off = lane * 16 + 1024 * j + 8 * h;
+        const u32x2 v0 = *reinterpret_cast<const u32x2*>(base + 2 * GB + off);
+        const u32x2 v1 = *reinterpret_cast<const u32x2*>(base + 3 * GB + off);
+        va[2 * j + h] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      }
+      asm volatile("" ::: "memory");
     }
 
     // Online softmax over the step's 32 tokens (lane: tokens 4 c16 + i of each
     // group, row r16 of each row tile).  kfac > 0, so the max of the raw
-    // scores gives the max logit.
-    // Masked scores become -inf (a select: stale slots may hold NaN), so
-    // their P is exp2(-inf) = 0.
+    // scores gives the max logit.  Masked scores become -inf (a select: stale
+    // slots may hold NaN), so their P is exp2(-inf) = 0.
     const int tok0 = t_begin + 2 * step * 16 + 4 * c16;
-    float mz[RT];
-    bool need = false;
+    if (checked) {
 #pragma unroll
-    for (int k = 0; k < RT; ++k) {
-      if constexpr (checked) {
+      for (int k = 0; k < RT; ++k)
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
@@ -324,16 +337,20 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
             const bool ok = 4 * c16 + i < n_valid[gi] && tok0 + 16 * gi + i <= prow[k];
             s[k][gi][i] = ok ? s[k][gi][i] : -__builtin_inff();
           }
-      }
-      const float mx = fmaxf(fmaxf(fmaxf(s[k][0][0], s[k][0][1]), fmaxf(s[k][0][2], s[k][0][3])),
-                             fmaxf(fmaxf(s[k][1][0], s[k][1][1]), fmaxf(s[k][1][2], s[k][1][3])));
+    }
+    float mz[RT];
+    bool need = false;
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      const float mx = fmax2(fmax4(s[k][0][0], s[k][0][1], s[k][0][2], s[k][0][3]),
+                             fmax4(s[k][1][0], s[k][1][1], s[k][1][2], s[k][1][3]));
       mz[k] = rows_max(mx) * kfac;
       need = need || mz[k] > m_run[k] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        const float m_new = fmaxf(m_run[k], mz[k]);
+        const float m_new = fmax2(m_run[k], mz[k]);
         // (a row that has seen no token keeps -inf and zeros)
         const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
 #pragma unroll
@@ -347,7 +364,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     for (int k = 0; k < RT; ++k) {
       // (a row that has seen no token: every score is -inf, and the finite
       // reference keeps exp2 at 0 rather than NaN)
-      const float mref = checked ? fmaxf(m_run[k], -3.402823466e38f) : m_run[k];
+      const float mref = fmax2(m_run[k], -3.402823466e38f);
       float p[8];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
@@ -358,29 +375,25 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
     }
 
-    // O^T += V^T P^T, 32 tokens deep.  Lane 16 c16 + r16 of a V group holds,
-    // for d = 16 nc + r16, tokens 4 c16 .. 4 c16 + 3 (two words per chunk nc).
-    // Slots past the context may hold anything: their V words are zeroed.
-    uint32_t vm[2][2];
+    // O^T += V^T P^T, 32 tokens deep.  Slots past the context may hold
+    // anything: their V values are zeroed.
+    if (checked) {
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const int cnt = n_valid[gi] - 4 * c16;
-      vm[gi][0] = (cnt > 0 ? 0xFFFFu : 0u) | (cnt > 1 ? 0xFFFF0000u : 0u);
-      vm[gi][1] = (cnt > 2 ? 0xFFFFu : 0u) | (cnt > 3 ? 0xFFFF0000u : 0u);
-    }
+      for (int gi = 0; gi < 2; ++gi) {
+        const int cnt = n_valid[gi] - 4 * c16;
+        const uint32_t m0 = (cnt > 0 ? 0xFFFFu : 0u) | (cnt > 1 ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (cnt > 2 ? 0xFFFFu : 0u) | (cnt > 3 ? 0xFFFF0000u : 0u);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
-      const u32x4 v0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16 + 1024 * j);
-      const u32x4 v1 = *reinterpret_cast<const u32x4*>(base + 3 * GB + lane * 16 + 1024 * j);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {       // d chunk nc = 2 j + h
-        u32x4 va = {v0[2 * h], v0[2 * h + 1], v1[2 * h], v1[2 * h + 1]};
-        if constexpr (checked)
-          va = u32x4{va[0] & vm[0][0], va[1] & vm[0][1], va[2] & vm[1][0], va[3] & vm[1][1]};
-#pragma unroll
-        for (int k = 0; k < RT; ++k) acc[k][2 * j + h] = mfma32(va, pb[k], acc[k][2 * j + h]);
+        for (int nc = 0; nc < NC; ++nc) {
+          va[nc][2 * gi] &= m0;
+          va[nc][2 * gi + 1] &= m1;
+        }
       }
     }
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc)
+#pragma unroll
+      for (int k = 0; k < RT; ++k) acc[k][nc] = mfma32(va[nc], pb[k], acc[k][nc]);
   };
 
   // ---- the step loop: loads of step s + 1 in flight while step s is
@@ -410,12 +423,9 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
           step_phys(nx, phq0[nb], phq1[nb]);
           issue(nx, phq0[nb], phq1[nb], nb);
         }
-        if (wave_live) {
-          if (2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0)
-            compute(std::false_type{}, step, u, phq0[u], phq1[u]);
-          else
-            compute(std::true_type{}, step, u, phq0[u], phq1[u]);
-        }
+        if (wave_live)
+          compute(!(2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0), step, u, phq0[u],
+                  phq1[u]);
         step_barrier(more);                        // step + 1 has landed everywhere
       }
     }

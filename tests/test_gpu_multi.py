@@ -178,3 +178,18 @@ def test_prompt_chunk_on_a_long_context_is_split_and_merged():
     items and merged.  Every row of the chunk is checked."""
     w = W.custom(torch.float16, "f16", [12000], 8, 1, 128, 16, name="prompt-split")
     run_multi(w, [64])
+
+
+@pytest.mark.parametrize("hq,hkv,qlen", [(64, 8, None), (16, 2, 16)])
+def test_more_than_1024_sequences(hq, hkv, qlen):
+    """1100 sequences: the planning pass takes them in two rounds of 1024 and
+    its virtual sequences pass the 4096 whose contexts it keeps in LDS.  One
+    or two draft tokens each at GQA-8 (the multi-token decode kernel), or
+    16-token chunks at G = 8 (the prompt-chunk kernel).  Sampled sequences
+    from both rounds are checked."""
+    rng = np.random.default_rng(7)
+    B = 1100
+    lens = rng.integers(1, 3, B) if qlen is None else np.full(B, qlen)
+    ctx = np.maximum(rng.integers(16, 100, B), lens)
+    w = W.custom(torch.float16, "f16", ctx, hq, hkv, 128, 16, name=f"B{B}-{hq}x{hkv}")
+    run_multi(w, lens, seqs_check=[0, 511, 1023, 1024, 1099])
