@@ -1021,10 +1021,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     int inc_items = cnt, inc_tiles = n, tot_items = 0, tot_tiles = 0;
     block_scan2(inc_items, inc_tiles, wtot, tot_items, tot_tiles);
     // Groups (the units of one chunk: one workgroup of the prompt-chunk
-    // kernel) to XCDs: group = chunk c of v, weighted by its tiles; XCD x
-    // takes the groups whose middle tile falls in the x-th eighth of all
-    // tiles (monotone in the group number, so counts give the ranges).
-    if (v < a.batch && total_tiles > 0) {
+    // kernel, the only one that reads these ranges) to XCDs: group = chunk c
+    // of v, weighted by its tiles; XCD x takes the groups whose middle tile
+    // falls in the x-th eighth of all tiles (monotone in the group number, so
+    // counts give the ranges).
+    if (a.prefill && v < a.batch && total_tiles > 0) {
       const int64_t t0 = carry_tiles + inc_tiles - n;
       for (int c = 0; c < m; ++c) {
         const int64_t cs = (int64_t)c * n / m, ce = (int64_t)(c + 1) * n / m;
