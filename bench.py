@@ -35,7 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 COUNTERS = os.path.join(ROOT, "profiles", "decode_counters_llama70b_gqa8.json")
 DECODE_SOURCES = ("paged_kv_cache_435_amd/csrc/pkv_decode.hip",
                   "paged_kv_cache_435_amd/csrc/pkv_common.h",
-                  "paged_kv_cache_435_amd/csrc/pkv_internal.h")
+                  "paged_kv_cache_435_amd/csrc/pkv_internal.h",
+                  "paged_kv_cache_435_amd/csrc/pkv_kernel.h")
 DECODE_KERNELS = ("decode_partition_kernel", "decode_merge_kernel")
 COPY_KERNEL = "pkv_probe_copy_kernel"
 
