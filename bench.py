@@ -331,13 +331,15 @@ def bench_multi(args, name):
         f"sum(ctx)={int(w.context_lens.sum())} workspace {ws.numel()} B")
 
     def step(events=None):
-        pkv.kv_cache_append(new_k, new_v, slots, case.k_cache, case.v_cache)
+        pkv.kv_cache_append(new_k, new_v, slots, case.k_cache, case.v_cache, case.k_scale,
+                            case.v_scale, kv_dtype=case.kv_dtype)
         if events is not None:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
         pkv.paged_attention_multi_query(out, q, starts, case.k_cache, case.v_cache,
                                         case.block_tables, case.context_lens, w.scale, mcl,
-                                        workspace=ws)
+                                        k_scale=case.k_scale, v_scale=case.v_scale,
+                                        kv_dtype=case.kv_dtype, workspace=ws)
         if events is not None:
             e1.record()
             events.append((e0, e1))
@@ -372,7 +374,8 @@ def bench_multi(args, name):
     print(json.dumps({
         "metric": "multi-token query attention: query tokens/s, 1 GPU", "value": T * args.steps / elapsed,
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True, "dtype": "f16",
+        "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
+        "dtype": "f16" if w.kv_format == "f16" else f"f16 (KV {w.kv_format})",
         "data": "synthetic",
         "config": {"workload": name, "batch": w.batch, "query_tokens": T,
                    "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,

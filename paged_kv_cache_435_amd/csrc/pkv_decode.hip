@@ -1177,14 +1177,14 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
 }
 
 template <int QT, int D>
-static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vctx, int block_size,
-                                      int num_cus, hipStream_t st) {
-  hipError_t e = launch_prefill(a, QT, D, block_size, num_cus, true, st);   // a.slots
+static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vctx, int kv_dtype,
+                                      int block_size, int num_cus, hipStream_t st) {
+  hipError_t e = launch_prefill(a, QT, kv_dtype, D, block_size, num_cus, true, st);   // a.slots
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(multi_prep_kernel, dim3(1), dim3(1024), 0, st, a, batch_real, vctx);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_prefill(a, QT, D, block_size, num_cus, false, st);
+  e = launch_prefill(a, QT, kv_dtype, D, block_size, num_cus, false, st);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch), dim3(64 * kMergeWaves), 0, st, a);
   return hipGetLastError();
@@ -1193,14 +1193,16 @@ static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vc
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
                         int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st) {
   if (prefill) {
-    if (kv_dtype != q_dtype || (q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
-        (head_dim != 64 && head_dim != 128))
+    if ((q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
+        (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3FN) || (head_dim != 64 && head_dim != 128))
       return hipErrorInvalidValue;
     if (q_dtype == PKV_F16)
-      return head_dim == 64 ? launch_prefill_call<PKV_F16, 64>(a, batch_real, vctx, block_size, num_cus, st)
-                            : launch_prefill_call<PKV_F16, 128>(a, batch_real, vctx, block_size, num_cus, st);
-    return head_dim == 64 ? launch_prefill_call<PKV_BF16, 64>(a, batch_real, vctx, block_size, num_cus, st)
-                          : launch_prefill_call<PKV_BF16, 128>(a, batch_real, vctx, block_size, num_cus, st);
+      return head_dim == 64
+                 ? launch_prefill_call<PKV_F16, 64>(a, batch_real, vctx, kv_dtype, block_size, num_cus, st)
+                 : launch_prefill_call<PKV_F16, 128>(a, batch_real, vctx, kv_dtype, block_size, num_cus, st);
+    return head_dim == 64
+               ? launch_prefill_call<PKV_BF16, 64>(a, batch_real, vctx, kv_dtype, block_size, num_cus, st)
+               : launch_prefill_call<PKV_BF16, 128>(a, batch_real, vctx, kv_dtype, block_size, num_cus, st);
   }
   if (a.wave_rows != 16 * kMultiRowTiles) return hipErrorInvalidValue;
   return launch0<true>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus,

@@ -101,7 +101,7 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
 // Multi-query: a.batch = virtual sequences (upper bound), a.context_lens =
 // vctx (written by the prep kernel first), batch_real real sequences.
 // prefill: the LDS-sharing kernel (a.head_tiles = kPrefillWaves, a.wave_rows =
-// 16 kPrefillRowTiles; 16-bit caches of the query's type), else the
+// 16 kPrefillRowTiles; 16-bit caches of the query's type or FP8), else the
 // multi-token decode kernel (a.wave_rows = 16 kMultiRowTiles).
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
                         int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st);
@@ -109,8 +109,8 @@ hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtyp
 // The prefill kernel alone (pkv_prefill.hip); launch_multi runs the plan
 // before it and the merge after it.  slots_only: set a.slots (the resident
 // waves the plan is made for) and launch nothing.
-hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int head_dim, int block_size, int num_cus,
-                          bool slots_only, hipStream_t st);
+hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
+                          int num_cus, bool slots_only, hipStream_t st);
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t n_rows, int row_len, int out_dtype,
                            void* out, float* scale, int scale_given, hipStream_t st);

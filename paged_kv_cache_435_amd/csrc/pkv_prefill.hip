@@ -34,7 +34,9 @@
 //    kernel) and the split-K merge are those of the multi-token decode kernel
 //    (pkv_decode.hip): a virtual sequence here is a group of W * RT * 16 rows.
 //
-// 16-bit caches read by queries of the same type (f16/f16, bf16/bf16).
+// Caches: 16-bit of the query's type (f16/f16, bf16/bf16), or FP8 E4M3FN with
+// f16 or bf16 queries (codes converted exactly after the LDS read, the
+// per-tensor scales folded into the logits and the output).
 #include <atomic>
 
 #include "pkv_common.h"
@@ -54,10 +56,10 @@
 namespace pkv {
 
 // Sizes of one instance.
-template <int QT, int D>
+template <int KV, int D>
 struct PrefillShape {
   static constexpr int W = kPrefillWaves;
-  static constexpr int R = 2 * D;                 // bytes per stored row
+  static constexpr int R = (int)row_bytes_of(KV, D);   // bytes per stored row
   static constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
   static constexpr int STEP = 4 * GB;             // K and V of two groups
   static constexpr int NB = PKV_PREFILL_DEPTH;    // LDS buffers: NB - 1 steps in flight
@@ -65,23 +67,28 @@ struct PrefillShape {
 
 // One group of the plan: the W items (row tiles of one virtual sequence,
 // chunk of its context) starting at item0, one per wave.
-template <int QT, int D, int BS>
+// KV: the cache's storage type, QT (f16 or bf16, the MFMA type) or FP8
+// E4M3FN (converted exactly after the LDS read).
+template <int QT, int KV, int D, int BS>
 __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0,
-                                              uint8_t (*lds)[PrefillShape<QT, D>::STEP]) {
+                                              uint8_t (*lds)[PrefillShape<KV, D>::STEP]) {
   constexpr int MT = MfmaOf<QT>::value;
-  static_assert(MT == MT_F16 || MT == MT_BF16, "16-bit queries and caches");
+  static_assert(MT == MT_F16 || MT == MT_BF16, "f16 or bf16 queries");
+  static_assert(KV == QT || KV == PKV_FP8_E4M3FN, "a 16-bit cache of the query's type, or FP8");
+  constexpr bool fp8 = KV == PKV_FP8_E4M3FN;
+  using C = Cvt<KV, MT>;
   constexpr int W = kPrefillWaves;
   constexpr int RT = kPrefillRowTiles;
-  constexpr int R = PrefillShape<QT, D>::R;
-  constexpr int GB = PrefillShape<QT, D>::GB;
+  constexpr int R = PrefillShape<KV, D>::R;
+  constexpr int GB = PrefillShape<KV, D>::GB;
   constexpr int NL = R / 64;               // 16-byte reads per lane per group
-  constexpr int KW = 4 * NL;               // K operand words per lane per group (D / 8)
+  constexpr int KQ = D / 32;               // MFMA operand quads per lane per K group
   constexpr int NC = D / 16;               // 16-wide d chunks of the output
-  constexpr int STEP = PrefillShape<QT, D>::STEP;
+  constexpr int STEP = PrefillShape<KV, D>::STEP;
   constexpr int NLD = STEP / (16 * 64 * W);   // 16-byte global loads per thread per step
   static_assert(NLD >= 1 && STEP % (16 * 64 * W) == 0, "step must split evenly over the threads");
-  static_assert((2 * D) % 64 == 0, "a wave's loads stay inside one group");
-  constexpr int NB = PrefillShape<QT, D>::NB;
+  static_assert(GB % 1024 == 0, "a wave's loads stay inside one group");
+  constexpr int NB = PrefillShape<KV, D>::NB;
   static_assert(NB >= 2 && (NB - 2) * NLD <= 63, "vmcnt threshold");
 
   const int tid = threadIdx.x;
@@ -160,18 +167,31 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 
   // ---- query operands (lane: row r16 of each row tile, the d positions of
   // its K chunks) ----
-  u32x4 qop[RT][NL];                       // (quads: the MFMA's B operands as they are)
+  // Query operands, in the d order of the K operands: 16-bit K chunks carry
+  // d = 32 j + 8 c16 .. + 7 (quad j); FP8 K chunks carry d = 64 j + 16 c16 ..
+  // + 15 (quads 2 j and 2 j + 1 after conversion).
+  u32x4 qop[RT][KQ];                       // (quads: the MFMA's B operands as they are)
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
 #pragma unroll
-    for (int j = 0; j < NL; ++j) qop[k][j] = u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < KQ; ++j) qop[k][j] = u32x4{0u, 0u, 0u, 0u};
     if (head_ok[k]) {
-      const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + 8 * c16) * 2;
+      const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + hq[k] * D * 2;
 #pragma unroll
-      for (int j = 0; j < NL; ++j) qop[k][j] = *reinterpret_cast<const u32x4*>(src + 64 * j);
+      for (int j = 0; j < KQ; ++j) {
+        const int d0 = fp8 ? 64 * (j / 2) + 16 * c16 + 8 * (j % 2) : 32 * j + 8 * c16;
+        qop[k][j] = *reinterpret_cast<const u32x4*>(qrow + d0 * 2);
+      }
     }
   }
-  const float kfac = a.scale * 1.4426950408889634f;   // logits in the exp2 domain
+  // logits in the exp2 domain; FP8: the per-tensor scales (K into the logits,
+  // V into the output)
+  float kfac = a.scale * 1.4426950408889634f;
+  float vfac = 1.0f;
+  if constexpr (fp8) {
+    kfac *= a.k_scale[0];
+    vfac = a.v_scale[0];
+  }
 
   // Per row: m_run, the reference the row's P values are taken against (exp2
   // domain), acc = unnormalised O^T and lsum = the sum of those P, from one
@@ -291,15 +311,24 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     f32x4 s[RT][2];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
-      u32x4 kr[NL];
+      u32x4 kq[KQ];
 #pragma unroll
-      for (int j = 0; j < NL; ++j)
-        kr[j] = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
+      for (int j = 0; j < NL; ++j) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
+        if constexpr (fp8) {
+          uint32_t w[8];
+          C::run(raw, w);
+          kq[2 * j] = u32x4{w[0], w[1], w[2], w[3]};
+          kq[2 * j + 1] = u32x4{w[4], w[5], w[6], w[7]};
+        } else {
+          kq[j] = raw;
+        }
+      }
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
         s[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NL; ++c) s[k][gi] = mfma32(kr[c], qop[k][c], s[k][gi]);
+        for (int c = 0; c < KQ; ++c) s[k][gi] = mfma32(kq[c], qop[k][c], s[k][gi]);
       }
     }
     // V operands, read now so their latency hides behind the softmax.  Lane
@@ -309,17 +338,34 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     // (the first halves of all chunks, then the second halves: the empty asm
     // statement keeps the two halves of one 16-byte slot from being read as
     // one and copied apart).
+    // (FP8: a lane's 16 bytes hold four chunks of 4 bytes, each converted
+    // to two words; the operand is group 0's pair then group 1's.)
     u32x4 va[NC];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    if constexpr (fp8) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        const int off = lane * 16 + 1024 * j + 8 * h;
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(base + 2 * GB + off);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(base + 3 * GB + off);
-        va[2 * j + h] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        const u32x4 r0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16 + 1024 * j);
+        const u32x4 r1 = *reinterpret_cast<const u32x4*>(base + 3 * GB + lane * 16 + 1024 * j);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w0[2], w1[2];
+          C::word(r0[q], w0);
+          C::word(r1[q], w1);
+          va[4 * j + q] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+        }
       }
-      asm volatile("" ::: "memory");
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+          const int off = lane * 16 + 1024 * j + 8 * h;
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(base + 2 * GB + off);
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(base + 3 * GB + off);
+          va[2 * j + h] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+        }
+        asm volatile("" ::: "memory");
+      }
     }
 
     // Online softmax over the step's 32 tokens (lane: tokens 4 c16 + i of each
@@ -438,7 +484,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     const float l_tot = lsum[k][0];        // (every entry holds the row's sum)
     if (!head_ok[k]) continue;
     if (whole_unit) {
-      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc)
         store_out4<QT>(a.out, hq[k] * D + nc * 16 + c16 * 4, acc[k][nc][0] * inv,
@@ -451,7 +497,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
       }
 #pragma unroll
       for (int nc = 0; nc < NC; ++nc)
-        *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[k][nc];
+        *reinterpret_cast<f32x4*>(a.ws_acc + slot * D + nc * 16 + c16 * 4) = acc[k][nc] * vfac;
     }
   }
 }
@@ -463,26 +509,26 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 // sequences' K/V, and no XCD is left with the longest contexts.  A workgroup
 // takes every S-th group of its XCD's range (S workgroups per XCD); the
 // hardware starts workgroups as others finish, which evens out the rest.
-template <int QT, int D, int BS>
+template <int QT, int KV, int D, int BS>
 __global__ __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(DecodeArgs a) {
-  using Sh = PrefillShape<QT, D>;
+  using Sh = PrefillShape<KV, D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[Sh::NB][Sh::STEP];   // [K g0][K g1][V g0][V g1]
   const int x = blockIdx.x % 8;
   const int64_t per_xcd = gridDim.x / 8;
   const int64_t hi = a.plan_info[3 + x];
   for (int64_t grp = a.plan_info[2 + x] + blockIdx.x / 8; grp < hi; grp += per_xcd)
-    prefill_group<QT, D, BS>(a, grp * kPrefillWaves, lds);
+    prefill_group<QT, KV, D, BS>(a, grp * kPrefillWaves, lds);
 }
 
-template <int QT, int D, int BS>
+template <int QT, int KV, int D, int BS>
 static hipError_t prefill_slots3(DecodeArgs& a, int num_cus) {
   static std::atomic<int> occupancy{0};    // resident workgroups per CU (compiled property)
   int per_cu = occupancy.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(prefill_kernel<QT, D, BS>), 64 * kPrefillWaves, 0);
+        &per_cu, reinterpret_cast<const void*>(prefill_kernel<QT, KV, D, BS>), 64 * kPrefillWaves, 0);
     if (e != hipSuccess) return e;
     occupancy.store(per_cu, std::memory_order_relaxed);
   }
@@ -493,34 +539,43 @@ static hipError_t prefill_slots3(DecodeArgs& a, int num_cus) {
   return hipSuccess;
 }
 
-template <int QT, int D, int BS>
+template <int QT, int KV, int D, int BS>
 static hipError_t launch_prefill3(DecodeArgs& a, int num_cus, bool slots_only, hipStream_t st) {
-  if (slots_only) return prefill_slots3<QT, D, BS>(a, num_cus);
+  if (slots_only) return prefill_slots3<QT, KV, D, BS>(a, num_cus);
   const int64_t need = max_items_bound(a.batch, a.head_tiles, a.ctx_cap, a.slots);
   const int64_t grid = ((need + kPrefillWaves - 1) / kPrefillWaves + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<QT, D, BS>), dim3((unsigned)grid), dim3(64 * kPrefillWaves),
+  hipLaunchKernelGGL((prefill_kernel<QT, KV, D, BS>), dim3((unsigned)grid), dim3(64 * kPrefillWaves),
                      0, st, a);
   return hipGetLastError();
 }
 
-template <int QT, int D>
+template <int QT, int KV, int D>
 static hipError_t launch_prefill2(DecodeArgs& a, int bs, int num_cus, bool slots_only,
                                   hipStream_t st) {
-  return bs == 16 ? launch_prefill3<QT, D, 16>(a, num_cus, slots_only, st)
-                  : launch_prefill3<QT, D, 256>(a, num_cus, slots_only, st);
+  return bs == 16 ? launch_prefill3<QT, KV, D, 16>(a, num_cus, slots_only, st)
+                  : launch_prefill3<QT, KV, D, 256>(a, num_cus, slots_only, st);
 }
 
-hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int head_dim, int block_size, int num_cus,
-                          bool slots_only, hipStream_t st) {
-  if (a.head_tiles != kPrefillWaves || a.wave_rows != 16 * kPrefillRowTiles)
+template <int QT, int KV>
+static hipError_t launch_prefill1(DecodeArgs& a, int head_dim, int bs, int num_cus,
+                                  bool slots_only, hipStream_t st) {
+  return head_dim == 64 ? launch_prefill2<QT, KV, 64>(a, bs, num_cus, slots_only, st)
+                        : launch_prefill2<QT, KV, 128>(a, bs, num_cus, slots_only, st);
+}
+
+hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
+                          int num_cus, bool slots_only, hipStream_t st) {
+  if (a.head_tiles != kPrefillWaves || a.wave_rows != 16 * kPrefillRowTiles ||
+      (head_dim != 64 && head_dim != 128))
     return hipErrorInvalidValue;
-  if (q_dtype == PKV_F16)
-    return head_dim == 64 ? launch_prefill2<PKV_F16, 64>(a, block_size, num_cus, slots_only, st)
-                          : launch_prefill2<PKV_F16, 128>(a, block_size, num_cus, slots_only, st);
-  if (q_dtype == PKV_BF16)
-    return head_dim == 64 ? launch_prefill2<PKV_BF16, 64>(a, block_size, num_cus, slots_only, st)
-                          : launch_prefill2<PKV_BF16, 128>(a, block_size, num_cus, slots_only, st);
+  const bool fp8 = kv_dtype == PKV_FP8_E4M3FN;
+  if (q_dtype == PKV_F16 && (kv_dtype == PKV_F16 || fp8))
+    return fp8 ? launch_prefill1<PKV_F16, PKV_FP8_E4M3FN>(a, head_dim, block_size, num_cus, slots_only, st)
+               : launch_prefill1<PKV_F16, PKV_F16>(a, head_dim, block_size, num_cus, slots_only, st);
+  if (q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || fp8))
+    return fp8 ? launch_prefill1<PKV_BF16, PKV_FP8_E4M3FN>(a, head_dim, block_size, num_cus, slots_only, st)
+               : launch_prefill1<PKV_BF16, PKV_BF16>(a, head_dim, block_size, num_cus, slots_only, st);
   return hipErrorInvalidValue;
 }
 

@@ -170,7 +170,7 @@ NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70
 #                       to verify
 #   llama70b_prefill512 8 sequences of the 70B GQA-8 shape, cached prefixes
 #                       U[0, 4096] (seed 0) and a 512-token prompt chunk each
-MULTI_NAMES = ("llama70b_verify4", "llama70b_prefill512")
+MULTI_NAMES = ("llama70b_verify4", "llama70b_prefill512", "llama70b_prefill512_fp8")
 
 
 def make_multi(name):
@@ -178,12 +178,15 @@ def make_multi(name):
         w = make("llama70b_gqa8")
         w.name, w.appends = name, False
         return w, np.full(w.batch, 4, dtype=np.int64)
-    if name == "llama70b_prefill512":
+    if name in ("llama70b_prefill512", "llama70b_prefill512_fp8"):
+        # 512-token prompt chunks of 8 sequences with prefixes U[0, 4096]; f16
+        # queries over an f16 or an FP8 E4M3FN cache
         prefix = np.random.default_rng(0).integers(0, 4096, 8, endpoint=True)
         ctx = (prefix + 512).astype(np.int32)
         bs = 16
         nb = pool_for(ctx, bs)
-        w = Workload(name, torch.float16, "f16", 8, 64, 8, 128, bs, 1, ctx, nb,
+        fmt = "fp8" if name.endswith("_fp8") else "f16"
+        w = Workload(name, torch.float16, fmt, 8, 64, 8, 128, bs, 1, ctx, nb,
                      deal_blocks(ctx, bs, nb), appends=False,
                      seeds=dict(context=0, permutation=1, q=2, k=3, v=4, new=6))
         return w, np.full(8, 512, dtype=np.int64)

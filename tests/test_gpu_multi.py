@@ -137,7 +137,7 @@ def test_benchmark_workloads_sampled(name):
     w, q_lens = W.make_multi(name)
     ctx = w.context_lens
     seqs = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 3})
-    if name == "llama70b_prefill512":
+    if name.startswith("llama70b_prefill512"):
         starts = np.concatenate([[0], np.cumsum(q_lens)])
         pick = lambda b: [int(starts[b]), int(starts[b]) + 255, int(starts[b + 1]) - 1]
         run_multi(w, q_lens, seqs_check=seqs, rows_of=pick)
@@ -153,19 +153,24 @@ def test_sequences_without_new_tokens_are_skipped():
 
 
 # Prompt chunks: a mean of several hundred (query token, head) rows per
-# sequence, 16-bit caches read by queries of their type, so the calls take the
-# LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
+# sequence, f16/bf16 queries over a cache of their type or FP8, so the calls
+# take the LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
 # new tokens, one with more new tokens than cached ones (rows before the
 # cache), a whole prompt (L = context), both block sizes, d 64 and 128, GQA,
 # MHA and MQA.
-@pytest.mark.parametrize("q_dtype,d,bs,hq,hkv,ctx,lens", [
-    (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90]),
-    (torch.bfloat16, 128, 256, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90]),
-    (torch.float16, 64, 256, 4, 4, [600, 1000], [600, 400]),
-    (torch.bfloat16, 64, 16, 16, 1, [300, 129], [64, 129]),
+@pytest.mark.parametrize("q_dtype,d,bs,hq,hkv,ctx,lens,kv", [
+    (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], None),
+    (torch.bfloat16, 128, 256, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], None),
+    (torch.float16, 64, 256, 4, 4, [600, 1000], [600, 400], None),
+    (torch.bfloat16, 64, 16, 16, 1, [300, 129], [64, 129], None),
+    (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], "fp8"),
+    (torch.bfloat16, 128, 256, 16, 1, [300, 129], [64, 129], "fp8"),
+    (torch.bfloat16, 64, 16, 4, 4, [600, 1000], [600, 400], "fp8"),
 ])
-def test_prompt_chunks(q_dtype, d, bs, hq, hkv, ctx, lens):
-    kv = "f16" if q_dtype == torch.float16 else "bf16"
+def test_prompt_chunks(q_dtype, d, bs, hq, hkv, ctx, lens, kv):
+    """(FP8 rows: the same kernel over an FP8 E4M3FN cache, codes converted
+    after the LDS read.)"""
+    kv = kv or ("f16" if q_dtype == torch.float16 else "bf16")
     w = W.custom(q_dtype, kv, ctx, hq, hkv, d, bs, name=f"prompt-{kv}-d{d}-bs{bs}-{hq}x{hkv}")
     got, _, _, starts = run_multi(w, lens)
     if ctx[1] < lens[1] and len(lens) > 2:
