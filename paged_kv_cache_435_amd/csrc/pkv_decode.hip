@@ -842,8 +842,14 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
     const int64_t rho = row0 + r;
     return (q0 + rho / G) * a.num_q_heads + g * G + rho % G;
   };
+  // Rows r = blockIdx.y * kMergeWaves + wave + k * kMergeWaves * gridDim.y: a
+  // second grid dimension gives every wave one row when rows per virtual
+  // sequence are few and split many times (each row's merge is a chain of
+  // dependent loads).
+  const int r_first = blockIdx.y * kMergeWaves + wave;
+  const int r_step = kMergeWaves * gridDim.y;
   if (seq_ctx(a, v) == 0) {
-    for (int r = wave; r < rows; r += kMergeWaves)
+    for (int r = r_first; r < rows; r += r_step)
       if (lane < D / 4) store_out4<QT>(a.out, out_row(r) * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
     return;
   }
@@ -854,7 +860,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   // (one KV head per virtual sequence) chunk c, row tile ht: item
   // first + c*head_tiles + ht, rows item*TR ..
   if (first + (int64_t)m * a.head_tiles - 1 >= a.max_items) return;
-  for (int r = wave; r < rows; r += kMergeWaves)
+  for (int r = r_first; r < rows; r += r_step)
     merge_row<QT, D>(a, (first + r / TR) * TR + r % TR, (int64_t)a.head_tiles * TR, m, out_row(r),
                      lane);
 }
@@ -1121,9 +1127,11 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * wpg), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (MULTI)
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch),
+  if constexpr (MULTI) {
+    const int rows = a.wave_rows * a.head_tiles;   // rows of a virtual sequence: one per wave
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, (rows + kMergeWaves - 1) / kMergeWaves),
                        dim3(64 * kMergeWaves), 0, st, a);
+  }
   else
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
                        st, a);
