@@ -1201,8 +1201,8 @@ static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vc
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
                         int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st) {
   if (prefill) {
-    if ((q_dtype != PKV_F16 && q_dtype != PKV_BF16) ||
-        (kv_dtype != q_dtype && kv_dtype != PKV_FP8_E4M3FN) || (head_dim != 64 && head_dim != 128))
+    // (the cache types the prompt-chunk kernel takes are checked by launch_prefill)
+    if ((q_dtype != PKV_F16 && q_dtype != PKV_BF16) || (head_dim != 64 && head_dim != 128))
       return hipErrorInvalidValue;
     if (q_dtype == PKV_F16)
       return head_dim == 64

@@ -34,9 +34,11 @@
 //    kernel) and the split-K merge are those of the multi-token decode kernel
 //    (pkv_decode.hip): a virtual sequence here is a group of W * RT * 16 rows.
 //
-// Caches: 16-bit of the query's type (f16/f16, bf16/bf16), or FP8 E4M3FN with
-// f16 or bf16 queries (codes converted exactly after the LDS read, the
-// per-tensor scales folded into the logits and the output).
+// Caches: 16-bit of the query's type (f16/f16, bf16/bf16), FP8 E4M3FN (codes
+// converted exactly after the LDS read, the per-tensor scales folded into the
+// logits and the output) or INT8 with row scales (f16 queries: offset f16
+// subnormal codes, as in the decode kernel; bf16: exact conversion), with f16
+// or bf16 queries.
 #include <atomic>
 
 #include "pkv_common.h"
@@ -63,19 +65,28 @@ struct PrefillShape {
   static constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
   static constexpr int STEP = 4 * GB;             // K and V of two groups
   static constexpr int NB = PKV_PREFILL_DEPTH;    // LDS buffers: NB - 1 steps in flight
+  // INT8: each wave's copy of a step's 64 row scales (K g0, K g1, V g0, V g1)
+  static constexpr int SCW = KV == PKV_I8 ? kPrefillWaves : 1;
 };
 
 // One group of the plan: the W items (row tiles of one virtual sequence,
 // chunk of its context) starting at item0, one per wave.
-// KV: the cache's storage type, QT (f16 or bf16, the MFMA type) or FP8
-// E4M3FN (converted exactly after the LDS read).
+// KV: the cache's storage type, QT (f16 or bf16, the MFMA type), FP8 E4M3FN
+// (converted exactly after the LDS read) or INT8 with row scales (f16 queries:
+// offset f16 subnormal codes, the offsets taken back out; bf16: converted
+// exactly through f32).
 template <int QT, int KV, int D, int BS>
-__device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0,
-                                              uint8_t (*lds)[PrefillShape<KV, D>::STEP]) {
+__device__ __forceinline__ void prefill_group(
+    const DecodeArgs& a, int64_t item0, uint8_t (*lds)[PrefillShape<KV, D>::STEP],
+    float (*lds_sc)[PrefillShape<KV, D>::SCW][64]) {
   constexpr int MT = MfmaOf<QT>::value;
   static_assert(MT == MT_F16 || MT == MT_BF16, "f16 or bf16 queries");
-  static_assert(KV == QT || KV == PKV_FP8_E4M3FN, "a 16-bit cache of the query's type, or FP8");
+  static_assert(KV == QT || KV == PKV_FP8_E4M3FN || KV == PKV_I8,
+                "a 16-bit cache of the query's type, FP8 or INT8");
   constexpr bool fp8 = KV == PKV_FP8_E4M3FN;
+  constexpr bool i8 = KV == PKV_I8;
+  constexpr bool bytewide = fp8 || i8;     // one byte per element: 16 d per K chunk
+  constexpr bool offset = i8 && MT == MT_F16;   // INT8 codes as offset f16 subnormals
   using C = Cvt<KV, MT>;
   constexpr int W = kPrefillWaves;
   constexpr int RT = kPrefillRowTiles;
@@ -89,7 +100,8 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
   static_assert(NLD >= 1 && STEP % (16 * 64 * W) == 0, "step must split evenly over the threads");
   static_assert(GB % 1024 == 0, "a wave's loads stay inside one group");
   constexpr int NB = PrefillShape<KV, D>::NB;
-  static_assert(NB >= 2 && (NB - 2) * NLD <= 63, "vmcnt threshold");
+  constexpr int NLW = NLD + (i8 ? 1 : 0);   // loads per thread per step (INT8: + row scales)
+  static_assert(NB >= 2 && (NB - 2) * NLW <= 63, "vmcnt threshold");
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);         // (uniform: keeps the load addresses scalar)
@@ -168,8 +180,8 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
   // ---- query operands (lane: row r16 of each row tile, the d positions of
   // its K chunks) ----
   // Query operands, in the d order of the K operands: 16-bit K chunks carry
-  // d = 32 j + 8 c16 .. + 7 (quad j); FP8 K chunks carry d = 64 j + 16 c16 ..
-  // + 15 (quads 2 j and 2 j + 1 after conversion).
+  // d = 32 j + 8 c16 .. + 7 (quad j); FP8 and INT8 K chunks carry
+  // d = 64 j + 16 c16 .. + 15 (quads 2 j and 2 j + 1 after conversion).
   u32x4 qop[RT][KQ];                       // (quads: the MFMA's B operands as they are)
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
@@ -179,18 +191,40 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
       const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + hq[k] * D * 2;
 #pragma unroll
       for (int j = 0; j < KQ; ++j) {
-        const int d0 = fp8 ? 64 * (j / 2) + 16 * c16 + 8 * (j % 2) : 32 * j + 8 * c16;
+        const int d0 = bytewide ? 64 * (j / 2) + 16 * c16 + 8 * (j % 2) : 32 * j + 8 * c16;
         qop[k][j] = *reinterpret_cast<const u32x4*>(qrow + d0 * 2);
       }
     }
   }
   // logits in the exp2 domain; FP8: the per-tensor scales (K into the logits,
-  // V into the output)
+  // V into the output); INT8: per token, 1/s (s = 127 / absmax of the row)
+  // into the logit and into P.
   float kfac = a.scale * 1.4426950408889634f;
   float vfac = 1.0f;
   if constexpr (fp8) {
     kfac *= a.k_scale[0];
     vfac = a.v_scale[0];
+  }
+  // Offset codes: K enters the MFMA as (q + 128) 2^-24, so the logit is
+  // (2^24 S_mfma - 128 sum(q)) kfac / s, with sum(q) over the row's query as
+  // fed; V comes out as 2^-24 (sum p' q + 128 sum p'), with sum p' (the P
+  // values fed, p / s) from one more MFMA against ones.
+  const float kf24 = kfac * 16777216.0f;
+  float kbias[RT];
+#pragma unroll
+  for (int k = 0; k < RT; ++k) {
+    float qs = 0.f;
+    if constexpr (offset) {
+#pragma unroll
+      for (int j = 0; j < KQ; ++j) {
+        const f16x8 h = __builtin_bit_cast(f16x8, qop[k][j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qs += (float)h[e];
+      }
+      qs += __shfl_xor(qs, 16, kWave);
+      qs += __shfl_xor(qs, 32, kWave);
+    }
+    kbias[k] = -128.0f * qs * kfac;
   }
 
   // Per row: m_run, the reference the row's P values are taken against (exp2
@@ -202,12 +236,14 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
   constexpr float kLazy = 8.0f;
   f32x4 acc[RT][NC];
   f32x4 lsum[RT];
+  f32x4 accp[RT];                          // offset codes: sum of the P fed to PV
   float m_run[RT];
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
 #pragma unroll
     for (int nc = 0; nc < NC; ++nc) acc[k][nc] = f32x4{0.f, 0.f, 0.f, 0.f};
     lsum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accp[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = -__builtin_inff();
   }
 
@@ -244,6 +280,19 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
                                        (__attribute__((address_space(3))) void*)(&lds[buf][c0 * 16]),
                                        16, 0, 0);
     }
+    if constexpr (i8) {
+      // The step's row scales, 4 bytes per lane into this wave's copy: lane
+      // l is token l % 16 of group (l / 16) % 2 of K (l < 32) or V.
+      const int gsel = (lane >> 4) & 1;
+      const int phys = gsel ? p1 : p0;
+      const int tile = 2 * step + gsel;
+      const int64_t row =
+          phys >= 0 ? ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS) : 0;
+      const float* src = (lane < 32 ? a.k_scale : a.v_scale) + row + (lane & 15);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
+                                       (__attribute__((address_space(3))) void*)(&lds_sc[buf][wave][0]),
+                                       4, 0, 0);
+    }
   };
   // End of a step: this wave's LDS reads are done (lgkmcnt 0, so the buffer
   // can be refilled after the barrier) and its loads of the next step have
@@ -252,7 +301,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
   // flight; the empty asm statements keep the compiler from moving LDS
   // accesses across it.
   auto step_barrier = [](bool steady) {
-    constexpr int n = (NB - 2) * NLD;
+    constexpr int n = (NB - 2) * NLW;
     if (steady)
       __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));   // vmcnt(n) lgkmcnt(0)
     else
@@ -315,7 +364,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
-        if constexpr (fp8) {
+        if constexpr (bytewide) {
           uint32_t w[8];
           C::run(raw, w);
           kq[2 * j] = u32x4{w[0], w[1], w[2], w[3]};
@@ -338,10 +387,10 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     // (the first halves of all chunks, then the second halves: the empty asm
     // statement keeps the two halves of one 16-byte slot from being read as
     // one and copied apart).
-    // (FP8: a lane's 16 bytes hold four chunks of 4 bytes, each converted
-    // to two words; the operand is group 0's pair then group 1's.)
+    // (FP8, INT8: a lane's 16 bytes hold four chunks of 4 bytes, each
+    // converted to two words; the operand is group 0's pair then group 1's.)
     u32x4 va[NC];
-    if constexpr (fp8) {
+    if constexpr (bytewide) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const u32x4 r0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16 + 1024 * j);
@@ -373,6 +422,29 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     // scores gives the max logit.  Masked scores become -inf (a select: stale
     // slots may hold NaN), so their P is exp2(-inf) = 0.
     const int tok0 = t_begin + 2 * step * 16 + 4 * c16;
+    // INT8: the logits themselves (per-token factors), so kf = 1 below.
+    float kf = kfac;
+    f32x4 vr[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};   // INT8: 1 / s_v
+    if constexpr (i8) {
+      kf = 1.0f;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const f32x4 ks = *reinterpret_cast<const f32x4*>(&lds_sc[buf][wave][16 * gi + 4 * c16]);
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(&lds_sc[buf][wave][32 + 16 * gi + 4 * c16]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float kr = __builtin_amdgcn_rcpf(ks[i]);
+          vr[gi][i] = __builtin_amdgcn_rcpf(vs[i]);
+#pragma unroll
+          for (int k = 0; k < RT; ++k) {
+            if constexpr (offset)
+              s[k][gi][i] = __builtin_fmaf(s[k][gi][i], kf24, kbias[k]) * kr;
+            else
+              s[k][gi][i] = s[k][gi][i] * kfac * kr;
+          }
+        }
+      }
+    }
     if (checked) {
 #pragma unroll
       for (int k = 0; k < RT; ++k)
@@ -390,7 +462,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
     for (int k = 0; k < RT; ++k) {
       const float mx = fmax2(fmax4(s[k][0][0], s[k][0][1], s[k][0][2], s[k][0][3]),
                              fmax4(s[k][1][0], s[k][1][1], s[k][1][2], s[k][1][3]));
-      mz[k] = rows_max(mx) * kfac;
+      mz[k] = rows_max(mx) * kf;
       need = need || mz[k] > m_run[k] + kLazy;
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
@@ -402,6 +474,7 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
 #pragma unroll
         for (int nc = 0; nc < NC; ++nc) acc[k][nc] *= alpha;
         lsum[k] *= alpha;
+        if constexpr (offset) accp[k] *= alpha;
         m_run[k] = m_new;
       }
     }
@@ -416,9 +489,22 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kfac, -mref));
+          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kf, -mref));
       pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
+      if constexpr (i8) {
+        // P fed to PV: p / s_v (a masked token's p is 0, and its slot's scale
+        // may be anything: kept at 0)
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float pv = p[4 * gi + i] * vr[gi][i];
+            p[4 * gi + i] = checked ? (p[4 * gi + i] > 0.f ? pv : 0.f) : pv;
+          }
+        pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
+        if constexpr (offset) accp[k] = mfma32(ones, pb[k], accp[k]);
+      }
     }
 
     // O^T += V^T P^T, 32 tokens deep.  Slots past the context may hold
@@ -483,6 +569,10 @@ __device__ __forceinline__ void prefill_group(const DecodeArgs& a, int64_t item0
   for (int k = 0; k < RT; ++k) {
     const float l_tot = lsum[k][0];        // (every entry holds the row's sum)
     if (!head_ok[k]) continue;
+    if constexpr (offset) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) acc[k][nc] = acc[k][nc] * 16777216.0f - 128.0f * accp[k][0];
+    }
     if (whole_unit) {
       const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
 #pragma unroll
@@ -515,11 +605,12 @@ __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
 void prefill_kernel(DecodeArgs a) {
   using Sh = PrefillShape<KV, D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[Sh::NB][Sh::STEP];   // [K g0][K g1][V g0][V g1]
+  __shared__ __attribute__((aligned(16))) float lds_sc[Sh::NB][Sh::SCW][64];   // INT8 row scales
   const int x = blockIdx.x % 8;
   const int64_t per_xcd = gridDim.x / 8;
   const int64_t hi = a.plan_info[3 + x];
   for (int64_t grp = a.plan_info[2 + x] + blockIdx.x / 8; grp < hi; grp += per_xcd)
-    prefill_group<QT, KV, D, BS>(a, grp * kPrefillWaves, lds);
+    prefill_group<QT, KV, D, BS>(a, grp * kPrefillWaves, lds, lds_sc);
 }
 
 template <int QT, int KV, int D, int BS>
@@ -569,13 +660,25 @@ hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim
   if (a.head_tiles != kPrefillWaves || a.wave_rows != 16 * kPrefillRowTiles ||
       (head_dim != 64 && head_dim != 128))
     return hipErrorInvalidValue;
-  const bool fp8 = kv_dtype == PKV_FP8_E4M3FN;
-  if (q_dtype == PKV_F16 && (kv_dtype == PKV_F16 || fp8))
-    return fp8 ? launch_prefill1<PKV_F16, PKV_FP8_E4M3FN>(a, head_dim, block_size, num_cus, slots_only, st)
-               : launch_prefill1<PKV_F16, PKV_F16>(a, head_dim, block_size, num_cus, slots_only, st);
-  if (q_dtype == PKV_BF16 && (kv_dtype == PKV_BF16 || fp8))
-    return fp8 ? launch_prefill1<PKV_BF16, PKV_FP8_E4M3FN>(a, head_dim, block_size, num_cus, slots_only, st)
-               : launch_prefill1<PKV_BF16, PKV_BF16>(a, head_dim, block_size, num_cus, slots_only, st);
+  const int hd = head_dim, bs = block_size;
+  if (q_dtype == PKV_F16) {
+    switch (kv_dtype) {
+      case PKV_F16: return launch_prefill1<PKV_F16, PKV_F16>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_FP8_E4M3FN:
+        return launch_prefill1<PKV_F16, PKV_FP8_E4M3FN>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_I8: return launch_prefill1<PKV_F16, PKV_I8>(a, hd, bs, num_cus, slots_only, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (q_dtype == PKV_BF16) {
+    switch (kv_dtype) {
+      case PKV_BF16: return launch_prefill1<PKV_BF16, PKV_BF16>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_FP8_E4M3FN:
+        return launch_prefill1<PKV_BF16, PKV_FP8_E4M3FN>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_I8: return launch_prefill1<PKV_BF16, PKV_I8>(a, hd, bs, num_cus, slots_only, st);
+      default: return hipErrorInvalidValue;
+    }
+  }
   return hipErrorInvalidValue;
 }
 
