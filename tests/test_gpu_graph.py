@@ -52,10 +52,13 @@ def test_captured_decode_step_replays_bit_exact(kv):
         assert torch.equal(case.out, eager), f"replay {i} differs from the eager step"
 
 
-def test_captured_multi_query_replays_bit_exact():
+@pytest.mark.parametrize("q_lens", [[64, 100, 1], [4, 4, 4]])
+def test_captured_multi_query_replays_bit_exact(q_lens):
+    """[64, 100, 1]: 220 rows per sequence on average, the prompt-chunk kernel;
+    [4, 4, 4]: draft tokens, the multi-token decode kernel."""
     w = W.custom(torch.float16, "f16", [700, 1300, 260], 32, 8, 128, 16, name="graph-multi")
-    q_lens = np.array([64, 100, 1])
-    say(f"[graph] {w.name}")
+    q_lens = np.array(q_lens)
+    say(f"[graph] {w.name} L={q_lens.tolist()}")
     case = DeviceCase(w)
     g0 = torch.Generator(device="cuda")
     g0.manual_seed(3)
