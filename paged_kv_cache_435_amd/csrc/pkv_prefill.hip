@@ -345,19 +345,9 @@ __device__ __forceinline__ void prefill_group(
   // (uniform): the step may hold tokens past the context, past a row's causal
   // position or outside the pool, which are masked; only the masking is
   // conditional, so the accumulators never cross a branch. ----
-  auto compute = [&](bool checked, int step, int buf, int p0, int p1) {
+  // S^T = K Q^T for both groups of the step in LDS buffer `buf`.
+  auto qk = [&](int buf, f32x4 (&s)[RT][2]) {
     const uint8_t* base = lds[buf];
-    int n_valid[2] = {16, 16};
-    if (checked) {
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        int n = t_end - (t_begin + (2 * step + gi) * 16);
-        n = n > 16 ? 16 : (n < 0 ? 0 : n);
-        n_valid[gi] = (gi ? p1 : p0) < 0 ? 0 : n;
-      }
-    }
-    // S^T = K Q^T for both groups.
-    f32x4 s[RT][2];
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
       u32x4 kq[KQ];
@@ -378,6 +368,19 @@ __device__ __forceinline__ void prefill_group(
         s[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < KQ; ++c) s[k][gi] = mfma32(kq[c], qop[k][c], s[k][gi]);
+      }
+    }
+  };
+  // The rest of a step: softmax of its scores s, then PV.
+  auto finish = [&](bool checked, int step, int buf, int p0, int p1, f32x4 (&s)[RT][2]) {
+    const uint8_t* base = lds[buf];
+    int n_valid[2] = {16, 16};
+    if (checked) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        int n = t_end - (t_begin + (2 * step + gi) * 16);
+        n = n > 16 ? 16 : (n < 0 ? 0 : n);
+        n_valid[gi] = (gi ? p1 : p0) < 0 ? 0 : n;
       }
     }
     // V operands, read now so their latency hides behind the softmax.  Lane
@@ -528,8 +531,8 @@ __device__ __forceinline__ void prefill_group(
       for (int k = 0; k < RT; ++k) acc[k][nc] = mfma32(va[nc], pb[k], acc[k][nc]);
   };
 
-  // ---- the step loop: loads of step s + 1 in flight while step s is
-  // multiplied; one barrier per step ----
+  // ---- the step loop: loads of the next NB - 1 steps in flight while step s
+  // is multiplied; one barrier per step ----
   // Physical blocks of the tiles of the steps in LDS or in flight, by buffer.
   int phq0[NB], phq1[NB];
 #pragma unroll
@@ -555,9 +558,12 @@ __device__ __forceinline__ void prefill_group(
           step_phys(nx, phq0[nb], phq1[nb]);
           issue(nx, phq0[nb], phq1[nb], nb);
         }
-        if (wave_live)
-          compute(!(2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0), step, u, phq0[u],
-                  phq1[u]);
+        if (wave_live) {
+          f32x4 sc[RT][2];
+          qk(u, sc);
+          finish(!(2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0), step, u, phq0[u],
+                 phq1[u], sc);
+        }
         step_barrier(more);                        // step + 1 has landed everywhere
       }
     }
