@@ -86,9 +86,14 @@ struct MultiShape {
   int64_t waves;       // waves (row groups) per virtual sequence
   bool prefill;
 };
+#ifndef PKV_PREFILL_MIN_ROWS
+#define PKV_PREFILL_MIN_ROWS (16 * PKV_PREFILL_ROW_TILES * PKV_PREFILL_WAVES)
+#endif
 MultiShape multi_shape(int64_t batch, int64_t num_query_tokens, int64_t group, bool prefill_ok) {
   const int64_t rows = num_query_tokens * group;
-  if (prefill_ok && rows >= batch * 16 * pkv::kPrefillRowTiles * pkv::kPrefillWaves)
+  // (PKV_PREFILL_MIN_ROWS, a tuning knob: mean rows per sequence from which the
+  // prompt-chunk kernel is used; one workgroup's rows by default)
+  if (prefill_ok && rows >= batch * PKV_PREFILL_MIN_ROWS)
     return MultiShape{pkv::kPrefillRowTiles, pkv::kPrefillWaves, true};
   const int64_t tr = 16 * pkv::kMultiRowTiles;
   int64_t g = (rows + batch * tr - 1) / (batch * tr);
