@@ -509,11 +509,10 @@ void decode_partition_kernel(DecodeArgs a) {
           const bool ok = 4 * c16 + i < n_valid && t_begin + tile * 16 + 4 * c16 + i <= prow[k];
           z[i] = ok ? z[i] : -__builtin_inff();
         }
-        mx = fmaxf(mx, z[i]);
+        mx = fmax_ieee(mx, z[i]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-      const float m_new = fmaxf(m_run[k], mx);
+      mx = rows_max(mx);
+      const float m_new = fmax_ieee(m_run[k], mx);
       // A live tile has a finite max, so exp2(-inf) = 0 covers the first one.
       const bool live = !checked || m_new != -__builtin_inff();
       // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may

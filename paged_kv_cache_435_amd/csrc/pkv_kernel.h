@@ -154,13 +154,31 @@ __device__ __forceinline__ void store_out4(void* out, int64_t idx, float a, floa
   }
 }
 
+// Two f32 values -> a packed f16 or bf16 pair, round to nearest even (one
+// v_cvt_pk_f16_f32 / v_cvt_pk_bf16_f32 on gfx950).
 template <int MT>
 __device__ __forceinline__ uint32_t pack_p(float a, float b) {
+  const f32x2 v = {a, b};
   if constexpr (MT == MT_F16) {
-    return (uint32_t)f32_to_f16(a) | ((uint32_t)f32_to_f16(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
   } else {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
   }
+}
+
+// IEEE maximum: no operand canonicalisation (which fmaxf costs on MFMA
+// results).  The softmax takes it over scores that are finite or -inf.
+__device__ __forceinline__ float fmax_ieee(float x, float y) {
+  return __builtin_elementwise_maximum(x, y);
+}
+
+// Max of a value over the four 16-lane rows of a wave (lanes L, L ^ 16,
+// L ^ 32, L ^ 48): gfx950's row swaps, no LDS round trip.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto x16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
+  v = fmax_ieee(bitsf(x16[0]), bitsf(x16[1]));
+  const auto x32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
+  return fmax_ieee(bitsf(x32[0]), bitsf(x32[1]));
 }
 
 // ---------------------------------------------------------------------------

@@ -311,25 +311,11 @@ __device__ __forceinline__ void prefill_group(
     asm volatile("" ::: "memory");
   };
 
-  // Max of a value over the four 16-lane rows (lanes L, L ^ 16, L ^ 32, L ^ 48):
-  // gfx950's row swaps, no LDS round trip.
-  // (IEEE maximum: no operand canonicalisation, which fmaxf costs on MFMA
-  // results; scores here are finite or -inf, never NaN)
-  auto fmax2 = [](float x, float y) { return __builtin_elementwise_maximum(x, y); };
+  // (scores here are finite or -inf, never NaN: IEEE maximum and the row
+  // swaps of pkv_kernel.h)
+  auto fmax2 = [](float x, float y) { return fmax_ieee(x, y); };
   auto fmax4 = [&](float x, float y, float z, float w) { return fmax2(fmax2(x, y), fmax2(z, w)); };
-  auto rows_max = [&](float v) -> float {
-    const auto x16 = __builtin_amdgcn_permlane16_swap(fbits(v), fbits(v), false, false);
-    v = fmax2(bitsf(x16[0]), bitsf(x16[1]));
-    const auto x32 = __builtin_amdgcn_permlane32_swap(fbits(v), fbits(v), false, false);
-    return fmax2(bitsf(x32[0]), bitsf(x32[1]));
-  };
-  auto pack2 = [](float x, float y) -> uint32_t {   // round to nearest even
-    const f32x2 v = {x, y};
-    if constexpr (MT == MT_F16)
-      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
-    else
-      return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-  };
+  auto pack2 = [](float x, float y) -> uint32_t { return pack_p<MT>(x, y); };
   const uint32_t one2 = MT == MT_F16 ? 0x3C003C00u : 0x3F803F80u;   // (1, 1) as f16 / bf16
   const u32x4 ones = {one2, one2, one2, one2};
   auto mfma32 = [](const u32x4& x, const u32x4& y, const f32x4& c) -> f32x4 {
