@@ -205,7 +205,10 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
 /*
  * paged_attention_multi_workspace_size — bytes of device scratch
  * paged_attention_multi_query needs for these sizes (never 0 for valid sizes:
- * the call keeps its row-tile plan there).  Host only.  0 for invalid sizes.
+ * the call keeps its work plan there — virtual sequences, an item map — and,
+ * when contexts are long enough to be cut, partial rows for the merge).  The
+ * size depends on the sizes only, not on the dtypes: it covers either kernel
+ * the call may take.  Host only.  0 for invalid sizes.
  */
 size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tokens,
                                             int32_t num_q_heads, int32_t num_kv_heads,
@@ -232,8 +235,13 @@ size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tok
  *   workspace     device scratch of paged_attention_multi_workspace_size(...) bytes,
  *                 256-byte aligned; contents overwritten; calls that share it
  *                 must be ordered.
- *   Supported: as paged_attention_decode.  L_b = 1 for every b gives exactly
- *   the decode result.
+ *   Supported: as paged_attention_decode, and num_query_tokens x (num_q_heads /
+ *   num_kv_heads) < 2^31 - 4096.  Calls with several tokens per sequence and a
+ *   mean of at least 128 (query token, head) rows per sequence, f16 or bf16
+ *   queries and a cache of the query's type, FP8 or INT8 (prompt chunks) run
+ *   on a kernel that shares each K/V step among 128 rows through LDS; all other
+ *   calls (draft verification, INT4 and f32 caches) on the decode kernel.
+ *   L_b = 1 for every b gives exactly the decode result.
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  */
 pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype, int32_t batch,

@@ -92,8 +92,10 @@ struct MultiShape {
 MultiShape multi_shape(int64_t batch, int64_t num_query_tokens, int64_t group, bool prefill_ok) {
   const int64_t rows = num_query_tokens * group;
   // (PKV_PREFILL_MIN_ROWS, a tuning knob: mean rows per sequence from which the
-  // prompt-chunk kernel is used; one workgroup's rows by default)
-  if (prefill_ok && rows >= batch * PKV_PREFILL_MIN_ROWS)
+  // prompt-chunk kernel is used; one workgroup's rows by default.  One token
+  // per sequence always takes the decode-shaped kernel, whose result is then
+  // exactly paged_attention_decode's.)
+  if (prefill_ok && num_query_tokens > batch && rows >= batch * PKV_PREFILL_MIN_ROWS)
     return MultiShape{pkv::kPrefillRowTiles, pkv::kPrefillWaves, true};
   const int64_t tr = 16 * pkv::kMultiRowTiles;
   int64_t g = (rows + batch * tr - 1) / (batch * tr);

@@ -100,8 +100,12 @@ def test_chunked_prefill_and_block_sizes(bs):
     run_multi(w, [256, 100, 260])
 
 
-def test_one_token_each_equals_decode():
-    w = W.custom(torch.float16, "f16", [5, 900, 3000, 17], 16, 2, 128, 16, name="L1")
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (128, 1)])
+def test_one_token_each_equals_decode(hq, hkv):
+    """(128 query heads over one KV head: 128 rows per sequence, which would
+    reach the prompt-chunk kernel's threshold; one token per sequence stays on
+    the decode-shaped kernel, bit for bit equal to decode.)"""
+    w = W.custom(torch.float16, "f16", [5, 900, 3000, 17], hq, hkv, 128, 16, name=f"L1-{hq}x{hkv}")
     got, case, q, starts = run_multi(w, [1, 1, 1, 1])
     dec = torch.empty_like(case.q)
     pkv.paged_attention_decode(dec, q.cuda(), case.k_cache, case.v_cache, case.block_tables,
