@@ -238,9 +238,9 @@ size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tok
  *   Supported: as paged_attention_decode, and num_query_tokens x (num_q_heads /
  *   num_kv_heads) < 2^31 - 4096.  Calls with several tokens per sequence and a
  *   mean of at least 128 (query token, head) rows per sequence, f16 or bf16
- *   queries and a cache of the query's type, FP8 or INT8 (prompt chunks) run
- *   on a kernel that shares each K/V step among 128 rows through LDS; all other
- *   calls (draft verification, INT4 and f32 caches) on the decode kernel.
+ *   queries and a cache of the query's type, FP8, INT8 or INT4 (prompt chunks)
+ *   run on a kernel that shares each K/V step among 128 rows through LDS; all
+ *   other calls (draft verification, f32 caches) on the decode kernel.
  *   L_b = 1 for every b gives exactly the decode result.
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  */

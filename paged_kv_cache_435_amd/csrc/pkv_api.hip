@@ -76,7 +76,7 @@ constexpr int32_t kSwapDmaRuns = 32;
 // head of its group), are cut into virtual sequences, the planner's unit of
 // work, each run as one workgroup whose waves read every K/V tile together.
 // Two shapes: prompt chunks (a mean of at least one workgroup's rows per
-// sequence, f16/bf16 queries over a cache of their type, FP8 or INT8) take the
+// sequence, f16/bf16 queries over a cache of their type, FP8, INT8 or INT4) take the
 // LDS-sharing kernel, kPrefillWaves waves of kPrefillRowTiles 16-row tiles;
 // everything else takes the multi-token decode kernel, whose waves hold
 // kMultiRowTiles tiles and whose group size follows the mean rows per
@@ -104,8 +104,9 @@ MultiShape multi_shape(int64_t batch, int64_t num_query_tokens, int64_t group, b
 }
 bool prefill_types(int32_t q_dtype, int32_t kv_dtype, int32_t head_dim) {
   return (q_dtype == PKV_F16 || q_dtype == PKV_BF16) &&
-         (kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3FN || kv_dtype == PKV_I8) &&
-         (head_dim == 64 || head_dim == 128);
+         (((kv_dtype == q_dtype || kv_dtype == PKV_FP8_E4M3FN || kv_dtype == PKV_I8) &&
+           (head_dim == 64 || head_dim == 128)) ||
+          (kv_dtype == PKV_I4 && head_dim == 128));
 }
 int64_t multi_vseqs(int64_t batch, int64_t num_query_tokens, int64_t group, int64_t kv_heads,
                     const MultiShape& sh) {

@@ -101,7 +101,7 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
 // Multi-query: a.batch = virtual sequences (upper bound), a.context_lens =
 // vctx (written by the prep kernel first), batch_real real sequences.
 // prefill: the LDS-sharing kernel (a.head_tiles = kPrefillWaves, a.wave_rows =
-// 16 kPrefillRowTiles; 16-bit caches of the query's type, FP8 or INT8), else the
+// 16 kPrefillRowTiles; 16-bit caches of the query's type, FP8, INT8 or INT4), else the
 // multi-token decode kernel (a.wave_rows = 16 kMultiRowTiles).
 hipError_t launch_multi(DecodeArgs& a, int batch_real, int32_t* vctx, int q_dtype, int kv_dtype,
                         int head_dim, int block_size, int num_cus, bool prefill, hipStream_t st);

@@ -66,7 +66,7 @@ struct PrefillShape {
   static constexpr int STEP = 4 * GB;             // K and V of two groups
   static constexpr int NB = PKV_PREFILL_DEPTH;    // LDS buffers: NB - 1 steps in flight
   // INT8: each wave's copy of a step's 64 row scales (K g0, K g1, V g0, V g1)
-  static constexpr int SCW = KV == PKV_I8 ? kPrefillWaves : 1;
+  static constexpr int SCW = row_scaled(KV) ? kPrefillWaves : 1;
 };
 
 // One group of the plan: the W items (row tiles of one virtual sequence,
@@ -81,12 +81,14 @@ __device__ __forceinline__ void prefill_group(
     float (*lds_sc)[PrefillShape<KV, D>::SCW][64]) {
   constexpr int MT = MfmaOf<QT>::value;
   static_assert(MT == MT_F16 || MT == MT_BF16, "f16 or bf16 queries");
-  static_assert(KV == QT || KV == PKV_FP8_E4M3FN || KV == PKV_I8,
-                "a 16-bit cache of the query's type, FP8 or INT8");
+  static_assert(KV == QT || KV == PKV_FP8_E4M3FN || KV == PKV_I8 || (KV == PKV_I4 && D == 128),
+                "a 16-bit cache of the query's type, FP8, INT8 or INT4 (d 128)");
   constexpr bool fp8 = KV == PKV_FP8_E4M3FN;
-  constexpr bool i8 = KV == PKV_I8;
-  constexpr bool bytewide = fp8 || i8;     // one byte per element: 16 d per K chunk
-  constexpr bool offset = i8 && MT == MT_F16;   // INT8 codes as offset f16 subnormals
+  constexpr bool i4 = KV == PKV_I4;
+  constexpr bool i8 = row_scaled(KV);      // INT8 or INT4: row scales (names below say i8)
+  constexpr bool bytewide = fp8 || KV == PKV_I8;   // one byte per element: 16 d per K chunk
+  constexpr bool offset = i8 && MT == MT_F16;      // codes as offset f16 subnormals
+  constexpr float code_offset = i4 ? 8.0f : 128.0f;
   using C = Cvt<KV, MT>;
   constexpr int W = kPrefillWaves;
   constexpr int RT = kPrefillRowTiles;
@@ -181,7 +183,8 @@ __device__ __forceinline__ void prefill_group(
   // its K chunks) ----
   // Query operands, in the d order of the K operands: 16-bit K chunks carry
   // d = 32 j + 8 c16 .. + 7 (quad j); FP8 and INT8 K chunks carry
-  // d = 64 j + 16 c16 .. + 15 (quads 2 j and 2 j + 1 after conversion).
+  // d = 64 j + 16 c16 .. + 15 (quads 2 j and 2 j + 1 after conversion); an
+  // INT4 chunk carries d = 32 c16 .. + 31, word j as quad j.
   u32x4 qop[RT][KQ];                       // (quads: the MFMA's B operands as they are)
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
@@ -189,10 +192,24 @@ __device__ __forceinline__ void prefill_group(
     for (int j = 0; j < KQ; ++j) qop[k][j] = u32x4{0u, 0u, 0u, 0u};
     if (head_ok[k]) {
       const uint8_t* qrow = static_cast<const uint8_t*>(a.q) + hq[k] * D * 2;
+      if constexpr (i4) {
+        // INT4: the lane's K chunk holds d = 32 c16 .. 32 c16 + 31, and input
+        // word j converts to elements 8 j + (0 4 1 5 2 6 3 7): q pairs are
+        // taken in that order.
 #pragma unroll
-      for (int j = 0; j < KQ; ++j) {
-        const int d0 = bytewide ? 64 * (j / 2) + 16 * c16 + 8 * (j % 2) : 32 * j + 8 * c16;
-        qop[k][j] = *reinterpret_cast<const u32x4*>(qrow + d0 * 2);
+        for (int j = 0; j < KQ; ++j) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + (32 * c16 + 8 * j) * 2);
+          qop[k][j] = u32x4{__builtin_amdgcn_perm(w[2], w[0], 0x05040100u),
+                            __builtin_amdgcn_perm(w[2], w[0], 0x07060302u),
+                            __builtin_amdgcn_perm(w[3], w[1], 0x05040100u),
+                            __builtin_amdgcn_perm(w[3], w[1], 0x07060302u)};
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < KQ; ++j) {
+          const int d0 = bytewide ? 64 * (j / 2) + 16 * c16 + 8 * (j % 2) : 32 * j + 8 * c16;
+          qop[k][j] = *reinterpret_cast<const u32x4*>(qrow + d0 * 2);
+        }
       }
     }
   }
@@ -205,10 +222,11 @@ __device__ __forceinline__ void prefill_group(
     kfac *= a.k_scale[0];
     vfac = a.v_scale[0];
   }
-  // Offset codes: K enters the MFMA as (q + 128) 2^-24, so the logit is
-  // (2^24 S_mfma - 128 sum(q)) kfac / s, with sum(q) over the row's query as
-  // fed; V comes out as 2^-24 (sum p' q + 128 sum p'), with sum p' (the P
-  // values fed, p / s) from one more MFMA against ones.
+  // Offset codes: K enters the MFMA as (q + o) 2^-24 (o = 128 for INT8, 8
+  // for INT4), so the logit is (2^24 S_mfma - o sum(q)) kfac / s, with sum(q)
+  // over the row's query (INT4: at full weight); V comes out as
+  // 2^-24 (sum p' q + o sum p') (2^-20 for INT4's odd column blocks), with
+  // sum p' (the P values fed, p / s) from one more MFMA against ones.
   const float kf24 = kfac * 16777216.0f;
   float kbias[RT];
 #pragma unroll
@@ -217,14 +235,23 @@ __device__ __forceinline__ void prefill_group(
     if constexpr (offset) {
 #pragma unroll
       for (int j = 0; j < KQ; ++j) {
-        const f16x8 h = __builtin_bit_cast(f16x8, qop[k][j]);
+        f16x8 h = __builtin_bit_cast(f16x8, qop[k][j]);
+        if constexpr (i4) {
+          // INT4 high nibbles (odd words) enter as (q + 8) 2^-20: the query
+          // words that meet them are taken at 1/16, a power of two.
+          const f16x8 w16 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0625f, (_Float16)0.0625f,
+                             (_Float16)1.0f, (_Float16)1.0f, (_Float16)0.0625f, (_Float16)0.0625f};
+          h = h * w16;
+          qop[k][j] = __builtin_bit_cast(u32x4, h);
+        }
+        // (sum of the words as fed, the scaled ones at 16 times their value)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qs += (float)h[e];
+        for (int e = 0; e < 8; ++e) qs += (i4 && (e & 2)) ? 16.0f * (float)h[e] : (float)h[e];
       }
       qs += __shfl_xor(qs, 16, kWave);
       qs += __shfl_xor(qs, 32, kWave);
     }
-    kbias[k] = -128.0f * qs * kfac;
+    kbias[k] = -code_offset * qs * kfac;
   }
 
   // Per row: m_run, the reference the row's P values are taken against (exp2
@@ -340,7 +367,14 @@ __device__ __forceinline__ void prefill_group(
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
-        if constexpr (bytewide) {
+        if constexpr (i4) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            uint32_t w[4];
+            C::word(raw[c], w);
+            kq[c] = u32x4{w[0], w[1], w[2], w[3]};
+          }
+        } else if constexpr (bytewide) {
           uint32_t w[8];
           C::run(raw, w);
           kq[2 * j] = u32x4{w[0], w[1], w[2], w[3]};
@@ -379,7 +413,21 @@ __device__ __forceinline__ void prefill_group(
     // (FP8, INT8: a lane's 16 bytes hold four chunks of 4 bytes, each
     // converted to two words; the operand is group 0's pair then group 1's.)
     u32x4 va[NC];
-    if constexpr (bytewide) {
+    if constexpr (i4) {
+      // INT4: word w of a lane's 16 bytes converts to column blocks 2 w
+      // (words 0, 2 of the result) and 2 w + 1 (words 1, 3), each as tokens
+      // (0, 2), (1, 3) of the lane's four (P is packed in that order).
+      const u32x4 r0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16);
+      const u32x4 r1 = *reinterpret_cast<const u32x4*>(base + 3 * GB + lane * 16);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t w0[4], w1[4];
+        C::word(r0[w], w0);
+        C::word(r1[w], w1);
+        va[2 * w] = u32x4{w0[0], w0[2], w1[0], w1[2]};
+        va[2 * w + 1] = u32x4{w0[1], w0[3], w1[1], w1[3]};
+      }
+    } else if constexpr (bytewide) {
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         const u32x4 r0 = *reinterpret_cast<const u32x4*>(base + 2 * GB + lane * 16 + 1024 * j);
@@ -491,14 +539,18 @@ __device__ __forceinline__ void prefill_group(
             const float pv = p[4 * gi + i] * vr[gi][i];
             p[4 * gi + i] = checked ? (p[4 * gi + i] > 0.f ? pv : 0.f) : pv;
           }
-        pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
+        if constexpr (i4)   // (token order of the INT4 V operand)
+          pb[k] = u32x4{pack2(p[0], p[2]), pack2(p[1], p[3]), pack2(p[4], p[6]), pack2(p[5], p[7])};
+        else
+          pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
         if constexpr (offset) accp[k] = mfma32(ones, pb[k], accp[k]);
       }
     }
 
     // O^T += V^T P^T, 32 tokens deep.  Slots past the context may hold
-    // anything: their V values are zeroed.
-    if (checked) {
+    // anything: their V values are zeroed (INT8/INT4 codes are finite and P
+    // is 0 there, and INT4's token order differs: no mask).
+    if (!i8 && checked) {
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         const int cnt = n_valid[gi] - 4 * c16;
@@ -563,7 +615,9 @@ __device__ __forceinline__ void prefill_group(
     if (!head_ok[k]) continue;
     if constexpr (offset) {
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) acc[k][nc] = acc[k][nc] * 16777216.0f - 128.0f * accp[k][0];
+      for (int nc = 0; nc < NC; ++nc)
+        acc[k][nc] = acc[k][nc] * ((i4 && (nc & 1)) ? 1048576.0f : 16777216.0f) -
+                     code_offset * accp[k][0];
     }
     if (whole_unit) {
       const float inv = l_tot > 0.f ? vfac / l_tot : 0.f;
@@ -659,6 +713,9 @@ hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim
       case PKV_FP8_E4M3FN:
         return launch_prefill1<PKV_F16, PKV_FP8_E4M3FN>(a, hd, bs, num_cus, slots_only, st);
       case PKV_I8: return launch_prefill1<PKV_F16, PKV_I8>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_I4:
+        return hd == 128 ? launch_prefill2<PKV_F16, PKV_I4, 128>(a, bs, num_cus, slots_only, st)
+                         : hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }
@@ -668,6 +725,9 @@ hipError_t launch_prefill(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim
       case PKV_FP8_E4M3FN:
         return launch_prefill1<PKV_BF16, PKV_FP8_E4M3FN>(a, hd, bs, num_cus, slots_only, st);
       case PKV_I8: return launch_prefill1<PKV_BF16, PKV_I8>(a, hd, bs, num_cus, slots_only, st);
+      case PKV_I4:
+        return hd == 128 ? launch_prefill2<PKV_BF16, PKV_I4, 128>(a, bs, num_cus, slots_only, st)
+                         : hipErrorInvalidValue;
       default: return hipErrorInvalidValue;
     }
   }

@@ -171,7 +171,7 @@ NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70
 #   llama70b_prefill512 8 sequences of the 70B GQA-8 shape, cached prefixes
 #                       U[0, 4096] (seed 0) and a 512-token prompt chunk each
 MULTI_NAMES = ("llama70b_verify4", "llama70b_prefill512", "llama70b_prefill512_fp8",
-               "llama70b_prefill512_i8")
+               "llama70b_prefill512_i8", "llama70b_prefill512_i4")
 
 
 def make_multi(name):
@@ -179,14 +179,15 @@ def make_multi(name):
         w = make("llama70b_gqa8")
         w.name, w.appends = name, False
         return w, np.full(w.batch, 4, dtype=np.int64)
-    if name in ("llama70b_prefill512", "llama70b_prefill512_fp8", "llama70b_prefill512_i8"):
+    if name in ("llama70b_prefill512", "llama70b_prefill512_fp8", "llama70b_prefill512_i8",
+                "llama70b_prefill512_i4"):
         # 512-token prompt chunks of 8 sequences with prefixes U[0, 4096]; f16
-        # queries over an f16, FP8 E4M3FN or INT8 cache
+        # queries over an f16, FP8 E4M3FN, INT8 or INT4 cache
         prefix = np.random.default_rng(0).integers(0, 4096, 8, endpoint=True)
         ctx = (prefix + 512).astype(np.int32)
         bs = 16
         nb = pool_for(ctx, bs)
-        fmt = {"fp8": "fp8", "i8": "i8"}.get(name.rsplit("_", 1)[-1], "f16")
+        fmt = {"fp8": "fp8", "i8": "i8", "i4": "i4"}.get(name.rsplit("_", 1)[-1], "f16")
         w = Workload(name, torch.float16, fmt, 8, 64, 8, 128, bs, 1, ctx, nb,
                      deal_blocks(ctx, bs, nb), appends=False,
                      seeds=dict(context=0, permutation=1, q=2, k=3, v=4, new=6))

@@ -157,8 +157,8 @@ def test_sequences_without_new_tokens_are_skipped():
 
 
 # Prompt chunks: a mean of several hundred (query token, head) rows per
-# sequence, f16/bf16 queries over a cache of their type, FP8 or INT8, so the
-# calls take the LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
+# sequence, f16/bf16 queries over a cache of their type, FP8, INT8 or INT4, so
+# the calls take the LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
 # new tokens, one with more new tokens than cached ones (rows before the
 # cache), a whole prompt (L = context), both block sizes, d 64 and 128, GQA,
 # MHA and MQA.
@@ -173,12 +173,15 @@ def test_sequences_without_new_tokens_are_skipped():
     (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], "i8"),
     (torch.bfloat16, 128, 256, 16, 1, [300, 129], [64, 129], "i8"),
     (torch.float16, 64, 256, 4, 4, [600, 1000], [600, 400], "i8"),
+    (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], "i4"),
+    (torch.bfloat16, 128, 256, 16, 1, [300, 129], [64, 129], "i4"),
+    (torch.float16, 128, 256, 4, 4, [600, 1000], [600, 400], "i4"),
 ])
 def test_prompt_chunks(q_dtype, d, bs, hq, hkv, ctx, lens, kv):
     """(FP8 rows: the same kernel over an FP8 E4M3FN cache, codes converted
-    after the LDS read.  INT8 rows: row-scaled codes, offset f16 subnormals
-    with f16 queries, exact bf16 with bf16 queries; unused slots' scales are
-    NaN.)"""
+    after the LDS read.  INT8 and INT4 rows: row-scaled codes, offset f16
+    subnormals with f16 queries, exact bf16 with bf16 queries; unused slots'
+    scales are NaN.)"""
     kv = kv or ("f16" if q_dtype == torch.float16 else "bf16")
     w = W.custom(q_dtype, kv, ctx, hq, hkv, d, bs, name=f"prompt-{kv}-d{d}-bs{bs}-{hq}x{hkv}")
     got, _, _, starts = run_multi(w, lens)
