@@ -13,7 +13,9 @@
 //    group.  Every wave plans the cut itself from the device-resident context
 //    lengths, so that one round of near-equal items fills the waves the GPU
 //    runs at once (ragged batches otherwise leave a tail of stragglers).
-//    Items are dealt to the 8 XCDs in contiguous ranges.
+//    Items are dealt to the 8 XCDs in contiguous ranges, and the KV heads of
+//    one (sequence, chunk) go to the waves of one workgroup, so that adjacent
+//    (block, head) tiles are read together.
 //  * The cache stores each 16-token group of a (block, KV head) tile in MFMA
 //    operand order (pkv_common.h: k_group_offset, v_group_offset), so K and V
 //    are both read with 16 B per lane and 1 KB contiguous per instruction
@@ -107,7 +109,7 @@ namespace pkv {
 // The tile loop is software-pipelined: while tile i is converted and
 // multiplied, the K/V loads of the next tiles are already in flight (register
 // sets used in rotation, the loop unrolled so no register copy waits on a
-// load).  The workgroup is one wave and needs no LDS.
+// load).  The waves of a workgroup are independent and need no LDS.
 // ---------------------------------------------------------------------------
 // Lane L of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
 template <int L>
@@ -153,7 +155,7 @@ struct Tuning {
 // (written by multi_prep_kernel).  A wave takes one 32-row tile; the
 // head_tiles waves of a group form one workgroup.
 template <int KV, int QT, int D, int BS, bool MULTI>
-__global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64)
+__global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64 * kDecodeWaves)
 __attribute__((amdgpu_waves_per_eu(MULTI ? PKV_MULTI_WAVES_PER_EU : Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
@@ -175,11 +177,14 @@ void decode_partition_kernel(DecodeArgs a) {
   const int c16 = lane >> 4;   // MFMA k-group of this lane
 
   // ---- which item: contiguous item ranges per XCD (workgroups go round-robin
-  // over the 8 XCDs, so blockIdx % 8 is the XCD).  A multi-token workgroup is
-  // head_tiles waves taking aligned consecutive items: the row tiles of one
-  // (virtual sequence, KV head, chunk), which read the same K/V tiles in step,
-  // so the copies after the first come from the CU's caches. ----
-  const int wpg = MULTI ? a.head_tiles : 1;           // waves per workgroup
+  // over the 8 XCDs, so blockIdx % 8 is the XCD).  A workgroup's waves take
+  // aligned consecutive items.  Multi-token: head_tiles waves, the row tiles of
+  // one (virtual sequence, KV head, chunk), which read the same K/V tiles in
+  // step, so the copies after the first come from the CU's caches.  Decode:
+  // kDecodeWaves waves, the KV heads of one (sequence, chunk), which read
+  // adjacent tiles of the same blocks.  The waves share nothing (no LDS, no
+  // barrier), so any of them may stop early. ----
+  const int wpg = MULTI ? a.head_tiles : kDecodeWaves;   // waves per workgroup
   Plan plan;
   if constexpr (MULTI) {
     plan.items = planned_items(a);                    // made by multi_prep_kernel
@@ -202,9 +207,9 @@ void decode_partition_kernel(DecodeArgs a) {
   }
   b = uni(b);
   const int local = uni((int)(item - sq.first));   // < m * units per sequence
-  const int per_g = sq.m * a.head_tiles;
-  const int g = MULTI ? uni(a.vseq_g[b]) : uni(local / per_g);
-  const int chunk = uni((local % per_g) / a.head_tiles);
+  const int upc = a.plan_heads * a.head_tiles;       // items per chunk
+  const int g = MULTI ? uni(a.vseq_g[b]) : uni((local % upc) / a.head_tiles);
+  const int chunk = uni(local / upc);
   const int ht = uni(local % a.head_tiles);
   const int ctx = uni(sq.ctx);
   const int t_begin = uni((int)((int64_t)chunk * sq.n / sq.m) * kTileTokens);
@@ -805,10 +810,11 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int g = h / G;
   const int ht = (h % G) / 16;
   const int r = (h % G) % 16;
-  // Partial row of chunk c: item (first + (g*m + c)*head_tiles + ht), head r.
-  if (first + ((int64_t)g * m + m - 1) * a.head_tiles + ht >= a.max_items) return;
-  merge_row<QT, D>(a, (first + (int64_t)g * m * a.head_tiles + ht) * 16 + r,
-                   (int64_t)a.head_tiles * 16, m, hq, lane);
+  // Partial row of chunk c: item (first + (c*plan_heads + g)*head_tiles + ht), head r.
+  const int64_t upc = (int64_t)a.plan_heads * a.head_tiles;
+  if (first + ((int64_t)(m - 1) * a.plan_heads + g) * a.head_tiles + ht >= a.max_items) return;
+  merge_row<QT, D>(a, (first + (int64_t)g * a.head_tiles + ht) * 16 + r, upc * 16, m, hq,
+                   lane);
 }
 
 // Several query tokens per sequence: one workgroup of 8 waves per virtual
@@ -1115,7 +1121,7 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   const int64_t units = (int64_t)a.plan_heads * a.head_tiles;
   // The workspace was sized for kMaxSlots; fewer slots never need more items.
   const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
-  const int wpg = MULTI ? a.head_tiles : 1;
+  const int wpg = MULTI ? a.head_tiles : kDecodeWaves;
   const int64_t grid = ((need + wpg - 1) / wpg + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if constexpr (MULTI) {

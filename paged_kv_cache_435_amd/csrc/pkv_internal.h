@@ -26,6 +26,14 @@ constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
 #ifndef PKV_MULTI_GROUP_MAX
 #define PKV_MULTI_GROUP_MAX 4
 #endif
+// One-token decode: waves per workgroup.  A workgroup takes consecutive items,
+// which are the KV heads of one (sequence, chunk): its waves then read the
+// same blocks' adjacent (block, head) tiles at about the same time, which
+// HBM serves faster than the same bytes spread over unrelated blocks.
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 8
+#endif
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 constexpr int kMultiRowTiles = PKV_MULTI_ROW_TILES;
 constexpr int kMultiGroupMax = PKV_MULTI_GROUP_MAX;
 // Prompt chunks (many rows per sequence, 16-bit caches): waves per workgroup

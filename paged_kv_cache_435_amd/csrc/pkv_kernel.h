@@ -290,11 +290,12 @@ __device__ inline Plan make_plan(const DecodeArgs& a, int lane) {
   return p;
 }
 
-// Items of a sequence are numbered g-major, then by chunk, then by head tile:
-// item = first + (g * m + c) * head_tiles + ht, with m = ceil(n / tpi) chunks of
-// the sequence's n tiles per unit; chunk c covers tiles [c*n/m, (c+1)*n/m).
-// (g runs over plan_heads KV heads: all of them for decode, one for a
-// multi-token virtual sequence, which carries its own.)
+// Items of a sequence are numbered chunk-major, then by KV head, then by head
+// tile: item = first + (c * plan_heads + g) * head_tiles + ht, with
+// m = ceil(n / tpi) chunks of the sequence's n tiles per unit; chunk c covers
+// tiles [c*n/m, (c+1)*n/m).  (g runs over plan_heads KV heads: all of them for
+// decode, one for a multi-token virtual sequence, which carries its own.)
+// Consecutive items thus read the same blocks, one (block, KV head) tile each.
 struct SeqItems {
   int64_t first;   // number of the sequence's first item
   int ctx;         // clamped context length
