@@ -119,8 +119,75 @@ def decode_traffic(workload):
                for k in DECODE_KERNELS)
 
 
-def kernel_launch_times(pairs):
-    return [a.elapsed_time(b) * 1e-3 for a, b in pairs]   # seconds
+class LaunchEvents:
+    """Timing-only HIP events recorded on the launch stream (the current torch
+    stream when recorded), made before the timed loop.
+
+    They are created with hipEventDisableSystemFence: recording one then does
+    not write back and invalidate the caches, as a default event does, which
+    delays the next kernel and starts it on cold caches.  They are read only
+    after a device-wide synchronize, so they need no fence of their own.  The
+    HIP runtime is the one torch has loaded (same soname)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n):
+        import ctypes
+        import torch
+        self._c, self._torch = ctypes, torch
+        try:
+            hip = ctypes.CDLL("libamdhip64.so.7")
+        except OSError as e:
+            raise RuntimeError(f"HIP runtime not found for timing events: {e}")
+        hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self._hip = hip
+        self.pairs = [(self._make(), self._make()) for _ in range(n)]
+        self.used = 0
+
+    def _make(self):
+        e = self._c.c_void_p()
+        st = self._hip.hipEventCreateWithFlags(self._c.byref(e), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+        return e
+
+    def _record(self, e):
+        st = self._hip.hipEventRecord(e, self._c.c_void_p(
+            self._torch.cuda.current_stream().cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def begin(self):
+        """Record the start of the next pair; returns its index."""
+        if self.used >= len(self.pairs):
+            raise RuntimeError("more timed launches than events made")
+        i = self.used
+        self.used += 1
+        self._record(self.pairs[i][0])
+        return i
+
+    def end(self, i):
+        self._record(self.pairs[i][1])
+
+    def seconds(self):
+        """Durations of the recorded pairs (call after a synchronize)."""
+        out = []
+        for a, b in self.pairs[:self.used]:
+            ms = self._c.c_float()
+            st = self._hip.hipEventElapsedTime(self._c.byref(ms), a, b)
+            if st != 0:
+                raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+            out.append(ms.value * 1e-3)
+        return out
+
+    def close(self):
+        for a, b in self.pairs:
+            self._hip.hipEventDestroy(a)
+            self._hip.hipEventDestroy(b)
+        self.pairs, self.used = [], 0
 
 
 def cpu_baseline(w, cases, budget_s):
@@ -209,15 +276,14 @@ def bench_blocks(args):
     for _ in range(3):
         pkv.kv_copy_blocks(kc, vc, pairs)
     torch.cuda.synchronize()
-    ev = []
+    ev = LaunchEvents(args.steps)
     for _ in range(args.steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
+        i = ev.begin()
         pkv.kv_copy_blocks(kc, vc, pairs)
-        e1.record()
-        ev.append((e0, e1))
+        ev.end(i)
     torch.cuda.synchronize()
-    t = float(np.mean(kernel_launch_times(ev)))
+    t = float(np.mean(ev.seconds()))
+    ev.close()
     moved = 2 * 2 * n_pairs * block_bytes      # K and V, read + write
     gbps = moved / t / 1e9
 
@@ -235,19 +301,19 @@ def bench_blocks(args):
     swap_bytes = 2 * n_swap * block_bytes
 
     def timed_swap(pairs, to_host, reps):
-        ts = []
+        ts = LaunchEvents(reps)
         for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             with torch.cuda.stream(side):
-                e0.record()
+                i = ts.begin()
                 if to_host:
                     pkv.kv_swap_blocks(kc, vc, hk, hv, pairs)
                 else:
                     pkv.kv_swap_blocks(hk, hv, kc, vc, pairs)
-                e1.record()
-            ts.append((e0, e1))
-        side.synchronize()
-        return float(np.mean(kernel_launch_times(ts)))
+                ts.end(i)
+        torch.cuda.synchronize()
+        t = float(np.mean(ts.seconds()))
+        ts.close()
+        return t
 
     timed_swap(out_pairs, True, 1)
     t_out = timed_swap(out_pairs, True, 5)
@@ -334,26 +400,26 @@ def bench_multi(args, name):
         pkv.kv_cache_append(new_k, new_v, slots, case.k_cache, case.v_cache, case.k_scale,
                             case.v_scale, kv_dtype=case.kv_dtype)
         if events is not None:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            i = events.begin()
         pkv.paged_attention_multi_query(out, q, starts, case.k_cache, case.v_cache,
                                         case.block_tables, case.context_lens, w.scale, mcl,
                                         k_scale=case.k_scale, v_scale=case.v_scale,
                                         kv_dtype=case.kv_dtype, workspace=ws)
         if events is not None:
-            e1.record()
-            events.append((e0, e1))
+            events.end(i)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = []
+    events = LaunchEvents(args.steps)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    t_attn = float(np.mean(kernel_launch_times(events)))
+    t_attn = float(np.mean(events.seconds()))
+    events.close()
     kv_bytes = w.kv_bytes_per_layer()
     visible = 0                                 # (row, visible token) pairs per KV head group
     for b in range(w.batch):
@@ -454,21 +520,19 @@ def main():
                 pkv.kv_cache_append(c.new_k, c.new_v, c.slots, c.k_cache, c.v_cache,
                                     c.k_scale, c.v_scale, kv_dtype=kv_dtype)
             if events is not None:
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
+                i = events.begin()
             pkv.paged_attention_decode(c.out, c.q, c.k_cache, c.v_cache, c.block_tables,
                                        c.context_lens, w.scale, mcl, k_scale=c.k_scale,
                                        v_scale=c.v_scale, kv_dtype=kv_dtype, workspace=ws)
             if events is not None:
-                e1.record()
-                events.append((e0, e1))
+                events.end(i)
 
     log(f"[bench] warmup {args.warmup} steps (workspace {ws_bytes} B)")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = []
+    events = LaunchEvents(args.steps * len(cases))
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
@@ -476,7 +540,8 @@ def main():
         step(events)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    launch_s = kernel_launch_times(events)
+    launch_s = events.seconds()
+    events.close()
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = w.batch * args.steps / elapsed
 
@@ -492,19 +557,18 @@ def main():
     cold = None
     if args.cold_reps > 0:
         flush = torch.empty(2**30, dtype=torch.uint8, device=dev)
-        cold_ev = []
+        cold_ev = LaunchEvents(args.cold_reps)
         for i in range(args.cold_reps):
             flush.fill_(i & 0xFF)
             c = cases[i % len(cases)]
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
+            j = cold_ev.begin()
             pkv.paged_attention_decode(c.out, c.q, c.k_cache, c.v_cache, c.block_tables,
                                        c.context_lens, w.scale, mcl, k_scale=c.k_scale,
                                        v_scale=c.v_scale, kv_dtype=kv_dtype, workspace=ws)
-            e1.record()
-            cold_ev.append((e0, e1))
+            cold_ev.end(j)
         torch.cuda.synchronize()
-        cs = kernel_launch_times(cold_ev)
+        cs = cold_ev.seconds()
+        cold_ev.close()
         cold = {"avg_us": float(np.mean(cs)) * 1e6, "median_us": float(np.median(cs)) * 1e6,
                 "kv_gbps": kv_bytes / float(np.median(cs)) / 1e9, "reps": args.cold_reps}
         del flush
