@@ -409,9 +409,10 @@ void decode_partition_kernel(DecodeArgs a) {
   auto issue = [&](int tile, u32x4* kr, u32x4* vr, float& ks, float& vs, int& phys) {
     phys = tile_phys(tile);
     const int64_t row0 = tile_row0(tile, phys);
-    const uint64_t tile_bytes = (uint64_t)row0 * R;   // uniform: keep it scalar
-    const uint64_t tb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(tile_bytes >> 32)) << 32) |
-                        (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)tile_bytes);
+    // Uniform: keep it scalar.  (uni64 moves the two halves as unsigned words;
+    // readfirstlane returns a signed int, and widening the low half directly
+    // would copy its bit 31 into the high word, past 2^31 bytes into a pool.)
+    const uint64_t tb = (uint64_t)uni64((int64_t)row0 * R);
     const uint8_t* ktile = kbase + tb;
     const uint8_t* vtile = vbase + tb;
 #pragma unroll
@@ -419,8 +420,7 @@ void decode_partition_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + loff + 1024 * j);
     if constexpr (row_scaled(KV)) {
-      const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)row0 >> 32))
-                           << 32) | (uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)row0);
+      const uint64_t sb = (uint64_t)uni64(row0);
       ks = (a.k_scale + sb)[scale_tok];
       vs = (a.v_scale + sb)[scale_tok];
     }

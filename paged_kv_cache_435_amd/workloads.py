@@ -23,6 +23,9 @@ The five workloads (shapes of the Llama-2 family the pages discuss):
   llama13b_int4 the llama13b_int8 case with an INT4 cache (per-row scale,
                 packed nibbles)
   llama70b_int4 the llama70b_gqa8 case with an INT4 cache
+  llama70b_gqa8_32k  the llama70b_gqa8 layer with every context at 32768 tokens:
+                4 GiB of K+V per decode step, pools of 2.7 GB per cache (past
+                2**31 bytes)
 
 Pools hold 1.25x the blocks the sequences need (16 for the tiny case).  Blocks
 are dealt from ``default_rng(1).permutation(pool)`` to sequence 0's logical
@@ -140,6 +143,13 @@ def make(name, block_size=None, layers=None):
         return Workload(name, torch.float16, fmt, 32, 64, 8, 128, bs, 1, ctx, nb,
                         deal_blocks(ctx, bs, nb), appends=True,
                         seeds=dict(context=0, permutation=1, q=2, k=3, v=4, new=6))
+    if name == "llama70b_gqa8_32k":
+        ctx = np.full(32, 32768, dtype=np.int32)
+        bs = 16
+        nb = pool_for(ctx, bs)
+        return Workload(name, torch.float16, "f16", 32, 64, 8, 128, bs, 1, ctx, nb,
+                        deal_blocks(ctx, bs, nb), appends=True,
+                        seeds=dict(context=None, permutation=1, q=2, k=3, v=4, new=6))
     if name in ("llama13b_int8", "llama13b_int4"):
         ctx = np.full(32, 2049, dtype=np.int32)
         bs = 16
@@ -160,7 +170,7 @@ def make(name, block_size=None, layers=None):
 
 
 NAMES = ("tiny_fp32", "llama7b_bf16", "llama70b_gqa8", "llama13b_int8", "llama70b_fp8",
-         "llama13b_int4", "llama70b_int4")
+         "llama13b_int4", "llama70b_int4", "llama70b_gqa8_32k")
 
 
 # Several new query tokens per sequence (paged_attention_multi_query): each

@@ -9,7 +9,8 @@ import oracle
 import paged_kv_cache_435_amd as pkv
 from paged_kv_cache_435_amd import workloads as W
 from paged_kv_cache_435_amd.device_cache import DeviceCase
-from tests.gpu_util import OracleSide, append_and_decode, compare, run_and_check, say
+from tests.gpu_util import (OracleSide, append_and_decode, compare, per_head_rel_l2,
+                            run_and_check, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +207,27 @@ def test_int4_f32_queries_are_rejected():
                                    case.block_tables, case.context_lens, w.scale,
                                    w.max_context_len, k_scale=case.k_scale, v_scale=case.v_scale,
                                    kv_dtype="i4")
+
+
+@pytest.mark.parametrize("lo_frac", [0.0, 0.77])
+def test_pool_past_2_31_bytes(lo_frac):
+    """A 2.8 GB pool per cache (85,197 fp16 blocks of 8 heads): tables dealt from
+    the whole pool, and from the blocks past the 2**31-byte mark only, whose
+    tile offsets have bit 31 set.  Every head's output row must match the
+    oracle's (relative L2), not just pass the elementwise bound."""
+    nb, nseq, ctx = 85197, 4, 4096
+    lo = int(nb * lo_frac)
+    assert lo_frac == 0.0 or lo * 8 * 16 * 128 * 2 >= 2**31
+    need = nseq * ctx // 16
+    tables = (lo + np.random.default_rng(1).permutation(nb - lo)[:need]).reshape(nseq, -1)
+    w = W.Workload("pool_past_2_31", torch.float16, "f16", nseq, 64, 8, 128, 16, 1,
+                   np.full(nseq, ctx, dtype=np.int32), nb, tables.astype(np.int32),
+                   appends=False, seeds=dict(permutation=1, q=2, k=3, v=4, new=6))
+    assert int(w.block_tables.max()) < nb
+    err, case, got = run_and_check(w)
+    ref = OracleSide(w, case).attention()
+    e = per_head_rel_l2(got, ref)
+    say(f"  per-head relative L2 error: max {e.max():.3e}")
+    assert e.max() < 1e-2
+    del case
+    torch.cuda.empty_cache()

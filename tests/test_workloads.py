@@ -37,6 +37,11 @@ def test_published_shapes():
     # packed nibbles plus one float32 scale per row
     assert i4.kv_bytes_per_layer() == 2 * 560359 * 8 * (128 // 2 + 4)
     assert W.make("llama13b_int4").kv_format == "i4"
+    # every context at 32K: 2048 blocks per sequence, a pool past 2**31 bytes per cache
+    f = W.make("llama70b_gqa8_32k")
+    assert np.all(f.context_lens == 32768) and f.num_blocks == 81920
+    assert f.num_blocks * f.num_kv_heads * f.block_size * f.head_dim * 2 > 2**31
+    assert f.kv_bytes_per_layer() == 2 * 32 * 32768 * 8 * 128 * 2 == 4 * 2**30
 
 
 @pytest.mark.parametrize("name", W.NAMES)
