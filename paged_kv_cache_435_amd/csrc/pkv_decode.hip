@@ -100,6 +100,12 @@
 #ifndef PKV_SLOTS_PER_CU_I4
 #define PKV_SLOTS_PER_CU_I4 16
 #endif
+#ifndef PKV_ITEM_TILES_I8
+#define PKV_ITEM_TILES_I8 512
+#endif
+#ifndef PKV_ITEM_TILES_I4
+#define PKV_ITEM_TILES_I4 256
+#endif
 
 namespace pkv {
 
@@ -145,6 +151,12 @@ struct Tuning {
   static constexpr int slots_per_cu =
       KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8
                    : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4 : PKV_SLOTS_PER_CU_DEFAULT);
+  // Most tiles per item (block-table registers per lane at 16-token blocks:
+  // one per 64 tiles).  Longer items keep long contexts to one round of items;
+  // INT4's loop, bound by vector work, measured slower with 8 registers.
+  static constexpr int item_tiles =
+      KV == PKV_I4 ? PKV_ITEM_TILES_I4 : (KV == PKV_I8 ? PKV_ITEM_TILES_I8 : kItemTilesMax);
+  static_assert(item_tiles >= kItemTilesMin && item_tiles <= kItemTilesMax, "item limit");
 };
 
 // MULTI: several query tokens per sequence (causal).  The planner then works
@@ -263,7 +275,8 @@ void decode_partition_kernel(DecodeArgs a) {
   const int nfull = full_end > t_begin ? (full_end - t_begin) >> 4 : 0;
 
   // Block-table entries of the item, one per lane per register.
-  constexpr int NREG = (kItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
+  constexpr int NREG =
+      (Tuning<KV>::item_tiles * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
   const int first_blk = t_begin / BS;
   const int nblk = (t_end - 1) / BS - first_blk + 1;
   int blk[NREG];
@@ -1018,8 +1031,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // The prompt-chunk kernel is bound by its products, not by HBM: once the
   // units fill a round of slots, items take whole contexts up to the item
   // limit (fewer partial rows to write and merge); otherwise make_plan's rule.
-  const int tpi = a.prefill && live * units >= a.slots ? kItemTilesMax
-                                                        : plan_tpi(tiles * units, live * units, a.slots);
+  const int cap = a.prefill ? kPrefillItemTilesMax : a.item_cap;
+  const int tpi = a.prefill && live * units >= a.slots
+                      ? cap
+                      : plan_tpi(tiles * units, live * units, a.slots, cap);
   const int64_t total_tiles = tiles;       // of one unit per virtual sequence
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
@@ -1100,6 +1115,7 @@ struct MultiLaunch {
 template <int KV, int QT, int D, int BS, bool MULTI>
 static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hipStream_t st) {
   auto* kern = decode_partition_kernel<KV, QT, D, BS, MULTI>;
+  a.item_cap = Tuning<KV>::item_tiles;   // the plan's item limit is this instance's
   // Resident waves per CU of this instance: a property of the compiled code,
   // queried once (every device the library runs on is gfx950).
   static std::atomic<int> occupancy{0};
@@ -1192,6 +1208,7 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
 template <int QT, int D>
 static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vctx, int kv_dtype,
                                       int block_size, int num_cus, hipStream_t st) {
+  a.item_cap = kPrefillItemTilesMax;
   hipError_t e = launch_prefill(a, QT, kv_dtype, D, block_size, num_cus, true, st);   // a.slots
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(multi_prep_kernel, dim3(1), dim3(1024), 0, st, a, batch_real, vctx);

@@ -14,7 +14,12 @@ namespace pkv {
 // round of near-equal items, no tail of stragglers.
 constexpr int kTileTokens = 16;
 constexpr int kItemTilesMin = 16;    // 256 tokens: keeps merge work small for short batches
-constexpr int kItemTilesMax = 256;   // 4096 tokens: 4 block-table registers per lane at bs 16
+// Most tiles per item: a lane holds one block-table entry per 64 tiles (at 16-token
+// blocks).  The decode kernels take up to kItemTilesMax (8 registers; INT4,
+// whose loop is bound by vector work, keeps 4); the prompt-chunk kernel, short of
+// registers, kPrefillItemTilesMax.
+constexpr int kItemTilesMax = 512;          // 8192 tokens
+constexpr int kPrefillItemTilesMax = 256;   // 4096 tokens
 constexpr int kWavesPerCuCap = 16;   // at most 4 waves per SIMD are planned for
 constexpr int kMaxCus = 256;         // MI355X; plans never use more slots than this many CUs give
 constexpr int kMaxSlots = kMaxCus * kWavesPerCuCap;
@@ -67,6 +72,7 @@ struct DecodeArgs {
   int32_t head_tiles;          // ceil(G / 16): query heads of a group are taken 16 at a time
                                // (multi: row tiles per virtual sequence)
   int32_t plan_heads;          // KV heads per planned sequence: num_kv_heads (multi: 1)
+  int32_t item_cap;            // most tiles per item the launched kernel holds table entries for
   int32_t num_blocks;
   int32_t max_blocks_per_seq;
   int32_t ctx_cap;             // context lengths are clamped to [0, ctx_cap]
@@ -93,14 +99,15 @@ struct DecodeArgs {
 
 // Host-side bound on the items a plan can make (grid size and workspace rows).
 // With N tiles in U units and S slots, the plan uses S' = max(S - U, S/2) and
-// t >= N / (k S') tiles per item over k rounds, so it makes at most
-// sum ceil(n_u / t) <= k S' + U items, with k S' < N / kItemTilesMax + S'.
-// Hence at most N / kItemTilesMax + S + U.
+// t >= N / (k S') tiles per item over k rounds with an item limit L, so it
+// makes at most sum ceil(n_u / t) <= k S' + U items, with k S' < N / L + S'.
+// Hence at most N / L + S + U; the smaller limit (the prompt-chunk kernel's)
+// bounds the plans of every kernel.
 inline int64_t max_items_bound(int64_t batch, int64_t units_per_seq, int64_t max_context_len,
                                int64_t slots) {
   const int64_t units = batch * units_per_seq;
   const int64_t tiles = units * ((max_context_len + kTileTokens - 1) / kTileTokens);
-  return (tiles + kItemTilesMax - 1) / kItemTilesMax + slots + units;
+  return (tiles + kPrefillItemTilesMax - 1) / kPrefillItemTilesMax + slots + units;
 }
 
 hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,

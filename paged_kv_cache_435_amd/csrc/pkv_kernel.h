@@ -257,18 +257,18 @@ __device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqTil
 
 // Tiles per item: about (total tiles) / (slots - units), so that one round of
 // items fits the slots even after each unit's count is rounded up; several
-// rounds when an item would pass kItemTilesMax.  (Filling the slots exactly,
-// with more and smaller items, measured slower.)  tiles and live count
-// (unit, tile) pairs and units with any tile.
-__device__ __forceinline__ int plan_tpi(int64_t tiles, int64_t live, int64_t slots) {
+// rounds when an item would pass the kernel's item limit `cap`.  (Filling the
+// slots exactly, with more and smaller items, measured slower.)  tiles and
+// live count (unit, tile) pairs and units with any tile.
+__device__ __forceinline__ int plan_tpi(int64_t tiles, int64_t live, int64_t slots, int cap) {
   slots = slots > 0 ? slots : 1;
   int64_t se = slots - live;
   if (se < slots / 2) se = slots / 2;
   if (se < 1) se = 1;
-  int64_t k = (tiles + se * kItemTilesMax - 1) / (se * kItemTilesMax);
+  int64_t k = (tiles + se * cap - 1) / (se * cap);
   if (k < 1) k = 1;
   int64_t t = (tiles + k * se - 1) / (k * se);
-  t = t < kItemTilesMin ? kItemTilesMin : (t > kItemTilesMax ? kItemTilesMax : t);
+  t = t < kItemTilesMin ? kItemTilesMin : (t > cap ? cap : t);
   return (int)t;
 }
 
@@ -285,7 +285,7 @@ __device__ inline Plan make_plan(const DecodeArgs& a, int lane) {
   tiles = uni64(wave_sum_i64(tiles) * ups);
   live = uni64(wave_sum_i64(live) * ups);
   Plan p;
-  p.tpi = plan_tpi(tiles, live, a.slots);
+  p.tpi = plan_tpi(tiles, live, a.slots, a.item_cap);
   p.items = count_items(a, st, p.tpi, lane);
   return p;
 }

@@ -156,7 +156,7 @@ __device__ __forceinline__ void prefill_group(
   const int nfull = full_end > t_begin ? (full_end - t_begin) >> 4 : 0;   // whole tiles
 
   // Block-table entries of the item, one per lane per register.
-  constexpr int NREG = (kItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
+  constexpr int NREG = (kPrefillItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
   const int first_blk = t_begin / BS;
   const int nblk = ntiles > 0 ? (t_end - 1) / BS - first_blk + 1 : 0;
   int blk[NREG];
