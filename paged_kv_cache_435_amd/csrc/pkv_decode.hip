@@ -761,6 +761,7 @@ void decode_partition_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // One output row from its m partial rows row0 + c * row_step (a row that saw
 // no token in any item, M = -inf, gets zeros).
+constexpr int kMergeFast = 32;   // partials merged from registers after one round of loads
 template <int QT, int D>
 __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int64_t row_step,
                                           int m, int64_t hq, int lane) {
@@ -768,6 +769,48 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int
   constexpr int PPI = kWave / LPP;    // partials per load instruction
   const int grp = lane / LPP;         // which partial of an instruction
   const int dq = lane % LPP;          // which 4 output elements
+  if (m <= kMergeFast) {
+    // Up to kMergeFast partials: every (max, sum) and every output row is
+    // loaded in one round, before any of them is used (the general path
+    // below needs the maxima before it reads the rows).  Same sums in the
+    // same order, so the same result.
+    constexpr int NV = kMergeFast / PPI;
+    float mc = -__builtin_inff(), lc = 0.f;
+    if (lane < m) {
+      const int64_t row = row0 + lane * row_step;
+      mc = a.ws_ml[2 * row];
+      lc = a.ws_ml[2 * row + 1];
+    }
+    f32x4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = i * PPI + grp;
+      v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < m) v[i] = *reinterpret_cast<const f32x4*>(a.ws_acc + (row0 + c * row_step) * D + 4 * dq);
+    }
+    const float M = wave_max(mc);
+    if (M == -__builtin_inff()) {
+      if (grp == 0) store_out4<QT>(a.out, hq * D + 4 * dq, 0.f, 0.f, 0.f, 0.f);
+      return;
+    }
+    const float L = wave_sum(lane < m ? __builtin_amdgcn_exp2f(mc - M) * lc : 0.f);
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = i * PPI + grp;
+      const float mi = __shfl(mc, c < m ? c : 0, kWave);
+      if (c < m) o += __builtin_amdgcn_exp2f(mi - M) * v[i];
+    }
+#pragma unroll
+    for (int off = LPP; off < kWave; off <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] += __shfl_xor(o[i], off, kWave);
+    }
+    if (grp != 0) return;
+    const float inv = 1.0f / L;
+    store_out4<QT>(a.out, hq * D + 4 * dq, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+    return;
+  }
   float M = -__builtin_inff();
   for (int c = lane; c < m; c += kWave) M = fmaxf(M, a.ws_ml[2 * (row0 + c * row_step)]);
   M = wave_max(M);
@@ -811,13 +854,19 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int64_t hq = (int64_t)b * a.num_q_heads + h;
-  if (seq_ctx(a, b) == 0) {
+  // The context and the sequence's record are loaded together (the record is
+  // only used when the context is not empty).
+  const int ctx = seq_ctx(a, b);
+  int64_t first = 0;
+  int m = 0;
+  if (a.ws_seq) {                     // no workspace: every unit was one item
+    first = a.ws_seq[2 * b];
+    m = (int)a.ws_seq[2 * b + 1];
+  }
+  if (ctx == 0) {
     if (lane < D / 4) store_out4<QT>(a.out, hq * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
     return;
   }
-  if (!a.ws_seq) return;              // no workspace: every unit was one item
-  const int64_t first = a.ws_seq[2 * b];
-  const int m = (int)a.ws_seq[2 * b + 1];
   if (m <= 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int g = h / G;
