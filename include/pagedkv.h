@@ -156,7 +156,7 @@ pkv_status kv_cache_append(const void* k, const void* v, int32_t src_dtype, int3
  * paged_attention_workspace_size — bytes of device scratch paged_attention_decode
  * needs for these sizes (partial softmax state of contexts split over several
  * waves; sized for up to 256 compute units x 16 resident waves).  Host only, no
- * device needed.  0 when no context can be split (max_context_len <= 256) or
+ * device needed.  0 when no context can be split (max_context_len <= 128) or
  * the sizes are invalid.
  */
 size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -1185,7 +1185,13 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.plan_heads * a.head_tiles;
   // The workspace was sized for kMaxSlots; fewer slots never need more items.
-  const int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
+  // Every item has at least kItemTilesMin tiles, so a unit makes at most
+  // ceil(tiles / kItemTilesMin) items: small batches launch few workgroups.
+  int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
+  const int64_t unit_tiles = ((int64_t)a.ctx_cap + kTileTokens - 1) / kTileTokens;
+  const int64_t short_bound =
+      (int64_t)a.batch * units * ((unit_tiles + kItemTilesMin - 1) / kItemTilesMin);
+  if (short_bound < need) need = short_bound > 0 ? short_bound : 1;
   const int wpg = MULTI ? a.head_tiles : kDecodeWaves;
   const int64_t grid = ((need + wpg - 1) / wpg + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;

@@ -13,7 +13,14 @@ namespace pkv {
 // that the item count matches the number of waves the GPU runs at once: one
 // round of near-equal items, no tail of stragglers.
 constexpr int kTileTokens = 16;
-constexpr int kItemTilesMin = 16;    // 256 tokens: keeps merge work small for short batches
+// Fewest tiles per item (128 tokens).  Small batches are latency-bound: a wave
+// walks its tiles one load after another, so shorter items finish sooner
+// (one 512-token sequence: 21.2 us at 16 tiles, 16.9 at 8); large batches plan
+// far longer items and do not see it.  Tuning knob.
+#ifndef PKV_ITEM_TILES_MIN
+#define PKV_ITEM_TILES_MIN 8
+#endif
+constexpr int kItemTilesMin = PKV_ITEM_TILES_MIN;
 // Most tiles per item: a lane holds one block-table entry per 64 tiles (at 16-token
 // blocks).  The decode kernels take up to kItemTilesMax (8 registers; INT4,
 // whose loop is bound by vector work, keeps 4); the prompt-chunk kernel, short of

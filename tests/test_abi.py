@@ -42,8 +42,10 @@ def test_kv_cache_bytes_closed_form(lib):
 
 
 def test_workspace_sizing(lib):
-    # Contexts of at most 256 tokens are never split: no workspace.
-    assert pkv.paged_attention_workspace_size(4, 8, 2, 128, 256) == 0
+    # Contexts of at most 128 tokens (the shortest item) are never split: no
+    # workspace; longer ones may be.
+    assert pkv.paged_attention_workspace_size(4, 8, 2, 128, 128) == 0
+    assert pkv.paged_attention_workspace_size(4, 8, 2, 128, 129) > 0
     assert pkv.paged_attention_workspace_size(4, 6, 4, 128, 4096) == 0      # 6 % 4 != 0
     # Longer ones: rows of 16 heads x (2 + head_dim) floats, one per planned item;
     # at least one item per (sequence, KV head) unit plus a full round of slots.
@@ -117,10 +119,10 @@ def test_multi_query_sizing_and_rejections(lib):
     # sequence 107, too few for the prompt-chunk kernel), so at most 8 KV heads x
     # (ceil(320 / 128) + 3) = 48 virtual sequences.  The plan: 128 B of scalars, six
     # int32 per virtual sequence, and an item map with room for the most items any
-    # plan makes: 48 x 4 units x 16 tiles / 256 + 4096 slots + 192 units = 4300
-    # entries.  Contexts <= 256 are never split: nothing else.
+    # plan makes: 48 x 4 units x 8 tiles / 256 + 4096 slots + 192 units = 4294
+    # entries.  Contexts <= 128 are never split: nothing else.
     plan = lambda entries: -(-(128 + 6 * 4 * 48 + 4 * entries) // 256) * 256
-    assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 256) == plan(4300)
+    assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 128) == plan(4294)
     # 32K contexts: 192 units x 2048 tiles / 256 + 4096 + 192 = 5824 items, each
     # with 32 partial rows of (2 + d) floats, and 16 B per virtual sequence.
     big = pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 32768)
