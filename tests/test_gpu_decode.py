@@ -209,21 +209,31 @@ def test_int4_f32_queries_are_rejected():
                                    kv_dtype="i4")
 
 
-@pytest.mark.parametrize("lo_frac", [0.0, 0.77])
-def test_pool_past_2_31_bytes(lo_frac):
-    """A 2.8 GB pool per cache (85,197 fp16 blocks of 8 heads): tables dealt from
-    the whole pool, and from the blocks past the 2**31-byte mark only, whose
-    tile offsets have bit 31 set.  Every head's output row must match the
-    oracle's (relative L2), not just pass the elementwise bound."""
-    nb, nseq, ctx = 85197, 4, 4096
-    lo = int(nb * lo_frac)
-    assert lo_frac == 0.0 or lo * 8 * 16 * 128 * 2 >= 2**31
-    need = nseq * ctx // 16
+def _high_block_workload(name, q_dtype, fmt, bs, nb, high_only, nseq=4, ctx=4096):
+    """nseq sequences of ctx tokens, 8 KV heads (64 query heads), d 128, over a
+    pool of nb blocks whose bytes pass 2**31; tables dealt from the whole pool,
+    or only from the blocks whose first byte is past the 2**31 mark."""
+    row = {"f16": 256, "bf16": 256, "i8": 128, "fp8": 128, "i4": 64}[fmt]
+    block_bytes = 8 * bs * row
+    assert nb * block_bytes > 2**31
+    lo = -(-2**31 // block_bytes) if high_only else 0
+    need = nseq * ctx // bs
+    assert nb - lo >= need
     tables = (lo + np.random.default_rng(1).permutation(nb - lo)[:need]).reshape(nseq, -1)
-    w = W.Workload("pool_past_2_31", torch.float16, "f16", nseq, 64, 8, 128, 16, 1,
-                   np.full(nseq, ctx, dtype=np.int32), nb, tables.astype(np.int32),
-                   appends=False, seeds=dict(permutation=1, q=2, k=3, v=4, new=6))
-    assert int(w.block_tables.max()) < nb
+    return W.Workload(name, q_dtype, fmt, nseq, 64, 8, 128, bs, 1,
+                      np.full(nseq, ctx, dtype=np.int32), nb, tables.astype(np.int32),
+                      appends=False, seeds=dict(permutation=1, q=2, k=3, v=4, new=6))
+
+
+@pytest.mark.parametrize("fmt,bs,nb,high_only", [
+    ("f16", 16, 85197, False), ("f16", 16, 85197, True),
+    ("i8", 16, 140000, True), ("fp8", 256, 8750, True), ("i4", 16, 270000, True)])
+def test_pool_past_2_31_bytes(fmt, bs, nb, high_only):
+    """Pools of 2.2-2.8 GB per cache, read from all of it or from its blocks past
+    the 2**31-byte mark only (tile offsets with bit 31 set).  Every head's
+    output row must match the oracle's (relative L2), not just pass the
+    elementwise bound."""
+    w = _high_block_workload(f"pool_past_2_31_{fmt}", torch.float16, fmt, bs, nb, high_only)
     err, case, got = run_and_check(w)
     ref = OracleSide(w, case).attention()
     e = per_head_rel_l2(got, ref)

@@ -27,7 +27,7 @@ def _queries(w, q_lens, seed=41):
     return torch.randn(T, w.num_q_heads, w.head_dim, generator=g).to(w.q_dtype)
 
 
-def run_multi(w, q_lens, seqs_check=None, what="", rows_of=None):
+def run_multi(w, q_lens, seqs_check=None, what="", rows_of=None, want_ref=False):
     q_lens = np.asarray(q_lens, dtype=np.int64)
     say(f"[multi] {what or w.name} fmt={w.kv_format} q={w.q_dtype} B={w.batch} "
         f"Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} bs={w.block_size} "
@@ -68,6 +68,8 @@ def run_multi(w, q_lens, seqs_check=None, what="", rows_of=None):
                                        side.v_cache, side.tables, side.context_lens, w.scale,
                                        w.block_size, w.kv_format, side.k_scale, side.v_scale)
     compare(got, ref, w.kv_format, what or w.name)
+    if want_ref:
+        return got, case, q, starts, ref
     return got, case, q, starts
 
 
@@ -210,3 +212,21 @@ def test_more_than_1024_sequences(hq, hkv, qlen):
     ctx = np.maximum(rng.integers(16, 100, B), lens)
     w = W.custom(torch.float16, "f16", ctx, hq, hkv, 128, 16, name=f"B{B}-{hq}x{hkv}")
     run_multi(w, lens, seqs_check=[0, 511, 1023, 1024, 1099])
+
+
+@pytest.mark.parametrize("q_len", [4, 512])
+def test_pool_past_2_31_bytes(q_len):
+    """A 2.8 GB fp16 pool per cache read only from its blocks past the 2**31-byte
+    mark: 4 draft tokens per sequence (the decode-shaped kernel) and 512-token
+    prompt chunks (the prompt-chunk kernel).  Every (row, head) output must
+    match the oracle's (relative L2)."""
+    from tests.gpu_util import per_head_rel_l2
+    from tests.test_gpu_decode import _high_block_workload
+    w = _high_block_workload("multi_pool_past_2_31", torch.float16, "f16", 16, 85197, True,
+                             nseq=4, ctx=2048)
+    got, case, _, _, ref = run_multi(w, [q_len] * 4, want_ref=True)
+    e = per_head_rel_l2(got, ref)
+    say(f"  per-row relative L2 error: max {e.max():.3e}")
+    assert e.max() < 1e-2
+    del case
+    torch.cuda.empty_cache()
