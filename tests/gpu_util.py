@@ -183,15 +183,31 @@ def per_head_rel_l2(got, ref):
     return num / np.maximum(den, 1e-30)
 
 
+# Every output row (one head of one query token, head_dim values) is also held
+# to a relative L2 error, with a small absolute floor for rows that are zero
+# (empty contexts).  Rounding alone gives about 3e-4 for 16-bit outputs and
+# less for f32; a dropped block or a misread tile moves a row far more.
+ROW_RTOL, ROW_ATOL = 1e-2, 1e-3
+
+
 def compare(got, ref, fmt, what=""):
     atol, rtol = TOL[fmt]
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     err = np.abs(got - ref)
     bad = err > atol + rtol * np.abs(ref)
+    rows_bad, row_err = 0, 0.0
+    if got.size and got.ndim >= 2:
+        num = np.linalg.norm(got - ref, axis=-1)
+        den = np.linalg.norm(ref, axis=-1)
+        rows_bad = int((num > ROW_RTOL * den + ROW_ATOL).sum())
+        row_err = float((num / np.maximum(den, 1e-30)).max())
     say(f"  {what}: max|err| = {err.max() if err.size else 0:.3e}, "
         f"max|ref| = {np.abs(ref).max() if ref.size else 0:.3e}, "
-        f"{err.size} elements, {int(bad.sum())} outside tolerance")
+        f"{err.size} elements, {int(bad.sum())} outside tolerance; "
+        f"max row relative L2 {row_err:.2e}, {rows_bad} rows outside")
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside (atol={atol}, rtol={rtol})"
+    assert rows_bad == 0, (f"{what}: {rows_bad} output rows outside relative L2 {ROW_RTOL} "
+                           f"(+{ROW_ATOL})")
     return float(err.max()) if err.size else 0.0
 
 
