@@ -616,7 +616,9 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": decode_traffic(w.name),
                      "kernel": "paged_attention_decode",
-                     "bytes_per_launch": kv_bytes, "avg_launch_us": avg_launch * 1e6},
+                     "bytes_per_launch": kv_bytes, "avg_launch_us": avg_launch * 1e6,
+                     "launch_us_p10_p50_p90": [float(np.percentile(launch_s, q)) * 1e6
+                                               for q in (10, 50, 90)]},
         "cold_cache": cold,
         "cpu_baseline": cpu,
     }
