@@ -73,3 +73,12 @@ def test_llama70b_gqa8_32k_sampled():
     assert e.max() < 1e-2, f"per-head relative L2 error {e.max():.3e}"
     del case
     torch.cuda.empty_cache()
+
+
+def test_two_round_plan_int4_32k_sampled():
+    # The 70B GQA-8 layer at every context 32K over an INT4 cache: INT4 items stop
+    # at 256 tiles, so 524,288 tiles over 2,048 slots need two rounds of items.
+    ctx = [32768] * 32
+    w = W.custom(torch.float16, "i4", ctx, 64, 8, 128, 16, name="int4-32k-two-rounds")
+    run_and_check(w, seqs=[0, 13, 31])
+    torch.cuda.empty_cache()
