@@ -159,6 +159,14 @@ struct Tuning {
   static_assert(item_tiles >= kItemTilesMin && item_tiles <= kItemTilesMax, "item limit");
 };
 
+// Waves per workgroup: decode takes kDecodeWaves consecutive items (the KV
+// heads of one (sequence, chunk)); a multi-token call takes the row tiles of
+// one virtual sequence, or kDecodeWaves items when a virtual sequence is one
+// wave (then the prep kernel may number a sequence's KV heads chunk by chunk).
+__host__ __device__ __forceinline__ int multi_wpg(const DecodeArgs& a, bool multi) {
+  return multi && a.head_tiles > 1 ? a.head_tiles : kDecodeWaves;
+}
+
 // MULTI: several query tokens per sequence (causal).  The planner then works
 // on virtual sequences, one per (sequence, KV head, group of head_tiles 32-row
 // tiles of (query token, head of the group) rows), whose context ends at the
@@ -167,7 +175,8 @@ struct Tuning {
 // (written by multi_prep_kernel).  A wave takes one 32-row tile; the
 // head_tiles waves of a group form one workgroup.
 template <int KV, int QT, int D, int BS, bool MULTI>
-__global__ __launch_bounds__(MULTI ? 64 * kMultiGroupMax : 64 * kDecodeWaves)
+__global__ __launch_bounds__(64 * (MULTI && kMultiGroupMax > kDecodeWaves ? kMultiGroupMax
+                                                                           : kDecodeWaves))
 __attribute__((amdgpu_waves_per_eu(MULTI ? PKV_MULTI_WAVES_PER_EU : Tuning<KV>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
@@ -196,7 +205,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // kDecodeWaves waves, the KV heads of one (sequence, chunk), which read
   // adjacent tiles of the same blocks.  The waves share nothing (no LDS, no
   // barrier), so any of them may stop early. ----
-  const int wpg = MULTI ? a.head_tiles : kDecodeWaves;   // waves per workgroup
+  const int wpg = multi_wpg(a, MULTI);               // waves per workgroup
   Plan plan;
   if constexpr (MULTI) {
     plan.items = planned_items(a);                    // made by multi_prep_kernel
@@ -219,7 +228,10 @@ void decode_partition_kernel(DecodeArgs a) {
   }
   b = uni(b);
   const int local = uni((int)(item - sq.first));   // < m * units per sequence
-  const int upc = a.plan_heads * a.head_tiles;       // items per chunk
+  // items per chunk: a multi-token call whose virtual sequences are single
+  // row groups numbers the KV heads of a sequence chunk by chunk (plan_info[11])
+  const int upc = MULTI ? (a.plan_info[11] ? a.num_kv_heads * a.head_tiles : a.head_tiles)
+                        : a.plan_heads * a.head_tiles;
   const int g = MULTI ? uni(a.vseq_g[b]) : uni((local % upc) / a.head_tiles);
   const int chunk = uni(local / upc);
   const int ht = uni(local % a.head_tiles);
@@ -925,11 +937,12 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int m = (int)a.ws_seq[2 * v + 1];
   if (m <= 1) return;
   // (one KV head per virtual sequence) chunk c, row tile ht: item
-  // first + c*head_tiles + ht, rows item*TR ..
-  if (first + (int64_t)m * a.head_tiles - 1 >= a.max_items) return;
+  // first + c*S + ht with S items per chunk (head_tiles, or the KV heads of the
+  // sequence when they are numbered chunk by chunk), rows item*TR ..
+  const int64_t S = a.plan_info[11] ? (int64_t)a.num_kv_heads * a.head_tiles : a.head_tiles;
+  if (first + (int64_t)(m - 1) * S + a.head_tiles - 1 >= a.max_items) return;
   for (int r = r_first; r < rows; r += r_step)
-    merge_row<QT, D>(a, (first + r / TR) * TR + r % TR, (int64_t)a.head_tiles * TR, m, out_row(r),
-                     lane);
+    merge_row<QT, D>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
 }
 
 // Inclusive prefix sums of two ints per thread over a 1024-thread block:
@@ -982,10 +995,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   constexpr int kCtxCache = 4096;               // contexts of the first virtual sequences
   __shared__ int vctx_s[kCtxCache];
   __shared__ int carry;
+  __shared__ int several_groups;               // some sequence has more than one row group
   __shared__ int wtot[1024 / kWave][2];
   const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
-  if (t == 0) carry = 0;
+  if (t == 0) carry = several_groups = 0;
   __syncthreads();
   for (int b0 = 0; b0 < batch_real; b0 += 1024) {
     const int b = b0 + t;
@@ -999,6 +1013,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     seq_len[t] = L;
     seq_cx[t] = cx;
     const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
+    if ((L * G + ROWS - 1) / ROWS > 1) atomicOr(&several_groups, 1);
     int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
     int unused = 0, total = 0, unused_tot = 0;
     block_scan2(n, unused, wtot, total, unused_tot);
@@ -1085,6 +1100,13 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
                       ? cap
                       : plan_tpi(tiles * units, live * units, a.slots, cap);
   const int64_t total_tiles = tiles;       // of one unit per virtual sequence
+  // When every virtual sequence is one wave and one row group, the KV heads of
+  // a sequence are consecutive virtual sequences with one context, hence one
+  // chunk count m: their items are numbered chunk by chunk (item = F + c*Hkv +
+  // g), so a workgroup's waves read the same blocks' adjacent (block, head)
+  // tiles, as in decode.  Otherwise each virtual sequence's items are
+  // consecutive.
+  const bool by_chunk = !a.prefill && a.head_tiles == 1 && several_groups == 0;
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
     int m = 0, n = 0;
@@ -1110,14 +1132,21 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
     }
     if (v < a.batch) {
-      const int64_t first = carry_items + inc_items - cnt;
+      int64_t first = carry_items + inc_items - cnt;
+      int64_t step = 1;
+      if (by_chunk) {
+        // (the scan gave F + g*m; the sequence's group starts at F)
+        const int g = a.vseq_g[v];
+        first -= (int64_t)g * (m - 1);
+        step = a.num_kv_heads;
+      }
       a.vseq_first[v] = (int32_t)first;
       a.vseq_m[v] = m;
       if (a.ws_seq) {
         a.ws_seq[2 * v] = first;
         a.ws_seq[2 * v + 1] = m;
       }
-      for (int i = 0; i < cnt && first + i < a.map_cap; ++i) a.item_vseq[first + i] = v;
+      for (int i = 0; i < cnt && first + i * step < a.map_cap; ++i) a.item_vseq[first + i * step] = v;
     }
     __syncthreads();
     if (t == 0) {
@@ -1136,6 +1165,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       f += xcd_groups[x];
     }
     a.plan_info[10] = f;
+    a.plan_info[11] = by_chunk ? 1 : 0;
   }
 }
 
@@ -1180,7 +1210,8 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   const int target = slots_per_cu_override() > 0 ? slots_per_cu_override()
                                                  : Tuning<KV>::slots_per_cu;
   if (target < per_cu) per_cu = target;
-  if (MULTI && per_cu > a.head_tiles) per_cu = per_cu / a.head_tiles * a.head_tiles;   // whole workgroups
+  const int wpg = multi_wpg(a, MULTI);
+  if (MULTI && per_cu > wpg) per_cu = per_cu / wpg * wpg;   // whole workgroups
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.plan_heads * a.head_tiles;
@@ -1192,7 +1223,6 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   const int64_t short_bound =
       (int64_t)a.batch * units * ((unit_tiles + kItemTilesMin - 1) / kItemTilesMin);
   if (short_bound < need) need = short_bound > 0 ? short_bound : 1;
-  const int wpg = MULTI ? a.head_tiles : kDecodeWaves;
   const int64_t grid = ((need + wpg - 1) / wpg + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
   if constexpr (MULTI) {

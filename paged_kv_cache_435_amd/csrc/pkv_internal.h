@@ -96,7 +96,7 @@ struct DecodeArgs {
   int32_t q_rows;              // query rows (tokens) in q and out
   int32_t wave_rows;           // (query token, head) rows per wave: 16 x row tiles
   // The plan of a multi-query call, made by its prep kernel.
-  int64_t* plan_info;          // [items, tiles per item, first group of XCD 0..7, groups]
+  int64_t* plan_info;          // [items, tiles per item, first group of XCD 0..7, groups, by-chunk numbering]
   int32_t* vseq_first;         // first item of each virtual sequence
   int32_t* vseq_m;             // items (chunks of its context) per row tile
   int32_t* item_vseq;          // virtual sequence of each item
