@@ -773,20 +773,22 @@ void decode_partition_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // One output row from its m partial rows row0 + c * row_step (a row that saw
 // no token in any item, M = -inf, gets zeros).
-constexpr int kMergeFast = 32;   // partials merged from registers after one round of loads
-template <int QT, int D>
+// Fast path of merge_row: up to NV * (64 / (D / 4)) partials are held in NV
+// registers of 4 floats after one round of loads.  The decode merge (one wave
+// per (head, sequence)) takes 16; the multi-token merge (a wave per row, many
+// more waves) takes 4, which keeps it at 8 resident waves per SIMD.
+template <int QT, int D, int NV>
 __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int64_t row_step,
                                           int m, int64_t hq, int lane) {
   constexpr int LPP = D / 4;          // lanes per partial row
   constexpr int PPI = kWave / LPP;    // partials per load instruction
   const int grp = lane / LPP;         // which partial of an instruction
   const int dq = lane % LPP;          // which 4 output elements
-  if (m <= kMergeFast) {
-    // Up to kMergeFast partials: every (max, sum) and every output row is
+  if (m <= NV * PPI) {
+    // Up to NV * PPI partials: every (max, sum) and every output row is
     // loaded in one round, before any of them is used (the general path
     // below needs the maxima before it reads the rows).  Same sums in the
     // same order, so the same result.
-    constexpr int NV = kMergeFast / PPI;
     float mc = -__builtin_inff(), lc = 0.f;
     if (lane < m) {
       const int64_t row = row0 + lane * row_step;
@@ -838,7 +840,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int
   L = wave_sum(L);
 
   f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
+#pragma unroll 1
   for (int c0 = 0; c0 < m; c0 += PPI) {
     const int c = c0 + grp;
     if (c < m) {
@@ -887,8 +889,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   // Partial row of chunk c: item (first + (c*plan_heads + g)*head_tiles + ht), head r.
   const int64_t upc = (int64_t)a.plan_heads * a.head_tiles;
   if (first + ((int64_t)(m - 1) * a.plan_heads + g) * a.head_tiles + ht >= a.max_items) return;
-  merge_row<QT, D>(a, (first + (int64_t)g * a.head_tiles + ht) * 16 + r, upc * 16, m, hq,
-                   lane);
+  merge_row<QT, D, 16>(a, (first + (int64_t)g * a.head_tiles + ht) * 16 + r, upc * 16, m, hq,
+                       lane);
 }
 
 // Several query tokens per sequence: one workgroup of 8 waves per virtual
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int64_t S = a.plan_info[11] ? (int64_t)a.num_kv_heads * a.head_tiles : a.head_tiles;
   if (first + (int64_t)(m - 1) * S + a.head_tiles - 1 >= a.max_items) return;
   for (int r = r_first; r < rows; r += r_step)
-    merge_row<QT, D>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
+    merge_row<QT, D, 4>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
 }
 
 // Inclusive prefix sums of two ints per thread over a 1024-thread block:
