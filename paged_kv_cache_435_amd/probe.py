@@ -22,6 +22,9 @@ def _lib():
         lib.pkv_probe_read.restype = ctypes.c_int32
         lib.pkv_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
                                        ctypes.c_void_p]
+        lib.pkv_probe_read_slabs.restype = ctypes.c_int32
+        lib.pkv_probe_read_slabs.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p,
+                                             ctypes.c_int32, ctypes.c_void_p]
         lib.pkv_probe_copy.restype = ctypes.c_int32
         lib.pkv_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                        ctypes.c_void_p]
@@ -33,9 +36,15 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
-def read_gbps(nbytes=4 << 30, reps=10, device="cuda"):
-    """Median GB/s of the plain read kernel over a fresh ``nbytes`` buffer."""
+def read_gbps(nbytes=4 << 30, reps=10, device="cuda", slabs=0):
+    """Median GB/s of a plain read of a fresh ``nbytes`` buffer: grid-stride
+    16-byte loads, or (``slabs`` > 0) contiguous 16 KB slabs per workgroup over
+    ``slabs`` workgroups of 4 waves."""
     lib = _lib()
+    if slabs:
+        fn = lambda x, n, s, st: lib.pkv_probe_read_slabs(x, n, s, slabs, st)
+    else:
+        fn = lib.pkv_probe_read
     x = torch.empty(nbytes, dtype=torch.uint8, device=device)
     x.fill_(1)
     sink = torch.empty(lib.pkv_probe_grid(), dtype=torch.int32, device=device)
@@ -43,8 +52,7 @@ def read_gbps(nbytes=4 << 30, reps=10, device="cuda"):
     for _ in range(reps + 2):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        if lib.pkv_probe_read(ctypes.c_void_p(x.data_ptr()), nbytes,
-                              ctypes.c_void_p(sink.data_ptr()), _stream()):
+        if fn(ctypes.c_void_p(x.data_ptr()), nbytes, ctypes.c_void_p(sink.data_ptr()), _stream()):
             raise RuntimeError("pkv_probe_read failed")
         e1.record()
         times.append((e0, e1))
