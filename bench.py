@@ -628,6 +628,9 @@ def main():
                                                for q in (10, 50, 90)]},
         "cold_cache": cold,
         "cpu_baseline": cpu,
+        "seeds": {k: v for k, v in w.seeds.items() if v is not None},
+        "versions": {"torch": torch.__version__, "hip": torch.version.hip,
+                     "device": torch.cuda.get_device_name(dev)},
     }
     print(json.dumps(record), flush=True)
 
