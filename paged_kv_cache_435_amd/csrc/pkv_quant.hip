@@ -210,40 +210,71 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k,
   if (row >= rows) return;
   const int64_t t = row / num_kv_heads;
   const int g = (int)(row % num_kv_heads);
+  const int64_t src_row = t * num_kv_heads + g;
+  // The slot and the row's source values are loaded together (the source
+  // addresses do not depend on the slot); the slot is checked after.
   const int64_t slot = slots[t];
+
+  if constexpr (CT == PKV_I4) {
+    // Lane i holds two elements that share a stored byte: K elements 2i, 2i+1;
+    // V elements d and d + 16 with d = 32 (i / 16) + i % 16.
+    static_assert(D == 128, "INT4 rows are 128 elements");
+    float x[2][2];
+    int d0[2];
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      const void* src = which == 0 ? k : v;
+      d0[which] = which == 0 ? 2 * lane : 32 * (lane >> 4) + (lane & 15);
+      const int d1 = which == 0 ? d0[which] + 1 : d0[which] + 16;
+      x[which][0] = load_f32<ST>(src, src_row * D + d0[which]);
+      x[which][1] = load_f32<ST>(src, src_row * D + d1);
+    }
+    if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
+    const int64_t blk = slot / block_size;
+    const int off = (int)(slot % block_size);
+    const int t16 = off & 15;
+    const int64_t dst_row = (blk * num_kv_heads + g) * block_size + off;   // scale index
+    const int64_t group_byte = (dst_row - t16) * R;                      // first byte of the group
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+      uint8_t* cache = static_cast<uint8_t*>(which == 0 ? k_cache : v_cache) + group_byte;
+      float* sc = which == 0 ? k_scale : v_scale;
+      const float a = wave_max(fmaxf(__builtin_fabsf(x[which][0]), __builtin_fabsf(x[which][1])));
+      const float s = int4_row_scale(a);
+      const uint32_t bits = int4_nibble(x[which][0], s) | (int4_nibble(x[which][1], s) << 4);
+      const int pos = which == 0 ? k_group_offset(t16, lane, 1) : v4_group_nibble(t16, d0[which]) >> 1;
+      cache[pos] = (uint8_t)bits;
+      if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
+    }
+    return;
+  }
+  // Same type: the stored bits; otherwise the values as f32.
+  uint32_t raw[2][PER];
+  float xv[2][PER];
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const void* src = which == 0 ? k : v;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int64_t i = src_row * D + lane * PER + e;
+      if constexpr (CT == ST) {
+        if constexpr (eb == 4)
+          raw[which][e] = static_cast<const uint32_t*>(src)[i];
+        else
+          raw[which][e] = static_cast<const uint16_t*>(src)[i];
+      } else {
+        xv[which][e] = load_f32<ST>(src, i);
+      }
+    }
+  }
   if (slot < 0 || slot >= (int64_t)num_blocks * block_size) return;
   const int64_t blk = slot / block_size;
   const int off = (int)(slot % block_size);
   const int t16 = off & 15;
   const int64_t dst_row = (blk * num_kv_heads + g) * block_size + off;   // scale index
   const int64_t group_byte = (dst_row - t16) * R;                      // first byte of the group
-  const int64_t src_row = t * num_kv_heads + g;
-
-  if constexpr (CT == PKV_I4) {
-    // Lane i holds two elements that share a stored byte: K elements 2i, 2i+1;
-    // V elements d and d + 16 with d = 32 (i / 16) + i % 16.
-    static_assert(D == 128, "INT4 rows are 128 elements");
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const void* src = which == 0 ? k : v;
-      uint8_t* cache = static_cast<uint8_t*>(which == 0 ? k_cache : v_cache) + group_byte;
-      float* sc = which == 0 ? k_scale : v_scale;
-      const int d0 = which == 0 ? 2 * lane : 32 * (lane >> 4) + (lane & 15);
-      const int d1 = which == 0 ? d0 + 1 : d0 + 16;
-      const float x0 = load_f32<ST>(src, src_row * D + d0);
-      const float x1 = load_f32<ST>(src, src_row * D + d1);
-      const float a = wave_max(fmaxf(__builtin_fabsf(x0), __builtin_fabsf(x1)));
-      const float s = int4_row_scale(a);
-      const uint32_t b = int4_nibble(x0, s) | (int4_nibble(x1, s) << 4);
-      const int pos = which == 0 ? k_group_offset(t16, lane, 1) : v4_group_nibble(t16, d0) >> 1;
-      cache[pos] = (uint8_t)b;
-      if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
-    }
-    return;
-  }
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    const void* src = which == 0 ? k : v;
     uint8_t* cache = static_cast<uint8_t*>(which == 0 ? k_cache : v_cache) + group_byte;
     float* sc = which == 0 ? k_scale : v_scale;
     int pos[PER];
@@ -255,31 +286,25 @@ __global__ __launch_bounds__(256) void append_kernel(const void* __restrict__ k,
     if constexpr (CT == ST) {
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const int64_t i = src_row * D + lane * PER + e;
         if constexpr (eb == 4)
-          *reinterpret_cast<uint32_t*>(cache + pos[e]) = static_cast<const uint32_t*>(src)[i];
+          *reinterpret_cast<uint32_t*>(cache + pos[e]) = raw[which][e];
         else
-          *reinterpret_cast<uint16_t*>(cache + pos[e]) = static_cast<const uint16_t*>(src)[i];
+          *reinterpret_cast<uint16_t*>(cache + pos[e]) = (uint16_t)raw[which][e];
       }
-    } else {
-      float xv[PER];
+    } else if constexpr (CT == PKV_I8) {
+      float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < PER; ++e) xv[e] = load_f32<ST>(src, src_row * D + lane * PER + e);
-      if constexpr (CT == PKV_I8) {
-        float a = 0.0f;
+      for (int e = 0; e < PER; ++e) a = fmaxf(a, __builtin_fabsf(xv[which][e]));
+      a = wave_max(a);
+      const float s = int8_row_scale(a);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) a = fmaxf(a, __builtin_fabsf(xv[e]));
-        a = wave_max(a);
-        const float s = int8_row_scale(a);
+      for (int e = 0; e < PER; ++e)
+        cache[pos[e]] = (uint8_t)(s == 0.0f ? (int8_t)0 : int8_code(xv[which][e], s));
+      if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
+    } else {  // FP8 with the tensor's scale
+      const float s = sc[0];
 #pragma unroll
-        for (int e = 0; e < PER; ++e)
-          cache[pos[e]] = (uint8_t)(s == 0.0f ? (int8_t)0 : int8_code(xv[e], s));
-        if (lane == 0) sc[dst_row] = s == 0.0f ? 1.0f : s;
-      } else {  // FP8 with the tensor's scale
-        const float s = sc[0];
-#pragma unroll
-        for (int e = 0; e < PER; ++e) cache[pos[e]] = fp8_code(xv[e], s);
-      }
+      for (int e = 0; e < PER; ++e) cache[pos[e]] = fp8_code(xv[which][e], s);
     }
   }
 }
