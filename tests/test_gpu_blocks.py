@@ -280,3 +280,21 @@ def test_manager_swap_out_reuse_and_swap_in_end_to_end():
         for h in range(Hq):
             ref[b, h] = oracle.attend(q[b, h].double().numpy(), K[:, h // G], V[:, h // G], d ** -0.5)
     compare(got, ref, "f16", "swap end to end")
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_paged_pools_of_a_32k_sequence_match_the_closed_form(bs):
+    # One Llama-2-70B-shaped sequence of 32,768 tokens (8 KV heads, head_dim 128,
+    # fp16, 80 layers): its K and V pools, in whole blocks, take exactly the
+    # closed-form KV size the pages print (10,737,418,240 bytes); no tail is wasted.
+    blocks = -(-32768 // bs)
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    pools = [torch.empty((blocks, 8, bs, 128), dtype=torch.float16, device="cuda")
+             for _ in range(2 * 80)]
+    delta = torch.cuda.memory_allocated() - before
+    want = pkv.kv_cache_bytes(1, 32768, 80, 8, 128, 2)
+    del pools
+    torch.cuda.empty_cache()
+    assert want == 10_737_418_240
+    assert delta == want
