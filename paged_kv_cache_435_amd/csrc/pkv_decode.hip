@@ -37,11 +37,12 @@
 //    in unused slots never reach the sums.
 //  * Several query tokens per sequence (prompt chunks, draft verification) use
 //    the same kernel with MULTI set: a wave takes 32 rows of (query token, head
-//    of the group), each lane masking tokens past its row's causal position,
-//    and up to four such waves of one (sequence, KV head, chunk) form a
-//    workgroup.  multi_prep_kernel turns each sequence's rows into "virtual
-//    sequences" whose contexts end at their last row's position, so the planner
-//    and the merge above work unchanged.
+//    of the group), each lane masking tokens past its row's causal position;
+//    up to four such waves of one (sequence, KV head, chunk) form a
+//    workgroup, or, when a virtual sequence is one wave, eight waves take the
+//    KV heads of one (sequence, chunk) as in decode.  multi_prep_kernel turns
+//    each sequence's rows into "virtual sequences" whose contexts end at their
+//    last row's position, so the planner and the merge above work unchanged.
 #include <stdlib.h>
 
 #include <atomic>
@@ -173,7 +174,7 @@ __host__ __device__ __forceinline__ int multi_wpg(const DecodeArgs& a, bool mult
 // group's last causal limit; a.context_lens holds those lengths and a.vseq_b /
 // a.vseq_g / a.vseq_rt say which sequence, KV head and row group each is
 // (written by multi_prep_kernel).  A wave takes one 32-row tile; the
-// head_tiles waves of a group form one workgroup.
+// head_tiles waves of a group form one workgroup (multi_wpg).
 template <int KV, int QT, int D, int BS, bool MULTI>
 __global__ __launch_bounds__(64 * (MULTI && kMultiGroupMax > kDecodeWaves ? kMultiGroupMax
                                                                            : kDecodeWaves))
