@@ -287,6 +287,22 @@ def bench_blocks(args):
     moved = 2 * 2 * n_pairs * block_bytes      # K and V, read + write
     gbps = moved / t / 1e9
 
+    # Yardstick: a plain grid-stride copy of 1 GiB (read + write) on the same device.
+    from paged_kv_cache_435_amd import probe
+    csrc = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    cdst = torch.empty_like(csrc)
+    probe.copy(cdst, csrc)
+    cev = LaunchEvents(10)
+    for _ in range(10):
+        i = cev.begin()
+        probe.copy(cdst, csrc)
+        cev.end(i)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / float(np.median(cev.seconds())) / 1e9
+    cev.close()
+    del csrc, cdst
+    log(f"[bench] kv_copy_blocks {gbps:.0f} GB/s; plain 1 GiB copy {copy_gbps:.0f} GB/s (read + write)")
+
     # Swap: 4096 blocks (512 MiB of K+V at this shape) to pinned host memory and
     # back, each direction as one kv_swap_blocks call on a side stream (DMA);
     # runs of consecutive blocks are merged, so the pairs are shuffled singles.
@@ -345,7 +361,8 @@ def bench_blocks(args):
                   "block-manager host ops/s",
         "copy_blocks": {"pairs": n_pairs, "block_bytes_per_cache": block_bytes,
                         "avg_launch_us": t * 1e6, "achieved": gbps, "peak": HBM_PEAK_GBPS,
-                        "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS},
+                        "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                        "plain_copy_gbps": copy_gbps},
         "swap": {"blocks": n_swap, "bytes": swap_bytes, "pairs": "shuffled single blocks",
                  "out_us": t_out * 1e6, "out_gbps": swap_bytes / t_out / 1e9,
                  "in_us": t_in * 1e6, "in_gbps": swap_bytes / t_in / 1e9,
