@@ -337,6 +337,32 @@ def bench_blocks(args):
     log(f"[bench] swap {n_swap} blocks: out {swap_bytes / t_out / 1e9:.1f} GB/s, "
         f"in {swap_bytes / t_in / 1e9:.1f} GB/s")
 
+    # Yardstick: one contiguous copy of the same bytes between pinned host memory
+    # and the device (torch's copy), each way.
+    hbuf = torch.empty(swap_bytes, dtype=torch.uint8, pin_memory=True)
+    dbuf = torch.empty(swap_bytes, dtype=torch.uint8, device=dev)
+
+    def timed_copy(to_host, reps=5):
+        ts = LaunchEvents(reps)
+        for _ in range(reps):
+            i = ts.begin()
+            if to_host:
+                hbuf.copy_(dbuf, non_blocking=True)
+            else:
+                dbuf.copy_(hbuf, non_blocking=True)
+            ts.end(i)
+        torch.cuda.synchronize()
+        t = float(np.median(ts.seconds()))
+        ts.close()
+        return t
+
+    timed_copy(True, 1)
+    pin_out = swap_bytes / timed_copy(True) / 1e9
+    pin_in = swap_bytes / timed_copy(False) / 1e9
+    del hbuf, dbuf
+    log(f"[bench] contiguous pinned copy of the same bytes: out {pin_out:.1f} GB/s, "
+        f"in {pin_in:.1f} GB/s")
+
     bm = pkv.BlockManager(1 << 16, 16, prefix_caching=True)
     rng = np.random.default_rng(1)
     B = 256
@@ -364,6 +390,7 @@ def bench_blocks(args):
                         "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                         "plain_copy_gbps": copy_gbps},
         "swap": {"blocks": n_swap, "bytes": swap_bytes, "pairs": "shuffled single blocks",
+                 "contiguous_pinned_copy_gbps": {"out": pin_out, "in": pin_in},
                  "out_us": t_out * 1e6, "out_gbps": swap_bytes / t_out / 1e9,
                  "in_us": t_in * 1e6, "in_gbps": swap_bytes / t_in / 1e9,
                  "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
