@@ -171,6 +171,20 @@ def test_planner_shapes(name, ctx, hq, hkv, d, bs):
     run_and_check(w)
 
 
+@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("d,ctx", [(128, [4096, 4097, 4095, 4111, 1]),
+                                   (64, [8192, 8193, 8191, 8207, 1])])
+def test_merge_one_round_limit(q_dtype, d, ctx):
+    """A batch this small plans items of the minimum 8 tiles, so a sequence of
+    n 16-token tiles is merged from ceil(n / 8) partials per row.  The merge
+    loads up to 16 x 64 / (d / 4) of them in one round (32 at d 128, 64 at
+    d 64) and loops over them beyond that: these contexts put 31-33 (d 128) and
+    63-65 (d 64) partials on each side of the switch."""
+    w = W.custom(q_dtype, "f16" if q_dtype == torch.float16 else "bf16", ctx, 8, 1, d, 16,
+                 name=f"merge-limit-d{d}")
+    run_and_check(w)
+
+
 @pytest.mark.parametrize("q_dtype,kv", [
     (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
     (torch.float16, "i8"), (torch.bfloat16, "fp8"), (torch.float32, "i8"), (torch.float32, "fp8"),

@@ -199,6 +199,17 @@ def test_prompt_chunk_on_a_long_context_is_split_and_merged():
     run_multi(w, [64])
 
 
+@pytest.mark.parametrize("lens", [[1, 1, 1, 1, 1], [3, 2, 4, 1, 1]])
+def test_merge_one_round_limit(lens):
+    """Items of the minimum 8 tiles: a row over a context of n tiles is merged
+    from ceil(n / 8) partials, and this merge loads up to 4 x 64 / 32 = 8 of
+    them in one round at d 128.  Contexts of 1023-1040 tokens give a row
+    group 8 or 9 partials, on both sides of that switch."""
+    w = W.custom(torch.bfloat16, "bf16", [1024, 1025, 1023, 1040, 1], 16, 2, 128, 16,
+                 name="multi-merge-limit")
+    run_multi(w, lens)
+
+
 @pytest.mark.parametrize("hq,hkv,qlen", [(64, 8, None), (16, 2, 16)])
 def test_more_than_1024_sequences(hq, hkv, qlen):
     """1100 sequences: the planning pass takes them in two rounds of 1024 and
