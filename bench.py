@@ -7,7 +7,7 @@ A step is the whole hot path for one batch: ``kv_cache_append`` writes the new
 token of every sequence into its slot (quantizing it for INT8/FP8 caches), then
 ``paged_attention_decode`` attends each query head over its sequence's cache,
 found through the block table, for every layer of the workload.  Inputs are
-synthetic and seeded (``paged_kv_cache_435_amd.workloads``) and already resident
+synthetic and seeded (``harness.workloads``) and already resident
 in HBM when timing starts.
 
 The default workload is the Llama-2-70B-shaped GQA-8 layer: fp16 KV, 64 query
@@ -63,7 +63,13 @@ def parse():
                          "known traffic, for calibrating hardware byte counters)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle sample (0 = skip)")
-    return ap.parse_args()
+    ap.add_argument("--library", default=os.environ.get("PKV_LIBRARY"),
+                    help="another build of libpagedkv.so to time (compile-time tuning; "
+                         "default: the in-tree build)")
+    args = ap.parse_args()
+    import paged_kv_cache_435_amd as pkv
+    pkv.load_library(args.library)   # raises if the HIP library was not built
+    return args
 
 
 def decode_sources_sha256():
@@ -200,7 +206,7 @@ def cpu_baseline(w, cases, budget_s):
     import torch
 
     import oracle
-    from paged_kv_cache_435_amd.device_cache import cache_to_host, q_to_host
+    from harness.device_cache import cache_to_host, q_to_host
 
     try:
         from threadpoolctl import threadpool_info
@@ -288,7 +294,7 @@ def bench_blocks(args):
     gbps = moved / t / 1e9
 
     # Yardstick: a plain grid-stride copy of 1 GiB (read + write) on the same device.
-    from paged_kv_cache_435_amd import probe
+    from harness import probe
     csrc = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     cdst = torch.empty_like(csrc)
     probe.copy(cdst, csrc)
@@ -414,8 +420,8 @@ def bench_multi(args, name):
     import torch
 
     import paged_kv_cache_435_amd as pkv
-    from paged_kv_cache_435_amd import workloads as W
-    from paged_kv_cache_435_amd.device_cache import DeviceCase
+    from harness import workloads as W
+    from harness.device_cache import DeviceCase
 
     dev = torch.device("cuda:0")
     w, q_lens = W.make_multi(name)
@@ -519,13 +525,12 @@ def main():
     import torch
 
     import paged_kv_cache_435_amd as pkv
-    from paged_kv_cache_435_amd import workloads as W
-    from paged_kv_cache_435_amd.device_cache import DeviceCase
+    from harness import workloads as W
+    from harness.device_cache import DeviceCase
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
-    pkv.load_library()   # raises if the HIP library was not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
@@ -543,7 +548,7 @@ def main():
     torch.cuda.synchronize()
 
     if args.copy_probe > 0:
-        from paged_kv_cache_435_amd import probe
+        from harness import probe
         n = args.copy_probe << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -624,7 +629,7 @@ def main():
     # MI355X), and the grid-stride read for reference.
     ceiling = plain = None
     if args.read_ceiling:
-        from paged_kv_cache_435_amd import probe
+        from harness import probe
         ceiling = probe.read_gbps(4 << 30, reps=10, device=dev, slabs=256)
         plain = probe.read_gbps(4 << 30, reps=10, device=dev)
         log(f"[bench] 4 GiB streaming read: {ceiling:.0f} GB/s (contiguous slabs), "

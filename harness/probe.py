@@ -16,7 +16,7 @@ def _lib():
     if _LIB is None:
         path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpkvprobe.so")
         if not os.path.exists(path):
-            raise RuntimeError(f"{path} is missing: build with `python -m paged_kv_cache_435_amd.build`")
+            raise RuntimeError(f"{path} is missing: build with `python -m harness.build_probe`")
         lib = ctypes.CDLL(path)
         lib.pkv_probe_grid.restype = ctypes.c_int32
         lib.pkv_probe_read.restype = ctypes.c_int32

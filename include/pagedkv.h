@@ -290,11 +290,14 @@ pkv_status kv_copy_blocks(void* k_cache, void* v_cache, float* k_scale, float* v
  *     writing the new rows (copy-on-write).
  *   - With prefix caching, each full block is keyed by a hash chained over all
  *     token ids from the sequence start through the block's end; a new
- *     sequence whose leading full blocks match cached keys shares those blocks
+ *     sequence whose leading full blocks match cached blocks shares those blocks
  *     (their slots come back as -1: their rows are already stored, and
- *     kv_cache_append skips negative slots).  Unreferenced cached blocks stay
- *     reusable until a fresh block is needed and no free block is left; then
- *     the least recently released is taken.
+ *     kv_cache_append skips negative slots).  A key match is only a candidate:
+ *     it is shared only if the cached block holds the same token ids and was
+ *     sealed after the block just matched for the previous position (still
+ *     holding that content), so equal keys of different prefixes are misses.
+ *     Unreferenced cached blocks stay reusable until a fresh block is needed
+ *     and no free block is left; then the least recently released is taken.
  *   - Failed calls change nothing.  Every call is host only and thread-safe.
  */
 typedef struct pkv_block_manager pkv_block_manager;
@@ -312,6 +315,12 @@ void pkv_bm_destroy(pkv_block_manager* bm);
 int32_t pkv_bm_num_free(pkv_block_manager* bm);
 /* References held on a block (-1 for a bad index). */
 int32_t pkv_bm_ref_count(pkv_block_manager* bm, int32_t block);
+
+/* Test hook, for tests of the content check only: keep just the bits of `mask`
+ * of every lookup key, so that unrelated blocks collide (mask 0: every key is
+ * the same).  Only before the manager's first sequence (PKV_ERR_INVALID_ARG
+ * after).  Sharing stays exact; only the number of misses changes. */
+pkv_status pkv_bm_debug_hash_mask(pkv_block_manager* bm, uint64_t mask);
 
 /* Starts sequence seq_id with its n prompt tokens (host int32 ids; ids only
  * matter for prefix caching).  Writes the pool slot of every token to host

@@ -3,10 +3,16 @@
     python -m paged_kv_cache_435_amd.build
 
 Every HIP source under csrc/ is compiled to an object (in parallel), then linked
-into ``paged_kv_cache_435_amd/libpagedkv.so``.  The streaming yardstick kernels
-under csrc/probe/ (not part of the attention path) go into ``libpkvprobe.so``.  No fast-math: the INT8/FP8
+into ``paged_kv_cache_435_amd/libpagedkv.so``.  No fast-math: the INT8/FP8
 quantizers rely on IEEE division and round-half-even.  Packed-FP32 instruction
 selection is turned off for all device code.
+
+Denormals are kept, explicitly, for every floating-point type
+(``-fdenormal-fp-math=ieee``, ``-fno-gpu-flush-denormals-to-zero``): with f16
+queries, INT8 and INT4 codes enter the matrix instructions as f16 subnormals
+(code + offset) * 2^-24, so a mode that flushed f16 denormals would turn every
+code into zero.  The kernels' descriptors then carry denormal mode 3 (in and out
+kept) for f32 and for f16/f64.
 """
 import glob
 import os
@@ -19,7 +25,6 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpagedkv.so")
-PROBE_LIB = os.path.join(PKG, "libpkvprobe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
@@ -28,6 +33,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fdenormal-fp-math=ieee", "-fno-gpu-flush-denormals-to-zero",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
@@ -60,11 +66,6 @@ def build(verbose=False, out=None, defines=()):
     tmp = lib + ".tmp"
     logs.append(_run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
     os.replace(tmp, lib)
-    if out is None:
-        probe_src = os.path.join(CSRC, "probe", "pkv_probe.hip")
-        tmp = PROBE_LIB + ".tmp"
-        logs.append(_run([HIPCC, *CFLAGS, "-shared", probe_src, "-o", tmp]))
-        os.replace(tmp, PROBE_LIB)
     if verbose:
         for log in logs:
             if log.strip():

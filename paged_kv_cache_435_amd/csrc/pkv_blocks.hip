@@ -12,10 +12,15 @@
 // written.  Appending into a shared, partly filled last block first moves the
 // sequence to a fresh copy (copy-on-write; the caller copies the block's bytes
 // on the device with kv_copy_blocks).  Full blocks are immutable, so prefix
-// caching shares them by content: a full block is keyed by a hash chained over
-// every token from the start of the sequence through the block's end.  Cached
-// blocks nobody references stay reusable until a fresh block is needed and the
-// free list is empty; then the least recently released one is taken.
+// caching shares them by content: a full block is looked up by a hash chained
+// over every token from the start of the sequence through the block's end, and
+// a hit is taken only once its content is proven equal: the block's own token
+// ids match, and its predecessor when it was sealed is the block just matched
+// for the previous position, unchanged since (same epoch).  By induction the
+// whole prefix then matches, so a hash collision costs a miss, never a wrong
+// block.  Cached blocks nobody references stay reusable until a fresh block is
+// needed and the free list is empty; then the least recently released one is
+// taken.
 //
 // Swap space ([P3], vLLM configuration: swap_space moves inactive KV cache to
 // CPU memory so more requests fit than HBM holds): with a host pool enabled, a
@@ -39,8 +44,10 @@ namespace {
 
 constexpr uint64_t kNoHash = 0;
 
-// 64-bit FNV-1a over the previous block's key and this block's token ids.
-uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int n) {
+// 64-bit FNV-1a over the previous block's key and this block's token ids,
+// keeping the bits of `mask` (all of them, except under the test hook
+// pkv_bm_debug_hash_mask).  Only a lookup key: hits are checked by content.
+uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int n, uint64_t mask) {
   uint64_t h = 1469598103934665603ull;
   auto mix = [&h](uint64_t x) {
     for (int i = 0; i < 8; ++i) {
@@ -50,6 +57,7 @@ uint64_t chain_hash(uint64_t prev, const int32_t* tokens, int n) {
   };
   mix(prev);
   for (int i = 0; i < n; ++i) mix((uint32_t)tokens[i]);
+  h &= mask;
   return h == kNoHash ? 1 : h;
 }
 
@@ -69,6 +77,12 @@ struct pkv_block_manager {
   bool prefix_caching;
   std::vector<int32_t> ref;                    // references per block
   std::vector<uint64_t> key;                   // content key of a cached full block (0: none)
+  // Prefix caching: what a keyed block holds, to check a hit by content.
+  std::vector<int32_t> key_tokens;             // [num_blocks][block_size] token ids
+  std::vector<int32_t> key_parent;             // predecessor block when sealed (-1: first)
+  std::vector<uint32_t> key_parent_epoch;      // that predecessor's epoch then
+  std::vector<uint32_t> epoch;                 // bumped each time a block is handed out fresh
+  uint64_t hash_mask = ~0ull;
   std::vector<int32_t> free_list;              // blocks with no references and no key
   std::list<int32_t> evictable;                // cached blocks with no references, oldest first
   std::vector<std::list<int32_t>::iterator> evict_pos;
@@ -100,6 +114,7 @@ int32_t take_fresh(pkv_block_manager* bm) {
     const int32_t b = bm->free_list.back();
     bm->free_list.pop_back();
     bm->ref[b] = 1;
+    ++bm->epoch[b];
     return b;
   }
   if (bm->evictable.empty()) return -1;
@@ -109,7 +124,19 @@ int32_t take_fresh(pkv_block_manager* bm) {
   bm->cache.erase(bm->key[b]);
   bm->key[b] = kNoHash;
   bm->ref[b] = 1;
+  ++bm->epoch[b];   // its content is about to change: blocks sealed after it stop matching
   return b;
+}
+
+// Is cached block x, found under the key of logical block j of a new
+// sequence, that sequence's block?  Its token ids must equal `tokens` (the
+// block's bs ids) and its predecessor when sealed must be `prev` (the block
+// matched for j - 1, -1 for j = 0) in its current epoch.
+bool same_content(const pkv_block_manager* bm, int32_t x, const int32_t* tokens, int32_t prev) {
+  const int bs = bm->block_size;
+  if (memcmp(&bm->key_tokens[(size_t)x * bs], tokens, sizeof(int32_t) * bs) != 0) return false;
+  if (bm->key_parent[x] != prev) return false;
+  return prev < 0 || bm->key_parent_epoch[x] == bm->epoch[prev];
 }
 
 void take_ref(pkv_block_manager* bm, int32_t b) {
@@ -134,15 +161,22 @@ void drop_ref(pkv_block_manager* bm, int32_t b) {
 // The sequence's last block just filled: give it its content key and, with
 // prefix caching, offer it for sharing (a block already holding that key wins).
 void seal_block(pkv_block_manager* bm, Sequence& s) {
-  const uint64_t k = chain_hash(s.last_full_key, s.pending.data(), (int)s.pending.size());
+  const uint64_t k =
+      chain_hash(s.last_full_key, s.pending.data(), (int)s.pending.size(), bm->hash_mask);
   s.last_full_key = k;
-  s.pending.clear();
-  if (!bm->prefix_caching) return;
-  const int32_t b = s.blocks.back();
-  if (bm->ref[b] == 1 && bm->key[b] == kNoHash && bm->cache.find(k) == bm->cache.end()) {
-    bm->key[b] = k;
-    bm->cache[k] = b;
+  if (bm->prefix_caching) {
+    const int32_t b = s.blocks.back();
+    if (bm->ref[b] == 1 && bm->key[b] == kNoHash && bm->cache.find(k) == bm->cache.end()) {
+      bm->key[b] = k;
+      bm->cache[k] = b;
+      const size_t bs = (size_t)bm->block_size;
+      memcpy(&bm->key_tokens[(size_t)b * bs], s.pending.data(), sizeof(int32_t) * bs);
+      const int32_t prev = s.blocks.size() >= 2 ? s.blocks[s.blocks.size() - 2] : -1;
+      bm->key_parent[b] = prev;
+      bm->key_parent_epoch[b] = prev >= 0 ? bm->epoch[prev] : 0u;
+    }
   }
+  s.pending.clear();
 }
 
 int64_t slot_of(const pkv_block_manager* bm, const Sequence& s, int64_t pos) {
@@ -168,6 +202,12 @@ pkv_block_manager* pkv_bm_create(int32_t num_blocks, int32_t block_size,
   bm->prefix_caching = enable_prefix_caching != 0;
   bm->ref.assign(num_blocks, 0);
   bm->key.assign(num_blocks, kNoHash);
+  bm->epoch.assign(num_blocks, 0u);
+  if (bm->prefix_caching) {
+    bm->key_tokens.assign((size_t)num_blocks * block_size, 0);
+    bm->key_parent.assign(num_blocks, -1);
+    bm->key_parent_epoch.assign(num_blocks, 0u);
+  }
   bm->evict_pos.resize(num_blocks);
   bm->in_evictable.assign(num_blocks, false);
   bm->free_list.reserve(num_blocks);
@@ -189,6 +229,15 @@ int32_t pkv_bm_ref_count(pkv_block_manager* bm, int32_t block) {
   return bm->ref[block];
 }
 
+pkv_status pkv_bm_debug_hash_mask(pkv_block_manager* bm, uint64_t mask) {
+  if (!bm) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_debug_hash_mask: NULL manager");
+  std::lock_guard<std::mutex> lock(bm->mu);
+  if (!bm->seqs.empty() || !bm->cache.empty())
+    return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_debug_hash_mask: only before the first sequence");
+  bm->hash_mask = mask;
+  return PKV_OK;
+}
+
 pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens,
                                int32_t n, int64_t* slots) {
   if (!bm) return bm_fail(PKV_ERR_INVALID_ARG, "pkv_bm_add_sequence: NULL manager");
@@ -203,9 +252,11 @@ pkv_status pkv_bm_add_sequence(pkv_block_manager* bm, int64_t seq_id, const int3
   uint64_t k = kNoHash;
   if (bm->prefix_caching) {
     for (int64_t j = 0; j < n / bs; ++j) {
-      const uint64_t kj = chain_hash(k, tokens + j * bs, bs);
+      const uint64_t kj = chain_hash(k, tokens + j * bs, bs, bm->hash_mask);
       auto it = bm->cache.find(kj);
       if (it == bm->cache.end()) break;
+      // (a key match that is not this content is a collision: a miss)
+      if (!same_content(bm, it->second, tokens + j * bs, hits.empty() ? -1 : hits.back())) break;
       hits.push_back(it->second);
       k = kj;
     }

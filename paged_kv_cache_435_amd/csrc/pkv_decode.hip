@@ -158,6 +158,10 @@ struct Tuning {
   static constexpr int item_tiles =
       KV == PKV_I4 ? PKV_ITEM_TILES_I4 : (KV == PKV_I8 ? PKV_ITEM_TILES_I8 : kItemTilesMax);
   static_assert(item_tiles >= kItemTilesMin && item_tiles <= kItemTilesMax, "item limit");
+  // The host bounds the items of every plan (grid and workspace rows) with the
+  // smallest limit of any kernel, kPrefillItemTilesMax: no decode instance may
+  // plan shorter items than that.
+  static_assert(item_tiles >= kPrefillItemTilesMax, "max_items_bound assumes this limit");
 };
 
 // Waves per workgroup: decode takes kDecodeWaves consecutive items (the KV
@@ -208,11 +212,12 @@ void decode_partition_kernel(DecodeArgs a) {
   // barrier), so any of them may stop early. ----
   const int wpg = multi_wpg(a, MULTI);               // waves per workgroup
   Plan plan;
+  SeqCtx seqs;                                        // (decode: the contexts read once)
   if constexpr (MULTI) {
     plan.items = planned_items(a);                    // made by multi_prep_kernel
     plan.tpi = 0;
   } else {
-    plan = make_plan(a, lane);
+    plan = make_plan(a, lane, seqs);
   }
   const int64_t groups = (plan.items + wpg - 1) / wpg;
   const int64_t per_xcd = (groups + 7) / 8;
@@ -225,7 +230,7 @@ void decode_partition_kernel(DecodeArgs a) {
   if constexpr (MULTI) {
     planned_seq(a, item, b, sq);
   } else {
-    if (!seq_of_item(a, plan, item, lane, b, sq)) return;
+    if (!seq_of_item(a, plan, seqs, item, lane, b, sq)) return;
   }
   b = uni(b);
   const int local = uni((int)(item - sq.first));   // < m * units per sequence
@@ -260,8 +265,10 @@ void decode_partition_kernel(DecodeArgs a) {
     bq = uni(a.vseq_b[b]);
     if (bq < 0) return;                                // padding (never planned: no context)
     const int rt = uni(a.vseq_rt[b]);
-    const int q0 = uni(a.query_start[bq]);
-    const int L = uni(a.query_start[bq + 1]) - q0;
+    int q0, L;
+    query_span(a, bq, q0, L);
+    q0 = uni(q0);
+    L = uni(L);
     int cr = a.real_ctx[bq];
     cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
     const int row0 = (a.head_tiles * rt + ht) * 16 * RT;   // first row of this wave
@@ -291,7 +298,7 @@ void decode_partition_kernel(DecodeArgs a) {
   constexpr int NREG =
       (Tuning<KV>::item_tiles * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
   const int first_blk = t_begin / BS;
-  const int nblk = (t_end - 1) / BS - first_blk + 1;
+  const int nblk = ntiles > 0 ? (t_end - 1) / BS - first_blk + 1 : 0;   // (empty: an item of zeros)
   int blk[NREG];
 #pragma unroll
   for (int r = 0; r < NREG; ++r) {
@@ -861,27 +868,17 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int64_t row0, int
   store_out4<QT>(a.out, hq * D + 4 * dq, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
-// Decode: one wave per (query head, sequence).  A sequence with no context
-// gets zeros here.
+// Decode: one wave per (query head, sequence).  Launched only when a unit may
+// be split (a workspace); units that were one item, empty sequences
+// included, were finished by the partition kernel.
 template <int QT, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int lane = threadIdx.x;
   const int64_t hq = (int64_t)b * a.num_q_heads + h;
-  // The context and the sequence's record are loaded together (the record is
-  // only used when the context is not empty).
-  const int ctx = seq_ctx(a, b);
-  int64_t first = 0;
-  int m = 0;
-  if (a.ws_seq) {                     // no workspace: every unit was one item
-    first = a.ws_seq[2 * b];
-    m = (int)a.ws_seq[2 * b + 1];
-  }
-  if (ctx == 0) {
-    if (lane < D / 4) store_out4<QT>(a.out, hq * D + 4 * lane, 0.f, 0.f, 0.f, 0.f);
-    return;
-  }
+  const int64_t first = a.ws_seq[2 * b];
+  const int m = (int)a.ws_seq[2 * b + 1];
   if (m <= 1) return;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int g = h / G;
@@ -912,8 +909,8 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   const int bq = a.vseq_b[v];
   if (bq < 0) return;                 // a padding entry
   const int64_t row0 = (int64_t)ROWS * a.vseq_rt[v];   // first row of this virtual sequence
-  const int q0 = a.query_start[bq];
-  const int L = a.query_start[bq + 1] - q0;
+  int q0, L;
+  query_span(a, bq, q0, L);
   int64_t rows = (int64_t)L * G - row0;
   rows = rows > ROWS ? ROWS : rows;
   // rows past the query tensor (inconsistent query_start) are never written
@@ -1008,24 +1005,31 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     const int b = b0 + t;
     int L = 0, cx = 0;
     if (b < batch_real) {
-      L = a.query_start[b + 1] - a.query_start[b];
-      L = L < 0 ? 0 : L;
+      // (query_start is a precondition; clamped so that a bad entry cannot
+      // make a count overflow or an index leave its array: 0 <= L <= q_rows)
+      int q0;
+      query_span(a, b, q0, L);
       cx = a.real_ctx[b];
       cx = cx < 0 ? 0 : (cx > a.ctx_cap ? a.ctx_cap : cx);
     }
     seq_len[t] = L;
     seq_cx[t] = cx;
     const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
+    // (L * G < 2^31: the host limits q_rows * G)
     if ((L * G + ROWS - 1) / ROWS > 1) atomicOr(&several_groups, 1);
-    int n = a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);   // (KV head, row group) entries
+    const int64_t n64 = (int64_t)a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);
+    // (KV head, row group) entries; past a.batch (the host's bound) nothing is
+    // written, so the count is capped there
+    int n = (int)(n64 < a.batch ? n64 : a.batch);
     int unused = 0, total = 0, unused_tot = 0;
     block_scan2(n, unused, wtot, total, unused_tot);
     scan[t] = n;                             // inclusive
     __syncthreads();
     const int base = carry;
     for (int e = t; e < total; e += 1024) {
-      const int v = base + e;
-      if (v >= a.batch) break;
+      const int64_t v64 = (int64_t)base + e;
+      if (v64 < 0 || v64 >= a.batch) break;
+      const int v = (int)v64;
       int lo = 0, hi = 1023;                 // first sequence whose scan passes e
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
@@ -1051,7 +1055,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       a.vseq_g[v] = gg;
     }
     __syncthreads();
-    if (t == 0) carry = base + total;
+    if (t == 0) {
+      int64_t c = (int64_t)base + total;
+      carry = (int)(c < 0 ? 0 : (c > a.batch ? a.batch : c));
+    }
     __syncthreads();
   }
   for (int v = carry + t; v < a.batch; v += 1024) {
@@ -1222,9 +1229,11 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   // Every item has at least kItemTilesMin tiles, so a unit makes at most
   // ceil(tiles / kItemTilesMin) items: small batches launch few workgroups.
   int64_t need = max_items_bound(a.batch, units, a.ctx_cap, a.slots);
+  // (an empty decode sequence still makes one item per unit, its zeros)
   const int64_t unit_tiles = ((int64_t)a.ctx_cap + kTileTokens - 1) / kTileTokens;
-  const int64_t short_bound =
-      (int64_t)a.batch * units * ((unit_tiles + kItemTilesMin - 1) / kItemTilesMin);
+  int64_t unit_items = (unit_tiles + kItemTilesMin - 1) / kItemTilesMin;
+  unit_items = unit_items < 1 ? 1 : unit_items;
+  const int64_t short_bound = (int64_t)a.batch * units * unit_items;
   if (short_bound < need) need = short_bound > 0 ? short_bound : 1;
   const int64_t grid = ((need + wpg - 1) / wpg + 7) / 8 * 8;
   if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
@@ -1241,7 +1250,7 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
     hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, (rows + kMergeWaves - 1) / kMergeWaves),
                        dim3(64 * kMergeWaves), 0, st, a);
   }
-  else
+  else if (a.ws_seq)   // (no workspace: no unit can be split, every item finished in place)
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
                        st, a);
   return hipGetLastError();

@@ -224,18 +224,19 @@ struct Plan {
   int tpi;         // tiles per item (a unit of n tiles makes ceil(n / tpi) items)
 };
 
-// Tiles of sequence 64*c + lane (0 past the batch).  The first 256 sequences'
-// counts come from registers filled once; later ones are read again.
-struct SeqTiles {
+// Clamped context lengths of sequences 64*c + lane (0 past the batch).  The
+// first 256 sequences' come from registers filled once (the only read of
+// context_lens for batches up to 256); later ones are read again.
+struct SeqCtx {
   int cached[4];
   __device__ __forceinline__ void fill(const DecodeArgs& a, int lane) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = 64 * i + lane;
-      cached[i] = b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+      cached[i] = b < a.batch ? seq_ctx(a, b) : 0;
     }
   }
-  __device__ __forceinline__ int get(const DecodeArgs& a, int c, int lane) const {
+  __device__ __forceinline__ int ctx(const DecodeArgs& a, int c, int lane) const {
     if (c < 4) {   // uniform selects: the array stays in registers
       int v = cached[0];
       v = c == 1 ? cached[1] : v;
@@ -244,14 +245,25 @@ struct SeqTiles {
       return v;
     }
     const int b = 64 * c + lane;
-    return b < a.batch ? (seq_ctx(a, b) + kTileTokens - 1) / kTileTokens : 0;
+    return b < a.batch ? seq_ctx(a, b) : 0;
+  }
+  __device__ __forceinline__ int tiles(const DecodeArgs& a, int c, int lane) const {
+    return (ctx(a, c, lane) + kTileTokens - 1) / kTileTokens;
   }
 };
 
-__device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqTiles& st, int tpi,
+// Chunks (items per unit) of a decode sequence of n tiles: ceil(n / tpi), and
+// one for an empty sequence, whose item writes its zeros (so that a call whose
+// units are never split needs no second kernel).
+__device__ __forceinline__ int seq_chunks(int n, int tpi) {
+  return n > 0 ? (n + tpi - 1) / tpi : 1;
+}
+
+__device__ __forceinline__ int64_t count_items(const DecodeArgs& a, const SeqCtx& st, int tpi,
                                                int lane) {
   int64_t items = 0;
-  for (int c = 0; 64 * c < a.batch; ++c) items += (st.get(a, c, lane) + tpi - 1) / tpi;
+  for (int c = 0; 64 * c < a.batch; ++c)
+    if (64 * c + lane < a.batch) items += seq_chunks(st.tiles(a, c, lane), tpi);
   return uni64(wave_sum_i64(items) * ((int64_t)a.plan_heads * a.head_tiles));
 }
 
@@ -272,12 +284,13 @@ __device__ __forceinline__ int plan_tpi(int64_t tiles, int64_t live, int64_t slo
   return (int)t;
 }
 
-__device__ inline Plan make_plan(const DecodeArgs& a, int lane) {
-  SeqTiles st;
+// The decode plan (every wave computes it the same way); st keeps the
+// contexts it read, for seq_of_item.
+__device__ inline Plan make_plan(const DecodeArgs& a, int lane, SeqCtx& st) {
   st.fill(a, lane);
   int64_t tiles = 0, live = 0;
   for (int c = 0; 64 * c < a.batch; ++c) {
-    const int n = st.get(a, c, lane);
+    const int n = st.tiles(a, c, lane);
     tiles += n;
     live += n > 0;
   }
@@ -292,10 +305,11 @@ __device__ inline Plan make_plan(const DecodeArgs& a, int lane) {
 
 // Items of a sequence are numbered chunk-major, then by KV head, then by head
 // tile: item = first + (c * plan_heads + g) * head_tiles + ht, with
-// m = ceil(n / tpi) chunks of the sequence's n tiles per unit; chunk c covers
-// tiles [c*n/m, (c+1)*n/m).  (g runs over plan_heads KV heads: all of them for
-// decode, one for a multi-token virtual sequence, which carries its own.)
-// Consecutive items thus read the same blocks, one (block, KV head) tile each.
+// m = seq_chunks(n, tpi) chunks of the sequence's n tiles per unit; chunk c
+// covers tiles [c*n/m, (c+1)*n/m).  (g runs over plan_heads KV heads: all of
+// them for decode, one for a multi-token virtual sequence, which carries its
+// own.)  Consecutive items thus read the same blocks, one (block, KV head)
+// tile each.
 struct SeqItems {
   int64_t first;   // number of the sequence's first item
   int ctx;         // clamped context length
@@ -303,16 +317,16 @@ struct SeqItems {
   int m;           // chunks per unit
 };
 
-// The sequence holding item q (found = false if q is past the last item).
-__device__ inline bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q, int lane,
-                            int& b_out, SeqItems& s) {
+// The decode sequence holding item q (false if q is past the last item).
+__device__ inline bool seq_of_item(const DecodeArgs& a, const Plan& p, const SeqCtx& st,
+                                   int64_t q, int lane, int& b_out, SeqItems& s) {
   const int64_t units_per_seq = (int64_t)a.plan_heads * a.head_tiles;
   int64_t base = 0;
   for (int b0 = 0; b0 < a.batch; b0 += kWave) {
     const int b = b0 + lane;
-    const int ctx = b < a.batch ? seq_ctx(a, b) : 0;
+    const int ctx = st.ctx(a, b0 / kWave, lane);
     const int n = (ctx + kTileTokens - 1) / kTileTokens;
-    const int m = (n + p.tpi - 1) / p.tpi;
+    const int m = b < a.batch ? seq_chunks(n, p.tpi) : 0;
     const int64_t cnt = (int64_t)m * units_per_seq;
     const int64_t incl = wave_incl_scan_i64(cnt, lane) + base;
     const uint64_t hit = __builtin_amdgcn_ballot_w64(q >= incl - cnt && q < incl);
@@ -328,6 +342,18 @@ __device__ inline bool seq_of_item(const DecodeArgs& a, const Plan& p, int64_t q
     base = readlane_i64(incl, kWave - 1);
   }
   return false;
+}
+
+// Query rows of real sequence b of a multi-token call: first row q0 and count
+// L.  query_start is a precondition (0, nondecreasing, ending at q_rows); for
+// memory safety only, both ends are clamped into [0, q_rows], so every row
+// q0 .. q0 + L - 1 lies inside q and out.
+__device__ __forceinline__ void query_span(const DecodeArgs& a, int b, int& q0, int& L) {
+  int s = a.query_start[b], e = a.query_start[b + 1];
+  s = s < 0 ? 0 : (s > a.q_rows ? a.q_rows : s);
+  e = e < s ? s : (e > a.q_rows ? a.q_rows : e);
+  q0 = s;
+  L = e - s;
 }
 
 // Multi-token calls: the plan is made once per call by multi_prep_kernel,

@@ -132,8 +132,10 @@ __device__ __forceinline__ void prefill_group(
 
   // ---- this wave's rows: row = query token * G + head of the group ----
   const int G = a.num_q_heads / a.num_kv_heads;
-  const int q0 = uni(a.query_start[bq]);
-  const int L = uni(a.query_start[bq + 1]) - q0;
+  int q0, L;
+  query_span(a, bq, q0, L);
+  q0 = uni(q0);
+  L = uni(L);
   int cr = a.real_ctx[bq];
   cr = uni(cr < 0 ? 0 : (cr > a.ctx_cap ? a.ctx_cap : cr));
   const int row0 = (W * rt + wave) * 16 * RT;

@@ -22,7 +22,7 @@ import torch
 
 import oracle
 import paged_kv_cache_435_amd as pkv
-from paged_kv_cache_435_amd.device_cache import DeviceCase
+from harness.device_cache import DeviceCase
 
 # Parity bar (|gpu - ref| <= atol + rtol * |ref|).  fp16/bf16 KV: 2e-2 abs /
 # 1e-2 rel; INT8/FP8/INT4 KV: 5e-2 abs and rel against the oracle on the same stored

@@ -158,3 +158,25 @@ def test_swap_blocks_checks_pairs_on_the_host(lib):
     assert "row scales" in lib.pkv_last_error().decode()
     assert lib.kv_swap_blocks(None, None, None, None, 4, None, None, None, None, 8, 16, 2, 128,
                               pkv.PKV_F16, None, 0, None) == 0
+
+
+def test_build_keeps_denormals_for_every_float_type(tmp_path):
+    """INT8 / INT4 codes with f16 queries enter the matrix instructions as f16
+    subnormals: the build must keep f16 (and f32) denormals, explicitly, and the
+    flags must have that effect on this toolchain (denormal mode 3 in the
+    kernel descriptor)."""
+    import subprocess
+    from paged_kv_cache_435_amd import build as B
+    assert "-fdenormal-fp-math=ieee" in B.CFLAGS
+    assert "-fno-gpu-flush-denormals-to-zero" in B.CFLAGS
+    assert not any("flush-denormals-to-zero" in f and "no-" not in f for f in B.CFLAGS)
+    src = tmp_path / "k.hip"
+    src.write_text("#include <hip/hip_runtime.h>\n"
+                   "__global__ void k(_Float16* x) { x[0] = x[1] * x[2]; }\n")
+    asm = tmp_path / "k.s"
+    flags = [f for f in B.CFLAGS if not f.startswith("-I")]
+    subprocess.run([B.HIPCC, *flags, "--cuda-device-only", "-S", str(src), "-o", str(asm)],
+                   check=True, capture_output=True)
+    text = asm.read_text()
+    assert ".amdhsa_float_denorm_mode_16_64 3" in text
+    assert ".amdhsa_float_denorm_mode_32 3" in text

@@ -237,3 +237,81 @@ def test_swap_failures_change_nothing():
     h.free(2)                                      # a swapped sequence can end: host blocks back
     assert h.bm.num_free_host == 2
     h.check()
+
+
+# ---- prefix caching under forced key collisions: a key match is only a
+# candidate, a block is shared only when its content (token ids, and the
+# prefix it was sealed after) is the new sequence's ----
+
+def test_colliding_key_with_other_tokens_is_a_miss():
+    h = Harness(nb=16, bs=4, prefix=True)
+    h.bm.debug_hash_mask(0)                       # every lookup key is the same
+    h.add(1, list(range(8)))
+    s = h.add(2, list(range(10, 18)))             # same key, other tokens: shares nothing
+    assert np.all(s >= 0)
+    assert all(h.bm.ref_count(b) <= 1 for b in range(h.nb))
+    h.check()
+
+
+def test_same_tokens_after_another_prefix_are_a_miss():
+    h = Harness(nb=16, bs=2, prefix=True)
+    h.bm.debug_hash_mask(0)
+    h.add(1, [5, 5, 7, 7])                        # block 0 is the cached entry
+    s = h.add(2, [5, 5, 5, 5, 1])                 # block 1 holds [5, 5] after a prefix: own block
+    assert np.all(s[:2] == -1) and np.all(s[2:] >= 0)
+    t, _ = h.bm.block_tables([2], 4)
+    assert len(set(t[0][:3].tolist())) == 3
+    h.check()
+
+
+def test_equal_prefix_still_shares_under_collisions():
+    h = Harness(nb=16, bs=4, prefix=True)
+    h.bm.debug_hash_mask(0)
+    h.add(1, list(range(9)))
+    s = h.add(2, list(range(4)) + [50, 51])       # first block equal: shared
+    assert np.all(s[:4] == -1) and np.all(s[4:] >= 0)
+    h.check()
+
+
+def test_hash_mask_only_before_the_first_sequence():
+    h = Harness(nb=4, bs=4, prefix=True)
+    h.add(1, [1, 2, 3, 4])
+    with pytest.raises(RuntimeError, match="before the first sequence"):
+        h.bm.debug_hash_mask(0)
+
+
+@pytest.mark.parametrize("mask", [0, 2, 6, 0xFF])
+@pytest.mark.parametrize("seed", range(4))
+def test_random_operations_with_colliding_keys(mask, seed):
+    """The random mix of the first test with few distinct lookup keys and a
+    tiny token alphabet (equal blocks at different prefixes are common)."""
+    rng = np.random.default_rng(100 + seed)
+    bs = int(rng.choice([2, 4]))
+    h = Harness(nb=40, bs=bs, prefix=True, host_blocks=24)
+    h.bm.debug_hash_mask(mask)
+    stems = [rng.integers(0, 3, size=4 * bs).tolist() for _ in range(4)]
+    next_id = 0
+    for _ in range(260):
+        op = rng.random()
+        ids = list(h.seqs)
+        try:
+            if op < 0.08 and ids:
+                sid = ids[rng.integers(len(ids))]
+                (h.swap_in if sid in h.swapped else h.swap_out)(sid)
+            elif op < 0.4 or not ids:
+                stem = stems[rng.integers(len(stems))]
+                cut = int(rng.integers(0, len(stem) + 1))
+                tail = rng.integers(0, 3, size=int(rng.integers(0, 3 * bs))).tolist()
+                h.add(next_id, stem[:cut] + tail)
+                next_id += 1
+            elif op < 0.7:
+                sid = ids[rng.integers(len(ids))]
+                h.append(sid, rng.integers(0, 3, size=int(rng.integers(1, bs + 2))).tolist())
+            elif op < 0.8:
+                h.fork(ids[rng.integers(len(ids))], next_id)
+                next_id += 1
+            else:
+                h.free(ids[rng.integers(len(ids))])
+        except RuntimeError as e:
+            assert any(m in str(e) for m in ("out of blocks", "out of host blocks", "swapped out"))
+        h.check()

@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from paged_kv_cache_435_amd import workloads as W
+from harness import workloads as W
 from tests.gpu_util import OracleSide, per_head_rel_l2, run_and_check
 
 pytestmark = pytest.mark.gpu

@@ -7,8 +7,8 @@ import torch
 
 import oracle
 import paged_kv_cache_435_amd as pkv
-from paged_kv_cache_435_amd import workloads as W
-from paged_kv_cache_435_amd.device_cache import DeviceCase
+from harness import workloads as W
+from harness.device_cache import DeviceCase
 from tests.gpu_util import (OracleSide, append_and_decode, compare, per_head_rel_l2,
                             run_and_check, say)
 

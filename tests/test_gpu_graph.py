@@ -8,8 +8,8 @@ import pytest
 import torch
 
 import paged_kv_cache_435_amd as pkv
-from paged_kv_cache_435_amd import workloads as W
-from paged_kv_cache_435_amd.device_cache import DeviceCase
+from harness import workloads as W
+from harness.device_cache import DeviceCase
 from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu

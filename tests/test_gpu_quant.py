@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import paged_kv_cache_435_amd as pkv
-from paged_kv_cache_435_amd import workloads as W
+from harness import workloads as W
 from tests.gpu_util import say
 
 pytestmark = pytest.mark.gpu

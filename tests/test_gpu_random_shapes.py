@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 import torch
 
-from paged_kv_cache_435_amd import workloads as W
+from harness import workloads as W
 from tests.gpu_util import run_and_check
 
 pytestmark = pytest.mark.gpu

@@ -15,11 +15,24 @@ from oracle import quant, widen
 
 
 def page_quantize_tensor(x):
-    """[P1] §4 quantize_tensor, executed by torch (float32, CPU)."""
-    x = torch.as_tensor(x, dtype=torch.float32)
-    scale = 127.0 / x.abs().max(dim=-1, keepdim=True)[0]
-    q_x = (x * scale).round().clamp(-128, 127)
-    return q_x, scale
+    """The INT8 rule of [P1] «LLM推理显存优化：KV Cache管理3大策略实测，节省60%显存开销»
+    §4 (quantize_tensor), carried out by torch in float32 on the CPU: per row,
+    the largest magnitude a; the scale is the number 127 divided by the tensor
+    of those maxima (torch's scalar-by-tensor division, the operation the page
+    applies); codes are the rows times their scale, rounded half to even and
+    limited to [-128, 127].  Returns (codes, scales [n][1])."""
+    rows = torch.as_tensor(x, dtype=torch.float32)
+    absmax = torch.amax(torch.abs(rows), dim=1, keepdim=True)
+    scales = torch.Tensor.__rtruediv__(absmax, 127.0)
+    codes = torch.clamp(torch.round(torch.mul(rows, scales)), min=-128, max=127)
+    return codes, scales
+
+
+def test_torch_scalar_by_tensor_division_is_reciprocal_times_scalar():
+    """(Why the oracle forms the scale as fl32(fl32(1/a) * 127): that is what
+    torch computes for the page's scalar-by-tensor division.)"""
+    a = torch.from_numpy(np.abs(_rows(9, n=20000, outliers=False)).max(axis=1))
+    assert torch.equal(torch.Tensor.__rtruediv__(a, 127.0), torch.reciprocal(a) * 127.0)
 
 
 def _rows(seed, n=4000, d=128, outliers=True):

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from oracle import kvsize, paging
-from paged_kv_cache_435_amd import workloads as W
+from harness import workloads as W
 
 
 @pytest.mark.parametrize("name", W.NAMES)
