@@ -55,6 +55,22 @@ def test_zero_length_sequence_gives_zeros():
     compare(got, ref, "f16", "zero-len")
 
 
+def test_zero_length_sequence_without_workspace():
+    """Contexts of at most 128 tokens need no workspace and no merge kernel:
+    the partition kernel itself writes an empty sequence's zeros."""
+    w = W.custom(torch.float16, "f16", [100, 1, 37, 128], 8, 2, 128, 16, name="zero-len-short")
+    assert pkv.paged_attention_workspace_size(w.batch, 8, 2, 128, w.max_context_len) == 0
+    case = DeviceCase(w, keep_sources=True)
+    case.out.fill_(float("nan"))
+    case.context_lens[1] = 0
+    got = append_and_decode(case)
+    assert np.all(got[1] == 0)
+    ctx = w.context_lens.copy()
+    ctx[1] = 0
+    ref = OracleSide(w, case, context_lens=ctx).attention()
+    compare(got, ref, "f16", "zero-len-short")
+
+
 def test_single_token_is_its_value_row_exactly():
     for q_dtype, fmt in [(torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32")]:
         w = W.custom(q_dtype, fmt, [1, 1, 1], 8, 2, 128, 16, name="ctx1")
