@@ -204,6 +204,31 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attention_decode_noalloc — paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, hosts that forbid allocation): the same arguments without a
+ * workspace, the same kernels and the same result bit for bit.  The partial
+ * rows of split contexts go to a static scratch array of
+ * PKV_NOALLOC_SCRATCH_BYTES in the library, one per device, held from the first
+ * call on that device until the process ends; nothing is allocated or freed.
+ * The scratch needs no clearing (every byte read was written by the same call).
+ * Calls on one device share the scratch: calls that may overlap there (other
+ * streams, other threads) must be ordered by the caller, or they race.
+ * Errors: as paged_attention_decode, and PKV_ERR_WORKSPACE when these sizes
+ * need more scratch than PKV_NOALLOC_SCRATCH_BYTES (the message gives both).
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+pkv_status paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
+                                          int32_t batch, int32_t num_q_heads, const void* k_cache,
+                                          const void* v_cache, const float* k_scale,
+                                          const float* v_scale, int32_t num_blocks,
+                                          int32_t block_size, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t kv_dtype,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t max_context_len,
+                                          float scale, void* stream);
+
+/*
  * paged_attention_multi_workspace_size — bytes of device scratch
  * paged_attention_multi_query needs for these sizes (never 0 for valid sizes:
  * the call keeps its work plan there — virtual sequences, an item map — and,

@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "kv_quantize", "kv_cache_append", "paged_attention_decode", "paged_attention_multi_query",
     "kv_copy_blocks", "kv_swap_blocks", "BlockManager", "paged_attention_workspace_size",
+    "paged_attention_decode_noalloc",
     "paged_attention_multi_workspace_size", "kv_cache_bytes", "library_path", "load_library",
     "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_I8", "PKV_FP8_E4M3FN", "PKV_I4", "EXPORTED_SYMBOLS",
 ]
@@ -30,7 +31,7 @@ EXPORTED_SYMBOLS = (
     "pkv_bm_last_error", "pkv_bm_create", "pkv_bm_destroy", "pkv_bm_num_free",
     "pkv_bm_ref_count", "pkv_bm_add_sequence", "pkv_bm_append", "pkv_bm_fork", "pkv_bm_free",
     "pkv_bm_block_tables", "pkv_bm_enable_swap", "pkv_bm_num_free_host", "pkv_bm_swap_out",
-    "pkv_bm_swap_in", "kv_swap_blocks", "pkv_bm_debug_hash_mask",
+    "pkv_bm_swap_in", "kv_swap_blocks", "pkv_bm_debug_hash_mask", "paged_attention_decode_noalloc",
 )
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,6 +72,9 @@ def load_library(path=None):
     lib.paged_attention_decode.restype = I32
     lib.paged_attention_decode.argtypes = [P, P, I32, I32, I32, P, P, P, P, I32, I32, I32, I32,
                                            I32, P, I32, P, I32, F, P, SZ, P]
+    lib.paged_attention_decode_noalloc.restype = I32
+    lib.paged_attention_decode_noalloc.argtypes = [P, P, I32, I32, I32, P, P, P, P, I32, I32, I32,
+                                                   I32, I32, P, I32, P, I32, F, P]
     lib.paged_attention_multi_workspace_size.restype = SZ
     lib.paged_attention_multi_workspace_size.argtypes = [I32] * 6
     lib.paged_attention_multi_query.restype = I32
@@ -276,6 +280,40 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
         _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, kc,
         _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
         float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, lib)
+    return out
+
+
+def paged_attention_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale,
+                                   max_context_len, k_scale=None, v_scale=None, kv_dtype=None,
+                                   stream=None):
+    """paged_attention_decode without a workspace: the library's static
+    per-device scratch holds the partial rows (nothing is allocated, here or in
+    the library).  Calls that may overlap on one device must be ordered."""
+    lib = load_library()
+    for t, n in ((out, "out"), (q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                 (block_tables, "block_tables"), (context_lens, "context_lens"),
+                 (k_scale, "k_scale"), (v_scale, "v_scale")):
+        _dev(t, n)
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    B, Hq, d = q.shape
+    NB, Hkv, bs, dk = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must have k_cache's shape and dtype")
+    kc = _kv_code(k_cache, kv_dtype, "k_cache")
+    if kc == PKV_I4:
+        dk *= 2
+    if tuple(out.shape) != (B, Hq, d) or out.dtype != q.dtype or dk != d:
+        raise ValueError("out must match q, and the cache's head_dim must match q's")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B][MB] and context_lens [B]")
+    _need_scales(k_scale, v_scale, kc, NB * Hkv * bs, "paged_attention_decode_noalloc")
+    st = lib.paged_attention_decode_noalloc(
+        _ptr(out), _ptr(q), _dtype_code(q, "q"), B, Hq, _ptr(k_cache), _ptr(v_cache),
+        _ptr(k_scale), _ptr(v_scale), NB, bs, Hkv, d, kc,
+        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), int(max_context_len),
+        float(scale), _stream(stream))
     _check(st, lib)
     return out
 

@@ -144,6 +144,145 @@ int64_t multi_workspace_of(int64_t batch, int64_t num_query_tokens, int64_t grou
                          map_entries(v, sh.waves, max_context_len));
 }
 
+// Scratch of paged_attention_decode_noalloc (partial softmax rows of split
+// contexts), for callers that cannot allocate.  Each device the library runs
+// on holds its own copy for the life of the process; its address is taken once
+// per device with hipGetSymbolAddress (host code never uses the symbol itself,
+// which on the host side is not a device address).  Calls on one device share
+// it: calls that overlap there race, like calls that share a workspace.
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+pkv_status scratch_of_device(const char* fn, void** out) {
+  static std::mutex mu;
+  static std::map<int, void*> ptrs;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, fn);
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = ptrs.find(dev);
+  if (it != ptrs.end()) {
+    *out = it->second;
+    return PKV_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));   // (device dev is current)
+  if (e != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return fail(PKV_ERR_HIP, std::string(fn) + ": cannot take the scratch's device address: " +
+                                 hipGetErrorString(e));
+  }
+  ptrs[dev] = ptr;
+  *out = ptr;
+  return PKV_OK;
+}
+
+// Checks, workspace layout and launch of one decode step; static_scratch: the
+// workspace is the library's static scratch (sized for the launched instance).
+pkv_status decode_impl(const char* fn, void* out, const void* q, int32_t q_dtype, int32_t batch,
+                       int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, int32_t num_blocks,
+                                  int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t kv_dtype, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                  int32_t max_context_len, float scale, void* workspace,
+                                  size_t workspace_bytes, bool static_scratch, void* stream) {
+  if (!is_float_dtype(q_dtype))
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": q_dtype must be F32, F16 or BF16");
+  if (kv_dtype != q_dtype && kv_dtype != PKV_I8 && kv_dtype != PKV_FP8_E4M3FN &&
+      kv_dtype != PKV_I4)
+    return fail(PKV_ERR_UNSUPPORTED,
+                std::string(fn) + ": kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
+  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
+    return fail(PKV_ERR_UNSUPPORTED,
+                std::string(fn) + ": INT4 caches need head_dim 128 and F16 or BF16 queries");
+  if (block_size != 16 && block_size != 256)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": block_size must be 16 or 256");
+  if (batch < 0 || batch > 65535 || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0)
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": need 0 <= batch <= 65535 and num_q_heads a multiple of "
+                "num_kv_heads");
+  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": bad pool or table sizes");
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": max_context_len exceeds max_blocks_per_seq * block_size");
+  if (!(scale == scale) || __builtin_isinf(scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": scale must be finite");
+  if (batch == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": NULL pointer");
+  if ((pkv::row_scaled(kv_dtype) || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": quantized cache needs k_scale and v_scale");
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      (pkv::row_scaled(kv_dtype) && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
+    return fail(PKV_ERR_INVALID_ARG,
+                std::string(fn) + ": misaligned pointer (q, out, caches and row scales need 16 B)");
+
+  const int32_t G = num_q_heads / num_kv_heads;
+  const int32_t head_tiles = (G + 15) / 16;
+  int64_t items = workspace_items(batch, num_q_heads, num_kv_heads, max_context_len);
+  if (items > 0x7FFFFFF0)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": batch x heads x context too large");
+  pkv::DecodeArgs a{};
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_tiles = head_tiles;
+  a.plan_heads = num_kv_heads;
+  a.ctx_cap = max_context_len;
+  if (static_scratch && items > 0) {
+    // The library's own scratch: sized by the launched instance's own slots
+    // and item limit (tighter than the dtype-blind workspace size).
+    const int cus = device_cus();
+    if (cus <= 0) return fail(PKV_ERR_HIP, std::string(fn) + ": cannot query the device");
+    const hipError_t e = pkv::decode_items_needed(a, q_dtype, kv_dtype, head_dim, block_size, cus,
+                                                  &items);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  const size_t need = items > 0 ? (size_t)(seq_bytes(batch) + items * row_bytes(head_dim)) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE,
+                std::string(fn) + (static_scratch ? ": these sizes need " : ": workspace needs ") +
+                    std::to_string(need) + " bytes of scratch, " +
+                    (static_scratch ? "more than the library's static scratch of "
+                                    : "got ") +
+                    std::to_string(workspace_bytes));
+  if (need > 0 && !aligned(workspace, 256))
+    return fail(PKV_ERR_INVALID_ARG, std::string(fn) + ": workspace must be 256-byte aligned");
+
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_items = (int32_t)items;
+  a.scale = scale;
+  const int cus = device_cus();
+  if (cus <= 0) return fail(PKV_ERR_HIP, std::string(fn) + ": cannot query the device");
+  if (need > 0) {
+    uint8_t* w = static_cast<uint8_t*>(workspace);
+    a.ws_seq = reinterpret_cast<int64_t*>(w);
+    a.ws_ml = reinterpret_cast<float*>(w + seq_bytes(batch));
+    a.ws_acc = reinterpret_cast<float*>(w + seq_bytes(batch) + items * 16 * 2 * 4);
+  }
+  return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, cus,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,85 +395,29 @@ pkv_status paged_attention_decode(void* out, const void* q, int32_t q_dtype, int
                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
                                   int32_t max_context_len, float scale, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  if (!is_float_dtype(q_dtype))
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: q_dtype must be F32, F16 or BF16");
-  if (kv_dtype != q_dtype && kv_dtype != PKV_I8 && kv_dtype != PKV_FP8_E4M3FN &&
-      kv_dtype != PKV_I4)
-    return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_decode: kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
-  if (head_dim != 64 && head_dim != 128)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: head_dim must be 64 or 128");
-  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
-    return fail(PKV_ERR_UNSUPPORTED,
-                "paged_attention_decode: INT4 caches need head_dim 128 and F16 or BF16 queries");
-  if (block_size != 16 && block_size != 256)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: block_size must be 16 or 256");
-  if (batch < 0 || batch > 65535 || num_q_heads < 1 || num_kv_heads < 1 ||
-      num_q_heads % num_kv_heads != 0)
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: need 0 <= batch <= 65535 and num_q_heads a multiple of "
-                "num_kv_heads");
-  if (num_blocks < 1 || max_blocks_per_seq < 1 || max_context_len < 0)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: bad pool or table sizes");
-  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: max_context_len exceeds max_blocks_per_seq * block_size");
-  if (!(scale == scale) || __builtin_isinf(scale))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: scale must be finite");
-  if (batch == 0) return ok();
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: NULL pointer");
-  if ((pkv::row_scaled(kv_dtype) || kv_dtype == PKV_FP8_E4M3FN) && (!k_scale || !v_scale))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: quantized cache needs k_scale and v_scale");
-  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
-      (pkv::row_scaled(kv_dtype) && (!aligned(k_scale, 16) || !aligned(v_scale, 16))))
-    return fail(PKV_ERR_INVALID_ARG,
-                "paged_attention_decode: misaligned pointer (q, out, caches and row scales need 16 B)");
+  return decode_impl("paged_attention_decode", out, q, q_dtype, batch, num_q_heads, k_cache,
+                     v_cache, k_scale, v_scale, num_blocks, block_size, num_kv_heads, head_dim,
+                     kv_dtype, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                     scale, workspace, workspace_bytes, false, stream);
+}
 
-  const int32_t G = num_q_heads / num_kv_heads;
-  const int32_t head_tiles = (G + 15) / 16;
-  const int64_t items = workspace_items(batch, num_q_heads, num_kv_heads, max_context_len);
-  if (items > 0x7FFFFFF0)
-    return fail(PKV_ERR_UNSUPPORTED, "paged_attention_decode: batch x heads x context too large");
-  const size_t need = items > 0 ? (size_t)(seq_bytes(batch) + items * row_bytes(head_dim)) : 0;
-  if (need > 0 && (!workspace || workspace_bytes < need))
-    return fail(PKV_ERR_WORKSPACE, "paged_attention_decode: workspace needs " +
-                                       std::to_string(need) + " bytes, got " +
-                                       std::to_string(workspace_bytes));
-  if (need > 0 && !aligned(workspace, 256))
-    return fail(PKV_ERR_INVALID_ARG, "paged_attention_decode: workspace must be 256-byte aligned");
-
-  pkv::DecodeArgs a{};
-  a.out = out;
-  a.q = q;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.k_scale = k_scale;
-  a.v_scale = v_scale;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.head_tiles = head_tiles;
-  a.plan_heads = num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  a.ctx_cap = max_context_len;
-  a.max_items = (int32_t)items;
-  a.scale = scale;
-  const int cus = device_cus();
-  if (cus <= 0) return fail(PKV_ERR_HIP, "paged_attention_decode: cannot query the device");
-  if (need > 0) {
-    uint8_t* w = static_cast<uint8_t*>(workspace);
-    a.ws_seq = reinterpret_cast<int64_t*>(w);
-    a.ws_ml = reinterpret_cast<float*>(w + seq_bytes(batch));
-    a.ws_acc = reinterpret_cast<float*>(w + seq_bytes(batch) + items * 16 * 2 * 4);
-  }
-  return hip_status(pkv::launch_decode(a, q_dtype, kv_dtype, head_dim, block_size, cus,
-                                       static_cast<hipStream_t>(stream)),
-                    "paged_attention_decode");
+pkv_status paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
+                                          int32_t batch, int32_t num_q_heads, const void* k_cache,
+                                          const void* v_cache, const float* k_scale,
+                                          const float* v_scale, int32_t num_blocks,
+                                          int32_t block_size, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t kv_dtype,
+                                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                          const int32_t* context_lens, int32_t max_context_len,
+                                          float scale, void* stream) {
+  const char* fn = "paged_attention_decode_noalloc";
+  void* ptr = nullptr;
+  const pkv_status st = scratch_of_device(fn, &ptr);
+  if (st != PKV_OK) return st;
+  return decode_impl(fn, out, q, q_dtype, batch, num_q_heads, k_cache, v_cache, k_scale, v_scale,
+                     num_blocks, block_size, num_kv_heads, head_dim, kv_dtype, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, scale, ptr,
+                     PKV_NOALLOC_SCRATCH_BYTES, true, stream);
 }
 
 size_t paged_attention_multi_workspace_size(int32_t batch, int32_t num_query_tokens,

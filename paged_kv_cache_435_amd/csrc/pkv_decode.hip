@@ -1195,10 +1195,12 @@ static int slots_per_cu_override() {
   return v;
 }
 
-// Extra arguments of a multi-query call.
+// Extra arguments of a multi-query call; bound_only: compute the items bound
+// of the instance into *bound_only and launch nothing.
 struct MultiLaunch {
   int batch_real;
   int32_t* vctx;
+  int64_t* bound_only = nullptr;
 };
 
 template <int KV, int QT, int D, int BS, bool MULTI>
@@ -1225,6 +1227,10 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   a.slots = num_cus * per_cu;
   if (a.slots > kMaxSlots) a.slots = kMaxSlots;
   const int64_t units = (int64_t)a.plan_heads * a.head_tiles;
+  if (ml.bound_only) {   // this instance's own limit and slots
+    *ml.bound_only = max_items_bound(a.batch, units, a.ctx_cap, a.slots, a.item_cap);
+    return hipSuccess;
+  }
   // The workspace was sized for kMaxSlots; fewer slots never need more items.
   // Every item has at least kItemTilesMin tiles, so a unit makes at most
   // ceil(tiles / kItemTilesMin) items: small batches launch few workgroups.
@@ -1300,6 +1306,12 @@ hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
                          int num_cus, hipStream_t st) {
   return launch0<false>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus, MultiLaunch{0, nullptr},
                         st);
+}
+
+hipError_t decode_items_needed(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                               int block_size, int num_cus, int64_t* items) {
+  return launch0<false>(a, q_dtype, kv_dtype, head_dim, block_size, num_cus,
+                        MultiLaunch{0, nullptr, items}, nullptr);
 }
 
 template <int QT, int D>

@@ -111,14 +111,20 @@ struct DecodeArgs {
 // Hence at most N / L + S + U; the smaller limit (the prompt-chunk kernel's)
 // bounds the plans of every kernel.
 inline int64_t max_items_bound(int64_t batch, int64_t units_per_seq, int64_t max_context_len,
-                               int64_t slots) {
+                               int64_t slots, int64_t item_cap = kPrefillItemTilesMax) {
   const int64_t units = batch * units_per_seq;
   const int64_t tiles = units * ((max_context_len + kTileTokens - 1) / kTileTokens);
-  return (tiles + kPrefillItemTilesMax - 1) / kPrefillItemTilesMax + slots + units;
+  return (tiles + item_cap - 1) / item_cap + slots + units;
 }
 
 hipError_t launch_decode(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim, int block_size,
                          int num_cus, hipStream_t st);
+
+// The most items the decode instance for these types and sizes can plan on
+// this device (its own slots and item limit; no launch): a tighter bound than
+// the dtype-blind one the workspace size uses.
+hipError_t decode_items_needed(DecodeArgs& a, int q_dtype, int kv_dtype, int head_dim,
+                               int block_size, int num_cus, int64_t* items);
 
 // Multi-query: a.batch = virtual sequences (upper bound), a.context_lens =
 // vctx (written by the prep kernel first), batch_real real sequences.
