@@ -46,9 +46,12 @@ def library_path():
 
 def load_library(path=None):
     """Load libpagedkv.so (once): the in-tree build, or ``path`` (another build
-    of the same sources, e.g. with other compile-time tuning).  Raises if it
-    has not been built, or if a different file is already loaded."""
+    of the same sources, e.g. with other compile-time tuning).  Without a path,
+    the library already loaded is returned.  Raises if it has not been built,
+    or if ``path`` names another file than the one loaded."""
     global _LIB, _LIB_PATH
+    if path is None and _LIB is not None:
+        return _LIB
     path = os.path.abspath(path) if path else library_path()
     if _LIB is not None:
         if path != _LIB_PATH:
