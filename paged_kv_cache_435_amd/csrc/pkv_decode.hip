@@ -54,6 +54,7 @@
 
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_NT_LOADS            KV loads carry the non-temporal hint
+//   PKV_NT_SCALE_LOADS      row-scale loads (INT8, INT4) carry it too
 //   PKV_WAVES_PER_EU        occupancy target, KV other than INT8
 //   PKV_STAGES_2B           pipeline depth (tiles in flight), 16-bit and f32 KV
 //   PKV_STAGES_I8           pipeline depth (tiles in flight), INT8 KV
@@ -65,8 +66,14 @@
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
 //   PKV_SLOTS_PER_CU_I4       the same for INT4 KV
+//   PKV_TILES_PER_UPDATE_I4   16-token tiles per online-softmax step, INT4 KV
+//   PKV_TILES_PER_UPDATE_I8   the same for INT8 KV
+//   PKV_TILES_PER_UPDATE_FP8  the same for FP8 KV
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
+#endif
+#ifndef PKV_NT_SCALE_LOADS
+#define PKV_NT_SCALE_LOADS 1
 #endif
 #ifndef PKV_WAVES_PER_EU
 #define PKV_WAVES_PER_EU 3
@@ -107,6 +114,15 @@
 #ifndef PKV_ITEM_TILES_I4
 #define PKV_ITEM_TILES_I4 256
 #endif
+#ifndef PKV_TILES_PER_UPDATE_I4
+#define PKV_TILES_PER_UPDATE_I4 1
+#endif
+#ifndef PKV_TILES_PER_UPDATE_I8
+#define PKV_TILES_PER_UPDATE_I8 1
+#endif
+#ifndef PKV_TILES_PER_UPDATE_FP8
+#define PKV_TILES_PER_UPDATE_FP8 1
+#endif
 
 namespace pkv {
 
@@ -119,16 +135,37 @@ namespace pkv {
 // load).  The waves of a workgroup are independent and need no LDS.
 // ---------------------------------------------------------------------------
 // Lane L of each 16-lane row, broadcast to the whole row (DPP row_newbcast).
+// Every lane is written, so the destination's old value is not needed (no
+// initialising move).
 template <int L>
 __device__ __forceinline__ float row_bcast(float v) {
-  return bitsf((uint32_t)__builtin_amdgcn_update_dpp(0, (int)fbits(v), 0x150 + L, 0xF, 0xF, false));
+  return bitsf((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(v), 0x150 + L, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
+// (global-memory pointers: the bases come through readfirstlane, which hides
+// their address space from the compiler)
+// The base is cast first and the lane's offset added to the global pointer,
+// so the load takes the scalar base and a 32-bit vector offset.  (The empty
+// asm makes the offset a value of the load's own block: instruction selection
+// then sees that it is a zero-extended 32-bit one, rather than a 64-bit copy
+// made once before the loop.)
+__device__ __forceinline__ u32x4 ld16(const uint8_t* base, uint32_t off) {
+  asm("" : "+v"(off));
+  const __attribute__((address_space(1))) uint8_t* g = (const __attribute__((address_space(1))) uint8_t*)base;
+  const __attribute__((address_space(1))) u32x4* p = (const __attribute__((address_space(1))) u32x4*)(g + off);
 #if PKV_NT_LOADS
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load(p);
 #else
-  return *reinterpret_cast<const u32x4*>(p);
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ float ld_f32(const float* base, int idx) {
+  const __attribute__((address_space(1))) float* p = (const __attribute__((address_space(1))) float*)base + idx;
+#if PKV_NT_SCALE_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
 #endif
 }
 
@@ -162,6 +199,12 @@ struct Tuning {
   // smallest limit of any kernel, kPrefillItemTilesMax: no decode instance may
   // plan shorter items than that.
   static_assert(item_tiles >= kPrefillItemTilesMax, "max_items_bound assumes this limit");
+  // Tiles per online-softmax step (their loads are issued together; INT4's PV
+  // products then run 32 tokens deep).
+  static constexpr int tiles_per_update =
+      KV == PKV_I4 ? PKV_TILES_PER_UPDATE_I4
+                   : (KV == PKV_I8 ? PKV_TILES_PER_UPDATE_I8
+                                   : (KV == PKV_FP8_E4M3FN ? PKV_TILES_PER_UPDATE_FP8 : 1));
 };
 
 // Waves per workgroup: decode takes kDecodeWaves consecutive items (the KV
@@ -197,6 +240,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // multi-token calls, whose query tokens x heads of a KV head run to dozens of
   // rows (each loaded K/V tile then serves twice the rows).
   constexpr int RT = MULTI ? kMultiRowTiles : 1;
+  constexpr int NT = MULTI ? 1 : Tuning<KV>::tiles_per_update;   // tiles per softmax step
 
   const int lane = threadIdx.x & (kWave - 1);
   const int r16 = lane & 15;   // MFMA row/column index of this lane
@@ -385,11 +429,21 @@ void decode_partition_kernel(DecodeArgs a) {
   // Constant factors: logits are taken in the exp2 domain.
   float kfac = a.scale * 1.4426950408889634f;
   float vfac = 1.0f;
-  // offset codes: z = (s * 2^24 - o qsum) * kfac * (1 / row scale)
-  const float kf24 = kfac * 16777216.0f;
-  float kbias[RT];
+  // Offset codes: z = (s - o qsum 2^-24) * (kfac 2^24 / row scale), the first
+  // term by starting the QK accumulation at -o qsum 2^-24, the second one
+  // factor per token (row-scaled caches: kfac enters the reciprocal once).
+  f32x4 s_init[RT];
 #pragma unroll
-  for (int k = 0; k < RT; ++k) kbias[k] = -code_offset * qsum[k] * kfac;
+  for (int k = 0; k < RT; ++k) {
+    const float b0 = offset_codes ? -code_offset * qsum[k] * 5.9604644775390625e-8f : 0.f;
+    s_init[k] = f32x4{b0, b0, b0, b0};
+  }
+  const float kf_row = offset_codes ? kfac * 16777216.0f : kfac;   // times 1 / row scale
+  // Lazy-rescaling slack (log2 units): P <= 2^kSlack.  Row-scaled caches feed
+  // P / s to the 16-bit PV operand (1/s = amax/127 for INT8, amax/7 for INT4),
+  // so their slack is smaller: with it, P / s stays finite in f16 for every row
+  // whose values are finite in f16 (amax <= 65504; INT4: 4 * 65504 / 7).
+  constexpr float kSlack = KV == PKV_I4 ? 2.0f : (row_scaled(KV) ? 4.0f : 8.0f);
   if constexpr (KV == PKV_FP8_E4M3FN) {
     kfac *= a.k_scale[0] * cvt_gain<KV, MT>();
     vfac = a.v_scale[0] * cvt_gain<KV, MT>();
@@ -445,296 +499,397 @@ void decode_partition_kernel(DecodeArgs a) {
     // Uniform: keep it scalar.  (uni64 moves the two halves as unsigned words;
     // readfirstlane returns a signed int, and widening the low half directly
     // would copy its bit 31 into the high word, past 2^31 bytes into a pool.)
+    // The tile bases pass through readfirstlane, so each load takes them as
+    // its scalar base with the lane's 32-bit offset (no 64-bit vector add).
     const uint64_t tb = (uint64_t)uni64((int64_t)row0 * R);
-    const uint8_t* ktile = kbase + tb;
-    const uint8_t* vtile = vbase + tb;
+    const uint8_t* ktile = sptr(kbase + tb);
+    const uint8_t* vtile = sptr(vbase + tb);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile + loff + 1024 * j);
+    for (int j = 0; j < NL; ++j) kr[j] = ld16(ktile, loff + 1024 * j);
 #pragma unroll
-    for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile + loff + 1024 * j);
+    for (int j = 0; j < NL; ++j) vr[j] = ld16(vtile, loff + 1024 * j);
     if constexpr (row_scaled(KV)) {
       const uint64_t sb = (uint64_t)uni64(row0);
-      ks = (a.k_scale + sb)[scale_tok];
-      vs = (a.v_scale + sb)[scale_tok];
+      ks = ld_f32(sptr(a.k_scale + sb), scale_tok);
+      vs = ld_f32(sptr(a.v_scale + sb), scale_tok);
     }
     __builtin_amdgcn_sched_barrier(0);   // keep the loads ahead of the compute they overlap
   };
 
-  // Softmax update and both contractions for one loaded tile.
-  // `checked` (a std::bool_constant): the tile may be partial or outside the
-  // pool, so tokens are masked one by one; otherwise all 16 are live.
-  auto compute = [&](auto checked_c, int tile, const u32x4* kraw, const u32x4* vraw, float ks1,
-                     float vs1, int phys) {
+  // Softmax update and both contractions for NT loaded tiles: one online-
+  // softmax step over their 16 NT tokens (the running max, its cross-lane
+  // reduction and the rescale decision are taken once per NT tiles).
+  // `checked` (a std::bool_constant): a tile may be partial, outside the pool
+  // or past the item, so tokens are masked one by one; otherwise all are live.
+  auto compute = [&](auto checked_c, int tile, const u32x4 (*kraw)[NL], const u32x4 (*vraw)[NL],
+                     const float* ks1, const float* vs1, const int* phys) {
     constexpr bool checked = decltype(checked_c)::value;
     // INT8 / INT4: 1/s of this lane's scale (v_rcp_f32, ~1 ulp), then each lane
     // takes its four tokens' values from its row's first four lanes (DPP row
     // broadcast of lane i of each 16-lane row).
-    f32x4 krcp = {1.f, 1.f, 1.f, 1.f}, vrcp = krcp;
-    if constexpr (row_scaled(KV)) {
-      const float kr1 = __builtin_amdgcn_rcpf(ks1);
-      const float vr1 = __builtin_amdgcn_rcpf(vs1);
-      krcp[0] = row_bcast<0>(kr1);
-      krcp[1] = row_bcast<1>(kr1);
-      krcp[2] = row_bcast<2>(kr1);
-      krcp[3] = row_bcast<3>(kr1);
-      vrcp[0] = row_bcast<0>(vr1);
-      vrcp[1] = row_bcast<1>(vr1);
-      vrcp[2] = row_bcast<2>(vr1);
-      vrcp[3] = row_bcast<3>(vr1);
-    }
-    int n_valid = 16;
-    if constexpr (checked) {
-      n_valid = t_end - (t_begin + tile * 16);
-      n_valid = n_valid > 16 ? 16 : n_valid;
-      if (phys < 0) n_valid = 0;
+    auto bcast4 = [&](float x) {
+      return f32x4{row_bcast<0>(x), row_bcast<1>(x), row_bcast<2>(x), row_bcast<3>(x)};
+    };
+    // Live tokens of each tile (<= 0: a tile outside the pool or past the item).
+    int n_valid[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      n_valid[t] = 16;
+      if constexpr (checked) {
+        const int n = t_end - (t_begin + (tile + t) * 16);
+        n_valid[t] = phys[t] < 0 ? 0 : (n > 16 ? 16 : n);
+      }
     }
 
     // Tokens 4*c16 + i of this lane past the context get zero V (masks on the
     // converted operands; all ones for a full tile).
-    const int vcnt = n_valid - 4 * c16;
-    uint32_t vmask[4];
+    uint32_t vmask[NT][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vmask[i] = i < vcnt ? 0xFFFFFFFFu : 0u;
+    for (int t = 0; t < NT; ++t) {
+      const int vcnt = n_valid[t] - 4 * c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vmask[t][i] = i < vcnt ? 0xFFFFFFFFu : 0u;
+    }
 
     // S^T = K Q^T
-    uint32_t kop[KW];
+    f32x4 s[NT][RT];
 #pragma unroll
-    for (int j = 0; j < NL; ++j) C::run(kraw[j], kop + j * WPC);
-    f32x4 s[RT];
+    for (int t = 0; t < NT; ++t) {
+      uint32_t kop[KW];
 #pragma unroll
-    for (int k = 0; k < RT; ++k) {
-      s[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (MT == MT_F16) {
+      for (int j = 0; j < NL; ++j) C::run(kraw[t][j], kop + j * WPC);
 #pragma unroll
-        for (int c = 0; c < KW / 4; ++c) {
-          const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
-          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
-          s[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka),
-                                                        __builtin_bit_cast(f16x8, qb), s[k], 0, 0, 0);
+      for (int k = 0; k < RT; ++k) {
+        s[t][k] = s_init[k];
+        if constexpr (MT == MT_F16) {
+#pragma unroll
+          for (int c = 0; c < KW / 4; ++c) {
+            const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+            const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
+            s[t][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ka),
+                                                             __builtin_bit_cast(f16x8, qb), s[t][k], 0, 0, 0);
+          }
+        } else if constexpr (MT == MT_BF16) {
+#pragma unroll
+          for (int c = 0; c < KW / 4; ++c) {
+            const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
+            const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
+            s[t][k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
+                                                              __builtin_bit_cast(bf16x8, qb), s[t][k], 0, 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < KW; ++c)
+            s[t][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[k][c]), s[t][k], 0, 0, 0);
         }
-      } else if constexpr (MT == MT_BF16) {
+      }
+      // (several tiles: one tile's converted K at a time)
+      if constexpr (NT > 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    f32x4 krcp[NT], vrcp[NT];
 #pragma unroll
-        for (int c = 0; c < KW / 4; ++c) {
-          const u32x4 ka = {kop[4 * c], kop[4 * c + 1], kop[4 * c + 2], kop[4 * c + 3]};
-          const u32x4 qb = {qop[k][4 * c], qop[k][4 * c + 1], qop[k][4 * c + 2], qop[k][4 * c + 3]};
-          s[k] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ka),
-                                                         __builtin_bit_cast(bf16x8, qb), s[k], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < KW; ++c)
-          s[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(kop[c]), bitsf(qop[k][c]), s[k], 0, 0, 0);
+    for (int t = 0; t < NT; ++t) {
+      krcp[t] = vrcp[t] = f32x4{1.f, 1.f, 1.f, 1.f};
+      if constexpr (row_scaled(KV)) {
+        krcp[t] = bcast4(__builtin_amdgcn_rcpf(ks1[t]) * kf_row);
+        vrcp[t] = bcast4(__builtin_amdgcn_rcpf(vs1[t]));
       }
     }
 
     // Online softmax (lane: tokens 4*c16 + i of row r16 of each row tile).
-    float p[RT][4];
-    float alpha[RT];
+    float p[RT][NT][4];
+    float m_new[RT], p_sum[RT];
+    bool up[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      float z[4];
+      float z[NT][4];
       float mx = -__builtin_inff();
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (offset_codes) {
-          z[i] = __builtin_fmaf(s[k][i], kf24, kbias[k]) * krcp[i];
-        } else {
-          float f = kfac;
-          if constexpr (row_scaled(KV)) f = kfac * krcp[i];
-          z[i] = s[k][i] * f;
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (row_scaled(KV))
+            z[t][i] = s[t][k][i] * krcp[t][i];   // (kfac, and 2^24 for offset codes, inside)
+          else
+            z[t][i] = s[t][k][i] * kfac;
+          if constexpr (checked) {
+            const bool ok =
+                4 * c16 + i < n_valid[t] && t_begin + (tile + t) * 16 + 4 * c16 + i <= prow[k];
+            z[t][i] = ok ? z[t][i] : -__builtin_inff();
+          }
+          mx = fmax_ieee(mx, z[t][i]);
         }
-        if constexpr (checked) {
-          const bool ok = 4 * c16 + i < n_valid && t_begin + tile * 16 + 4 * c16 + i <= prow[k];
-          z[i] = ok ? z[i] : -__builtin_inff();
-        }
-        mx = fmax_ieee(mx, z[i]);
       }
       mx = rows_max(mx);
-      const float m_new = fmax_ieee(m_run[k], mx);
-      // A live tile has a finite max, so exp2(-inf) = 0 covers the first one.
-      const bool live = !checked || m_new != -__builtin_inff();
-      // v_exp_f32 directly: arguments are <= 0 and results below 2^-126 may
-      // flush to zero, which only drops weights under 1e-38 of the largest.
-      alpha[k] = live ? __builtin_amdgcn_exp2f(m_run[k] - m_new) : 1.0f;
+      // Lazy rescaling: the reference max m_run moves only when a tile's max
+      // passes it by more than kSlack (log2 units), so most tiles neither
+      // rescale nor take an exponential for it.  P is then at most 2^kSlack:
+      // the result is the same up to rounding, and the partial (m, l, acc)
+      // a split unit leaves stays consistent (l and acc share the reference).
+      // -inf + kSlack is -inf, so a row's first live tile always moves it; a
+      // row that has seen no live token keeps m_run = -inf and P = 0.
+      up[k] = mx > m_run[k] + kSlack;
+      m_new[k] = up[k] ? mx : m_run[k];
       float psum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if constexpr (checked)
-          p[k][i] = (live && z[i] != -__builtin_inff()) ? __builtin_amdgcn_exp2f(z[i] - m_new) : 0.f;
-        else
-          p[k][i] = __builtin_amdgcn_exp2f(z[i] - m_new);
-        psum += p[k][i];
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // v_exp_f32 directly: results below 2^-126 may flush to zero, which
+          // only drops weights under 1e-38 of the largest.
+          float e;
+          if constexpr (checked)   // (z finite implies m_new finite)
+            e = z[t][i] != -__builtin_inff() ? __builtin_amdgcn_exp2f(z[t][i] - m_new[k]) : 0.f;
+          else
+            e = __builtin_amdgcn_exp2f(z[t][i] - m_new[k]);
+          p[k][t][i] = e;
+          psum = (t == 0 && i == 0) ? e : psum + e;
+        }
       }
-      l_run[k] = l_run[k] * alpha[k] + psum;
-      m_run[k] = m_new;
+      p_sum[k] = psum;
       if constexpr (row_scaled(KV)) {
         // (the guard keeps a masked token's P at 0 even if its slot's scale is NaN)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          p[k][i] = (!checked || p[k][i] > 0.f) ? p[k][i] * vrcp[i] : 0.f;
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            p[k][t][i] = (!checked || p[k][t][i] > 0.f) ? p[k][t][i] * vrcp[t][i] : 0.f;
       }
     }
-    // Rescale only when some row's running max moved (alpha == 1 elsewhere
-    // leaves the values unchanged, so the result is the same either way).
+    // Rescale only when some row's reference max moved.
     bool moved = false;
 #pragma unroll
-    for (int k = 0; k < RT; ++k) moved = moved || alpha[k] != 1.0f;
+    for (int k = 0; k < RT; ++k) moved = moved || up[k];
     if (__builtin_amdgcn_ballot_w64(moved) != 0) {
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
+        const float alpha = up[k] ? __builtin_amdgcn_exp2f(m_run[k] - m_new[k]) : 1.0f;
 #pragma unroll
-        for (int nc = 0; nc < NC; ++nc) acc[k][nc] *= alpha[k];
-        if constexpr (offset_codes) acc_p[k][0] *= alpha[k];   // only row 0 is read
+        for (int nc = 0; nc < NC; ++nc) acc[k][nc] *= alpha;
+        if constexpr (offset_codes) acc_p[k][0] *= alpha;   // only row 0 is read
+        l_run[k] *= alpha;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < RT; ++k) {
+      l_run[k] += p_sum[k];
+      m_run[k] = m_new[k];
     }
 
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
     // of tokens 4*c16 .. 4*c16+3 (storage order), i.e. the A operand.
     const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-    if constexpr (KV == PKV_I4) {
-      // Word wd of the lane's 16 bytes converts to column blocks 2 wd (words
-      // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
-      // lane's four: P is packed in the same token order.
-      u32x2 pb[RT];
+    if constexpr (KV == PKV_I4 && NT == 2) {
+      // Two tiles in one 32-deep product per column block: the lane's four
+      // tokens of each tile, in the order of the 16-deep form below.
+      u32x4 pb[RT];
 #pragma unroll
       for (int k = 0; k < RT; ++k)
-        pb[k] = u32x2{pack_p<MT>(p[k][0], p[k][2]), pack_p<MT>(p[k][1], p[k][3])};
+        pb[k] = u32x4{pack_p<MT>(p[k][0][0], p[k][0][2]), pack_p<MT>(p[k][0][1], p[k][0][3]),
+                      pack_p<MT>(p[k][1][0], p[k][1][2]), pack_p<MT>(p[k][1][1], p[k][1][3])};
       // Codes are finite and P is exactly 0 past the context, so no mask.
 #pragma unroll
       for (int wd = 0; wd < NC / 2; ++wd) {
-        uint32_t w[4];
-        C::word(vraw[0][wd], w);
-        const u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
+        uint32_t w0[4], w1[4];
+        C::word(vraw[0][0][wd], w0);
+        C::word(vraw[1][0][wd], w1);
+        const u32x4 va = {w0[0], w0[2], w1[0], w1[2]}, vb = {w0[1], w0[3], w1[1], w1[3]};
 #pragma unroll
         for (int k = 0; k < RT; ++k) {
           if constexpr (MT == MT_F16) {
-            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd], 0, 0, 0);
-            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-                __builtin_bit_cast(f16x4, vb), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd + 1], 0,
+            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, va), __builtin_bit_cast(f16x8, pb[k]), acc[k][2 * wd], 0, 0, 0);
+            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                __builtin_bit_cast(f16x8, vb), __builtin_bit_cast(f16x8, pb[k]), acc[k][2 * wd + 1], 0,
                 0, 0);
           } else {
-            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(i16x4, va), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd], 0, 0,
+            acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, va), __builtin_bit_cast(bf16x8, pb[k]), acc[k][2 * wd], 0, 0,
                 0);
-            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd + 1], 0,
+            acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, vb), __builtin_bit_cast(bf16x8, pb[k]), acc[k][2 * wd + 1], 0,
                 0, 0);
           }
         }
       }
       if constexpr (offset_codes) {
+        const f16x8 ones8 = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f,
+                             (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
         for (int k = 0; k < RT; ++k)
-          acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
-                                                           acc_p[k], 0, 0, 0);
-      }
-    } else if constexpr (MT == MT_F32) {
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        uint32_t w[4];
-        if constexpr (eb == 4) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = vraw[nc][i];
-        } else if constexpr (eb == 1) {
-          C::word(vraw[nc / VG][nc % VG], w);
-        } else {
-          C::word(vraw[nc / VG][2 * (nc % VG)], w);
-          C::word(vraw[nc / VG][2 * (nc % VG) + 1], w + 2);
-        }
-#pragma unroll
-        for (int k = 0; k < RT; ++k)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[i] & vmask[i]), p[k][i],
-                                                              acc[k][nc], 0, 0, 0);
+          acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones8, __builtin_bit_cast(f16x8, pb[k]),
+                                                            acc_p[k], 0, 0, 0);
       }
     } else {
-      u32x2 pb[RT];
 #pragma unroll
-      for (int k = 0; k < RT; ++k)
-        pb[k] = u32x2{pack_p<MT>(p[k][0], p[k][1]), pack_p<MT>(p[k][2], p[k][3])};
-      const uint32_t m01 = (vmask[0] & 0xFFFFu) | (vmask[1] & 0xFFFF0000u);
-      const uint32_t m23 = (vmask[2] & 0xFFFFu) | (vmask[3] & 0xFFFF0000u);
-      // uniform: only a sequence's last tile is partial.  INT8 codes are finite
-      // and P is exactly 0 past the context: no mask needed.
-      const bool full = !checked || n_valid == 16 || KV == PKV_I8;
+      for (int t = 0; t < NT; ++t) {
+        if constexpr (KV == PKV_I4) {
+          // Word wd of the lane's 16 bytes converts to column blocks 2 wd (words
+          // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
+          // lane's four: P is packed in the same token order.
+          u32x2 pb[RT];
 #pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        uint32_t w[2];
-        if constexpr (eb == 1) {
-          C::word(vraw[nc / VG][nc % VG], w);
+          for (int k = 0; k < RT; ++k)
+            pb[k] = u32x2{pack_p<MT>(p[k][t][0], p[k][t][2]), pack_p<MT>(p[k][t][1], p[k][t][3])};
+          // Codes are finite and P is exactly 0 past the context, so no mask.
+#pragma unroll
+          for (int wd = 0; wd < NC / 2; ++wd) {
+            uint32_t w[4];
+            C::word(vraw[t][0][wd], w);
+            const u32x2 va = {w[0], w[2]}, vb = {w[1], w[3]};
+#pragma unroll
+            for (int k = 0; k < RT; ++k) {
+              if constexpr (MT == MT_F16) {
+                acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                    __builtin_bit_cast(f16x4, va), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd], 0, 0,
+                    0);
+                acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+                    __builtin_bit_cast(f16x4, vb), __builtin_bit_cast(f16x4, pb[k]), acc[k][2 * wd + 1], 0,
+                    0, 0);
+              } else {
+                acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(i16x4, va), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd], 0, 0,
+                    0);
+                acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                    __builtin_bit_cast(i16x4, vb), __builtin_bit_cast(i16x4, pb[k]), acc[k][2 * wd + 1], 0,
+                    0, 0);
+              }
+            }
+          }
+          if constexpr (offset_codes) {
+#pragma unroll
+            for (int k = 0; k < RT; ++k)
+              acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
+                                                               acc_p[k], 0, 0, 0);
+          }
+        } else if constexpr (MT == MT_F32) {
+#pragma unroll
+          for (int nc = 0; nc < NC; ++nc) {
+            uint32_t w[4];
+            if constexpr (eb == 4) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) w[i] = vraw[t][nc][i];
+            } else if constexpr (eb == 1) {
+              C::word(vraw[t][nc / VG][nc % VG], w);
+            } else {
+              C::word(vraw[t][nc / VG][2 * (nc % VG)], w);
+              C::word(vraw[t][nc / VG][2 * (nc % VG) + 1], w + 2);
+            }
+#pragma unroll
+            for (int k = 0; k < RT; ++k)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[i] & vmask[t][i]), p[k][t][i],
+                                                                  acc[k][nc], 0, 0, 0);
+          }
         } else {
-          w[0] = vraw[nc / VG][2 * (nc % VG)];
-          w[1] = vraw[nc / VG][2 * (nc % VG) + 1];
-        }
-        u32x2 va = {w[0], w[1]};
-        if (!full) va = u32x2{w[0] & m01, w[1] & m23};
+          u32x2 pb[RT];
 #pragma unroll
-        for (int k = 0; k < RT; ++k) {
-          if constexpr (MT == MT_F16) {
-            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
-                                                               __builtin_bit_cast(f16x4, pb[k]),
-                                                               acc[k][nc], 0, 0, 0);
-          } else {
-            acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, va),
-                                                                   __builtin_bit_cast(i16x4, pb[k]),
+          for (int k = 0; k < RT; ++k)
+            pb[k] = u32x2{pack_p<MT>(p[k][t][0], p[k][t][1]), pack_p<MT>(p[k][t][2], p[k][t][3])};
+          const uint32_t m01 = (vmask[t][0] & 0xFFFFu) | (vmask[t][1] & 0xFFFF0000u);
+          const uint32_t m23 = (vmask[t][2] & 0xFFFFu) | (vmask[t][3] & 0xFFFF0000u);
+          // uniform: only a sequence's last tile is partial.  INT8 codes are finite
+          // and P is exactly 0 past the context: no mask needed.
+          const bool full = !checked || n_valid[t] == 16 || KV == PKV_I8;
+#pragma unroll
+          for (int nc = 0; nc < NC; ++nc) {
+            uint32_t w[2];
+            if constexpr (eb == 1) {
+              C::word(vraw[t][nc / VG][nc % VG], w);
+            } else {
+              w[0] = vraw[t][nc / VG][2 * (nc % VG)];
+              w[1] = vraw[t][nc / VG][2 * (nc % VG) + 1];
+            }
+            u32x2 va = {w[0], w[1]};
+            if (!full) va = u32x2{w[0] & m01, w[1] & m23};
+#pragma unroll
+            for (int k = 0; k < RT; ++k) {
+              if constexpr (MT == MT_F16) {
+                acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, va),
+                                                                   __builtin_bit_cast(f16x4, pb[k]),
                                                                    acc[k][nc], 0, 0, 0);
+              } else {
+                acc[k][nc] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, va),
+                                                                       __builtin_bit_cast(i16x4, pb[k]),
+                                                                       acc[k][nc], 0, 0, 0);
+              }
+            }
+          }
+          if constexpr (offset_codes) {
+#pragma unroll
+            for (int k = 0; k < RT; ++k)
+              acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
+                                                               acc_p[k], 0, 0, 0);
           }
         }
-      }
-      if constexpr (offset_codes) {
-#pragma unroll
-        for (int k = 0; k < RT; ++k)
-          acc_p[k] = __builtin_amdgcn_mfma_f32_16x16x16f16(ones, __builtin_bit_cast(f16x4, pb[k]),
-                                                           acc_p[k], 0, 0, 0);
       }
     }
   };
 
-  // S-deep pipeline: tile t lives in register set t % S; while tile t is
-  // multiplied, tiles t+1 .. t+S-1 are in flight.  1-byte KV tiles carry half
-  // the bytes of 16-bit ones, so they keep twice as many in flight.  The
-  // steady state has no branch around the loads (a load issued on one path
-  // only would make the wait counts conservative); a short tail follows.
+  // S-deep pipeline over groups of NT tiles: group i lives in register set
+  // i % S; while it is multiplied, groups i+1 .. i+S-1 are in flight.  1-byte
+  // KV tiles carry half the bytes of 16-bit ones, so they keep more in flight.
+  // The steady state has no branch around the loads (a load issued on one
+  // path only would make the wait counts conservative); a short tail follows.
   constexpr int S = MULTI ? PKV_STAGES_MULTI : Tuning<KV>::stages;
-  u32x4 kr[S][NL], vr[S][NL];
-  float ks[S], vs[S];
-  int ph[S];   // physical block of the tile in each register set (-1: skipped)
+  u32x4 kr[S][NT][NL], vr[S][NT][NL];
+  float ks[S][NT], vs[S][NT];
+  int ph[S][NT];   // physical block of each tile in each register set (-1: skipped)
 #pragma unroll
-  for (int i = 0; i < S; ++i) {
-    ks[i] = vs[i] = 1.f;
-    ph[i] = -1;
-  }
-  // The steady loop takes only tiles that every row sees whole and never an
-  // item's last tile (the only one that can be partial), so its tiles take the
-  // unchecked path; a table entry outside the pool skips its tile (a uniform
-  // branch with nothing on the other side).  The tail takes the checked path.
-  int tile = 0;
-  if (ntiles > 2 * S - 1) {
+  for (int i = 0; i < S; ++i)
 #pragma unroll
-    for (int i = 0; i < S - 1; ++i) issue(i, kr[i], vr[i], ks[i], vs[i], ph[i]);
-    for (; tile + 2 * S - 1 < ntiles && tile + S <= nfull; tile += S) {
+    for (int t = 0; t < NT; ++t) {
+      ks[i][t] = vs[i][t] = 1.f;
+      ph[i][t] = -1;
+    }
+  // Loads of group gr into register set st; `guarded`: tiles past the item
+  // (only in an item's last group) are not loaded.
+  auto issue_group = [&](int gr, int st, bool guarded) {
 #pragma unroll
-      for (int i = 0; i < S; ++i) {
-        const int nx = (i + S - 1) % S;
-        issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx], ph[nx]);
-        if (ph[i] >= 0)
-          compute(std::false_type{}, tile + i, kr[i], vr[i], ks[i], vs[i], ph[i]);
+    for (int t = 0; t < NT; ++t) {
+      const int tl = gr * NT + t;
+      if (!guarded || tl < ntiles)
+        issue(tl, kr[st][t], vr[st][t], ks[st][t], vs[st][t], ph[st][t]);
+      else
+        ph[st][t] = -1;
+    }
+  };
+  // The steady loop takes only groups that every row sees whole and never an
+  // item's last group (the only one that can be partial), so its tiles take
+  // the unchecked path.  An item whose table has an entry outside the pool
+  // (whose tiles are skipped) and the tail take the checked path.
+  bool bad_entry = false;
+#pragma unroll
+  for (int r = 0; r < NREG; ++r) bad_entry = bad_entry || (r * 64 + lane < nblk && blk[r] < 0);
+  const bool table_ok = __builtin_amdgcn_ballot_w64(bad_entry) == 0;
+  const int ngroups = (ntiles + NT - 1) / NT;
+  int gr = 0;
+  if (ngroups > 2 * S - 1) {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue_group(i, i, false);
+    if (table_ok) {
+      for (; gr + 2 * S - 1 < ngroups && (gr + S) * NT <= nfull; gr += S) {
+#pragma unroll
+        for (int i = 0; i < S; ++i) {
+          const int nx = (i + S - 1) % S;
+          issue_group(gr + i + S - 1, nx, false);
+          compute(std::false_type{}, (gr + i) * NT, kr[i], vr[i], ks[i], vs[i], ph[i]);
+        }
       }
     }
   } else {
 #pragma unroll
     for (int i = 0; i < S - 1; ++i)
-      if (i < ntiles) issue(i, kr[i], vr[i], ks[i], vs[i], ph[i]);
+      if (i < ngroups) issue_group(i, i, true);
   }
-  for (; tile < ntiles; tile += S) {
+  for (; gr < ngroups; gr += S) {
 #pragma unroll
     for (int i = 0; i < S; ++i) {
-      if (tile + i < ntiles) {
+      if (gr + i < ngroups) {
         const int nx = (i + S - 1) % S;
-        if (tile + i + S - 1 < ntiles) issue(tile + i + S - 1, kr[nx], vr[nx], ks[nx], vs[nx], ph[nx]);
-        compute(std::true_type{}, tile + i, kr[i], vr[i], ks[i], vs[i], ph[i]);
+        if (gr + i + S - 1 < ngroups) issue_group(gr + i + S - 1, nx, true);
+        compute(std::true_type{}, (gr + i) * NT, kr[i], vr[i], ks[i], vs[i], ph[i]);
       }
     }
   }

@@ -207,6 +207,13 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// A wave-uniform pointer, moved to SGPRs (so that address arithmetic on it
+// stays scalar and memory instructions take it as their scalar base).
+template <typename T>
+__device__ __forceinline__ T* sptr(T* p) {
+  return reinterpret_cast<T*>(uni64(reinterpret_cast<int64_t>(p)));
+}
+
 __device__ __forceinline__ int64_t readlane_i64(int64_t v, int lane) {
   const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
   const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)((uint64_t)v >> 32), lane);
