@@ -127,7 +127,7 @@ def decode_traffic(workload):
 
 class LaunchEvents:
     """Timing-only HIP events recorded on the launch stream (the current torch
-    stream when recorded), made before the timed loop.
+    stream when they are made), made before the timed loop.
 
     They are created with hipEventDisableSystemFence: recording one then does
     not write back and invalidate the caches, as a default event does, which
@@ -150,6 +150,9 @@ class LaunchEvents:
                                             ctypes.c_void_p]
         hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self._hip = hip
+        # (taken once: building torch's Stream object at every record would put
+        # microseconds of host work inside the timed pairs of short launches)
+        self._stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.pairs = [(self._make(), self._make()) for _ in range(n)]
         self.used = 0
 
@@ -161,8 +164,7 @@ class LaunchEvents:
         return e
 
     def _record(self, e):
-        st = self._hip.hipEventRecord(e, self._c.c_void_p(
-            self._torch.cuda.current_stream().cuda_stream))
+        st = self._hip.hipEventRecord(e, self._stream)
         if st != 0:
             raise RuntimeError(f"hipEventRecord failed ({st})")
 

@@ -143,7 +143,7 @@ def _kv_code(t, kv_dtype, what):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()   # (an int: the argtypes make it a pointer)
 
 
 def _dev(t, what):
@@ -155,9 +155,17 @@ def _dev(t, what):
         raise ValueError(f"{what} must be contiguous")
 
 
+# The current stream's raw handle without building a Stream object (which
+# costs about as much as the rest of a decode call's host work).
+_RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream):
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return stream.cuda_stream
+    if _RAW_STREAM is not None:
+        return _RAW_STREAM(torch.cuda.current_device())
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(status, lib):
@@ -274,9 +282,10 @@ def paged_attention_decode(out, q, k_cache, v_cache, block_tables, context_lens,
     if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
         raise ValueError("block_tables must be [B][MB] and context_lens [B]")
     _need_scales(k_scale, v_scale, kc, NB * Hkv * bs, "paged_attention_decode")
-    need = lib.paged_attention_workspace_size(B, Hq, Hkv, d, int(max_context_len))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:   # (a given one is checked against the need by the library)
+        need = lib.paged_attention_workspace_size(B, Hq, Hkv, d, int(max_context_len))
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.paged_attention_decode(
         _ptr(out), _ptr(q), _dtype_code(q, "q"), B, Hq, _ptr(k_cache), _ptr(v_cache),

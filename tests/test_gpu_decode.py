@@ -161,6 +161,41 @@ def test_needles_localise_every_position(bs):
     compare(got, OracleSide(w, case).attention(), "f32", "needles")
 
 
+@pytest.mark.parametrize("q_dtype,kv", [(torch.float16, "f16"), (torch.float32, "f32"),
+                                        (torch.float16, "i8"), (torch.float16, "i4"),
+                                        (torch.bfloat16, "i4")])
+def test_softmax_ramp_and_jump(q_dtype, kv):
+    """Logits that rise along the context by 0.12 log2 units per token (just
+    under two units per 16-token tile), then jump by 20 units two thirds of the
+    way: the online softmax's reference maximum lags the running max, so P
+    climbs towards its bound between the moves, and the jump moves it at once."""
+    bs, d = 16, 128
+    ctx = [1000, 700, 333]
+    w = W.custom(q_dtype, kv, ctx, 4, 1, d, bs, name=f"ramp-{kv}")
+    case = DeviceCase(w, keep_sources=True)
+    src_k, src_v = case.sources["k"], case.sources["v"]
+    slots, krows, vrows = [], [], []
+    for b, n in enumerate(ctx):
+        case.q[b, 1:] = case.q[b, 0]
+        qf = case.q[b, 0].float().cpu()
+        unit = qf / qf.norm()
+        per_log2 = 1.0 / (w.scale * float(qf.norm()) * 1.4426950408889634)   # K lift per log2 unit
+        for t in range(n):
+            blk = int(w.block_tables[b, t // bs])
+            lift = 0.12 * t + (20.0 if t >= 2 * n // 3 else 0.0)
+            row = src_k[blk, 0, t % bs].float() + lift * per_log2 * unit
+            src_k[blk, 0, t % bs] = row.to(src_k.dtype)
+            slots.append(blk * bs + t % bs)
+            krows.append(src_k[blk, 0, t % bs].view(1, d))
+            vrows.append(src_v[blk, 0, t % bs].view(1, d))
+    pkv.kv_cache_append(torch.stack(krows).cuda(), torch.stack(vrows).cuda(),
+                        torch.tensor(slots, dtype=torch.int64, device="cuda"),
+                        case.k_cache, case.v_cache, case.k_scale, case.v_scale,
+                        kv_dtype=case.kv_dtype)
+    got = append_and_decode(case)
+    compare(got, OracleSide(w, case).attention(), kv, f"ramp-{kv}")
+
+
 def test_workspace_too_small_raises():
     w = W.custom(torch.float16, "f16", [3000], 8, 2, 128, 16, name="ws")
     case = DeviceCase(w)
