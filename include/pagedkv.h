@@ -190,7 +190,7 @@ size_t paged_attention_workspace_size(int32_t batch, int32_t num_q_heads, int32_
  *                 size is 0); contents are overwritten.  Calls that share a
  *                 workspace must be ordered.
  *   Supported: head_dim 64 or 128; block_size 16 or 256; num_q_heads a multiple
- *   of num_kv_heads.  INT4 caches: head_dim 128 and q_dtype F16 or BF16.  Pools
+ *   of num_kv_heads.  INT4 caches: head_dim 128.  Pools
  *   may exceed 2^31 bytes (byte offsets are 64-bit).
  *   Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE, PKV_ERR_HIP.
  */

@@ -198,9 +198,8 @@ pkv_status decode_impl(const char* fn, void* out, const void* q, int32_t q_dtype
                 std::string(fn) + ": kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
-  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
-    return fail(PKV_ERR_UNSUPPORTED,
-                std::string(fn) + ": INT4 caches need head_dim 128 and F16 or BF16 queries");
+  if (kv_dtype == PKV_I4 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": INT4 caches need head_dim 128");
   if (block_size != 16 && block_size != 256)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": block_size must be 16 or 256");
   if (batch < 0 || batch > 65535 || num_q_heads < 1 || num_kv_heads < 1 ||
@@ -452,9 +451,8 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
                 std::string(fn) + ": kv_dtype must equal q_dtype, or be I8, FP8_E4M3FN or I4");
   if (head_dim != 64 && head_dim != 128)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": head_dim must be 64 or 128");
-  if (kv_dtype == PKV_I4 && (head_dim != 128 || q_dtype == PKV_F32))
-    return fail(PKV_ERR_UNSUPPORTED,
-                std::string(fn) + ": INT4 caches need head_dim 128 and F16 or BF16 queries");
+  if (kv_dtype == PKV_I4 && head_dim != 128)
+    return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": INT4 caches need head_dim 128");
   if (block_size != 16 && block_size != 256)
     return fail(PKV_ERR_UNSUPPORTED, std::string(fn) + ": block_size must be 16 or 256");
   if (batch < 0 || num_query_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1 ||

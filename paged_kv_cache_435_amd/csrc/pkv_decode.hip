@@ -63,6 +63,8 @@
 //   PKV_STAGES_MULTI        pipeline depth (tiles in flight), multi-token calls
 //   PKV_MULTI_WAVES_PER_EU  occupancy target, multi-token calls
 //   PKV_WAVES_PER_EU_I4     occupancy target, INT4 KV
+//   PKV_WAVES_PER_EU_FP8    occupancy target, FP8 KV
+//   PKV_SLOTS_PER_CU_FP8      items planned per compute unit and round, FP8 KV
 //   PKV_SLOTS_PER_CU_DEFAULT  items planned per compute unit and round
 //   PKV_SLOTS_PER_CU_I8       the same for INT8 KV
 //   PKV_SLOTS_PER_CU_I4       the same for INT4 KV
@@ -107,6 +109,12 @@
 #endif
 #ifndef PKV_SLOTS_PER_CU_I4
 #define PKV_SLOTS_PER_CU_I4 16
+#endif
+#ifndef PKV_WAVES_PER_EU_FP8
+#define PKV_WAVES_PER_EU_FP8 PKV_WAVES_PER_EU
+#endif
+#ifndef PKV_SLOTS_PER_CU_FP8
+#define PKV_SLOTS_PER_CU_FP8 PKV_SLOTS_PER_CU_DEFAULT
 #endif
 #ifndef PKV_ITEM_TILES_I8
 #define PKV_ITEM_TILES_I8 512
@@ -185,10 +193,14 @@ struct Tuning {
                    : KV == PKV_I4 ? PKV_STAGES_I4
                                   : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
   static constexpr int waves_per_eu =
-      KV == PKV_I8 ? 4 : (KV == PKV_I4 ? PKV_WAVES_PER_EU_I4 : PKV_WAVES_PER_EU);
+      KV == PKV_I8 ? 4
+                   : (KV == PKV_I4 ? PKV_WAVES_PER_EU_I4
+                                   : (KV == PKV_FP8_E4M3FN ? PKV_WAVES_PER_EU_FP8 : PKV_WAVES_PER_EU));
   static constexpr int slots_per_cu =
       KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8
-                   : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4 : PKV_SLOTS_PER_CU_DEFAULT);
+                   : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4
+                                   : (KV == PKV_FP8_E4M3FN ? PKV_SLOTS_PER_CU_FP8
+                                                           : PKV_SLOTS_PER_CU_DEFAULT));
   // Most tiles per item (block-table registers per lane at 16-token blocks:
   // one per 64 tiles).  Longer items keep long contexts to one round of items;
   // INT4's loop, bound by vector work, measured slower with 8 registers.
@@ -361,7 +373,19 @@ void decode_partition_kernel(DecodeArgs a) {
     for (int i = 0; i < KW; ++i) qop[k][i] = 0u;
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
-  if constexpr (KV == PKV_I4) {
+  if constexpr (KV == PKV_I4 && MT == MT_F32) {
+   if (head_ok[k]) {
+    // INT4, f32 queries: the lane's K chunk holds d = 32 c16 .. 32 c16 + 31,
+    // converted one element per word in that order.
+    const uint8_t* src = static_cast<const uint8_t*>(a.q) + (hq[k] * D + 32 * c16) * 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(src + 16 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qop[k][4 * i + e] = w[e];
+    }
+   }
+  } else if constexpr (KV == PKV_I4) {
    if (head_ok[k]) {
     // INT4: the lane's K chunk holds d = 32 c16 .. 32 c16 + 31; word i of it
     // converts to elements 8 i + (0 4 1 5 2 6 3 7), so q pairs are taken in
@@ -679,7 +703,7 @@ void decode_partition_kernel(DecodeArgs a) {
     // O^T += V^T P^T.  Lane 16*c16 + r16 holds, for d = 16*nc + r16, the V values
     // of tokens 4*c16 .. 4*c16+3 (storage order), i.e. the A operand.
     const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
-    if constexpr (KV == PKV_I4 && NT == 2) {
+    if constexpr (KV == PKV_I4 && NT == 2 && MT != MT_F32) {
       // Two tiles in one 32-deep product per column block: the lane's four
       // tokens of each tile, in the order of the 16-deep form below.
       u32x4 pb[RT];
@@ -723,7 +747,26 @@ void decode_partition_kernel(DecodeArgs a) {
     } else {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if constexpr (KV == PKV_I4) {
+        if constexpr (KV == PKV_I4 && MT == MT_F32) {
+          // Byte b of word wd of the lane's 16 bytes holds token 4 c16 + b of
+          // column blocks 2 wd (low nibble) and 2 wd + 1 (high): converted,
+          // word 2 b and 2 b + 1.  Codes are finite and P is exactly 0 past the
+          // context, so no mask.
+#pragma unroll
+          for (int wd = 0; wd < NC / 2; ++wd) {
+            uint32_t w[8];
+            C::word(vraw[t][0][wd], w);
+#pragma unroll
+            for (int k = 0; k < RT; ++k)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[k][2 * wd] = __builtin_amdgcn_mfma_f32_16x16x4f32(bitsf(w[2 * i]), p[k][t][i],
+                                                                      acc[k][2 * wd], 0, 0, 0);
+                acc[k][2 * wd + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    bitsf(w[2 * i + 1]), p[k][t][i], acc[k][2 * wd + 1], 0, 0, 0);
+              }
+          }
+        } else if constexpr (KV == PKV_I4) {
           // Word wd of the lane's 16 bytes converts to column blocks 2 wd (words
           // 0, 2) and 2 wd + 1 (words 1, 3), each as tokens (0, 2), (1, 3) of the
           // lane's four: P is packed in the same token order.
@@ -1437,12 +1480,8 @@ static hipError_t launch1(DecodeArgs& a, int kv, int d, int bs, int cus, const M
     case PKV_I8: return launch2<PKV_I8, QT, MULTI>(a, d, bs, cus, ml, st);
     case PKV_FP8_E4M3FN: return launch2<PKV_FP8_E4M3FN, QT, MULTI>(a, d, bs, cus, ml, st);
     case PKV_I4:
-      if constexpr (QT == PKV_F32) {
-        return hipErrorInvalidValue;   // rejected by the entry point
-      } else {
-        if (d != 128) return hipErrorInvalidValue;
-        return launch3<PKV_I4, QT, 128, MULTI>(a, bs, cus, ml, st);
-      }
+      if (d != 128) return hipErrorInvalidValue;   // (rejected by the entry points)
+      return launch3<PKV_I4, QT, 128, MULTI>(a, bs, cus, ml, st);
     default: return launch2<QT, QT, MULTI>(a, d, bs, cus, ml, st);
   }
 }

@@ -27,7 +27,8 @@ struct MfmaOf {
 // 16 bits apart, so word w of the output holds nibbles (w, w + 4) of the
 // input word (an order the query operand is loaded in to match): -> f16 as
 // offset subnormals (q + 8) 2^-24 / 2^-20, corrected after the products;
-// -> bf16 exactly, through f32 (2^23 + u - (2^23 + 8)).
+// -> bf16 exactly, through f32 (2^23 + u - (2^23 + 8)); -> f32 exactly, one
+// element per word in the nibbles' own order.
 // ---------------------------------------------------------------------------
 template <int KV, int MT>
 struct Cvt {
@@ -58,6 +59,11 @@ struct Cvt {
       w[1] = (raw & 0x00F000F0u) ^ 0x00800080u;
       w[2] = (x8 & 0x000F000Fu) ^ 0x00080008u;
       w[3] = (x8 & 0x00F000F0u) ^ 0x00800080u;
+    } else if constexpr (KV == PKV_I4 && MT == MT_F32) {
+      // Exact: nibble e of the word (element 8 i + e of the chunk's word i),
+      // sign-extended.
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[e] = fbits((float)((int32_t)(raw << (28 - 4 * e)) >> 28));
     } else if constexpr (KV == PKV_I4 && MT == MT_BF16) {
       const uint32_t x = raw ^ 0x88888888u;
 #pragma unroll

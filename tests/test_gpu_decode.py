@@ -21,7 +21,7 @@ RAGGED = [1, 15, 16, 17, 255, 256, 257, 511, 513, 700, 1024, 2049]
     (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
     (torch.float16, "i8"), (torch.bfloat16, "i8"), (torch.float32, "i8"),
     (torch.float16, "fp8"), (torch.bfloat16, "fp8"), (torch.float32, "fp8"),
-    (torch.float16, "i4"), (torch.bfloat16, "i4"),
+    (torch.float16, "i4"), (torch.bfloat16, "i4"), (torch.float32, "i4"),
 ])
 def test_dtype_pairs_ragged(q_dtype, kv):
     w = W.custom(q_dtype, kv, RAGGED, 8, 2, 128, 16, appends=True, name=f"ragged-{kv}")
@@ -249,7 +249,7 @@ def test_head_dim_64_every_format(q_dtype, kv, bs):
     run_and_check(w)
 
 
-@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("name,ctx,hq,hkv,bs", [
     ("i4-bs256-ragged", [1, 15, 255, 256, 257, 3000], 8, 2, 256),
     ("i4-mqa", [40, 600, 1100], 16, 1, 16),
@@ -263,14 +263,16 @@ def test_int4_shapes(q_dtype, name, ctx, hq, hkv, bs):
     run_and_check(w)
 
 
-def test_int4_f32_queries_are_rejected():
-    w = W.custom(torch.float16, "i4", [20], 4, 4, 128, 16, name="i4-f32q")
+def test_int4_head_dim_64_is_rejected():
+    """INT4 caches are laid out for head_dim 128 only; d = 64 fails before any launch."""
+    w = W.custom(torch.float16, "f16", [20], 4, 4, 64, 16, name="i4-d64")
     case = DeviceCase(w)
-    q = case.q.float()
-    with pytest.raises(RuntimeError, match="F16 or BF16"):
-        pkv.paged_attention_decode(torch.empty_like(q), q, case.k_cache, case.v_cache,
+    kc = torch.zeros(w.num_blocks, 4, 16, 32, dtype=torch.uint8, device="cuda")
+    sc = torch.ones(w.num_blocks, 4, 16, dtype=torch.float32, device="cuda")
+    with pytest.raises(RuntimeError, match="head_dim 128"):
+        pkv.paged_attention_decode(torch.empty_like(case.q), case.q, kc, kc.clone(),
                                    case.block_tables, case.context_lens, w.scale,
-                                   w.max_context_len, k_scale=case.k_scale, v_scale=case.v_scale,
+                                   w.max_context_len, k_scale=sc, v_scale=sc.clone(),
                                    kv_dtype="i4")
 
 

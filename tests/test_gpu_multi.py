@@ -76,6 +76,7 @@ def run_multi(w, q_lens, seqs_check=None, what="", rows_of=None, want_ref=False)
 @pytest.mark.parametrize("q_dtype,kv", [
     (torch.float16, "f16"), (torch.bfloat16, "bf16"), (torch.float32, "f32"),
     (torch.float16, "i8"), (torch.bfloat16, "fp8"), (torch.float16, "i4"), (torch.bfloat16, "i4"),
+    (torch.float32, "i4"),
 ])
 def test_dtype_pairs_ragged(q_dtype, kv):
     w = W.custom(q_dtype, kv, [1, 17, 300, 1025, 2600], 8, 2, 128, 16, name=f"multi-{kv}")
