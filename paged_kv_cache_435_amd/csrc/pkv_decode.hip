@@ -150,13 +150,12 @@ __device__ __forceinline__ float row_bcast(float v) {
   return bitsf((uint32_t)__builtin_amdgcn_mov_dpp((int)fbits(v), 0x150 + L, 0xF, 0xF, false));
 }
 
-// (global-memory pointers: the bases come through readfirstlane, which hides
-// their address space from the compiler)
-// The base is cast first and the lane's offset added to the global pointer,
-// so the load takes the scalar base and a 32-bit vector offset.  (The empty
-// asm makes the offset a value of the load's own block: instruction selection
-// then sees that it is a zero-extended 32-bit one, rather than a 64-bit copy
-// made once before the loop.)
+// A 16-byte load from a wave-uniform base plus the lane's byte offset.  The
+// base has passed through readfirstlane, which hides its address space, so it
+// is cast to a global pointer first and the offset added after: the load then
+// takes the scalar base and a 32-bit vector offset.  (The empty asm makes the
+// offset a value of the load's own block, so instruction selection sees a
+// zero-extended 32-bit value rather than a 64-bit copy made before the loop.)
 __device__ __forceinline__ u32x4 ld16(const uint8_t* base, uint32_t off) {
   asm("" : "+v"(off));
   const __attribute__((address_space(1))) uint8_t* g = (const __attribute__((address_space(1))) uint8_t*)base;
@@ -183,8 +182,8 @@ __device__ __forceinline__ float ld_f32(const float* base, int idx) {
 // roughly 14-16 MB outstanding over the chip: 16-bit and f32 KV (8 KB tiles)
 // run without prefetch at 8 waves per CU; FP8 (4 KB tiles) keeps two tiles in
 // flight at 8 waves per CU; INT8, whose tiles carry more vector work (row
-// scales), runs without prefetch at 16 waves per CU; INT4 (2 KB tiles, vector
-// bound) keeps two tiles in flight at 16 waves per CU.  Multi-token calls
+// scales), runs without prefetch at 16 waves per CU; INT4 (1 KB tiles per
+// cache) keeps two tiles in flight at 16 waves per CU.  Multi-token calls
 // (32 rows per wave, ~170 VGPRs) run at 2 waves per SIMD without prefetch.
 template <int KV>
 struct Tuning {
@@ -203,7 +202,8 @@ struct Tuning {
                                                            : PKV_SLOTS_PER_CU_DEFAULT));
   // Most tiles per item (block-table registers per lane at 16-token blocks:
   // one per 64 tiles).  Longer items keep long contexts to one round of items;
-  // INT4's loop, bound by vector work, measured slower with 8 registers.
+  // INT4 (four times the tiles per byte, each reading its entry) measured
+  // slower with 8 registers.
   static constexpr int item_tiles =
       KV == PKV_I4 ? PKV_ITEM_TILES_I4 : (KV == PKV_I8 ? PKV_ITEM_TILES_I8 : kItemTilesMax);
   static_assert(item_tiles >= kItemTilesMin && item_tiles <= kItemTilesMax, "item limit");

@@ -23,7 +23,7 @@ constexpr int kTileTokens = 16;
 constexpr int kItemTilesMin = PKV_ITEM_TILES_MIN;
 // Most tiles per item: a lane holds one block-table entry per 64 tiles (at 16-token
 // blocks).  The decode kernels take up to kItemTilesMax (8 registers; INT4,
-// whose loop is bound by vector work, keeps 4); the prompt-chunk kernel, short of
+// measured slower with 8, keeps 4); the prompt-chunk kernel, short of
 // registers, kPrefillItemTilesMax.
 constexpr int kItemTilesMax = 512;          // 8192 tokens
 constexpr int kPrefillItemTilesMax = 256;   // 4096 tokens
