@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 
 _Q_FOR = {"f32": [torch.float32], "f16": [torch.float16], "bf16": [torch.bfloat16],
           "i8": [torch.float16, torch.bfloat16], "fp8": [torch.float16, torch.bfloat16],
-          "i4": [torch.float16, torch.bfloat16]}
+          "i4": [torch.float16, torch.bfloat16, torch.float32]}
 
 
 def _draw(seed):
