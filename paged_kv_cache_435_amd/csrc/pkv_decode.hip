@@ -71,6 +71,9 @@
 //   PKV_TILES_PER_UPDATE_I4   16-token tiles per online-softmax step, INT4 KV
 //   PKV_TILES_PER_UPDATE_I8   the same for INT8 KV
 //   PKV_TILES_PER_UPDATE_FP8  the same for FP8 KV
+//   PKV_I4_DEEP_UNITS         INT4 decode: most units for the DEEP instance
+//   PKV_*_I4_DEEP             stages, occupancy, items per CU and tiles per
+//                             step of that instance
 #ifndef PKV_NT_LOADS
 #define PKV_NT_LOADS 1
 #endif
@@ -131,6 +134,21 @@
 #ifndef PKV_TILES_PER_UPDATE_FP8
 #define PKV_TILES_PER_UPDATE_FP8 1
 #endif
+#ifndef PKV_I4_DEEP_UNITS
+#define PKV_I4_DEEP_UNITS 512
+#endif
+#ifndef PKV_STAGES_I4_DEEP
+#define PKV_STAGES_I4_DEEP 2
+#endif
+#ifndef PKV_WAVES_PER_EU_I4_DEEP
+#define PKV_WAVES_PER_EU_I4_DEEP 2
+#endif
+#ifndef PKV_SLOTS_PER_CU_I4_DEEP
+#define PKV_SLOTS_PER_CU_I4_DEEP 8
+#endif
+#ifndef PKV_TILES_PER_UPDATE_I4_DEEP
+#define PKV_TILES_PER_UPDATE_I4_DEEP 2
+#endif
 
 namespace pkv {
 
@@ -185,21 +203,29 @@ __device__ __forceinline__ float ld_f32(const float* base, int idx) {
 // scales), runs without prefetch at 16 waves per CU; INT4 (1 KB tiles per
 // cache) keeps two tiles in flight at 16 waves per CU.  Multi-token calls
 // (32 rows per wave, ~170 VGPRs) run at 2 waves per SIMD without prefetch.
-template <int KV>
+// DEEP (INT4 only, chosen by the host when the batch has few units, so that
+// half the items still split every unit): 8 items per CU at 2 waves per
+// SIMD, two tiles per softmax step and the next two in flight.
+template <int KV, bool DEEP = false>
 struct Tuning {
+  static constexpr bool deep = DEEP && KV == PKV_I4;
   static constexpr int stages =
-      KV == PKV_I8 ? PKV_STAGES_I8
-                   : KV == PKV_I4 ? PKV_STAGES_I4
-                                  : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
+      deep ? PKV_STAGES_I4_DEEP
+           : KV == PKV_I8 ? PKV_STAGES_I8
+                          : KV == PKV_I4 ? PKV_STAGES_I4
+                                         : (KV == PKV_FP8_E4M3FN ? PKV_STAGES_FP8 : PKV_STAGES_2B);
   static constexpr int waves_per_eu =
-      KV == PKV_I8 ? 4
-                   : (KV == PKV_I4 ? PKV_WAVES_PER_EU_I4
-                                   : (KV == PKV_FP8_E4M3FN ? PKV_WAVES_PER_EU_FP8 : PKV_WAVES_PER_EU));
+      deep ? PKV_WAVES_PER_EU_I4_DEEP
+           : KV == PKV_I8 ? 4
+                          : (KV == PKV_I4 ? PKV_WAVES_PER_EU_I4
+                                          : (KV == PKV_FP8_E4M3FN ? PKV_WAVES_PER_EU_FP8
+                                                                  : PKV_WAVES_PER_EU));
   static constexpr int slots_per_cu =
-      KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8
-                   : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4
-                                   : (KV == PKV_FP8_E4M3FN ? PKV_SLOTS_PER_CU_FP8
-                                                           : PKV_SLOTS_PER_CU_DEFAULT));
+      deep ? PKV_SLOTS_PER_CU_I4_DEEP
+           : KV == PKV_I8 ? PKV_SLOTS_PER_CU_I8
+                          : (KV == PKV_I4 ? PKV_SLOTS_PER_CU_I4
+                                          : (KV == PKV_FP8_E4M3FN ? PKV_SLOTS_PER_CU_FP8
+                                                                  : PKV_SLOTS_PER_CU_DEFAULT));
   // Most tiles per item (block-table registers per lane at 16-token blocks:
   // one per 64 tiles).  Longer items keep long contexts to one round of items;
   // INT4 (four times the tiles per byte, each reading its entry) measured
@@ -214,9 +240,10 @@ struct Tuning {
   // Tiles per online-softmax step (their loads are issued together; INT4's PV
   // products then run 32 tokens deep).
   static constexpr int tiles_per_update =
-      KV == PKV_I4 ? PKV_TILES_PER_UPDATE_I4
-                   : (KV == PKV_I8 ? PKV_TILES_PER_UPDATE_I8
-                                   : (KV == PKV_FP8_E4M3FN ? PKV_TILES_PER_UPDATE_FP8 : 1));
+      deep ? PKV_TILES_PER_UPDATE_I4_DEEP
+           : KV == PKV_I4 ? PKV_TILES_PER_UPDATE_I4
+                          : (KV == PKV_I8 ? PKV_TILES_PER_UPDATE_I8
+                                          : (KV == PKV_FP8_E4M3FN ? PKV_TILES_PER_UPDATE_FP8 : 1));
 };
 
 // Waves per workgroup: decode takes kDecodeWaves consecutive items (the KV
@@ -234,10 +261,10 @@ __host__ __device__ __forceinline__ int multi_wpg(const DecodeArgs& a, bool mult
 // a.vseq_g / a.vseq_rt say which sequence, KV head and row group each is
 // (written by multi_prep_kernel).  A wave takes one 32-row tile; the
 // head_tiles waves of a group form one workgroup (multi_wpg).
-template <int KV, int QT, int D, int BS, bool MULTI>
+template <int KV, int QT, int D, int BS, bool MULTI, bool DEEP = false>
 __global__ __launch_bounds__(64 * (MULTI && kMultiGroupMax > kDecodeWaves ? kMultiGroupMax
                                                                            : kDecodeWaves))
-__attribute__((amdgpu_waves_per_eu(MULTI ? PKV_MULTI_WAVES_PER_EU : Tuning<KV>::waves_per_eu)))
+__attribute__((amdgpu_waves_per_eu(MULTI ? PKV_MULTI_WAVES_PER_EU : Tuning<KV, DEEP>::waves_per_eu)))
 void decode_partition_kernel(DecodeArgs a) {
   constexpr int MT = MfmaOf<QT>::value;
   constexpr int eb = dtype_bytes(KV);  // (INT4: handled apart wherever it matters)
@@ -252,7 +279,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // multi-token calls, whose query tokens x heads of a KV head run to dozens of
   // rows (each loaded K/V tile then serves twice the rows).
   constexpr int RT = MULTI ? kMultiRowTiles : 1;
-  constexpr int NT = MULTI ? 1 : Tuning<KV>::tiles_per_update;   // tiles per softmax step
+  constexpr int NT = MULTI ? 1 : Tuning<KV, DEEP>::tiles_per_update;   // tiles per softmax step
 
   const int lane = threadIdx.x & (kWave - 1);
   const int r16 = lane & 15;   // MFMA row/column index of this lane
@@ -352,7 +379,7 @@ void decode_partition_kernel(DecodeArgs a) {
 
   // Block-table entries of the item, one per lane per register.
   constexpr int NREG =
-      (Tuning<KV>::item_tiles * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
+      (Tuning<KV, DEEP>::item_tiles * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
   const int first_blk = t_begin / BS;
   const int nblk = ntiles > 0 ? (t_end - 1) / BS - first_blk + 1 : 0;   // (empty: an item of zeros)
   int blk[NREG];
@@ -875,7 +902,7 @@ void decode_partition_kernel(DecodeArgs a) {
   // KV tiles carry half the bytes of 16-bit ones, so they keep more in flight.
   // The steady state has no branch around the loads (a load issued on one
   // path only would make the wait counts conservative); a short tail follows.
-  constexpr int S = MULTI ? PKV_STAGES_MULTI : Tuning<KV>::stages;
+  constexpr int S = MULTI ? PKV_STAGES_MULTI : Tuning<KV, DEEP>::stages;
   u32x4 kr[S][NT][NL], vr[S][NT][NL];
   float ks[S][NT], vs[S][NT];
   int ph[S][NT];   // physical block of each tile in each register set (-1: skipped)
@@ -1401,10 +1428,11 @@ struct MultiLaunch {
   int64_t* bound_only = nullptr;
 };
 
-template <int KV, int QT, int D, int BS, bool MULTI>
-static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hipStream_t st) {
-  auto* kern = decode_partition_kernel<KV, QT, D, BS, MULTI>;
-  a.item_cap = Tuning<KV>::item_tiles;   // the plan's item limit is this instance's
+template <int KV, int QT, int D, int BS, bool MULTI, bool DEEP>
+static hipError_t launch5(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hipStream_t st) {
+  using T = Tuning<KV, DEEP>;
+  auto* kern = decode_partition_kernel<KV, QT, D, BS, MULTI, DEEP>;
+  a.item_cap = T::item_tiles;   // the plan's item limit is this instance's
   // Resident waves per CU of this instance: a property of the compiled code,
   // queried once (every device the library runs on is gfx950).
   static std::atomic<int> occupancy{0};
@@ -1417,8 +1445,7 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
     occupancy.store(per_cu, std::memory_order_relaxed);
   }
   per_cu = per_cu < 1 ? 1 : (per_cu > kWavesPerCuCap ? kWavesPerCuCap : per_cu);
-  const int target = slots_per_cu_override() > 0 ? slots_per_cu_override()
-                                                 : Tuning<KV>::slots_per_cu;
+  const int target = slots_per_cu_override() > 0 ? slots_per_cu_override() : T::slots_per_cu;
   if (target < per_cu) per_cu = target;
   const int wpg = multi_wpg(a, MULTI);
   if (MULTI && per_cu > wpg) per_cu = per_cu / wpg * wpg;   // whole workgroups
@@ -1458,6 +1485,21 @@ static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
     hipLaunchKernelGGL((decode_merge_kernel<QT, D>), dim3(a.num_q_heads, a.batch), dim3(64), 0,
                        st, a);
   return hipGetLastError();
+}
+
+// INT4 decode takes the DEEP instance when the batch has at most
+// PKV_I4_DEEP_UNITS (sequence, KV head, head tile) units: its 8 items per CU
+// then still split the units (measured on the 70B GQA-8 layer, 256 units:
+// 112.7 against 119.6 us; on 13B MHA-40, 1,280 units, the 16-items-per-CU
+// instance stays ahead, 69.1 against 76.2 us).  The choice depends only on
+// the call's sizes, so the workspace bound and the launch agree.
+template <int KV, int QT, int D, int BS, bool MULTI>
+static hipError_t launch4(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hipStream_t st) {
+  if constexpr (KV == PKV_I4 && !MULTI) {
+    const int64_t units = (int64_t)a.batch * a.plan_heads * a.head_tiles;
+    if (units <= PKV_I4_DEEP_UNITS) return launch5<KV, QT, D, BS, MULTI, true>(a, num_cus, ml, st);
+  }
+  return launch5<KV, QT, D, BS, MULTI, false>(a, num_cus, ml, st);
 }
 
 template <int KV, int QT, int D, bool MULTI>

@@ -263,6 +263,16 @@ def test_int4_shapes(q_dtype, name, ctx, hq, hkv, bs):
     run_and_check(w)
 
 
+@pytest.mark.parametrize("q_dtype", [torch.float16, torch.bfloat16, torch.float32])
+def test_int4_many_units(q_dtype):
+    """INT4 decode has two instances, chosen by the number of (sequence, KV head,
+    head tile) units: this batch (18 x 40 = 720 units) takes the one with 16
+    items per CU; the shape tests above (few units) take the deeper one."""
+    ctx = [int(c) for c in np.random.default_rng(5).integers(1, 400, size=18)]
+    w = W.custom(q_dtype, "i4", ctx, 40, 40, 128, 16, appends=True, name="i4-many-units")
+    run_and_check(w)
+
+
 def test_int4_head_dim_64_is_rejected():
     """INT4 caches are laid out for head_dim 128 only; d = 64 fails before any launch."""
     w = W.custom(torch.float16, "f16", [20], 4, 4, 64, 16, name="i4-d64")
