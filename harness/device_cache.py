@@ -32,6 +32,7 @@ def poison_mask(w):
     mask = W.unused_slot_mask(w)
     if w.appends:
         slots = w.append_slots()
+        slots = slots[slots >= 0]          # empty sequences append nothing
         mask[slots // w.block_size, slots % w.block_size] = True
     return mask
 

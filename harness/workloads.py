@@ -82,10 +82,11 @@ class Workload:
 
     def append_slots(self):
         """int64 [B]: pool slot of each sequence's newest token (position ctx - 1),
-        = physical block * block_size + offset."""
+        = physical block * block_size + offset; -1 for an empty sequence."""
         pos = self.context_lens.astype(np.int64) - 1
-        phys = self.block_tables[np.arange(self.batch), pos // self.block_size].astype(np.int64)
-        return phys * self.block_size + pos % self.block_size
+        phys = self.block_tables[np.arange(self.batch), np.maximum(pos, 0) // self.block_size]
+        slots = phys.astype(np.int64) * self.block_size + np.maximum(pos, 0) % self.block_size
+        return np.where(pos >= 0, slots, -1)   # (an empty sequence appends nothing)
 
 
 def deal_blocks(context_lens, block_size, num_blocks, seed=1):

@@ -110,8 +110,9 @@ class OracleSide:
         ks, vs = scales
         if w.appends:
             pos = self.context_lens.astype(np.int64) - 1
+            # (an empty sequence appends nothing: slot -1, which the append skips)
             slots = np.array([oracle.paging.slot_of(self.tables[i], int(pos[i]), self.block_size)
-                              for i in range(len(seqs))], dtype=np.int64)
+                              if pos[i] >= 0 else -1 for i in range(len(seqs))], dtype=np.int64)
             nk, nv = case.new_k.cpu()[seqs], case.new_v.cpu()[seqs]
             k, v, ks, vs = oracle.append.append_expected(
                 k, v, storage(nk), storage(nv), slots, self.block_size, self.fmt, ks, vs,

@@ -273,6 +273,15 @@ def test_int4_many_units(q_dtype):
     run_and_check(w)
 
 
+@pytest.mark.parametrize("batch", [512, 513])
+def test_int4_instance_boundary(batch):
+    """512 units take INT4's deeper instance, 513 the other: both sides of the
+    switch, one KV head per sequence, short ragged contexts."""
+    ctx = [int(c) for c in np.random.default_rng(batch).integers(0, 70, size=batch)]
+    w = W.custom(torch.float16, "i4", ctx, 2, 1, 128, 16, appends=True, name=f"i4-units-{batch}")
+    run_and_check(w)
+
+
 def test_int4_head_dim_64_is_rejected():
     """INT4 caches are laid out for head_dim 128 only; d = 64 fails before any launch."""
     w = W.custom(torch.float16, "f16", [20], 4, 4, 64, 16, name="i4-d64")

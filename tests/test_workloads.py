@@ -1,6 +1,7 @@
 """Host logic of the input generator: block tables, slots and poison masks
 (checked against oracle.paging, which shares no code with it)."""
 import numpy as np
+import torch
 import pytest
 
 from oracle import kvsize, paging
@@ -56,6 +57,21 @@ def test_append_slots_match_oracle_slot_arithmetic(name):
     got = w.append_slots()
     for b in range(w.batch):
         assert got[b] == paging.slot_of(w.block_tables[b], int(w.context_lens[b]) - 1, w.block_size)
+
+
+def test_empty_sequences_append_nowhere():
+    """An empty sequence's append slot is -1 and poisons no pool slot.  Two empty
+    and two 48-token sequences fill a pool of exactly 6 blocks, so the poisoned
+    slots are the two appended ones and nothing else (a -1 taken as an index
+    would poison slot 15 of the pool's last block, a live middle block here)."""
+    from harness.device_cache import poison_mask
+    w = W.custom(torch.float16, "i4", [0, 48, 0, 48], 2, 1, 128, 16,
+                 pool_factor=1.0, perm_seed=1, appends=True)
+    assert w.num_blocks == 6 and w.block_tables[3, 1] == w.num_blocks - 1
+    slots = w.append_slots()
+    assert slots[0] == -1 and slots[2] == -1 and np.all(slots[[1, 3]] >= 0)
+    m = poison_mask(w)
+    assert m.sum() == 2 and m[slots[1] // 16, slots[1] % 16] and m[slots[3] // 16, slots[3] % 16]
 
 
 def test_unused_mask_counts_live_slots():
