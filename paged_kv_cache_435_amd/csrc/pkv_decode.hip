@@ -1301,8 +1301,15 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // fence makes it visible.) ----
   __syncthreads();
   __shared__ int64_t red[2][1024 / kWave];
-  __shared__ int64_t carry_items, carry_tiles;
-  __shared__ int xcd_groups[8];
+  __shared__ int64_t carry_items;
+  // Prompt-chunk groups by size: key 256 - tiles (a group holds 1 ..
+  // kPrefillItemTilesMax tiles); per key, the first free position of the order,
+  // and each wave's count of the current round.
+  static_assert(kPrefillItemTilesMax == 256, "one key per possible group size");
+  constexpr int kKeys = 256;
+  __shared__ int key_next[kKeys];
+  __shared__ int key_wave[1024 / kWave][kKeys];
+  __shared__ int rounds;                       // most groups of one virtual sequence
   const int units = a.head_tiles;
   // (contexts of the first kCtxCache virtual sequences from LDS, the rest
   // from the workspace)
@@ -1319,8 +1326,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     red[0][t / kWave] = tiles;
     red[1][t / kWave] = live;
   }
-  if (t == 0) carry_items = carry_tiles = 0;
-  if (t < 8) xcd_groups[t] = 0;
+  if (t == 0) carry_items = 0;
+  if (t == 0) rounds = 0;
+  if (t < kKeys) key_next[t] = 0;
+  for (int i = t; i < (1024 / kWave) * kKeys; i += 1024) (&key_wave[0][0])[i] = 0;
   __syncthreads();
   tiles = live = 0;
   for (int w = 0; w < 1024 / kWave; ++w) {
@@ -1334,7 +1343,6 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   const int tpi = a.prefill && live * units >= a.slots
                       ? cap
                       : plan_tpi(tiles * units, live * units, a.slots, cap);
-  const int64_t total_tiles = tiles;       // of one unit per virtual sequence
   // When every virtual sequence is one wave and one row group, the KV heads of
   // a sequence are consecutive virtual sequences with one context, hence one
   // chunk count m: their items are numbered chunk by chunk (item = F + c*Hkv +
@@ -1342,6 +1350,43 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // tiles, as in decode.  Otherwise each virtual sequence's items are
   // consecutive.
   const bool by_chunk = !a.prefill && a.head_tiles == 1 && several_groups == 0;
+  // The prompt-chunk kernel takes its groups (the units of one chunk of one
+  // virtual sequence, one workgroup each) in decreasing order of their tiles:
+  // the hardware starts workgroups in grid order as others finish and deals
+  // them round-robin over the 8 XCDs, so this is longest-first list scheduling
+  // on every XCD, with the sizes spread evenly over the XCDs.  (Left in
+  // numbering order, the longest sequences' groups filled whole XCDs and
+  // finished one round after the rest.)  Groups of one size keep numbering
+  // order, so the KV heads of one row group sit side by side and, with as many
+  // KV heads as XCDs, each XCD reads one head's K/V.  A stable counting sort:
+  // the sizes first, then the groups placed round by round below.
+  const bool order_groups = a.prefill && a.group_order != nullptr;
+  auto group_tiles = [](int n, int m, int c) {
+    return (int)((int64_t)(c + 1) * n / m - (int64_t)c * n / m);
+  };
+  if (order_groups) {
+    int my_rounds = 0;
+    for (int v = t; v < a.batch; v += 1024) {
+      const int n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
+      const int m = (n + tpi - 1) / tpi;
+      my_rounds = m > my_rounds ? m : my_rounds;
+      for (int c = 0; c < m; ++c) {
+        int key = kKeys - group_tiles(n, m, c);
+        key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);
+        atomicAdd(&key_next[key], 1);
+      }
+    }
+    atomicMax(&rounds, my_rounds);
+    __syncthreads();
+    const int cnt0 = t < kKeys ? key_next[t] : 0;
+    int x = cnt0, y = 0, tx, ty;
+    block_scan2(x, y, wtot, tx, ty);           // (ends with a barrier)
+    if (t < kKeys) key_next[t] = x - cnt0;     // groups of larger sizes come first
+    __syncthreads();
+  }
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const uint64_t below = (1ull << lane) - 1;
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
     int m = 0, n = 0;
@@ -1350,24 +1395,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       m = (n + tpi - 1) / tpi;
     }
     const int cnt = m * units;
-    int inc_items = cnt, inc_tiles = n, tot_items = 0, tot_tiles = 0;
-    block_scan2(inc_items, inc_tiles, wtot, tot_items, tot_tiles);
-    // Groups (the units of one chunk: one workgroup of the prompt-chunk
-    // kernel, the only one that reads these ranges) to XCDs: group = chunk c
-    // of v, weighted by its tiles; XCD x takes the groups whose middle tile
-    // falls in the x-th eighth of all tiles (monotone in the group number, so
-    // counts give the ranges).
-    if (a.prefill && v < a.batch && total_tiles > 0) {
-      const int64_t t0 = carry_tiles + inc_tiles - n;
-      for (int c = 0; c < m; ++c) {
-        const int64_t cs = (int64_t)c * n / m, ce = (int64_t)(c + 1) * n / m;
-        int64_t x = (8 * (2 * (t0 + cs) + (ce - cs))) / (2 * total_tiles);
-        x = x > 7 ? 7 : x;
-        atomicAdd(&xcd_groups[x], 1);
-      }
-    }
+    int inc_items = cnt, unused = 0, tot_items = 0, unused_tot = 0;
+    block_scan2(inc_items, unused, wtot, tot_items, unused_tot);
+    int64_t first = 0;
     if (v < a.batch) {
-      int64_t first = carry_items + inc_items - cnt;
+      first = carry_items + inc_items - cnt;
       int64_t step = 1;
       if (by_chunk) {
         // (the scan gave F + g*m; the sequence's group starts at F)
@@ -1383,23 +1415,50 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
       for (int i = 0; i < cnt && first + i * step < a.map_cap; ++i) a.item_vseq[first + i * step] = v;
     }
-    __syncthreads();
-    if (t == 0) {
-      carry_items += tot_items;
-      carry_tiles += tot_tiles;
+    if (order_groups) {
+      // Round c places chunk c of every virtual sequence of this block: the
+      // group's rank among the round's groups of its size comes from ballots
+      // (lanes of equal key, in lane order) and the counts of the waves before.
+      for (int c = 0; c < rounds; ++c) {
+        const bool has = v < a.batch && c < m;
+        int key = has ? kKeys - group_tiles(n, m, c) : 0;
+        key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (tiles <= tpi <= 256)
+        uint64_t peers = __builtin_amdgcn_ballot_w64(has);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+          const uint64_t on = __builtin_amdgcn_ballot_w64(((key >> bit) & 1) != 0);
+          peers &= ((key >> bit) & 1) ? on : ~on;
+        }
+        if (has && (peers & below) == 0) key_wave[wave][key] = __builtin_popcountll(peers);
+        __syncthreads();
+        if (has) {
+          int pos = key_next[key] + __builtin_popcountll(peers & below);
+          for (int w = 0; w < wave; ++w) pos += key_wave[w][key];
+          if (pos < a.group_cap) a.group_order[pos] = (int32_t)(first / units + c);
+        }
+        __syncthreads();
+        if (t < kKeys) {
+          int sum = 0;
+          for (int w = 0; w < 1024 / kWave; ++w) {
+            sum += key_wave[w][t];
+            key_wave[w][t] = 0;
+          }
+          key_next[t] += sum;
+        }
+        __syncthreads();
+      }
     }
+    __syncthreads();
+    if (t == 0) carry_items += tot_items;
     __syncthreads();
   }
   if (t == 0) {
     // (the host sizes the map for the most items any plan makes)
     a.plan_info[0] = carry_items < a.map_cap ? carry_items : a.map_cap;
     a.plan_info[1] = tpi;
-    int64_t f = 0;                         // first group of each XCD, and the end
-    for (int x = 0; x < 8; ++x) {
-      a.plan_info[2 + x] = f;
-      f += xcd_groups[x];
-    }
-    a.plan_info[10] = f;
+    // (groups of the prompt-chunk kernel: whole workgroups of items)
+    const int64_t groups = carry_items / units;
+    a.plan_info[10] = groups < a.group_cap ? groups : a.group_cap;
     a.plan_info[11] = by_chunk ? 1 : 0;
   }
 }

@@ -96,7 +96,10 @@ struct DecodeArgs {
   int32_t q_rows;              // query rows (tokens) in q and out
   int32_t wave_rows;           // (query token, head) rows per wave: 16 x row tiles
   // The plan of a multi-query call, made by its prep kernel.
-  int64_t* plan_info;          // [items, tiles per item, first group of XCD 0..7, groups, by-chunk numbering]
+  int64_t* plan_info;          // [0] items, [1] tiles per item, [10] prompt-chunk groups,
+                               // [11] by-chunk numbering
+  int32_t* group_order;        // prompt-chunk groups, longest first (multi_prep_kernel)
+  int64_t group_cap;           // entries of group_order
   int32_t* vseq_first;         // first item of each virtual sequence
   int32_t* vseq_m;             // items (chunks of its context) per row tile
   int32_t* item_vseq;          // virtual sequence of each item

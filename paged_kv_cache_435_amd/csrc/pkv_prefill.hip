@@ -260,13 +260,17 @@ __device__ __forceinline__ void prefill_group(
   // domain), acc = unnormalised O^T and lsum = the sum of those P, from one
   // more MFMA against ones (so it adds exactly the rounded P of the PV
   // product).  The reference moves only when a row's max passes it by more
-  // than 2^kLazy, so P <= 2^kLazy and most steps rescale nothing; the
-  // normalised result is the same whichever reference is used.
+  // than kLazy (log2 units), so P <= 2^kLazy and most steps rescale nothing;
+  // the normalised result is the same whichever reference is used.  The test
+  // is made on each lane's own scores against thr = (m_run + kLazy) / kf, a
+  // raw-score bound (kf > 0), so the row's max over lanes is taken only on the
+  // steps that move the reference.  mref: m_run kept finite for the
+  // exponentials.
   constexpr float kLazy = 8.0f;
   f32x4 acc[RT][NC];
   f32x4 lsum[RT];
   f32x4 accp[RT];                          // offset codes: sum of the P fed to PV
-  float m_run[RT];
+  float m_run[RT], thr[RT], mref[RT];
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
 #pragma unroll
@@ -274,6 +278,8 @@ __device__ __forceinline__ void prefill_group(
     lsum[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     accp[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = -__builtin_inff();
+    thr[k] = -__builtin_inff();
+    mref[k] = -3.402823466e38f;
   }
 
   // ---- global -> registers -> LDS.  Thread tid's load j of a step is the
@@ -408,10 +414,11 @@ __device__ __forceinline__ void prefill_group(
     // V operands, read now so their latency hides behind the softmax.  Lane
     // 16 c16 + r16 of a V group holds, for d = 16 nc + r16, tokens
     // 4 c16 .. 4 c16 + 3 (8 bytes per chunk nc); the operand of chunk nc is
-    // group 0's 8 bytes then group 1's, each read straight into its registers
-    // (the first halves of all chunks, then the second halves: the empty asm
-    // statement keeps the two halves of one 16-byte slot from being read as
-    // one and copied apart).
+    // group 0's 8 bytes then group 1's, read straight into its registers (one
+    // two-address LDS read: the groups lie 8 x 512 bytes apart).  The empty
+    // asm statement after each operand keeps the compiler from pairing reads
+    // of different operands instead, which leaves every operand to be copied
+    // together register by register.
     // (FP8, INT8: a lane's 16 bytes hold four chunks of 4 bytes, each
     // converted to two words; the operand is group 0's pair then group 1's.)
     u32x4 va[NC];
@@ -451,8 +458,8 @@ __device__ __forceinline__ void prefill_group(
           const u32x2 v0 = *reinterpret_cast<const u32x2*>(base + 2 * GB + off);
           const u32x2 v1 = *reinterpret_cast<const u32x2*>(base + 3 * GB + off);
           va[2 * j + h] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          asm volatile("" ::: "memory");
         }
-        asm volatile("" ::: "memory");
       }
     }
 
@@ -495,19 +502,19 @@ __device__ __forceinline__ void prefill_group(
             s[k][gi][i] = ok ? s[k][gi][i] : -__builtin_inff();
           }
     }
-    float mz[RT];
+    float mx[RT];
     bool need = false;
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      const float mx = fmax2(fmax4(s[k][0][0], s[k][0][1], s[k][0][2], s[k][0][3]),
-                             fmax4(s[k][1][0], s[k][1][1], s[k][1][2], s[k][1][3]));
-      mz[k] = rows_max(mx) * kf;
-      need = need || mz[k] > m_run[k] + kLazy;
+      mx[k] = fmax2(fmax4(s[k][0][0], s[k][0][1], s[k][0][2], s[k][0][3]),
+                    fmax4(s[k][1][0], s[k][1][1], s[k][1][2], s[k][1][3]));
+      need = need || mx[k] > thr[k];
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float rkf = 1.0f / kf;
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        const float m_new = fmax2(m_run[k], mz[k]);
+        const float m_new = fmax2(m_run[k], rows_max(mx[k]) * kf);
         // (a row that has seen no token keeps -inf and zeros)
         const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
 #pragma unroll
@@ -515,20 +522,21 @@ __device__ __forceinline__ void prefill_group(
         lsum[k] *= alpha;
         if constexpr (offset) accp[k] *= alpha;
         m_run[k] = m_new;
+        thr[k] = (m_new + kLazy) * rkf;
+        // (a row that has seen no token: every score is -inf, and the finite
+        // reference keeps exp2 at 0 rather than NaN)
+        mref[k] = fmax2(m_new, -3.402823466e38f);
       }
     }
     u32x4 pb[RT];
 #pragma unroll
     for (int k = 0; k < RT; ++k) {
-      // (a row that has seen no token: every score is -inf, and the finite
-      // reference keeps exp2 at 0 rather than NaN)
-      const float mref = fmax2(m_run[k], -3.402823466e38f);
       float p[8];
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kf, -mref));
+          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kf, -mref[k]));
       pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
       if constexpr (i8) {
@@ -641,12 +649,11 @@ __device__ __forceinline__ void prefill_group(
 }
 
 // Slots (resident waves) the plan is made for: whole workgroups per CU.
-// The groups of the plan go to the 8 XCDs in contiguous ranges of near-equal
-// tiles (workgroups go round-robin over the XCDs, so blockIdx % 8 is the XCD;
-// the ranges were cut by multi_prep_kernel): each XCD's L2 serves few
-// sequences' K/V, and no XCD is left with the longest contexts.  A workgroup
-// takes every S-th group of its XCD's range (S workgroups per XCD); the
-// hardware starts workgroups as others finish, which evens out the rest.
+// Workgroup k takes the k-th group of multi_prep_kernel's order, longest
+// first: the hardware deals workgroups round-robin over the 8 XCDs and starts
+// each XCD's next one as another finishes, so every XCD runs a longest-first
+// schedule over an even share of the sizes.  (The grid is the host's bound on
+// the groups; workgroups past the plan's count return at once.)
 template <int QT, int KV, int D, int BS>
 __global__ __launch_bounds__(64 * kPrefillWaves)
 __attribute__((amdgpu_waves_per_eu(PKV_PREFILL_WAVES_PER_EU)))
@@ -654,11 +661,12 @@ void prefill_kernel(DecodeArgs a) {
   using Sh = PrefillShape<KV, D>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[Sh::NB][Sh::STEP];   // [K g0][K g1][V g0][V g1]
   __shared__ __attribute__((aligned(16))) float lds_sc[Sh::NB][Sh::SCW][64];   // INT8 row scales
-  const int x = blockIdx.x % 8;
-  const int64_t per_xcd = gridDim.x / 8;
-  const int64_t hi = a.plan_info[3 + x];
-  for (int64_t grp = a.plan_info[2 + x] + blockIdx.x / 8; grp < hi; grp += per_xcd)
-    prefill_group<QT, KV, D, BS>(a, grp * kPrefillWaves, lds, lds_sc);
+  const int64_t groups = a.plan_info[10];
+  const int64_t items = planned_items(a);   // (the item map's entries)
+  for (int64_t k = blockIdx.x; k < groups; k += gridDim.x) {
+    const int64_t item0 = (int64_t)a.group_order[k] * kPrefillWaves;
+    if (item0 + kPrefillWaves <= items) prefill_group<QT, KV, D, BS>(a, item0, lds, lds_sc);
+  }
 }
 
 template <int QT, int KV, int D, int BS>

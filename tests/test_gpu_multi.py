@@ -200,6 +200,21 @@ def test_prompt_chunk_on_a_long_context_is_split_and_merged():
     run_multi(w, [64])
 
 
+def test_prompt_chunks_of_mixed_lengths():
+    """512-token chunks at GQA-8 over contexts of 9,000, 5,000, 300 and 4,500
+    tokens: 1,024 virtual sequences, enough to fill the GPU, so items take whole
+    contexts up to 256 tiles and the longest rows' contexts are cut into 2 or 3
+    items.  The workgroups take the groups longest first, which interleaves
+    sequences, row groups and chunks of every size."""
+    w = W.custom(torch.float16, "f16", [9000, 5000, 300, 4500], 64, 8, 128, 16,
+                 name="prompt-mixed")
+    lens = [512] * 4
+    starts = np.concatenate([[0], np.cumsum(lens)])
+    # (the first and last 24 tokens of each checked chunk: several row groups each)
+    ends = lambda b: list(range(starts[b], starts[b] + 24)) + list(range(starts[b + 1] - 24, starts[b + 1]))
+    run_multi(w, lens, seqs_check=[0, 2, 3], rows_of=ends)
+
+
 @pytest.mark.parametrize("lens", [[1, 1, 1, 1, 1], [3, 2, 4, 1, 1]])
 def test_merge_one_round_limit(lens):
     """Items of the minimum 8 tiles: a row over a context of n tiles is merged
