@@ -18,9 +18,9 @@
 //    cache once per workgroup (16 bytes per thread and instruction, in the
 //    storage order, which is already the MFMA operand order) into LDS, and
 //    every wave reads it from there: no copy per wave through the caches.
-//    LDS is double-buffered and filled by direct global-to-LDS loads, so the
-//    next step's loads are in flight while the current one is multiplied,
-//    with no registers held for them; one barrier per step.
+//    LDS holds several steps, filled by direct global-to-LDS loads, so the
+//    next steps' loads are in flight while the current ones are multiplied,
+//    with no registers held for them; one barrier per set of steps.
 //  * A wave holds RT tiles of 16 rows: Q in registers for the whole item,
 //    S^T = K Q^T with v_mfma_f32_16x16x32_{f16,bf16} per 16 tokens, online
 //    softmax in the exp2 domain, and O^T += V^T P^T with the same 32-deep MFMA
@@ -47,12 +47,29 @@
 
 // Compile-time tuning knobs (defaults are the shipped configuration):
 //   PKV_PREFILL_WAVES_PER_EU   occupancy target of the prefill kernel
-//   PKV_PREFILL_DEPTH          LDS buffers (steps in flight + the one multiplied)
+//   PKV_PREFILL_DEPTH_2B       LDS buffers of one step each, 16-bit caches
+//   PKV_PREFILL_SYNC_2B        steps multiplied between two barriers, 16-bit
+//                              caches (the buffers go round in sets of it; the
+//                              loads of NB - SPS steps are in flight)
+//   PKV_PREFILL_DEPTH_Q, PKV_PREFILL_SYNC_Q   the same for FP8, INT8, INT4
+// (16-bit caches: 2 steps per barrier in 4 buffers, 64 KB of LDS, took the
+// f16 prompt chunk from 352 to 331 us; 1 step in 3 buffers measured the same
+// as 2 in 4 or 8, or 4 in 8, for the one-byte and INT4 caches, whose steps
+// are smaller.)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
-#ifndef PKV_PREFILL_DEPTH
-#define PKV_PREFILL_DEPTH 3
+#ifndef PKV_PREFILL_DEPTH_2B
+#define PKV_PREFILL_DEPTH_2B 4
+#endif
+#ifndef PKV_PREFILL_SYNC_2B
+#define PKV_PREFILL_SYNC_2B 2
+#endif
+#ifndef PKV_PREFILL_DEPTH_Q
+#define PKV_PREFILL_DEPTH_Q 3
+#endif
+#ifndef PKV_PREFILL_SYNC_Q
+#define PKV_PREFILL_SYNC_Q 1
 #endif
 
 namespace pkv {
@@ -64,7 +81,9 @@ struct PrefillShape {
   static constexpr int R = (int)row_bytes_of(KV, D);   // bytes per stored row
   static constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
   static constexpr int STEP = 4 * GB;             // K and V of two groups
-  static constexpr int NB = PKV_PREFILL_DEPTH;    // LDS buffers: NB - 1 steps in flight
+  static constexpr bool two_byte = KV == PKV_F16 || KV == PKV_BF16;
+  static constexpr int NB = two_byte ? PKV_PREFILL_DEPTH_2B : PKV_PREFILL_DEPTH_Q;   // LDS buffers
+  static constexpr int SPS = two_byte ? PKV_PREFILL_SYNC_2B : PKV_PREFILL_SYNC_Q;   // steps per barrier
   // INT8: each wave's copy of a step's 64 row scales (K g0, K g1, V g0, V g1)
   static constexpr int SCW = row_scaled(KV) ? kPrefillWaves : 1;
 };
@@ -103,7 +122,9 @@ __device__ __forceinline__ void prefill_group(
   static_assert(GB % 1024 == 0, "a wave's loads stay inside one group");
   constexpr int NB = PrefillShape<KV, D>::NB;
   constexpr int NLW = NLD + (i8 ? 1 : 0);   // loads per thread per step (INT8: + row scales)
-  static_assert(NB >= 2 && (NB - 2) * NLW <= 63, "vmcnt threshold");
+  constexpr int SPS = PrefillShape<KV, D>::SPS;
+  static_assert(SPS >= 1 && NB % SPS == 0 && NB >= 2 * SPS, "buffers in whole sets of SPS");
+  static_assert((NB - 2 * SPS) * NLW <= 63, "vmcnt threshold");
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);         // (uniform: keeps the load addresses scalar)
@@ -329,14 +350,15 @@ __device__ __forceinline__ void prefill_group(
                                        4, 0, 0);
     }
   };
-  // End of a step: this wave's LDS reads are done (lgkmcnt 0, so the buffer
-  // can be refilled after the barrier) and its loads of the next step have
-  // landed: all its loads, or all but the newest NB - 2 steps' (vmcnt n).
+  // End of a set of steps: this wave's LDS reads are done (lgkmcnt 0, so the
+  // buffers can be refilled after the barrier) and its loads of the next set
+  // have landed: all its loads, or all but the newest NB - 2 SPS steps'
+  // (vmcnt n).
   // The barrier carries no memory fence, which would wait for every load in
   // flight; the empty asm statements keep the compiler from moving LDS
   // accesses across it.
   auto step_barrier = [](bool steady) {
-    constexpr int n = (NB - 2) * NLW;
+    constexpr int n = (NB - 2 * SPS) * NLW;
     if (steady)
       __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));   // vmcnt(n) lgkmcnt(0)
     else
@@ -579,14 +601,14 @@ __device__ __forceinline__ void prefill_group(
       for (int k = 0; k < RT; ++k) acc[k][nc] = mfma32(va[nc], pb[k], acc[k][nc]);
   };
 
-  // ---- the step loop: loads of the next NB - 1 steps in flight while step s
-  // is multiplied; one barrier per step ----
+  // ---- the step loop: SPS steps multiplied per barrier, the loads of the
+  // next NB - SPS steps in flight meanwhile ----
   // Physical blocks of the tiles of the steps in LDS or in flight, by buffer.
   int phq0[NB], phq1[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) phq0[i] = phq1[i] = -1;
 #pragma unroll
-  for (int i = 0; i < NB - 1; ++i) {
+  for (int i = 0; i < NB - SPS; ++i) {
     if (i < nsteps) {
       step_phys(i, phq0[i], phq1[i]);
       issue(i, phq0[i], phq1[i], i);
@@ -596,23 +618,32 @@ __device__ __forceinline__ void prefill_group(
   for (int step0 = 0; step0 < nsteps; step0 += NB) {
     // (unrolled by NB so the buffer numbers are constants)
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int step = step0 + u;
-      if (step < nsteps) {
-        const int nx = step + NB - 1;              // the step loaded now, into the buffer
-        const int nb = (u + NB - 1) % NB;          // read during step - 1 (before the barrier)
-        const bool more = nx < nsteps;
-        if (more) {
-          step_phys(nx, phq0[nb], phq1[nb]);
-          issue(nx, phq0[nb], phq1[nb], nb);
+    for (int u = 0; u < NB; u += SPS) {
+      if (step0 + u < nsteps) {
+        // The set loaded now goes into the buffers read before the last
+        // barrier.
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) {
+          const int nx = step0 + u + NB - SPS + e;
+          const int nb = (u + NB - SPS + e) % NB;
+          if (nx < nsteps) {
+            step_phys(nx, phq0[nb], phq1[nb]);
+            issue(nx, phq0[nb], phq1[nb], nb);
+          }
         }
-        if (wave_live) {
-          f32x4 sc[RT][2];
-          qk(u, sc);
-          finish(!(2 * step + 2 <= nfull && phq0[u] >= 0 && phq1[u] >= 0), step, u, phq0[u],
-                 phq1[u], sc);
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) {
+          const int step = step0 + u + e;
+          if (wave_live && step < nsteps) {
+            f32x4 sc[RT][2];
+            qk(u + e, sc);
+            finish(!(2 * step + 2 <= nfull && phq0[u + e] >= 0 && phq1[u + e] >= 0), step, u + e,
+                   phq0[u + e], phq1[u + e], sc);
+          }
         }
-        step_barrier(more);                        // step + 1 has landed everywhere
+        // (the next set has landed everywhere: all but the newest NB - 2 SPS
+        // steps' loads, when every one of them was issued, else all loads)
+        step_barrier(step0 + u + NB - 1 < nsteps);
       }
     }
   }
