@@ -1361,7 +1361,14 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // KV heads as XCDs, each XCD reads one head's K/V.  A stable counting sort:
   // the sizes first, then the groups placed round by round below.
   const bool order_groups = a.prefill && a.group_order != nullptr;
+  // Tiles of chunk c of a unit's n tiles cut into m chunks: floor((c+1)n/m) -
+  // floor(cn/m), = q + floor((c+1)r/m) - floor(cr/m) with n = qm + r, in 32-bit
+  // arithmetic while (c+1)r < 2^32 (m <= 65535), else in 64-bit.
   auto group_tiles = [](int n, int m, int c) {
+    if (m <= 65535) {
+      const uint32_t um = (uint32_t)m, q = (uint32_t)n / um, r = (uint32_t)n - q * um;
+      return (int)(q + ((uint32_t)(c + 1) * r) / um - ((uint32_t)c * r) / um);
+    }
     return (int)((int64_t)(c + 1) * n / m - (int64_t)c * n / m);
   };
   if (order_groups) {
@@ -1434,7 +1441,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
         if (has) {
           int pos = key_next[key] + __builtin_popcountll(peers & below);
           for (int w = 0; w < wave; ++w) pos += key_wave[w][key];
-          if (pos < a.group_cap) a.group_order[pos] = (int32_t)(first / units + c);
+          // (first < 2^31: items are counted in int32 on the host)
+          if (pos < a.group_cap) a.group_order[pos] = (int32_t)((int32_t)first / units + c);
         }
         __syncthreads();
         if (t < kKeys) {
