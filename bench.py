@@ -50,6 +50,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup-ms", type=float, default=None,
+                    help="after the warmup steps, keep warming up until this much wall time "
+                         "has passed (default: 300 for --multi, 0 otherwise): the compute "
+                         "clock rises over tens of ms of sustained work, which moves "
+                         "MFMA-bound calls by ~15 %% and HBM-bound ones by under 1 %%")
     ap.add_argument("--workload", default="llama70b_gqa8")
     ap.add_argument("--block-size", type=int, default=None, help="llama70b_fp8 only: 16 or 256")
     ap.add_argument("--layers", type=int, default=None,
@@ -410,6 +415,21 @@ def bench_blocks(args):
           flush=True)
 
 
+def warm_until(args, step, default_ms):
+    """More untimed steps until --warmup-ms (else default_ms) of wall time has
+    passed since the first of them, synchronizing every few steps.  Returns the
+    wall time of the whole warmup in ms."""
+    import torch
+    target = (args.warmup_ms if args.warmup_ms is not None else default_ms) / 1e3
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < target:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
+
+
 def bench_multi(args, name):
     """Multi-token query row: one step appends the new tokens' K/V rows (every
     sequence's L new tokens, written to their slots) and runs
@@ -462,7 +482,7 @@ def bench_multi(args, name):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    warm_ms = warm_until(args, step, 300.0)
     events = LaunchEvents(args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -492,6 +512,7 @@ def bench_multi(args, name):
     print(json.dumps({
         "metric": "multi-token query attention: query tokens/s, 1 GPU", "value": T * args.steps / elapsed,
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": elapsed / args.steps * 1e3, "higher_is_better": True,
         "dtype": "f16" if w.kv_format == "f16" else f"f16 (KV {w.kv_format})",
         "data": "synthetic",
@@ -581,7 +602,7 @@ def main():
     log(f"[bench] warmup {args.warmup} steps (workspace {ws_bytes} B)")
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+    warm_ms = warm_until(args, step, 0.0)
 
     events = LaunchEvents(args.steps * len(cases))
     log(f"[bench] timing {args.steps} steps")
@@ -650,6 +671,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_ms": round(warm_ms, 1),
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",

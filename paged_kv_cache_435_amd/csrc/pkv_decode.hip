@@ -1255,7 +1255,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       const int64_t v64 = (int64_t)base + e;
       if (v64 < 0 || v64 >= a.batch) break;
       const int v = (int)v64;
-      int lo = 0, hi = 1023;                 // first sequence whose scan passes e
+      // first sequence whose scan passes e (among this block's sequences)
+      int lo = 0, hi = batch_real - b0 - 1 < 1023 ? batch_real - b0 - 1 : 1023;
       while (lo < hi) {
         const int mid = (lo + hi) >> 1;
         if (scan[mid] > e) hi = mid; else lo = mid + 1;
@@ -1371,16 +1372,38 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     }
     return (int)((int64_t)(c + 1) * n / m - (int64_t)c * n / m);
   };
+  const int lane = t & (kWave - 1);
+  const int wave = t / kWave;
+  const uint64_t below = (1ull << lane) - 1;
+  // Lanes of this wave whose key equals this lane's, among the lanes in
+  // `peers` (8 ballots over the bits of the key).
+  auto same_key = [](uint64_t peers, int key) {
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t on = __builtin_amdgcn_ballot_w64(((key >> bit) & 1) != 0);
+      peers &= ((key >> bit) & 1) ? on : ~on;
+    }
+    return peers;
+  };
   if (order_groups) {
+    // Groups per size: one LDS atomic per (wave, size), by the size's first
+    // lane (the sizes of many groups are equal: per-lane atomics on one
+    // address serialise).
     int my_rounds = 0;
-    for (int v = t; v < a.batch; v += 1024) {
-      const int n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
-      const int m = (n + tpi - 1) / tpi;
+    for (int v0 = 0; v0 < a.batch; v0 += 1024) {
+      const int v = v0 + t;
+      int n = 0, m = 0;
+      if (v < a.batch) {
+        n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
+        m = (n + tpi - 1) / tpi;
+      }
       my_rounds = m > my_rounds ? m : my_rounds;
-      for (int c = 0; c < m; ++c) {
-        int key = kKeys - group_tiles(n, m, c);
+      for (int c = 0; __builtin_amdgcn_ballot_w64(c < m) != 0; ++c) {
+        const bool has = c < m;
+        int key = has ? kKeys - group_tiles(n, m, c) : 0;
         key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);
-        atomicAdd(&key_next[key], 1);
+        const uint64_t peers = same_key(__builtin_amdgcn_ballot_w64(has), key);
+        if (has && (peers & below) == 0) atomicAdd(&key_next[key], __builtin_popcountll(peers));
       }
     }
     atomicMax(&rounds, my_rounds);
@@ -1391,9 +1414,6 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     if (t < kKeys) key_next[t] = x - cnt0;     // groups of larger sizes come first
     __syncthreads();
   }
-  const int lane = t & (kWave - 1);
-  const int wave = t / kWave;
-  const uint64_t below = (1ull << lane) - 1;
   for (int v0 = 0; v0 < a.batch; v0 += 1024) {
     const int v = v0 + t;
     int m = 0, n = 0;
@@ -1430,27 +1450,24 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
         const bool has = v < a.batch && c < m;
         int key = has ? kKeys - group_tiles(n, m, c) : 0;
         key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (tiles <= tpi <= 256)
-        uint64_t peers = __builtin_amdgcn_ballot_w64(has);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-          const uint64_t on = __builtin_amdgcn_ballot_w64(((key >> bit) & 1) != 0);
-          peers &= ((key >> bit) & 1) ? on : ~on;
-        }
+        const uint64_t peers = same_key(__builtin_amdgcn_ballot_w64(has), key);
         if (has && (peers & below) == 0) key_wave[wave][key] = __builtin_popcountll(peers);
         __syncthreads();
         if (has) {
+          // (the 16 reads are independent: unrolled, they are in flight together)
           int pos = key_next[key] + __builtin_popcountll(peers & below);
-          for (int w = 0; w < wave; ++w) pos += key_wave[w][key];
+#pragma unroll
+          for (int w = 0; w < 1024 / kWave; ++w) pos += w < wave ? key_wave[w][key] : 0;
           // (first < 2^31: items are counted in int32 on the host)
           if (pos < a.group_cap) a.group_order[pos] = (int32_t)((int32_t)first / units + c);
         }
         __syncthreads();
         if (t < kKeys) {
           int sum = 0;
-          for (int w = 0; w < 1024 / kWave; ++w) {
-            sum += key_wave[w][t];
-            key_wave[w][t] = 0;
-          }
+#pragma unroll
+          for (int w = 0; w < 1024 / kWave; ++w) sum += key_wave[w][t];
+#pragma unroll
+          for (int w = 0; w < 1024 / kWave; ++w) key_wave[w][t] = 0;
           key_next[t] += sum;
         }
         __syncthreads();

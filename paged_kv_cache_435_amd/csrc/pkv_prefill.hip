@@ -495,14 +495,20 @@ __device__ __forceinline__ void prefill_group(
     f32x4 vr[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};   // INT8: 1 / s_v
     if constexpr (i8) {
       kf = 1.0f;
+      // The step's 64 row scales (this wave's own copy) become their
+      // reciprocals in place, one per lane; each lane then reads the 16 it
+      // uses (its four tokens of each group, K and V).  (A wave's LDS
+      // accesses complete in order: the reads see the writes.)
+      float* sc = &lds_sc[buf][wave][0];
+      sc[lane] = __builtin_amdgcn_rcpf(sc[lane]);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-        const f32x4 ks = *reinterpret_cast<const f32x4*>(&lds_sc[buf][wave][16 * gi + 4 * c16]);
-        const f32x4 vs = *reinterpret_cast<const f32x4*>(&lds_sc[buf][wave][32 + 16 * gi + 4 * c16]);
+        const f32x4 ks = *reinterpret_cast<const f32x4*>(&sc[16 * gi + 4 * c16]);
+        const f32x4 vs = *reinterpret_cast<const f32x4*>(&sc[32 + 16 * gi + 4 * c16]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float kr = __builtin_amdgcn_rcpf(ks[i]);
-          vr[gi][i] = __builtin_amdgcn_rcpf(vs[i]);
+          const float kr = ks[i];
+          vr[gi][i] = vs[i];
 #pragma unroll
           for (int k = 0; k < RT; ++k) {
             if constexpr (offset)
