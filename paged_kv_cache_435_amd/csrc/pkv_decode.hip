@@ -1170,21 +1170,41 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
     merge_row<QT, D, 4>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
+// round trips): Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4,
+// 8; a source before the row's first lane reads 0), then lane 15 of rows 0
+// and 2 added to rows 1 and 3 (row_bcast 15), then lane 31 to rows 2 and 3
+// (row_bcast 31).  Rows left out by the row mask keep their value.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return x;
+}
+
+// Largest value over the 64 lanes of a wave, the same DPP pattern as the scan.
+__device__ __forceinline__ int wave_max(int x) {
+  auto mx = [](int p, int q) { return p > q ? p : q; };
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x111, 0xf, 0xf, false));   // row_shr:1
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x112, 0xf, 0xf, false));   // row_shr:2
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x114, 0xf, 0xf, false));   // row_shr:4
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x118, 0xf, 0xf, false));   // row_shr:8
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x142, 0xa, 0xf, false));   // row_bcast:15
+  x = mx(x, __builtin_amdgcn_update_dpp(x, x, 0x143, 0xc, 0xf, false));   // row_bcast:31
+  return __builtin_amdgcn_readlane(x, kWave - 1);
+}
+
 // Inclusive prefix sums of two ints per thread over a 1024-thread block:
-// shuffle scans within each wave, then the 16 wave totals (two barriers in
-// all); tot_x, tot_y get the block totals.  wtot: LDS, [16][2].
+// scans within each wave, then the 16 wave totals (two barriers in all);
+// tot_x, tot_y get the block totals.  wtot: LDS, [16][2].
 __device__ __forceinline__ void block_scan2(int& x, int& y, int (*wtot)[2], int& tot_x, int& tot_y) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int xs = __shfl_up(x, o, kWave);
-    const int ys = __shfl_up(y, o, kWave);
-    if (lane >= o) {
-      x += xs;
-      y += ys;
-    }
-  }
+  x = wave_incl_scan(x);
+  y = wave_incl_scan(y);
   if (lane == kWave - 1) {
     wtot[w][0] = x;
     wtot[w][1] = y;
@@ -1207,6 +1227,12 @@ __device__ __forceinline__ void block_scan2(int& x, int& y, int (*wtot)[2], int&
   __syncthreads();   // (wtot is reused by the next call)
 }
 
+// x / d for x >= 0 and a uniform d > 0, by a shift when d is a power of two
+// (sh = log2 d, else -1).  The prep kernel runs on one compute unit with four
+// waves per SIMD, so every vector instruction costs; integer division is tens.
+__device__ __forceinline__ int div_by(int x, int d, int sh) { return sh >= 0 ? x >> sh : x / d; }
+__device__ __forceinline__ int log2_if_pow2(int d) { return (d & (d - 1)) == 0 ? __builtin_ctz(d) : -1; }
+
 // Virtual sequences of a multi-token call (one workgroup): for sequence b, each
 // KV head (head-major, so the workgroups running together on an XCD share one
 // head's K/V in its L2) times each group of row tiles, with the context the
@@ -1224,6 +1250,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   __shared__ int wtot[1024 / kWave][2];
   const int t = threadIdx.x;
   const int G = a.num_q_heads / a.num_kv_heads;
+  const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
+  const int g_sh = log2_if_pow2(G), rows_sh = log2_if_pow2(ROWS);
   if (t == 0) carry = several_groups = 0;
   __syncthreads();
   for (int b0 = 0; b0 < batch_real; b0 += 1024) {
@@ -1239,10 +1267,12 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     }
     seq_len[t] = L;
     seq_cx[t] = cx;
-    const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
     // (L * G < 2^31: the host limits q_rows * G)
-    if ((L * G + ROWS - 1) / ROWS > 1) atomicOr(&several_groups, 1);
-    const int64_t n64 = (int64_t)a.num_kv_heads * ((L * G + ROWS - 1) / ROWS);
+    const int ng = div_by(L * G + ROWS - 1, ROWS, rows_sh);   // row groups of the sequence
+    // (one atomic per wave: an atomic on one LDS address from many lanes is
+    // turned into a loop over the lanes)
+    if (__builtin_amdgcn_ballot_w64(ng > 1) != 0 && (t & (kWave - 1)) == 0) atomicOr(&several_groups, 1);
+    const int64_t n64 = (int64_t)a.num_kv_heads * ng;
     // (KV head, row group) entries; past a.batch (the host's bound) nothing is
     // written, so the count is capped there
     int n = (int)(n64 < a.batch ? n64 : a.batch);
@@ -1263,16 +1293,14 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
       const int bb = b0 + lo;
       const int Lb = seq_len[lo];
-      const int ng = (Lb * G + a.wave_rows * a.head_tiles - 1) /
-                     (a.wave_rows * a.head_tiles);   // row groups of the sequence
+      const int ng = div_by(Lb * G + ROWS - 1, ROWS, rows_sh);   // row groups of the sequence
       const int local = e - (lo > 0 ? scan[lo - 1] : 0);   // KV head major, then row group
-      const int gg = local / ng;
-      const int rt = local % ng;
+      const int gg = ng == 1 ? local : local / ng;
+      const int rt = local - gg * ng;
       const int ctx = seq_cx[lo];
-      const int ROWS = a.wave_rows * a.head_tiles;
       int last = ROWS * rt + ROWS - 1;
       last = last < Lb * G - 1 ? last : Lb * G - 1;
-      int c = ctx - Lb + last / G + 1;
+      int c = ctx - Lb + div_by(last, G, g_sh) + 1;
       c = c < 0 ? 0 : c;
       vctx[v] = c;
       if (v < kCtxCache) vctx_s[v] = c;
@@ -1310,7 +1338,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   constexpr int kKeys = 256;
   __shared__ int key_next[kKeys];
   __shared__ int key_wave[1024 / kWave][kKeys];
-  __shared__ int rounds;                       // most groups of one virtual sequence
+  __shared__ int wave_rounds[1024 / kWave];    // most groups of one virtual sequence, per wave
   const int units = a.head_tiles;
   // (contexts of the first kCtxCache virtual sequences from LDS, the rest
   // from the workspace)
@@ -1328,7 +1356,6 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     red[1][t / kWave] = live;
   }
   if (t == 0) carry_items = 0;
-  if (t == 0) rounds = 0;
   if (t < kKeys) key_next[t] = 0;
   for (int i = t; i < (1024 / kWave) * kKeys; i += 1024) (&key_wave[0][0])[i] = 0;
   __syncthreads();
@@ -1362,10 +1389,12 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // KV heads as XCDs, each XCD reads one head's K/V.  A stable counting sort:
   // the sizes first, then the groups placed round by round below.
   const bool order_groups = a.prefill && a.group_order != nullptr;
+  const int tpi_sh = log2_if_pow2(tpi);   // (the prompt-chunk kernel's tpi is 256)
   // Tiles of chunk c of a unit's n tiles cut into m chunks: floor((c+1)n/m) -
   // floor(cn/m), = q + floor((c+1)r/m) - floor(cr/m) with n = qm + r, in 32-bit
   // arithmetic while (c+1)r < 2^32 (m <= 65535), else in 64-bit.
   auto group_tiles = [](int n, int m, int c) {
+    if (m == 1) return n;
     if (m <= 65535) {
       const uint32_t um = (uint32_t)m, q = (uint32_t)n / um, r = (uint32_t)n - q * um;
       return (int)(q + ((uint32_t)(c + 1) * r) / um - ((uint32_t)c * r) / um);
@@ -1385,6 +1414,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     }
     return peers;
   };
+  int rounds = 0;   // most groups of one virtual sequence (order_groups only)
   if (order_groups) {
     // Groups per size: one LDS atomic per (wave, size), by the size's first
     // lane (the sizes of many groups are equal: per-lane atomics on one
@@ -1395,7 +1425,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       int n = 0, m = 0;
       if (v < a.batch) {
         n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
-        m = (n + tpi - 1) / tpi;
+        m = div_by(n + tpi - 1, tpi, tpi_sh);
       }
       my_rounds = m > my_rounds ? m : my_rounds;
       for (int c = 0; __builtin_amdgcn_ballot_w64(c < m) != 0; ++c) {
@@ -1406,8 +1436,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
         if (has && (peers & below) == 0) atomicAdd(&key_next[key], __builtin_popcountll(peers));
       }
     }
-    atomicMax(&rounds, my_rounds);
+    my_rounds = wave_max(my_rounds);
+    if (lane == 0) wave_rounds[wave] = my_rounds;
     __syncthreads();
+#pragma unroll
+    for (int w = 0; w < 1024 / kWave; ++w) rounds = wave_rounds[w] > rounds ? wave_rounds[w] : rounds;
     const int cnt0 = t < kKeys ? key_next[t] : 0;
     int x = cnt0, y = 0, tx, ty;
     block_scan2(x, y, wtot, tx, ty);           // (ends with a barrier)
@@ -1419,7 +1452,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     int m = 0, n = 0;
     if (v < a.batch) {
       n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
-      m = (n + tpi - 1) / tpi;
+      m = div_by(n + tpi - 1, tpi, tpi_sh);
     }
     const int cnt = m * units;
     int inc_items = cnt, unused = 0, tot_items = 0, unused_tot = 0;
