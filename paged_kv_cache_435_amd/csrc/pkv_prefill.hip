@@ -125,6 +125,7 @@ __device__ __forceinline__ void prefill_group(
   constexpr int SPS = PrefillShape<KV, D>::SPS;
   static_assert(SPS >= 1 && NB % SPS == 0 && NB >= 2 * SPS, "buffers in whole sets of SPS");
   static_assert((NB - 2 * SPS) * NLW <= 63, "vmcnt threshold");
+  static_assert(BS >= 16 && (BS & (BS - 1)) == 0, "block sizes are powers of two, >= 16");
 
   const int tid = threadIdx.x;
   const int wave = uni(tid >> 6);         // (uniform: keeps the load addresses scalar)
@@ -178,29 +179,20 @@ __device__ __forceinline__ void prefill_group(
   const int full_end = p_min < t_end ? p_min + 1 : t_end;
   const int nfull = full_end > t_begin ? (full_end - t_begin) >> 4 : 0;   // whole tiles
 
-  // Block-table entries of the item, one per lane per register.
-  constexpr int NREG = (kPrefillItemTilesMax * kTileTokens / BS + (BS > kTileTokens ? 1 : 0) + 63) / 64;
-  const int first_blk = t_begin / BS;
-  const int nblk = ntiles > 0 ? (t_end - 1) / BS - first_blk + 1 : 0;
-  int blk[NREG];
-#pragma unroll
-  for (int r = 0; r < NREG; ++r) {
-    const int idx = r * 64 + lane;
-    int v = -1;
-    if (idx < nblk) v = a.block_tables[(int64_t)bq * a.max_blocks_per_seq + first_blk + idx];
-    blk[r] = (v >= a.num_blocks) ? -1 : v;
-  }
-  // Physical block of a tile (-1: outside the pool; its tokens are skipped).
-  auto tile_phys = [&](int tile) -> int {
-    const int rel = (t_begin + tile * 16) / BS - first_blk;
-    int v = __builtin_amdgcn_readlane(blk[0], rel & 63);
-#pragma unroll
-    for (int r = 1; r < NREG; ++r) {
-      const int w = __builtin_amdgcn_readlane(blk[r], rel & 63);
-      v = (rel >> 6) == r ? w : v;
-    }
-    return v;
+  // Physical block of a tile (-1: outside the pool; its tokens are skipped),
+  // read by a scalar load from the sequence's block table: one instruction
+  // on the step's scalar path, where the wave's registers of entries took
+  // four lane reads and a choice among them.  (The table is read-only here.)
+  using ConstI32 = const __attribute__((address_space(4))) int32_t;
+  ConstI32* bt_row = (ConstI32*)(uintptr_t)(a.block_tables + (int64_t)bq * a.max_blocks_per_seq);
+  // (raw entry of a tile, clamped to the item's last tile so that the read
+  // stays in the table; phys_of checks it where it is used)
+  auto tile_entry = [&](int tile) -> int {
+    const uint32_t tc = (uint32_t)(tile < ntiles ? tile : ntiles - 1);
+    return bt_row[((uint32_t)t_begin + tc * 16u) / (uint32_t)BS];
   };
+  auto phys_of = [&](int tile, int v) { return tile < ntiles && v < a.num_blocks ? v : -1; };
+  auto tile_phys = [&](int tile) -> int { return phys_of(tile, tile_entry(tile)); };
 
   // ---- query operands (lane: row r16 of each row tile, the d positions of
   // its K chunks) ----
@@ -322,16 +314,28 @@ __device__ __forceinline__ void prefill_group(
   // item or outside the pool loads the first group of block 0 instead, which
   // the products mask like any token past the context), so a fixed vmcnt
   // threshold waits for exactly the oldest step.
+  // (Scalar work here is on the step's critical path: each part's row is
+  // formed once per step, and when a load instruction covers exactly one
+  // part, the part is a constant.)
+  constexpr bool part_per_load = 64 * W == GB / 16;
   auto issue = [&](int step, int p0, int p1, int buf) {
+    // rows of the step's two tiles (their first token); 0 for a tile past the
+    // item or outside the pool
+    // ((block, head) pairs number under 2^32: each holds at least 1 KB)
+    const int s0 = (t_begin + 32 * step) & (BS - 1);   // slot of the step's first token
+    const uint64_t row0 =
+        p0 >= 0 ? (uint64_t)((uint32_t)p0 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS + s0 : 0;
+    const uint64_t row1 =
+        p1 >= 0 ? (uint64_t)((uint32_t)p1 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS +
+                      ((s0 + 16) & (BS - 1))
+                : 0;
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int c0 = j * 64 * W + wave * 64;           // the wave's first chunk
-      const int part = c0 / (GB / 16);                 // 0 K g0, 1 K g1, 2 V g0, 3 V g1
-      const int tile = 2 * step + (part & 1);
-      const int phys = (part & 1) ? p1 : p0;
-      const int64_t row =
-          phys >= 0 ? ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS) : 0;
-      const uint8_t* src = (part < 2 ? kbase : vbase) + (uint64_t)row * R + (c0 % (GB / 16) + lane) * 16;
+      const int part = part_per_load ? j : c0 / (GB / 16);   // 0 K g0, 1 K g1, 2 V g0, 3 V g1
+      const uint64_t row = (part & 1) ? row1 : row0;
+      const int cw = part_per_load ? wave * 64 : c0 % (GB / 16);   // chunk within the part
+      const uint8_t* src = (part < 2 ? kbase : vbase) + row * R + (cw + lane) * 16;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                        (__attribute__((address_space(3))) void*)(&lds[buf][c0 * 16]),
                                        16, 0, 0);
@@ -620,6 +624,15 @@ __device__ __forceinline__ void prefill_group(
       issue(i, phq0[i], phq1[i], i);
     }
   }
+  // Block-table entries of the set loaded next, read (scalar loads) one set
+  // ahead and checked where they are used, so that the loads' latency never
+  // stands between a step and its global loads.
+  int nxt0[SPS], nxt1[SPS];
+#pragma unroll
+  for (int e = 0; e < SPS; ++e) {
+    nxt0[e] = tile_entry(2 * (NB - SPS + e));
+    nxt1[e] = tile_entry(2 * (NB - SPS + e) + 1);
+  }
   step_barrier(false);
   for (int step0 = 0; step0 < nsteps; step0 += NB) {
     // (unrolled by NB so the buffer numbers are constants)
@@ -633,9 +646,16 @@ __device__ __forceinline__ void prefill_group(
           const int nx = step0 + u + NB - SPS + e;
           const int nb = (u + NB - SPS + e) % NB;
           if (nx < nsteps) {
-            step_phys(nx, phq0[nb], phq1[nb]);
+            phq0[nb] = phys_of(2 * nx, nxt0[e]);
+            phq1[nb] = phys_of(2 * nx + 1, nxt1[e]);
             issue(nx, phq0[nb], phq1[nb], nb);
           }
+        }
+#pragma unroll
+        for (int e = 0; e < SPS; ++e) {
+          const int nn = step0 + u + NB + e;   // (loaded at the next set)
+          nxt0[e] = tile_entry(2 * nn);
+          nxt1[e] = tile_entry(2 * nn + 1);
         }
 #pragma unroll
         for (int e = 0; e < SPS; ++e) {
