@@ -186,13 +186,15 @@ __device__ __forceinline__ void prefill_group(
   using ConstI32 = const __attribute__((address_space(4))) int32_t;
   ConstI32* bt_row = (ConstI32*)(uintptr_t)(a.block_tables + (int64_t)bq * a.max_blocks_per_seq);
   // (raw entry of a tile, clamped to the item's last tile so that the read
-  // stays in the table; phys_of checks it where it is used)
+  // stays in the table; phys_of checks it where it is used.  A tile past the
+  // item thus reads a block of the item: its tokens lie past the context and
+  // are masked like any other such token.)
   auto tile_entry = [&](int tile) -> int {
     const uint32_t tc = (uint32_t)(tile < ntiles ? tile : ntiles - 1);
     return bt_row[((uint32_t)t_begin + tc * 16u) / (uint32_t)BS];
   };
-  auto phys_of = [&](int tile, int v) { return tile < ntiles && v < a.num_blocks ? v : -1; };
-  auto tile_phys = [&](int tile) -> int { return phys_of(tile, tile_entry(tile)); };
+  auto phys_of = [&](int v) { return (uint32_t)v < (uint32_t)a.num_blocks ? v : -1; };
+  auto tile_phys = [&](int tile) -> int { return phys_of(tile_entry(tile)); };
 
   // ---- query operands (lane: row r16 of each row tile, the d positions of
   // its K chunks) ----
@@ -305,8 +307,8 @@ __device__ __forceinline__ void prefill_group(
   // outside the pool).
   auto step_phys = [&](int step, int& p0, int& p1) {
     const int t0 = 2 * step;
-    p0 = t0 < ntiles ? tile_phys(t0) : -1;
-    p1 = t0 + 1 < ntiles ? tile_phys(t0 + 1) : -1;
+    p0 = tile_phys(t0);
+    p1 = tile_phys(t0 + 1);
   };
   // The loads go straight to LDS (gfx950's 16-byte global_load_lds: lane l
   // writes at the wave's LDS base + 16 l), so no registers hold the steps in
@@ -323,12 +325,10 @@ __device__ __forceinline__ void prefill_group(
     // item or outside the pool
     // ((block, head) pairs number under 2^32: each holds at least 1 KB)
     const int s0 = (t_begin + 32 * step) & (BS - 1);   // slot of the step's first token
-    const uint64_t row0 =
-        p0 >= 0 ? (uint64_t)((uint32_t)p0 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS + s0 : 0;
-    const uint64_t row1 =
-        p1 >= 0 ? (uint64_t)((uint32_t)p1 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS +
-                      ((s0 + 16) & (BS - 1))
-                : 0;
+    // (a block outside the pool, -1, loads block 0's rows instead: masked)
+    const uint32_t b0 = (uint32_t)(p0 > 0 ? p0 : 0), b1 = (uint32_t)(p1 > 0 ? p1 : 0);
+    const uint64_t row0 = (uint64_t)(b0 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS + s0;
+    const uint64_t row1 = (uint64_t)(b1 * (uint32_t)a.num_kv_heads + (uint32_t)g) * BS + ((s0 + 16) & (BS - 1));
 #pragma unroll
     for (int j = 0; j < NLD; ++j) {
       const int c0 = j * 64 * W + wave * 64;           // the wave's first chunk
@@ -343,11 +343,7 @@ __device__ __forceinline__ void prefill_group(
     if constexpr (i8) {
       // The step's row scales, 4 bytes per lane into this wave's copy: lane
       // l is token l % 16 of group (l / 16) % 2 of K (l < 32) or V.
-      const int gsel = (lane >> 4) & 1;
-      const int phys = gsel ? p1 : p0;
-      const int tile = 2 * step + gsel;
-      const int64_t row =
-          phys >= 0 ? ((int64_t)phys * a.num_kv_heads + g) * BS + ((t_begin + tile * 16) % BS) : 0;
+      const uint64_t row = ((lane >> 4) & 1) ? row1 : row0;
       const float* src = (lane < 32 ? a.k_scale : a.v_scale) + row + (lane & 15);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src),
                                        (__attribute__((address_space(3))) void*)(&lds_sc[buf][wave][0]),
@@ -646,8 +642,8 @@ __device__ __forceinline__ void prefill_group(
           const int nx = step0 + u + NB - SPS + e;
           const int nb = (u + NB - SPS + e) % NB;
           if (nx < nsteps) {
-            phq0[nb] = phys_of(2 * nx, nxt0[e]);
-            phq1[nb] = phys_of(2 * nx + 1, nxt1[e]);
+            phq0[nb] = phys_of(nxt0[e]);
+            phq1[nb] = phys_of(nxt1[e]);
             issue(nx, phq0[nb], phq1[nb], nb);
           }
         }
@@ -663,7 +659,7 @@ __device__ __forceinline__ void prefill_group(
           if (wave_live && step < nsteps) {
             f32x4 sc[RT][2];
             qk(u + e, sc);
-            finish(!(2 * step + 2 <= nfull && phq0[u + e] >= 0 && phq1[u + e] >= 0), step, u + e,
+            finish(2 * step + 2 > nfull || (phq0[u + e] | phq1[u + e]) < 0, step, u + e,
                    phq0[u + e], phq1[u + e], sc);
           }
         }
