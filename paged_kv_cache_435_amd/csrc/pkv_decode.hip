@@ -1327,8 +1327,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // all virtual sequences (one KV head each, head_tiles units), then each
   // one's items numbered in order and mapped back to it.  (Only this
   // workgroup reads what was written above: the barrier's workgroup-scope
-  // fence makes it visible.) ----
+  // fence makes it visible.)  Padding entries (from carry on) have no context,
+  // hence no tiles and no items, and nothing reads their plan: the loops
+  // below stop at carry. ----
   __syncthreads();
+  const int nv = carry;
   __shared__ int64_t red[2][1024 / kWave];
   __shared__ int64_t carry_items;
   // Prompt-chunk groups by size: key 256 - tiles (a group holds 1 ..
@@ -1344,7 +1347,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // from the workspace)
   auto vctx_of = [&](int v) { return v < kCtxCache ? vctx_s[v] : seq_ctx(a, v); };
   int64_t tiles = 0, live = 0;
-  for (int v = t; v < a.batch; v += 1024) {
+  for (int v = t; v < nv; v += 1024) {
     const int n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
     tiles += n;
     live += n > 0;
@@ -1420,10 +1423,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     // lane (the sizes of many groups are equal: per-lane atomics on one
     // address serialise).
     int my_rounds = 0;
-    for (int v0 = 0; v0 < a.batch; v0 += 1024) {
+    for (int v0 = 0; v0 < nv; v0 += 1024) {
       const int v = v0 + t;
       int n = 0, m = 0;
-      if (v < a.batch) {
+      if (v < nv) {
         n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
         m = div_by(n + tpi - 1, tpi, tpi_sh);
       }
@@ -1447,10 +1450,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     if (t < kKeys) key_next[t] = x - cnt0;     // groups of larger sizes come first
     __syncthreads();
   }
-  for (int v0 = 0; v0 < a.batch; v0 += 1024) {
+  for (int v0 = 0; v0 < nv; v0 += 1024) {
     const int v = v0 + t;
     int m = 0, n = 0;
-    if (v < a.batch) {
+    if (v < nv) {
       n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
       m = div_by(n + tpi - 1, tpi, tpi_sh);
     }
@@ -1458,7 +1461,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     int inc_items = cnt, unused = 0, tot_items = 0, unused_tot = 0;
     block_scan2(inc_items, unused, wtot, tot_items, unused_tot);
     int64_t first = 0;
-    if (v < a.batch) {
+    if (v < nv) {
       first = carry_items + inc_items - cnt;
       int64_t step = 1;
       if (by_chunk) {
@@ -1480,7 +1483,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       // group's rank among the round's groups of its size comes from ballots
       // (lanes of equal key, in lane order) and the counts of the waves before.
       for (int c = 0; c < rounds; ++c) {
-        const bool has = v < a.batch && c < m;
+        const bool has = v < nv && c < m;
         int key = has ? kKeys - group_tiles(n, m, c) : 0;
         key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (tiles <= tpi <= 256)
         const uint64_t peers = same_key(__builtin_amdgcn_ballot_w64(has), key);

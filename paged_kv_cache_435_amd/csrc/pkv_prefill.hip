@@ -51,11 +51,12 @@
 //   PKV_PREFILL_SYNC_2B        steps multiplied between two barriers, 16-bit
 //                              caches (the buffers go round in sets of it; the
 //                              loads of NB - SPS steps are in flight)
-//   PKV_PREFILL_DEPTH_Q, PKV_PREFILL_SYNC_Q   the same for FP8, INT8, INT4
+//   PKV_PREFILL_DEPTH_FP8, PKV_PREFILL_SYNC_FP8   the same for FP8 caches
+//   PKV_PREFILL_DEPTH_Q, PKV_PREFILL_SYNC_Q   the same for INT8, INT4
 // (16-bit caches: 2 steps per barrier in 4 buffers, 64 KB of LDS, took the
-// f16 prompt chunk from 352 to 331 us; 1 step in 3 buffers measured the same
-// as 2 in 4 or 8, or 4 in 8, for the one-byte and INT4 caches, whose steps
-// are smaller.)
+// f16 prompt chunk from 352 to 331 us.  For FP8, 2 steps in 4 buffers took
+// 262 -> 251 us once the step's scalar work was trimmed; INT8 and INT4 keep
+// 1 step in 3 buffers (2 in 4 or 6: equal or 1 % slower).)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
@@ -64,6 +65,12 @@
 #endif
 #ifndef PKV_PREFILL_SYNC_2B
 #define PKV_PREFILL_SYNC_2B 2
+#endif
+#ifndef PKV_PREFILL_DEPTH_FP8
+#define PKV_PREFILL_DEPTH_FP8 4
+#endif
+#ifndef PKV_PREFILL_SYNC_FP8
+#define PKV_PREFILL_SYNC_FP8 2
 #endif
 #ifndef PKV_PREFILL_DEPTH_Q
 #define PKV_PREFILL_DEPTH_Q 3
@@ -82,8 +89,12 @@ struct PrefillShape {
   static constexpr int GB = 16 * R;               // bytes of one 16-token group of one cache
   static constexpr int STEP = 4 * GB;             // K and V of two groups
   static constexpr bool two_byte = KV == PKV_F16 || KV == PKV_BF16;
-  static constexpr int NB = two_byte ? PKV_PREFILL_DEPTH_2B : PKV_PREFILL_DEPTH_Q;   // LDS buffers
-  static constexpr int SPS = two_byte ? PKV_PREFILL_SYNC_2B : PKV_PREFILL_SYNC_Q;   // steps per barrier
+  static constexpr int NB = two_byte ? PKV_PREFILL_DEPTH_2B
+                            : KV == PKV_FP8_E4M3FN ? PKV_PREFILL_DEPTH_FP8
+                                                   : PKV_PREFILL_DEPTH_Q;   // LDS buffers
+  static constexpr int SPS = two_byte ? PKV_PREFILL_SYNC_2B
+                             : KV == PKV_FP8_E4M3FN ? PKV_PREFILL_SYNC_FP8
+                                                    : PKV_PREFILL_SYNC_Q;   // steps per barrier
   // INT8: each wave's copy of a step's 64 row scales (K g0, K g1, V g0, V g1)
   static constexpr int SCW = row_scaled(KV) ? kPrefillWaves : 1;
 };
