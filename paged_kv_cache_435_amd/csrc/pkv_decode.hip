@@ -1334,10 +1334,9 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   const int nv = carry;
   __shared__ int64_t red[2][1024 / kWave];
   __shared__ int64_t carry_items;
-  // Prompt-chunk groups by size: key 256 - tiles (a group holds 1 ..
-  // kPrefillItemTilesMax tiles); per key, the first free position of the order,
+  // Prompt-chunk groups by size: key 256 - tiles, at least 0 (a group holds
+  // 1 .. kItemTilesMax tiles); per key, the first free position of the order,
   // and each wave's count of the current round.
-  static_assert(kPrefillItemTilesMax == 256, "one key per possible group size");
   constexpr int kKeys = 256;
   __shared__ int key_next[kKeys];
   __shared__ int key_wave[1024 / kWave][kKeys];
@@ -1370,7 +1369,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // The prompt-chunk kernel is bound by its products, not by HBM: once the
   // units fill a round of slots, items take whole contexts up to the item
   // limit (fewer partial rows to write and merge); otherwise make_plan's rule.
-  const int cap = a.prefill ? kPrefillItemTilesMax : a.item_cap;
+  // (the prompt-chunk kernel reads its block-table entries with scalar loads,
+  // so its items are not limited by registers of entries: up to kItemTilesMax;
+  // groups of more than kKeys - 1 tiles all sort first, in numbering order)
+  const int cap = a.prefill ? kItemTilesMax : a.item_cap;
   const int tpi = a.prefill && live * units >= a.slots
                       ? cap
                       : plan_tpi(tiles * units, live * units, a.slots, cap);
@@ -1485,7 +1487,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       for (int c = 0; c < rounds; ++c) {
         const bool has = v < nv && c < m;
         int key = has ? kKeys - group_tiles(n, m, c) : 0;
-        key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (tiles <= tpi <= 256)
+        key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (256 tiles or more: key 0)
         const uint64_t peers = same_key(__builtin_amdgcn_ballot_w64(has), key);
         if (has && (peers & below) == 0) key_wave[wave][key] = __builtin_popcountll(peers);
         __syncthreads();

@@ -203,8 +203,8 @@ def test_prompt_chunk_on_a_long_context_is_split_and_merged():
 def test_prompt_chunks_of_mixed_lengths():
     """512-token chunks at GQA-8 over contexts of 9,000, 5,000, 300 and 4,500
     tokens: 1,024 virtual sequences, enough to fill the GPU, so items take whole
-    contexts up to 256 tiles and the longest rows' contexts are cut into 2 or 3
-    items.  The workgroups take the groups longest first, which interleaves
+    contexts up to 512 tiles (the 5,000- and 4,500-token rows: items of more
+    than 256 tiles) and the longest rows' contexts are cut into 2 items.  The workgroups take the groups longest first, which interleaves
     sequences, row groups and chunks of every size."""
     w = W.custom(torch.float16, "f16", [9000, 5000, 300, 4500], 64, 8, 128, 16,
                  name="prompt-mixed")
