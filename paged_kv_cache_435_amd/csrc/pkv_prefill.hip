@@ -252,11 +252,13 @@ __device__ __forceinline__ void prefill_group(
   }
   // Offset codes: K enters the MFMA as (q + o) 2^-24 (o = 128 for INT8, 8
   // for INT4), so the logit is (2^24 S_mfma - o sum(q)) kfac / s, with sum(q)
-  // over the row's query (INT4: at full weight); V comes out as
-  // 2^-24 (sum p' q + o sum p') (2^-20 for INT4's odd column blocks), with
-  // sum p' (the P values fed, p / s) from one more MFMA against ones.
-  const float kf24 = kfac * 16777216.0f;
-  float kbias[RT];
+  // over the row's query (INT4: at full weight): the QK accumulation starts
+  // at -o sum(q) 2^-24, and each token's factor 2^24 kfac / s is formed once
+  // per step with its reciprocal.  V comes out as 2^-24 (sum p' q + o sum p')
+  // (2^-20 for INT4's odd column blocks), with sum p' (the P values fed,
+  // p / s) from one more MFMA against ones.
+  const float kmul = offset ? kfac * 16777216.0f : kfac;   // times 1 / s per token
+  float s_init[RT];
 #pragma unroll
   for (int k = 0; k < RT; ++k) {
     float qs = 0.f;
@@ -279,7 +281,7 @@ __device__ __forceinline__ void prefill_group(
       qs += __shfl_xor(qs, 16, kWave);
       qs += __shfl_xor(qs, 32, kWave);
     }
-    kbias[k] = -code_offset * qs * kfac;
+    s_init[k] = offset ? -code_offset * qs * 5.9604644775390625e-8f : 0.0f;   // (2^-24)
   }
 
   // Per row: m_run, the reference the row's P values are taken against (exp2
@@ -426,7 +428,7 @@ __device__ __forceinline__ void prefill_group(
       }
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        s[k][gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[k][gi] = f32x4{s_init[k], s_init[k], s_init[k], s_init[k]};
 #pragma unroll
         for (int c = 0; c < KQ; ++c) s[k][gi] = mfma32(kq[c], qop[k][c], s[k][gi]);
       }
@@ -507,11 +509,11 @@ __device__ __forceinline__ void prefill_group(
     if constexpr (i8) {
       kf = 1.0f;
       // The step's 64 row scales (this wave's own copy) become their
-      // reciprocals in place, one per lane; each lane then reads the 16 it
-      // uses (its four tokens of each group, K and V).  (A wave's LDS
-      // accesses complete in order: the reads see the writes.)
+      // reciprocals in place, one per lane (K's times kmul); each lane then
+      // reads the 16 it uses (its four tokens of each group, K and V).  (A
+      // wave's LDS accesses complete in order: the reads see the writes.)
       float* sc = &lds_sc[buf][wave][0];
-      sc[lane] = __builtin_amdgcn_rcpf(sc[lane]);
+      sc[lane] = __builtin_amdgcn_rcpf(sc[lane]) * (lane < 32 ? kmul : 1.0f);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         const f32x4 ks = *reinterpret_cast<const f32x4*>(&sc[16 * gi + 4 * c16]);
@@ -521,12 +523,7 @@ __device__ __forceinline__ void prefill_group(
           const float kr = ks[i];
           vr[gi][i] = vs[i];
 #pragma unroll
-          for (int k = 0; k < RT; ++k) {
-            if constexpr (offset)
-              s[k][gi][i] = __builtin_fmaf(s[k][gi][i], kf24, kbias[k]) * kr;
-            else
-              s[k][gi][i] = s[k][gi][i] * kfac * kr;
-          }
+          for (int k = 0; k < RT; ++k) s[k][gi][i] *= kr;
         }
       }
     }
