@@ -123,16 +123,17 @@ int64_t map_entries(int64_t vseqs, int64_t units_per_vseq, int64_t max_context_l
   return pkv::max_items_bound(vseqs, units_per_vseq, max_context_len, pkv::kMaxSlots);
 }
 // The plan of a call: 128 bytes of scalars (items, tiles per item, groups of
-// the prompt-chunk kernel, ...), six int32 per virtual sequence (context,
-// sequence, row group, KV head, first item, items per row tile), the item map
-// and the order of the prompt-chunk kernel's groups (one per kPrefillWaves
-// items).
+// the prompt-chunk kernel, virtual sequences to merge, ...), six int32 per
+// virtual sequence (context, sequence, row group, KV head, first item, items
+// per row tile), the item map, the order of the prompt-chunk kernel's groups
+// (one per kPrefillWaves items) and the list of virtual sequences the merge
+// kernel visits (one int32 per virtual sequence).
 constexpr int64_t kPlanHead = 128;
 int64_t group_entries(int64_t map_cap) {
   return (map_cap + pkv::kPrefillWaves - 1) / pkv::kPrefillWaves;
 }
 int64_t vseq_bytes(int64_t vseqs, int64_t map_cap) {
-  return (kPlanHead + 6 * 4 * vseqs + 4 * map_cap + 4 * group_entries(map_cap) + 255) / 256 * 256;
+  return (kPlanHead + 7 * 4 * vseqs + 4 * map_cap + 4 * group_entries(map_cap) + 255) / 256 * 256;
 }
 // Partial rows of an item: 16 x row tiles, each (max, sum) and head_dim floats.
 int64_t multi_workspace(int64_t vseqs, int64_t items, int64_t head_dim, int64_t row_tiles,
@@ -531,6 +532,7 @@ pkv_status paged_attention_multi_query(void* out, const void* q, int32_t q_dtype
   a.map_cap = map_cap;
   a.group_order = a.item_vseq + map_cap;
   a.group_cap = group_entries(map_cap);
+  a.merge_list = a.group_order + a.group_cap;
   a.plan_info = reinterpret_cast<int64_t*>(w);
   a.query_start = query_start;
   a.real_ctx = context_lens;

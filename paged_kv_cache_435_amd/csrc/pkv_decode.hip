@@ -1119,14 +1119,16 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // Several query tokens per sequence: one workgroup of 8 waves per virtual
 // sequence (sequence, KV head, group of 32-row tiles of (query token, head)
 // rows), each wave merging every 8th row; rows of a virtual sequence with no context (rows
-// before the cache) get zeros.  A unit that was one item (the common case for
-// prompt chunks) costs one read of its record.
+// before the cache) get zeros.  Only the virtual sequences of the prep kernel's
+// merge list are visited (units cut into several items, or no context): a
+// call whose units were all whole items launches this kernel and ends it at
+// once.
 constexpr int kMergeWaves = 8;
+constexpr int kMergeGroups = 512;   // workgroups along x; each takes every 512th list entry
 template <int QT, int D>
-__global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
+__device__ __forceinline__ void merge_vseq(const DecodeArgs& a, int v) {
   const int TR = a.wave_rows;                 // rows of a wave's tile
   const int ROWS = TR * a.head_tiles;         // rows of a virtual sequence
-  const int v = blockIdx.x;
   const int g = a.vseq_g[v];
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -1168,6 +1170,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArg
   if (first + (int64_t)(m - 1) * S + a.head_tiles - 1 >= a.max_items) return;
   for (int r = r_first; r < rows; r += r_step)
     merge_row<QT, D, 4>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
+}
+template <int QT, int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
+  const int64_t n = a.plan_info[12];          // entries of the merge list
+  for (int64_t i = blockIdx.x; i < n; i += gridDim.x) merge_vseq<QT, D>(a, a.merge_list[i]);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS
@@ -1334,6 +1341,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   const int nv = carry;
   __shared__ int64_t red[2][1024 / kWave];
   __shared__ int64_t carry_items;
+  __shared__ int carry_mrg;                    // entries of the merge list so far
   // Prompt-chunk groups by size: key 256 - tiles, at least 0 (a group holds
   // 1 .. kItemTilesMax tiles); per key, the first free position of the order,
   // and each wave's count of the current round.
@@ -1351,13 +1359,20 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     tiles += n;
     live += n > 0;
   }
-  tiles = wave_sum_i64(tiles);
-  live = wave_sum_i64(live);
+  // Wave sums by DPP scans in 32-bit pieces: live counts fit; tiles as 24-bit
+  // low and high parts (a thread's tiles stay under 2^48, so each part's sum
+  // over 64 lanes stays under 2^30).
+  {
+    const int lo = __builtin_amdgcn_readlane(wave_incl_scan((int)(tiles & 0xFFFFFF)), kWave - 1);
+    const int hi = __builtin_amdgcn_readlane(wave_incl_scan((int)(tiles >> 24)), kWave - 1);
+    tiles = ((int64_t)hi << 24) + lo;
+    live = __builtin_amdgcn_readlane(wave_incl_scan((int)live), kWave - 1);
+  }
   if ((t & (kWave - 1)) == 0) {
     red[0][t / kWave] = tiles;
     red[1][t / kWave] = live;
   }
-  if (t == 0) carry_items = 0;
+  if (t == 0) carry_items = 0, carry_mrg = 0;
   if (t < kKeys) key_next[t] = 0;
   for (int i = t; i < (1024 / kWave) * kKeys; i += 1024) (&key_wave[0][0])[i] = 0;
   __syncthreads();
@@ -1460,8 +1475,11 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       m = div_by(n + tpi - 1, tpi, tpi_sh);
     }
     const int cnt = m * units;
-    int inc_items = cnt, unused = 0, tot_items = 0, unused_tot = 0;
-    block_scan2(inc_items, unused, wtot, tot_items, unused_tot);
+    // (merge: a unit cut into several items, or no context: rows of zeros)
+    const int mrg = v < nv && (m > 1 || n == 0) ? 1 : 0;
+    int inc_items = cnt, inc_mrg = mrg, tot_items = 0, tot_mrg = 0;
+    block_scan2(inc_items, inc_mrg, wtot, tot_items, tot_mrg);
+    if (mrg) a.merge_list[carry_mrg + inc_mrg - 1] = v;
     int64_t first = 0;
     if (v < nv) {
       first = carry_items + inc_items - cnt;
@@ -1512,7 +1530,10 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       }
     }
     __syncthreads();
-    if (t == 0) carry_items += tot_items;
+    if (t == 0) {
+      carry_items += tot_items;
+      carry_mrg += tot_mrg;
+    }
     __syncthreads();
   }
   if (t == 0) {
@@ -1523,6 +1544,7 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     const int64_t groups = carry_items / units;
     a.plan_info[10] = groups < a.group_cap ? groups : a.group_cap;
     a.plan_info[11] = by_chunk ? 1 : 0;
+    a.plan_info[12] = carry_mrg;
   }
 }
 
@@ -1600,7 +1622,8 @@ static hipError_t launch5(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   if (e != hipSuccess) return e;
   if constexpr (MULTI) {
     const int rows = a.wave_rows * a.head_tiles;   // rows of a virtual sequence: one per wave
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, (rows + kMergeWaves - 1) / kMergeWaves),
+    const unsigned gx = (unsigned)(a.batch < kMergeGroups ? a.batch : kMergeGroups);
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(gx, (rows + kMergeWaves - 1) / kMergeWaves),
                        dim3(64 * kMergeWaves), 0, st, a);
   }
   else if (a.ws_seq)   // (no workspace: no unit can be split, every item finished in place)
@@ -1683,7 +1706,8 @@ static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vc
   if (e != hipSuccess) return e;
   e = launch_prefill(a, QT, kv_dtype, D, block_size, num_cus, false, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch), dim3(64 * kMergeWaves), 0, st, a);
+  hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch < kMergeGroups ? a.batch : kMergeGroups),
+                     dim3(64 * kMergeWaves), 0, st, a);
   return hipGetLastError();
 }
 

@@ -100,6 +100,8 @@ struct DecodeArgs {
                                // [11] by-chunk numbering
   int32_t* group_order;        // prompt-chunk groups, longest first (multi_prep_kernel)
   int64_t group_cap;           // entries of group_order
+  int32_t* merge_list;         // virtual sequences the merge kernel visits (multi_prep_kernel):
+                               // units cut into several items, or no context (rows of zeros)
   int32_t* vseq_first;         // first item of each virtual sequence
   int32_t* vseq_m;             // items (chunks of its context) per row tile
   int32_t* item_vseq;          // virtual sequence of each item

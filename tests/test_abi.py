@@ -119,9 +119,10 @@ def test_multi_query_sizing_and_rejections(lib):
     # (ceil(320 / 128) + 3) = 48 virtual sequences.  The plan: 128 B of scalars, six
     # int32 per virtual sequence, an item map with room for the most items any
     # plan makes: 48 x 4 units x 8 tiles / 256 + 4096 slots + 192 units = 4294
-    # entries, and one int32 per 4 of them for the order of the prompt-chunk
-    # kernel's workgroups.  Contexts <= 128 are never split: nothing else.
-    plan = lambda entries: -(-(128 + 6 * 4 * 48 + 4 * entries + 4 * -(-entries // 4)) // 256) * 256
+    # entries, one int32 per 4 of them for the order of the prompt-chunk
+    # kernel's workgroups, and one int32 per virtual sequence for the list the
+    # merge kernel visits.  Contexts <= 128 are never split: nothing else.
+    plan = lambda entries: -(-(128 + 7 * 4 * 48 + 4 * entries + 4 * -(-entries // 4)) // 256) * 256
     assert pkv.paged_attention_multi_workspace_size(3, 40, 64, 8, 128, 128) == plan(4294)
     # 32K contexts: 192 units x 2048 tiles / 256 + 4096 + 192 = 5824 items, each
     # with 32 partial rows of (2 + d) floats, and 16 B per virtual sequence.
