@@ -1120,9 +1120,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
 // sequence (sequence, KV head, group of 32-row tiles of (query token, head)
 // rows), each wave merging every 8th row; rows of a virtual sequence with no context (rows
 // before the cache) get zeros.  Only the virtual sequences of the prep kernel's
-// merge list are visited (units cut into several items, or no context): a
-// call whose units were all whole items launches this kernel and ends it at
-// once.
+// merge list are visited by prompt-chunk calls (units cut into several
+// items, or no context): a call whose units were all whole items launches
+// this kernel and ends it at once.  The decode-shaped kernel's calls keep one
+// workgroup column per virtual sequence.
 constexpr int kMergeWaves = 8;
 constexpr int kMergeGroups = 512;   // workgroups along x; each takes every 512th list entry
 template <int QT, int D>
@@ -1171,8 +1172,15 @@ __device__ __forceinline__ void merge_vseq(const DecodeArgs& a, int v) {
   for (int r = r_first; r < rows; r += r_step)
     merge_row<QT, D, 4>(a, (first + r / TR) * TR + r % TR, S * TR, m, out_row(r), lane);
 }
+// (the decode-shaped kernel's calls: few virtual sequences, most of them
+// split; one workgroup column per virtual sequence, no list to read first)
 template <int QT, int D>
 __global__ __launch_bounds__(64 * kMergeWaves) void multi_merge_kernel(DecodeArgs a) {
+  merge_vseq<QT, D>(a, blockIdx.x);
+}
+// (prompt chunks: the virtual sequences of the merge list)
+template <int QT, int D>
+__global__ __launch_bounds__(64 * kMergeWaves) void prefill_merge_kernel(DecodeArgs a) {
   const int64_t n = a.plan_info[12];          // entries of the merge list
   for (int64_t i = blockIdx.x; i < n; i += gridDim.x) merge_vseq<QT, D>(a, a.merge_list[i]);
 }
@@ -1622,8 +1630,7 @@ static hipError_t launch5(DecodeArgs& a, int num_cus, const MultiLaunch& ml, hip
   if (e != hipSuccess) return e;
   if constexpr (MULTI) {
     const int rows = a.wave_rows * a.head_tiles;   // rows of a virtual sequence: one per wave
-    const unsigned gx = (unsigned)(a.batch < kMergeGroups ? a.batch : kMergeGroups);
-    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(gx, (rows + kMergeWaves - 1) / kMergeWaves),
+    hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch, (rows + kMergeWaves - 1) / kMergeWaves),
                        dim3(64 * kMergeWaves), 0, st, a);
   }
   else if (a.ws_seq)   // (no workspace: no unit can be split, every item finished in place)
@@ -1706,7 +1713,7 @@ static hipError_t launch_prefill_call(DecodeArgs& a, int batch_real, int32_t* vc
   if (e != hipSuccess) return e;
   e = launch_prefill(a, QT, kv_dtype, D, block_size, num_cus, false, st);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((multi_merge_kernel<QT, D>), dim3(a.batch < kMergeGroups ? a.batch : kMergeGroups),
+  hipLaunchKernelGGL((prefill_merge_kernel<QT, D>), dim3(a.batch < kMergeGroups ? a.batch : kMergeGroups),
                      dim3(64 * kMergeWaves), 0, st, a);
   return hipGetLastError();
 }
