@@ -1249,11 +1249,17 @@ __device__ __forceinline__ int div_by(int x, int d, int sh) { return sh >= 0 ? x
 __device__ __forceinline__ int log2_if_pow2(int d) { return (d & (d - 1)) == 0 ? __builtin_ctz(d) : -1; }
 
 // Virtual sequences of a multi-token call (one workgroup): for sequence b, each
-// KV head (head-major, so the workgroups running together on an XCD share one
-// head's K/V in its L2) times each group of row tiles, with the context the
-// group's last row may see; entries past the last are padding with no context.  Sequences go 1024
-// at a time: a block scan gives each its first entry, then every thread fills
-// entries, finding its sequence by binary search over the scan.
+// KV head times each group of row tiles, with the context the group's last row
+// may see; entries past the last are padding with no context.  Decode-shaped
+// calls number them KV head major (the workgroups running together on an XCD,
+// which take items in numbering order, share one head's K/V in its L2).  Prompt
+// chunks number them row group major, so the KV heads of one row group, which
+// share its context and hence its tiles, chunks and place in the order of
+// groups, are adjacent: the plan below then takes one row group at a time
+// instead of each of its KV heads (the one-workgroup kernel's work drops by
+// the KV head count).  Sequences go 1024 at a time: a block scan gives each
+// its first entry, then every thread fills entries, finding its sequence by
+// binary search over the scan.
 __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batch_real,
                                                           int32_t* vctx) {
   __shared__ int scan[1024];   // inclusive: entries of sequences b0 .. b0 + t
@@ -1267,6 +1273,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   const int G = a.num_q_heads / a.num_kv_heads;
   const int ROWS = a.wave_rows * a.head_tiles;   // rows of a virtual sequence
   const int g_sh = log2_if_pow2(G), rows_sh = log2_if_pow2(ROWS);
+  const int H = a.num_kv_heads, h_sh = log2_if_pow2(H);
+  const bool by_row_group = a.prefill;   // numbering (row group, KV head)
   if (t == 0) carry = several_groups = 0;
   __syncthreads();
   for (int b0 = 0; b0 < batch_real; b0 += 1024) {
@@ -1309,16 +1317,28 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
       const int bb = b0 + lo;
       const int Lb = seq_len[lo];
       const int ng = div_by(Lb * G + ROWS - 1, ROWS, rows_sh);   // row groups of the sequence
-      const int local = e - (lo > 0 ? scan[lo - 1] : 0);   // KV head major, then row group
-      const int gg = ng == 1 ? local : local / ng;
-      const int rt = local - gg * ng;
+      const int local = e - (lo > 0 ? scan[lo - 1] : 0);
+      int gg, rt;
+      if (by_row_group) {
+        rt = div_by(local, H, h_sh);
+        gg = local - rt * H;
+      } else {
+        gg = ng == 1 ? local : local / ng;
+        rt = local - gg * ng;
+      }
       const int ctx = seq_cx[lo];
       int last = ROWS * rt + ROWS - 1;
       last = last < Lb * G - 1 ? last : Lb * G - 1;
       int c = ctx - Lb + div_by(last, G, g_sh) + 1;
       c = c < 0 ? 0 : c;
       vctx[v] = c;
-      if (v < kCtxCache) vctx_s[v] = c;
+      // (LDS copy: per row group when numbered by row groups, else per entry)
+      if (by_row_group) {
+        const int r = div_by(v, H, h_sh);
+        if (gg == 0 && r < kCtxCache) vctx_s[r] = c;
+      } else if (v < kCtxCache) {
+        vctx_s[v] = c;
+      }
       a.vseq_b[v] = bb;
       a.vseq_rt[v] = rt;
       a.vseq_g[v] = gg;
@@ -1332,7 +1352,6 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   }
   for (int v = carry + t; v < a.batch; v += 1024) {
     vctx[v] = 0;
-    if (v < kCtxCache) vctx_s[v] = 0;
     a.vseq_b[v] = -1;            // padding: no sequence, no rows
     a.vseq_rt[v] = 0;
     a.vseq_g[v] = 0;
@@ -1340,13 +1359,19 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
 
   // ---- the plan, once for every kernel of the call: make_plan's rule over
   // all virtual sequences (one KV head each, head_tiles units), then each
-  // one's items numbered in order and mapped back to it.  (Only this
-  // workgroup reads what was written above: the barrier's workgroup-scope
+  // one's items numbered and mapped back to it.  It runs over planning units:
+  // row groups, each standing for its wt = H adjacent virtual sequences, when
+  // numbered by row groups; else single virtual sequences (wt = 1).  (Only
+  // this workgroup reads what was written above: the barrier's workgroup-scope
   // fence makes it visible.)  Padding entries (from carry on) have no context,
   // hence no tiles and no items, and nothing reads their plan: the loops
   // below stop at carry. ----
   __syncthreads();
   const int nv = carry;
+  // (every sequence's entry count is a multiple of H, and so is a.batch (the
+  // host's bound), hence carry: the row groups are whole)
+  const int wt = by_row_group ? H : 1;
+  const int nu = by_row_group ? div_by(nv, H, h_sh) : nv;   // planning units
   __shared__ int64_t red[2][1024 / kWave];
   __shared__ int64_t carry_items;
   __shared__ int carry_mrg;                    // entries of the merge list so far
@@ -1356,14 +1381,15 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   constexpr int kKeys = 256;
   __shared__ int key_next[kKeys];
   __shared__ int key_wave[1024 / kWave][kKeys];
-  __shared__ int wave_rounds[1024 / kWave];    // most groups of one virtual sequence, per wave
+  __shared__ int wave_rounds[1024 / kWave];    // most groups of one unit, per wave
+  __shared__ int pos_s[1024], grp_s[1024];     // a round's place and group of unit u0 + t
   const int units = a.head_tiles;
-  // (contexts of the first kCtxCache virtual sequences from LDS, the rest
-  // from the workspace)
-  auto vctx_of = [&](int v) { return v < kCtxCache ? vctx_s[v] : seq_ctx(a, v); };
+  // (contexts of the first kCtxCache units from LDS, the rest from the
+  // workspace: a row group's is its first virtual sequence's)
+  auto ctx_of = [&](int u) { return u < kCtxCache ? vctx_s[u] : seq_ctx(a, u * wt); };
   int64_t tiles = 0, live = 0;
-  for (int v = t; v < nv; v += 1024) {
-    const int n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
+  for (int u = t; u < nu; u += 1024) {
+    const int n = (ctx_of(u) + kTileTokens - 1) / kTileTokens;
     tiles += n;
     live += n > 0;
   }
@@ -1389,6 +1415,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     tiles += red[0][w];
     live += red[1][w];
   }
+  tiles *= wt;
+  live *= wt;
   // The prompt-chunk kernel is bound by its products, not by HBM: once the
   // units fill a round of slots, items take whole contexts up to the item
   // limit (fewer partial rows to write and merge); otherwise make_plan's rule.
@@ -1404,7 +1432,8 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // chunk count m: their items are numbered chunk by chunk (item = F + c*Hkv +
   // g), so a workgroup's waves read the same blocks' adjacent (block, head)
   // tiles, as in decode.  Otherwise each virtual sequence's items are
-  // consecutive.
+  // consecutive, and a row group's H virtual sequences' items follow one
+  // another.
   const bool by_chunk = !a.prefill && a.head_tiles == 1 && several_groups == 0;
   // The prompt-chunk kernel takes its groups (the units of one chunk of one
   // virtual sequence, one workgroup each) in decreasing order of their tiles:
@@ -1414,8 +1443,9 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
   // numbering order, the longest sequences' groups filled whole XCDs and
   // finished one round after the rest.)  Groups of one size keep numbering
   // order, so the KV heads of one row group sit side by side and, with as many
-  // KV heads as XCDs, each XCD reads one head's K/V.  A stable counting sort:
-  // the sizes first, then the groups placed round by round below.
+  // KV heads as XCDs, each XCD reads one head's K/V.  A stable counting sort
+  // over planning units (a row group's H groups of a chunk take H adjacent
+  // places): the sizes first, then the groups placed round by round below.
   const bool order_groups = a.prefill && a.group_order != nullptr;
   const int tpi_sh = log2_if_pow2(tpi);   // (the prompt-chunk kernel's tpi is 256)
   // Tiles of chunk c of a unit's n tiles cut into m chunks: floor((c+1)n/m) -
@@ -1442,17 +1472,17 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     }
     return peers;
   };
-  int rounds = 0;   // most groups of one virtual sequence (order_groups only)
+  int rounds = 0;   // most groups of one unit (order_groups only)
   if (order_groups) {
-    // Groups per size: one LDS atomic per (wave, size), by the size's first
-    // lane (the sizes of many groups are equal: per-lane atomics on one
-    // address serialise).
+    // Groups per size, in planning units: one LDS atomic per (wave, size), by
+    // the size's first lane (the sizes of many groups are equal: per-lane
+    // atomics on one address serialise).
     int my_rounds = 0;
-    for (int v0 = 0; v0 < nv; v0 += 1024) {
-      const int v = v0 + t;
+    for (int u0 = 0; u0 < nu; u0 += 1024) {
+      const int u = u0 + t;
       int n = 0, m = 0;
-      if (v < nv) {
-        n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
+      if (u < nu) {
+        n = (ctx_of(u) + kTileTokens - 1) / kTileTokens;
         m = div_by(n + tpi - 1, tpi, tpi_sh);
       }
       my_rounds = m > my_rounds ? m : my_rounds;
@@ -1472,75 +1502,113 @@ __global__ __launch_bounds__(1024) void multi_prep_kernel(DecodeArgs a, int batc
     const int cnt0 = t < kKeys ? key_next[t] : 0;
     int x = cnt0, y = 0, tx, ty;
     block_scan2(x, y, wtot, tx, ty);           // (ends with a barrier)
-    if (t < kKeys) key_next[t] = x - cnt0;     // groups of larger sizes come first
+    // (groups of larger sizes come first; a unit's groups are wt groups.  The
+    // count stays under 2^31: groups are counted in int32 on the host)
+    if (t < kKeys) key_next[t] = (x - cnt0) * wt;
     __syncthreads();
   }
-  for (int v0 = 0; v0 < nv; v0 += 1024) {
-    const int v = v0 + t;
+  for (int u0 = 0; u0 < nu; u0 += 1024) {
+    const int u = u0 + t;
     int m = 0, n = 0;
-    if (v < nv) {
-      n = (vctx_of(v) + kTileTokens - 1) / kTileTokens;
+    if (u < nu) {
+      n = (ctx_of(u) + kTileTokens - 1) / kTileTokens;
       m = div_by(n + tpi - 1, tpi, tpi_sh);
     }
-    const int cnt = m * units;
+    const int cnt = m * units;                 // items of each of the unit's virtual sequences
     // (merge: a unit cut into several items, or no context: rows of zeros)
-    const int mrg = v < nv && (m > 1 || n == 0) ? 1 : 0;
+    const int mrg = u < nu && (m > 1 || n == 0) ? 1 : 0;
     int inc_items = cnt, inc_mrg = mrg, tot_items = 0, tot_mrg = 0;
     block_scan2(inc_items, inc_mrg, wtot, tot_items, tot_mrg);
-    if (mrg) a.merge_list[carry_mrg + inc_mrg - 1] = v;
+    // first item of the unit's first virtual sequence; its k-th follows at
+    // first + k * cnt.  The unit's first item, chunks and merge-list place go
+    // through LDS (the sequence arrays of the first phase, no longer used) to
+    // one thread per virtual sequence, whose stores are then adjacent.
     int64_t first = 0;
-    if (v < nv) {
-      first = carry_items + inc_items - cnt;
+    if (u < nu) {
+      first = carry_items + (int64_t)wt * (inc_items - cnt);
+      scan[t] = (int)first;                    // (< 2^31: items are counted in int32 on the host)
+      seq_len[t] = m;
+      seq_cx[t] = mrg ? carry_mrg + wt * (inc_mrg - 1) : -1;
+    }
+    __syncthreads();
+    const int nb = nu - u0 < 1024 ? nu - u0 : 1024;   // units of this block
+    for (int j = t; j < wt * nb; j += 1024) {
+      const int uj = by_row_group ? div_by(j, H, h_sh) : j;
+      const int k = j - uj * wt;                 // the unit's k-th virtual sequence
+      const int v = u0 * wt + j;
+      const int mj = seq_len[uj];
+      const int cj = mj * units;
+      if (seq_cx[uj] >= 0) a.merge_list[seq_cx[uj] + k] = v;
+      int64_t f = scan[uj] + (int64_t)k * cj;
       int64_t step = 1;
       if (by_chunk) {
         // (the scan gave F + g*m; the sequence's group starts at F)
         const int g = a.vseq_g[v];
-        first -= (int64_t)g * (m - 1);
+        f -= (int64_t)g * (mj - 1);
         step = a.num_kv_heads;
       }
-      a.vseq_first[v] = (int32_t)first;
-      a.vseq_m[v] = m;
-      if (a.ws_seq) {
-        a.ws_seq[2 * v] = first;
-        a.ws_seq[2 * v + 1] = m;
+      a.vseq_first[v] = (int32_t)f;
+      a.vseq_m[v] = mj;
+      if (a.ws_seq) *reinterpret_cast<i64x2*>(a.ws_seq + 2 * v) = i64x2{f, mj};   // (16-byte aligned)
+      // The item map.  The prompt-chunk kernel reads only each group's first
+      // item (a group is the units items of one chunk), so prompt chunks write
+      // those alone: the map's stores are most of this one compute unit's
+      // memory traffic.
+      if (a.prefill) {
+        for (int c = 0; c < mj && f + c * units < a.map_cap; ++c) a.item_vseq[f + c * units] = v;
+      } else {
+        for (int i = 0; i < cj && f + i * step < a.map_cap; ++i) a.item_vseq[f + i * step] = v;
       }
-      for (int i = 0; i < cnt && first + i * step < a.map_cap; ++i) a.item_vseq[first + i * step] = v;
     }
     if (order_groups) {
-      // Round c places chunk c of every virtual sequence of this block: the
-      // group's rank among the round's groups of its size comes from ballots
-      // (lanes of equal key, in lane order) and the counts of the waves before.
+      // Round c places chunk c of every unit of this block: the unit's rank
+      // among the round's units of its size comes from ballots (lanes of equal
+      // key, in lane order) and the counts of the waves before; its wt groups
+      // take wt adjacent places, written by wt adjacent threads (the place and
+      // group number go through LDS).
       for (int c = 0; c < rounds; ++c) {
-        const bool has = v < nv && c < m;
+        const bool has = u < nu && c < m;
         int key = has ? kKeys - group_tiles(n, m, c) : 0;
         key = key < 0 ? 0 : (key > kKeys - 1 ? kKeys - 1 : key);   // (256 tiles or more: key 0)
         const uint64_t peers = same_key(__builtin_amdgcn_ballot_w64(has), key);
         if (has && (peers & below) == 0) key_wave[wave][key] = __builtin_popcountll(peers);
         __syncthreads();
-        if (has) {
-          // (the 16 reads are independent: unrolled, they are in flight together)
-          int pos = key_next[key] + __builtin_popcountll(peers & below);
+        if (u < nu) {
+          int pos = -1;
+          if (has) {
+            // (the 16 reads are independent: unrolled, they are in flight together)
+            int rank = __builtin_popcountll(peers & below);
 #pragma unroll
-          for (int w = 0; w < 1024 / kWave; ++w) pos += w < wave ? key_wave[w][key] : 0;
-          // (first < 2^31: items are counted in int32 on the host)
-          if (pos < a.group_cap) a.group_order[pos] = (int32_t)((int32_t)first / units + c);
+            for (int w = 0; w < 1024 / kWave; ++w) rank += w < wave ? key_wave[w][key] : 0;
+            pos = key_next[key] + rank * wt;
+          }
+          pos_s[t] = pos;
+          // (first < 2^31: items are counted in int32 on the host; the group
+          // of virtual sequence k of the unit is (first + k*cnt) / units + c)
+          grp_s[t] = (int32_t)first / units + c;
         }
         __syncthreads();
+        for (int j = t; j < wt * nb; j += 1024) {
+          const int uj = by_row_group ? div_by(j, H, h_sh) : j;
+          const int k = j - uj * wt;
+          const int pos = pos_s[uj];
+          if (pos >= 0 && pos + k < a.group_cap) a.group_order[pos + k] = grp_s[uj] + k * seq_len[uj];
+        }
         if (t < kKeys) {
           int sum = 0;
 #pragma unroll
           for (int w = 0; w < 1024 / kWave; ++w) sum += key_wave[w][t];
 #pragma unroll
           for (int w = 0; w < 1024 / kWave; ++w) key_wave[w][t] = 0;
-          key_next[t] += sum;
+          key_next[t] += sum * wt;
         }
         __syncthreads();
       }
     }
     __syncthreads();
     if (t == 0) {
-      carry_items += tot_items;
-      carry_mrg += tot_mrg;
+      carry_items += (int64_t)wt * tot_items;
+      carry_mrg += wt * tot_mrg;
     }
     __syncthreads();
   }
