@@ -444,7 +444,10 @@ __device__ __forceinline__ void prefill_group(
   auto scales = [&](int buf, f32x4 (&ks)[2], f32x4 (&vs)[2]) {
     if constexpr (i8) {
       float* sc = &lds_sc[buf][wave][0];
-      sc[lane] = __builtin_amdgcn_rcpf(sc[lane]) * (lane < 32 ? kmul : 1.0f);
+      const float r = __builtin_amdgcn_rcpf(sc[lane]);
+      // (V's kept finite: a stored scale is positive, and a slot past the
+      // context may hold anything, whose P of 0 must then give 0)
+      sc[lane] = lane < 32 ? r * kmul : fminf(fabsf(r), 3.402823466e38f);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
         ks[gi] = *reinterpret_cast<const f32x4*>(&sc[16 * gi + 4 * c16]);
@@ -589,15 +592,11 @@ __device__ __forceinline__ void prefill_group(
       pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
       if constexpr (i8) {
-        // P fed to PV: p / s_v (a masked token's p is 0, and its slot's scale
-        // may be anything: kept at 0)
+        // P fed to PV: p / s_v (a masked token's p is 0 and its 1 / s_v finite)
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float pv = p[4 * gi + i] * vr[gi][i];
-            p[4 * gi + i] = checked ? (p[4 * gi + i] > 0.f ? pv : 0.f) : pv;
-          }
+          for (int i = 0; i < 4; ++i) p[4 * gi + i] *= vr[gi][i];
         if constexpr (i4)   // (token order of the INT4 V operand)
           pb[k] = u32x4{pack2(p[0], p[2]), pack2(p[1], p[3]), pack2(p[4], p[6]), pack2(p[5], p[7])};
         else

@@ -241,6 +241,19 @@ def test_more_than_1024_sequences(hq, hkv, qlen):
     run_multi(w, lens, seqs_check=[0, 511, 1023, 1024, 1099])
 
 
+def test_prompt_chunks_past_4096_row_groups():
+    """4200 sequences of 16-token chunks at G = 8: one 128-row group each, so
+    the planning pass takes its row groups in five rounds of 1024 and the
+    contexts of those past the 4096 it keeps in LDS come from the workspace.
+    Sampled sequences on both sides of each limit are checked."""
+    rng = np.random.default_rng(11)
+    B = 4200
+    lens = np.full(B, 16)
+    ctx = rng.integers(16, 80, B)
+    w = W.custom(torch.float16, "f16", ctx, 16, 2, 128, 16, name=f"B{B}-rowgroups")
+    run_multi(w, lens, seqs_check=[0, 1023, 1024, 4095, 4096, 4199])
+
+
 @pytest.mark.parametrize("q_len", [4, 512])
 def test_pool_past_2_31_bytes(q_len):
     """A 2.8 GB fp16 pool per cache read only from its blocks past the 2**31-byte
