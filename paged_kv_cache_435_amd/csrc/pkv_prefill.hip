@@ -293,7 +293,11 @@ __device__ __forceinline__ void prefill_group(
   // is made on each lane's own scores against thr = (m_run + kLazy) / kf, a
   // raw-score bound (kf > 0), so the row's max over lanes is taken only on the
   // steps that move the reference.  mref: m_run kept finite for the
-  // exponentials.
+  // exponentials.  INT8, INT4: the step's scores become exponents x = logit -
+  // mref at once, one fma per score with its token's factor (which a raw-score
+  // bound cannot take: the factor varies by token), and the test is x > kLazy
+  // (thr = kLazy; -inf while the row has no reference, mref 0 until then); a
+  // step that moves the reference shifts its exponents by the change.
   constexpr float kLazy = 8.0f;
   f32x4 acc[RT][NC];
   f32x4 lsum[RT];
@@ -307,7 +311,7 @@ __device__ __forceinline__ void prefill_group(
     accp[k] = f32x4{0.f, 0.f, 0.f, 0.f};
     m_run[k] = -__builtin_inff();
     thr[k] = -__builtin_inff();
-    mref[k] = -3.402823466e38f;
+    mref[k] = i8 ? 0.0f : -3.402823466e38f;
   }
 
   // ---- global -> registers -> LDS.  Thread tid's load j of a step is the
@@ -524,7 +528,7 @@ __device__ __forceinline__ void prefill_group(
     // scores gives the max logit.  Masked scores become -inf (a select: stale
     // slots may hold NaN), so their P is exp2(-inf) = 0.
     const int tok0 = t_begin + 2 * step * 16 + 4 * c16;
-    // INT8: the logits themselves (per-token factors), so kf = 1 below.
+    // INT8, INT4: exponents against mref (per-token factors), so kf = 1 below.
     float kf = kfac;
     f32x4 vr[2] = {f32x4{1.f, 1.f, 1.f, 1.f}, f32x4{1.f, 1.f, 1.f, 1.f}};   // INT8: 1 / s_v
     if constexpr (i8) {
@@ -539,7 +543,7 @@ __device__ __forceinline__ void prefill_group(
           const float kr = ks[i];
           vr[gi][i] = vs[i];
 #pragma unroll
-          for (int k = 0; k < RT; ++k) s[k][gi][i] *= kr;
+          for (int k = 0; k < RT; ++k) s[k][gi][i] = __builtin_fmaf(s[k][gi][i], kr, -mref[k]);
         }
       }
     }
@@ -566,7 +570,8 @@ __device__ __forceinline__ void prefill_group(
       const float rkf = 1.0f / kf;
 #pragma unroll
       for (int k = 0; k < RT; ++k) {
-        const float m_new = fmax2(m_run[k], rows_max(mx[k]) * kf);
+        // (INT8, INT4: the scores are exponents against mref)
+        const float m_new = fmax2(m_run[k], i8 ? rows_max(mx[k]) + mref[k] : rows_max(mx[k]) * kf);
         // (a row that has seen no token keeps -inf and zeros)
         const float alpha = m_new == -__builtin_inff() ? 1.0f : __builtin_amdgcn_exp2f(m_run[k] - m_new);
 #pragma unroll
@@ -574,10 +579,21 @@ __device__ __forceinline__ void prefill_group(
         lsum[k] *= alpha;
         if constexpr (offset) accp[k] *= alpha;
         m_run[k] = m_new;
-        thr[k] = (m_new + kLazy) * rkf;
-        // (a row that has seen no token: every score is -inf, and the finite
-        // reference keeps exp2 at 0 rather than NaN)
-        mref[k] = fmax2(m_new, -3.402823466e38f);
+        if constexpr (i8) {
+          const float ref = m_new == -__builtin_inff() ? 0.0f : m_new;
+          const float delta = ref - mref[k];
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[k][gi][i] -= delta;
+          mref[k] = ref;
+          thr[k] = m_new == -__builtin_inff() ? -__builtin_inff() : kLazy;
+        } else {
+          thr[k] = (m_new + kLazy) * rkf;
+          // (a row that has seen no token: every score is -inf, and the finite
+          // reference keeps exp2 at 0 rather than NaN)
+          mref[k] = fmax2(m_new, -3.402823466e38f);
+        }
       }
     }
     u32x4 pb[RT];
@@ -588,7 +604,8 @@ __device__ __forceinline__ void prefill_group(
       for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          p[4 * gi + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kf, -mref[k]));
+          p[4 * gi + i] = i8 ? __builtin_amdgcn_exp2f(s[k][gi][i])
+                             : __builtin_amdgcn_exp2f(__builtin_fmaf(s[k][gi][i], kf, -mref[k]));
       pb[k] = u32x4{pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
       lsum[k] = mfma32(ones, pb[k], lsum[k]);
       if constexpr (i8) {
