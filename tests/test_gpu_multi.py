@@ -164,7 +164,7 @@ def test_sequences_without_new_tokens_are_skipped():
 # the calls take the LDS-sharing prefill kernel.  Cases: ragged chunk lengths, a sequence with no
 # new tokens, one with more new tokens than cached ones (rows before the
 # cache), a whole prompt (L = context), both block sizes, d 64 and 128, GQA,
-# MHA and MQA.
+# MHA and MQA, KV head counts that are not powers of two.
 @pytest.mark.parametrize("q_dtype,d,bs,hq,hkv,ctx,lens,kv", [
     (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], None),
     (torch.bfloat16, 128, 256, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], None),
@@ -179,6 +179,10 @@ def test_sequences_without_new_tokens_are_skipped():
     (torch.float16, 128, 16, 8, 2, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], "i4"),
     (torch.bfloat16, 128, 256, 16, 1, [300, 129], [64, 129], "i4"),
     (torch.float16, 128, 256, 4, 4, [600, 1000], [600, 400], "i4"),
+    # three KV heads (not a power of two: the planning pass divides, and a row
+    # group's heads are numbered 3 apart), at G = 4 and G = 3
+    (torch.float16, 128, 16, 12, 3, [700, 64, 1500, 300, 90], [300, 100, 200, 0, 90], None),
+    (torch.bfloat16, 128, 16, 9, 3, [900, 500, 40], [300, 200, 40], "i8"),
 ])
 def test_prompt_chunks(q_dtype, d, bs, hq, hkv, ctx, lens, kv):
     """(FP8 rows: the same kernel over an FP8 E4M3FN cache, codes converted
