@@ -75,6 +75,9 @@
 #ifndef PKV_PREFILL_DEPTH_Q
 #define PKV_PREFILL_DEPTH_Q 3
 #endif
+#ifndef PKV_PREFILL_K_AHEAD
+#define PKV_PREFILL_K_AHEAD 1
+#endif
 #ifndef PKV_PREFILL_SYNC_Q
 #define PKV_PREFILL_SYNC_Q 1
 #endif
@@ -438,6 +441,41 @@ __device__ __forceinline__ void prefill_group(
       }
     }
   };
+  // Two or more steps per barrier (16-bit and FP8 caches): a step's K bytes
+  // read during the previous step of its set (its buffer landed with the set),
+  // then converted and multiplied from those registers.
+  constexpr bool kAhead = PKV_PREFILL_K_AHEAD != 0 && PrefillShape<KV, D>::SPS >= 2 && !i8;
+  auto read_k = [&](int buf, u32x4 (&kk)[2][NL]) {
+    const uint8_t* base = lds[buf];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int j = 0; j < NL; ++j)
+        kk[gi][j] = *reinterpret_cast<const u32x4*>(base + gi * GB + lane * 16 + 1024 * j);
+  };
+  auto qk_pre = [&](const u32x4 (&kk)[2][NL], f32x4 (&s)[RT][2]) {
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      u32x4 kq[KQ];
+#pragma unroll
+      for (int j = 0; j < NL; ++j) {
+        if constexpr (bytewide) {
+          uint32_t w[8];
+          C::run(kk[gi][j], w);
+          kq[2 * j] = u32x4{w[0], w[1], w[2], w[3]};
+          kq[2 * j + 1] = u32x4{w[4], w[5], w[6], w[7]};
+        } else {
+          kq[j] = kk[gi][j];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < RT; ++k) {
+        s[k][gi] = f32x4{s_init[k], s_init[k], s_init[k], s_init[k]};
+#pragma unroll
+        for (int c = 0; c < KQ; ++c) s[k][gi] = mfma32(kq[c], qop[k][c], s[k][gi]);
+      }
+    }
+  };
   // The rest of a step: softmax of its scores s, then PV.
   // INT8, INT4: the step's 64 row scales (this wave's own copy) become their
   // reciprocals in place, one per lane (K's times kmul); each lane then reads
@@ -460,7 +498,8 @@ __device__ __forceinline__ void prefill_group(
     }
   };
   auto finish = [&](bool checked, int step, int buf, int p0, int p1, f32x4 (&s)[RT][2],
-                    const f32x4 (&ksp)[2], const f32x4 (&vsp)[2]) {
+                    const f32x4 (&ksp)[2], const f32x4 (&vsp)[2], int kbuf,
+                    u32x4 (&knext)[2][NL]) {
     const uint8_t* base = lds[buf];
     int n_valid[2] = {16, 16};
     if (checked) {
@@ -509,6 +548,12 @@ __device__ __forceinline__ void prefill_group(
           va[4 * j + q] = u32x4{w0[0], w0[1], w1[0], w1[1]};
         }
       }
+      if constexpr (kAhead) {
+        if (kbuf >= 0) {
+          read_k(kbuf, knext);
+          asm volatile("" ::: "memory");
+        }
+      }
     } else {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -518,6 +563,12 @@ __device__ __forceinline__ void prefill_group(
           const u32x2 v0 = *reinterpret_cast<const u32x2*>(base + 2 * GB + off);
           const u32x2 v1 = *reinterpret_cast<const u32x2*>(base + 3 * GB + off);
           va[2 * j + h] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+          asm volatile("" ::: "memory");
+        }
+      }
+      if constexpr (kAhead) {
+        if (kbuf >= 0) {
+          read_k(kbuf, knext);
           asm volatile("" ::: "memory");
         }
       }
@@ -667,6 +718,7 @@ __device__ __forceinline__ void prefill_group(
     nxt1[e] = tile_entry(2 * (NB - SPS + e) + 1);
   }
   step_barrier(false);
+  u32x4 knext[2][NL];                      // (kAhead: the next step's K bytes)
   for (int step0 = 0; step0 < nsteps; step0 += NB) {
     // (unrolled by NB so the buffer numbers are constants)
 #pragma unroll
@@ -697,9 +749,14 @@ __device__ __forceinline__ void prefill_group(
             f32x4 sc[RT][2];
             f32x4 ksp[2], vsp[2];
             scales(u + e, ksp, vsp);
-            qk(u + e, sc);
+            if (kAhead && e > 0)
+              qk_pre(knext, sc);
+            else
+              qk(u + e, sc);
+            // (the next step of the set: its K read at the end of this one's V reads)
+            const int kbuf = kAhead && e + 1 < SPS && step + 1 < nsteps ? u + e + 1 : -1;
             finish(2 * step + 2 > nfull || (phq0[u + e] | phq1[u + e]) < 0, step, u + e,
-                   phq0[u + e], phq1[u + e], sc, ksp, vsp);
+                   phq0[u + e], phq1[u + e], sc, ksp, vsp, kbuf, knext);
           }
         }
         // (the next set has landed everywhere: all but the newest NB - 2 SPS
