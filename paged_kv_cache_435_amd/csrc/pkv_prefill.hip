@@ -53,10 +53,14 @@
 //                              loads of NB - SPS steps are in flight)
 //   PKV_PREFILL_DEPTH_FP8, PKV_PREFILL_SYNC_FP8   the same for FP8 caches
 //   PKV_PREFILL_DEPTH_Q, PKV_PREFILL_SYNC_Q   the same for INT8, INT4
+//   PKV_PREFILL_K_AHEAD        with 2 or more steps per barrier, each later
+//                              step's K bytes read during the step before it
 // (16-bit caches: 2 steps per barrier in 4 buffers, 64 KB of LDS, took the
 // f16 prompt chunk from 352 to 331 us.  For FP8, 2 steps in 4 buffers took
-// 262 -> 251 us once the step's scalar work was trimmed; INT8 and INT4 keep
-// 1 step in 3 buffers (2 in 4 or 6: equal or 1 % slower).)
+// 262 -> 251 us once the step's scalar work was trimmed.  INT8 and INT4 gained
+// nothing from 2 steps in 4 buffers until the second step's K was read ahead:
+// then 293.7 -> 286.9 us (INT8) and 273.1 -> 266.4 (INT4); the read-ahead took
+// f16 252.1 -> 248.9 and FP8 243.1 -> 240.1.)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
@@ -73,13 +77,13 @@
 #define PKV_PREFILL_SYNC_FP8 2
 #endif
 #ifndef PKV_PREFILL_DEPTH_Q
-#define PKV_PREFILL_DEPTH_Q 3
+#define PKV_PREFILL_DEPTH_Q 4
 #endif
 #ifndef PKV_PREFILL_K_AHEAD
 #define PKV_PREFILL_K_AHEAD 1
 #endif
 #ifndef PKV_PREFILL_SYNC_Q
-#define PKV_PREFILL_SYNC_Q 1
+#define PKV_PREFILL_SYNC_Q 2
 #endif
 
 namespace pkv {
@@ -444,7 +448,7 @@ __device__ __forceinline__ void prefill_group(
   // Two or more steps per barrier (16-bit and FP8 caches): a step's K bytes
   // read during the previous step of its set (its buffer landed with the set),
   // then converted and multiplied from those registers.
-  constexpr bool kAhead = PKV_PREFILL_K_AHEAD != 0 && PrefillShape<KV, D>::SPS >= 2 && !i8;
+  constexpr bool kAhead = PKV_PREFILL_K_AHEAD != 0 && PrefillShape<KV, D>::SPS >= 2;
   auto read_k = [&](int buf, u32x4 (&kk)[2][NL]) {
     const uint8_t* base = lds[buf];
 #pragma unroll
@@ -459,7 +463,14 @@ __device__ __forceinline__ void prefill_group(
       u32x4 kq[KQ];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
-        if constexpr (bytewide) {
+        if constexpr (i4) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            uint32_t w[4];
+            C::word(kk[gi][j][c], w);
+            kq[c] = u32x4{w[0], w[1], w[2], w[3]};
+          }
+        } else if constexpr (bytewide) {
           uint32_t w[8];
           C::run(kk[gi][j], w);
           kq[2 * j] = u32x4{w[0], w[1], w[2], w[3]};
@@ -534,6 +545,12 @@ __device__ __forceinline__ void prefill_group(
         C::word(r1[w], w1);
         va[2 * w] = u32x4{w0[0], w0[2], w1[0], w1[2]};
         va[2 * w + 1] = u32x4{w0[1], w0[3], w1[1], w1[3]};
+      }
+      if constexpr (kAhead) {
+        if (kbuf >= 0) {
+          read_k(kbuf, knext);
+          asm volatile("" ::: "memory");
+        }
       }
     } else if constexpr (bytewide) {
 #pragma unroll
