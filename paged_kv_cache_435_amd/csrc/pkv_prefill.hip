@@ -59,8 +59,9 @@
 // f16 prompt chunk from 352 to 331 us.  For FP8, 2 steps in 4 buffers took
 // 262 -> 251 us once the step's scalar work was trimmed.  INT8 and INT4 gained
 // nothing from 2 steps in 4 buffers until the second step's K was read ahead:
-// then 293.7 -> 286.9 us (INT8) and 273.1 -> 266.4 (INT4); the read-ahead took
-// f16 252.1 -> 248.9 and FP8 243.1 -> 240.1.)
+// then 293.7 -> 286.9 us (INT8) and 273.1 -> 266.4 (INT4), and 3 steps in 6
+// buffers another 285.5 -> 283.2 and 266.6 -> 263.6 (FP8 that way: 0.5 %
+// slower); the read-ahead took f16 252.1 -> 248.9 and FP8 243.1 -> 240.1.)
 #ifndef PKV_PREFILL_WAVES_PER_EU
 #define PKV_PREFILL_WAVES_PER_EU 2
 #endif
@@ -77,13 +78,13 @@
 #define PKV_PREFILL_SYNC_FP8 2
 #endif
 #ifndef PKV_PREFILL_DEPTH_Q
-#define PKV_PREFILL_DEPTH_Q 4
+#define PKV_PREFILL_DEPTH_Q 6
 #endif
 #ifndef PKV_PREFILL_K_AHEAD
 #define PKV_PREFILL_K_AHEAD 1
 #endif
 #ifndef PKV_PREFILL_SYNC_Q
-#define PKV_PREFILL_SYNC_Q 2
+#define PKV_PREFILL_SYNC_Q 3
 #endif
 
 namespace pkv {
